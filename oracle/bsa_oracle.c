@@ -1,0 +1,664 @@
+/*
+ * bsa_oracle.c — plain, slow, obviously-correct CPU reference for the
+ * block-sparse video attention path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no
+ * source, header, table or helper with the HIP kernels it checks.
+ *
+ * Sources (web pages; each function below names the passage it follows):
+ *   [PARO]    pith.science machine verdict on arXiv 2506.16054,
+ *             "PAROAttention" (JSON fields: key_machinery, core_discovery,
+ *             pith_summary, referee_report).
+ *   [SPADE]   pith.science machine verdict on arXiv 2608.03335, "SPADE"
+ *             (key_machinery, core_discovery, referee minor comments on
+ *             §2.2 Eq. (2) and §3.1).
+ *   [COMPACT] pith.science review "Compact Attention: Exploiting Structured
+ *             Spatio-Temporal Sparsity for Fast Video Generation"
+ *             (section "What carries the argument").
+ *   [PASA]    pith.science review of arXiv 2604.12219 (top-k per query).
+ *
+ * Arithmetic: fp64 for attention; the block-pooling / scoring step follows
+ * a fixed fp32 operation sequence (sequential sums, fmaf chains, correctly
+ * rounded divide and sqrt) so that its integer outcome (the kept-block
+ * lists) is defined bit for bit; the INT8 quantiser follows a fixed fp32
+ * sequence for the same reason.  Build with -ffp-contract=off and without
+ * -ffast-math: no reassociation, no implicit contraction.
+ *
+ * Every pointer is a host pointer.  Functions return 0 on success and a
+ * negative value on a bad argument.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* element type codes used by this file only */
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_F64 = 3 };
+
+/* ------------------------------------------------------------------------
+ * Token order.  [PARO] key machinery: each head reorders the flattened
+ * F x H x W token sequence by one of the six orderings of the three axes.
+ * [PARO] pith summary: the 3D latent is flattened to a 1D sequence; the
+ * natural flattening used here is frame-major, width-minor:
+ *     n = (f*H + h)*W + w.
+ * Order code -> axes listed outermost to innermost (0=F, 1=H, 2=W):
+ *     0 FHW, 1 FWH, 2 HFW, 3 HWF, 4 WFH, 5 WHF.
+ * Position p of the reordered sequence enumerates the three coordinates
+ * with the first-listed axis slowest; perm[p] is that token's natural index.
+ * ---------------------------------------------------------------------- */
+static const int kAxes[6][3] = {
+    {0, 1, 2}, {0, 2, 1}, {1, 0, 2}, {1, 2, 0}, {2, 0, 1}, {2, 1, 0}};
+
+int oracle_perm(int order, int F, int H, int W, int32_t *perm) {
+  if (order < 0 || order > 5 || F <= 0 || H <= 0 || W <= 0 || !perm) return -1;
+  const int dims[3] = {F, H, W};
+  const int a0 = kAxes[order][0], a1 = kAxes[order][1], a2 = kAxes[order][2];
+  int x[3];
+  int64_t p = 0;
+  for (x[a0] = 0; x[a0] < dims[a0]; x[a0]++)
+    for (x[a1] = 0; x[a1] < dims[a1]; x[a1]++)
+      for (x[a2] = 0; x[a2] < dims[a2]; x[a2]++)
+        perm[p++] = (int32_t)(((int64_t)x[0] * H + x[1]) * W + x[2]);
+  return 0;
+}
+
+/* bf16 <-> fp32.  bf16 is the upper half of the binary32 pattern; narrowing
+ * rounds to nearest, ties to even (add 0x7FFF plus the kept LSB, truncate);
+ * NaN stays a quiet NaN. */
+static uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+static float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+void oracle_f32_to_bf16(const float *x, uint16_t *y, int64_t n) {
+  for (int64_t i = 0; i < n; i++) y[i] = f32_to_bf16(x[i]);
+}
+
+static double load_elem(const void *base, int dt, int64_t off) {
+  switch (dt) {
+    case OR_F32: return (double)((const float *)base)[off];
+    case OR_BF16: return (double)bf16_to_f32(((const uint16_t *)base)[off]);
+    case OR_I8: return (double)((const int8_t *)base)[off];
+    default: return ((const double *)base)[off];
+  }
+}
+
+/* Gather (direction 0) and its inverse (direction 1) for all heads.
+ * Natural side: element (n, g, c) at n*stride_n + g*stride_g + c.
+ * Permuted side: dense [G][N][d].  Types: OR_F32 or OR_BF16 on either side;
+ * fp32 -> bf16 rounds to nearest even, bf16 -> fp32 is exact. */
+int oracle_permute(int direction, const void *src, int src_dt, void *dst, int dst_dt,
+                   int64_t stride_g, int64_t stride_n, int G, int F, int H, int W, int d,
+                   const uint8_t *orders) {
+  if ((direction != 0 && direction != 1) || !src || !dst || !orders || G <= 0 || d <= 0)
+    return -1;
+  if ((src_dt != OR_F32 && src_dt != OR_BF16) || (dst_dt != OR_F32 && dst_dt != OR_BF16))
+    return -1;
+  const int64_t N = (int64_t)F * H * W;
+  int32_t *perm = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+  if (!perm) return -2;
+  for (int g = 0; g < G; g++) {
+    if (oracle_perm(orders[g], F, H, W, perm)) { free(perm); return -1; }
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < N; p++) {
+      const int64_t nat = (int64_t)perm[p] * stride_n + (int64_t)g * stride_g;
+      const int64_t pm = ((int64_t)g * N + p) * d;
+      for (int c = 0; c < d; c++) {
+        const int64_t so = direction == 0 ? nat + c : pm + c;
+        const int64_t doff = direction == 0 ? pm + c : nat + c;
+        float v = src_dt == OR_F32 ? ((const float *)src)[so]
+                                   : bf16_to_f32(((const uint16_t *)src)[so]);
+        if (dst_dt == OR_F32) ((float *)dst)[doff] = v;
+        else ((uint16_t *)dst)[doff] = src_dt == OR_BF16 ? ((const uint16_t *)src)[so]
+                                                          : f32_to_bf16(v);
+      }
+    }
+  }
+  free(perm);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Block summaries.  [SPADE] key machinery / minor comment on §3.1: each
+ * block of the reordered sequence is summarised (MEAN variant: the mean of
+ * its rows); [SPADE] key machinery also scores blocks by cosine similarity.
+ * Contract: per (head, block, channel) an fp32 running sum starting at +0,
+ * over the block's real rows in increasing order, each add rounded.
+ * X is bf16 [G][N][d]; S is fp32 [G][nb][d] with nb = ceil(N/B).
+ * ---------------------------------------------------------------------- */
+int oracle_block_sums(const uint16_t *X, int G, int64_t N, int d, int B, float *S) {
+  if (!X || !S || G <= 0 || N <= 0 || d <= 0 || B <= 0) return -1;
+  const int64_t nb = (N + B - 1) / B;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int g = 0; g < G; g++)
+    for (int64_t b = 0; b < nb; b++) {
+      const int64_t r0 = b * B, r1 = (r0 + B < N) ? r0 + B : N;
+      for (int c = 0; c < d; c++) {
+        float acc = 0.0f;
+        for (int64_t r = r0; r < r1; r++)
+          acc = acc + bf16_to_f32(X[((int64_t)g * N + r) * d + c]);
+        S[((int64_t)g * nb + b) * d + c] = acc;
+      }
+    }
+  return 0;
+}
+
+/* dot(x, y) := acc = +0; for c in 0..d-1: acc = fmaf(x[c], y[c], acc). */
+static float dot_chain(const float *x, const float *y, int d) {
+  float acc = 0.0f;
+  for (int c = 0; c < d; c++) acc = fmaf(x[c], y[c], acc);
+  return acc;
+}
+
+static int64_t block_len(int64_t b, int B, int64_t N) {
+  const int64_t r0 = b * B;
+  return (r0 + B <= N) ? B : N - r0;
+}
+
+/* Keys for one head: key[i][j] for i < nq, j < nk.
+ * score 0 (DOT of block means): a = Sq_i / len_i, b = Sk_j / len_j (each a
+ *   correctly rounded fp32 divide), key = dot(a, b).
+ * score 1 (COSINE of block sums): s = dot(Sq_i, Sk_j),
+ *   nq = sqrtf(dot(Sq_i, Sq_i)), nk = sqrtf(dot(Sk_j, Sk_j)),
+ *   den = nq*nk, key = den == 0 ? +0 : s/den. */
+int oracle_block_keys(const float *Sq, const float *Sk, int64_t nq, int64_t nk, int d,
+                      int Bq, int Bk, int64_t N, int score, float *key) {
+  if (!Sq || !Sk || !key || nq <= 0 || nk <= 0 || d <= 0 || (score != 0 && score != 1))
+    return -1;
+  float *a = (float *)malloc(sizeof(float) * (size_t)(nq * d));
+  float *b = (float *)malloc(sizeof(float) * (size_t)(nk * d));
+  float *na = (float *)malloc(sizeof(float) * (size_t)nq);
+  float *nb = (float *)malloc(sizeof(float) * (size_t)nk);
+  if (!a || !b || !na || !nb) { free(a); free(b); free(na); free(nb); return -2; }
+  for (int64_t i = 0; i < nq; i++) {
+    const float len = (float)block_len(i, Bq, N);
+    for (int c = 0; c < d; c++)
+      a[i * d + c] = score == 0 ? Sq[i * d + c] / len : Sq[i * d + c];
+    na[i] = sqrtf(dot_chain(Sq + i * d, Sq + i * d, d));
+  }
+  for (int64_t j = 0; j < nk; j++) {
+    const float len = (float)block_len(j, Bk, N);
+    for (int c = 0; c < d; c++)
+      b[j * d + c] = score == 0 ? Sk[j * d + c] / len : Sk[j * d + c];
+    nb[j] = sqrtf(dot_chain(Sk + j * d, Sk + j * d, d));
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < nq; i++)
+    for (int64_t j = 0; j < nk; j++) {
+      const float s = dot_chain(a + i * d, b + j * d, d);
+      if (score == 0) {
+        key[i * nk + j] = s;
+      } else {
+        const float den = na[i] * nb[j];
+        key[i * nk + j] = (den == 0.0f) ? 0.0f : s / den;
+      }
+    }
+  free(a); free(b); free(na); free(nb);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Per-row selection.
+ *   k = max(1, min(nk, floor(rho*nk + 1/2))), rho = rho_num/rho_den, in
+ *     integers.  [PARO] pith summary: density is the fraction of the map
+ *     that is computed; [PASA] top-k per query; [SPADE] core discovery:
+ *     Top-K plus a local window.
+ *   T_i: the first k kv-blocks under (key descending, index ascending);
+ *     IEEE comparison, so -0 and +0 tie.
+ *   D_i (force_diag): kv-blocks whose token range meets the q-block's own.
+ *   W_i (win_T >= 0): temporal window, [COMPACT] temporally varying
+ *     windows: with block centres c(b) = b*B + floor((len_b - 1)/2) in the
+ *     reordered sequence, mapped to natural coordinates (frame f, in-frame
+ *     offset o), keep (i, j) iff |f_i - f_j| <= T and
+ *     |o_i - o_j| <= (r0*W) >> |f_i - f_j|.
+ *   Row = T_i u D_i u W_i, emitted in ascending order.
+ * ---------------------------------------------------------------------- */
+static const float *g_sort_keys; /* qsort has no context argument */
+static int cmp_key_desc_idx_asc(const void *pa, const void *pb) {
+  const int32_t ia = *(const int32_t *)pa, ib = *(const int32_t *)pb;
+  const float ka = g_sort_keys[ia], kb = g_sort_keys[ib];
+  if (ka > kb) return -1;
+  if (ka < kb) return 1;
+  return (ia > ib) - (ia < ib);
+}
+
+int64_t oracle_select_k(int64_t nk, int rho_num, int rho_den) {
+  if (rho_den <= 0 || rho_num < 0) return -1;
+  int64_t k = (2 * (int64_t)rho_num * nk + rho_den) / (2 * (int64_t)rho_den);
+  if (k > nk) k = nk;
+  if (k < 1) k = 1;
+  return k;
+}
+
+/* Builds the CSR for all heads from per-head key matrices.
+ * keys: fp32 [G][nq][nk] (from oracle_block_keys); orders [G] (used by the
+ * window only).  row_ptr [G*nq+1]; col_idx capacity cap.  Returns 0, or -3
+ * when the capacity is too small (row_ptr is still complete then). */
+int oracle_select(const float *keys, int G, int F, int H, int W, int Bq, int Bk,
+                  const uint8_t *orders, int rho_num, int rho_den, int force_diag,
+                  int win_T, int win_r0, int32_t *row_ptr, int32_t *col_idx, int64_t cap,
+                  int64_t *nnz_out) {
+  const int64_t N = (int64_t)F * H * W;
+  if (!keys || !orders || !row_ptr || G <= 0 || Bq <= 0 || Bk <= 0) return -1;
+  const int64_t nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+  const int64_t k = oracle_select_k(nk, rho_num, rho_den);
+  if (k < 0) return -1;
+  int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)nk);
+  uint8_t *keep = (uint8_t *)malloc((size_t)nk);
+  int32_t *perm = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+  if (!idx || !keep || !perm) { free(idx); free(keep); free(perm); return -2; }
+  int64_t pos = 0;
+  int rc = 0;
+  const int64_t HW = (int64_t)H * W;
+  for (int g = 0; g < G; g++) {
+    if (oracle_perm(orders[g], F, H, W, perm)) { rc = -1; break; }
+    for (int64_t i = 0; i < nq; i++) {
+      const float *krow = keys + ((int64_t)g * nq + i) * nk;
+      memset(keep, 0, (size_t)nk);
+      for (int64_t j = 0; j < nk; j++) idx[j] = (int32_t)j;
+      g_sort_keys = krow;
+      qsort(idx, (size_t)nk, sizeof(int32_t), cmp_key_desc_idx_asc);
+      for (int64_t t = 0; t < k; t++) keep[idx[t]] = 1;
+      const int64_t q0 = i * Bq, q1 = (q0 + Bq < N ? q0 + Bq : N); /* [q0, q1) */
+      if (force_diag)
+        for (int64_t j = 0; j < nk; j++) {
+          const int64_t k0 = j * Bk, k1 = (k0 + Bk < N ? k0 + Bk : N);
+          if (k0 < q1 && q0 < k1) keep[j] = 1;
+        }
+      if (win_T >= 0) {
+        const int64_t ci = q0 + (block_len(i, Bq, N) - 1) / 2;
+        const int64_t ni = perm[ci], fi = ni / HW, oi = ni % HW;
+        for (int64_t j = 0; j < nk; j++) {
+          const int64_t cj = j * Bk + (block_len(j, Bk, N) - 1) / 2;
+          const int64_t nj = perm[cj], fj = nj / HW, oj = nj % HW;
+          const int64_t df = fi > fj ? fi - fj : fj - fi;
+          const int64_t dox = oi > oj ? oi - oj : oj - oi;
+          if (df <= win_T && dox <= (((int64_t)win_r0 * W) >> df)) keep[j] = 1;
+        }
+      }
+      row_ptr[(int64_t)g * nq + i] = (int32_t)pos;
+      for (int64_t j = 0; j < nk; j++)
+        if (keep[j]) {
+          if (col_idx && pos < cap) col_idx[pos] = (int32_t)j;
+          else rc = -3;
+          pos++;
+        }
+    }
+    if (rc == -1) break;
+  }
+  row_ptr[(int64_t)G * nq] = (int32_t)pos;
+  if (nnz_out) *nnz_out = pos;
+  free(idx); free(keep); free(perm);
+  return rc;
+}
+
+/* Whole mask build from reordered bf16 Q and K: sums -> keys -> select.
+ * near_ties (optional): count of rows whose k-th and (k+1)-th candidates
+ * have fp64-recomputed keys within 1e-5 relative (an audit of how close the
+ * fp32 ranking is to a tie; it does not change the result). */
+int oracle_build_mask(const uint16_t *Qp, const uint16_t *Kp, int G, int F, int H, int W, int d,
+                      const uint8_t *orders, int Bq, int Bk, int score, int rho_num, int rho_den,
+                      int force_diag, int win_T, int win_r0, int32_t *row_ptr, int32_t *col_idx,
+                      int64_t cap, int64_t *nnz_out, int64_t *near_ties) {
+  const int64_t N = (int64_t)F * H * W;
+  if (!Qp || !Kp || G <= 0 || N <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return -1;
+  const int64_t nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+  float *Sq = (float *)malloc(sizeof(float) * (size_t)(G * nq * d));
+  float *Sk = (float *)malloc(sizeof(float) * (size_t)(G * nk * d));
+  float *keys = (float *)malloc(sizeof(float) * (size_t)(G * nq * nk));
+  if (!Sq || !Sk || !keys) { free(Sq); free(Sk); free(keys); return -2; }
+  int rc = oracle_block_sums(Qp, G, N, d, Bq, Sq);
+  if (!rc) rc = oracle_block_sums(Kp, G, N, d, Bk, Sk);
+  for (int g = 0; g < G && !rc; g++)
+    rc = oracle_block_keys(Sq + (int64_t)g * nq * d, Sk + (int64_t)g * nk * d, nq, nk, d, Bq, Bk,
+                           N, score, keys + (int64_t)g * nq * nk);
+  if (!rc && near_ties) {
+    /* fp64 keys from fp64 sums, only at the top-k boundary of each row */
+    int64_t ties = 0;
+    const int64_t k = oracle_select_k(nk, rho_num, rho_den);
+    if (k < nk) {
+#pragma omp parallel for reduction(+ : ties) schedule(dynamic)
+      for (int64_t gi = 0; gi < (int64_t)G * nq; gi++) {
+        const int g = (int)(gi / nq);
+        const int64_t i = gi % nq;
+        const float *kk = keys + gi * nk;
+        /* the k-th and (k+1)-th candidates under (key desc, index asc):
+         * shell sort of a private index list (qsort's comparator would need
+         * shared state) */
+        int32_t *id = (int32_t *)malloc(sizeof(int32_t) * (size_t)nk);
+        for (int64_t j = 0; j < nk; j++) id[j] = (int32_t)j;
+        for (int64_t gap = nk / 2; gap > 0; gap /= 2)
+          for (int64_t a = gap; a < nk; a++) {
+            const int32_t t = id[a];
+            int64_t b = a;
+            while (b >= gap && (kk[id[b - gap]] < kk[t] ||
+                                (kk[id[b - gap]] == kk[t] && id[b - gap] > t))) {
+              id[b] = id[b - gap];
+              b -= gap;
+            }
+            id[b] = t;
+          }
+        const int64_t ja = id[k - 1], jb = id[k];
+        free(id);
+        const double li = (double)block_len(i, Bq, N);
+        const double la = (double)block_len(ja, Bk, N), lb = (double)block_len(jb, Bk, N);
+        double sa = 0, sb = 0, nqq = 0, nka = 0, nkb = 0;
+        for (int c = 0; c < d; c++) {
+          double q = 0, ka = 0, kb = 0;
+          for (int64_t r = i * Bq; r < i * Bq + (int64_t)li; r++)
+            q += bf16_to_f32(Qp[((int64_t)g * N + r) * d + c]);
+          for (int64_t r = ja * Bk; r < ja * Bk + (int64_t)la; r++)
+            ka += bf16_to_f32(Kp[((int64_t)g * N + r) * d + c]);
+          for (int64_t r = jb * Bk; r < jb * Bk + (int64_t)lb; r++)
+            kb += bf16_to_f32(Kp[((int64_t)g * N + r) * d + c]);
+          if (score == 0) {
+            sa += (q / li) * (ka / la);
+            sb += (q / li) * (kb / lb);
+          } else {
+            sa += q * ka; sb += q * kb;
+            nqq += q * q; nka += ka * ka; nkb += kb * kb;
+          }
+        }
+        if (score == 1) {
+          sa = (nqq * nka == 0) ? 0 : sa / sqrt(nqq * nka);
+          sb = (nqq * nkb == 0) ? 0 : sb / sqrt(nqq * nkb);
+        }
+        const double scale = fmax(fabs(sa), fabs(sb));
+        if (fabs(sa - sb) <= 1e-5 * scale) ties++;
+      }
+    }
+    *near_ties = ties;
+  }
+  if (!rc)
+    rc = oracle_select(keys, G, F, H, W, Bq, Bk, orders, rho_num, rho_den, force_diag, win_T,
+                       win_r0, row_ptr, col_idx, cap, nnz_out);
+  free(Sq); free(Sk); free(keys);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * INT8 quantiser.  [PARO] key machinery: block-wise INT8 quantisation whose
+ * blocks line up with the attention block; symmetric, per (head, block).
+ *   amax = max |x| over the block's real rows x d (exact);
+ *   amax == 0 -> scale 0, q 0;
+ *   else scale = amax/127, inv = 127/amax (fp32, correctly rounded),
+ *        q = clamp(rint(x*inv), -127, 127) with rint = round half to even.
+ * X bf16 [G][N][d] -> q int8 [G][N][d], scale fp32 [G][ceil(N/B)].
+ * ---------------------------------------------------------------------- */
+int oracle_quantize_int8(const uint16_t *X, int G, int64_t N, int d, int B, int8_t *q,
+                         float *scale) {
+  if (!X || !q || !scale || G <= 0 || N <= 0 || d <= 0 || B <= 0) return -1;
+  const int64_t nb = (N + B - 1) / B;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int g = 0; g < G; g++)
+    for (int64_t b = 0; b < nb; b++) {
+      const int64_t r0 = b * B, r1 = (r0 + B < N) ? r0 + B : N;
+      float amax = 0.0f;
+      for (int64_t r = r0; r < r1; r++)
+        for (int c = 0; c < d; c++) {
+          const float v = fabsf(bf16_to_f32(X[((int64_t)g * N + r) * d + c]));
+          if (v > amax) amax = v;
+        }
+      const float s = amax == 0.0f ? 0.0f : amax / 127.0f;
+      const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+      scale[(int64_t)g * nb + b] = s;
+      for (int64_t r = r0; r < r1; r++)
+        for (int c = 0; c < d; c++) {
+          const int64_t o = ((int64_t)g * N + r) * d + c;
+          float y = rintf(bf16_to_f32(X[o]) * inv);
+          if (y > 127.0f) y = 127.0f;
+          if (y < -127.0f) y = -127.0f;
+          q[o] = (int8_t)y;
+        }
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Masked softmax attention, fp64, on natural-order inputs.
+ * [SPADE] referee minor comment on §2.2 Eq. (2): the block mask is additive,
+ * 0 on kept block pairs and -inf on pruned ones.  Token n of head g may see
+ * token m iff the kv-block of m's reordered position is in the CSR row of
+ * the q-block of n's reordered position.  Written as the dense definition:
+ * every m in 0..N-1 is visited and masked ones contribute exp(-inf) = 0.
+ *   s_m = sm_scale * <q_n, k_m>,  M = max s,  l = sum exp(s_m - M),
+ *   O_n = sum exp(s_m - M) v_m / l,  LSE_n = M + ln l.
+ * Inputs: element (n, g, c) at n*stride_n + g*stride_g + c, type dt
+ * (OR_F32, OR_BF16 or OR_F64).  CSR row of (g, i) is (g % mask_G)*nq + i.
+ * rows: npairs of (g, n).  Outputs O [nrows][d], lse [nrows] (fp64).
+ * An empty row gives O = 0, LSE = -inf.  mask_all != 0 ignores the CSR and
+ * keeps everything (plain dense attention).
+ * ---------------------------------------------------------------------- */
+int oracle_attention_rows(const void *Q, const void *K, const void *V, int dt, int64_t stride_g,
+                          int64_t stride_n, int G, int F, int H, int W, int d,
+                          const uint8_t *orders, int Bq, int Bk, const int32_t *row_ptr,
+                          const int32_t *col_idx, int mask_G, int mask_all, double sm_scale,
+                          const int64_t *rows, int64_t nrows, double *O, double *lse) {
+  const int64_t N = (int64_t)F * H * W;
+  if (!Q || !K || !V || !orders || !rows || !O || !lse || G <= 0 || N <= 0 || d <= 0) return -1;
+  if (!mask_all && (!row_ptr || !col_idx || mask_G <= 0 || Bq <= 0 || Bk <= 0)) return -1;
+  if (dt != OR_F32 && dt != OR_BF16 && dt != OR_F64) return -1;
+  const int64_t nq = mask_all ? 1 : (N + Bq - 1) / Bq;
+  const int64_t nk = mask_all ? 1 : (N + Bk - 1) / Bk;
+  int32_t *perm = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+  int32_t *pos = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+  if (!perm || !pos) { free(perm); free(pos); return -2; }
+  int rc = 0;
+  for (int g = 0; g < G && !rc; g++) {
+    int any = 0;
+    for (int64_t t = 0; t < nrows; t++) any |= rows[2 * t] == g;
+    if (!any) continue;
+    if (oracle_perm(orders[g], F, H, W, perm)) { rc = -1; break; }
+    for (int64_t p = 0; p < N; p++) pos[perm[p]] = (int32_t)p;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t t = 0; t < nrows; t++) {
+      if (rows[2 * t] != g) continue;
+      const int64_t n = rows[2 * t + 1];
+      double *o = O + t * d;
+      uint8_t *kept = (uint8_t *)calloc((size_t)nk, 1);
+      double *s = (double *)malloc(sizeof(double) * (size_t)N);
+      double *qv = (double *)malloc(sizeof(double) * (size_t)d);
+      if (mask_all) kept[0] = 1;
+      else {
+        const int64_t i = pos[n] / Bq;
+        const int64_t row = (int64_t)(g % mask_G) * nq + i;
+        for (int64_t e = row_ptr[row]; e < row_ptr[row + 1]; e++)
+          if (col_idx[e] >= 0 && col_idx[e] < nk) kept[col_idx[e]] = 1;
+      }
+      for (int c = 0; c < d; c++) qv[c] = load_elem(Q, dt, n * stride_n + (int64_t)g * stride_g + c);
+      double mx = -INFINITY;
+      for (int64_t m = 0; m < N; m++) {
+        const int64_t j = mask_all ? 0 : pos[m] / Bk;
+        if (!kept[j]) { s[m] = -INFINITY; continue; }
+        double acc = 0.0;
+        const int64_t kb = m * stride_n + (int64_t)g * stride_g;
+        for (int c = 0; c < d; c++) acc += qv[c] * load_elem(K, dt, kb + c);
+        s[m] = sm_scale * acc;
+        if (s[m] > mx) mx = s[m];
+      }
+      for (int c = 0; c < d; c++) o[c] = 0.0;
+      if (mx == -INFINITY) {
+        lse[t] = -INFINITY;
+      } else {
+        double l = 0.0;
+        for (int64_t m = 0; m < N; m++) {
+          if (s[m] == -INFINITY) continue;
+          const double p = exp(s[m] - mx);
+          l += p;
+          const int64_t vb = m * stride_n + (int64_t)g * stride_g;
+          for (int c = 0; c < d; c++) o[c] += p * load_elem(V, dt, vb + c);
+        }
+        for (int c = 0; c < d; c++) o[c] /= l;
+        lse[t] = mx + log(l);
+      }
+      free(kept); free(s); free(qv);
+    }
+  }
+  free(perm); free(pos);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * INT8 block-sparse attention, emulating the online (flash) order, on
+ * reordered int8 tensors [G][N][d] with fp32 per-block scales.
+ * [PARO] key machinery / core discovery: Q.K^T in INT8 and the post-softmax
+ * map quantised to INT8 block-wise, with the FlashAttention block as the
+ * quantisation block.  For each (g, q-block i): m = -inf, l = 0, acc = 0;
+ * for each kv-block j of the CSR row, in CSR (ascending) order:
+ *   I   = sum_e q8[r][e] k8[c][e]                 (exact integer)
+ *   S   = I * sQ_i * sK_j * sm_scale
+ *   m'  = max(m, max_c S);  Pt = exp(S - m');  a = exp(m - m')
+ *   l   = l*a + sum_c Pt                          (unquantised Pt)
+ *   mP  = max of Pt over the tile's real rows and columns
+ *   P8  = clamp(rint(Pt * 127/mP), 0, 127), sP = mP/127   (mP == 0: P8 = 0)
+ *   acc = acc*a + sP * sV_j * sum_c P8[r][c] v8[c] (exact integer inner sum)
+ *   m   = m'
+ * O = acc/l, LSE = m + ln l (O = 0, LSE = -inf for an empty row).
+ * quantize_p == 0 replaces the P8 step by the exact product
+ * sum_c Pt[r][c] * (v8[c]*sV_j), i.e. attention on dequantised inputs.
+ * blocks: nblk pairs (g, i).  O [nblk][Bq][d], lse [nblk][Bq]; rows past N
+ * are left as 0 / -inf.
+ * ---------------------------------------------------------------------- */
+int oracle_attention_int8(const int8_t *Qq, const float *sQ, const int8_t *Kq, const float *sK,
+                          const int8_t *Vq, const float *sV, int G, int64_t N, int d, int Bq,
+                          int Bk, const int32_t *row_ptr, const int32_t *col_idx, int mask_G,
+                          double sm_scale, int quantize_p, const int64_t *blocks, int64_t nblk,
+                          double *O, double *lse) {
+  if (!Qq || !sQ || !Kq || !sK || !Vq || !sV || !row_ptr || !col_idx || !blocks || !O || !lse)
+    return -1;
+  if (G <= 0 || N <= 0 || d <= 0 || Bq <= 0 || Bk <= 0 || mask_G <= 0) return -1;
+  const int64_t nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t t = 0; t < nblk; t++) {
+    const int g = (int)blocks[2 * t];
+    const int64_t i = blocks[2 * t + 1];
+    const int64_t r0 = i * Bq, rn = (r0 + Bq < N ? Bq : N - r0);
+    double *o = O + t * (int64_t)Bq * d;
+    double *ls = lse + t * (int64_t)Bq;
+    double *m = (double *)malloc(sizeof(double) * Bq);
+    double *l = (double *)malloc(sizeof(double) * Bq);
+    double *S = (double *)malloc(sizeof(double) * (size_t)Bq * Bk);
+    int64_t *P8 = (int64_t *)malloc(sizeof(int64_t) * (size_t)Bq * Bk);
+    for (int r = 0; r < Bq; r++) { m[r] = -INFINITY; l[r] = 0.0; ls[r] = -INFINITY; }
+    for (int64_t e = 0; e < (int64_t)Bq * d; e++) o[e] = 0.0;
+    const int64_t row = (int64_t)(g % mask_G) * nq + i;
+    const double sq = sQ[(int64_t)g * nq + i];
+    for (int64_t e = row_ptr[row]; e < row_ptr[row + 1]; e++) {
+      const int64_t j = col_idx[e];
+      if (j < 0 || j >= nk) continue;
+      const int64_t c0 = j * Bk, cn = (c0 + Bk < N ? Bk : N - c0);
+      const double sk = sK[(int64_t)g * nk + j], sv = sV[(int64_t)g * nk + j];
+      double mP = 0.0;
+      for (int64_t r = 0; r < rn; r++) {
+        const int8_t *qr = Qq + ((int64_t)g * N + r0 + r) * d;
+        double tmax = -INFINITY;
+        for (int64_t c = 0; c < cn; c++) {
+          const int8_t *kc = Kq + ((int64_t)g * N + c0 + c) * d;
+          int64_t I = 0;
+          for (int x = 0; x < d; x++) I += (int64_t)qr[x] * (int64_t)kc[x];
+          S[r * Bk + c] = (double)I * sq * sk * sm_scale;
+          if (S[r * Bk + c] > tmax) tmax = S[r * Bk + c];
+        }
+        const double mnew = m[r] > tmax ? m[r] : tmax;
+        const double a = m[r] == -INFINITY ? 0.0 : exp(m[r] - mnew);
+        double rs = 0.0;
+        for (int64_t c = 0; c < cn; c++) {
+          S[r * Bk + c] = exp(S[r * Bk + c] - mnew); /* now holds Pt */
+          rs += S[r * Bk + c];
+          if (S[r * Bk + c] > mP) mP = S[r * Bk + c];
+        }
+        l[r] = l[r] * a + rs;
+        for (int x = 0; x < d; x++) o[r * d + x] *= a;
+        m[r] = mnew;
+      }
+      if (quantize_p) {
+        if (mP > 0.0) {
+          const double sP = mP / 127.0;
+          for (int64_t r = 0; r < rn; r++)
+            for (int64_t c = 0; c < cn; c++) {
+              double y = rint(S[r * Bk + c] * 127.0 / mP);
+              if (y > 127.0) y = 127.0;
+              if (y < 0.0) y = 0.0;
+              P8[r * Bk + c] = (int64_t)y;
+            }
+          for (int64_t r = 0; r < rn; r++)
+            for (int x = 0; x < d; x++) {
+              int64_t acc = 0;
+              for (int64_t c = 0; c < cn; c++)
+                acc += P8[r * Bk + c] * (int64_t)Vq[((int64_t)g * N + c0 + c) * d + x];
+              o[r * d + x] += sP * sv * (double)acc;
+            }
+        }
+      } else {
+        for (int64_t r = 0; r < rn; r++)
+          for (int x = 0; x < d; x++) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < cn; c++)
+              acc += S[r * Bk + c] * ((double)Vq[((int64_t)g * N + c0 + c) * d + x] * sv);
+            o[r * d + x] += acc;
+          }
+      }
+    }
+    for (int64_t r = 0; r < rn; r++) {
+      if (l[r] > 0.0) {
+        for (int x = 0; x < d; x++) o[r * d + x] /= l[r];
+        ls[r] = m[r] + log(l[r]);
+      }
+    }
+    free(m); free(l); free(S); free(P8);
+  }
+  return 0;
+}
+
+/* Exact integer tile products, the definitions the INT8 kernel's MFMA
+ * tiles must reproduce: S[r][c] = sum_e q8[i*Bq + r][e] * k8[j*Bk + c][e]
+ * and OV[r][x] = sum_c P8[r][c] * v8[j*Bk + c][x]; rows/cols past N are 0. */
+int oracle_int8_qk_tile(const int8_t *Qq, const int8_t *Kq, int g, int64_t N, int d, int Bq,
+                        int Bk, int64_t i, int64_t j, int32_t *S) {
+  for (int r = 0; r < Bq; r++)
+    for (int c = 0; c < Bk; c++) {
+      const int64_t qr = i * Bq + r, kc = j * Bk + c;
+      int64_t acc = 0;
+      if (qr < N && kc < N)
+        for (int x = 0; x < d; x++)
+          acc += (int64_t)Qq[((int64_t)g * N + qr) * d + x] * Kq[((int64_t)g * N + kc) * d + x];
+      S[r * Bk + c] = (int32_t)acc;
+    }
+  return 0;
+}
+
+int oracle_int8_pv_tile(const int8_t *P8, const int8_t *Vq, int g, int64_t N, int d, int Bq,
+                        int Bk, int64_t j, int32_t *OV) {
+  for (int r = 0; r < Bq; r++)
+    for (int x = 0; x < d; x++) {
+      int64_t acc = 0;
+      for (int c = 0; c < Bk; c++) {
+        const int64_t kc = j * Bk + c;
+        if (kc < N) acc += (int64_t)P8[r * Bk + c] * Vq[((int64_t)g * N + kc) * d + x];
+      }
+      OV[r * d + x] = (int32_t)acc;
+    }
+  return 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
