@@ -1,0 +1,26 @@
+"""MI355X-native block-sparse self-attention over 3D video tokens.
+
+Public surface (Python names mirror the C ABI in include/bsa.h):
+``permute``, ``mask_capacity``, ``mask_workspace``, ``build_mask``,
+``quantize_int8``, ``forward``, ``forward_int8``, ``debug_int8_qk``,
+``debug_int8_pv``, plus ``LayerPlan`` / ``layer_forward`` which chain them.
+The HIP library is loaded on first use and must be built; there is no
+fallback path.  ``synth`` holds the seeded synthetic workload generators.
+"""
+from .api import (  # noqa: F401
+    LayerPlan,
+    abi_version,
+    build_mask,
+    debug_int8_pv,
+    debug_int8_qk,
+    forward,
+    forward_int8,
+    last_error,
+    layer_forward,
+    mask_capacity,
+    mask_params,
+    mask_workspace,
+    permute,
+    quantize_int8,
+)
+from ._lib import BsaError, MaskParams  # noqa: F401

@@ -1,0 +1,248 @@
+"""Python binding of the C ABI in include/bsa.h, on torch device tensors.
+
+Each function checks tensor properties, passes raw device pointers and the
+current HIP stream to the C entry point of the same name, and allocates its
+outputs with torch (torch is only the allocator and stream provider here).
+Every step of the computation runs in the HIP kernels of libbsa.so.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import MaskParams, BSA_BF16, BSA_F32, check
+
+_DT = {torch.float32: BSA_F32, torch.bfloat16: BSA_BF16, torch.int8: _lib.BSA_I8}
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("bsa: tensors must live on the GPU")
+
+
+def abi_version() -> int:
+    return int(_lib.load().bsa_abi_version())
+
+
+def last_error() -> str:
+    m = _lib.load().bsa_last_error()
+    return m.decode() if m else ""
+
+
+def mask_params(Bq=64, Bk=64, score=0, rho=(30, 100), force_diag=True, win_T=-1, win_r0=0):
+    return MaskParams(Bq, Bk, score, rho[0], rho[1], 1 if force_diag else 0, win_T, win_r0)
+
+
+def permute(x, axis_order, F, H, W, direction=0, out=None, out_dtype=torch.bfloat16):
+    """bsa_permute.  direction 0: natural x [N][G][d] (any strides with unit
+    channel stride) -> reordered [G][N][d]; direction 1: reordered x [G][N][d]
+    -> natural (``out`` may be a strided [N][G][d] view; default new [N][G][d]).
+    ``axis_order``: uint8 device tensor [G]."""
+    _lib.load()
+    N = F * H * W
+    if direction == 0:
+        if x.dim() != 3 or x.shape[0] != N or x.stride(2) != 1:
+            raise ValueError("natural input must be [N][G][d] with unit channel stride")
+        G, d = x.shape[1], x.shape[2]
+        sn, sg = x.stride(0), x.stride(1)
+        if out is None:
+            out = torch.empty((G, N, d), dtype=out_dtype, device=x.device)
+        src, dst = x, out
+    else:
+        if x.dim() != 3 or x.shape[1] != N or not x.is_contiguous():
+            raise ValueError("reordered input must be contiguous [G][N][d]")
+        G, d = x.shape[0], x.shape[2]
+        if out is None:
+            out = torch.empty((N, G, d), dtype=out_dtype, device=x.device)
+        if out.shape != (N, G, d) or out.stride(2) != 1:
+            raise ValueError("natural output must be [N][G][d] with unit channel stride")
+        sn, sg = out.stride(0), out.stride(1)
+        src, dst = x, out
+    _dev(src, dst, axis_order)
+    if axis_order.dtype != torch.uint8 or axis_order.numel() < G:
+        raise ValueError("axis_order must be a uint8 tensor with G entries")
+    rc = _lib.load().bsa_permute(direction, _ptr(src), _DT[src.dtype], _ptr(dst), _DT[dst.dtype],
+                                 sg, sn, G, F, H, W, d, _ptr(axis_order), _stream())
+    check(rc)
+    return out
+
+
+def mask_capacity(G, F, H, W, params: MaskParams) -> int:
+    v = int(_lib.load().bsa_mask_capacity(G, F, H, W, ctypes.byref(params)))
+    if v < 0:
+        check(v)
+    return v
+
+
+def mask_workspace(G, F, H, W, d, params: MaskParams) -> int:
+    v = int(_lib.load().bsa_mask_workspace(G, F, H, W, d, ctypes.byref(params)))
+    if v < 0:
+        check(v)
+    return v
+
+
+def build_mask(Qp, Kp, axis_order, F, H, W, params: MaskParams, workspace=None):
+    """bsa_build_mask on reordered bf16 Qp, Kp [G][N][d].  Returns
+    (row_ptr int32[G*Nq+1], col_idx int32[capacity], nnz int32[1]) on the
+    device; only col_idx[:nnz] is meaningful."""
+    _dev(Qp, Kp, axis_order)
+    G, N, d = Qp.shape
+    cap = mask_capacity(G, F, H, W, params)
+    ws_bytes = mask_workspace(G, F, H, W, d, params)
+    nq = (N + params.Bq - 1) // params.Bq
+    row_ptr = torch.empty(G * nq + 1, dtype=torch.int32, device=Qp.device)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=Qp.device)
+    nnz = torch.empty(1, dtype=torch.int32, device=Qp.device)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=Qp.device)
+    rc = _lib.load().bsa_build_mask(_ptr(Qp), _ptr(Kp), _DT[Qp.dtype], G, F, H, W, d,
+                                    _ptr(axis_order), ctypes.byref(params), _ptr(row_ptr),
+                                    _ptr(col_idx), col_idx.numel(), _ptr(nnz), _ptr(workspace),
+                                    workspace.numel(), _stream())
+    check(rc)
+    return row_ptr, col_idx, nnz
+
+
+def quantize_int8(Xp, B):
+    """bsa_quantize_int8: bf16 [G][N][d] -> (int8 [G][N][d], fp32 scales [G][ceil(N/B)])."""
+    _dev(Xp)
+    G, N, d = Xp.shape
+    q = torch.empty((G, N, d), dtype=torch.int8, device=Xp.device)
+    s = torch.empty((G, (N + B - 1) // B), dtype=torch.float32, device=Xp.device)
+    check(_lib.load().bsa_quantize_int8(_ptr(Xp), _ptr(q), _ptr(s), G, N, d, B, _stream()))
+    return q, s
+
+
+def forward(Qp, Kp, Vp, row_ptr, col_idx, Bq, Bk, mask_G=None, sm_scale=0.0, out=None,
+            lse=None, want_lse=True, col_len=None):
+    """bsa_forward: bf16 block-sparse attention on reordered tensors.
+    Returns (O bf16 [G][N][d], lse fp32 [G][N] or None)."""
+    _dev(Qp, Kp, Vp, row_ptr, col_idx)
+    G, N, d = Qp.shape
+    if out is None:
+        out = torch.empty_like(Qp)
+    if lse is None and want_lse:
+        lse = torch.empty((G, N), dtype=torch.float32, device=Qp.device)
+    rc = _lib.load().bsa_forward(_ptr(Qp), _ptr(Kp), _ptr(Vp), _ptr(row_ptr), _ptr(col_idx),
+                                 col_idx.numel() if col_len is None else col_len,
+                                 G if mask_G is None else mask_G, _ptr(out), _ptr(lse), G, N, d, Bq,
+                                 Bk, float(sm_scale), _stream())
+    check(rc)
+    return out, lse
+
+
+def forward_int8(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, Bq, Bk, mask_G=None, sm_scale=0.0,
+                 out=None, lse=None, want_lse=True, col_len=None):
+    """bsa_forward_int8 on int8 reordered tensors with per-block scales."""
+    _dev(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx)
+    G, N, d = Qq.shape
+    if out is None:
+        out = torch.empty((G, N, d), dtype=torch.bfloat16, device=Qq.device)
+    if lse is None and want_lse:
+        lse = torch.empty((G, N), dtype=torch.float32, device=Qq.device)
+    rc = _lib.load().bsa_forward_int8(_ptr(Qq), _ptr(sQ), _ptr(Kq), _ptr(sK), _ptr(Vq), _ptr(sV),
+                                      _ptr(row_ptr), _ptr(col_idx),
+                                      col_idx.numel() if col_len is None else col_len,
+                                      G if mask_G is None else mask_G, _ptr(out), _ptr(lse), G, N,
+                                      d, Bq, Bk, float(sm_scale), _stream())
+    check(rc)
+    return out, lse
+
+
+def debug_int8_qk(Qq, Kq, gij, Bq, Bk):
+    """bsa_debug_int8_qk: exact int32 Q.K^T tiles for gij int32 [n][3] of (g, i, j)."""
+    _dev(Qq, Kq, gij)
+    G, N, d = Qq.shape
+    n = gij.shape[0]
+    S = torch.empty((n, Bq, Bk), dtype=torch.int32, device=Qq.device)
+    check(_lib.load().bsa_debug_int8_qk(_ptr(Qq), _ptr(Kq), G, N, d, Bq, Bk, _ptr(gij), n, _ptr(S),
+                                        _stream()))
+    return S
+
+
+def debug_int8_pv(P8, Vq, gj, Bq, Bk):
+    """bsa_debug_int8_pv: exact int32 P.V tiles, P8 int8 [n][Bq][Bk], gj int32 [n][2]."""
+    _dev(P8, Vq, gj)
+    G, N, d = Vq.shape
+    n = gj.shape[0]
+    OV = torch.empty((n, Bq, d), dtype=torch.int32, device=Vq.device)
+    check(_lib.load().bsa_debug_int8_pv(_ptr(P8), _ptr(Vq), G, N, d, Bq, Bk, _ptr(gj), n, _ptr(OV),
+                                        _stream()))
+    return OV
+
+
+class LayerPlan:
+    """Buffers for one attention layer over natural-order [N][G][d] tensors:
+    reordered copies, mask CSR, INT8 copies and the output, allocated once
+    and reused by :func:`layer_forward`."""
+
+    def __init__(self, G, F, H, W, d, device, params: MaskParams, int8=False, dynamic_mask=True):
+        N = F * H * W
+        self.G, self.F, self.H, self.W, self.d, self.N = G, F, H, W, d, N
+        self.params = params
+        self.int8 = int8
+        self.dynamic_mask = dynamic_mask
+        e = dict(device=device)
+        self.Qp = torch.empty((G, N, d), dtype=torch.bfloat16, **e)
+        self.Kp = torch.empty_like(self.Qp)
+        self.Vp = torch.empty_like(self.Qp)
+        self.Op = torch.empty_like(self.Qp)
+        self.lse = torch.empty((G, N), dtype=torch.float32, **e)
+        self.O = torch.empty((N, G, d), dtype=torch.bfloat16, **e)
+        nq = (N + params.Bq - 1) // params.Bq
+        cap = mask_capacity(G, F, H, W, params)
+        self.row_ptr = torch.zeros(G * nq + 1, dtype=torch.int32, **e)
+        self.col_idx = torch.zeros(max(cap, 1), dtype=torch.int32, **e)
+        self.nnz = torch.zeros(1, dtype=torch.int32, **e)
+        self.ws = torch.empty(mask_workspace(G, F, H, W, d, params), dtype=torch.uint8, **e)
+        if int8:
+            nk = (N + params.Bk - 1) // params.Bk
+            self.Qq = torch.empty((G, N, d), dtype=torch.int8, **e)
+            self.Kq = torch.empty_like(self.Qq)
+            self.Vq = torch.empty_like(self.Qq)
+            self.sQ = torch.empty((G, nq), dtype=torch.float32, **e)
+            self.sK = torch.empty((G, nk), dtype=torch.float32, **e)
+            self.sV = torch.empty((G, nk), dtype=torch.float32, **e)
+
+    def build_mask(self, axis_order):
+        lib = _lib.load()
+        p = self.params
+        check(lib.bsa_build_mask(_ptr(self.Qp), _ptr(self.Kp), BSA_BF16, self.G, self.F, self.H,
+                                 self.W, self.d, _ptr(axis_order), ctypes.byref(p),
+                                 _ptr(self.row_ptr), _ptr(self.col_idx), self.col_idx.numel(),
+                                 _ptr(self.nnz), _ptr(self.ws), self.ws.numel(), _stream()))
+
+
+def layer_forward(plan: LayerPlan, Q, K, V, axis_order):
+    """One pass of the whole path on natural-order Q, K, V [N][G][d]:
+    reorder (x3) -> [build mask] -> [quantize (x3)] -> block-sparse attention
+    -> inverse reorder.  Returns the natural-order output [N][G][d] (bf16)."""
+    F, H, W = plan.F, plan.H, plan.W
+    p = plan.params
+    permute(Q, axis_order, F, H, W, 0, out=plan.Qp)
+    permute(K, axis_order, F, H, W, 0, out=plan.Kp)
+    permute(V, axis_order, F, H, W, 0, out=plan.Vp)
+    if plan.dynamic_mask:
+        plan.build_mask(axis_order)
+    if plan.int8:
+        lib = _lib.load()
+        for x, q, s, B in ((plan.Qp, plan.Qq, plan.sQ, p.Bq), (plan.Kp, plan.Kq, plan.sK, p.Bk),
+                           (plan.Vp, plan.Vq, plan.sV, p.Bk)):
+            check(lib.bsa_quantize_int8(_ptr(x), _ptr(q), _ptr(s), plan.G, plan.N, plan.d, B,
+                                        _stream()))
+        forward_int8(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq, plan.sV, plan.row_ptr,
+                     plan.col_idx, p.Bq, p.Bk, out=plan.Op, lse=plan.lse)
+    else:
+        forward(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk, out=plan.Op,
+                lse=plan.lse)
+    permute(plan.Op, axis_order, F, H, W, 1, out=plan.O)
+    return plan.O

@@ -1,0 +1,624 @@
+// attn.hip — block-sparse flash attention forward for gfx950 (bf16 and INT8).
+//
+// SPADE machine verdict (pith.science, arXiv 2608.03335), key machinery: a
+// flash-style block-sparse kernel with online softmax computes only the
+// kept blocks; referee minor comment on §2.2 Eq. (2): the block mask is
+// additive (0 kept, -inf pruned).  PAROAttention machine verdict
+// (pith.science, arXiv 2506.16054), key machinery and core discovery: the
+// INT8 variant runs Q.K^T in INT8 and quantises the post-softmax map to
+// INT8, with quantisation blocks equal to the attention blocks.
+//
+// Work split: one workgroup per (head g, q-block i) of Bq rows; Bq/32 waves,
+// each owning 32 query rows.  The workgroup walks the CSR row of its
+// q-block; for each kept kv-block j it stages K_j (row-major) and V_j
+// (transposed) in LDS, then every wave computes
+//     S^T = K_j . Q^T          (32x32 MFMA tiles, A = K from LDS, B = Q regs)
+// so that the accumulator holds one query row per lane (the two wave halves
+// share a row); row max / row sum need one cross-half exchange.  P = exp2 of
+// the scaled, max-shifted scores is converted in registers and used
+// directly as the B operand of
+//     O^T += V_j^T . P^T       (A = V^T from LDS)
+// whose accumulator again holds one query row per lane, so the online-
+// softmax rescale is a per-lane scalar.  No LDS round trip for P.
+//
+// MFMA shapes: v_mfma_f32_32x32x16_bf16 and v_mfma_i32_32x32x32_i8.  Both
+// operands of one MFMA slot-map the reduction index the same way, so the
+// summation order inside a k-step is free: the V^T staging uses a column
+// order that makes each lane's 8 (bf16) or 16 (int8) reduction values
+// contiguous in LDS and equal to the kv indices its P values carry.
+//
+// Accumulator layout (32x32 tiles): lane l, element r holds row
+// 8*(r/4) + 4*(l/32) + (r%4), column l%32.
+#include "bsa_device.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// row of accumulator element r for lane-half h
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+template <int D, int BQ, int BK, int ESZ>
+struct Geo {
+  static constexpr int NW = BQ / 32;
+  static constexpr int NT = NW * kWave;
+  static constexpr int VEC = 16 / ESZ;               // elements per 16-byte chunk
+  static constexpr int KP = D + VEC;                 // K row pitch (elements)
+  static constexpr int VP = BK + VEC;                // V^T row pitch (elements)
+  static constexpr int CH = BK * D / VEC;            // 16-byte chunks per tile
+  static constexpr int CPT = CH / NT;                // chunks per thread
+  static_assert(CH % NT == 0, "tile must split evenly");
+};
+
+// --- global -> registers for one kv tile (rows past N and invalid tiles read as 0)
+template <int D, int BQ, int BK, int ESZ>
+__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ base, int g, int j, int N,
+                                          bool jvalid, uint4 (&reg)[Geo<D, BQ, BK, ESZ>::CPT]) {
+  using G_ = Geo<D, BQ, BK, ESZ>;
+  constexpr int CPR = D / G_::VEC;  // chunks per row
+#pragma unroll
+  for (int c = 0; c < G_::CPT; c++) {
+    const int chunk = threadIdx.x + c * G_::NT;
+    const int r = chunk / CPR, c0 = (chunk % CPR) * G_::VEC;
+    const int kv = j * BK + r;
+    if (jvalid && kv < N)
+      reg[c] = *reinterpret_cast<const uint4*>(
+          base + ((static_cast<int64_t>(g) * N + kv) * D + c0) * ESZ);
+    else
+      reg[c] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// --- registers -> LDS, K row-major
+template <int D, int BQ, int BK, int ESZ>
+__device__ __forceinline__ void store_k(uint8_t* ks, const uint4 (&reg)[Geo<D, BQ, BK, ESZ>::CPT]) {
+  using G_ = Geo<D, BQ, BK, ESZ>;
+  constexpr int CPR = D / G_::VEC;
+#pragma unroll
+  for (int c = 0; c < G_::CPT; c++) {
+    const int chunk = threadIdx.x + c * G_::NT;
+    const int r = chunk / CPR, c0 = (chunk % CPR) * G_::VEC;
+    *reinterpret_cast<uint4*>(ks + (r * G_::KP + c0) * ESZ) = reg[c];
+  }
+}
+
+// Position of kv index `kv` inside a V^T row.
+//  bf16 (k-step 16): kv = 16s + 8a + 4h + c  ->  16s + 8h + 4a + c
+//  int8 (k-step 32): kv = 32b + 8a + 4h + c  ->  32b + 16h + 4a + c   (a in 0..3)
+template <int ESZ>
+__device__ __forceinline__ int vt_col(int kv) {
+  if constexpr (ESZ == 2) {
+    return (kv & ~12) | ((kv & 4) << 1) | ((kv & 8) >> 1);
+  } else {
+    return (kv & ~31) | (((kv >> 2) & 1) << 4) | (((kv >> 3) & 3) << 2) | (kv & 3);
+  }
+}
+
+// --- registers -> LDS, V transposed with the column order above
+template <int D, int BQ, int BK, int ESZ>
+__device__ __forceinline__ void store_vt(uint8_t* vt, const uint4 (&reg)[Geo<D, BQ, BK, ESZ>::CPT]) {
+  using G_ = Geo<D, BQ, BK, ESZ>;
+  constexpr int CPR = D / G_::VEC;
+#pragma unroll
+  for (int c = 0; c < G_::CPT; c++) {
+    const int chunk = threadIdx.x + c * G_::NT;
+    const int r = chunk / CPR, c0 = (chunk % CPR) * G_::VEC;
+    const int pc = vt_col<ESZ>(r);
+    const uint32_t w[4] = {reg[c].x, reg[c].y, reg[c].z, reg[c].w};
+    if constexpr (ESZ == 2) {
+      uint16_t* v = reinterpret_cast<uint16_t*>(vt);
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        v[(c0 + e) * G_::VP + pc] = static_cast<uint16_t>((w[e / 2] >> (16 * (e % 2))) & 0xffffu);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; e++)
+        vt[(c0 + e) * G_::VP + pc] = static_cast<uint8_t>((w[e / 4] >> (8 * (e % 4))) & 0xffu);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 tile routines
+template <int D, int BQ, int BK>
+__device__ __forceinline__ void qk_tile_bf16(const uint16_t* ks, const bf16x8 (&qf)[D / 16],
+                                             f32x16 (&s)[BK / 32]) {
+  using G_ = Geo<D, BQ, BK, 2>;
+  const int lane = threadIdx.x % kWave, l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < BK / 32; b++) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks_ = 0; ks_ < D / 16; ks_++) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * b + l32) * G_::KP + 16 * ks_ + 8 * h);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks_], acc, 0, 0, 0);
+    }
+    s[b] = acc;
+  }
+}
+
+template <int D, int BQ, int BK>
+__device__ __forceinline__ void pv_tile_bf16(const uint16_t* vt, const bf16x8 (&pb)[BK / 16],
+                                             f32x16 (&o)[D / 32]) {
+  using G_ = Geo<D, BQ, BK, 2>;
+  const int lane = threadIdx.x % kWave, l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; db++) {
+#pragma unroll
+    for (int st = 0; st < BK / 16; st++) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + l32) * G_::VP + 16 * st + 8 * h);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[db], 0, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// int8 tile routines
+template <int D, int BQ, int BK>
+__device__ __forceinline__ void qk_tile_i8(const int8_t* ks, const i32x4 (&qf)[D / 32],
+                                           i32x16 (&s)[BK / 32]) {
+  using G_ = Geo<D, BQ, BK, 1>;
+  const int lane = threadIdx.x % kWave, l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < BK / 32; b++) {
+    i32x16 acc = {};
+#pragma unroll
+    for (int ks_ = 0; ks_ < D / 32; ks_++) {
+      const i32x4 a = *reinterpret_cast<const i32x4*>(ks + (32 * b + l32) * G_::KP + 32 * ks_ + 16 * h);
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[ks_], acc, 0, 0, 0);
+    }
+    s[b] = acc;
+  }
+}
+
+template <int D, int BQ, int BK>
+__device__ __forceinline__ void pv_tile_i8(const int8_t* vt, const i32x4 (&pf)[BK / 32],
+                                           i32x16 (&o)[D / 32]) {
+  using G_ = Geo<D, BQ, BK, 1>;
+  const int lane = threadIdx.x % kWave, l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; db++) {
+    i32x16 acc = {};
+#pragma unroll
+    for (int b = 0; b < BK / 32; b++) {
+      const i32x4 a = *reinterpret_cast<const i32x4*>(vt + (32 * db + l32) * G_::VP + 32 * b + 16 * h);
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[b], acc, 0, 0, 0);
+    }
+    o[db] = acc;
+  }
+}
+
+// Q fragments: lane (row l%32 of the wave's 32 rows, half h) holds the
+// channels of its k-steps that match the B-operand slot order.
+template <int D, int ESZ, int KSTEP, typename VT>
+__device__ __forceinline__ void load_q(const uint8_t* __restrict__ Q, int g, int qrow, int N,
+                                       VT (&qf)[D / KSTEP]) {
+  const int h = (threadIdx.x % kWave) >> 5;
+  const bool ok = qrow < N;
+  const uint8_t* p = Q + (static_cast<int64_t>(g) * N + (ok ? qrow : 0)) * D * ESZ;
+#pragma unroll
+  for (int s = 0; s < D / KSTEP; s++) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) v = *reinterpret_cast<const uint4*>(p + (KSTEP * s + (KSTEP / 2) * h) * ESZ);
+    qf[s] = __builtin_bit_cast(VT, v);
+  }
+}
+
+__device__ __forceinline__ void csr_range(const int32_t* row_ptr, int64_t row, int64_t col_len,
+                                          int64_t& e0, int64_t& e1) {
+  e0 = row_ptr[row];
+  e1 = row_ptr[row + 1];
+  e0 = e0 < 0 ? 0 : (e0 > col_len ? col_len : e0);
+  e1 = e1 < e0 ? e0 : (e1 > col_len ? col_len : e1);
+}
+
+// ---------------------------------------------------------------------------
+template <int D, int BQ, int BK>
+__global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
+    int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
+    float scale_log2) {
+  using G_ = Geo<D, BQ, BK, 2>;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[BK * G_::KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[D * G_::VP];
+
+  const int lid = static_cast<int>(xcd_swizzle(blockIdx.x, gridDim.x));
+  const int g = lid / nq, i = lid % nq;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int qrow = i * BQ + w * 32 + l32;
+
+  bf16x8 qf[D / 16];
+  load_q<D, 2, 16>(reinterpret_cast<const uint8_t*>(Q), g, qrow, N, qf);
+
+  int64_t e0, e1;
+  csr_range(row_ptr, static_cast<int64_t>(g % mask_G) * nq + i, col_len, e0, e1);
+
+  float m = -INFINITY, l = 0.0f;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; db++) o[db] = f32x16{};
+
+  uint4 kr[G_::CPT], vr[G_::CPT];
+  int jn = 0;
+  if (e0 < e1) {
+    jn = col_idx[e0];
+    const bool ok = static_cast<unsigned>(jn) < static_cast<unsigned>(nk);
+    load_tile<D, BQ, BK, 2>(reinterpret_cast<const uint8_t*>(K), g, jn, N, ok, kr);
+    load_tile<D, BQ, BK, 2>(reinterpret_cast<const uint8_t*>(V), g, jn, N, ok, vr);
+  }
+  for (int64_t e = e0; e < e1; e++) {
+    const int j = jn;
+    const bool jvalid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
+    __syncthreads();
+    store_k<D, BQ, BK, 2>(reinterpret_cast<uint8_t*>(ks), kr);
+    store_vt<D, BQ, BK, 2>(reinterpret_cast<uint8_t*>(vt), vr);
+    __syncthreads();
+    if (e + 1 < e1) {
+      jn = col_idx[e + 1];
+      const bool ok = static_cast<unsigned>(jn) < static_cast<unsigned>(nk);
+      load_tile<D, BQ, BK, 2>(reinterpret_cast<const uint8_t*>(K), g, jn, N, ok, kr);
+      load_tile<D, BQ, BK, 2>(reinterpret_cast<const uint8_t*>(V), g, jn, N, ok, vr);
+    }
+
+    f32x16 s[BK / 32];
+    qk_tile_bf16<D, BQ, BK>(ks, qf, s);
+
+    const bool ragged = !jvalid || j * BK + BK > N;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < BK / 32; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float x = s[b][r] * scale_log2;
+        if (ragged && (!jvalid || j * BK + 32 * b + acc_row(r, h) >= N)) x = -INFINITY;
+        s[b][r] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(m, tmax);
+    const float ref = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m - ref);
+    float psum = 0.0f;
+    bf16x8 pb[BK / 16];
+#pragma unroll
+    for (int b = 0; b < BK / 32; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float p = __builtin_amdgcn_exp2f(s[b][r] - ref);
+        psum += p;
+        pb[2 * b + r / 8][r % 8] = static_cast<__bf16>(p);
+      }
+    l = l * alpha + psum;
+    m = mnew;
+#pragma unroll
+    for (int db = 0; db < D / 32; db++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) o[db][r] *= alpha;
+    pv_tile_bf16<D, BQ, BK>(vt, pb, o);
+  }
+
+  l += __shfl_xor(l, 32);
+  if (qrow < N) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    uint16_t* op = O + (static_cast<int64_t>(g) * N + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; db++)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const int d0 = 32 * db + 8 * r4 + 4 * h;
+        uint2 pk;
+        pk.x = f32_to_bf16_bits(o[db][4 * r4 + 0] * inv) | (f32_to_bf16_bits(o[db][4 * r4 + 1] * inv) << 16);
+        pk.y = f32_to_bf16_bits(o[db][4 * r4 + 2] * inv) | (f32_to_bf16_bits(o[db][4 * r4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + d0) = pk;
+      }
+    if (lse != nullptr && h == 0)
+      lse[static_cast<int64_t>(g) * N + qrow] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, int BQ, int BK>
+__global__ __launch_bounds__(BQ * 2) void fwd_i8_kernel(
+    const int8_t* __restrict__ Q, const float* __restrict__ sQ, const int8_t* __restrict__ K,
+    const float* __restrict__ sK, const int8_t* __restrict__ V, const float* __restrict__ sV,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
+    int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
+    float scale_log2) {
+  using G_ = Geo<D, BQ, BK, 1>;
+  __shared__ __attribute__((aligned(16))) int8_t ks[BK * G_::KP];
+  __shared__ __attribute__((aligned(16))) int8_t vt[D * G_::VP];
+  __shared__ float s_red[G_::NW];
+
+  const int lid = static_cast<int>(xcd_swizzle(blockIdx.x, gridDim.x));
+  const int g = lid / nq, i = lid % nq;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int qrow = i * BQ + w * 32 + l32;
+  const bool qvalid = qrow < N;
+
+  i32x4 qf[D / 32];
+  load_q<D, 1, 32>(reinterpret_cast<const uint8_t*>(Q), g, qrow, N, qf);
+  const float sq = sQ[static_cast<int64_t>(g) * nq + i] * scale_log2;
+
+  int64_t e0, e1;
+  csr_range(row_ptr, static_cast<int64_t>(g % mask_G) * nq + i, col_len, e0, e1);
+
+  float m = -INFINITY, l = 0.0f;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; db++) o[db] = f32x16{};
+
+  uint4 kr[G_::CPT], vr[G_::CPT];
+  int jn = 0;
+  if (e0 < e1) {
+    jn = col_idx[e0];
+    const bool ok = static_cast<unsigned>(jn) < static_cast<unsigned>(nk);
+    load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(K), g, jn, N, ok, kr);
+    load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(V), g, jn, N, ok, vr);
+  }
+  for (int64_t e = e0; e < e1; e++) {
+    const int j = jn;
+    const bool jvalid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
+    const float skj = jvalid ? sK[static_cast<int64_t>(g) * nk + j] : 0.0f;
+    const float svj = jvalid ? sV[static_cast<int64_t>(g) * nk + j] : 0.0f;
+    __syncthreads();
+    store_k<D, BQ, BK, 1>(reinterpret_cast<uint8_t*>(ks), kr);
+    store_vt<D, BQ, BK, 1>(reinterpret_cast<uint8_t*>(vt), vr);
+    __syncthreads();
+    if (e + 1 < e1) {
+      jn = col_idx[e + 1];
+      const bool ok = static_cast<unsigned>(jn) < static_cast<unsigned>(nk);
+      load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(K), g, jn, N, ok, kr);
+      load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(V), g, jn, N, ok, vr);
+    }
+
+    i32x16 si[BK / 32];
+    qk_tile_i8<D, BQ, BK>(ks, qf, si);
+
+    const float c = sq * skj;
+    const bool ragged = !jvalid || j * BK + BK > N;
+    float sf[BK / 32][16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < BK / 32; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float x = static_cast<float>(si[b][r]) * c;
+        if (ragged && (!jvalid || j * BK + 32 * b + acc_row(r, h) >= N)) x = -INFINITY;
+        sf[b][r] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(m, tmax);
+    const float ref = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m - ref);
+    float psum = 0.0f, pmax = 0.0f;
+#pragma unroll
+    for (int b = 0; b < BK / 32; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float p = __builtin_amdgcn_exp2f(sf[b][r] - ref);
+        sf[b][r] = p;
+        psum += p;
+        pmax = fmaxf(pmax, p);
+      }
+    l = l * alpha + psum;
+    m = mnew;
+    // per-tile scale of P over the real rows of the whole workgroup
+    pmax = wave_max(qvalid ? pmax : 0.0f);
+    if (lane == 0) s_red[w] = pmax;
+    __syncthreads();
+    float mp = s_red[0];
+#pragma unroll
+    for (int ww = 1; ww < G_::NW; ww++) mp = fmaxf(mp, s_red[ww]);
+    const float qs = mp > 0.0f ? 127.0f / mp : 0.0f;
+    const float cv = (mp / 127.0f) * svj;
+    i32x4 pf[BK / 32];
+#pragma unroll
+    for (int b = 0; b < BK / 32; b++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float y = fminf(rintf(sf[b][4 * q4 + e] * qs), 127.0f);
+          word |= (static_cast<uint32_t>(static_cast<int>(y)) & 0xffu) << (8 * e);
+        }
+        pf[b][q4] = static_cast<int>(word);
+      }
+    i32x16 ov[D / 32];
+    pv_tile_i8<D, BQ, BK>(vt, pf, ov);
+#pragma unroll
+    for (int db = 0; db < D / 32; db++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) o[db][r] = o[db][r] * alpha + static_cast<float>(ov[db][r]) * cv;
+  }
+
+  l += __shfl_xor(l, 32);
+  if (qvalid) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    uint16_t* op = O + (static_cast<int64_t>(g) * N + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; db++)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const int d0 = 32 * db + 8 * r4 + 4 * h;
+        uint2 pk;
+        pk.x = f32_to_bf16_bits(o[db][4 * r4 + 0] * inv) | (f32_to_bf16_bits(o[db][4 * r4 + 1] * inv) << 16);
+        pk.y = f32_to_bf16_bits(o[db][4 * r4 + 2] * inv) | (f32_to_bf16_bits(o[db][4 * r4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + d0) = pk;
+      }
+    if (lse != nullptr && h == 0)
+      lse[static_cast<int64_t>(g) * N + qrow] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Debug entry points: the forward kernel's own int8 tile routines on chosen
+// tiles, writing exact int32 products.
+template <int D, int BQ, int BK>
+__global__ __launch_bounds__(BQ * 2) void dbg_qk_kernel(const int8_t* __restrict__ Q,
+                                                        const int8_t* __restrict__ K, int G, int N,
+                                                        int nq, int nk,
+                                                        const int32_t* __restrict__ gij,
+                                                        int32_t* __restrict__ S) {
+  using G_ = Geo<D, BQ, BK, 1>;
+  __shared__ __attribute__((aligned(16))) int8_t ks[BK * G_::KP];
+  const int t = blockIdx.x;
+  int g = gij[3 * t], i = gij[3 * t + 1];
+  const int j = gij[3 * t + 2];
+  // an out-of-range head or q-block yields an all-zero tile
+  const bool ok = g >= 0 && g < G && i >= 0 && i < nq;
+  if (!ok) { g = 0; i = nq; }
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int qrow = i * BQ + w * 32 + l32;
+  i32x4 qf[D / 32];
+  load_q<D, 1, 32>(reinterpret_cast<const uint8_t*>(Q), g, qrow, N, qf);
+  uint4 kr[G_::CPT];
+  load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(K), g, j, N,
+                          static_cast<unsigned>(j) < static_cast<unsigned>(nk), kr);
+  store_k<D, BQ, BK, 1>(reinterpret_cast<uint8_t*>(ks), kr);
+  __syncthreads();
+  i32x16 si[BK / 32];
+  qk_tile_i8<D, BQ, BK>(ks, qf, si);
+  int32_t* out = S + static_cast<int64_t>(t) * BQ * BK;
+  const int qr = w * 32 + l32;
+#pragma unroll
+  for (int b = 0; b < BK / 32; b++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) out[qr * BK + 32 * b + acc_row(r, h)] = si[b][r];
+}
+
+template <int D, int BQ, int BK>
+__global__ __launch_bounds__(BQ * 2) void dbg_pv_kernel(const int8_t* __restrict__ P8,
+                                                        const int8_t* __restrict__ V, int G, int N,
+                                                        int nk, const int32_t* __restrict__ gj,
+                                                        int32_t* __restrict__ OV) {
+  using G_ = Geo<D, BQ, BK, 1>;
+  __shared__ __attribute__((aligned(16))) int8_t vt[D * G_::VP];
+  const int t = blockIdx.x;
+  int g = gj[2 * t], j = gj[2 * t + 1];
+  // an out-of-range head or kv-block reads as an all-zero V tile
+  if (g < 0 || g >= G) { g = 0; j = -1; }
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int qr = w * 32 + l32;
+  const int8_t* prow = P8 + (static_cast<int64_t>(t) * BQ + qr) * BK;
+  i32x4 pf[BK / 32];
+#pragma unroll
+  for (int b = 0; b < BK / 32; b++)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        word |= (static_cast<uint32_t>(static_cast<uint8_t>(prow[32 * b + acc_row(4 * q4 + e, h)])))
+                << (8 * e);
+      pf[b][q4] = static_cast<int>(word);
+    }
+  uint4 vr[G_::CPT];
+  load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(V), g, j, N,
+                          static_cast<unsigned>(j) < static_cast<unsigned>(nk), vr);
+  store_vt<D, BQ, BK, 1>(reinterpret_cast<uint8_t*>(vt), vr);
+  __syncthreads();
+  i32x16 ov[D / 32];
+  pv_tile_i8<D, BQ, BK>(vt, pf, ov);
+  int32_t* out = OV + static_cast<int64_t>(t) * BQ * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; db++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) out[qr * D + 32 * db + acc_row(r, h)] = ov[db][r];
+}
+
+// ---------------------------------------------------------------------------
+template <template <int, int, int> class Launch, typename... Args>
+hipError_t dispatch(int d, int Bq, int Bk, Args&&... args) {
+  if (d == 128) {
+    if (Bq == 128 && Bk == 64) return Launch<128, 128, 64>::run(args...);
+    if (Bq == 128 && Bk == 128) return Launch<128, 128, 128>::run(args...);
+    if (Bq == 64 && Bk == 64) return Launch<128, 64, 64>::run(args...);
+    if (Bq == 64 && Bk == 128) return Launch<128, 64, 128>::run(args...);
+  } else {
+    if (Bq == 128 && Bk == 64) return Launch<64, 128, 64>::run(args...);
+    if (Bq == 128 && Bk == 128) return Launch<64, 128, 128>::run(args...);
+    if (Bq == 64 && Bk == 64) return Launch<64, 64, 64>::run(args...);
+    if (Bq == 64 && Bk == 128) return Launch<64, 64, 128>::run(args...);
+  }
+  return hipErrorInvalidValue;
+}
+
+float scale_log2_of(const AttnArgs& a) {
+  const float sm = a.sm_scale > 0.0f ? a.sm_scale : 1.0f / sqrtf(static_cast<float>(a.d));
+  return sm * kLog2e;
+}
+
+template <int D, int BQ, int BK>
+struct LaunchBf16 {
+  static hipError_t run(const AttnArgs& a, hipStream_t s) {
+    const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
+    const uint32_t nwg = static_cast<uint32_t>(a.G) * nq;
+    fwd_bf16_kernel<D, BQ, BK><<<nwg, BQ * 2, 0, s>>>(
+        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+        static_cast<const uint16_t*>(a.V), a.row_ptr, a.col_idx, a.col_len, a.mask_G, a.O, a.lse,
+        a.N, nq, nk, scale_log2_of(a));
+    return hipGetLastError();
+  }
+};
+
+template <int D, int BQ, int BK>
+struct LaunchI8 {
+  static hipError_t run(const AttnArgs& a, hipStream_t s) {
+    const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
+    const uint32_t nwg = static_cast<uint32_t>(a.G) * nq;
+    fwd_i8_kernel<D, BQ, BK><<<nwg, BQ * 2, 0, s>>>(
+        static_cast<const int8_t*>(a.Q), a.sQ, static_cast<const int8_t*>(a.K), a.sK,
+        static_cast<const int8_t*>(a.V), a.sV, a.row_ptr, a.col_idx, a.col_len, a.mask_G, a.O,
+        a.lse, a.N, nq, nk, scale_log2_of(a));
+    return hipGetLastError();
+  }
+};
+
+template <int D, int BQ, int BK>
+struct LaunchDbgQk {
+  static hipError_t run(const int8_t* Q, const int8_t* K, int G, int N, const int32_t* gij, int n,
+                        int32_t* S, hipStream_t s) {
+    const int nq = (N + BQ - 1) / BQ, nk = (N + BK - 1) / BK;
+    dbg_qk_kernel<D, BQ, BK><<<n, BQ * 2, 0, s>>>(Q, K, G, N, nq, nk, gij, S);
+    return hipGetLastError();
+  }
+};
+
+template <int D, int BQ, int BK>
+struct LaunchDbgPv {
+  static hipError_t run(const int8_t* P8, const int8_t* V, int G, int N, const int32_t* gj, int n,
+                        int32_t* OV, hipStream_t s) {
+    const int nk = (N + BK - 1) / BK;
+    dbg_pv_kernel<D, BQ, BK><<<n, BQ * 2, 0, s>>>(P8, V, G, N, nk, gj, OV);
+    return hipGetLastError();
+  }
+};
+
+}  // namespace
+
+hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s) {
+  return dispatch<LaunchBf16>(a.d, a.Bq, a.Bk, a, s);
+}
+hipError_t launch_forward_int8(const AttnArgs& a, hipStream_t s) {
+  return dispatch<LaunchI8>(a.d, a.Bq, a.Bk, a, s);
+}
+hipError_t launch_debug_int8_qk(const int8_t* Qq, const int8_t* Kq, int G, int N, int d, int Bq,
+                                int Bk, const int32_t* gij, int n, int32_t* S, hipStream_t s) {
+  return dispatch<LaunchDbgQk>(d, Bq, Bk, Qq, Kq, G, N, gij, n, S, s);
+}
+hipError_t launch_debug_int8_pv(const int8_t* P8, const int8_t* Vq, int G, int N, int d, int Bq,
+                                int Bk, const int32_t* gj, int n, int32_t* OV, hipStream_t s) {
+  return dispatch<LaunchDbgPv>(d, Bq, Bk, P8, Vq, G, N, gj, n, OV, s);
+}
+
+}  // namespace bsa

@@ -1,0 +1,70 @@
+// bsa_device.hpp — small device-side helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, round-robin dispatch
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even; NaN stays quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Natural token index of reordered position p for axis-order code `order`
+// (outermost -> innermost: 0 FHW, 1 FWH, 2 HFW, 3 HWF, 4 WFH, 5 WHF).
+// The innermost coordinate is p mod (its extent), the middle one the next
+// digit, the outermost what remains; natural index = (f*H + h)*W + w.
+__device__ __forceinline__ uint32_t natural_index(int order, uint32_t p, uint32_t F, uint32_t H,
+                                                  uint32_t W) {
+  uint32_t f, h, w;
+  switch (order) {
+    default:
+    case 0: w = p % W; p /= W; h = p % H; f = p / H; break;  // F H W
+    case 1: h = p % H; p /= H; w = p % W; f = p / W; break;  // F W H
+    case 2: w = p % W; p /= W; f = p % F; h = p / F; break;  // H F W
+    case 3: f = p % F; p /= F; w = p % W; h = p / W; break;  // H W F
+    case 4: h = p % H; p /= H; f = p % F; w = p / F; break;  // W F H
+    case 5: f = p % F; p /= F; h = p % H; w = p / H; break;  // W H F
+  }
+  return (f * H + h) * W + w;
+}
+
+// Workgroup id -> logical tile id so that each XCD (which receives every
+// 8th workgroup) owns one contiguous range of logical tiles; neighbouring
+// tiles of one head then share that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_swizzle(uint32_t bid, uint32_t nwg) {
+  const uint32_t q = nwg / kNumXcd, r = nwg % kNumXcd;
+  const uint32_t x = bid % kNumXcd, local = bid / kNumXcd;
+  return x * q + (x < r ? x : r) + local;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T u = __shfl_xor(v, o);
+    v = v > u ? v : u;
+  }
+  return v;
+}
+
+}  // namespace bsa

@@ -1,0 +1,66 @@
+// bsa_internal.hpp — declarations shared between the C-ABI front end
+// (capi.hip) and the kernel translation units.  Launchers assume their
+// arguments were validated by the front end; they only launch and return
+// the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// ---- permute.hip -----------------------------------------------------------
+hipError_t launch_permute(int direction, const void* src, int src_dt, void* dst, int dst_dt,
+                          int64_t stride_g, int64_t stride_n, int G, int F, int H, int W, int d,
+                          const uint8_t* orders, hipStream_t s);
+
+// ---- mask.hip --------------------------------------------------------------
+struct MaskGeom {
+  int G, F, H, W, d;
+  int64_t N;
+  int Bq, Bk;
+  int nq, nk;      // ceil(N/Bq), ceil(N/Bk)
+  int words;       // 64-bit words per bitmask row = ceil(nk/64)
+  int score;
+  int k;           // per-row top-k budget
+  int force_diag;
+  int win_T, win_r0;
+};
+// Workspace carve-up (byte offsets, 256-aligned).
+struct MaskWs {
+  size_t sum_q, sum_k, norm_q, norm_k, counts, bits, total;
+};
+MaskWs mask_workspace_layout(const MaskGeom& m);
+hipError_t launch_build_mask(const MaskGeom& m, const uint16_t* Qp, const uint16_t* Kp,
+                             const uint8_t* orders, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_capacity, int32_t* nnz, char* ws, hipStream_t s);
+
+// ---- quant.hip -------------------------------------------------------------
+hipError_t launch_quantize_int8(const uint16_t* X, int8_t* Xq, float* scale, int G, int N, int d,
+                                int B, hipStream_t s);
+
+// ---- attn.hip --------------------------------------------------------------
+struct AttnArgs {
+  const void* Q;  // bf16 or int8 [G][N][d]
+  const void* K;
+  const void* V;
+  const float* sQ;  // int8 path only
+  const float* sK;
+  const float* sV;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t col_len;
+  int mask_G;
+  uint16_t* O;  // bf16 [G][N][d]
+  float* lse;   // [G][N] or nullptr
+  int G, N, d, Bq, Bk;
+  float sm_scale;
+};
+hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_forward_int8(const AttnArgs& a, hipStream_t s);
+hipError_t launch_debug_int8_qk(const int8_t* Qq, const int8_t* Kq, int G, int N, int d, int Bq,
+                                int Bk, const int32_t* gij, int n, int32_t* S, hipStream_t s);
+hipError_t launch_debug_int8_pv(const int8_t* P8, const int8_t* Vq, int G, int N, int d, int Bq,
+                                int Bk, const int32_t* gj, int n, int32_t* OV, hipStream_t s);
+
+}  // namespace bsa

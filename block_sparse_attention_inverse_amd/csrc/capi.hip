@@ -1,0 +1,264 @@
+// capi.hip — the extern "C" boundary of libbsa.so (declared in bsa.h).
+//
+// Every entry point validates its arguments on the host before any launch,
+// leaves outputs untouched on failure, records a message in a thread-local
+// string, and returns a bsa_status.  No exception crosses the boundary.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/bsa.h"
+#include "bsa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BSA_OK;
+  return fail(BSA_EHIP, "%s: HIP error %d (%s)", what, static_cast<int>(e), hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool block_ok(int b) { return b == 64 || b == 128; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+template <typename F>
+int guarded(F&& f) {
+  try {
+    return f();
+  } catch (...) {
+    return fail(BSA_EHIP, "internal error");
+  }
+}
+
+// Shared validation of bsa_mask_params; fills the geometry.
+int mask_geom(int32_t G, int32_t F, int32_t H, int32_t W, int32_t d, const bsa_mask_params* p,
+              bsa::MaskGeom& m) {
+  if (!p) return fail(BSA_EINVAL, "mask params pointer is NULL");
+  if (G <= 0 || F <= 0 || H <= 0 || W <= 0) return fail(BSA_EINVAL, "G, F, H, W must be positive");
+  const int64_t N = static_cast<int64_t>(F) * H * W;
+  if (N >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "N = F*H*W must be < 2^31");
+  if (!block_ok(p->Bq) || !block_ok(p->Bk)) return fail(BSA_EUNSUPPORTED, "Bq, Bk must be 64 or 128");
+  if (p->score != 0 && p->score != 1) return fail(BSA_EINVAL, "score must be 0 (DOT) or 1 (COSINE)");
+  if (p->rho_den <= 0 || p->rho_num < 0) return fail(BSA_EINVAL, "rho_num >= 0 and rho_den > 0 required");
+  if (p->win_T >= 31) return fail(BSA_EINVAL, "win_T must be < 31");
+  if (p->win_T >= 0 && p->win_r0 < 0) return fail(BSA_EINVAL, "win_r0 must be >= 0");
+  m.G = G; m.F = F; m.H = H; m.W = W; m.d = d; m.N = N;
+  m.Bq = p->Bq; m.Bk = p->Bk;
+  m.nq = static_cast<int>((N + p->Bq - 1) / p->Bq);
+  m.nk = static_cast<int>((N + p->Bk - 1) / p->Bk);
+  if (m.nk > 8192) return fail(BSA_EUNSUPPORTED, "Nkv = %d exceeds 8192", m.nk);
+  m.words = (m.nk + 63) / 64;
+  m.score = p->score;
+  int64_t k = (2ll * p->rho_num * m.nk + p->rho_den) / (2ll * p->rho_den);
+  if (k > m.nk) k = m.nk;
+  if (k < 1) k = 1;
+  m.k = static_cast<int>(k);
+  m.force_diag = p->force_diag != 0;
+  m.win_T = p->win_T < 0 ? -1 : p->win_T;
+  m.win_r0 = p->win_r0;
+  if (static_cast<int64_t>(G) * m.nq >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "too many rows");
+  return BSA_OK;
+}
+
+int64_t capacity_of(const bsa::MaskGeom& m) {
+  int64_t per = m.k;
+  if (m.force_diag) per += (m.Bq + m.Bk - 1) / m.Bk + 1;
+  if (m.win_T >= 0) per = m.nk;
+  if (per > m.nk) per = m.nk;
+  return per * m.G * static_cast<int64_t>(m.nq);
+}
+
+int attn_common(const void* Q, const void* K, const void* V, const int32_t* row_ptr,
+                const int32_t* col_idx, int64_t col_len, int32_t mask_G, void* Op, int32_t G,
+                int32_t N, int32_t d, int32_t Bq, int32_t Bk) {
+  if (!Q || !K || !V || !row_ptr || !Op) return fail(BSA_EINVAL, "NULL tensor pointer");
+  if (col_len < 0 || (col_len > 0 && !col_idx)) return fail(BSA_EINVAL, "bad col_idx / col_len");
+  if (G <= 0 || N <= 0) return fail(BSA_EINVAL, "G and N must be positive");
+  if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  if (!block_ok(Bq) || !block_ok(Bk)) return fail(BSA_EUNSUPPORTED, "Bq, Bk must be 64 or 128");
+  if (mask_G <= 0 || mask_G > G) return fail(BSA_EINVAL, "mask_G must be in [1, G]");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(Op, 16))
+    return fail(BSA_EINVAL, "tensor pointers must be 16-byte aligned");
+  const int64_t nq = (static_cast<int64_t>(N) + Bq - 1) / Bq;
+  if (static_cast<int64_t>(G) * nq >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "grid too large");
+  if (static_cast<int64_t>(G) * N * d >= (1ll << 40)) return fail(BSA_EUNSUPPORTED, "tensor too large");
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bsa_abi_version(void) { return BSA_ABI_VERSION; }
+
+const char* bsa_last_error(void) { return g_err.c_str(); }
+
+int bsa_permute(int32_t direction, const void* src, int32_t src_dt, void* dst, int32_t dst_dt,
+                int64_t nat_stride_g, int64_t nat_stride_n, int32_t G, int32_t F, int32_t H,
+                int32_t W, int32_t d, const uint8_t* axis_order, void* stream) {
+  return guarded([&]() -> int {
+    if (direction != 0 && direction != 1) return fail(BSA_EINVAL, "direction must be 0 or 1");
+    if (!src || !dst || !axis_order) return fail(BSA_EINVAL, "NULL pointer");
+    if ((src_dt != BSA_F32 && src_dt != BSA_BF16) || (dst_dt != BSA_F32 && dst_dt != BSA_BF16))
+      return fail(BSA_EUNSUPPORTED, "permute dtypes must be F32 or BF16");
+    if (G <= 0 || F <= 0 || H <= 0 || W <= 0 || d <= 0) return fail(BSA_EINVAL, "sizes must be positive");
+    if (d % 8 != 0) return fail(BSA_EINVAL, "d must be a multiple of 8");
+    if (G > 65535) return fail(BSA_EUNSUPPORTED, "G must be <= 65535");
+    if (nat_stride_g < 0 || nat_stride_n < 0 || nat_stride_g % 8 || nat_stride_n % 8)
+      return fail(BSA_EINVAL, "natural strides must be non-negative multiples of 8");
+    const int64_t N = static_cast<int64_t>(F) * H * W;
+    if (N >= (1ll << 31) || N * (d / 8) >= (1ll << 31))
+      return fail(BSA_EUNSUPPORTED, "N*d/8 must be < 2^31");
+    if (N * G * d >= (1ll << 40)) return fail(BSA_EUNSUPPORTED, "tensor too large");
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(BSA_EINVAL, "pointers must be 16-byte aligned");
+    return hip_status(bsa::launch_permute(direction, src, src_dt, dst, dst_dt, nat_stride_g,
+                                          nat_stride_n, G, F, H, W, d, axis_order, as_stream(stream)),
+                      "bsa_permute");
+  });
+}
+
+int64_t bsa_mask_capacity(int32_t G, int32_t F, int32_t H, int32_t W, const bsa_mask_params* p_host) {
+  return guarded([&]() -> int64_t {
+    bsa::MaskGeom m{};
+    const int rc = mask_geom(G, F, H, W, 64, p_host, m);
+    if (rc != BSA_OK) return rc;
+    return capacity_of(m);
+  });
+}
+
+int64_t bsa_mask_workspace(int32_t G, int32_t F, int32_t H, int32_t W, int32_t d,
+                           const bsa_mask_params* p_host) {
+  return guarded([&]() -> int64_t {
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    bsa::MaskGeom m{};
+    const int rc = mask_geom(G, F, H, W, d, p_host, m);
+    if (rc != BSA_OK) return rc;
+    return static_cast<int64_t>(bsa::mask_workspace_layout(m).total);
+  });
+}
+
+int bsa_build_mask(const void* Qp, const void* Kp, int32_t dt, int32_t G, int32_t F, int32_t H,
+                   int32_t W, int32_t d, const uint8_t* axis_order, const bsa_mask_params* p_host,
+                   int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* nnz,
+                   void* workspace, int64_t ws_bytes, void* stream) {
+  return guarded([&]() -> int {
+    if (!Qp || !Kp || !axis_order || !row_ptr || !col_idx || !nnz || !workspace)
+      return fail(BSA_EINVAL, "NULL pointer");
+    if (dt != BSA_BF16) return fail(BSA_EUNSUPPORTED, "build_mask takes bf16 Qp/Kp");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    bsa::MaskGeom m{};
+    const int rc = mask_geom(G, F, H, W, d, p_host, m);
+    if (rc != BSA_OK) return rc;
+    const int64_t cap = capacity_of(m);
+    if (cap >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "mask capacity %lld exceeds int32", (long long)cap);
+    if (col_capacity < cap)
+      return fail(BSA_ECAPACITY, "col_capacity %lld < required bound %lld", (long long)col_capacity,
+                  (long long)cap);
+    const int64_t need = static_cast<int64_t>(bsa::mask_workspace_layout(m).total);
+    if (ws_bytes < need)
+      return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
+    if (!aligned(workspace, 256)) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+    if (!aligned(Qp, 16) || !aligned(Kp, 16)) return fail(BSA_EINVAL, "Qp/Kp must be 16-byte aligned");
+    return hip_status(bsa::launch_build_mask(m, static_cast<const uint16_t*>(Qp),
+                                             static_cast<const uint16_t*>(Kp), axis_order, row_ptr,
+                                             col_idx, col_capacity, nnz, static_cast<char*>(workspace),
+                                             as_stream(stream)),
+                      "bsa_build_mask");
+  });
+}
+
+int bsa_quantize_int8(const void* Xp, int8_t* Xq, float* scale, int32_t G, int32_t N, int32_t d,
+                      int32_t B, void* stream) {
+  return guarded([&]() -> int {
+    if (!Xp || !Xq || !scale) return fail(BSA_EINVAL, "NULL pointer");
+    if (G <= 0 || N <= 0 || d <= 0) return fail(BSA_EINVAL, "sizes must be positive");
+    if (!block_ok(B)) return fail(BSA_EUNSUPPORTED, "B must be 64 or 128");
+    if (d % 8 != 0 || d > 128) return fail(BSA_EUNSUPPORTED, "d must be a multiple of 8, <= 128");
+    if (G > 65535) return fail(BSA_EUNSUPPORTED, "G must be <= 65535");
+    if (!aligned(Xp, 16) || !aligned(Xq, 8)) return fail(BSA_EINVAL, "Xp 16-byte, Xq 8-byte alignment required");
+    return hip_status(bsa::launch_quantize_int8(static_cast<const uint16_t*>(Xp), Xq, scale, G, N, d,
+                                                B, as_stream(stream)),
+                      "bsa_quantize_int8");
+  });
+}
+
+int bsa_forward(const void* Qp, const void* Kp, const void* Vp, const int32_t* row_ptr,
+                const int32_t* col_idx, int64_t col_len, int32_t mask_G, void* Op, float* lse,
+                int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk, float sm_scale,
+                void* stream) {
+  return guarded([&]() -> int {
+    const int rc = attn_common(Qp, Kp, Vp, row_ptr, col_idx, col_len, mask_G, Op, G, N, d, Bq, Bk);
+    if (rc != BSA_OK) return rc;
+    if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");
+    bsa::AttnArgs a{};
+    a.Q = Qp; a.K = Kp; a.V = Vp;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.col_len = col_len; a.mask_G = mask_G;
+    a.O = static_cast<uint16_t*>(Op); a.lse = lse;
+    a.G = G; a.N = N; a.d = d; a.Bq = Bq; a.Bk = Bk; a.sm_scale = sm_scale;
+    return hip_status(bsa::launch_forward_bf16(a, as_stream(stream)), "bsa_forward");
+  });
+}
+
+int bsa_forward_int8(const int8_t* Qq, const float* sQ, const int8_t* Kq, const float* sK,
+                     const int8_t* Vq, const float* sV, const int32_t* row_ptr,
+                     const int32_t* col_idx, int64_t col_len, int32_t mask_G, void* Op, float* lse,
+                     int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk, float sm_scale,
+                     void* stream) {
+  return guarded([&]() -> int {
+    const int rc = attn_common(Qq, Kq, Vq, row_ptr, col_idx, col_len, mask_G, Op, G, N, d, Bq, Bk);
+    if (rc != BSA_OK) return rc;
+    if (!sQ || !sK || !sV) return fail(BSA_EINVAL, "NULL scale pointer");
+    if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");
+    bsa::AttnArgs a{};
+    a.Q = Qq; a.K = Kq; a.V = Vq; a.sQ = sQ; a.sK = sK; a.sV = sV;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.col_len = col_len; a.mask_G = mask_G;
+    a.O = static_cast<uint16_t*>(Op); a.lse = lse;
+    a.G = G; a.N = N; a.d = d; a.Bq = Bq; a.Bk = Bk; a.sm_scale = sm_scale;
+    return hip_status(bsa::launch_forward_int8(a, as_stream(stream)), "bsa_forward_int8");
+  });
+}
+
+int bsa_debug_int8_qk(const int8_t* Qq, const int8_t* Kq, int32_t G, int32_t N, int32_t d,
+                      int32_t Bq, int32_t Bk, const int32_t* gij, int32_t n, int32_t* S,
+                      void* stream) {
+  return guarded([&]() -> int {
+    if (!Qq || !Kq || !gij || !S) return fail(BSA_EINVAL, "NULL pointer");
+    if (G <= 0 || N <= 0 || n <= 0) return fail(BSA_EINVAL, "G, N, n must be positive");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    if (!block_ok(Bq) || !block_ok(Bk)) return fail(BSA_EUNSUPPORTED, "Bq, Bk must be 64 or 128");
+    if (!aligned(Qq, 16) || !aligned(Kq, 16)) return fail(BSA_EINVAL, "16-byte alignment required");
+    return hip_status(bsa::launch_debug_int8_qk(Qq, Kq, G, N, d, Bq, Bk, gij, n, S, as_stream(stream)),
+                      "bsa_debug_int8_qk");
+  });
+}
+
+int bsa_debug_int8_pv(const int8_t* P8, const int8_t* Vq, int32_t G, int32_t N, int32_t d,
+                      int32_t Bq, int32_t Bk, const int32_t* gj, int32_t n, int32_t* OV,
+                      void* stream) {
+  return guarded([&]() -> int {
+    if (!P8 || !Vq || !gj || !OV) return fail(BSA_EINVAL, "NULL pointer");
+    if (G <= 0 || N <= 0 || n <= 0) return fail(BSA_EINVAL, "G, N, n must be positive");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    if (!block_ok(Bq) || !block_ok(Bk)) return fail(BSA_EUNSUPPORTED, "Bq, Bk must be 64 or 128");
+    if (!aligned(Vq, 16)) return fail(BSA_EINVAL, "16-byte alignment required");
+    return hip_status(bsa::launch_debug_int8_pv(P8, Vq, G, N, d, Bq, Bk, gj, n, OV, as_stream(stream)),
+                      "bsa_debug_int8_pv");
+  });
+}
+
+}  // extern "C"

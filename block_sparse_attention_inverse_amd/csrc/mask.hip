@@ -1,0 +1,367 @@
+// mask.hip — online block selection: pooled block summaries, block keys,
+// per-row Top-K plus forced blocks, CSR emission.
+//
+// SPADE machine verdict (pith.science, arXiv 2608.03335), key machinery and
+// core discovery: blocks of the reordered Q/K are summarised (mean pooling,
+// the MEAN variant of referee minor comment on §3.1), scored, and each row
+// keeps its Top-K blocks together with a local window.  Compact Attention
+// review (pith.science), "What carries the argument": the window's extent
+// changes with the temporal distance between frames.  PASA review
+// (pith.science, arXiv 2604.12219): top-k per query bounds the cost by the
+// budget k rather than the sequence length.
+//
+// The selection is an integer outcome decided by fp32 keys, so the fp32
+// operation sequence is fixed (no contraction, sequential sums, fmaf chains,
+// correctly rounded divide and square root) and any conforming
+// implementation gets the same CSR bit for bit.
+//
+// Kernels (all on one stream, no host round trip):
+//   pool_kernel    per (head, block, channel) sequential fp32 sums -> means
+//                  (DOT) or sums + norms (COSINE)              [HBM-bound]
+//   select_kernel  one workgroup per (head, q-block): keys in LDS, exact
+//                  k-th-largest by 4-pass radix select, ties by index,
+//                  union with diagonal / window, 64-bit row bitmask + count
+//   scan_kernel    exclusive scan of the row counts -> row_ptr, nnz
+//   emit_kernel    one wave per row: bitmask -> ascending col_idx
+#pragma clang fp contract(off)
+
+#include "bsa_device.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr int kPoolThreads = 256;
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kMaxNk = 8192;
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ float div_rn(float x, float y) { return x / y; }  // correctly rounded build
+__device__ __forceinline__ float sqrt_rn(float x) { return __builtin_sqrtf(x); }
+
+// Ordered-integer image of an fp32 key: larger key <-> larger image, and
+// -0 maps like +0 so that IEEE-equal keys tie.
+__device__ __forceinline__ uint32_t key_order_bits(float k) {
+  uint32_t u = __float_as_uint(k);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// pool_kernel: TPB = D/2 threads per block (2 channels each), BPW blocks per
+// workgroup.  Logical blocks [0, G*nq) are q-blocks, then G*nk kv-blocks.
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(
+    const uint16_t* __restrict__ Qp, const uint16_t* __restrict__ Kp, int G, int N, int Bq,
+    int Bk, int nq, int nk, int score, float* __restrict__ sum_q, float* __restrict__ sum_k,
+    float* __restrict__ norm_q, float* __restrict__ norm_k) {
+  constexpr int TPB = D / 2;
+  constexpr int BPW = kPoolThreads / TPB;
+  __shared__ float sh[BPW][D];
+  const int slot = threadIdx.x / TPB;
+  const int c = 2 * (threadIdx.x % TPB);
+  const int64_t lb = static_cast<int64_t>(blockIdx.x) * BPW + slot;
+  const int64_t nqt = static_cast<int64_t>(G) * nq, total = nqt + static_cast<int64_t>(G) * nk;
+  const bool valid = lb < total;
+  const bool is_q = lb < nqt;
+  int g = 0, b = 0, B = Bq, nb = nq;
+  if (valid) {
+    if (is_q) { g = static_cast<int>(lb / nq); b = static_cast<int>(lb % nq); }
+    else { const int64_t t = lb - nqt; g = static_cast<int>(t / nk); b = static_cast<int>(t % nk); B = Bk; nb = nk; }
+  }
+  const uint16_t* X = is_q ? Qp : Kp;
+  const int r0 = b * B;
+  const int len = valid ? min(B, N - r0) : 0;
+  float a0 = 0.0f, a1 = 0.0f;
+  const uint32_t* src =
+      reinterpret_cast<const uint32_t*>(X + (static_cast<int64_t>(g) * N + r0) * D + c);
+  int r = 0;
+  for (; r + 8 <= len; r += 8) {
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) w[e] = src[(r + e) * (D / 2)];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      a0 = a0 + bf16_bits_to_f32(w[e] & 0xffffu);
+      a1 = a1 + bf16_bits_to_f32(w[e] >> 16);
+    }
+  }
+  for (; r < len; r++) {
+    const uint32_t w = src[r * (D / 2)];
+    a0 = a0 + bf16_bits_to_f32(w & 0xffffu);
+    a1 = a1 + bf16_bits_to_f32(w >> 16);
+  }
+  float* out = is_q ? sum_q : sum_k;
+  if (valid) {
+    float2 o;
+    if (score == 0) {
+      const float fl = static_cast<float>(len);
+      o = make_float2(div_rn(a0, fl), div_rn(a1, fl));
+    } else {
+      o = make_float2(a0, a1);
+    }
+    *reinterpret_cast<float2*>(out + (static_cast<int64_t>(g) * nb + b) * D + c) = o;
+  }
+  if (score == 1) {
+    sh[slot][c] = a0;
+    sh[slot][c + 1] = a1;
+    __syncthreads();
+    if (valid && c == 0) {
+      float acc = 0.0f;
+      for (int e = 0; e < D; e++) acc = __builtin_fmaf(sh[slot][e], sh[slot][e], acc);
+      (is_q ? norm_q : norm_k)[static_cast<int64_t>(g) * nb + b] = sqrt_rn(acc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Natural frame and in-frame offset of a block's centre position.
+__device__ __forceinline__ void block_centre(int order, int b, int B, int N, int F, int H, int W,
+                                             int& frame, int& offs) {
+  const int len = min(B, N - b * B);
+  const uint32_t c = static_cast<uint32_t>(b * B + (len - 1) / 2);
+  const uint32_t n = natural_index(order, c, F, H, W);
+  const uint32_t hw = static_cast<uint32_t>(H) * W;
+  frame = static_cast<int>(n / hw);
+  offs = static_cast<int>(n % hw);
+}
+
+template <int D>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float* __restrict__ sum_q, const float* __restrict__ sum_k,
+    const float* __restrict__ norm_q, const float* __restrict__ norm_k,
+    const uint8_t* __restrict__ orders, int N, int F, int H, int W, int Bq, int Bk, int nq,
+    int nk, int words, int score, int k, int force_diag, int win_T, int win_r0,
+    int32_t* __restrict__ counts, unsigned long long* __restrict__ bits) {
+  __shared__ float a[D];
+  __shared__ uint32_t ukey[kMaxNk];
+  __shared__ int hist[256];
+  __shared__ uint32_t s_prefix, s_mask;
+  __shared__ int s_krem;
+  __shared__ int s_wave[kSelWaves];
+  __shared__ int s_count;
+
+  const int row = blockIdx.x;  // g*nq + i
+  const int g = row / nq, i = row % nq;
+  const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
+
+  const float* aq = sum_q + static_cast<int64_t>(row) * D;
+  for (int c = t; c < D; c += kSelThreads) a[c] = aq[c];
+  if (t == 0) { s_prefix = 0; s_mask = 0; s_krem = k; s_count = 0; }
+  __syncthreads();
+
+  // keys
+  const float nqi = score == 1 ? norm_q[row] : 0.0f;
+  for (int j = t; j < nk; j += kSelThreads) {
+    const float4* bj = reinterpret_cast<const float4*>(sum_k + (static_cast<int64_t>(g) * nk + j) * D);
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int c4 = 0; c4 < D / 4; c4++) {
+      const float4 v = bj[c4];
+      acc = __builtin_fmaf(a[4 * c4 + 0], v.x, acc);
+      acc = __builtin_fmaf(a[4 * c4 + 1], v.y, acc);
+      acc = __builtin_fmaf(a[4 * c4 + 2], v.z, acc);
+      acc = __builtin_fmaf(a[4 * c4 + 3], v.w, acc);
+    }
+    float key = acc;
+    if (score == 1) {
+      const float den = nqi * norm_k[static_cast<int64_t>(g) * nk + j];
+      key = (den == 0.0f) ? 0.0f : div_rn(acc, den);
+    }
+    ukey[j] = key_order_bits(key);
+  }
+
+  // exact k-th largest image by MSB-first radix select (8-bit digits)
+  for (int pass = 0; pass < 4; pass++) {
+    const int shift = 24 - 8 * pass;
+    for (int e = t; e < 256; e += kSelThreads) hist[e] = 0;
+    __syncthreads();
+    const uint32_t pre = s_prefix, msk = s_mask;
+    for (int j = t; j < nk; j += kSelThreads) {
+      const uint32_t u = ukey[j];
+      if ((u & msk) == pre) atomicAdd(&hist[(u >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (t == 0) {
+      int krem = s_krem, cum = 0, dg = 255;
+      for (; dg > 0; dg--) {
+        if (cum + hist[dg] >= krem) break;
+        cum += hist[dg];
+      }
+      s_krem = krem - cum;
+      s_prefix = pre | (static_cast<uint32_t>(dg) << shift);
+      s_mask = msk | (255u << shift);
+    }
+    __syncthreads();
+  }
+  const uint32_t T = s_prefix;
+  const int take_eq = s_krem;  // how many keys equal to T are kept (lowest indices first)
+
+  // q-block geometry for the forced sets
+  const int q0 = i * Bq, q1 = min(q0 + Bq, N);
+  const int order = orders[g];
+  int fi = 0, oi = 0;
+  if (win_T >= 0) block_centre(order, i, Bq, N, F, H, W, fi, oi);
+
+  int eq_carry = 0, my_count = 0;
+  const int chunks = (nk + kSelThreads - 1) / kSelThreads;
+  for (int ch = 0; ch < chunks; ch++) {
+    const int j = ch * kSelThreads + t;
+    const bool inr = j < nk;
+    const uint32_t u = inr ? ukey[j] : 0u;
+    const bool eq = inr && u == T;
+    // rank of this element among the equal ones, in ascending index order
+    const unsigned long long eb = __ballot(eq);
+    const int below = __popcll(eb & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wave[wv] = __popcll(eb);
+    __syncthreads();
+    int before = eq_carry;
+    for (int w = 0; w < wv; w++) before += s_wave[w];
+    int chunk_total = 0;
+    for (int w = 0; w < kSelWaves; w++) chunk_total += s_wave[w];
+    bool keep = inr && (u > T || (eq && before + below < take_eq));
+    if (inr && force_diag) {
+      const int k0 = j * Bk, k1 = min(k0 + Bk, N);
+      keep = keep || (k0 < q1 && q0 < k1);
+    }
+    if (inr && win_T >= 0 && !keep) {
+      int fj, oj;
+      block_centre(order, j, Bk, N, F, H, W, fj, oj);
+      const int df = abs(fi - fj), dox = abs(oi - oj);
+      keep = df <= win_T && static_cast<int64_t>(dox) <= ((static_cast<int64_t>(win_r0) * W) >> df);
+    }
+    const unsigned long long kb = __ballot(keep);
+    const int word = (ch * kSelThreads + wv * kWave) / 64;
+    if (lane == 0 && word < words) {
+      bits[static_cast<int64_t>(row) * words + word] = kb;
+      my_count += __popcll(kb);
+    }
+    eq_carry += chunk_total;
+    __syncthreads();  // s_wave reuse
+  }
+  if (lane == 0) atomicAdd(&s_count, my_count);
+  __syncthreads();
+  if (t == 0) counts[row] = s_count;
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ counts,
+                                                            int R, int32_t* __restrict__ row_ptr,
+                                                            int32_t* __restrict__ nnz) {
+  __shared__ int s_w[kScanThreads / kWave];
+  __shared__ int s_carry;
+  const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
+  if (t == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < R; base += kScanThreads) {
+    const int idx = base + t;
+    const int v = idx < R ? counts[idx] : 0;
+    int x = v;  // inclusive wave scan
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) s_w[wv] = x;
+    __syncthreads();
+    int wbase = 0, tot = 0;
+    for (int w = 0; w < kScanThreads / kWave; w++) {
+      if (w < wv) wbase += s_w[w];
+      tot += s_w[w];
+    }
+    const int carry = s_carry;
+    if (idx < R) row_ptr[idx] = carry + wbase + x - v;
+    __syncthreads();
+    if (t == 0) s_carry = carry + tot;
+    __syncthreads();
+  }
+  if (t == 0) {
+    row_ptr[R] = s_carry;
+    nnz[0] = s_carry;
+  }
+}
+
+// one wave per row, 4 rows per workgroup
+__global__ __launch_bounds__(256) void emit_kernel(const unsigned long long* __restrict__ bits,
+                                                   const int32_t* __restrict__ row_ptr, int R,
+                                                   int words, int32_t* __restrict__ col_idx,
+                                                   int64_t cap) {
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (row >= R) return;
+  int64_t pos = row_ptr[row];
+  for (int w0 = 0; w0 < words; w0 += kWave) {
+    const int w = w0 + lane;
+    const unsigned long long b = w < words ? bits[static_cast<int64_t>(row) * words + w] : 0ull;
+    const int c = __popcll(b);
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    int64_t p = pos + (x - c);
+    unsigned long long m = b;
+    while (m) {
+      const int bit = __builtin_ctzll(m);
+      m &= m - 1ull;
+      if (p < cap) col_idx[p] = w * 64 + bit;
+      p++;
+    }
+    pos += __shfl(x, kWave - 1);
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+MaskWs mask_workspace_layout(const MaskGeom& m) {
+  MaskWs w{};
+  size_t off = 0;
+  const size_t R = static_cast<size_t>(m.G) * m.nq;
+  w.sum_q = off; off = align256(off + sizeof(float) * R * m.d);
+  w.sum_k = off; off = align256(off + sizeof(float) * static_cast<size_t>(m.G) * m.nk * m.d);
+  w.norm_q = off; off = align256(off + sizeof(float) * R);
+  w.norm_k = off; off = align256(off + sizeof(float) * static_cast<size_t>(m.G) * m.nk);
+  w.counts = off; off = align256(off + sizeof(int32_t) * R);
+  w.bits = off; off = align256(off + sizeof(unsigned long long) * R * m.words);
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_build_mask(const MaskGeom& m, const uint16_t* Qp, const uint16_t* Kp,
+                             const uint8_t* orders, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_capacity, int32_t* nnz, char* ws, hipStream_t s) {
+  const MaskWs L = mask_workspace_layout(m);
+  float* sum_q = reinterpret_cast<float*>(ws + L.sum_q);
+  float* sum_k = reinterpret_cast<float*>(ws + L.sum_k);
+  float* norm_q = reinterpret_cast<float*>(ws + L.norm_q);
+  float* norm_k = reinterpret_cast<float*>(ws + L.norm_k);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  auto* bits = reinterpret_cast<unsigned long long*>(ws + L.bits);
+  const int N = static_cast<int>(m.N);
+  const int R = m.G * m.nq;
+  const int64_t total_blocks = static_cast<int64_t>(m.G) * (m.nq + m.nk);
+  if (m.d == 128) {
+    const int bpw = kPoolThreads / 64;
+    pool_kernel<128><<<static_cast<uint32_t>((total_blocks + bpw - 1) / bpw), kPoolThreads, 0, s>>>(
+        Qp, Kp, m.G, N, m.Bq, m.Bk, m.nq, m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
+    select_kernel<128><<<R, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F, m.H,
+                                                 m.W, m.Bq, m.Bk, m.nq, m.nk, m.words, m.score,
+                                                 m.k, m.force_diag, m.win_T, m.win_r0, counts, bits);
+  } else {
+    const int bpw = kPoolThreads / 32;
+    pool_kernel<64><<<static_cast<uint32_t>((total_blocks + bpw - 1) / bpw), kPoolThreads, 0, s>>>(
+        Qp, Kp, m.G, N, m.Bq, m.Bk, m.nq, m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
+    select_kernel<64><<<R, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F, m.H,
+                                                m.W, m.Bq, m.Bk, m.nq, m.nk, m.words, m.score, m.k,
+                                                m.force_diag, m.win_T, m.win_r0, counts, bits);
+  }
+  scan_kernel<<<1, kScanThreads, 0, s>>>(counts, R, row_ptr, nnz);
+  emit_kernel<<<(R + 3) / 4, 256, 0, s>>>(bits, row_ptr, R, m.words, col_idx, col_capacity);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

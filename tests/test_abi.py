@@ -1,0 +1,109 @@
+"""The C ABI library: it loads, exports every entry point the header
+declares (and no undeclared bsa_* symbol), and its host-side checks answer
+without touching a GPU.  No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(bsa_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_sparse_attention_inverse_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_attention_inverse_amd import build
+
+        build.build()
+    return _lib.load()
+
+
+def test_header_lists_the_entry_points():
+    names = header_functions()
+    for n in ("bsa_permute", "bsa_build_mask", "bsa_forward", "bsa_forward_int8",
+              "bsa_quantize_int8", "bsa_mask_capacity", "bsa_mask_workspace",
+              "bsa_debug_int8_qk", "bsa_debug_int8_pv", "bsa_abi_version", "bsa_last_error"):
+        assert n in names
+
+
+def test_exports_match_header(lib):
+    from block_sparse_attention_inverse_amd import _lib
+
+    names = header_functions()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_lib.SIGNATURES) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if re.search(r" T bsa_", l)})
+    assert exported == names
+
+
+def test_version_and_error_text(lib):
+    assert lib.bsa_abi_version() == 1
+    assert lib.bsa_last_error() in (b"", None) or isinstance(lib.bsa_last_error(), bytes)
+
+
+def test_mask_capacity_and_workspace_host_only(lib):
+    from block_sparse_attention_inverse_amd._lib import MaskParams
+
+    p = MaskParams(128, 64, 0, 30, 100, 1, -1, 0)
+    cap = lib.bsa_mask_capacity(40, 21, 45, 80, ctypes.byref(p))
+    nq, nk = -(-75600 // 128), -(-75600 // 64)
+    assert cap == 40 * nq * (355 + 3)
+    ws = lib.bsa_mask_workspace(40, 21, 45, 80, 128, ctypes.byref(p))
+    assert ws >= 4 * 40 * (nq + nk) * 128
+    pw = MaskParams(128, 128, 1, 15, 100, 1, 2, 4)
+    assert lib.bsa_mask_capacity(24, 33, 45, 80, ctypes.byref(pw)) == 24 * 929 * 929
+    bad = MaskParams(96, 64, 0, 30, 100, 1, -1, 0)
+    assert lib.bsa_mask_capacity(1, 4, 8, 8, ctypes.byref(bad)) == -2
+    assert b"64 or 128" in lib.bsa_last_error()
+    bad2 = MaskParams(64, 64, 0, 30, 0, 1, -1, 0)
+    assert lib.bsa_mask_capacity(1, 4, 8, 8, ctypes.byref(bad2)) == -1
+    assert lib.bsa_mask_capacity(1, 4, 8, 8, None) == -1
+
+
+def test_argument_errors_before_any_launch(lib):
+    """Rejected calls return an error code and a message; none reaches HIP."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    # NULL tensors
+    assert lib.bsa_forward(None, None, None, None, None, 0, 1, None, None, 1, 64, 128, 128, 64,
+                           0.0, None) == -1
+    # unsupported head dim
+    assert lib.bsa_forward(fake, fake, fake, fake, fake, 10, 1, fake, None, 1, 64, 96, 128, 64,
+                           0.0, None) == -2
+    assert b"d must be 64 or 128" in lib.bsa_last_error()
+    # misaligned pointer
+    assert lib.bsa_forward(P(0x1001), fake, fake, fake, fake, 10, 1, fake, None, 1, 64, 128, 128,
+                           64, 0.0, None) == -1
+    # bad mask_G
+    assert lib.bsa_forward(fake, fake, fake, fake, fake, 10, 3, fake, None, 2, 64, 128, 128, 64,
+                           0.0, None) == -1
+    # permute: bad direction, bad d, bad dtype
+    assert lib.bsa_permute(2, fake, 1, fake, 1, 8, 8, 1, 1, 1, 8, 8, fake, None) == -1
+    assert lib.bsa_permute(0, fake, 1, fake, 1, 8, 8, 1, 1, 1, 8, 12, fake, None) == -1
+    assert lib.bsa_permute(0, fake, 2, fake, 1, 8, 8, 1, 1, 1, 8, 8, fake, None) == -2
+    # quantize: bad block
+    assert lib.bsa_quantize_int8(fake, fake, fake, 1, 64, 64, 32, None) == -2
+    # build_mask: capacity too small
+    from block_sparse_attention_inverse_amd._lib import MaskParams
+
+    p = MaskParams(64, 64, 0, 30, 100, 1, -1, 0)
+    assert lib.bsa_build_mask(fake, fake, 1, 1, 4, 8, 8, 64, fake, ctypes.byref(p), fake, fake, 1,
+                              fake, P(0x1000), 1 << 20, None) == -3
+    assert b"col_capacity" in lib.bsa_last_error()
+    assert lib.bsa_build_mask(fake, fake, 0, 1, 4, 8, 8, 64, fake, ctypes.byref(p), fake, fake,
+                              1 << 20, fake, P(0x1000), 1 << 20, None) == -2
