@@ -1,0 +1,263 @@
+"""Benchmark of the block-sparse video attention path on one MI355X.
+
+One step = one pass of the bf16 layer chain over one synthetic batch:
+reorder Q, K, V -> build the block mask (pooled DOT scores, per-row top-k,
+diagonal) -> bf16 block-sparse flash attention -> inverse reorder of O.
+The INT8 chain (reorder -> mask -> quantise Q, K, V -> INT8 attention ->
+inverse reorder) is timed in the same run, over the same number of steps,
+and reported under "int8".
+
+Workload: the 720p-shaped DiT layer, F=21, H=45, W=80 (75,600 tokens),
+40 heads, d=128, 128x64 blocks, 30% density; inputs resident in HBM.
+
+value = dense-equivalent attention TFLOPS = 4*N^2*d*G / (time per step).
+roofline: the dominant kernel (bf16 attention) against the bf16 MFMA peak,
+achieved = kept-block FLOPs per launch / its mean launch time, measured with
+HIP events on the launch stream inside the timed region.
+cpu_baseline: the CPU oracle on one head's share, extrapolated to the layer.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_INT8_TOPS = 5000.0  # MI355X dense int8 MFMA
+METRIC = "dense-equiv attention TFLOPS + MFMA util at 30% density, 75.6k tokens"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_720p_traffic.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kept_flops(row_ptr, col_idx, G, N, Bq, Bk, d):
+    import numpy as np
+
+    nq = (N + Bq - 1) // Bq
+    counts = np.diff(row_ptr.astype(np.int64))
+    rows_real = np.minimum(Bq, N - np.arange(nq) * Bq)
+    rows_per_entry = np.repeat(np.tile(rows_real, G), counts)
+    cols_real = np.minimum(Bk, N - col_idx.astype(np.int64) * Bk)
+    return 4.0 * d * float(np.sum(rows_per_entry * cols_real))
+
+
+def source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "block_sparse_attention_inverse_amd", "csrc", "attn.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(flops_per_launch):
+    """HBM bytes per launch of the bf16 attention kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("attn_source_sha256_16") != source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, Qn, Kn, Vn, orders, p, budget_s=12.0):
+    """Oracle on head 0 (reorder, mask build, masked attention on sampled
+    rows), extrapolated to the whole layer (all heads, all rows)."""
+    import numpy as np
+
+    import oracle
+    from block_sparse_attention_inverse_amd import synth
+
+    F, H, W, d, N, G = cfg["F"], cfg["H"], cfg["W"], cfg["d"], cfg["N"], cfg["G"]
+    q, k, v = (synth.bf16_bits(x[:, :1, :]) for x in (Qn, Kn, Vn))
+    o1 = orders[:1]
+    t0 = time.perf_counter()
+    qp = oracle.permute(0, q, np.uint16, 1, F, H, W, d, o1)
+    kp = oracle.permute(0, k, np.uint16, 1, F, H, W, d, o1)
+    vp = oracle.permute(0, v, np.uint16, 1, F, H, W, d, o1)
+    rp, ci = oracle.build_mask(qp, kp, F, H, W, o1, p.Bq, p.Bk, p.score, p.rho_num, p.rho_den,
+                               p.force_diag, p.win_T, p.win_r0)
+    t_head = time.perf_counter() - t0
+    r = np.random.Generator(np.random.PCG64(7))
+    probe = np.stack([np.zeros(64, np.int64), r.integers(0, N, 64)], axis=1)
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, 1, F, H, W, d, o1, probe, p.Bq, p.Bk, rp, ci)
+    t_probe = time.perf_counter() - t0
+    nrows = int(max(64, min(N, (budget_s - t_head) / max(t_probe / 64, 1e-6))))
+    rows = np.stack([np.zeros(nrows, np.int64), r.integers(0, N, nrows)], axis=1)
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, 1, F, H, W, d, o1, rows, p.Bq, p.Bk, rp, ci)
+    t_rows = time.perf_counter() - t0
+    t_layer = G * (t_head + t_rows * N / nrows)
+    dense = 4.0 * N * N * d * G
+    return {
+        "value": dense / t_layer / 1e12,
+        "unit": "TFLOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"head 0 of {G}: reorder Q/K/V + mask build ({t_head:.2f} s) and fp64 masked "
+                   f"attention on {nrows} of {N} rows ({t_rows:.2f} s); layer time extrapolated "
+                   f"as {G} x (head + rows*N/{nrows}) = {t_layer:.0f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-int8", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); "
+              "the path shards by head across GPUs and is not run multi-GPU here.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_inverse_amd as bsa
+    from block_sparse_attention_inverse_amd import synth
+
+    cfg = synth.config(4)
+    F, H, W, G, d, N = cfg["F"], cfg["H"], cfg["W"], cfg["G"], cfg["d"], cfg["N"]
+    seed = synth.seed_of(4)
+    orders = synth.make_orders(cfg, seed)
+    log(f"[bench] generating 720p inputs N={N} G={G} d={d}")
+    Q, K, V = synth.cast_inputs(cfg, *synth.make_qkv(cfg, orders, seed, device="cuda"))
+    od = torch.from_numpy(orders).cuda()
+    p = bsa.mask_params(cfg["Bq"], cfg["Bk"], 0, cfg["rho"], True)
+    plan = bsa.LayerPlan(G, F, H, W, d, "cuda", p, int8=not args.no_int8)
+    torch.cuda.synchronize()
+
+    def step_bf16(ev=None):
+        bsa.permute(Q, od, F, H, W, 0, out=plan.Qp)
+        bsa.permute(K, od, F, H, W, 0, out=plan.Kp)
+        bsa.permute(V, od, F, H, W, 0, out=plan.Vp)
+        if ev:
+            ev[0].record()
+        plan.build_mask(od)
+        if ev:
+            ev[1].record()
+        bsa.forward(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk,
+                    out=plan.Op, lse=plan.lse)
+        if ev:
+            ev[2].record()
+        bsa.permute(plan.Op, od, F, H, W, 1, out=plan.O)
+
+    def step_int8(ev=None):
+        bsa.permute(Q, od, F, H, W, 0, out=plan.Qp)
+        bsa.permute(K, od, F, H, W, 0, out=plan.Kp)
+        bsa.permute(V, od, F, H, W, 0, out=plan.Vp)
+        plan.build_mask(od)
+        plan.quantize()
+        if ev:
+            ev[0].record()
+        bsa.forward_int8(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq, plan.sV, plan.row_ptr,
+                         plan.col_idx, p.Bq, p.Bk, out=plan.Op, lse=plan.lse)
+        if ev:
+            ev[1].record()
+        bsa.permute(plan.Op, od, F, H, W, 1, out=plan.O)
+
+    def timed(step, nev, label):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev + 1)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            evs[s][0].record()
+            step(evs[s][1:])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        seg = np.array([[evs[s][k].elapsed_time(evs[s][k + 1]) for k in range(nev)]
+                        for s in range(args.steps)])
+        log(f"[bench] {label}: {wall * 1e3:.3f} ms/step; segments (ms) {seg.mean(axis=0)}")
+        return wall, seg.mean(axis=0)
+
+    log("[bench] bf16 chain")
+    wall, seg = timed(step_bf16, 3, "bf16")
+    rp_h = plan.row_ptr.cpu().numpy()
+    nnz = int(plan.nnz.item())
+    ci_h = plan.col_idx[:nnz].cpu().numpy()
+    nq, nk = -(-N // p.Bq), -(-N // p.Bk)
+    fl_kept = kept_flops(rp_h, ci_h, G, N, p.Bq, p.Bk, d)
+    dense = 4.0 * N * N * d * G
+    t_fwd = seg[2] / 1e3
+    achieved = fl_kept / t_fwd / 1e12
+    traffic = read_traffic(fl_kept)
+    result = {
+        "metric": METRIC,
+        "value": dense / wall / 1e12,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "720p DiT attention layer: F=21,H=45,W=80 (75600 tokens), 40 heads, d=128, "
+                        "128x64 blocks, DOT top-k 30% + diagonal, bf16",
+            "tokens": N, "heads": G, "head_dim": d, "block": [p.Bq, p.Bk],
+            "rho": p.rho_num / p.rho_den,
+            "block_density": nnz / (G * nq * nk),
+            "kept_tflop": fl_kept / 1e12,
+            "dense_tflop": dense / 1e12,
+        },
+        "roofline": {
+            "kernel": "bsa_forward (fwd_bf16_kernel<128,128,64>)",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+        },
+        "breakdown_ms": {
+            "reorder_qkv": float(seg[0]),
+            "build_mask": float(seg[1]),
+            "attention": float(seg[2]),
+            "inverse_reorder_and_gaps": float(wall * 1e3 - seg.sum()),
+        },
+        "kept_tflops_attention": achieved,
+        "dense_equiv_tflops_attention": dense / t_fwd / 1e12,
+    }
+    if not args.no_int8:
+        log("[bench] int8 chain")
+        wall8, seg8 = timed(step_int8, 2, "int8")
+        t8 = seg8[1] / 1e3
+        result["int8"] = {
+            "ms_per_step": wall8 * 1e3,
+            "dense_equiv_tflops": dense / wall8 / 1e12,
+            "attention_ms": float(seg8[1]),
+            "attention_kept_tops": fl_kept / t8 / 1e12,
+            "frac_int8_peak": fl_kept / t8 / 1e12 / PEAK_INT8_TOPS,
+            "frac_bf16_peak": fl_kept / t8 / 1e12 / PEAK_BF16_TFLOPS,
+        }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(cfg, Q, K, V, orders, p)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -112,12 +112,16 @@ def build_mask(Qp, Kp, axis_order, F, H, W, params: MaskParams, workspace=None):
     return row_ptr, col_idx, nnz
 
 
-def quantize_int8(Xp, B):
-    """bsa_quantize_int8: bf16 [G][N][d] -> (int8 [G][N][d], fp32 scales [G][ceil(N/B)])."""
+def quantize_int8(Xp, B, out=None):
+    """bsa_quantize_int8: bf16 [G][N][d] -> (int8 [G][N][d], fp32 scales
+    [G][ceil(N/B)]); ``out`` = (q, scale) reuses preallocated tensors."""
     _dev(Xp)
     G, N, d = Xp.shape
-    q = torch.empty((G, N, d), dtype=torch.int8, device=Xp.device)
-    s = torch.empty((G, (N + B - 1) // B), dtype=torch.float32, device=Xp.device)
+    if out is None:
+        q = torch.empty((G, N, d), dtype=torch.int8, device=Xp.device)
+        s = torch.empty((G, (N + B - 1) // B), dtype=torch.float32, device=Xp.device)
+    else:
+        q, s = out
     check(_lib.load().bsa_quantize_int8(_ptr(Xp), _ptr(q), _ptr(s), G, N, d, B, _stream()))
     return q, s
 
@@ -213,6 +217,12 @@ class LayerPlan:
             self.sK = torch.empty((G, nk), dtype=torch.float32, **e)
             self.sV = torch.empty((G, nk), dtype=torch.float32, **e)
 
+    def quantize(self):
+        p = self.params
+        quantize_int8(self.Qp, p.Bq, out=(self.Qq, self.sQ))
+        quantize_int8(self.Kp, p.Bk, out=(self.Kq, self.sK))
+        quantize_int8(self.Vp, p.Bk, out=(self.Vq, self.sV))
+
     def build_mask(self, axis_order):
         lib = _lib.load()
         p = self.params
@@ -234,11 +244,7 @@ def layer_forward(plan: LayerPlan, Q, K, V, axis_order):
     if plan.dynamic_mask:
         plan.build_mask(axis_order)
     if plan.int8:
-        lib = _lib.load()
-        for x, q, s, B in ((plan.Qp, plan.Qq, plan.sQ, p.Bq), (plan.Kp, plan.Kq, plan.sK, p.Bk),
-                           (plan.Vp, plan.Vq, plan.sV, p.Bk)):
-            check(lib.bsa_quantize_int8(_ptr(x), _ptr(q), _ptr(s), plan.G, plan.N, plan.d, B,
-                                        _stream()))
+        plan.quantize()
         forward_int8(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq, plan.sV, plan.row_ptr,
                      plan.col_idx, p.Bq, p.Bk, out=plan.Op, lse=plan.lse)
     else:
