@@ -13,13 +13,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsa.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["capi.hip", "permute.hip", "mask.hip", "quant.hip", "attn.hip"]
+SOURCES = ["capi.hip", "permute.hip", "mask.hip", "quant.hip", "attn.hip", "attn_bf16.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-Wall",
     # fp32 divide and sqrt correctly rounded (the block-scoring contract)
@@ -51,7 +51,7 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 5) -> str:
+def build(verbose: bool = False, jobs: int = 6) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))

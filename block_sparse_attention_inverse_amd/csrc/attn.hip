@@ -1,4 +1,5 @@
-// attn.hip — block-sparse flash attention forward for gfx950 (bf16 and INT8).
+// attn.hip — INT8 block-sparse flash attention forward for gfx950, and the
+// debug entry points exposing its integer tile routines.
 //
 // SPADE machine verdict (pith.science, arXiv 2608.03335), key machinery: a
 // flash-style block-sparse kernel with online softmax computes only the
@@ -122,40 +123,6 @@ __device__ __forceinline__ void store_vt(uint8_t* vt, const uint4 (&reg)[Geo<D, 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 tile routines
-template <int D, int BQ, int BK>
-__device__ __forceinline__ void qk_tile_bf16(const uint16_t* ks, const bf16x8 (&qf)[D / 16],
-                                             f32x16 (&s)[BK / 32]) {
-  using G_ = Geo<D, BQ, BK, 2>;
-  const int lane = threadIdx.x % kWave, l32 = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int b = 0; b < BK / 32; b++) {
-    f32x16 acc = {};
-#pragma unroll
-    for (int ks_ = 0; ks_ < D / 16; ks_++) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * b + l32) * G_::KP + 16 * ks_ + 8 * h);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks_], acc, 0, 0, 0);
-    }
-    s[b] = acc;
-  }
-}
-
-template <int D, int BQ, int BK>
-__device__ __forceinline__ void pv_tile_bf16(const uint16_t* vt, const bf16x8 (&pb)[BK / 16],
-                                             f32x16 (&o)[D / 32]) {
-  using G_ = Geo<D, BQ, BK, 2>;
-  const int lane = threadIdx.x % kWave, l32 = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int db = 0; db < D / 32; db++) {
-#pragma unroll
-    for (int st = 0; st < BK / 16; st++) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + l32) * G_::VP + 16 * st + 8 * h);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[db], 0, 0, 0);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // int8 tile routines
 template <int D, int BQ, int BK>
 __device__ __forceinline__ void qk_tile_i8(const int8_t* ks, const i32x4 (&qf)[D / 32],
@@ -213,112 +180,6 @@ __device__ __forceinline__ void csr_range(const int32_t* row_ptr, int64_t row, i
   e1 = row_ptr[row + 1];
   e0 = e0 < 0 ? 0 : (e0 > col_len ? col_len : e0);
   e1 = e1 < e0 ? e0 : (e1 > col_len ? col_len : e1);
-}
-
-// ---------------------------------------------------------------------------
-template <int D, int BQ, int BK>
-__global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
-    int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
-    float scale_log2) {
-  using G_ = Geo<D, BQ, BK, 2>;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[BK * G_::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * G_::VP];
-
-  const int lid = static_cast<int>(xcd_swizzle(blockIdx.x, gridDim.x));
-  const int g = lid / nq, i = lid % nq;
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int qrow = i * BQ + w * 32 + l32;
-
-  bf16x8 qf[D / 16];
-  load_q<D, 2, 16>(reinterpret_cast<const uint8_t*>(Q), g, qrow, N, qf);
-
-  int64_t e0, e1;
-  csr_range(row_ptr, static_cast<int64_t>(g % mask_G) * nq + i, col_len, e0, e1);
-
-  float m = -INFINITY, l = 0.0f;
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; db++) o[db] = f32x16{};
-
-  uint4 kr[G_::CPT], vr[G_::CPT];
-  int jn = 0;
-  if (e0 < e1) {
-    jn = col_idx[e0];
-    const bool ok = static_cast<unsigned>(jn) < static_cast<unsigned>(nk);
-    load_tile<D, BQ, BK, 2>(reinterpret_cast<const uint8_t*>(K), g, jn, N, ok, kr);
-    load_tile<D, BQ, BK, 2>(reinterpret_cast<const uint8_t*>(V), g, jn, N, ok, vr);
-  }
-  for (int64_t e = e0; e < e1; e++) {
-    const int j = jn;
-    const bool jvalid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
-    __syncthreads();
-    store_k<D, BQ, BK, 2>(reinterpret_cast<uint8_t*>(ks), kr);
-    store_vt<D, BQ, BK, 2>(reinterpret_cast<uint8_t*>(vt), vr);
-    __syncthreads();
-    if (e + 1 < e1) {
-      jn = col_idx[e + 1];
-      const bool ok = static_cast<unsigned>(jn) < static_cast<unsigned>(nk);
-      load_tile<D, BQ, BK, 2>(reinterpret_cast<const uint8_t*>(K), g, jn, N, ok, kr);
-      load_tile<D, BQ, BK, 2>(reinterpret_cast<const uint8_t*>(V), g, jn, N, ok, vr);
-    }
-
-    f32x16 s[BK / 32];
-    qk_tile_bf16<D, BQ, BK>(ks, qf, s);
-
-    const bool ragged = !jvalid || j * BK + BK > N;
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < BK / 32; b++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        float x = s[b][r] * scale_log2;
-        if (ragged && (!jvalid || j * BK + 32 * b + acc_row(r, h) >= N)) x = -INFINITY;
-        s[b][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    const float ref = mnew == -INFINITY ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - ref);
-    float psum = 0.0f;
-    bf16x8 pb[BK / 16];
-#pragma unroll
-    for (int b = 0; b < BK / 32; b++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const float p = __builtin_amdgcn_exp2f(s[b][r] - ref);
-        psum += p;
-        pb[2 * b + r / 8][r % 8] = static_cast<__bf16>(p);
-      }
-    l = l * alpha + psum;
-    m = mnew;
-#pragma unroll
-    for (int db = 0; db < D / 32; db++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) o[db][r] *= alpha;
-    pv_tile_bf16<D, BQ, BK>(vt, pb, o);
-  }
-
-  l += __shfl_xor(l, 32);
-  if (qrow < N) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    uint16_t* op = O + (static_cast<int64_t>(g) * N + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; db++)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; r4++) {
-        const int d0 = 32 * db + 8 * r4 + 4 * h;
-        uint2 pk;
-        pk.x = f32_to_bf16_bits(o[db][4 * r4 + 0] * inv) | (f32_to_bf16_bits(o[db][4 * r4 + 1] * inv) << 16);
-        pk.y = f32_to_bf16_bits(o[db][4 * r4 + 2] * inv) | (f32_to_bf16_bits(o[db][4 * r4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + d0) = pk;
-      }
-    if (lse != nullptr && h == 0)
-      lse[static_cast<int64_t>(g) * N + qrow] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -559,19 +420,6 @@ float scale_log2_of(const AttnArgs& a) {
 }
 
 template <int D, int BQ, int BK>
-struct LaunchBf16 {
-  static hipError_t run(const AttnArgs& a, hipStream_t s) {
-    const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
-    const uint32_t nwg = static_cast<uint32_t>(a.G) * nq;
-    fwd_bf16_kernel<D, BQ, BK><<<nwg, BQ * 2, 0, s>>>(
-        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
-        static_cast<const uint16_t*>(a.V), a.row_ptr, a.col_idx, a.col_len, a.mask_G, a.O, a.lse,
-        a.N, nq, nk, scale_log2_of(a));
-    return hipGetLastError();
-  }
-};
-
-template <int D, int BQ, int BK>
 struct LaunchI8 {
   static hipError_t run(const AttnArgs& a, hipStream_t s) {
     const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
@@ -606,9 +454,6 @@ struct LaunchDbgPv {
 
 }  // namespace
 
-hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s) {
-  return dispatch<LaunchBf16>(a.d, a.Bq, a.Bk, a, s);
-}
 hipError_t launch_forward_int8(const AttnArgs& a, hipStream_t s) {
   return dispatch<LaunchI8>(a.d, a.Bq, a.Bk, a, s);
 }
