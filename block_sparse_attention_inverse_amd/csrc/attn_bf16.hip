@@ -245,7 +245,7 @@ struct Stage {
 template <int D, int NW, bool ISV, bool SMALLN>
 __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int win, int q,
                                          uint8_t* tile) {
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const uint32_t soff = static_cast<uint32_t>(win * Ly<D, NW>::ROWB + q * NW * 1024);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(tile + (q * NW + w) * 1024), 16,
                                            voff, soff, 0, 0);
@@ -262,44 +262,37 @@ __device__ __forceinline__ void stage_all(__amdgpu_buffer_rsrc_t kr, __amdgpu_bu
   }
 }
 
-// Scheduling description of one steady-state iteration (see step()).
-template <int NA, int NB, int NG, int VB>
-__device__ __forceinline__ void describe_pipeline() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           // first two K operands
-  [&]<int... X>(std::integer_sequence<int, X...>) {
-    ((__builtin_amdgcn_sched_group_barrier(0x100, X + 2 < NA ? 1 : 0, 0),
-      __builtin_amdgcn_sched_group_barrier(0x020, (X + 1) * NG / NA - X * NG / NA, 0),
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0)), ...);
-  }(std::make_integer_sequence<int, NA>{});
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);           // first two V operands
-  [&]<int... X>(std::integer_sequence<int, X...>) {
-    ((__builtin_amdgcn_sched_group_barrier(0x100, X + 2 < NB ? 2 : 0, 0),
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0),
-      __builtin_amdgcn_sched_group_barrier(0x002, VB, 0)), ...);
-  }(std::make_integer_sequence<int, NB>{});
-}
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+// Pins a value's computation to this point of the instruction stream (an
+// empty volatile asm that reads and rewrites it).
+__device__ __forceinline__ void anchor(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void anchor(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
-// One steady-state iteration:
+// One steady-state iteration, in an explicit instruction order:
 //   phase A: S(t+1) = K(t+1).Q^T — 2*(D/16) steps of 2 MFMAs (alternating kv
-//            halves so that four accumulation chains are in flight), the K
-//            operand of step x+2 read during step x, and the global->LDS
-//            loads of K(t+2) and V(t+1) spread over the steps;
-//   phase B: O += P(t).V(t) — 4*(D/32) steps of 2 MFMAs, V operands read two
-//            steps ahead, and the softmax of S(t+1) spread between them.
-// The order is handed to the machine scheduler as a pipeline of groups.
-template <int D, int NW, int BK, bool SMALLN, bool MASK>
+//            halves so that four accumulation chains are in flight); step x
+//            reads the K operand of step x+2 and issues a share of the
+//            global->LDS loads of K(t+2) and V(t+1);
+//   phase B: O += P(t).V(t) — 4*(D/32) steps of 2 MFMAs with the V operands
+//            read two steps ahead; the softmax of S(t+1) is cut into as many
+//            slices, one per step (row maxima in the first two, then the
+//            exponentials, bf16 packing and row sums).
+// A scheduling fence closes every step and each slice's results are pinned
+// inside it, so the compiler cannot regroup the stream.
+template <int D, int NW, bool SMALLN>
 __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
                                      __amdgpu_buffer_rsrc_t vrs, const Stage<D, NW>& sg,
                                      uint32_t kread, uint32_t vread, uint8_t* kb_next,
                                      uint8_t* kb_free, uint8_t* vb_cur, uint8_t* vb_free,
                                      const Tile& Tn, const Tile& Tk,
                                      const bf16x8 (&qf)[2][D / 16], f32x16 (&o)[2][D / 32],
-                                     bf16x8 (&p)[2][4], float (&m)[2], float (&l)[2],
-                                     float (&alpha)[2]) {
+                                     const bf16x8 (&p)[2][4], bf16x8 (&p_nxt)[2][4],
+                                     float (&m)[2], float (&l)[2], float (&alpha)[2]) {
   using L = Ly<D, NW>;
   constexpr int NA = 2 * (D / 16);   // phase A steps
   constexpr int NB = 4 * (D / 32);   // phase B steps
   constexpr int NG = 2 * L::NI;      // global loads per wave
+  constexpr int DB = D / 32;
   const int h = (threadIdx.x & 63) >> 5;
 
   // ---- phase A
@@ -323,13 +316,12 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
     }
     s[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % 3], qf[0][ks], s[0][b], 0, 0, 0);
     s[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % 3], qf[1][ks], s[1][b], 0, 0, 0);
+    fence();
   }
 
-  // ---- phase B
-  bf16x8 pn[2][4];
-  float ref[2], sum[2] = {0.0f, 0.0f};
-  bool upd_any = false;
-  if constexpr (MASK) {
+  // columns outside the sub-tile (ragged tail, invalid block index): -inf.
+  // Only the scores pass through this branch.
+  if (Tn.mask) {
 #pragma unroll
     for (int qb = 0; qb < 2; qb++)
 #pragma unroll
@@ -340,50 +332,69 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
           if (!Tn.valid || kv < Tn.kv0 || kv >= N) s[qb][b][r] = -INFINITY;
         }
   }
-#pragma unroll
-  for (int qb = 0; qb < 2; qb++) {
-    float x = s[qb][0][0];
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) x = fmaxf(x, s[qb][b][r]);
-    const float mt2 = halves_max(x) * c;
-    const bool upd = mt2 > m[qb] + kTau;
-    alpha[qb] = upd ? __builtin_amdgcn_exp2f(m[qb] - mt2) : 1.0f;
-    m[qb] = upd ? mt2 : m[qb];
-    upd_any |= upd;
-    ref[qb] = m[qb] == -INFINITY ? 0.0f : m[qb];
-  }
+
+  // ---- phase B
+  uint32_t pw[2][16];  // P as packed bf16 pairs: pw[qb][4*st + w] = P[qb][st] word w
+  float mt[2], ref[2], sum[2] = {0.0f, 0.0f};
+  bool upd_any = false;
+  bf16x8 va[3];
+  va[0] = v_operand<D, NW>(vb_cur, vread, 0, 0);
+  va[1] = v_operand<D, NW>(vb_cur, vread, 1 / DB, 1 % DB);
   const bf16x2 ones = (bf16x2){static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++)
+  for (int k = 0; k < NB; k++) {
+    if (k + 2 < NB) va[(k + 2) % 3] = v_operand<D, NW>(vb_cur, vread, (k + 2) / DB, (k + 2) % DB);
+    const int st = k / DB, db = k % DB;
+    o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % 3], p[0][st], o[0][db], 0, 0, 0);
+    o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % 3], p[1][st], o[1][db], 0, 0, 0);
+    if (k < 2) {
+      const int qb = k;
+      float x = s[qb][0][0];
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+      for (int b = 0; b < 2; b++)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
+        for (int r = 0; r < 16; r++) x = fmaxf(x, s[qb][b][r]);
+      mt[qb] = halves_max(x);
+      anchor(mt[qb]);
+      if (k == 1) {
+#pragma unroll
+        for (int q2 = 0; q2 < 2; q2++) {
+          const float mt2 = mt[q2] * c;
+          const bool upd = mt2 > m[q2] + kTau;
+          alpha[q2] = upd ? __builtin_amdgcn_exp2f(m[q2] - mt2) : 1.0f;
+          m[q2] = upd ? mt2 : m[q2];
+          upd_any |= upd;
+          ref[q2] = m[q2] == -INFINITY ? 0.0f : m[q2];
+          anchor(ref[q2]);
+        }
+      }
+    } else {
+      // exponentials of score pairs [lo, hi) out of 32
+      const int lo = (k - 2) * 32 / (NB - 2), hi = (k - 1) * 32 / (NB - 2);
+#pragma unroll
+      for (int pp = lo; pp < hi; pp++) {
+        const int qb = pp >> 4, b = (pp >> 3) & 1, r = 2 * (pp & 7);
         const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r], c, -ref[qb]));
         const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r + 1], c, -ref[qb]));
         const bf16x2 pr = (bf16x2){static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
-        pn[qb][2 * b + (r >> 3)][r & 7] = pr[0];
-        pn[qb][2 * b + (r >> 3)][(r & 7) + 1] = pr[1];
         sum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[qb], false);
+        uint32_t wv = __builtin_bit_cast(uint32_t, pr);
+        anchor(wv);
+        pw[qb][(pp & 15)] = wv;  // pair pp&15 of qb: st = (pp&15)/4, word (pp&15)%4
       }
-  bf16x8 va[3];
-  va[0] = v_operand<D, NW>(vb_cur, vread, 0, 0);
-  va[1] = v_operand<D, NW>(vb_cur, vread, 1 / (D / 32), 1 % (D / 32));
-#pragma unroll
-  for (int k = 0; k < NB; k++) {
-    const int st = k / (D / 32), db = k % (D / 32);
-    if (k + 2 < NB) va[(k + 2) % 3] = v_operand<D, NW>(vb_cur, vread, (k + 2) / (D / 32), (k + 2) % (D / 32));
-    o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % 3], p[0][st], o[0][db], 0, 0, 0);
-    o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % 3], p[1][st], o[1][db], 0, 0, 0);
+      anchor(sum[0]);
+      anchor(sum[1]);
+    }
+    fence();
   }
-  describe_pipeline<NA, NB, NG, (MASK ? 440 : 320) / NB>();
 #pragma unroll
   for (int qb = 0; qb < 2; qb++) {
     l[qb] = l[qb] * alpha[qb] + sum[qb];
 #pragma unroll
-    for (int st = 0; st < 4; st++) p[qb][st] = pn[qb][st];
+    for (int st = 0; st < 4; st++)
+      p_nxt[qb][st] = __builtin_bit_cast(bf16x8, (uint32_t __attribute__((ext_vector_type(4)))){
+                                                 pw[qb][4 * st], pw[qb][4 * st + 1],
+                                                 pw[qb][4 * st + 2], pw[qb][4 * st + 3]});
   }
   wait_loads();
   return upd_any;
@@ -403,8 +414,8 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t vb0[L::TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vb1[L::TB];
 
-  const int lid = static_cast<int>(xcd_swizzle(blockIdx.x, gridDim.x));
-  const int g = lid / nq, i = lid % nq;
+  int g, i;
+  if (!head_sync_tile(blockIdx.x, nq, g, i)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int qbase = i * BQ + w * 64;
@@ -470,25 +481,22 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
     }
     bool upd = false;  // O is still zero: nothing to rescale yet
     // tiles t+1 and t+2 are fetched one iteration ahead; pinning them at the
-    // end of the iteration retires the scalar loads outside the LDS phases
+    // end of the iteration retires the scalar loads outside the LDS phases.
     // K(t+2) is always loaded (at t+2 == nt the last tile is reloaded into a
-    // buffer that is not read again), which keeps the iteration branch-free
+    // buffer that is not read again), which keeps the iteration branch-free.
     Tile Tn = tile_of<BK>(col_idx, e0, nt > 1 ? 1 : 0, N, nk);
     Tile Tk = tile_of<BK>(col_idx, e0, nt > 2 ? 2 : nt - 1, N, nk);
     int t = 0;
     for (; t + 1 < nt; t++) {
       if (__ballot(upd) != 0ull) rescale<D>(o, alpha);
       const bool odd = t & 1;
-      uint8_t* kb_next = odd ? kb0 : kb1;
-      uint8_t* kb_free = odd ? kb1 : kb0;
-      uint8_t* vb_cur = odd ? vb1 : vb0;
-      uint8_t* vb_free = odd ? vb0 : vb1;
-      if (Tn.mask)
-        upd = step<D, NW, BK, SMALLN, true>(N, c, krs, vrs, sg, kread, vread, kb_next, kb_free,
-                                            vb_cur, vb_free, Tn, Tk, qf, o, p, m, l, alpha);
-      else
-        upd = step<D, NW, BK, SMALLN, false>(N, c, krs, vrs, sg, kread, vread, kb_next, kb_free,
-                                             vb_cur, vb_free, Tn, Tk, qf, o, p, m, l, alpha);
+      bf16x8 pn[2][4];
+      upd = step<D, NW, SMALLN>(N, c, krs, vrs, sg, kread, vread, odd ? kb0 : kb1, odd ? kb1 : kb0,
+                                odd ? vb1 : vb0, odd ? vb0 : vb1, Tn, Tk, qf, o, p, pn, m, l, alpha);
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+        for (int st = 0; st < 4; st++) p[qb][st] = pn[qb][st];
       Tn = Tk;
       Tk = tile_of<BK>(col_idx, e0, t + 3 < nt ? t + 3 : nt - 1, N, nk);
       asm volatile("" ::"s"(Tk.win), "s"(Tk.kv0), "s"(static_cast<int>(Tk.valid)));
@@ -526,7 +534,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
 template <int D, int BQ, int BK>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
   const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
-  const uint32_t nwg = static_cast<uint32_t>(a.G) * nq;
+  const uint32_t nwg = static_cast<uint32_t>(a.G) * kNumXcd * ((nq + kNumXcd - 1) / kNumXcd);
   const float sm = a.sm_scale > 0.0f ? a.sm_scale : 1.0f / sqrtf(static_cast<float>(a.d));
   auto kern = a.N >= KT ? fwd_bf16_kernel<D, BQ, BK, false> : fwd_bf16_kernel<D, BQ, BK, true>;
   kern<<<nwg, BQ, 0, s>>>(static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),

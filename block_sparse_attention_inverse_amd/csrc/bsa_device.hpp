@@ -57,6 +57,21 @@ __device__ __forceinline__ uint32_t xcd_swizzle(uint32_t bid, uint32_t nwg) {
   return x * q + (x < r ? x : r) + local;
 }
 
+// Head-synchronous tile order for (head, row-block) grids: workgroup `bid`
+// runs on XCD bid % 8 as that XCD's (bid / 8)-th workgroup.  XCD x takes
+// rows [x*per, (x+1)*per) of every head, heads in order, so all XCDs work
+// on the same head at the same time (one head's K/V stays resident in the
+// shared last-level cache) while each XCD's L2 serves neighbouring rows.
+// Grid size must be 8 * per * G with per = ceil(nq / 8); returns false for
+// the padding slots (i >= nq).
+__device__ __forceinline__ bool head_sync_tile(uint32_t bid, int nq, int& g, int& i) {
+  const int per = (nq + kNumXcd - 1) / kNumXcd;
+  const int x = static_cast<int>(bid % kNumXcd), k = static_cast<int>(bid / kNumXcd);
+  g = k / per;
+  i = x * per + k % per;
+  return i < nq;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll
