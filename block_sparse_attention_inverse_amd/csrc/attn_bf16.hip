@@ -52,6 +52,14 @@ constexpr int KT = 64;          // kv rows per sub-tile
 constexpr float kTau = 8.0f;    // lazy-rescale threshold, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+#ifndef BSA_PF_A
+#define BSA_PF_A 2
+#endif
+#ifndef BSA_PF_B
+#define BSA_PF_B 2
+#endif
+constexpr int kPfA = BSA_PF_A;  // LDS operand prefetch distance (MFMA steps), S = K.Q^T
+constexpr int kPfB = BSA_PF_B;  // same for O += P.V
 
 template <int D, int NW>
 struct Ly {
@@ -299,13 +307,14 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
   f32x16 s[2][2];
 #pragma unroll
   for (int b = 0; b < 2; b++) { s[0][b] = f32x16{}; s[1][b] = f32x16{}; }
-  bf16x8 ka[3];
-  ka[0] = k_operand<D, NW>(kb_next, kread, 0, 0);
-  ka[1] = k_operand<D, NW>(kb_next, kread, 1, 0);
+  bf16x8 ka[kPfA + 1];
+#pragma unroll
+  for (int x = 0; x < kPfA; x++) ka[x] = k_operand<D, NW>(kb_next, kread, x & 1, x >> 1);
 #pragma unroll
   for (int x = 0; x < NA; x++) {
     const int b = x & 1, ks = x >> 1;
-    if (x + 2 < NA) ka[(x + 2) % 3] = k_operand<D, NW>(kb_next, kread, (x + 2) & 1, (x + 2) >> 1);
+    if (x + kPfA < NA)
+      ka[(x + kPfA) % (kPfA + 1)] = k_operand<D, NW>(kb_next, kread, (x + kPfA) & 1, (x + kPfA) >> 1);
 #pragma unroll
     for (int gq = x * NG / NA; gq < (x + 1) * NG / NA; gq++) {
       if (gq < L::NI)
@@ -314,8 +323,8 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
         load_one<D, NW, true, SMALLN>(vrs, sg.template lane_off<true, SMALLN>(gq - L::NI, N), Tn.win,
                                       gq - L::NI, vb_free);
     }
-    s[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % 3], qf[0][ks], s[0][b], 0, 0, 0);
-    s[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % 3], qf[1][ks], s[1][b], 0, 0, 0);
+    s[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % (kPfA + 1)], qf[0][ks], s[0][b], 0, 0, 0);
+    s[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % (kPfA + 1)], qf[1][ks], s[1][b], 0, 0, 0);
     fence();
   }
 
@@ -334,19 +343,21 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
   }
 
   // ---- phase B
-  uint32_t pw[2][16];  // P as packed bf16 pairs: pw[qb][4*st + w] = P[qb][st] word w
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 pw[2][4];  // P as packed bf16 pairs: pw[qb][st][w] = words of P[qb][st]
   float mt[2], ref[2], sum[2] = {0.0f, 0.0f};
   bool upd_any = false;
-  bf16x8 va[3];
-  va[0] = v_operand<D, NW>(vb_cur, vread, 0, 0);
-  va[1] = v_operand<D, NW>(vb_cur, vread, 1 / DB, 1 % DB);
+  bf16x8 va[kPfB + 1];
+#pragma unroll
+  for (int k = 0; k < kPfB; k++) va[k] = v_operand<D, NW>(vb_cur, vread, k / DB, k % DB);
   const bf16x2 ones = (bf16x2){static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
   for (int k = 0; k < NB; k++) {
-    if (k + 2 < NB) va[(k + 2) % 3] = v_operand<D, NW>(vb_cur, vread, (k + 2) / DB, (k + 2) % DB);
+    if (k + kPfB < NB)
+      va[(k + kPfB) % (kPfB + 1)] = v_operand<D, NW>(vb_cur, vread, (k + kPfB) / DB, (k + kPfB) % DB);
     const int st = k / DB, db = k % DB;
-    o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % 3], p[0][st], o[0][db], 0, 0, 0);
-    o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % 3], p[1][st], o[1][db], 0, 0, 0);
+    o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % (kPfB + 1)], p[0][st], o[0][db], 0, 0, 0);
+    o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % (kPfB + 1)], p[1][st], o[1][db], 0, 0, 0);
     if (k < 2) {
       const int qb = k;
       float x = s[qb][0][0];
@@ -378,12 +389,10 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
         const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r + 1], c, -ref[qb]));
         const bf16x2 pr = (bf16x2){static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
         sum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[qb], false);
-        uint32_t wv = __builtin_bit_cast(uint32_t, pr);
-        anchor(wv);
-        pw[qb][(pp & 15)] = wv;  // pair pp&15 of qb: st = (pp&15)/4, word (pp&15)%4
+        // pair pp&15 of row half qb is word (pp&3) of P[qb][(pp&15)/4]
+        pw[qb][(pp & 15) >> 2][pp & 3] = __builtin_bit_cast(uint32_t, pr);
+        if ((pp & 3) == 3) asm volatile("" : "+v"(pw[qb][(pp & 15) >> 2]));
       }
-      anchor(sum[0]);
-      anchor(sum[1]);
     }
     fence();
   }
@@ -391,10 +400,7 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
   for (int qb = 0; qb < 2; qb++) {
     l[qb] = l[qb] * alpha[qb] + sum[qb];
 #pragma unroll
-    for (int st = 0; st < 4; st++)
-      p_nxt[qb][st] = __builtin_bit_cast(bf16x8, (uint32_t __attribute__((ext_vector_type(4)))){
-                                                 pw[qb][4 * st], pw[qb][4 * st + 1],
-                                                 pw[qb][4 * st + 2], pw[qb][4 * st + 3]});
+    for (int st = 0; st < 4; st++) p_nxt[qb][st] = __builtin_bit_cast(bf16x8, pw[qb][st]);
   }
   wait_loads();
   return upd_any;
