@@ -47,10 +47,17 @@ def kept_flops(row_ptr, col_idx, G, N, Bq, Bk, d):
     return 4.0 * d * float(np.sum(rows_per_entry * cols_real))
 
 
+ATTN_SOURCES = ("attn_bf16.hip", "bsa_device.hpp")
+COPY_BYTES = 1 << 31  # plain device copy used to calibrate the HBM byte counters
+
+
 def source_hash():
+    """Hash of the bf16 attention kernel's sources: a traffic figure taken on
+    other sources is stale and is not reported."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "block_sparse_attention_inverse_amd", "csrc", "attn.hip"), "rb") as f:
-        h.update(f.read())
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_inverse_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -120,6 +127,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run 3 plain device copies of 2 GiB (reference dispatches for "
+                         "the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); "
@@ -142,6 +152,14 @@ def main():
     p = bsa.mask_params(cfg["Bq"], cfg["Bk"], 0, cfg["rho"], True)
     plan = bsa.LayerPlan(G, F, H, W, d, "cuda", p, int8=not args.no_int8)
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 copies of {COPY_BYTES} bytes")
+        del src, dst
 
     def step_bf16(ev=None):
         bsa.permute(Q, od, F, H, W, 0, out=plan.Qp)

@@ -60,6 +60,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 #endif
 constexpr int kPfA = BSA_PF_A;  // LDS operand prefetch distance (MFMA steps), S = K.Q^T
 constexpr int kPfB = BSA_PF_B;  // same for O += P.V
+#ifndef BSA_LOAD_STEPS
+#define BSA_LOAD_STEPS 0
+#endif
 
 template <int D, int NW>
 struct Ly {
@@ -290,8 +293,9 @@ __device__ __forceinline__ void anchor(uint32_t& x) { asm volatile("" : "+v"(x))
 template <int D, int NW, bool SMALLN>
 __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
                                      __amdgpu_buffer_rsrc_t vrs, const Stage<D, NW>& sg,
-                                     uint32_t kread, uint32_t vread, uint8_t* kb_next,
-                                     uint8_t* kb_free, uint8_t* vb_cur, uint8_t* vb_free,
+                                     uint32_t kread, uint32_t vread, uint8_t* __restrict__ kb_next,
+                                     uint8_t* __restrict__ kb_free, uint8_t* __restrict__ vb_cur,
+                                     uint8_t* __restrict__ vb_free,
                                      const Tile& Tn, const Tile& Tk,
                                      const bf16x8 (&qf)[2][D / 16], f32x16 (&o)[2][D / 32],
                                      const bf16x8 (&p)[2][4], bf16x8 (&p_nxt)[2][4],
@@ -300,6 +304,8 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
   constexpr int NA = 2 * (D / 16);   // phase A steps
   constexpr int NB = 4 * (D / 32);   // phase B steps
   constexpr int NG = 2 * L::NI;      // global loads per wave
+  // the global loads go out over the first NL steps of phase A
+  constexpr int NL = BSA_LOAD_STEPS > 0 && BSA_LOAD_STEPS < NA ? BSA_LOAD_STEPS : NA;
   constexpr int DB = D / 32;
   const int h = (threadIdx.x & 63) >> 5;
 
@@ -316,7 +322,7 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
     if (x + kPfA < NA)
       ka[(x + kPfA) % (kPfA + 1)] = k_operand<D, NW>(kb_next, kread, (x + kPfA) & 1, (x + kPfA) >> 1);
 #pragma unroll
-    for (int gq = x * NG / NA; gq < (x + 1) * NG / NA; gq++) {
+    for (int gq = x * NG / NL; gq < (x + 1) * NG / NL && gq < NG; gq++) {
       if (gq < L::NI)
         load_one<D, NW, false, SMALLN>(krs, sg.template lane_off<false, SMALLN>(gq, N), Tk.win, gq, kb_free);
       else
