@@ -46,10 +46,13 @@ namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int KT = 64;          // kv rows per sub-tile
-constexpr float kTau = 8.0f;    // lazy-rescale threshold, log2 units
+constexpr float kTau = 8.0f;    // lazy-rescale threshold of the first tile, log2 units
+constexpr float kRefInit = -1.0e30f;    // reference before any score: finite, below every score
+constexpr float kSumBound = 65536.0f;   // tile row-half sum that raises the reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 #ifndef BSA_PF_A
@@ -169,7 +172,7 @@ __device__ __forceinline__ bool softmax(f32x16 (&s)[2][2], const Tile& T, int N,
     alpha[qb] = upd ? __builtin_amdgcn_exp2f(m[qb] - mt2) : 1.0f;
     m[qb] = upd ? mt2 : m[qb];
     upd_any |= upd;
-    const float ref = m[qb] == -INFINITY ? 0.0f : m[qb];
+    const float ref = m[qb];
     float sum = 0.0f;
 #pragma unroll
     for (int b = 0; b < 2; b++)
@@ -290,8 +293,22 @@ __device__ __forceinline__ void anchor(uint32_t& x) { asm volatile("" : "+v"(x))
 //            exponentials, bf16 packing and row sums).
 // A scheduling fence closes every step and each slice's results are pinned
 // inside it, so the compiler cannot regroup the stream.
+// exponentials of score pair pp (of 32: row half pp/16, kv half (pp/8)%2,
+// accumulator slots 2(pp%8), +1) against reference m, their sum, and their
+// bf16 pair as word pp%4 of P[pp/16][(pp%16)/4]
+__device__ __forceinline__ void exp_pair(const f32x16 (&s)[2][2], float c, const float (&m)[2],
+                                         int pp, float (&sum)[2], u32x4 (&pw)[2][4]) {
+  const int qb = pp >> 4, b = (pp >> 3) & 1, r = 2 * (pp & 7);
+  const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r], c, -m[qb]));
+  const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r + 1], c, -m[qb]));
+  sum[qb] = (sum[qb] + x0) + x1;
+  pw[qb][(pp & 15) >> 2][pp & 3] =
+      __builtin_bit_cast(uint32_t, (bf16x2){static_cast<__bf16>(x0), static_cast<__bf16>(x1)});
+  if ((pp & 3) == 3) asm volatile("" : "+v"(pw[qb][(pp & 15) >> 2]));
+}
+
 template <int D, int NW, bool SMALLN>
-__device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
+__device__ __forceinline__ uint64_t step(int N, float c, __amdgpu_buffer_rsrc_t krs,
                                      __amdgpu_buffer_rsrc_t vrs, const Stage<D, NW>& sg,
                                      uint32_t kread, uint32_t vread, uint8_t* __restrict__ kb_next,
                                      uint8_t* __restrict__ kb_free, uint8_t* __restrict__ vb_cur,
@@ -349,14 +366,11 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
   }
 
   // ---- phase B
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   u32x4 pw[2][4];  // P as packed bf16 pairs: pw[qb][st][w] = words of P[qb][st]
-  float mt[2], ref[2], sum[2] = {0.0f, 0.0f};
-  bool upd_any = false;
+  float sum[2] = {0.0f, 0.0f};
   bf16x8 va[kPfB + 1];
 #pragma unroll
   for (int k = 0; k < kPfB; k++) va[k] = v_operand<D, NW>(vb_cur, vread, k / DB, k % DB);
-  const bf16x2 ones = (bf16x2){static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
   for (int k = 0; k < NB; k++) {
     if (k + kPfB < NB)
@@ -364,52 +378,41 @@ __device__ __forceinline__ bool step(int N, float c, __amdgpu_buffer_rsrc_t krs,
     const int st = k / DB, db = k % DB;
     o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % (kPfB + 1)], p[0][st], o[0][db], 0, 0, 0);
     o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % (kPfB + 1)], p[1][st], o[1][db], 0, 0, 0);
-    if (k < 2) {
-      const int qb = k;
+    // exponentials of score pairs [lo, hi) out of 32 against the running reference
+#pragma unroll
+    for (int pp = k * 32 / NB; pp < (k + 1) * 32 / NB; pp++) exp_pair(s, c, m, pp, sum, pw);
+    fence();
+  }
+  // A tile row-half sum past the bound means scores rose well above the
+  // reference: redo this tile's exponentials against its exact row maximum
+  // (and rescale O before the next product).  Rare after the first tiles.
+  const uint64_t upd = __ballot(!(sum[0] <= kSumBound && sum[1] <= kSumBound));
+  if (upd != 0ull) {
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
       float x = s[qb][0][0];
 #pragma unroll
       for (int b = 0; b < 2; b++)
 #pragma unroll
         for (int r = 0; r < 16; r++) x = fmaxf(x, s[qb][b][r]);
-      mt[qb] = halves_max(x);
-      anchor(mt[qb]);
-      if (k == 1) {
+      const float mn = fmaxf(m[qb], halves_max(x) * c);
+      alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mn);
+      m[qb] = mn;
+      sum[qb] = 0.0f;
 #pragma unroll
-        for (int q2 = 0; q2 < 2; q2++) {
-          const float mt2 = mt[q2] * c;
-          const bool upd = mt2 > m[q2] + kTau;
-          alpha[q2] = upd ? __builtin_amdgcn_exp2f(m[q2] - mt2) : 1.0f;
-          m[q2] = upd ? mt2 : m[q2];
-          upd_any |= upd;
-          ref[q2] = m[q2] == -INFINITY ? 0.0f : m[q2];
-          anchor(ref[q2]);
-        }
-      }
-    } else {
-      // exponentials of score pairs [lo, hi) out of 32
-      const int lo = (k - 2) * 32 / (NB - 2), hi = (k - 1) * 32 / (NB - 2);
-#pragma unroll
-      for (int pp = lo; pp < hi; pp++) {
-        const int qb = pp >> 4, b = (pp >> 3) & 1, r = 2 * (pp & 7);
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r], c, -ref[qb]));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r + 1], c, -ref[qb]));
-        const bf16x2 pr = (bf16x2){static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
-        sum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[qb], false);
-        // pair pp&15 of row half qb is word (pp&3) of P[qb][(pp&15)/4]
-        pw[qb][(pp & 15) >> 2][pp & 3] = __builtin_bit_cast(uint32_t, pr);
-        if ((pp & 3) == 3) asm volatile("" : "+v"(pw[qb][(pp & 15) >> 2]));
-      }
+      for (int pp = 16 * qb; pp < 16 * qb + 16; pp++) exp_pair(s, c, m, pp, sum, pw);
+      l[qb] = l[qb] * alpha[qb] + sum[qb];
     }
-    fence();
+  } else {
+    l[0] += sum[0];
+    l[1] += sum[1];
   }
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++) {
-    l[qb] = l[qb] * alpha[qb] + sum[qb];
+  for (int qb = 0; qb < 2; qb++)
 #pragma unroll
     for (int st = 0; st < 4; st++) p_nxt[qb][st] = __builtin_bit_cast(bf16x8, pw[qb][st]);
-  }
   wait_loads();
-  return upd_any;
+  return upd;
 }
 
 template <int D, int BQ, int BK, bool SMALLN>
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(V + static_cast<int64_t>(g) * N * D), 0, head_bytes, 0x00020000);
 
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f}, alpha[2] = {1.0f, 1.0f};
+  float m[2] = {kRefInit, kRefInit}, l[2] = {0.0f, 0.0f}, alpha[2] = {1.0f, 1.0f};
   f32x16 o[2][D / 32];
 #pragma unroll
   for (int qb = 0; qb < 2; qb++)
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
       else softmax<false>(s, T0, N, c, m, l, p, alpha);
       __syncthreads();
     }
-    bool upd = false;  // O is still zero: nothing to rescale yet
+    uint64_t upd = 0;  // O is still zero: nothing to rescale yet
     // tiles t+1 and t+2 are fetched one iteration ahead; pinning them at the
     // end of the iteration retires the scalar loads outside the LDS phases.
     // K(t+2) is always loaded (at t+2 == nt the last tile is reloaded into a
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
     Tile Tk = tile_of<BK>(col_idx, e0, nt > 2 ? 2 : nt - 1, N, nk);
     int t = 0;
     for (; t + 1 < nt; t++) {
-      if (__ballot(upd) != 0ull) rescale<D>(o, alpha);
+      if (upd != 0ull) rescale<D>(o, alpha);
       const bool odd = t & 1;
       bf16x8 pn[2][4];
       upd = step<D, NW, SMALLN>(N, c, krs, vrs, sg, kread, vread, odd ? kb0 : kb1, odd ? kb1 : kb0,
@@ -514,7 +517,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
       asm volatile("" ::"s"(Tk.win), "s"(Tk.kv0), "s"(static_cast<int>(Tk.valid)));
       __syncthreads();
     }
-    if (__ballot(upd) != 0ull) rescale<D>(o, alpha);
+    if (upd != 0ull) rescale<D>(o, alpha);
     pv<D, NW>((t & 1) ? vb1 : vb0, vread, p, o);
   }
 
