@@ -29,6 +29,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# per-source extra flags.  The bf16 attention kernel takes no NaN inputs into
+# account (a NaN in Q, K or V gives unspecified output), which lets its row
+# maxima fuse into v_max3 without quieting every operand first.
+EXTRA_FLAGS = {"attn_bf16.hip": ["-fno-honor-nans"]}
+
+
 def _hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
         if cand and (os.path.sep not in cand or os.path.exists(cand)):
@@ -38,7 +44,7 @@ def _hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -9,392 +9,481 @@
 // INT8 variant runs Q.K^T in INT8 and quantises the post-softmax map to
 // INT8, with quantisation blocks equal to the attention blocks.
 //
-// Work split: one workgroup per (head g, q-block i) of Bq rows; Bq/32 waves,
-// each owning 32 query rows.  The workgroup walks the CSR row of its
-// q-block; for each kept kv-block j it stages K_j (row-major) and V_j
-// (transposed) in LDS, then every wave computes
-//     S^T = K_j . Q^T          (32x32 MFMA tiles, A = K from LDS, B = Q regs)
-// so that the accumulator holds one query row per lane (the two wave halves
-// share a row); row max / row sum need one cross-half exchange.  P = exp2 of
-// the scaled, max-shifted scores is converted in registers and used
-// directly as the B operand of
-//     O^T += V_j^T . P^T       (A = V^T from LDS)
-// whose accumulator again holds one query row per lane, so the online-
-// softmax rescale is a per-lane scalar.  No LDS round trip for P.
+// Per kept tile (q-block i, kv-block j), in CSR order, for every row r:
+//   I   = q8 . k8 (exact int32),  x = I * sQ_i * sK_j * sm_scale * log2(e)
+//   m'  = max(m, max_c x),  Pt = 2^(x - m'),  l = l * 2^(m - m') + sum_c Pt
+//   mP  = max of Pt over the tile's real rows and columns (whole workgroup)
+//   P8  = rint(Pt * 127 / mP) in [0, 127]
+//   acc = acc * 2^(m - m') + (mP / 127) * sV_j * (P8 . v8) (exact int32)
+// and O = acc / l, LSE = (m + log2 l) * ln 2.
 //
-// MFMA shapes: v_mfma_f32_32x32x16_bf16 and v_mfma_i32_32x32x32_i8.  Both
-// operands of one MFMA slot-map the reduction index the same way, so the
-// summation order inside a k-step is free: the V^T staging uses a column
-// order that makes each lane's 8 (bf16) or 16 (int8) reduction values
-// contiguous in LDS and equal to the kv indices its P values carry.
-//
-// Accumulator layout (32x32 tiles): lane l, element r holds row
-// 8*(r/4) + 4*(l/32) + (r%4), column l%32.
+// Work split: one workgroup per (head g, q-block i); Bq/64 waves, each owning
+// 64 query rows as two 32-row halves, so every K and V operand read from LDS
+// feeds two v_mfma_i32_32x32x32_i8.  A tile is one kv-block (the
+// quantisation unit of P).
+//   S^T = K . Q^T     A = K rows from LDS (ds_read_b128), B = Q fragments in
+//                     registers; the accumulator gives every lane one query
+//                     row (the two wave halves share a row): lane half h, slot
+//                     s of a 32-column group holds kv 8(s/4) + 4h + s%4.
+//   O^T += V^T . P8^T A = V^T read by ds_read_b64_tr_b8 (a 16-lane group
+//                     reads an 8-row x 16-column byte block and hands every
+//                     lane its column's 8 rows), B = P8 packed in registers.
+//                     V rows are permuted within each 32-row block on their
+//                     way into LDS so that the two transposed reads of a lane
+//                     half return exactly the kv indices its P8 slots carry.
+// K and V move global -> LDS with 16-byte buffer loads that write LDS
+// directly; chunk c of LDS row r sits at c ^ ((r / (16/CH)) mod CH) (CH
+// chunks per row), which keeps the K and V operand reads conflict-free.  Rows
+// past N read as zero through the buffer range check; their columns are
+// masked.  K is triple- and V double-buffered so one barrier per tile covers
+// both the staging hand-off and the workgroup-wide maximum of Pt.
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
 
 namespace bsa {
 namespace {
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2_127 = 6.988684686772166f;
+constexpr float kRefInit = -1.0e30f;  // running maximum before any score: finite, below all
 
-// row of accumulator element r for lane-half h
+// accumulator row of element r for lane half h (32x32 MFMA tiles)
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-template <int D, int BQ, int BK, int ESZ>
-struct Geo {
-  static constexpr int NW = BQ / 32;
-  static constexpr int NT = NW * kWave;
-  static constexpr int VEC = 16 / ESZ;               // elements per 16-byte chunk
-  static constexpr int KP = D + VEC;                 // K row pitch (elements)
-  static constexpr int VP = BK + VEC;                // V^T row pitch (elements)
-  static constexpr int CH = BK * D / VEC;            // 16-byte chunks per tile
-  static constexpr int CPT = CH / NT;                // chunks per thread
-  static_assert(CH % NT == 0, "tile must split evenly");
+template <int D, int BK, int NW>
+struct L8 {
+  static constexpr int ROWB = D;                 // bytes per K / V row
+  static constexpr int CH = D / 16;              // 16-byte chunks per row
+  static constexpr int SROW = 16 / CH;           // rows per 256-byte bank line
+  static constexpr int TB = BK * D;              // bytes per tile
+  static constexpr int NI = TB / 1024 / NW;      // 1 KB staging loads per wave per tile
+  // staging lane offsets repeat every P loads (32 rows: the V row permutation)
+  static constexpr int P0 = 32 * ROWB / (NW * 1024);
+  static constexpr int P = P0 < 1 ? 1 : (P0 > NI ? NI : P0);
+  static_assert(NI >= 1, "tile too small for the staging loads");
+  // stage one tile (kv rows kv0 .. kv0+BK) of K or V (one head: base, nrec
+  // bytes; rows past the end read as zero) into LDS; offs: the matching lane
+  // offsets (Stage8::k or Stage8::v)
+  static __device__ __forceinline__ void stage(const int8_t* base, int nrec, const uint32_t* offs,
+                                               int kv0, uint8_t* tile) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), 0, nrec, 0x00020000);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int q = 0; q < NI; q++) {
+      const uint32_t soff = static_cast<uint32_t>(kv0 * ROWB + (q / P) * P * NW * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(tile + (q * NW + w) * 1024),
+                                               16, offs[q % P], soff, 0, 0);
+    }
+  }
 };
 
-// --- global -> registers for one kv tile (rows past N and invalid tiles read as 0)
-template <int D, int BQ, int BK, int ESZ>
-__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ base, int g, int j, int N,
-                                          bool jvalid, uint4 (&reg)[Geo<D, BQ, BK, ESZ>::CPT]) {
-  using G_ = Geo<D, BQ, BK, ESZ>;
-  constexpr int CPR = D / G_::VEC;  // chunks per row
-#pragma unroll
-  for (int c = 0; c < G_::CPT; c++) {
-    const int chunk = threadIdx.x + c * G_::NT;
-    const int r = chunk / CPR, c0 = (chunk % CPR) * G_::VEC;
-    const int kv = j * BK + r;
-    if (jvalid && kv < N)
-      reg[c] = *reinterpret_cast<const uint4*>(
-          base + ((static_cast<int64_t>(g) * N + kv) * D + c0) * ESZ);
-    else
-      reg[c] = make_uint4(0u, 0u, 0u, 0u);
-  }
+// chunk swizzle of LDS row r
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return (r / (16 / (D / 16))) % (D / 16);
 }
 
-// --- registers -> LDS, K row-major
-template <int D, int BQ, int BK, int ESZ>
-__device__ __forceinline__ void store_k(uint8_t* ks, const uint4 (&reg)[Geo<D, BQ, BK, ESZ>::CPT]) {
-  using G_ = Geo<D, BQ, BK, ESZ>;
-  constexpr int CPR = D / G_::VEC;
-#pragma unroll
-  for (int c = 0; c < G_::CPT; c++) {
-    const int chunk = threadIdx.x + c * G_::NT;
-    const int r = chunk / CPR, c0 = (chunk % CPR) * G_::VEC;
-    *reinterpret_cast<uint4*>(ks + (r * G_::KP + c0) * ESZ) = reg[c];
-  }
+// LDS row p of a V tile holds kv row sigma(p): within each 32-row block,
+// LDS rows 8q..8q+7 hold kv {0-3, 8-11} + 16(q%2) + 4(q/2).
+__device__ __forceinline__ int sigma(int p) {
+  const int q = (p >> 3) & 3, e = p & 7;
+  return (p & ~31) | (16 * (q & 1) + 4 * (q >> 1) + 8 * (e >> 2) + (e & 3));
 }
 
-// Position of kv index `kv` inside a V^T row.
-//  bf16 (k-step 16): kv = 16s + 8a + 4h + c  ->  16s + 8h + 4a + c
-//  int8 (k-step 32): kv = 32b + 8a + 4h + c  ->  32b + 16h + 4a + c   (a in 0..3)
-template <int ESZ>
-__device__ __forceinline__ int vt_col(int kv) {
-  if constexpr (ESZ == 2) {
-    return (kv & ~12) | ((kv & 4) << 1) | ((kv & 8) >> 1);
-  } else {
-    return (kv & ~31) | (((kv >> 2) & 1) << 4) | (((kv >> 3) & 3) << 2) | (kv & 3);
-  }
-}
-
-// --- registers -> LDS, V transposed with the column order above
-template <int D, int BQ, int BK, int ESZ>
-__device__ __forceinline__ void store_vt(uint8_t* vt, const uint4 (&reg)[Geo<D, BQ, BK, ESZ>::CPT]) {
-  using G_ = Geo<D, BQ, BK, ESZ>;
-  constexpr int CPR = D / G_::VEC;
+// Lane offsets of the staging loads: load q of wave w writes LDS bytes
+// [(q*NW + w)*1024, +1024), lane l the 16 bytes at +16l: LDS row p, physical
+// chunk x, which hold logical chunk x ^ swz(p) of source row p (K) or
+// sigma(p) (V).  Offsets repeat every P loads up to a shift of P*NW*1024.
+template <int D, int BK, int NW>
+struct Stage8 {
+  using L = L8<D, BK, NW>;
+  uint32_t k[L::P], v[L::P];
+  __device__ __forceinline__ void init() {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int c = 0; c < G_::CPT; c++) {
-    const int chunk = threadIdx.x + c * G_::NT;
-    const int r = chunk / CPR, c0 = (chunk % CPR) * G_::VEC;
-    const int pc = vt_col<ESZ>(r);
-    const uint32_t w[4] = {reg[c].x, reg[c].y, reg[c].z, reg[c].w};
-    if constexpr (ESZ == 2) {
-      uint16_t* v = reinterpret_cast<uint16_t*>(vt);
-#pragma unroll
-      for (int e = 0; e < 8; e++)
-        v[(c0 + e) * G_::VP + pc] = static_cast<uint16_t>((w[e / 2] >> (16 * (e % 2))) & 0xffffu);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; e++)
-        vt[(c0 + e) * G_::VP + pc] = static_cast<uint8_t>((w[e / 4] >> (8 * (e % 4))) & 0xffu);
+    for (int q = 0; q < L::P; q++) {
+      const int o = (q * NW + w) * 1024 + 16 * lane;
+      const int p = o / L::ROWB, x = (o % L::ROWB) / 16;
+      const int c = x ^ swz<D>(p);
+      k[q] = static_cast<uint32_t>(p * L::ROWB + 16 * c);
+      v[q] = static_cast<uint32_t>(sigma(p) * L::ROWB + 16 * c);
     }
   }
+};
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS read offsets of this lane's operands
+template <int D>
+__device__ __forceinline__ uint32_t k_read_off() {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+  return static_cast<uint32_t>(l32 * D + ((h ^ swz<D>(l32)) << 4));
+}
+template <int D>
+__device__ __forceinline__ uint32_t v_read_off() {
+  const int lane = threadIdx.x & 63, li = lane & 15, grp = lane >> 4, h = lane >> 5;
+  const int row = 16 * h + (li >> 1);
+  return static_cast<uint32_t>(row * D + (((grp & 1) ^ swz<D>(row)) << 4) + (li & 1) * 8);
 }
 
-// ---------------------------------------------------------------------------
-// int8 tile routines
-template <int D, int BQ, int BK>
-__device__ __forceinline__ void qk_tile_i8(const int8_t* ks, const i32x4 (&qf)[D / 32],
-                                           i32x16 (&s)[BK / 32]) {
-  using G_ = Geo<D, BQ, BK, 1>;
-  const int lane = threadIdx.x % kWave, l32 = lane & 31, h = lane >> 5;
+// S^T = K . Q^T for the wave's two row halves: s[qb][b] covers kv 32b..32b+31
+template <int D, int BK>
+__device__ __forceinline__ void qk_i8(const uint8_t* kt, uint32_t kread,
+                                      const i32x4 (&qf)[2][D / 32], i32x16 (&s)[2][BK / 32]) {
 #pragma unroll
-  for (int b = 0; b < BK / 32; b++) {
-    i32x16 acc = {};
+  for (int b = 0; b < BK / 32; b++) { s[0][b] = i32x16{}; s[1][b] = i32x16{}; }
 #pragma unroll
-    for (int ks_ = 0; ks_ < D / 32; ks_++) {
-      const i32x4 a = *reinterpret_cast<const i32x4*>(ks + (32 * b + l32) * G_::KP + 32 * ks_ + 16 * h);
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[ks_], acc, 0, 0, 0);
-    }
-    s[b] = acc;
-  }
-}
-
-template <int D, int BQ, int BK>
-__device__ __forceinline__ void pv_tile_i8(const int8_t* vt, const i32x4 (&pf)[BK / 32],
-                                           i32x16 (&o)[D / 32]) {
-  using G_ = Geo<D, BQ, BK, 1>;
-  const int lane = threadIdx.x % kWave, l32 = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int db = 0; db < D / 32; db++) {
-    i32x16 acc = {};
+  for (int ks = 0; ks < D / 32; ks++)
 #pragma unroll
     for (int b = 0; b < BK / 32; b++) {
-      const i32x4 a = *reinterpret_cast<const i32x4*>(vt + (32 * db + l32) * G_::VP + 32 * b + 16 * h);
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[b], acc, 0, 0, 0);
+      const i32x4 a = *reinterpret_cast<const i32x4*>(kt + b * 32 * D + (kread ^ (ks << 5)));
+      s[0][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[0][ks], s[0][b], 0, 0, 0);
+      s[1][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[1][ks], s[1][b], 0, 0, 0);
     }
-    o[db] = acc;
-  }
 }
 
-// Q fragments: lane (row l%32 of the wave's 32 rows, half h) holds the
-// channels of its k-steps that match the B-operand slot order.
-template <int D, int ESZ, int KSTEP, typename VT>
-__device__ __forceinline__ void load_q(const uint8_t* __restrict__ Q, int g, int qrow, int N,
-                                       VT (&qf)[D / KSTEP]) {
-  const int h = (threadIdx.x % kWave) >> 5;
-  const bool ok = qrow < N;
-  const uint8_t* p = Q + (static_cast<int64_t>(g) * N + (ok ? qrow : 0)) * D * ESZ;
+// One channel block of O^T (int32, this tile only) = V^T . P8^T for both row
+// halves: ov0 / ov1 cover channels 32db..32db+31 of halves 0 / 1
+template <int D, int BK>
+__device__ __forceinline__ void pv_block(const uint8_t* vt, uint32_t vread, const i32x4 (&pf)[2][BK / 32],
+                                         int db, i32x16& ov0, i32x16& ov1) {
+  const uint32_t vhi = (vread ^ ((D / 32) << 4)) + 8 * D;  // rows +8: the swizzle flips CH/2
+  ov0 = i32x16{};
+  ov1 = i32x16{};
 #pragma unroll
-  for (int s = 0; s < D / KSTEP; s++) {
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (ok) v = *reinterpret_cast<const uint4*>(p + (KSTEP * s + (KSTEP / 2) * h) * ESZ);
-    qf[s] = __builtin_bit_cast(VT, v);
+  for (int b = 0; b < BK / 32; b++) {
+    const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (LDS_AS i32x2*)(vt + b * 32 * D + (vread ^ (db << 5))));
+    const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (LDS_AS i32x2*)(vt + b * 32 * D + (vhi ^ (db << 5))));
+    const i32x4 a = (i32x4){lo[0], lo[1], hi[0], hi[1]};
+    ov0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[0][b], ov0, 0, 0, 0);
+    ov1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[1][b], ov1, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void csr_range(const int32_t* row_ptr, int64_t row, int64_t col_len,
-                                          int64_t& e0, int64_t& e1) {
-  e0 = row_ptr[row];
-  e1 = row_ptr[row + 1];
-  e0 = e0 < 0 ? 0 : (e0 > col_len ? col_len : e0);
-  e1 = e1 < e0 ? e0 : (e1 > col_len ? col_len : e1);
+// Q fragments of the wave's rows qbase + 32qb + l32: k-step ks holds channels
+// 32ks + 16h .. +15 (rows past N read as zero)
+template <int D>
+__device__ __forceinline__ void load_q(const int8_t* __restrict__ Q, int g, int qbase, int N,
+                                       i32x4 (&qf)[2][D / 32]) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    const int row = qbase + 32 * qb + l32;
+    const bool ok = row < N;
+    const int8_t* p = Q + (static_cast<int64_t>(g) * N + (ok ? row : 0)) * D + 16 * h;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ks++) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) v = *reinterpret_cast<const uint4*>(p + 32 * ks);
+      qf[qb][ks] = __builtin_bit_cast(i32x4, v);
+    }
+  }
 }
 
-// ---------------------------------------------------------------------------
+// max over the lanes that carry real rows; both lane halves of a row agree
+__device__ __forceinline__ float rows_max(float x) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
 template <int D, int BQ, int BK>
-__global__ __launch_bounds__(BQ * 2) void fwd_i8_kernel(
+__global__ __launch_bounds__(BQ) void fwd_i8_kernel(
     const int8_t* __restrict__ Q, const float* __restrict__ sQ, const int8_t* __restrict__ K,
     const float* __restrict__ sK, const int8_t* __restrict__ V, const float* __restrict__ sV,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
     int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
     float scale_log2) {
-  using G_ = Geo<D, BQ, BK, 1>;
-  __shared__ __attribute__((aligned(16))) int8_t ks[BK * G_::KP];
-  __shared__ __attribute__((aligned(16))) int8_t vt[D * G_::VP];
-  __shared__ float s_red[G_::NW];
+  constexpr int NW = BQ / 64;
+  constexpr int NB = BK / 32;
+  using L = L8<D, BK, NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[3][L::TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][L::TB];
+  __shared__ float tile_max[2][NW];
 
-  const int lid = static_cast<int>(xcd_swizzle(blockIdx.x, gridDim.x));
-  const int g = lid / nq, i = lid % nq;
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  int g, i;
+  if (!head_sync_tile(blockIdx.x, nq, g, i)) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int qrow = i * BQ + w * 32 + l32;
-  const bool qvalid = qrow < N;
+  const int qbase = i * BQ + w * 64;
 
-  i32x4 qf[D / 32];
-  load_q<D, 1, 32>(reinterpret_cast<const uint8_t*>(Q), g, qrow, N, qf);
+  Stage8<D, BK, NW> sg;
+  sg.init();
+  const uint32_t kread = k_read_off<D>(), vread = v_read_off<D>();
+
+  i32x4 qf[2][D / 32];
+  load_q<D>(Q, g, qbase, N, qf);
   const float sq = sQ[static_cast<int64_t>(g) * nq + i] * scale_log2;
 
-  int64_t e0, e1;
-  csr_range(row_ptr, static_cast<int64_t>(g % mask_G) * nq + i, col_len, e0, e1);
+  int64_t e0 = row_ptr[static_cast<int64_t>(g % mask_G) * nq + i];
+  int64_t e1 = row_ptr[static_cast<int64_t>(g % mask_G) * nq + i + 1];
+  e0 = e0 < 0 ? 0 : (e0 > col_len ? col_len : e0);
+  e1 = e1 < e0 ? e0 : (e1 > col_len ? col_len : e1);
+  const int nt = static_cast<int>(e1 - e0);
 
-  float m = -INFINITY, l = 0.0f;
-  f32x16 o[D / 32];
+  const int head_bytes = N * L::ROWB;
+  const int8_t* kh = K + static_cast<int64_t>(g) * N * D;
+  const int8_t* vh = V + static_cast<int64_t>(g) * N * D;
+  auto kv0_of = [&](int t) {
+    const int j = col_idx[e0 + t];
+    return static_cast<unsigned>(j) < static_cast<unsigned>(nk) ? j * BK : 0;
+  };
+
+  float m[2] = {kRefInit, kRefInit}, l[2] = {0.0f, 0.0f};
+  f32x16 o[2][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; db++) o[db] = f32x16{};
+  for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+    for (int db = 0; db < D / 32; db++) o[qb][db] = f32x16{};
 
-  uint4 kr[G_::CPT], vr[G_::CPT];
-  int jn = 0;
-  if (e0 < e1) {
-    jn = col_idx[e0];
-    const bool ok = static_cast<unsigned>(jn) < static_cast<unsigned>(nk);
-    load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(K), g, jn, N, ok, kr);
-    load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(V), g, jn, N, ok, vr);
-  }
-  for (int64_t e = e0; e < e1; e++) {
-    const int j = jn;
-    const bool jvalid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
-    const float skj = jvalid ? sK[static_cast<int64_t>(g) * nk + j] : 0.0f;
-    const float svj = jvalid ? sV[static_cast<int64_t>(g) * nk + j] : 0.0f;
+  if (nt > 0) {
+    // prologue: K(0), K(1), V(0)
+    L::stage(kh, head_bytes, sg.k, kv0_of(0), kbuf[0]);
+    if (nt > 1) L::stage(kh, head_bytes, sg.k, kv0_of(1), kbuf[1]);
+    L::stage(vh, head_bytes, sg.v, kv0_of(0), vbuf[0]);
+    wait_loads();
     __syncthreads();
-    store_k<D, BQ, BK, 1>(reinterpret_cast<uint8_t*>(ks), kr);
-    store_vt<D, BQ, BK, 1>(reinterpret_cast<uint8_t*>(vt), vr);
-    __syncthreads();
-    if (e + 1 < e1) {
-      jn = col_idx[e + 1];
-      const bool ok = static_cast<unsigned>(jn) < static_cast<unsigned>(nk);
-      load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(K), g, jn, N, ok, kr);
-      load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(V), g, jn, N, ok, vr);
+    for (int t = 0; t < nt; t++) {
+      const int j = col_idx[e0 + t];
+      const bool jvalid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
+      const int kv0 = jvalid ? j * BK : 0;
+      const bool masked = !jvalid || kv0 + BK > N;
+      const float f = jvalid ? sq * sK[static_cast<int64_t>(g) * nk + j] : 0.0f;
+      const float svj = jvalid ? sV[static_cast<int64_t>(g) * nk + j] : 0.0f;
+
+      // ---- scores and the exact running maximum of every row
+      i32x16 s[2][NB];
+      qk_i8<D, BK>(kbuf[t % 3], kread, qf, s);
+      float x_max[2];
+      if (!masked) {
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++) {
+          int im = s[qb][0][0];
+#pragma unroll
+          for (int b = 0; b < NB; b++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) im = im > s[qb][b][r] ? im : s[qb][b][r];
+          const auto sw = __builtin_amdgcn_permlane32_swap(im, im, false, false);
+          im = static_cast<int>(sw[0]) > static_cast<int>(sw[1]) ? static_cast<int>(sw[0])
+                                                                 : static_cast<int>(sw[1]);
+          x_max[qb] = static_cast<float>(im) * f;
+        }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++) {
+          float xm = -INFINITY;
+#pragma unroll
+          for (int b = 0; b < NB; b++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const int kv = kv0 + 32 * b + acc_row(r, h);
+              if (jvalid && kv < N) xm = fmaxf(xm, static_cast<float>(s[qb][b][r]) * f);
+            }
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(xm), __float_as_uint(xm),
+                                                           false, false);
+          x_max[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+      }
+      float alpha[2], dmax = -INFINITY;
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++) {
+        const float mn = fmaxf(m[qb], x_max[qb]);
+        alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mn);
+        m[qb] = mn;
+        // largest log2 Pt of this row in the tile (real rows only)
+        if (qbase + 32 * qb + l32 < N) dmax = fmaxf(dmax, x_max[qb] - mn);
+      }
+      dmax = rows_max(dmax);
+      if (lane == 0) tile_max[t & 1][w] = dmax;
+
+      // ---- hand-off: this tile's V and the next K are in LDS, the tile
+      // maximum of every wave is visible
+      wait_loads();
+      __syncthreads();
+      if (t + 2 < nt) L::stage(kh, head_bytes, sg.k, kv0_of(t + 2), kbuf[(t + 2) % 3]);
+      if (t + 1 < nt) L::stage(vh, head_bytes, sg.v, kv0_of(t + 1), vbuf[(t + 1) & 1]);
+      float dm = tile_max[t & 1][0];
+#pragma unroll
+      for (int ww = 1; ww < NW; ww++) dm = fmaxf(dm, tile_max[t & 1][ww]);
+
+      // ---- P8 = rint(Pt * 127 / mP), mP = 2^dm; l sums Pt = y * mP / 127
+      const bool any = dm > -INFINITY;
+      const float mp127 = any ? __builtin_amdgcn_exp2f(dm - kLog2_127) : 0.0f;  // mP / 127
+      i32x4 pf[2][NB];
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++) {
+        const float off = any ? m[qb] + dm - kLog2_127 : 0.0f;
+        float ys = 0.0f;
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; q4++) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              const int r = 4 * q4 + e;
+              float y = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[qb][b][r]), f, -off));
+              if (masked) {
+                const int kv = kv0 + 32 * b + acc_row(r, h);
+                if (!jvalid || kv >= N) y = 0.0f;
+              }
+              if (!any) y = 0.0f;
+              ys += y;
+              word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(y), e, word);
+            }
+            pf[qb][b][q4] = static_cast<int>(word);
+          }
+        l[qb] = l[qb] * alpha[qb] + ys * mp127;
+      }
+
+      // ---- O = O * alpha + (mP/127) sV_j (P8 . V8), one channel block at a time
+      const float cv = mp127 * svj;
+      if (__ballot(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0ull) {
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+          for (int db = 0; db < D / 32; db++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) o[qb][db][r] *= alpha[qb];
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; db++) {
+        i32x16 ov0, ov1;
+        pv_block<D, BK>(vbuf[t & 1], vread, pf, db, ov0, ov1);
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          o[0][db][r] = __builtin_fmaf(static_cast<float>(ov0[r]), cv, o[0][db][r]);
+          o[1][db][r] = __builtin_fmaf(static_cast<float>(ov1[r]), cv, o[1][db][r]);
+        }
+      }
     }
+  }
 
-    i32x16 si[BK / 32];
-    qk_tile_i8<D, BQ, BK>(ks, qf, si);
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const int row = qbase + 32 * qb + l32;
+    if (row < N) {
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      uint16_t* op = O + (static_cast<int64_t>(g) * N + row) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; db++)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+          const int d0 = 32 * db + 8 * r4 + 4 * h;
+          uint2 pk;
+          pk.x = f32_to_bf16_bits(o[qb][db][4 * r4 + 0] * inv) |
+                 (f32_to_bf16_bits(o[qb][db][4 * r4 + 1] * inv) << 16);
+          pk.y = f32_to_bf16_bits(o[qb][db][4 * r4 + 2] * inv) |
+                 (f32_to_bf16_bits(o[qb][db][4 * r4 + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(op + d0) = pk;
+        }
+      if (lse != nullptr && h == 0)
+        lse[static_cast<int64_t>(g) * N + row] = lt > 0.0f ? m[qb] * kLn2 + logf(lt) : -INFINITY;
+    }
+  }
+}
 
-    const float c = sq * skj;
-    const bool ragged = !jvalid || j * BK + BK > N;
-    float sf[BK / 32][16];
-    float tmax = -INFINITY;
+// ---------------------------------------------------------------------------
+// Debug entry points: the forward kernel's own staging and int8 tile
+// routines on chosen tiles, writing exact int32 products.
+template <int D, int BQ, int BK>
+__global__ __launch_bounds__(BQ) void dbg_qk_kernel(const int8_t* __restrict__ Q,
+                                                    const int8_t* __restrict__ K, int G, int N,
+                                                    int nq, int nk, const int32_t* __restrict__ gij,
+                                                    int32_t* __restrict__ S) {
+  constexpr int NW = BQ / 64;
+  using L = L8<D, BK, NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[1][L::TB];
+  const int t = blockIdx.x;
+  int g = gij[3 * t], i = gij[3 * t + 1];
+  const int j = gij[3 * t + 2];
+  // an out-of-range head or q-block yields an all-zero tile; an out-of-range
+  // kv-block reads as zero
+  const bool ok = g >= 0 && g < G && i >= 0 && i < nq;
+  if (!ok) { g = 0; i = nq; }
+  const bool jvalid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  Stage8<D, BK, NW> sg;
+  sg.init();
+  const int nrec = jvalid ? N * D : 0;
+  L::stage(K + static_cast<int64_t>(g) * N * D, nrec, sg.k, jvalid ? j * BK : 0, kt[0]);
+  i32x4 qf[2][D / 32];
+  load_q<D>(Q, g, i * BQ + w * 64, N, qf);
+  wait_loads();
+  __syncthreads();
+  i32x16 s[2][BK / 32];
+  qk_i8<D, BK>(kt[0], k_read_off<D>(), qf, s);
+  int32_t* out = S + static_cast<int64_t>(t) * BQ * BK;
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    const int qr = w * 64 + 32 * qb + l32;
 #pragma unroll
     for (int b = 0; b < BK / 32; b++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        float x = static_cast<float>(si[b][r]) * c;
-        if (ragged && (!jvalid || j * BK + 32 * b + acc_row(r, h) >= N)) x = -INFINITY;
-        sf[b][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    const float ref = mnew == -INFINITY ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - ref);
-    float psum = 0.0f, pmax = 0.0f;
+      for (int r = 0; r < 16; r++) out[qr * BK + 32 * b + acc_row(r, h)] = s[qb][b][r];
+  }
+}
+
+template <int D, int BQ, int BK>
+__global__ __launch_bounds__(BQ) void dbg_pv_kernel(const int8_t* __restrict__ P8,
+                                                    const int8_t* __restrict__ V, int G, int N,
+                                                    int nk, const int32_t* __restrict__ gj,
+                                                    int32_t* __restrict__ OV) {
+  constexpr int NW = BQ / 64;
+  using L = L8<D, BK, NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t vt[1][L::TB];
+  const int t = blockIdx.x;
+  int g = gj[2 * t], j = gj[2 * t + 1];
+  // an out-of-range head or kv-block reads as an all-zero V tile
+  if (g < 0 || g >= G) { g = 0; j = -1; }
+  const bool jvalid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  Stage8<D, BK, NW> sg;
+  sg.init();
+  const int nrec = jvalid ? N * D : 0;
+  L::stage(V + static_cast<int64_t>(g) * N * D, nrec, sg.v, jvalid ? j * BK : 0, vt[0]);
+  // P8 operand: slot s of lane half h carries kv 8(s/4) + 4h + s%4
+  i32x4 pf[2][BK / 32];
 #pragma unroll
-    for (int b = 0; b < BK / 32; b++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const float p = __builtin_amdgcn_exp2f(sf[b][r] - ref);
-        sf[b][r] = p;
-        psum += p;
-        pmax = fmaxf(pmax, p);
-      }
-    l = l * alpha + psum;
-    m = mnew;
-    // per-tile scale of P over the real rows of the whole workgroup
-    pmax = wave_max(qvalid ? pmax : 0.0f);
-    if (lane == 0) s_red[w] = pmax;
-    __syncthreads();
-    float mp = s_red[0];
-#pragma unroll
-    for (int ww = 1; ww < G_::NW; ww++) mp = fmaxf(mp, s_red[ww]);
-    const float qs = mp > 0.0f ? 127.0f / mp : 0.0f;
-    const float cv = (mp / 127.0f) * svj;
-    i32x4 pf[BK / 32];
+  for (int qb = 0; qb < 2; qb++) {
+    const int8_t* prow = P8 + (static_cast<int64_t>(t) * BQ + w * 64 + 32 * qb + l32) * BK;
 #pragma unroll
     for (int b = 0; b < BK / 32; b++)
 #pragma unroll
       for (int q4 = 0; q4 < 4; q4++) {
         uint32_t word = 0;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const float y = fminf(rintf(sf[b][4 * q4 + e] * qs), 127.0f);
-          word |= (static_cast<uint32_t>(static_cast<int>(y)) & 0xffu) << (8 * e);
-        }
-        pf[b][q4] = static_cast<int>(word);
+        for (int e = 0; e < 4; e++)
+          word |= static_cast<uint32_t>(static_cast<uint8_t>(prow[32 * b + acc_row(4 * q4 + e, h)]))
+                  << (8 * e);
+        pf[qb][b][q4] = static_cast<int>(word);
       }
-    i32x16 ov[D / 32];
-    pv_tile_i8<D, BQ, BK>(vt, pf, ov);
-#pragma unroll
-    for (int db = 0; db < D / 32; db++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) o[db][r] = o[db][r] * alpha + static_cast<float>(ov[db][r]) * cv;
   }
-
-  l += __shfl_xor(l, 32);
-  if (qvalid) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    uint16_t* op = O + (static_cast<int64_t>(g) * N + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; db++)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; r4++) {
-        const int d0 = 32 * db + 8 * r4 + 4 * h;
-        uint2 pk;
-        pk.x = f32_to_bf16_bits(o[db][4 * r4 + 0] * inv) | (f32_to_bf16_bits(o[db][4 * r4 + 1] * inv) << 16);
-        pk.y = f32_to_bf16_bits(o[db][4 * r4 + 2] * inv) | (f32_to_bf16_bits(o[db][4 * r4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + d0) = pk;
-      }
-    if (lse != nullptr && h == 0)
-      lse[static_cast<int64_t>(g) * N + qrow] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Debug entry points: the forward kernel's own int8 tile routines on chosen
-// tiles, writing exact int32 products.
-template <int D, int BQ, int BK>
-__global__ __launch_bounds__(BQ * 2) void dbg_qk_kernel(const int8_t* __restrict__ Q,
-                                                        const int8_t* __restrict__ K, int G, int N,
-                                                        int nq, int nk,
-                                                        const int32_t* __restrict__ gij,
-                                                        int32_t* __restrict__ S) {
-  using G_ = Geo<D, BQ, BK, 1>;
-  __shared__ __attribute__((aligned(16))) int8_t ks[BK * G_::KP];
-  const int t = blockIdx.x;
-  int g = gij[3 * t], i = gij[3 * t + 1];
-  const int j = gij[3 * t + 2];
-  // an out-of-range head or q-block yields an all-zero tile
-  const bool ok = g >= 0 && g < G && i >= 0 && i < nq;
-  if (!ok) { g = 0; i = nq; }
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int qrow = i * BQ + w * 32 + l32;
-  i32x4 qf[D / 32];
-  load_q<D, 1, 32>(reinterpret_cast<const uint8_t*>(Q), g, qrow, N, qf);
-  uint4 kr[G_::CPT];
-  load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(K), g, j, N,
-                          static_cast<unsigned>(j) < static_cast<unsigned>(nk), kr);
-  store_k<D, BQ, BK, 1>(reinterpret_cast<uint8_t*>(ks), kr);
+  wait_loads();
   __syncthreads();
-  i32x16 si[BK / 32];
-  qk_tile_i8<D, BQ, BK>(ks, qf, si);
-  int32_t* out = S + static_cast<int64_t>(t) * BQ * BK;
-  const int qr = w * 32 + l32;
-#pragma unroll
-  for (int b = 0; b < BK / 32; b++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) out[qr * BK + 32 * b + acc_row(r, h)] = si[b][r];
-}
-
-template <int D, int BQ, int BK>
-__global__ __launch_bounds__(BQ * 2) void dbg_pv_kernel(const int8_t* __restrict__ P8,
-                                                        const int8_t* __restrict__ V, int G, int N,
-                                                        int nk, const int32_t* __restrict__ gj,
-                                                        int32_t* __restrict__ OV) {
-  using G_ = Geo<D, BQ, BK, 1>;
-  __shared__ __attribute__((aligned(16))) int8_t vt[D * G_::VP];
-  const int t = blockIdx.x;
-  int g = gj[2 * t], j = gj[2 * t + 1];
-  // an out-of-range head or kv-block reads as an all-zero V tile
-  if (g < 0 || g >= G) { g = 0; j = -1; }
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int qr = w * 32 + l32;
-  const int8_t* prow = P8 + (static_cast<int64_t>(t) * BQ + qr) * BK;
-  i32x4 pf[BK / 32];
-#pragma unroll
-  for (int b = 0; b < BK / 32; b++)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; q4++) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < 4; e++)
-        word |= (static_cast<uint32_t>(static_cast<uint8_t>(prow[32 * b + acc_row(4 * q4 + e, h)])))
-                << (8 * e);
-      pf[b][q4] = static_cast<int>(word);
-    }
-  uint4 vr[G_::CPT];
-  load_tile<D, BQ, BK, 1>(reinterpret_cast<const uint8_t*>(V), g, j, N,
-                          static_cast<unsigned>(j) < static_cast<unsigned>(nk), vr);
-  store_vt<D, BQ, BK, 1>(reinterpret_cast<uint8_t*>(vt), vr);
-  __syncthreads();
-  i32x16 ov[D / 32];
-  pv_tile_i8<D, BQ, BK>(vt, pf, ov);
   int32_t* out = OV + static_cast<int64_t>(t) * BQ * D;
+  const uint32_t vread = v_read_off<D>();
 #pragma unroll
-  for (int db = 0; db < D / 32; db++)
+  for (int db = 0; db < D / 32; db++) {
+    i32x16 ov[2];
+    pv_block<D, BK>(vt[0], vread, pf, db, ov[0], ov[1]);
 #pragma unroll
-    for (int r = 0; r < 16; r++) out[qr * D + 32 * db + acc_row(r, h)] = ov[db][r];
+    for (int qb = 0; qb < 2; qb++) {
+      const int qr = w * 64 + 32 * qb + l32;
+#pragma unroll
+      for (int r = 0; r < 16; r++) out[qr * D + 32 * db + acc_row(r, h)] = ov[qb][r];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -423,8 +512,8 @@ template <int D, int BQ, int BK>
 struct LaunchI8 {
   static hipError_t run(const AttnArgs& a, hipStream_t s) {
     const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
-    const uint32_t nwg = static_cast<uint32_t>(a.G) * nq;
-    fwd_i8_kernel<D, BQ, BK><<<nwg, BQ * 2, 0, s>>>(
+    const uint32_t nwg = static_cast<uint32_t>(a.G) * kNumXcd * ((nq + kNumXcd - 1) / kNumXcd);
+    fwd_i8_kernel<D, BQ, BK><<<nwg, BQ, 0, s>>>(
         static_cast<const int8_t*>(a.Q), a.sQ, static_cast<const int8_t*>(a.K), a.sK,
         static_cast<const int8_t*>(a.V), a.sV, a.row_ptr, a.col_idx, a.col_len, a.mask_G, a.O,
         a.lse, a.N, nq, nk, scale_log2_of(a));
@@ -437,7 +526,7 @@ struct LaunchDbgQk {
   static hipError_t run(const int8_t* Q, const int8_t* K, int G, int N, const int32_t* gij, int n,
                         int32_t* S, hipStream_t s) {
     const int nq = (N + BQ - 1) / BQ, nk = (N + BK - 1) / BK;
-    dbg_qk_kernel<D, BQ, BK><<<n, BQ * 2, 0, s>>>(Q, K, G, N, nq, nk, gij, S);
+    dbg_qk_kernel<D, BQ, BK><<<n, BQ, 0, s>>>(Q, K, G, N, nq, nk, gij, S);
     return hipGetLastError();
   }
 };
@@ -447,7 +536,7 @@ struct LaunchDbgPv {
   static hipError_t run(const int8_t* P8, const int8_t* V, int G, int N, const int32_t* gj, int n,
                         int32_t* OV, hipStream_t s) {
     const int nk = (N + BK - 1) / BK;
-    dbg_pv_kernel<D, BQ, BK><<<n, BQ * 2, 0, s>>>(P8, V, G, N, nk, gj, OV);
+    dbg_pv_kernel<D, BQ, BK><<<n, BQ, 0, s>>>(P8, V, G, N, nk, gj, OV);
     return hipGetLastError();
   }
 };

@@ -301,9 +301,16 @@ __device__ __forceinline__ void exp_pair(const f32x16 (&s)[2][2], float c, const
   const int qb = pp >> 4, b = (pp >> 3) & 1, r = 2 * (pp & 7);
   const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r], c, -m[qb]));
   const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r + 1], c, -m[qb]));
+#ifdef BSA_SUM_DOT2
+  const bf16x2 pr = (bf16x2){static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+  sum[qb] = __builtin_amdgcn_fdot2_f32_bf16(
+      pr, (bf16x2){static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)}, sum[qb], false);
+  pw[qb][(pp & 15) >> 2][pp & 3] = __builtin_bit_cast(uint32_t, pr);
+#else
   sum[qb] = (sum[qb] + x0) + x1;
   pw[qb][(pp & 15) >> 2][pp & 3] =
       __builtin_bit_cast(uint32_t, (bf16x2){static_cast<__bf16>(x0), static_cast<__bf16>(x1)});
+#endif
   if ((pp & 3) == 3) asm volatile("" : "+v"(pw[qb][(pp & 15) >> 2]));
 }
 
