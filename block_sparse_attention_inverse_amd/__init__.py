@@ -2,8 +2,9 @@
 
 Public surface (Python names mirror the C ABI in include/bsa.h):
 ``permute``, ``mask_capacity``, ``mask_workspace``, ``build_mask``,
-``quantize_int8``, ``forward``, ``forward_int8``, ``debug_int8_qk``,
-``debug_int8_pv``, plus ``LayerPlan`` / ``layer_forward`` which chain them.
+``permute_pool``, ``build_mask_pooled``, ``order_workspace``,
+``order_scores``, ``select_orders``, ``quantize_int8``, ``forward``,
+``forward_int8``, ``debug_int8_qk``, ``debug_int8_pv``, plus ``LayerPlan`` / ``layer_forward`` which chain them.
 The HIP library is loaded on first use and must be built; there is no
 fallback path.  ``synth`` holds the seeded synthetic workload generators.
 """
@@ -11,6 +12,7 @@ from .api import (  # noqa: F401
     LayerPlan,
     abi_version,
     build_mask,
+    build_mask_pooled,
     debug_int8_pv,
     debug_int8_qk,
     forward,
@@ -20,7 +22,11 @@ from .api import (  # noqa: F401
     mask_capacity,
     mask_params,
     mask_workspace,
+    order_scores,
+    order_workspace,
     permute,
+    permute_pool,
     quantize_int8,
+    select_orders,
 )
 from ._lib import BsaError, MaskParams  # noqa: F401

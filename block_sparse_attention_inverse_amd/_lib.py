@@ -38,6 +38,12 @@ SIGNATURES = {
     "bsa_mask_workspace": (_L, [_I, _I, _I, _I, _I, ctypes.POINTER(MaskParams)]),
     "bsa_build_mask": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, ctypes.POINTER(MaskParams), _P, _P,
                             _L, _P, _P, _L, _P]),
+    "bsa_build_mask_pooled": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, ctypes.POINTER(MaskParams), _P,
+                                   _P, _L, _P, _P, _L, _P]),
+    "bsa_permute_pool": (_I, [_P, _I, _P, _L, _L, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
+    "bsa_order_workspace": (_L, [_I, _I, _I, _I, _I]),
+    "bsa_order_scores": (_I, [_P, _I, _L, _L, _I, _I, _I, _I, _I, _I, _P, _P, _L, _P]),
+    "bsa_select_orders": (_I, [_P, _P, _I, _P, _P]),
     "bsa_quantize_int8": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "bsa_forward": (_I, [_P, _P, _P, _P, _P, _L, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "bsa_forward_int8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _L, _I, _P, _P, _I, _I, _I, _I, _I,

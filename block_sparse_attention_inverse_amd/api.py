@@ -112,6 +112,126 @@ def build_mask(Qp, Kp, axis_order, F, H, W, params: MaskParams, workspace=None):
     return row_ptr, col_idx, nnz
 
 
+def permute_pool(x, axis_order, F, H, W, B, out=None, sums=None, int8=None, reordered=True):
+    """bsa_permute_pool: natural x [N][G][d] -> reordered bf16 [G][N][d] in one
+    pass, also writing per-block channel sums and INT8 codes when asked.
+    ``sums``: True (allocate) or an fp32 [G][ceil(N/B)][d] tensor, or None;
+    ``int8``: True or a (codes int8 [G][N][d], scales fp32 [G][ceil(N/B)])
+    pair, or None; ``reordered=False`` skips the bf16 copy.  Returns
+    (xp or None, sums or None, (codes, scales) or None)."""
+    _lib.load()
+    N = F * H * W
+    if x.dim() != 3 or x.shape[0] != N or x.stride(2) != 1:
+        raise ValueError("natural input must be [N][G][d] with unit channel stride")
+    G, d = x.shape[1], x.shape[2]
+    nb = (N + B - 1) // B
+    dev = x.device
+    if not reordered:
+        out = None
+    elif out is None:
+        out = torch.empty((G, N, d), dtype=torch.bfloat16, device=dev)
+    if sums is True:
+        sums = torch.empty((G, nb, d), dtype=torch.float32, device=dev)
+    if int8 is True:
+        int8 = (torch.empty((G, N, d), dtype=torch.int8, device=dev),
+                torch.empty((G, nb), dtype=torch.float32, device=dev))
+    xq, sc = int8 if int8 else (None, None)
+    _dev(x, axis_order, *(t for t in (out, sums, xq, sc) if t is not None))
+    if axis_order.dtype != torch.uint8 or axis_order.numel() < G:
+        raise ValueError("axis_order must be a uint8 tensor with G entries")
+    if out is not None and (out.shape != (G, N, d) or not out.is_contiguous()
+                            or out.dtype != torch.bfloat16):
+        raise ValueError("out must be contiguous bf16 [G][N][d]")
+    if sums is not None and (sums.shape != (G, nb, d) or sums.dtype != torch.float32
+                             or not sums.is_contiguous()):
+        raise ValueError("sums must be contiguous fp32 [G][ceil(N/B)][d]")
+    if xq is not None and (xq.shape != (G, N, d) or xq.dtype != torch.int8 or not xq.is_contiguous()
+                           or sc.shape != (G, nb) or sc.dtype != torch.float32
+                           or not sc.is_contiguous()):
+        raise ValueError("int8 must be (int8 [G][N][d], fp32 [G][ceil(N/B)]), both contiguous")
+    rc = _lib.load().bsa_permute_pool(
+        _ptr(x), _DT[x.dtype], _ptr(out) if out is not None else None, x.stride(1), x.stride(0), G,
+        F, H, W, d, _ptr(axis_order),
+        B, _ptr(sums) if sums is not None else None, _ptr(xq) if xq is not None else None,
+        _ptr(sc) if sc is not None else None, _stream())
+    check(rc)
+    return out, sums, (int8 if int8 else None)
+
+
+def build_mask_pooled(sums_q, sums_k, axis_order, F, H, W, params: MaskParams, workspace=None):
+    """bsa_build_mask_pooled from per-block channel sums (Bq blocks of the
+    reordered Q, Bk blocks of the reordered K).  Returns (row_ptr, col_idx,
+    nnz) as :func:`build_mask`."""
+    _dev(sums_q, sums_k, axis_order)
+    G, _, d = sums_q.shape
+    N = F * H * W
+    for t, B in ((sums_q, params.Bq), (sums_k, params.Bk)):
+        if (t.shape != (G, (N + B - 1) // B, d) or t.dtype != torch.float32
+                or not t.is_contiguous()):
+            raise ValueError("sums must be contiguous fp32 [G][ceil(N/B)][d] (Bq for Q, Bk for K)")
+    cap = mask_capacity(G, F, H, W, params)
+    ws_bytes = mask_workspace(G, F, H, W, d, params)
+    nq = (N + params.Bq - 1) // params.Bq
+    row_ptr = torch.empty(G * nq + 1, dtype=torch.int32, device=sums_q.device)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=sums_q.device)
+    nnz = torch.empty(1, dtype=torch.int32, device=sums_q.device)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=sums_q.device)
+    rc = _lib.load().bsa_build_mask_pooled(_ptr(sums_q), _ptr(sums_k), G, F, H, W, d,
+                                           _ptr(axis_order), ctypes.byref(params), _ptr(row_ptr),
+                                           _ptr(col_idx), col_idx.numel(), _ptr(nnz),
+                                           _ptr(workspace), workspace.numel(), _stream())
+    check(rc)
+    return row_ptr, col_idx, nnz
+
+
+def order_workspace(G, F, H, W, B) -> int:
+    v = int(_lib.load().bsa_order_workspace(G, F, H, W, B))
+    if v < 0:
+        raise ValueError("bsa_order_workspace: bad sizes or block")
+    return v
+
+
+def order_scores(x, F, H, W, B, out=None, workspace=None):
+    """bsa_order_scores: SICS score of every (head, axis order) for natural
+    x [N][G][d] (fp32 or bf16, unit channel stride) cut into B-row blocks.
+    Returns fp32 [G][6] on the device."""
+    _lib.load()
+    N = F * H * W
+    if x.dim() != 3 or x.shape[0] != N or x.stride(2) != 1:
+        raise ValueError("natural input must be [N][G][d] with unit channel stride")
+    G, d = x.shape[1], x.shape[2]
+    if out is None:
+        out = torch.empty((G, 6), dtype=torch.float32, device=x.device)
+    if out.shape != (G, 6) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [G][6]")
+    ws_bytes = order_workspace(G, F, H, W, B)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    _dev(x, out, workspace)
+    rc = _lib.load().bsa_order_scores(_ptr(x), _DT[x.dtype], x.stride(1), x.stride(0), G, F, H, W, d,
+                                      B, _ptr(out), _ptr(workspace), workspace.numel(), _stream())
+    check(rc)
+    return out
+
+
+def select_orders(scores_a, scores_b=None, out=None):
+    """bsa_select_orders: per head, the order code maximising
+    scores_a + scores_b (fp32), ties to the lowest code.  Returns uint8 [G]."""
+    G = scores_a.shape[0]
+    for t in (scores_a, scores_b):
+        if t is not None and (t.shape != (G, 6) or t.dtype != torch.float32
+                              or not t.is_contiguous()):
+            raise ValueError("scores must be contiguous fp32 [G][6]")
+    if out is None:
+        out = torch.empty(G, dtype=torch.uint8, device=scores_a.device)
+    _dev(scores_a, out, *(t for t in (scores_b,) if t is not None))
+    rc = _lib.load().bsa_select_orders(_ptr(scores_a), _ptr(scores_b) if scores_b is not None else None,
+                                       G, _ptr(out), _stream())
+    check(rc)
+    return out
+
+
 def quantize_int8(Xp, B, out=None):
     """bsa_quantize_int8: bf16 [G][N][d] -> (int8 [G][N][d], fp32 scales
     [G][ceil(N/B)]); ``out`` = (q, scale) reuses preallocated tensors."""
@@ -189,12 +309,14 @@ class LayerPlan:
     reordered copies, mask CSR, INT8 copies and the output, allocated once
     and reused by :func:`layer_forward`."""
 
-    def __init__(self, G, F, H, W, d, device, params: MaskParams, int8=False, dynamic_mask=True):
+    def __init__(self, G, F, H, W, d, device, params: MaskParams, int8=False, dynamic_mask=True,
+                 fused=False):
         N = F * H * W
         self.G, self.F, self.H, self.W, self.d, self.N = G, F, H, W, d, N
         self.params = params
         self.int8 = int8
         self.dynamic_mask = dynamic_mask
+        self.fused = fused
         e = dict(device=device)
         self.Qp = torch.empty((G, N, d), dtype=torch.bfloat16, **e)
         self.Kp = torch.empty_like(self.Qp)
@@ -208,6 +330,10 @@ class LayerPlan:
         self.col_idx = torch.zeros(max(cap, 1), dtype=torch.int32, **e)
         self.nnz = torch.zeros(1, dtype=torch.int32, **e)
         self.ws = torch.empty(mask_workspace(G, F, H, W, d, params), dtype=torch.uint8, **e)
+        if fused:
+            nk = (N + params.Bk - 1) // params.Bk
+            self.sums_q = torch.empty((G, nq, d), dtype=torch.float32, **e)
+            self.sums_k = torch.empty((G, nk, d), dtype=torch.float32, **e)
         if int8:
             nk = (N + params.Bk - 1) // params.Bk
             self.Qq = torch.empty((G, N, d), dtype=torch.int8, **e)
@@ -223,6 +349,32 @@ class LayerPlan:
         quantize_int8(self.Kp, p.Bk, out=(self.Kq, self.sK))
         quantize_int8(self.Vp, p.Bk, out=(self.Vq, self.sV))
 
+    def reorder_fused(self, Q, K, V, axis_order):
+        """Reorder Q, K, V with the block sums of Q and K (and, for INT8, the
+        codes of all three) in the same pass."""
+        p = self.params
+        q8 = (self.Qq, self.sQ) if self.int8 else None
+        k8 = (self.Kq, self.sK) if self.int8 else None
+        v8 = (self.Vq, self.sV) if self.int8 else None
+        F, H, W = self.F, self.H, self.W
+        bf = not self.int8  # the INT8 attention reads only the codes
+        permute_pool(Q, axis_order, F, H, W, p.Bq, out=self.Qp, sums=self.sums_q, int8=q8,
+                     reordered=bf)
+        permute_pool(K, axis_order, F, H, W, p.Bk, out=self.Kp, sums=self.sums_k, int8=k8,
+                     reordered=bf)
+        if self.int8:
+            permute_pool(V, axis_order, F, H, W, p.Bk, int8=v8, reordered=False)
+        else:
+            permute(V, axis_order, F, H, W, 0, out=self.Vp)
+
+    def build_mask_from_sums(self, axis_order):
+        lib = _lib.load()
+        check(lib.bsa_build_mask_pooled(_ptr(self.sums_q), _ptr(self.sums_k), self.G, self.F,
+                                        self.H, self.W, self.d, _ptr(axis_order),
+                                        ctypes.byref(self.params), _ptr(self.row_ptr),
+                                        _ptr(self.col_idx), self.col_idx.numel(), _ptr(self.nnz),
+                                        _ptr(self.ws), self.ws.numel(), _stream()))
+
     def build_mask(self, axis_order):
         lib = _lib.load()
         p = self.params
@@ -235,16 +387,24 @@ class LayerPlan:
 def layer_forward(plan: LayerPlan, Q, K, V, axis_order):
     """One pass of the whole path on natural-order Q, K, V [N][G][d]:
     reorder (x3) -> [build mask] -> [quantize (x3)] -> block-sparse attention
-    -> inverse reorder.  Returns the natural-order output [N][G][d] (bf16)."""
+    -> inverse reorder.  With ``plan.fused`` the reorder, the block pooling
+    and the INT8 quantisation share one pass per tensor.  Returns the
+    natural-order output [N][G][d] (bf16)."""
     F, H, W = plan.F, plan.H, plan.W
     p = plan.params
-    permute(Q, axis_order, F, H, W, 0, out=plan.Qp)
-    permute(K, axis_order, F, H, W, 0, out=plan.Kp)
-    permute(V, axis_order, F, H, W, 0, out=plan.Vp)
-    if plan.dynamic_mask:
-        plan.build_mask(axis_order)
+    if plan.fused:
+        plan.reorder_fused(Q, K, V, axis_order)
+        if plan.dynamic_mask:
+            plan.build_mask_from_sums(axis_order)
+    else:
+        permute(Q, axis_order, F, H, W, 0, out=plan.Qp)
+        permute(K, axis_order, F, H, W, 0, out=plan.Kp)
+        permute(V, axis_order, F, H, W, 0, out=plan.Vp)
+        if plan.dynamic_mask:
+            plan.build_mask(axis_order)
+        if plan.int8:
+            plan.quantize()
     if plan.int8:
-        plan.quantize()
         forward_int8(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq, plan.sV, plan.row_ptr,
                      plan.col_idx, p.Bq, p.Bk, out=plan.Op, lse=plan.lse)
     else:

@@ -13,7 +13,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsa.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["capi.hip", "permute.hip", "mask.hip", "quant.hip", "attn.hip", "attn_bf16.hip"]
+SOURCES = [
+    "capi.hip", "permute.hip", "mask.hip", "fused.hip", "order.hip", "quant.hip", "attn.hip",
+    "attn_bf16.hip",
+]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -34,6 +34,24 @@ MaskWs mask_workspace_layout(const MaskGeom& m);
 hipError_t launch_build_mask(const MaskGeom& m, const uint16_t* Qp, const uint16_t* Kp,
                              const uint8_t* orders, int32_t* row_ptr, int32_t* col_idx,
                              int64_t col_capacity, int32_t* nnz, char* ws, hipStream_t s);
+// as launch_build_mask from per-block channel sums (Bq blocks of Q, Bk of K)
+hipError_t launch_build_mask_pooled(const MaskGeom& m, const float* sums_q, const float* sums_k,
+                                    const uint8_t* orders, int32_t* row_ptr, int32_t* col_idx,
+                                    int64_t col_capacity, int32_t* nnz, char* ws, hipStream_t s);
+
+// ---- fused.hip -------------------------------------------------------------
+hipError_t launch_permute_pool(const void* src, int src_dt, uint16_t* dst, int64_t stride_g,
+                               int64_t stride_n, int G, int F, int H, int W, int d,
+                               const uint8_t* orders, int B, float* sums, int8_t* xq, float* scale,
+                               hipStream_t s);
+
+// ---- order.hip -------------------------------------------------------------
+size_t order_workspace_bytes(int G, int N, int B);
+hipError_t launch_order_scores(const void* src, int src_dt, int64_t stride_g, int64_t stride_n,
+                               int G, int F, int H, int W, int d, int B, float* scores, void* ws,
+                               hipStream_t s);
+hipError_t launch_select_orders(const float* a, const float* b, int G, uint8_t* orders,
+                                hipStream_t s);
 
 // ---- quant.hip -------------------------------------------------------------
 hipError_t launch_quantize_int8(const uint16_t* X, int8_t* Xq, float* scale, int G, int N, int d,

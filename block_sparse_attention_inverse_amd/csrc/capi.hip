@@ -182,6 +182,106 @@ int bsa_build_mask(const void* Qp, const void* Kp, int32_t dt, int32_t G, int32_
   });
 }
 
+int bsa_permute_pool(const void* src, int32_t src_dt, void* dst, int64_t nat_stride_g,
+                     int64_t nat_stride_n, int32_t G, int32_t F, int32_t H, int32_t W, int32_t d,
+                     const uint8_t* axis_order, int32_t B, float* sums, int8_t* xq, float* scale,
+                     void* stream) {
+  return guarded([&]() -> int {
+    if (!src || !axis_order) return fail(BSA_EINVAL, "NULL pointer");
+    if (!dst && !sums && !xq) return fail(BSA_EINVAL, "no output requested");
+    if ((xq == nullptr) != (scale == nullptr))
+      return fail(BSA_EINVAL, "xq and scale are given together or not at all");
+    if (src_dt != BSA_F32 && src_dt != BSA_BF16) return fail(BSA_EUNSUPPORTED, "src must be F32 or BF16");
+    if (G <= 0 || F <= 0 || H <= 0 || W <= 0) return fail(BSA_EINVAL, "sizes must be positive");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    if (!block_ok(B)) return fail(BSA_EUNSUPPORTED, "B must be 64 or 128");
+    if (G > 65535) return fail(BSA_EUNSUPPORTED, "G must be <= 65535");
+    if (nat_stride_g < 0 || nat_stride_n < 0 || nat_stride_g % 8 || nat_stride_n % 8)
+      return fail(BSA_EINVAL, "natural strides must be non-negative multiples of 8");
+    const int64_t N = static_cast<int64_t>(F) * H * W;
+    if (N >= (1ll << 31) || N * d >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "N*d must be < 2^31");
+    if ((N + B - 1) / B > 65535 * 64) return fail(BSA_EUNSUPPORTED, "too many blocks");
+    if (!aligned(src, 16) || (dst && !aligned(dst, 16)))
+      return fail(BSA_EINVAL, "src/dst must be 16-byte aligned");
+    if (sums && !aligned(sums, 4)) return fail(BSA_EINVAL, "sums must be 4-byte aligned");
+    if (xq && !aligned(xq, 8)) return fail(BSA_EINVAL, "xq must be 8-byte aligned");
+    return hip_status(bsa::launch_permute_pool(src, src_dt, static_cast<uint16_t*>(dst), nat_stride_g,
+                                               nat_stride_n, G, F, H, W, d, axis_order, B, sums, xq,
+                                               scale, as_stream(stream)),
+                      "bsa_permute_pool");
+  });
+}
+
+int bsa_build_mask_pooled(const float* sums_q, const float* sums_k, int32_t G, int32_t F, int32_t H,
+                          int32_t W, int32_t d, const uint8_t* axis_order,
+                          const bsa_mask_params* p_host, int32_t* row_ptr, int32_t* col_idx,
+                          int64_t col_capacity, int32_t* nnz, void* workspace, int64_t ws_bytes,
+                          void* stream) {
+  return guarded([&]() -> int {
+    if (!sums_q || !sums_k || !axis_order || !row_ptr || !col_idx || !nnz || !workspace)
+      return fail(BSA_EINVAL, "NULL pointer");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    bsa::MaskGeom m{};
+    const int rc = mask_geom(G, F, H, W, d, p_host, m);
+    if (rc != BSA_OK) return rc;
+    const int64_t cap = capacity_of(m);
+    if (cap >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "mask capacity %lld exceeds int32", (long long)cap);
+    if (col_capacity < cap)
+      return fail(BSA_ECAPACITY, "col_capacity %lld < required bound %lld", (long long)col_capacity,
+                  (long long)cap);
+    const int64_t need = static_cast<int64_t>(bsa::mask_workspace_layout(m).total);
+    if (ws_bytes < need)
+      return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
+    if (!aligned(workspace, 256)) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+    return hip_status(bsa::launch_build_mask_pooled(m, sums_q, sums_k, axis_order, row_ptr, col_idx,
+                                                    col_capacity, nnz, static_cast<char*>(workspace),
+                                                    as_stream(stream)),
+                      "bsa_build_mask_pooled");
+  });
+}
+
+int64_t bsa_order_workspace(int32_t G, int32_t F, int32_t H, int32_t W, int32_t B) {
+  if (G <= 0 || F <= 0 || H <= 0 || W <= 0 || !block_ok(B)) return -1;
+  const int64_t N = static_cast<int64_t>(F) * H * W;
+  if (N >= (1ll << 31)) return -1;
+  return static_cast<int64_t>(bsa::order_workspace_bytes(G, static_cast<int>(N), B));
+}
+
+int bsa_order_scores(const void* src, int32_t src_dt, int64_t nat_stride_g, int64_t nat_stride_n,
+                     int32_t G, int32_t F, int32_t H, int32_t W, int32_t d, int32_t B, float* scores,
+                     void* workspace, int64_t ws_bytes, void* stream) {
+  return guarded([&]() -> int {
+    if (!src || !scores || !workspace) return fail(BSA_EINVAL, "NULL pointer");
+    if (src_dt != BSA_F32 && src_dt != BSA_BF16) return fail(BSA_EUNSUPPORTED, "src must be F32 or BF16");
+    if (G <= 0 || F <= 0 || H <= 0 || W <= 0) return fail(BSA_EINVAL, "sizes must be positive");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    if (!block_ok(B)) return fail(BSA_EUNSUPPORTED, "B must be 64 or 128");
+    if (G > 65535) return fail(BSA_EUNSUPPORTED, "G must be <= 65535");
+    if (nat_stride_g < 0 || nat_stride_n < 0 || nat_stride_g % 8 || nat_stride_n % 8)
+      return fail(BSA_EINVAL, "natural strides must be non-negative multiples of 8");
+    const int64_t N = static_cast<int64_t>(F) * H * W;
+    if (N >= (1ll << 31) || N * d >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "N*d must be < 2^31");
+    if (!aligned(src, 16)) return fail(BSA_EINVAL, "src must be 16-byte aligned");
+    if (!aligned(workspace, 4)) return fail(BSA_EINVAL, "workspace must be 4-byte aligned");
+    const int64_t need = static_cast<int64_t>(bsa::order_workspace_bytes(G, static_cast<int>(N), B));
+    if (ws_bytes < need)
+      return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
+    return hip_status(bsa::launch_order_scores(src, src_dt, nat_stride_g, nat_stride_n, G, F, H, W, d,
+                                               B, scores, workspace, as_stream(stream)),
+                      "bsa_order_scores");
+  });
+}
+
+int bsa_select_orders(const float* scores_a, const float* scores_b, int32_t G, uint8_t* axis_order,
+                      void* stream) {
+  return guarded([&]() -> int {
+    if (!scores_a || !axis_order) return fail(BSA_EINVAL, "NULL pointer");
+    if (G <= 0) return fail(BSA_EINVAL, "G must be positive");
+    return hip_status(bsa::launch_select_orders(scores_a, scores_b, G, axis_order, as_stream(stream)),
+                      "bsa_select_orders");
+  });
+}
+
 int bsa_quantize_int8(const void* Xp, int8_t* Xq, float* scale, int32_t G, int32_t N, int32_t d,
                       int32_t B, void* stream) {
   return guarded([&]() -> int {

@@ -116,6 +116,39 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// finish_pool_kernel: pooled summaries from per-block channel sums produced
+// elsewhere (the fused reorder + pooling pass, same summation contract): the
+// means (DOT, sum / len correctly rounded) or the sums and their norms
+// (COSINE), exactly as pool_kernel leaves them.  One workgroup of D threads
+// per logical block (q-blocks, then kv-blocks).
+template <int D>
+__global__ __launch_bounds__(D) void finish_pool_kernel(
+    const float* __restrict__ in_q, const float* __restrict__ in_k, int G, int N, int Bq, int Bk,
+    int nq, int nk, int score, float* __restrict__ sum_q, float* __restrict__ sum_k,
+    float* __restrict__ norm_q, float* __restrict__ norm_k) {
+  __shared__ float sh[D];
+  const int64_t lb = blockIdx.x;
+  const int64_t nqt = static_cast<int64_t>(G) * nq;
+  const bool is_q = lb < nqt;
+  const int64_t idx = is_q ? lb : lb - nqt;  // g * nb + b
+  const int nb = is_q ? nq : nk, B = is_q ? Bq : Bk;
+  const int b = static_cast<int>(idx % nb);
+  const int len = min(B, N - b * B);
+  const int c = threadIdx.x;
+  const float a = (is_q ? in_q : in_k)[idx * D + c];
+  (is_q ? sum_q : sum_k)[idx * D + c] = score == 0 ? div_rn(a, static_cast<float>(len)) : a;
+  if (score == 1) {
+    sh[c] = a;
+    __syncthreads();
+    if (c == 0) {
+      float acc = 0.0f;
+      for (int e = 0; e < D; e++) acc = __builtin_fmaf(sh[e], sh[e], acc);
+      (is_q ? norm_q : norm_k)[idx] = sqrt_rn(acc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Natural frame and in-frame offset of a block's centre position.
 __device__ __forceinline__ void block_centre(int order, int b, int B, int N, int F, int H, int W,
                                              int& frame, int& offs) {
@@ -331,6 +364,36 @@ MaskWs mask_workspace_layout(const MaskGeom& m) {
   return w;
 }
 
+namespace {
+
+// Pooled summaries in the workspace -> keys, selection, CSR.
+hipError_t select_and_emit(const MaskGeom& m, const uint8_t* orders, int32_t* row_ptr,
+                           int32_t* col_idx, int64_t col_capacity, int32_t* nnz, char* ws,
+                           hipStream_t s) {
+  const MaskWs L = mask_workspace_layout(m);
+  const float* sum_q = reinterpret_cast<const float*>(ws + L.sum_q);
+  const float* sum_k = reinterpret_cast<const float*>(ws + L.sum_k);
+  const float* norm_q = reinterpret_cast<const float*>(ws + L.norm_q);
+  const float* norm_k = reinterpret_cast<const float*>(ws + L.norm_k);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  auto* bits = reinterpret_cast<unsigned long long*>(ws + L.bits);
+  const int N = static_cast<int>(m.N);
+  const int R = m.G * m.nq;
+  if (m.d == 128)
+    select_kernel<128><<<R, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F, m.H,
+                                                 m.W, m.Bq, m.Bk, m.nq, m.nk, m.words, m.score,
+                                                 m.k, m.force_diag, m.win_T, m.win_r0, counts, bits);
+  else
+    select_kernel<64><<<R, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F, m.H,
+                                                m.W, m.Bq, m.Bk, m.nq, m.nk, m.words, m.score, m.k,
+                                                m.force_diag, m.win_T, m.win_r0, counts, bits);
+  scan_kernel<<<1, kScanThreads, 0, s>>>(counts, R, row_ptr, nnz);
+  emit_kernel<<<(R + 3) / 4, 256, 0, s>>>(bits, row_ptr, R, m.words, col_idx, col_capacity);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_build_mask(const MaskGeom& m, const uint16_t* Qp, const uint16_t* Kp,
                              const uint8_t* orders, int32_t* row_ptr, int32_t* col_idx,
                              int64_t col_capacity, int32_t* nnz, char* ws, hipStream_t s) {
@@ -339,29 +402,37 @@ hipError_t launch_build_mask(const MaskGeom& m, const uint16_t* Qp, const uint16
   float* sum_k = reinterpret_cast<float*>(ws + L.sum_k);
   float* norm_q = reinterpret_cast<float*>(ws + L.norm_q);
   float* norm_k = reinterpret_cast<float*>(ws + L.norm_k);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  auto* bits = reinterpret_cast<unsigned long long*>(ws + L.bits);
   const int N = static_cast<int>(m.N);
-  const int R = m.G * m.nq;
   const int64_t total_blocks = static_cast<int64_t>(m.G) * (m.nq + m.nk);
   if (m.d == 128) {
     const int bpw = kPoolThreads / 64;
     pool_kernel<128><<<static_cast<uint32_t>((total_blocks + bpw - 1) / bpw), kPoolThreads, 0, s>>>(
         Qp, Kp, m.G, N, m.Bq, m.Bk, m.nq, m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
-    select_kernel<128><<<R, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F, m.H,
-                                                 m.W, m.Bq, m.Bk, m.nq, m.nk, m.words, m.score,
-                                                 m.k, m.force_diag, m.win_T, m.win_r0, counts, bits);
   } else {
     const int bpw = kPoolThreads / 32;
     pool_kernel<64><<<static_cast<uint32_t>((total_blocks + bpw - 1) / bpw), kPoolThreads, 0, s>>>(
         Qp, Kp, m.G, N, m.Bq, m.Bk, m.nq, m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
-    select_kernel<64><<<R, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F, m.H,
-                                                m.W, m.Bq, m.Bk, m.nq, m.nk, m.words, m.score, m.k,
-                                                m.force_diag, m.win_T, m.win_r0, counts, bits);
   }
-  scan_kernel<<<1, kScanThreads, 0, s>>>(counts, R, row_ptr, nnz);
-  emit_kernel<<<(R + 3) / 4, 256, 0, s>>>(bits, row_ptr, R, m.words, col_idx, col_capacity);
-  return hipGetLastError();
+  return select_and_emit(m, orders, row_ptr, col_idx, col_capacity, nnz, ws, s);
+}
+
+hipError_t launch_build_mask_pooled(const MaskGeom& m, const float* sums_q, const float* sums_k,
+                                    const uint8_t* orders, int32_t* row_ptr, int32_t* col_idx,
+                                    int64_t col_capacity, int32_t* nnz, char* ws, hipStream_t s) {
+  const MaskWs L = mask_workspace_layout(m);
+  float* sum_q = reinterpret_cast<float*>(ws + L.sum_q);
+  float* sum_k = reinterpret_cast<float*>(ws + L.sum_k);
+  float* norm_q = reinterpret_cast<float*>(ws + L.norm_q);
+  float* norm_k = reinterpret_cast<float*>(ws + L.norm_k);
+  const int N = static_cast<int>(m.N);
+  const uint32_t total_blocks = static_cast<uint32_t>(static_cast<int64_t>(m.G) * (m.nq + m.nk));
+  if (m.d == 128)
+    finish_pool_kernel<128><<<total_blocks, 128, 0, s>>>(sums_q, sums_k, m.G, N, m.Bq, m.Bk, m.nq,
+                                                         m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
+  else
+    finish_pool_kernel<64><<<total_blocks, 64, 0, s>>>(sums_q, sums_k, m.G, N, m.Bq, m.Bk, m.nq,
+                                                       m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
+  return select_and_emit(m, orders, row_ptr, col_idx, col_capacity, nnz, ws, s);
 }
 
 }  // namespace bsa

@@ -141,6 +141,75 @@ int bsa_build_mask(const void *Qp, const void *Kp, int32_t dt, int32_t G, int32_
                    int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity, int32_t *nnz,
                    void *workspace, int64_t ws_bytes, void *stream);
 
+/* bsa_build_mask_pooled — bsa_build_mask from per-block channel sums
+ * computed elsewhere (bsa_permute_pool): sums_q fp32 [G][ceil(N/Bq)][d]
+ * over Bq-row blocks of the reordered Q, sums_k fp32 [G][ceil(N/Bk)][d]
+ * over Bk-row blocks of the reordered K, each a running fp32 sum from +0
+ * over the block's rows in increasing order (the block-sum rule above).
+ * Everything else, outputs, workspace and errors as bsa_build_mask; the
+ * result is the same CSR bit for bit. */
+int bsa_build_mask_pooled(const float *sums_q, const float *sums_k, int32_t G, int32_t F, int32_t H,
+                          int32_t W, int32_t d, const uint8_t *axis_order,
+                          const bsa_mask_params *p_host, int32_t *row_ptr, int32_t *col_idx,
+                          int64_t col_capacity, int32_t *nnz, void *workspace, int64_t ws_bytes,
+                          void *stream);
+
+/* bsa_permute_pool — the reordering of bsa_permute (direction 0) fused with
+ * block pooling and, optionally, INT8 quantisation (PAROAttention verdict,
+ * key machinery: the permutation fused into neighbouring kernels; SPADE
+ * verdict, key machinery: fused layout transform and summarisation).  One
+ * pass over the natural src (F32 or BF16, strides as bsa_permute) writes:
+ *   dst   bf16 [G][N][d]            = bsa_permute(0, src, ..., dst BSA_BF16);
+ *         may be NULL (the INT8 path needs only the codes);
+ *   sums  fp32 [G][ceil(N/B)][d]    per-channel block sums of dst over B-row
+ *         blocks (running fp32 sum from +0, rows in increasing order), the
+ *         input of bsa_build_mask_pooled; may be NULL;
+ *   xq    int8 [G][N][d], scale fp32 [G][ceil(N/B)] = bsa_quantize_int8(dst,
+ *         B); both NULL or both given.
+ * At least one of dst, sums, xq is given.  All outputs equal the unfused
+ * calls bit for bit.  B in {64, 128}, d in {64, 128}; src and dst 16-byte
+ * aligned, xq 8-byte aligned.  Errors: EINVAL, EUNSUPPORTED. */
+int bsa_permute_pool(const void *src, int32_t src_dt, void *dst, int64_t nat_stride_g,
+                     int64_t nat_stride_n, int32_t G, int32_t F, int32_t H, int32_t W, int32_t d,
+                     const uint8_t *axis_order, int32_t B, float *sums, int8_t *xq, float *scale,
+                     void *stream);
+
+/* bsa_order_workspace — bytes of device workspace bsa_order_scores needs
+ * for G heads, an F x H x W grid and B-row blocks: 4 * G * 6 * ceil(N/B).
+ * Returns -1 for non-positive sizes, B not in {64, 128} or N >= 2^31. */
+int64_t bsa_order_workspace(int32_t G, int32_t F, int32_t H, int32_t W, int32_t B);
+
+/* bsa_order_scores — online per-head choice of the axis order by the sum
+ * of intra-block cosine similarities (SPADE verdict, key machinery and core
+ * discovery: each candidate blocking is scored by the summed pairwise
+ * cosine similarity inside its blocks, computed from per-block partial sums
+ * in O(B*d); the candidates are the six axis orders of the reordering,
+ * PAROAttention verdict, key machinery).  For head g and order o the
+ * natural src (F32 or BF16, strides as bsa_permute) is reordered and cut
+ * into B-row blocks; each block contributes |sum_r x_r/|x_r|| ^2, the sum of
+ * cos(x_a, x_b) over its ordered row pairs a, b (a == b included; an all-
+ * zero row counts as a zero vector).  scores fp32 [G][6] receives, per
+ * (g, o), this fixed fp32 sequence:
+ *   n_r  = fmaf chain over channels of x^2 from +0;  inv_r = 1/sqrtf(n_r)
+ *          (each correctly rounded; inv_r = 0 when n_r == 0);
+ *   u_c  = fmaf chain over the block's rows (increasing) of x_rc*inv_r;
+ *   q_b  = fmaf chain over channels of u_c^2;
+ *   score = running fp32 sum of q_b over blocks in increasing order.
+ * workspace: device, >= bsa_order_workspace bytes, 4-byte aligned; its
+ * contents are scratch.  src 16-byte aligned.  d in {64, 128}, B in
+ * {64, 128}.  Errors: EINVAL, EUNSUPPORTED, ECAPACITY (workspace short). */
+int bsa_order_scores(const void *src, int32_t src_dt, int64_t nat_stride_g, int64_t nat_stride_n,
+                     int32_t G, int32_t F, int32_t H, int32_t W, int32_t d, int32_t B, float *scores,
+                     void *workspace, int64_t ws_bytes, void *stream);
+
+/* bsa_select_orders — axis_order[g] (uint8, device) = the order code o
+ * maximising scores_a[g][o] + scores_b[g][o] (one rounded fp32 add; when
+ * scores_b is NULL, scores_a alone), ties to the lowest code.  Passing the
+ * scores of Q as scores_a and of K as scores_b picks the order under which
+ * both are most block-coherent.  Errors: EINVAL. */
+int bsa_select_orders(const float *scores_a, const float *scores_b, int32_t G, uint8_t *axis_order,
+                      void *stream);
+
 /* bsa_quantize_int8 — block-wise symmetric INT8 (PAROAttention verdict, key
  * machinery: quantisation blocks aligned to the attention block).  For each
  * (g, block b) of B rows (real rows only): amax = max|x|; amax == 0 gives

@@ -52,6 +52,7 @@ def _load():
                                        _I, _P, _L, _P, _P]),
         "oracle_int8_qk_tile": (_I, [_P, _P, _I, _L, _I, _I, _I, _L, _L, _P]),
         "oracle_int8_pv_tile": (_I, [_P, _P, _I, _L, _I, _I, _I, _L, _P]),
+        "oracle_sics_scores": (_I, [_P, _I, _L, _L, _I, _I, _I, _I, _I, _I, _P]),
         "oracle_num_threads": (_I, []),
     }
     for name, (res, args) in sig.items():
@@ -205,6 +206,28 @@ def quantize_int8(Xp: np.ndarray, B: int):
     s = np.empty((G, nb), dtype=np.float32)
     _check(_load().oracle_quantize_int8(_ptr(Xp), G, N, d, B, _ptr(q), _ptr(s)), "quantize_int8")
     return q, s
+
+
+def sics_scores(X, G, F, H, W, d, B, stride_g=None, stride_n=None):
+    """SPADE's online blocking score for each (head, PARO axis order): the
+    fp32 closed-form sum of intra-block cosine similarities, [G][6] fp32.
+    X: natural-order fp32 or bf16 (uint16) array, default [N][G][d]."""
+    if stride_g is None:
+        stride_g, stride_n = d, G * d
+    X = np.ascontiguousarray(X)
+    out = np.empty((G, 6), dtype=np.float32)
+    _check(_load().oracle_sics_scores(_ptr(X), _dtype_code(X), stride_g, stride_n, G, F, H, W, d,
+                                      B, _ptr(out)), "sics_scores")
+    return out
+
+
+def select_orders(scores_a, scores_b=None):
+    """Per head, the order code with the largest fp32 scores_a + scores_b;
+    ties go to the lowest code (numpy's argmax returns the first maximum)."""
+    s = np.asarray(scores_a, dtype=np.float32)
+    if scores_b is not None:
+        s = s + np.asarray(scores_b, dtype=np.float32)
+    return np.argmax(s, axis=1).astype(np.uint8)
 
 
 def attention_rows(Q, K, V, G, F, H, W, d, orders, rows, Bq=64, Bk=64, row_ptr=None,

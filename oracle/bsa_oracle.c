@@ -429,6 +429,64 @@ int oracle_quantize_int8(const uint16_t *X, int G, int64_t N, int d, int B, int8
 }
 
 /* ------------------------------------------------------------------------
+ * Online axis-order choice by the sum of intra-block cosine similarities.
+ * [SPADE] key machinery and core discovery: a candidate blocking of a
+ * head's tokens is scored by the summed pairwise cosine similarity inside
+ * its blocks, computed online in O(block * d) from per-block sums, and the
+ * highest-scoring candidate is used.  Candidates: the six axis orders of
+ * [PARO] key machinery, each cut into blocks of B consecutive reordered
+ * tokens.  Since cos(a, b) = <a/|a|, b/|b|>, the sum over ordered pairs of a
+ * block (self-pairs included) is |sum of the block's unit rows|^2; an
+ * all-zero row is taken as the zero vector.
+ * fp32 sequence (the choice is an integer decided by it): per row,
+ *   n = fmaf chain of x_c^2 over channels from +0, inv = 1/sqrtf(n) (or 0);
+ * per block, u_c = fmaf chain over rows in increasing position of x_c*inv,
+ *   q = fmaf chain of u_c^2 over channels;
+ * score[g][o] = running sum of q over blocks in increasing order.
+ * X: element (n, g, c) at n*stride_n + g*stride_g + c, type OR_F32/OR_BF16.
+ * ---------------------------------------------------------------------- */
+int oracle_sics_scores(const void *X, int dt, int64_t stride_g, int64_t stride_n, int G, int F,
+                       int H, int W, int d, int B, float *scores) {
+  if (!X || !scores || G <= 0 || F <= 0 || H <= 0 || W <= 0 || d <= 0 || B <= 0) return -1;
+  if (dt != OR_F32 && dt != OR_BF16) return -1;
+  const int64_t N = (int64_t)F * H * W;
+  const int64_t nb = (N + B - 1) / B;
+  int32_t *perm = (int32_t *)malloc(sizeof(int32_t) * (size_t)N * 6);
+  if (!perm) return -2;
+  for (int o = 0; o < 6; o++) oracle_perm(o, F, H, W, perm + (int64_t)o * N);
+  int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int g = 0; g < G; g++)
+    for (int o = 0; o < 6; o++) {
+      float *u = (float *)malloc(sizeof(float) * (size_t)d);
+      if (!u) { bad = 1; continue; }
+      const int32_t *pm = perm + (int64_t)o * N;
+      float score = 0.0f;
+      for (int64_t b = 0; b < nb; b++) {
+        for (int c = 0; c < d; c++) u[c] = 0.0f;
+        const int64_t r1 = (b + 1) * B < N ? (b + 1) * B : N;
+        for (int64_t p = b * B; p < r1; p++) {
+          const int64_t base = (int64_t)pm[p] * stride_n + (int64_t)g * stride_g;
+          float n2 = 0.0f;
+          for (int c = 0; c < d; c++) {
+            const float x = (float)load_elem(X, dt, base + c);
+            n2 = fmaf(x, x, n2);
+          }
+          const float inv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+          for (int c = 0; c < d; c++) u[c] = fmaf((float)load_elem(X, dt, base + c), inv, u[c]);
+        }
+        float q = 0.0f;
+        for (int c = 0; c < d; c++) q = fmaf(u[c], u[c], q);
+        score = score + q;
+      }
+      scores[g * 6 + o] = score;
+      free(u);
+    }
+  free(perm);
+  return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------
  * Masked softmax attention, fp64, on natural-order inputs.
  * [SPADE] referee minor comment on §2.2 Eq. (2): the block mask is additive,
  * 0 on kept block pairs and -inf on pruned ones.  Token n of head g may see

@@ -34,7 +34,9 @@ def test_header_lists_the_entry_points():
     names = header_functions()
     for n in ("bsa_permute", "bsa_build_mask", "bsa_forward", "bsa_forward_int8",
               "bsa_quantize_int8", "bsa_mask_capacity", "bsa_mask_workspace",
-              "bsa_debug_int8_qk", "bsa_debug_int8_pv", "bsa_abi_version", "bsa_last_error"):
+              "bsa_debug_int8_qk", "bsa_debug_int8_pv", "bsa_abi_version", "bsa_last_error",
+              "bsa_permute_pool", "bsa_build_mask_pooled", "bsa_order_workspace",
+              "bsa_order_scores", "bsa_select_orders"):
         assert n in names
 
 
@@ -107,3 +109,33 @@ def test_argument_errors_before_any_launch(lib):
     assert b"col_capacity" in lib.bsa_last_error()
     assert lib.bsa_build_mask(fake, fake, 0, 1, 4, 8, 8, 64, fake, ctypes.byref(p), fake, fake,
                               1 << 20, fake, P(0x1000), 1 << 20, None) == -2
+
+
+def test_fused_and_order_argument_errors(lib):
+    """Host checks of the fused pass, the pooled mask build and the order
+    scores; none of these calls reaches HIP."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    # permute_pool: no output at all, xq without scale, bad B, misaligned dst
+    assert lib.bsa_permute_pool(fake, 1, None, 8, 64, 1, 2, 4, 8, 64, fake, 64, None, None, None,
+                                None) == -1
+    assert b"no output" in lib.bsa_last_error()
+    assert lib.bsa_permute_pool(fake, 1, fake, 8, 64, 1, 2, 4, 8, 64, fake, 64, None, fake, None,
+                                None) == -1
+    assert lib.bsa_permute_pool(fake, 1, fake, 8, 64, 1, 2, 4, 8, 64, fake, 32, None, None, None,
+                                None) == -2
+    assert lib.bsa_permute_pool(fake, 1, P(0x1008), 8, 64, 1, 2, 4, 8, 64, fake, 64, None, None,
+                                None, None) == -1
+    # build_mask_pooled: capacity too small
+    from block_sparse_attention_inverse_amd._lib import MaskParams
+
+    p = MaskParams(64, 64, 0, 30, 100, 1, -1, 0)
+    assert lib.bsa_build_mask_pooled(fake, fake, 1, 4, 8, 8, 64, fake, ctypes.byref(p), fake, fake,
+                                     1, fake, P(0x1000), 1 << 20, None) == -3
+    # order scores: workspace size and a short workspace
+    assert lib.bsa_order_workspace(40, 21, 45, 80, 128) == 4 * 40 * 6 * 591
+    assert lib.bsa_order_workspace(1, 2, 3, 4, 96) == -1
+    assert lib.bsa_order_scores(fake, 1, 8, 64, 1, 2, 4, 8, 64, 64, fake, fake, 4, None) == -3
+    assert b"workspace" in lib.bsa_last_error()
+    assert lib.bsa_order_scores(fake, 2, 8, 64, 1, 2, 4, 8, 64, 64, fake, fake, 1 << 20, None) == -2
+    assert lib.bsa_select_orders(None, None, 4, fake, None) == -1

@@ -294,6 +294,129 @@ def test_build_mask_composes(orc):
         assert ties >= 0
 
 
+# ------------------------------------------------------- SICS order scores
+def _sics_pairwise_f64(X, G, F, H, W, B):
+    """Sum over blocks of cos(x_a, x_b) over ordered pairs (a == b included)
+    by brute force: an fp64 Gram matrix of unit rows (a zero row is the zero
+    vector), the pairs summed block by block.  Also returns the per-block
+    values and the unordered, self-excluded variant."""
+    N, _, d = X.shape
+    Xd = np.asarray(X, np.float64)
+    out = np.zeros((G, 6)), np.zeros((G, 6))
+    per_block = {}
+    for g in range(G):
+        nrm = np.sqrt((Xd[:, g, :] ** 2).sum(axis=1))
+        U = np.where(nrm[:, None] > 0, Xd[:, g, :] / np.where(nrm > 0, nrm, 1)[:, None], 0.0)
+        for o in range(6):
+            pm = np.array(brute.perm(o, F, H, W))
+            qs = []
+            for b in range(-(-N // B)):
+                rows = U[pm[b * B:(b + 1) * B]]
+                gram = rows @ rows.T
+                qs.append(gram.sum())
+                out[1][g, o] += (gram.sum() - np.trace(gram)) / 2
+            out[0][g, o] = math.fsum(qs)
+            per_block[g, o] = np.array(qs)
+    return out[0], out[1], per_block
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_sics_pairwise_brute_force(orc, dt):
+    """fp32 closed form vs the pairwise-cosine definition in fp64, within a
+    first-order rounding bound; includes all-zero rows and a tail block."""
+    r = rng(21)
+    G, F, H, W, d, B = 2, 3, 4, 5, 16, 8  # N = 60: 7 full blocks + 4-row tail
+    N = F * H * W
+    X = r.standard_normal((N, G, d)).astype(np.float32)
+    X[7] = 0.0
+    X[33, 1] = 0.0
+    if dt == "bf16":
+        X = to_bf16_bits(X)
+    got = orc.sics_scores(X, G, F, H, W, d, B)
+    Xv = bits_to_f64(X) if dt == "bf16" else X
+    want, _, per_block = _sics_pairwise_f64(Xv, G, F, H, W, B)
+    u = 2.0**-24
+    eps = (B + d / 2 + 3) * u
+    for g in range(G):
+        for o in range(6):
+            q = per_block[g, o]
+            nb = q.size
+            bound = (np.sum(2 * eps * B * np.sqrt(q) + (d + 1) * u * q) + nb * u * want[g, o]) * 1.5
+            assert abs(float(got[g, o]) - want[g, o]) <= bound, (g, o, got[g, o], want[g, o], bound)
+
+
+def test_sics_one_hot_rows_exact(orc):
+    """Rows +-e_k: unit rows are exact, so each block's value is the exact
+    integer sum over channels of (sum of signs landing on that channel)^2."""
+    r = rng(22)
+    G, F, H, W, d, B = 2, 5, 6, 7, 64, 64  # N = 210: 3 full blocks + 18-row tail
+    N = F * H * W
+    pos = r.integers(0, 8, size=(N, G))
+    sign = r.choice([-1.0, 1.0], size=(N, G))
+    X = np.zeros((N, G, d), np.float32)
+    for n in range(N):
+        for g in range(G):
+            X[n, g, pos[n, g]] = sign[n, g] * 3.0
+    got = orc.sics_scores(X, G, F, H, W, d, B)
+    for g in range(G):
+        for o in range(6):
+            pm = brute.perm(o, F, H, W)
+            total = 0
+            for b in range(-(-N // B)):
+                acc = [0] * d
+                for p in pm[b * B:(b + 1) * B]:
+                    acc[pos[p, g]] += int(sign[p, g])
+                total += sum(a * a for a in acc)
+            assert float(got[g, o]) == float(total)
+
+
+@pytest.mark.parametrize("axis", ["F", "H", "W"])
+def test_sics_planted_constant_axis(orc, axis):
+    """Tokens that do not vary along one axis whose extent is B: the two
+    orders with that axis innermost put B copies of one vector in every
+    block (value B^2 each, nb*B^2 in all) and win; the others mix
+    independent vectors (about B per block)."""
+    r = rng(23)
+    B, d, G = 8, 32, 2
+    dims = {"F": 3, "H": 4, "W": 5}
+    dims[axis] = B
+    F, H, W = dims["F"], dims["H"], dims["W"]
+    N = F * H * W
+    base = r.standard_normal((F, H, W, G, d)).astype(np.float32)
+    ax = "FHW".index(axis)
+    base = np.repeat(np.take(base, [0], axis=ax), dims[axis], axis=ax)
+    X = base.reshape(N, G, d)
+    got = orc.sics_scores(X, G, F, H, W, d, B)
+    nb = N // B
+    winners = [o for o, name in enumerate(brute.ORDER_NAMES) if name[2] == axis]
+    for g in range(G):
+        for o in range(6):
+            if o in winners:
+                assert abs(float(got[g, o]) - nb * B * B) <= 1e-4 * nb * B * B
+            else:
+                assert float(got[g, o]) < 0.5 * nb * B * B
+        assert orc.select_orders(got)[g] in winners
+    # the unordered, self-excluded count is an increasing affine map of the
+    # ordered one (same number of nonzero rows in every order): same winner
+    ordered, unordered, _ = _sics_pairwise_f64(X, G, F, H, W, B)
+    assert np.allclose(unordered, (ordered - N) / 2, rtol=1e-12, atol=1e-9)
+    assert np.array_equal(np.argmax(ordered, 1), np.argmax(unordered, 1))
+
+
+def test_select_orders_ties_and_sum():
+    """Ties go to the lowest code; the choice uses the fp32 sum of both."""
+    import oracle
+
+    a = np.array([[1, 1, 1, 1, 1, 1], [0, 2, 2, 0, 0, 0], [5, 0, 0, 0, 0, 6]], np.float32)
+    b = np.array([[0, 0, 0, 0, 0, 0], [0, 0, 0, 0, 0, 0], [2, 0, 0, 0, 0, 0]], np.float32)
+    assert oracle.select_orders(a).tolist() == [0, 1, 5]
+    assert oracle.select_orders(a, b).tolist() == [0, 1, 0]
+    # 2^24 + 1 is not an fp32 value: the sum rounds to a tie, lowest code wins
+    a2 = np.array([[2.0**24, 2.0**24, 0, 0, 0, 0]], np.float32)
+    b2 = np.array([[0, 1, 0, 0, 0, 0]], np.float32)
+    assert oracle.select_orders(a2, b2).tolist() == [0]
+
+
 # ------------------------------------------------------------- quantisation
 def test_quantize_invariants(orc):
     r = rng(10)
