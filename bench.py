@@ -150,7 +150,8 @@ def main():
     Q, K, V = synth.cast_inputs(cfg, *synth.make_qkv(cfg, orders, seed, device="cuda"))
     od = torch.from_numpy(orders).cuda()
     p = bsa.mask_params(cfg["Bq"], cfg["Bk"], 0, cfg["rho"], True)
-    plan = bsa.LayerPlan(G, F, H, W, d, "cuda", p, int8=not args.no_int8)
+    plan = bsa.LayerPlan(G, F, H, W, d, "cuda", p, fused=True)
+    plan8 = None if args.no_int8 else bsa.LayerPlan(G, F, H, W, d, "cuda", p, int8=True, fused=True)
     torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device="cuda").fill_(1)
@@ -162,6 +163,20 @@ def main():
         del src, dst
 
     def step_bf16(ev=None):
+        # reorder with the block sums of Q and K in the same pass
+        plan.reorder_fused(Q, K, V, od)
+        if ev:
+            ev[0].record()
+        plan.build_mask_from_sums(od)
+        if ev:
+            ev[1].record()
+        bsa.forward(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk,
+                    out=plan.Op, lse=plan.lse)
+        if ev:
+            ev[2].record()
+        bsa.permute(plan.Op, od, F, H, W, 1, out=plan.O)
+
+    def step_bf16_unfused(ev=None):
         bsa.permute(Q, od, F, H, W, 0, out=plan.Qp)
         bsa.permute(K, od, F, H, W, 0, out=plan.Kp)
         bsa.permute(V, od, F, H, W, 0, out=plan.Vp)
@@ -177,18 +192,26 @@ def main():
         bsa.permute(plan.Op, od, F, H, W, 1, out=plan.O)
 
     def step_int8(ev=None):
-        bsa.permute(Q, od, F, H, W, 0, out=plan.Qp)
-        bsa.permute(K, od, F, H, W, 0, out=plan.Kp)
-        bsa.permute(V, od, F, H, W, 0, out=plan.Vp)
-        plan.build_mask(od)
-        plan.quantize()
+        # one pass per tensor: INT8 codes and scales (+ Q/K block sums)
+        plan8.reorder_fused(Q, K, V, od)
+        plan8.build_mask_from_sums(od)
         if ev:
             ev[0].record()
-        bsa.forward_int8(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq, plan.sV, plan.row_ptr,
-                         plan.col_idx, p.Bq, p.Bk, out=plan.Op, lse=plan.lse)
+        bsa.forward_int8(plan8.Qq, plan8.sQ, plan8.Kq, plan8.sK, plan8.Vq, plan8.sV,
+                         plan8.row_ptr, plan8.col_idx, p.Bq, p.Bk, out=plan8.Op, lse=plan8.lse)
         if ev:
             ev[1].record()
-        bsa.permute(plan.Op, od, F, H, W, 1, out=plan.O)
+        bsa.permute(plan8.Op, od, F, H, W, 1, out=plan8.O)
+
+    sics_ws = torch.empty(bsa.order_workspace(G, F, H, W, min(p.Bq, p.Bk)), dtype=torch.uint8,
+                          device="cuda")
+    sq_buf = torch.empty((G, 6), dtype=torch.float32, device="cuda")
+    sk_buf = torch.empty_like(sq_buf)
+
+    def step_sics(ev=None):
+        bsa.order_scores(Q, F, H, W, p.Bq, out=sq_buf, workspace=sics_ws)
+        bsa.order_scores(K, F, H, W, p.Bk, out=sk_buf, workspace=sics_ws)
+        bsa.select_orders(sq_buf, sk_buf)
 
     def timed(step, nev, label):
         for _ in range(args.warmup):
@@ -210,6 +233,10 @@ def main():
 
     log("[bench] bf16 chain")
     wall, seg = timed(step_bf16, 3, "bf16")
+    log("[bench] bf16 chain, unfused reorder and pooling")
+    wall_u, seg_u = timed(step_bf16_unfused, 3, "bf16 unfused")
+    log("[bench] SICS order selection")
+    wall_s, _ = timed(step_sics, 0, "sics")
     rp_h = plan.row_ptr.cpu().numpy()
     nnz = int(plan.nnz.item())
     ci_h = plan.col_idx[:nnz].cpu().numpy()
@@ -251,11 +278,17 @@ def main():
             "traffic": traffic,
         },
         "breakdown_ms": {
-            "reorder_qkv": float(seg[0]),
-            "build_mask": float(seg[1]),
+            "reorder_qkv_with_qk_block_sums": float(seg[0]),
+            "build_mask_from_sums": float(seg[1]),
             "attention": float(seg[2]),
             "inverse_reorder_and_gaps": float(wall * 1e3 - seg.sum()),
         },
+        "unfused_ms": {
+            "step": wall_u * 1e3,
+            "reorder_qkv": float(seg_u[0]),
+            "build_mask_with_pooling": float(seg_u[1]),
+        },
+        "order_selection_ms": wall_s * 1e3,
         "kept_tflops_attention": achieved,
         "dense_equiv_tflops_attention": dense / t_fwd / 1e12,
     }
