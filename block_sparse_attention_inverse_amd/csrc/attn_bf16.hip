@@ -6,36 +6,55 @@
 // additive (0 on kept, -inf on pruned block pairs).
 //
 // Work split: one workgroup per (head g, q-block i); Bq/64 waves, each wave
-// owns 64 query rows as two 32-row halves, so every K and V operand read
-// from LDS feeds two MFMAs.  One wave per SIMD (two workgroups per CU): the
-// 64-row waves keep LDS read traffic at half of what 32-row waves need.
+// owns 64 query rows as two 32-row halves (qb), so every K and V operand
+// read from LDS feeds two MFMAs.  One wave per SIMD (two workgroups per CU).
 //
-// Per 64-row kv sub-tile (a 128-wide kv-block is two sub-tiles):
-//   S^T = K . Q^T     v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q
-//                     fragments in registers; the accumulator holds one query
-//                     row per lane (the two wave halves share a row).
-//   online softmax    in registers: one cross-half exchange per row max; row
-//                     sums stay per lane until the end (bf16 dot2 with 1s);
-//                     the reference max is raised only when a tile exceeds
-//                     it by 2^8, so the O rescale is rare and O = acc/l stays
-//                     exact.
-//   O^T += V^T . P^T  A = V^T read with ds_read_b64_tr_b16 from row-major V
-//                     (a 16-lane group reads a 4x16 block and receives it
-//                     transposed), B = P converted to bf16 in registers.
-// Both operands of an MFMA map the reduction index to slots the same way, so
-// the kv order inside a k-step only has to agree between P and V^T: P slot j
-// of lane half h carries kv 16s + 8(j/4) + 4h + j%4, which is what two
-// transposed reads at rows 16s + 4h and 16s + 8 + 4h return.
+// Products (v_mfma_f32_32x32x16_bf16), per 32-row kv half-tile u:
+//   S_u^T = K_u . Qc^T - m   A = K rows from LDS, B = Q fragments held in
+//                            registers, pre-scaled by c = sm_scale*log2(e);
+//                            the accumulator starts at -m (the row's running
+//                            reference), so the scores arrive in log2 units
+//                            relative to m: P = exp2(S) needs no VALU op
+//                            besides the exponential.  Every lane holds one
+//                            query row; lane half h, slot r carries kv
+//                            8(r/4) + 4h + r%4 of the half.
+//   O^T += V_u^T . P_u^T     A = V^T read with ds_read_b64_tr_b16 (the
+//                            transposing LDS read) from row-major V, B = P
+//                            converted to bf16 in registers: slots 8s..8s+7
+//                            of a lane are exactly the kv indices that the two
+//                            transposed reads at rows 16s + 4h and 16s + 8 + 4h
+//                            return, so P never moves between lanes.
 //
-// Pipeline (one barrier per sub-tile): iteration t issues the global->LDS
-// loads of K(t+2) and V(t+1), computes S(t+1) = K(t+1).Q^T, its softmax, and
-// O += P(t).V(t), so the MFMA stream of both products covers the softmax.
-// K and V move global -> LDS directly (16-byte global_load_lds).  LDS chunk
-// c of row r sits at c ^ (r mod 16) for K and c ^ (2r mod 16) for V, which
-// makes the MFMA operand reads conflict-free; the swizzle is realised by
-// choosing which global chunk each lane fetches.  A ragged last sub-tile is
-// loaded as the 64-row window that ends at row N (all rows real) and its
-// columns outside the sub-tile are masked.
+// Software pipeline, one step per half-tile u: the MFMA stream alternates
+// S_{u+1} = K_{u+1}.Qc^T and O += P_{u-1}.V_{u-1}, and under it the VALU
+// computes P_u = exp2(S_u), its bf16 pairs and row sums, one score per MFMA,
+// so the exponentials are spread over both products.  Two S and two P
+// register sets alternate between steps.
+//
+// Reference m: the first half-tile of a row sets it to the exact row maximum;
+// afterwards it only moves when a half-tile's row sum exceeds 2^16 (scores
+// rose far above m), in a rare uniform branch that raises m to the exact
+// maximum, redoes that half's exponentials, and rescales O and l.  O = acc / l
+// does not depend on m, so the only requirement on m is that no exponent
+// overflows.  The first half-tile of a row whose columns are all masked
+// leaves m unset until a real column arrives.
+//
+// K and V move HBM -> LDS in 64-row sub-tiles with 16-byte buffer loads that
+// write LDS directly, double-buffered (64 KB per workgroup).  LDS chunk c of
+// row r sits at c ^ (r mod 16) for K and c ^ (2r mod 16) for V, which makes
+// the operand reads conflict-free; the swizzle is realised by choosing which
+// global chunk each lane fetches.  The second step of a sub-tile issues the
+// loads of K two sub-tiles ahead and V one ahead; one barrier per sub-tile.
+// The kv-block index of each sub-tile reaches the scalar unit through a
+// vector load issued a sub-tile ahead (so no scalar memory load is pending
+// while LDS operand reads are waited on).  A ragged last sub-tile is loaded
+// as the 64-row window that ends at row N (all rows real) and its columns
+// outside the sub-tile are masked.
+//
+// Grid order: workgroup b runs on XCD b mod 8; XCD x takes q-blocks
+// [x*per, (x+1)*per) of every head, heads in order, so all XCDs work on one
+// head at a time (its K/V stays in the shared last-level cache) while each
+// XCD's L2 serves neighbouring q-blocks.
 #include <utility>
 
 #include "bsa_device.hpp"
@@ -46,25 +65,18 @@ namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int KT = 64;          // kv rows per sub-tile
-constexpr float kTau = 8.0f;    // lazy-rescale threshold of the first tile, log2 units
-constexpr float kRefInit = -1.0e30f;    // reference before any score: finite, below every score
-constexpr float kSumBound = 65536.0f;   // tile row-half sum that raises the reference
+constexpr int KT = 64;                  // kv rows per staged sub-tile
+constexpr float kSumBound = 0x1p96f;    // half-tile row sum that flags overflow
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-#ifndef BSA_PF_A
-#define BSA_PF_A 2
+#ifndef BSA_PF
+#define BSA_PF 2
 #endif
-#ifndef BSA_PF_B
-#define BSA_PF_B 2
-#endif
-constexpr int kPfA = BSA_PF_A;  // LDS operand prefetch distance (MFMA steps), S = K.Q^T
-constexpr int kPfB = BSA_PF_B;  // same for O += P.V
-#ifndef BSA_LOAD_STEPS
-#define BSA_LOAD_STEPS 0
+constexpr int kPf = BSA_PF;             // LDS operand prefetch distance (operands)
+#ifndef BSA_QSCALE
+#define BSA_QSCALE 0
 #endif
 
 template <int D, int NW>
@@ -75,6 +87,10 @@ struct Ly {
   static constexpr int RPI = 1024 / ROWB;      // rows per wave-wide 1 KB load
   static constexpr int NI = TB / 1024 / NW;    // loads per wave per sub-tile
   static constexpr int RW = NW * RPI;          // rows covered by one load of all waves
+  static constexpr int KS = D / 16;            // k-steps of S (and K operands per half)
+  static constexpr int DB = D / 32;            // 32-channel blocks of O
+  static constexpr int NV = 2 * DB;            // V operands per half
+  static constexpr int NS = D / 4;             // MFMA slots per step (KS*2 + NV*2)
 };
 
 // Where a sub-tile's rows come from: window start (all rows real when
@@ -87,10 +103,8 @@ struct Tile {
 };
 
 template <int BK>
-__device__ __forceinline__ Tile tile_of(const int32_t* __restrict__ col_idx, int64_t e0, int t,
-                                        int N, int nk) {
+__device__ __forceinline__ Tile make_tile(int j, int t, int N, int nk) {
   constexpr int SUB = BK / KT;
-  const int j = col_idx[e0 + t / SUB];
   Tile T;
   T.valid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
   T.kv0 = T.valid ? j * BK + (t % SUB) * KT : 0;
@@ -100,124 +114,28 @@ __device__ __forceinline__ Tile tile_of(const int32_t* __restrict__ col_idx, int
 }
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+template <typename T>
+__device__ __forceinline__ void opaque(T& x) { asm volatile("" : "+v"(x)); }
 
-template <int D, int NW>
-__device__ __forceinline__ void qk(const uint8_t* kt, uint32_t kread, const bf16x8 (&qf)[2][D / 16],
-                                   f32x16 (&s)[2][2]) {
-  using L = Ly<D, NW>;
-#pragma unroll
-  for (int b = 0; b < 2; b++) {
-    s[0][b] = f32x16{};
-    s[1][b] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ks++) {
-      const bf16x8 a =
-          *reinterpret_cast<const bf16x8*>(kt + b * 32 * L::ROWB + (kread ^ (ks << 5)));
-      s[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][ks], s[0][b], 0, 0, 0);
-      s[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][ks], s[1][b], 0, 0, 0);
-    }
-  }
+// S accumulation as VGPR-form MFMAs written out explicitly, so that the
+// scores land in VGPRs (where the exponentials read them) while O stays in
+// AGPRs and the Q fragments are read from AGPRs.  The compiler does not see
+// these as MFMAs: every VALU access to a score register within 24 wait
+// states of its MFMA is preceded by mfma_drain().
+__device__ __forceinline__ void mfma_s_init(f32x16& d, const bf16x8& a, const bf16x8& b,
+                                            const f32x16& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
 }
-
-template <int D, int NW>
-__device__ __forceinline__ void pv(const uint8_t* vt, uint32_t vread, const bf16x8 (&p)[2][4],
-                                   f32x16 (&o)[2][D / 32]) {
-  using L = Ly<D, NW>;
-#pragma unroll
-  for (int db = 0; db < D / 32; db++) {
-    const uint32_t cb = vread ^ (db << 6);
-#pragma unroll
-    for (int st = 0; st < 4; st++) {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS i16x4*)(vt + (16 * st) * L::ROWB + cb));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS i16x4*)(vt + (16 * st + 8) * L::ROWB + cb));
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[0][st], o[0][db], 0, 0, 0);
-      o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[1][st], o[1][db], 0, 0, 0);
-    }
-  }
+__device__ __forceinline__ void mfma_s_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
-
-// Online softmax of one sub-tile.  Raw scores s; c = sm_scale*log2(e).
-// Updates the reference max m (log2 units) and per-lane partial row sums l,
-// writes P (bf16) and the O rescale factors; returns whether any row of
-// this lane raised its reference.
-template <bool MASK>
-__device__ __forceinline__ bool softmax(f32x16 (&s)[2][2], const Tile& T, int N, float c,
-                                        float (&m)[2], float (&l)[2], bf16x8 (&p)[2][4],
-                                        float (&alpha)[2]) {
-  const int h = (threadIdx.x & 63) >> 5;
-  bool upd_any = false;
-#pragma unroll
-  for (int qb = 0; qb < 2; qb++) {
-    if constexpr (MASK) {
-#pragma unroll
-      for (int b = 0; b < 2; b++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int kv = T.win + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (!T.valid || kv < T.kv0 || kv >= N) s[qb][b][r] = -INFINITY;
-        }
-    }
-    float mt = s[qb][0][0];
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) mt = fmaxf(mt, s[qb][b][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mt2 = mt * c;
-    const bool upd = mt2 > m[qb] + kTau;
-    alpha[qb] = upd ? __builtin_amdgcn_exp2f(m[qb] - mt2) : 1.0f;
-    m[qb] = upd ? mt2 : m[qb];
-    upd_any |= upd;
-    const float ref = m[qb];
-    float sum = 0.0f;
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r], c, -ref));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r + 1], c, -ref));
-        const bf16x2 pr = (bf16x2){static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
-        p[qb][2 * b + (r >> 3)][r & 7] = pr[0];
-        p[qb][2 * b + (r >> 3)][(r & 7) + 1] = pr[1];
-        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, (bf16x2){static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)}, sum, false);
-      }
-    l[qb] = l[qb] * alpha[qb] + sum;
-  }
-  return upd_any;
-}
-
-template <int D>
-__device__ __forceinline__ void rescale(f32x16 (&o)[2][D / 32], const float (&alpha)[2]) {
-#pragma unroll
-  for (int qb = 0; qb < 2; qb++)
-#pragma unroll
-    for (int db = 0; db < D / 32; db++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) o[qb][db][r] *= alpha[qb];
-}
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // max of x over the two 32-lane halves (a row is split across them)
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-template <int D, int NW>
-__device__ __forceinline__ bf16x8 k_operand(const uint8_t* kt, uint32_t kread, int b, int ks) {
-  return *reinterpret_cast<const bf16x8*>(kt + b * 32 * Ly<D, NW>::ROWB + (kread ^ (ks << 5)));
-}
-
-template <int D, int NW>
-__device__ __forceinline__ bf16x8 v_operand(const uint8_t* vt, uint32_t vread, int st, int db) {
-  using L = Ly<D, NW>;
-  const uint32_t cb = vread ^ (db << 6);
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + (16 * st) * L::ROWB + cb));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + (16 * st + 8) * L::ROWB + cb));
-  return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
 // Lane offsets of the global->LDS loads.  Load q of wave w writes LDS bytes
@@ -256,170 +174,274 @@ struct Stage {
   }
 };
 
-template <int D, int NW, bool ISV, bool SMALLN>
-__device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int win, int q,
+template <int D, int NW>
+__device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int win, int q,
                                          uint8_t* tile) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const uint32_t soff = static_cast<uint32_t>(win * Ly<D, NW>::ROWB + q * NW * 1024);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(tile + (q * NW + w) * 1024), 16,
-                                           voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(tile + (q * NW + w) * 1024), 16, voff,
+                                           soff, 0, 0);
+}
+// load q of the staging of a K (ISV false) or V sub-tile whose window starts at row win
+template <int D, int NW, bool ISV, bool SMALLN>
+__device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, const Stage<D, NW>& sg, int N,
+                                         int win, int q, uint8_t* tile) {
+  load_raw<D, NW>(rsrc, sg.template lane_off<ISV, SMALLN>(q, N), win, q, tile);
 }
 
 template <int D, int NW, bool SMALLN>
-__device__ __forceinline__ void stage_all(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                          const Stage<D, NW>& sg, const Tile& T, int N, uint8_t* kt,
-                                          uint8_t* vt) {
+__device__ __forceinline__ void stage_tile(__amdgpu_buffer_rsrc_t rs, const Stage<D, NW>& sg, int N,
+                                           int win, uint8_t* tile, bool isv) {
 #pragma unroll
   for (int q = 0; q < Ly<D, NW>::NI; q++) {
-    if (kt) load_one<D, NW, false, SMALLN>(kr, sg.template lane_off<false, SMALLN>(q, N), T.win, q, kt);
-    if (vt) load_one<D, NW, true, SMALLN>(vr, sg.template lane_off<true, SMALLN>(q, N), T.win, q, vt);
+    if (isv) load_one<D, NW, true, SMALLN>(rs, sg, N, win, q, tile);
+    else load_one<D, NW, false, SMALLN>(rs, sg, N, win, q, tile);
   }
 }
 
-__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
-// Pins a value's computation to this point of the instruction stream (an
-// empty volatile asm that reads and rewrites it).
-__device__ __forceinline__ void anchor(float& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void anchor(uint32_t& x) { asm volatile("" : "+v"(x)); }
-
-// One steady-state iteration, in an explicit instruction order:
-//   phase A: S(t+1) = K(t+1).Q^T — 2*(D/16) steps of 2 MFMAs (alternating kv
-//            halves so that four accumulation chains are in flight); step x
-//            reads the K operand of step x+2 and issues a share of the
-//            global->LDS loads of K(t+2) and V(t+1);
-//   phase B: O += P(t).V(t) — 4*(D/32) steps of 2 MFMAs with the V operands
-//            read two steps ahead; the softmax of S(t+1) is cut into as many
-//            slices, one per step (row maxima in the first two, then the
-//            exponentials, bf16 packing and row sums).
-// A scheduling fence closes every step and each slice's results are pinned
-// inside it, so the compiler cannot regroup the stream.
-// exponentials of score pair pp (of 32: row half pp/16, kv half (pp/8)%2,
-// accumulator slots 2(pp%8), +1) against reference m, their sum, and their
-// bf16 pair as word pp%4 of P[pp/16][(pp%16)/4]
-__device__ __forceinline__ void exp_pair(const f32x16 (&s)[2][2], float c, const float (&m)[2],
-                                         int pp, float (&sum)[2], u32x4 (&pw)[2][4]) {
-  const int qb = pp >> 4, b = (pp >> 3) & 1, r = 2 * (pp & 7);
-  const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r], c, -m[qb]));
-  const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r + 1], c, -m[qb]));
-#ifdef BSA_SUM_DOT2
-  const bf16x2 pr = (bf16x2){static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
-  sum[qb] = __builtin_amdgcn_fdot2_f32_bf16(
-      pr, (bf16x2){static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)}, sum[qb], false);
-  pw[qb][(pp & 15) >> 2][pp & 3] = __builtin_bit_cast(uint32_t, pr);
-#else
-  sum[qb] = (sum[qb] + x0) + x1;
-  pw[qb][(pp & 15) >> 2][pp & 3] =
-      __builtin_bit_cast(uint32_t, (bf16x2){static_cast<__bf16>(x0), static_cast<__bf16>(x1)});
-#endif
-  if ((pp & 3) == 3) asm volatile("" : "+v"(pw[qb][(pp & 15) >> 2]));
-}
-
-template <int D, int NW, bool SMALLN>
-__device__ __forceinline__ uint64_t step(int N, float c, __amdgpu_buffer_rsrc_t krs,
-                                     __amdgpu_buffer_rsrc_t vrs, const Stage<D, NW>& sg,
-                                     uint32_t kread, uint32_t vread, uint8_t* __restrict__ kb_next,
-                                     uint8_t* __restrict__ kb_free, uint8_t* __restrict__ vb_cur,
-                                     uint8_t* __restrict__ vb_free,
-                                     const Tile& Tn, const Tile& Tk,
-                                     const bf16x8 (&qf)[2][D / 16], f32x16 (&o)[2][D / 32],
-                                     const bf16x8 (&p)[2][4], bf16x8 (&p_nxt)[2][4],
-                                     float (&m)[2], float (&l)[2], float (&alpha)[2]) {
+// Per-lane LDS read offsets of the MFMA operands: kx[ks] for the K operand of
+// k-step ks (row l32 of a 32-row half, chunk 2ks + h, swizzled), vx[db] for
+// the transposed V reads of channel block db.  Kept in registers so every
+// operand read is one ds_read with an immediate offset.
+template <int D, int NW>
+struct Addr {
   using L = Ly<D, NW>;
-  constexpr int NA = 2 * (D / 16);   // phase A steps
-  constexpr int NB = 4 * (D / 32);   // phase B steps
-  constexpr int NG = 2 * L::NI;      // global loads per wave
-  // the global loads go out over the first NL steps of phase A
-  constexpr int NL = BSA_LOAD_STEPS > 0 && BSA_LOAD_STEPS < NA ? BSA_LOAD_STEPS : NA;
-  constexpr int DB = D / 32;
-  const int h = (threadIdx.x & 63) >> 5;
-
-  // ---- phase A
-  f32x16 s[2][2];
+  uint32_t kx[L::KS], vx[L::DB];
+  __device__ __forceinline__ void init() {
+    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+    const uint32_t kread = static_cast<uint32_t>(l32 * L::ROWB + ((h ^ (l32 & (L::CH - 1))) << 4));
+    const int rsub = (lane & 15) >> 2;
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int sv = (2 * (4 * h + rsub)) & (L::CH - 1);
+    const uint32_t vread =
+        static_cast<uint32_t>((4 * h + rsub) * L::ROWB + ((cl ^ sv) << 4) + (lane & 1) * 8);
 #pragma unroll
-  for (int b = 0; b < 2; b++) { s[0][b] = f32x16{}; s[1][b] = f32x16{}; }
-  bf16x8 ka[kPfA + 1];
-#pragma unroll
-  for (int x = 0; x < kPfA; x++) ka[x] = k_operand<D, NW>(kb_next, kread, x & 1, x >> 1);
-#pragma unroll
-  for (int x = 0; x < NA; x++) {
-    const int b = x & 1, ks = x >> 1;
-    if (x + kPfA < NA)
-      ka[(x + kPfA) % (kPfA + 1)] = k_operand<D, NW>(kb_next, kread, (x + kPfA) & 1, (x + kPfA) >> 1);
-#pragma unroll
-    for (int gq = x * NG / NL; gq < (x + 1) * NG / NL && gq < NG; gq++) {
-      if (gq < L::NI)
-        load_one<D, NW, false, SMALLN>(krs, sg.template lane_off<false, SMALLN>(gq, N), Tk.win, gq, kb_free);
-      else
-        load_one<D, NW, true, SMALLN>(vrs, sg.template lane_off<true, SMALLN>(gq - L::NI, N), Tn.win,
-                                      gq - L::NI, vb_free);
+    for (int ks = 0; ks < L::KS; ks++) {
+      kx[ks] = kread ^ static_cast<uint32_t>(ks << 5);
+      opaque(kx[ks]);
     }
-    s[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % (kPfA + 1)], qf[0][ks], s[0][b], 0, 0, 0);
-    s[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % (kPfA + 1)], qf[1][ks], s[1][b], 0, 0, 0);
-    fence();
-  }
-
-  // columns outside the sub-tile (ragged tail, invalid block index): -inf.
-  // Only the scores pass through this branch.
-  if (Tn.mask) {
 #pragma unroll
-    for (int qb = 0; qb < 2; qb++)
-#pragma unroll
-      for (int b = 0; b < 2; b++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int kv = Tn.win + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (!Tn.valid || kv < Tn.kv0 || kv >= N) s[qb][b][r] = -INFINITY;
-        }
-  }
-
-  // ---- phase B
-  u32x4 pw[2][4];  // P as packed bf16 pairs: pw[qb][st][w] = words of P[qb][st]
-  float sum[2] = {0.0f, 0.0f};
-  bf16x8 va[kPfB + 1];
-#pragma unroll
-  for (int k = 0; k < kPfB; k++) va[k] = v_operand<D, NW>(vb_cur, vread, k / DB, k % DB);
-#pragma unroll
-  for (int k = 0; k < NB; k++) {
-    if (k + kPfB < NB)
-      va[(k + kPfB) % (kPfB + 1)] = v_operand<D, NW>(vb_cur, vread, (k + kPfB) / DB, (k + kPfB) % DB);
-    const int st = k / DB, db = k % DB;
-    o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % (kPfB + 1)], p[0][st], o[0][db], 0, 0, 0);
-    o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k % (kPfB + 1)], p[1][st], o[1][db], 0, 0, 0);
-    // exponentials of score pairs [lo, hi) out of 32 against the running reference
-#pragma unroll
-    for (int pp = k * 32 / NB; pp < (k + 1) * 32 / NB; pp++) exp_pair(s, c, m, pp, sum, pw);
-    fence();
-  }
-  // A tile row-half sum past the bound means scores rose well above the
-  // reference: redo this tile's exponentials against its exact row maximum
-  // (and rescale O before the next product).  Rare after the first tiles.
-  const uint64_t upd = __ballot(!(sum[0] <= kSumBound && sum[1] <= kSumBound));
-  if (upd != 0ull) {
-#pragma unroll
-    for (int qb = 0; qb < 2; qb++) {
-      float x = s[qb][0][0];
-#pragma unroll
-      for (int b = 0; b < 2; b++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) x = fmaxf(x, s[qb][b][r]);
-      const float mn = fmaxf(m[qb], halves_max(x) * c);
-      alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mn);
-      m[qb] = mn;
-      sum[qb] = 0.0f;
-#pragma unroll
-      for (int pp = 16 * qb; pp < 16 * qb + 16; pp++) exp_pair(s, c, m, pp, sum, pw);
-      l[qb] = l[qb] * alpha[qb] + sum[qb];
+    for (int db = 0; db < L::DB; db++) {
+      vx[db] = vread ^ static_cast<uint32_t>(db << 6);
+      opaque(vx[db]);
     }
-  } else {
-    l[0] += sum[0];
-    l[1] += sum[1];
   }
+};
+
+// K operand of k-step ks for kv half hb of the sub-tile at kt
+template <int D, int NW>
+__device__ __forceinline__ bf16x8 k_operand(const uint8_t* kt, const Addr<D, NW>& ad, int hb, int ks) {
+  return *reinterpret_cast<const bf16x8*>(kt + hb * 32 * Ly<D, NW>::ROWB + ad.kx[ks]);
+}
+
+// V^T operand of PV k-step st (16 kv rows 16st..16st+15 of the sub-tile,
+// transposed), channel block db
+template <int D, int NW>
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* vt, const Addr<D, NW>& ad, int st, int db) {
+  constexpr int R = Ly<D, NW>::ROWB;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + 16 * st * R + ad.vx[db]));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + (16 * st + 8) * R + ad.vx[db]));
+  return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+// operand index -> (k-step / channel block) for the prefetch rings:
+// K operand x: ks = x.  V operand x: s2 = x / DB, db = x % DB.
+template <int D, int NW>
+__device__ __forceinline__ bf16x8 v_operand_x(const uint8_t* vt, const Addr<D, NW>& ad, int hb, int x) {
+  constexpr int DB = Ly<D, NW>::DB;
+  return v_operand<D, NW>(vt, ad, 2 * hb + x / DB, x % DB);
+}
+
+// columns of kv half hb of tile T outside the sub-tile (ragged tail,
+// invalid block index): -inf
+__device__ __forceinline__ void mask_half(f32x16 (&s)[2], const Tile& T, int hb, int N) {
+  mfma_drain();
+  int base = T.win + 32 * hb + 4 * ((threadIdx.x & 63) >> 5);
+  opaque(base);  // per-slot offsets stay immediates
 #pragma unroll
   for (int qb = 0; qb < 2; qb++)
 #pragma unroll
-    for (int st = 0; st < 4; st++) p_nxt[qb][st] = __builtin_bit_cast(bf16x8, pw[qb][st]);
-  wait_loads();
-  return upd;
+    for (int r = 0; r < 16; r++) {
+      const int kv = base + 8 * (r >> 2) + (r & 3);
+      if (!T.valid || kv < T.kv0 || kv >= N) s[qb][r] = -INFINITY;
+    }
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Softmax of one half-tile, one score at a time: exp_issue(e) computes
+// y_e = 2^(c * S_e) for score e (0..31: row half e/16, slot e%16); its
+// consumers run one score later (exp_retire), so the exponential's latency
+// passes under the next MFMA: y_e joins the row-half sum, and every second
+// one completes a bf16 pair, word (e%8)/2 of P operand (e%16)/8.  The
+// exponential is written out (and each result pinned) so that the work stays
+// in its slot between the scheduling fences.
+struct Ex {
+  float y[4];  // y_e in y[e & 3]: a pair is packed while the next score is in flight
+};
+__device__ __forceinline__ void exp_issue(const f32x16 (&s)[2], int e, Ex& ex, float cs) {
+  const int qb = e >> 4, r = e & 15;
+  float x;
+#if BSA_QSCALE
+  (void)cs;
+  asm volatile("v_exp_f32 %0, %1" : "=v"(x) : "v"(s[qb][r]));
+#else
+  asm volatile("v_mul_f32 %0, %2, %1\n\tv_exp_f32 %0, %0" : "=&v"(x) : "v"(s[qb][r]), "s"(cs));
+#endif
+  ex.y[e & 3] = x;
+}
+__device__ __forceinline__ void exp_retire(int e, Ex& ex, float (&sum)[2], u32x4 (&p)[2][2]) {
+  const int qb = e >> 4, r = e & 15;
+  sum[qb] += ex.y[e & 3];
+  opaque(sum[qb]);
+  if (r & 1) {
+    uint32_t wd = __builtin_bit_cast(
+        uint32_t, (bf16x2){static_cast<__bf16>(ex.y[(e - 1) & 3]), static_cast<__bf16>(ex.y[e & 3])});
+    opaque(wd);
+    p[qb][r >> 3][(r & 7) >> 1] = wd;
+  }
+}
+
+// One pipeline step (kv half-tile u): the MFMA stream alternates
+// S_{u+1} = K.Qc^T - m (K of half u+1: half H of sub-tile kt) and
+// O += P_{u-1}.V (V of half u-1: half H of sub-tile vt); under it the
+// exponentials of S_u give P_u and their row sums.  A half-tile row sum past
+// kSumBound (scores far above the reference) raises the overflow flag.  The
+// K / V operand rings ka / va arrive with their first kPf entries read.
+// LM (staging issued under the step): 0 none; 1 the V sub-tile at row vwin
+// into vl, then the K sub-tile at row kwin into kl.
+template <int D, int NW, bool SMALLN, int H, bool PV, int LM>
+__device__ __forceinline__ void step(const Addr<D, NW>& ad, const Stage<D, NW>& sg, int N,
+                                     const uint8_t* __restrict__ kt, const uint8_t* __restrict__ vt,
+                                     const bf16x8 (&qf)[2][D / 16], const f32x16 (&negm)[2],
+                                     f32x16 (&o)[2][D / 32], const f32x16 (&s_cur)[2],
+                                     f32x16 (&s_nxt)[2], u32x4 (&p_cur)[2][2],
+                                     const u32x4 (&p_prv)[2][2], float (&l)[2], bool& ovf,
+                                     bf16x8 (&ka)[kPf + 1], bf16x8 (&va)[kPf + 1],
+                                     __amdgpu_buffer_rsrc_t krs, int kwin, uint8_t* __restrict__ kl,
+                                     __amdgpu_buffer_rsrc_t vrs, int vwin, uint8_t* __restrict__ vl,
+                                     float cs) {
+  using L = Ly<D, NW>;
+  constexpr int NS = L::NS;
+  // staging loads of this step per wave: V first, then K
+  constexpr int NG = LM == 1 ? 2 * L::NI : 0;
+  float sum[2] = {0.0f, 0.0f};
+  Ex ex;
+#pragma unroll
+  for (int x = 0; x < NS; x++) {
+    const int i = x >> 1;
+    if ((x & 1) == 0) {
+      // S_{u+1}: MFMA i = k-step i/2, row half i%2
+      const int ks = i >> 1, qb = i & 1;
+      if (qb == 0 && ks + kPf < L::KS) ka[(ks + kPf) % (kPf + 1)] = k_operand<D, NW>(kt, ad, H, ks + kPf);
+      if (ks == 0) mfma_s_init(s_nxt[qb], ka[ks % (kPf + 1)], qf[qb][ks], negm[qb]);
+      else mfma_s_acc(s_nxt[qb], ka[ks % (kPf + 1)], qf[qb][ks]);
+    } else if constexpr (PV) {
+      // O += P_{u-1} . V_{u-1}: MFMA i = V operand i/2, row half i%2
+      const int vi = i >> 1, qb = i & 1;
+      if (qb == 0 && vi + kPf < L::NV) va[(vi + kPf) % (kPf + 1)] = v_operand_x<D, NW>(vt, ad, H, vi + kPf);
+      const int s2 = vi / L::DB, db = vi % L::DB;
+      o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          va[vi % (kPf + 1)], __builtin_bit_cast(bf16x8, p_prv[qb][s2]), o[qb][db], 0, 0, 0);
+      asm volatile("" : "+a"(o[qb][db]));  // keeps the product in its slot
+    }
+    fence();  // the MFMA goes first in its slot
+    // softmax of S_u: scores [x*32/NS, (x+1)*32/NS), each retired one score later
+#pragma unroll
+    for (int e = x * 32 / NS; e < (x + 1) * 32 / NS; e++) {
+      exp_issue(s_cur, e, ex, cs);
+      if (e > 0) exp_retire(e - 1, ex, sum, p_cur);
+    }
+    if constexpr (LM != 0) {
+#pragma unroll
+      for (int gq = x * NG / NS; gq < (x + 1) * NG / NS; gq++) {
+        if (gq < L::NI) load_one<D, NW, true, SMALLN>(vrs, sg, N, vwin, gq, vl);
+        else load_one<D, NW, false, SMALLN>(krs, sg, N, kwin, gq - L::NI, kl);
+      }
+    }
+    fence();
+  }
+  exp_retire(31, ex, sum, p_cur);
+  l[0] += sum[0];
+  l[1] += sum[1];
+  ovf = ovf || !(sum[0] <= kSumBound && sum[1] <= kSumBound);
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void prefetch(const Addr<D, NW>& ad, const uint8_t* kt, const uint8_t* vt,
+                                         int hb, bf16x8 (&ka)[kPf + 1], bf16x8 (&va)[kPf + 1]) {
+#pragma unroll
+  for (int x = 0; x < kPf; x++) {
+    ka[x] = k_operand<D, NW>(kt, ad, hb, x);
+    va[x] = v_operand_x<D, NW>(vt, ad, hb, x);
+  }
+}
+
+// O += P . V of one half (no S product alongside): the last half of a row
+template <int D, int NW>
+__device__ __forceinline__ void pv_only(const Addr<D, NW>& ad, const uint8_t* vt, int hb,
+                                        const u32x4 (&p)[2][2], f32x16 (&o)[2][D / 32]) {
+  using L = Ly<D, NW>;
+#pragma unroll
+  for (int vi = 0; vi < L::NV; vi++) {
+    const bf16x8 a = v_operand_x<D, NW>(vt, ad, hb, vi);
+    const int s2 = vi / L::DB, db = vi % L::DB;
+    o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, p[0][s2]), o[0][db], 0, 0, 0);
+    o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, p[1][s2]), o[1][db], 0, 0, 0);
+  }
+}
+
+// S of half hb of the sub-tile at kt (accumulator start negm), drained
+template <int D, int NW>
+__device__ __forceinline__ void s_half(const Addr<D, NW>& ad, const uint8_t* kt, int hb,
+                                       const bf16x8 (&qf)[2][D / 16], const f32x16 (&negm)[2],
+                                       f32x16 (&s)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < Ly<D, NW>::KS; ks++) {
+    const bf16x8 a = k_operand<D, NW>(kt, ad, hb, ks);
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+      if (ks == 0) mfma_s_init(s[qb], a, qf[qb][ks], negm[qb]);
+      else mfma_s_acc(s[qb], a, qf[qb][ks]);
+    }
+  }
+  mfma_drain();
+}
+
+// row maximum of S over both lane halves (-inf if every column is masked)
+__device__ __forceinline__ void row_max(const f32x16 (&s)[2], float (&mx)[2]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    float x = s[qb][0];
+#pragma unroll
+    for (int r = 1; r < 16; r++) x = fmaxf(x, s[qb][r]);
+    mx[qb] = fmaxf(mx[qb], halves_max(x));
+  }
+}
+
+// Q fragments of the wave's rows qbase + 32qb + l32 (rows past N read as
+// zero); k-step ks holds channels 16ks + 8h .. +7.  With BSA_QSCALE the
+// fragments are pre-scaled by c (bf16, round to nearest).
+template <int D>
+__device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, int g, int N, int qbase, float c,
+                                       bf16x8 (&qf)[2][D / 16]) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    const int row = qbase + 32 * qb + l32;
+    const bool ok = row < N;
+    const uint16_t* qp = Q + (static_cast<int64_t>(g) * N + (ok ? row : 0)) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ks++) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) v = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+      const bf16x8 raw = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        qf[qb][ks][e] = BSA_QSCALE ? static_cast<__bf16>(static_cast<float>(raw[e]) * c) : raw[e];
+      asm volatile("" : "+a"(qf[qb][ks]));  // held in AGPRs: only MFMAs read it
+    }
+  }
 }
 
 template <int D, int BQ, int BK, bool SMALLN>
@@ -428,6 +450,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
     int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
     float c) {
+  static_assert(D == 64 || D == 128, "head dim");
   constexpr int NW = BQ / 64;
   constexpr int SUB = BK / KT;
   using L = Ly<D, NW>;
@@ -442,34 +465,16 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
   const int l32 = lane & 31, h = lane >> 5;
   const int qbase = i * BQ + w * 64;
 
-  // lane constants: staging offsets and the LDS read offsets of the MFMA operands
   Stage<D, NW> sg;
   sg.init();
-  const uint32_t kread = static_cast<uint32_t>(l32 * L::ROWB + ((h ^ (l32 & (L::CH - 1))) << 4));
-  uint32_t vread;
-  {
-    const int rsub = (lane & 15) >> 2;
-    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    const int sv = (2 * (4 * h + rsub)) & (L::CH - 1);
-    vread = static_cast<uint32_t>((4 * h + rsub) * L::ROWB + ((cl ^ sv) << 4) + (lane & 1) * 8);
-  }
+  Addr<D, NW> ad;
+  ad.init();
 
   bf16x8 qf[2][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < 2; qb++) {
-    const int row = qbase + 32 * qb + l32;
-    const bool ok = row < N;
-    const uint16_t* qp = Q + (static_cast<int64_t>(g) * N + (ok ? row : 0)) * D + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ks++) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) v = *reinterpret_cast<const uint4*>(qp + 16 * ks);
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+  load_q<D>(Q, g, N, qbase, c, qf);
 
-  int64_t e0 = row_ptr[static_cast<int64_t>(g % mask_G) * nq + i];
-  int64_t e1 = row_ptr[static_cast<int64_t>(g % mask_G) * nq + i + 1];
+  const int64_t rbase = static_cast<int64_t>(g % mask_G) * nq + i;
+  int64_t e0 = row_ptr[rbase], e1 = row_ptr[rbase + 1];
   e0 = e0 < 0 ? 0 : (e0 > col_len ? col_len : e0);
   e1 = e1 < e0 ? e0 : (e1 > col_len ? col_len : e1);
   const int nt = static_cast<int>(e1 - e0) * SUB;
@@ -479,53 +484,185 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
       const_cast<uint16_t*>(K + static_cast<int64_t>(g) * N * D), 0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(V + static_cast<int64_t>(g) * N * D), 0, head_bytes, 0x00020000);
+  // a resource with no records: staging through it fetches nothing
+  const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(K), 0, 0, 0x00020000);
 
-  float m[2] = {kRefInit, kRefInit}, l[2] = {0.0f, 0.0f}, alpha[2] = {1.0f, 1.0f};
+  float m[2] = {0.0f, 0.0f}, l[2] = {0.0f, 0.0f};
   f32x16 o[2][D / 32];
+  f32x16 negm[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++)
+  for (int qb = 0; qb < 2; qb++) {
+    negm[qb] = f32x16{};
 #pragma unroll
     for (int db = 0; db < D / 32; db++) o[qb][db] = f32x16{};
+  }
 
+  auto tile = [&](int j, int t) { return make_tile<BK>(j, t, N, nk); };
+  // kv-block index of sub-tile t through a vector load (a VGPR offset the
+  // compiler cannot see through keeps it off the scalar unit); indices past
+  // the row repeat its last entry
+  int vzero = 0;
+  opaque(vzero);
+  auto col_load = [&](int t) {
+    const int64_t e = e0 + t / SUB;
+    return col_idx[(e < e1 ? e : e1 - 1) + vzero];
+  };
+
+  // The reference comes from the first half-tile.  If a half-tile row sum
+  // then overflows the bound, or a row ends with no weight, the workgroup
+  // recomputes its rows on the exact path below (exact row maxima first).
+  bool ovf = false;
   if (nt > 0) {
-    bf16x8 p[2][4];
+    f32x16 sA[2], sB[2];
+    u32x4 pA[2][2], pB[2][2];
+    bf16x8 ka[kPf + 1], va[kPf + 1];
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; s2++) { pA[qb][s2] = u32x4{}; pB[qb][s2] = u32x4{}; }
+
+    // prologue: K(0), K(1), V(0) resident
+    Tile Tt = tile(col_idx[e0], 0);
+    Tile Tn = tile(nt > 1 ? col_idx[e0 + 1 / SUB] : -1, 1);
+    stage_tile<D, NW, SMALLN>(krs, sg, N, Tt.win, kb0, false);
+    stage_tile<D, NW, SMALLN>(nt > 1 ? krs : nrs, sg, N, Tn.win, kb1, false);
+    stage_tile<D, NW, SMALLN>(vrs, sg, N, Tt.win, vb0, true);
+    int jv = col_load(2);  // sub-tile 3, read at the first odd step
+    wait_loads();
+    __syncthreads();
+
+    // S_0 = K(0) half 0; pass 0 sets the reference to its row maxima
+    s_half<D, NW>(ad, kb0, 0, qf, negm, sA);
+    if (Tt.mask) mask_half(sA, Tt, 0, N);
     {
-      const Tile T0 = tile_of<BK>(col_idx, e0, 0, N, nk);
-      stage_all<D, NW, SMALLN>(krs, vrs, sg, T0, N, kb0, vb0);
-      if (nt > 1) stage_all<D, NW, SMALLN>(krs, vrs, sg, tile_of<BK>(col_idx, e0, 1, N, nk), N, kb1, nullptr);
+      float mx[2] = {-INFINITY, -INFINITY};
+      row_max(sA, mx);
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++) {
+        m[qb] = mx[qb] > -INFINITY ? mx[qb] : 0.0f;
+        sA[qb] -= m[qb];
+        negm[qb] -= m[qb];
+      }
+      asm volatile("s_nop 4" ::: "memory");  // VALU-written negm before an MFMA reads it
+    }
+    prefetch<D, NW>(ad, kb0, vb0, 1, ka, va);
+    // step 0: P_0; S_1 = K(0) half 1; no PV yet
+    step<D, NW, SMALLN, 1, false, 0>(ad, sg, N, kb0, vb0, qf, negm, o, sA, sB, pA, pB, l, ovf, ka, va,
+                                     nrs, 0, kb1, nrs, 0, vb1, c);
+    __syncthreads();  // K(0) free for K(2)
+    prefetch<D, NW>(ad, kb1, vb0, 0, ka, va);
+
+    // Steady state.  Iteration t (sub-tile t, with K(t+1) and V(t) resident):
+    //   odd step 2t+1:  P_{2t+1}; S_{2t+2} = K(t+1) half 0; O += P_{2t}.V(t)
+    //                   half 0; stage V(t+1) and K(t+2)
+    //   even step 2t+2: P_{2t+2}; S_{2t+3} = K(t+1) half 1; O += P_{2t+1}.V(t)
+    //                   half 1; wait for the staging, barrier.
+    // K(t) and V(t) live in buffer t % 2; two sub-tiles per loop trip keep
+    // every buffer choice static.  Tt, Tn: tiles t, t+1.
+    int t = 0;
+#define BSA_ITER(KC, VC, KL, VL, KF)                                                                 \
+  {                                                                                                  \
+    const Tile Tk = tile(__builtin_amdgcn_readfirstlane(jv), t + 2);                                 \
+    jv = col_load(t + 3);                                                                            \
+    if (Tt.mask) mask_half(sB, Tt, 1, N);                                                            \
+    step<D, NW, SMALLN, 0, true, 1>(ad, sg, N, KC, VC, qf, negm, o, sB, sA, pB, pA, l, ovf, ka, va,  \
+                                    t + 2 < nt ? krs : nrs, Tk.win, KL, t + 1 < nt ? vrs : nrs,      \
+                                    Tn.win, VL, c);                                                  \
+    if (t + 1 >= nt) break;                                                                          \
+    prefetch<D, NW>(ad, KC, VC, 1, ka, va);                                                          \
+    if (Tn.mask) mask_half(sA, Tn, 0, N);                                                            \
+    step<D, NW, SMALLN, 1, true, 0>(ad, sg, N, KC, VC, qf, negm, o, sA, sB, pA, pB, l, ovf, ka, va,  \
+                                    nrs, 0, KL, nrs, 0, VL, c);                                      \
+    wait_loads();                                                                                    \
+    __syncthreads();                                                                                 \
+    prefetch<D, NW>(ad, KF, VL, 0, ka, va);                                                          \
+    Tt = Tn;                                                                                         \
+    Tn = Tk;                                                                                         \
+    t++;                                                                                             \
+  }
+    while (true) {
+      BSA_ITER(kb1, vb0, kb0, vb1, kb0)  // t even
+      BSA_ITER(kb0, vb1, kb1, vb0, kb1)  // t odd
+    }
+#undef BSA_ITER
+    // last half (2nt-1): O += P_{2nt-1}.V(nt-1) half 1
+    if (t & 1) pv_only<D, NW>(ad, vb1, 1, pB, o);
+    else pv_only<D, NW>(ad, vb0, 1, pB, o);
+    // no staging may still be landing in LDS when the buffers are reused or
+    // the workgroup ends
+    wait_loads();
+
+    // a row with no weight left (every exponential underflowed) also takes
+    // the exact path
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) ovf = ovf || !(l[qb] + __shfl_xor(l[qb], 32) > 0.0f);
+    // workgroup-wide OR of the flag through the (now idle) staging buffer
+    __syncthreads();
+    if (lane == 0) reinterpret_cast<volatile int*>(kb0)[w] = __ballot(ovf) != 0ull;
+    __syncthreads();
+    ovf = false;
+#pragma unroll
+    for (int ww = 0; ww < NW; ww++) ovf = ovf || reinterpret_cast<volatile int*>(kb0)[ww] != 0;
+    __syncthreads();
+  }
+
+  if (ovf) {
+    // Exact path, one sub-tile at a time: the row maxima over every kept
+    // column, then O and l against them (every score <= 0).
+    load_q<D>(Q, g, N, qbase, c, qf);
+    f32x16 sA[2];
+    u32x4 pA[2][2];
+    float mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) negm[qb] = f32x16{};
+    asm volatile("s_nop 4" ::: "memory");
+    for (int t = 0; t < nt; t++) {
+      const Tile T = tile(col_idx[e0 + t / SUB], t);
+      stage_tile<D, NW, SMALLN>(krs, sg, N, T.win, kb0, false);
       wait_loads();
       __syncthreads();
-      f32x16 s[2][2];
-      qk<D, NW>(kb0, kread, qf, s);
-      if (T0.mask) softmax<true>(s, T0, N, c, m, l, p, alpha);
-      else softmax<false>(s, T0, N, c, m, l, p, alpha);
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++) {
+        s_half<D, NW>(ad, kb0, hb, qf, negm, sA);
+        if (T.mask) mask_half(sA, T, hb, N);
+        row_max(sA, mx);
+      }
       __syncthreads();
     }
-    uint64_t upd = 0;  // O is still zero: nothing to rescale yet
-    // tiles t+1 and t+2 are fetched one iteration ahead; pinning them at the
-    // end of the iteration retires the scalar loads outside the LDS phases.
-    // K(t+2) is always loaded (at t+2 == nt the last tile is reloaded into a
-    // buffer that is not read again), which keeps the iteration branch-free.
-    Tile Tn = tile_of<BK>(col_idx, e0, nt > 1 ? 1 : 0, N, nk);
-    Tile Tk = tile_of<BK>(col_idx, e0, nt > 2 ? 2 : nt - 1, N, nk);
-    int t = 0;
-    for (; t + 1 < nt; t++) {
-      if (upd != 0ull) rescale<D>(o, alpha);
-      const bool odd = t & 1;
-      bf16x8 pn[2][4];
-      upd = step<D, NW, SMALLN>(N, c, krs, vrs, sg, kread, vread, odd ? kb0 : kb1, odd ? kb1 : kb0,
-                                odd ? vb1 : vb0, odd ? vb0 : vb1, Tn, Tk, qf, o, p, pn, m, l, alpha);
 #pragma unroll
-      for (int qb = 0; qb < 2; qb++)
+    for (int qb = 0; qb < 2; qb++) {
+      m[qb] = mx[qb] > -INFINITY ? mx[qb] : 0.0f;
+      l[qb] = 0.0f;
+      negm[qb] = -m[qb];
 #pragma unroll
-        for (int st = 0; st < 4; st++) p[qb][st] = pn[qb][st];
-      Tn = Tk;
-      Tk = tile_of<BK>(col_idx, e0, t + 3 < nt ? t + 3 : nt - 1, N, nk);
-      asm volatile("" ::"s"(Tk.win), "s"(Tk.kv0), "s"(static_cast<int>(Tk.valid)));
+      for (int db = 0; db < D / 32; db++) o[qb][db] = f32x16{};
+    }
+    asm volatile("s_nop 4" ::: "memory");
+    for (int t = 0; t < nt; t++) {
+      const Tile T = tile(col_idx[e0 + t / SUB], t);
+      stage_tile<D, NW, SMALLN>(krs, sg, N, T.win, kb0, false);
+      stage_tile<D, NW, SMALLN>(vrs, sg, N, T.win, vb0, true);
+      wait_loads();
+      __syncthreads();
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++) {
+        s_half<D, NW>(ad, kb0, hb, qf, negm, sA);
+        if (T.mask) mask_half(sA, T, hb, N);
+        float sum[2] = {0.0f, 0.0f};
+        Ex ex;
+#pragma unroll
+        for (int e = 0; e < 32; e++) {
+          exp_issue(sA, e, ex, c);
+          asm volatile("s_nop 0");
+          exp_retire(e, ex, sum, pA);
+        }
+        l[0] += sum[0];
+        l[1] += sum[1];
+        pv_only<D, NW>(ad, vb0, hb, pA, o);
+      }
       __syncthreads();
     }
-    if (upd != 0ull) rescale<D>(o, alpha);
-    pv<D, NW>((t & 1) ? vb1 : vb0, vread, p, o);
   }
 
 #pragma unroll
@@ -548,7 +685,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
           *reinterpret_cast<uint2*>(op + d0) = pk;
         }
       if (lse != nullptr && h == 0)
-        lse[static_cast<int64_t>(g) * N + row] = lt > 0.0f ? m[qb] * kLn2 + logf(lt) : -INFINITY;
+        lse[static_cast<int64_t>(g) * N + row] = lt > 0.0f ? (BSA_QSCALE ? m[qb] : m[qb] * c) * kLn2 + logf(lt) : -INFINITY;
     }
   }
 }

@@ -360,3 +360,59 @@ def test_int8_tiles_bit_exact(bsa_gpu, orc, d, Bq, Bk):
     for t, (g, i, j) in enumerate(gij):
         assert np.array_equal(S[t], orc.int8_qk_tile(Qq, Kq, g, i, j, Bq, Bk)), (g, i, j)
         assert np.array_equal(OV[t], orc.int8_pv_tile(P8[t], Vq, g, j, Bq, Bk)), (g, j)
+
+
+# ---------------------------------------------------- reference edge cases
+def _forward_reordered_case(bsa, orc, Qn, Kn, Vn, rp, ci, F, H, W, Bq, Bk, tag):
+    """Identity axis order: natural bf16 Q/K/V [N][G][d] -> reorder -> bf16
+    forward with the given CSR -> inverse; every row against the oracle."""
+    N, G, d = Qn.shape
+    orders = np.zeros(G, np.uint8)
+    od = torch.from_numpy(orders).cuda()
+    dev = [torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda() for x in (Qn, Kn, Vn)]
+    Qp, Kp, Vp = (bsa.permute(x, od, F, H, W, 0) for x in dev)
+    Op, lse = bsa.forward(Qp, Kp, Vp, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(), Bq, Bk)
+    O = bsa.permute(Op, od, F, H, W, 1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    host = [_bits(x) for x in dev]
+    rows = np.array([(g, n) for g in range(G) for n in range(N)], np.int64)
+    Ow, Lw = orc.attention_rows(*host, G, F, H, W, d, orders, rows, Bq, Bk, rp, ci)
+    got = _np(O)[rows[:, 1], rows[:, 0]]
+    _compare(got, Ow, heads=rows[:, 0], tag=tag)
+    lg = _np(lse)[rows[:, 0], rows[:, 1]]
+    assert np.max(np.abs(lg - Lw)) <= LSE_ABS
+
+
+def test_forward_late_scores_far_above_reference(bsa_gpu, orc):
+    """Keys of the last kv-block aligned with the queries of the second
+    q-block: their scores exceed the reference taken from the first
+    half-tile by ~140 (log2 units), so the kernel must take its exact path
+    (row maxima first) for that workgroup.  Softmax then puts nearly all
+    weight on the aligned keys, which the oracle also computes in fp64."""
+    r = np.random.Generator(np.random.PCG64(31))
+    F, H, W, G, d, Bq, Bk = 1, 4, 64, 2, 128, 128, 64
+    N = F * H * W
+    Q = r.standard_normal((N, G, d))
+    K = r.standard_normal((N, G, d))
+    V = r.standard_normal((N, G, d))
+    u = r.standard_normal((G, d))
+    Q[128:] = 3.0 * u[None] + 0.1 * r.standard_normal((N - 128, G, d))
+    K[192:] = 3.0 * u[None] + 0.1 * r.standard_normal((N - 192, G, d))
+    nq, nk = N // Bq, N // Bk
+    rp = np.arange(0, G * nq * nk + 1, nk, dtype=np.int32)
+    ci = np.tile(np.arange(nk, dtype=np.int32), G * nq)
+    _forward_reordered_case(bsa_gpu, orc, Q, K, V, rp, ci, F, H, W, Bq, Bk, "late large scores")
+
+
+def test_forward_first_half_tile_masked(bsa_gpu, orc):
+    """N = 80 with 64-token blocks: the second q-block keeps only the ragged
+    last kv-block (16 real keys), whose staged window starts at row 16, so
+    the first 32-row half of that window is entirely masked and the row
+    reference is only set by the second half."""
+    r = np.random.Generator(np.random.PCG64(32))
+    F, H, W, G, d, Bq, Bk = 1, 1, 80, 1, 64, 64, 64
+    N = F * H * W
+    Q, K, V = (r.standard_normal((N, G, d)) for _ in range(3))
+    rp = np.array([0, 2, 3], np.int32)
+    ci = np.array([0, 1, 1], np.int32)
+    _forward_reordered_case(bsa_gpu, orc, Q, K, V, rp, ci, F, H, W, Bq, Bk, "masked first half")
