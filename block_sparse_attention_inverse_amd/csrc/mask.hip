@@ -25,6 +25,8 @@
 //   emit_kernel    one wave per row: bitmask -> ascending col_idx
 #pragma clang fp contract(off)
 
+#include <algorithm>
+
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
 
@@ -34,7 +36,8 @@ namespace {
 constexpr int kPoolThreads = 256;
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kMaxNk = 8192;
+constexpr int kSelRows = 8;                 // most q-block rows per select workgroup
+constexpr int kSelKeyBytes = 48 * 1024;     // LDS for their key images (Nkv <= 8192 keeps >= 1 row)
 constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ float div_rn(float x, float y) { return x / y; }  // correctly rounded build
@@ -165,117 +168,157 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ sum_q, const float* __restrict__ sum_k,
     const float* __restrict__ norm_q, const float* __restrict__ norm_k,
     const uint8_t* __restrict__ orders, int N, int F, int H, int W, int Bq, int Bk, int nq,
-    int nk, int words, int score, int k, int force_diag, int win_T, int win_r0,
+    int nk, int words, int score, int k, int force_diag, int win_T, int win_r0, int rows_per_wg,
     int32_t* __restrict__ counts, unsigned long long* __restrict__ bits) {
-  __shared__ float a[D];
-  __shared__ uint32_t ukey[kMaxNk];
+  extern __shared__ uint32_t ukeys[];  // [rows_per_wg][nk] ordered key images
+  __shared__ float a[kSelRows][D];
   __shared__ int hist[256];
   __shared__ uint32_t s_prefix, s_mask;
   __shared__ int s_krem;
   __shared__ int s_wave[kSelWaves];
   __shared__ int s_count;
 
-  const int row = blockIdx.x;  // g*nq + i
-  const int g = row / nq, i = row % nq;
+  // rows_per_wg consecutive q-blocks of one head: each kv-block summary is
+  // read once for all of them
+  const int gpr = (nq + rows_per_wg - 1) / rows_per_wg;
+  const int g = blockIdx.x / gpr, i0 = (blockIdx.x % gpr) * rows_per_wg;
+  const int nr = min(rows_per_wg, nq - i0);
   const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
 
-  const float* aq = sum_q + static_cast<int64_t>(row) * D;
-  for (int c = t; c < D; c += kSelThreads) a[c] = aq[c];
-  if (t == 0) { s_prefix = 0; s_mask = 0; s_krem = k; s_count = 0; }
+  for (int e = t; e < kSelRows * D; e += kSelThreads) {
+    const int r = e / D, c = e % D;
+    a[r][c] = r < nr ? sum_q[(static_cast<int64_t>(g) * nq + i0 + r) * D + c] : 0.0f;
+  }
   __syncthreads();
 
-  // keys
-  const float nqi = score == 1 ? norm_q[row] : 0.0f;
+  // keys: for every (row, j) one fp32 fma chain over the channels in order
   for (int j = t; j < nk; j += kSelThreads) {
     const float4* bj = reinterpret_cast<const float4*>(sum_k + (static_cast<int64_t>(g) * nk + j) * D);
-    float acc = 0.0f;
+    float acc[kSelRows];
+#pragma unroll
+    for (int r = 0; r < kSelRows; r++) acc[r] = 0.0f;
 #pragma unroll 4
     for (int c4 = 0; c4 < D / 4; c4++) {
       const float4 v = bj[c4];
-      acc = __builtin_fmaf(a[4 * c4 + 0], v.x, acc);
-      acc = __builtin_fmaf(a[4 * c4 + 1], v.y, acc);
-      acc = __builtin_fmaf(a[4 * c4 + 2], v.z, acc);
-      acc = __builtin_fmaf(a[4 * c4 + 3], v.w, acc);
-    }
-    float key = acc;
-    if (score == 1) {
-      const float den = nqi * norm_k[static_cast<int64_t>(g) * nk + j];
-      key = (den == 0.0f) ? 0.0f : div_rn(acc, den);
-    }
-    ukey[j] = key_order_bits(key);
-  }
-
-  // exact k-th largest image by MSB-first radix select (8-bit digits)
-  for (int pass = 0; pass < 4; pass++) {
-    const int shift = 24 - 8 * pass;
-    for (int e = t; e < 256; e += kSelThreads) hist[e] = 0;
-    __syncthreads();
-    const uint32_t pre = s_prefix, msk = s_mask;
-    for (int j = t; j < nk; j += kSelThreads) {
-      const uint32_t u = ukey[j];
-      if ((u & msk) == pre) atomicAdd(&hist[(u >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (t == 0) {
-      int krem = s_krem, cum = 0, dg = 255;
-      for (; dg > 0; dg--) {
-        if (cum + hist[dg] >= krem) break;
-        cum += hist[dg];
+#pragma unroll
+      for (int r = 0; r < kSelRows; r++) {
+        acc[r] = __builtin_fmaf(a[r][4 * c4 + 0], v.x, acc[r]);
+        acc[r] = __builtin_fmaf(a[r][4 * c4 + 1], v.y, acc[r]);
+        acc[r] = __builtin_fmaf(a[r][4 * c4 + 2], v.z, acc[r]);
+        acc[r] = __builtin_fmaf(a[r][4 * c4 + 3], v.w, acc[r]);
       }
-      s_krem = krem - cum;
-      s_prefix = pre | (static_cast<uint32_t>(dg) << shift);
-      s_mask = msk | (255u << shift);
     }
-    __syncthreads();
+    const float nkj = score == 1 ? norm_k[static_cast<int64_t>(g) * nk + j] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < kSelRows; r++) {
+      if (r < nr) {
+        float key = acc[r];
+        if (score == 1) {
+          const float den = norm_q[static_cast<int64_t>(g) * nq + i0 + r] * nkj;
+          key = (den == 0.0f) ? 0.0f : div_rn(acc[r], den);
+        }
+        ukeys[r * nk + j] = key_order_bits(key);
+      }
+    }
   }
-  const uint32_t T = s_prefix;
-  const int take_eq = s_krem;  // how many keys equal to T are kept (lowest indices first)
-
-  // q-block geometry for the forced sets
-  const int q0 = i * Bq, q1 = min(q0 + Bq, N);
-  const int order = orders[g];
-  int fi = 0, oi = 0;
-  if (win_T >= 0) block_centre(order, i, Bq, N, F, H, W, fi, oi);
-
-  int eq_carry = 0, my_count = 0;
-  const int chunks = (nk + kSelThreads - 1) / kSelThreads;
-  for (int ch = 0; ch < chunks; ch++) {
-    const int j = ch * kSelThreads + t;
-    const bool inr = j < nk;
-    const uint32_t u = inr ? ukey[j] : 0u;
-    const bool eq = inr && u == T;
-    // rank of this element among the equal ones, in ascending index order
-    const unsigned long long eb = __ballot(eq);
-    const int below = __popcll(eb & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wave[wv] = __popcll(eb);
-    __syncthreads();
-    int before = eq_carry;
-    for (int w = 0; w < wv; w++) before += s_wave[w];
-    int chunk_total = 0;
-    for (int w = 0; w < kSelWaves; w++) chunk_total += s_wave[w];
-    bool keep = inr && (u > T || (eq && before + below < take_eq));
-    if (inr && force_diag) {
-      const int k0 = j * Bk, k1 = min(k0 + Bk, N);
-      keep = keep || (k0 < q1 && q0 < k1);
-    }
-    if (inr && win_T >= 0 && !keep) {
-      int fj, oj;
-      block_centre(order, j, Bk, N, F, H, W, fj, oj);
-      const int df = abs(fi - fj), dox = abs(oi - oj);
-      keep = df <= win_T && static_cast<int64_t>(dox) <= ((static_cast<int64_t>(win_r0) * W) >> df);
-    }
-    const unsigned long long kb = __ballot(keep);
-    const int word = (ch * kSelThreads + wv * kWave) / 64;
-    if (lane == 0 && word < words) {
-      bits[static_cast<int64_t>(row) * words + word] = kb;
-      my_count += __popcll(kb);
-    }
-    eq_carry += chunk_total;
-    __syncthreads();  // s_wave reuse
-  }
-  if (lane == 0) atomicAdd(&s_count, my_count);
   __syncthreads();
-  if (t == 0) counts[row] = s_count;
+
+  for (int r = 0; r < nr; r++) {
+    const uint32_t* ukey = ukeys + r * nk;
+    const int i = i0 + r, row = g * nq + i;
+    if (t == 0) { s_prefix = 0; s_mask = 0; s_krem = k; s_count = 0; }
+    __syncthreads();
+
+    // exact k-th largest image by MSB-first radix select (8-bit digits)
+    for (int pass = 0; pass < 4; pass++) {
+      const int shift = 24 - 8 * pass;
+      for (int e = t; e < 256; e += kSelThreads) hist[e] = 0;
+      __syncthreads();
+      const uint32_t pre = s_prefix, msk = s_mask;
+      for (int j = t; j < nk; j += kSelThreads) {
+        const uint32_t u = ukey[j];
+        if ((u & msk) == pre) atomicAdd(&hist[(u >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (wv == 0) {
+        // the digit: the highest bin at which the count from the top reaches
+        // krem (bin 0 if none does); lane l holds bins 255-4l .. 252-4l
+        int hb[4], sl = 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) { hb[q] = hist[255 - 4 * lane - q]; sl += hb[q]; }
+        int x = sl;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int y = __shfl_up(x, o);
+          if (lane >= o) x += y;
+        }
+        const int krem = s_krem;
+        const unsigned long long reach = __ballot(x >= krem);
+        const int L = reach ? __builtin_ctzll(reach) : kWave - 1;
+        if (lane == L) {
+          int cum = x - sl, dg = 0;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int b = 255 - 4 * lane - q;
+            if (b == 0 || cum + hb[q] >= krem) { dg = b; break; }
+            cum += hb[q];
+          }
+          s_krem = krem - cum;
+          s_prefix = pre | (static_cast<uint32_t>(dg) << shift);
+          s_mask = msk | (255u << shift);
+        }
+      }
+      __syncthreads();
+    }
+    const uint32_t T = s_prefix;
+    const int take_eq = s_krem;  // how many keys equal to T are kept (lowest indices first)
+
+    // q-block geometry for the forced sets
+    const int q0 = i * Bq, q1 = min(q0 + Bq, N);
+    const int order = orders[g];
+    int fi = 0, oi = 0;
+    if (win_T >= 0) block_centre(order, i, Bq, N, F, H, W, fi, oi);
+
+    int eq_carry = 0, my_count = 0;
+    const int chunks = (nk + kSelThreads - 1) / kSelThreads;
+    for (int ch = 0; ch < chunks; ch++) {
+      const int j = ch * kSelThreads + t;
+      const bool inr = j < nk;
+      const uint32_t u = inr ? ukey[j] : 0u;
+      const bool eq = inr && u == T;
+      // rank of this element among the equal ones, in ascending index order
+      const unsigned long long eb = __ballot(eq);
+      const int below = __popcll(eb & ((1ull << lane) - 1ull));
+      if (lane == 0) s_wave[wv] = __popcll(eb);
+      __syncthreads();
+      int before = eq_carry;
+      for (int w = 0; w < wv; w++) before += s_wave[w];
+      int chunk_total = 0;
+      for (int w = 0; w < kSelWaves; w++) chunk_total += s_wave[w];
+      bool keep = inr && (u > T || (eq && before + below < take_eq));
+      if (inr && force_diag) {
+        const int k0 = j * Bk, k1 = min(k0 + Bk, N);
+        keep = keep || (k0 < q1 && q0 < k1);
+      }
+      if (inr && win_T >= 0 && !keep) {
+        int fj, oj;
+        block_centre(order, j, Bk, N, F, H, W, fj, oj);
+        const int df = abs(fi - fj), dox = abs(oi - oj);
+        keep = df <= win_T && static_cast<int64_t>(dox) <= ((static_cast<int64_t>(win_r0) * W) >> df);
+      }
+      const unsigned long long kb = __ballot(keep);
+      const int word = (ch * kSelThreads + wv * kWave) / 64;
+      if (lane == 0 && word < words) {
+        bits[static_cast<int64_t>(row) * words + word] = kb;
+        my_count += __popcll(kb);
+      }
+      eq_carry += chunk_total;
+      __syncthreads();  // s_wave reuse
+    }
+    if (lane == 0) atomicAdd(&s_count, my_count);
+    __syncthreads();
+    if (t == 0) counts[row] = s_count;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -379,14 +422,19 @@ hipError_t select_and_emit(const MaskGeom& m, const uint8_t* orders, int32_t* ro
   auto* bits = reinterpret_cast<unsigned long long*>(ws + L.bits);
   const int N = static_cast<int>(m.N);
   const int R = m.G * m.nq;
+  const int rpw = std::max(1, std::min(kSelRows, kSelKeyBytes / (4 * m.nk)));
+  const uint32_t grid = static_cast<uint32_t>(m.G) * ((m.nq + rpw - 1) / rpw);
+  const size_t lds = sizeof(uint32_t) * static_cast<size_t>(rpw) * m.nk;
   if (m.d == 128)
-    select_kernel<128><<<R, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F, m.H,
-                                                 m.W, m.Bq, m.Bk, m.nq, m.nk, m.words, m.score,
-                                                 m.k, m.force_diag, m.win_T, m.win_r0, counts, bits);
+    select_kernel<128><<<grid, kSelThreads, lds, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F,
+                                                      m.H, m.W, m.Bq, m.Bk, m.nq, m.nk, m.words,
+                                                      m.score, m.k, m.force_diag, m.win_T, m.win_r0,
+                                                      rpw, counts, bits);
   else
-    select_kernel<64><<<R, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F, m.H,
-                                                m.W, m.Bq, m.Bk, m.nq, m.nk, m.words, m.score, m.k,
-                                                m.force_diag, m.win_T, m.win_r0, counts, bits);
+    select_kernel<64><<<grid, kSelThreads, lds, s>>>(sum_q, sum_k, norm_q, norm_k, orders, N, m.F,
+                                                     m.H, m.W, m.Bq, m.Bk, m.nq, m.nk, m.words,
+                                                     m.score, m.k, m.force_diag, m.win_T, m.win_r0,
+                                                     rpw, counts, bits);
   scan_kernel<<<1, kScanThreads, 0, s>>>(counts, R, row_ptr, nnz);
   emit_kernel<<<(R + 3) / 4, 256, 0, s>>>(bits, row_ptr, R, m.words, col_idx, col_capacity);
   return hipGetLastError();
