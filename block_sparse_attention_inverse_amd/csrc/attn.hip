@@ -17,10 +17,11 @@
 //   acc = acc * 2^(m - m') + (mP / 127) * sV_j * (P8 . v8) (exact int32)
 // and O = acc / l, LSE = (m + log2 l) * ln 2.
 //
-// Work split: one workgroup per (head g, q-block i); Bq/64 waves, each owning
-// 64 query rows as two 32-row halves, so every K and V operand read from LDS
-// feeds two v_mfma_i32_32x32x32_i8.  A tile is one kv-block (the
-// quantisation unit of P).
+// Work split: one workgroup per (head g, q-block i); Bq/32 waves of 32 query
+// rows.  Two workgroups per CU put two waves on every SIMD, so one wave's
+// v_mfma_i32_32x32x32_i8 products run under the other's softmax, quantising
+// and rescaling work (each wave needs at most 256 registers).  A tile is one
+// kv-block (the quantisation unit of P).
 //   S^T = K . Q^T     A = K rows from LDS (ds_read_b128), B = Q fragments in
 //                     registers; the accumulator gives every lane one query
 //                     row (the two wave halves share a row): lane half h, slot
@@ -50,6 +51,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_127 = 6.988684686772166f;
 constexpr float kRefInit = -1.0e30f;  // running maximum before any score: finite, below all
+// 32-row halves per wave: one, so a 128-row q-block is four waves and two
+// workgroups give every SIMD two waves whose products and softmax interleave
+constexpr int kQB = 1;
+constexpr int kRowsPerWave = 32 * kQB;
 
 // accumulator row of element r for lane half h (32x32 MFMA tiles)
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -134,27 +139,30 @@ __device__ __forceinline__ uint32_t v_read_off() {
 // S^T = K . Q^T for the wave's two row halves: s[qb][b] covers kv 32b..32b+31
 template <int D, int BK>
 __device__ __forceinline__ void qk_i8(const uint8_t* kt, uint32_t kread,
-                                      const i32x4 (&qf)[2][D / 32], i32x16 (&s)[2][BK / 32]) {
+                                      const i32x4 (&qf)[kQB][D / 32], i32x16 (&s)[kQB][BK / 32]) {
 #pragma unroll
-  for (int b = 0; b < BK / 32; b++) { s[0][b] = i32x16{}; s[1][b] = i32x16{}; }
+  for (int b = 0; b < BK / 32; b++)
+#pragma unroll
+    for (int qb = 0; qb < kQB; qb++) s[qb][b] = i32x16{};
 #pragma unroll
   for (int ks = 0; ks < D / 32; ks++)
 #pragma unroll
     for (int b = 0; b < BK / 32; b++) {
       const i32x4 a = *reinterpret_cast<const i32x4*>(kt + b * 32 * D + (kread ^ (ks << 5)));
-      s[0][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[0][ks], s[0][b], 0, 0, 0);
-      s[1][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[1][ks], s[1][b], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < kQB; qb++)
+        s[qb][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[qb][ks], s[qb][b], 0, 0, 0);
     }
 }
 
-// One channel block of O^T (int32, this tile only) = V^T . P8^T for both row
-// halves: ov0 / ov1 cover channels 32db..32db+31 of halves 0 / 1
+// One channel block of O^T (int32, this tile only) = V^T . P8^T for the
+// wave's row halves: ov[qb] covers channels 32db..32db+31 of half qb
 template <int D, int BK>
-__device__ __forceinline__ void pv_block(const uint8_t* vt, uint32_t vread, const i32x4 (&pf)[2][BK / 32],
-                                         int db, i32x16& ov0, i32x16& ov1) {
+__device__ __forceinline__ void pv_block(const uint8_t* vt, uint32_t vread, const i32x4 (&pf)[kQB][BK / 32],
+                                         int db, i32x16 (&ov)[kQB]) {
   const uint32_t vhi = (vread ^ ((D / 32) << 4)) + 8 * D;  // rows +8: the swizzle flips CH/2
-  ov0 = i32x16{};
-  ov1 = i32x16{};
+#pragma unroll
+  for (int qb = 0; qb < kQB; qb++) ov[qb] = i32x16{};
 #pragma unroll
   for (int b = 0; b < BK / 32; b++) {
     const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -162,8 +170,8 @@ __device__ __forceinline__ void pv_block(const uint8_t* vt, uint32_t vread, cons
     const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
         (LDS_AS i32x2*)(vt + b * 32 * D + (vhi ^ (db << 5))));
     const i32x4 a = (i32x4){lo[0], lo[1], hi[0], hi[1]};
-    ov0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[0][b], ov0, 0, 0, 0);
-    ov1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[1][b], ov1, 0, 0, 0);
+#pragma unroll
+    for (int qb = 0; qb < kQB; qb++) ov[qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[qb][b], ov[qb], 0, 0, 0);
   }
 }
 
@@ -171,10 +179,10 @@ __device__ __forceinline__ void pv_block(const uint8_t* vt, uint32_t vread, cons
 // 32ks + 16h .. +15 (rows past N read as zero)
 template <int D>
 __device__ __forceinline__ void load_q(const int8_t* __restrict__ Q, int g, int qbase, int N,
-                                       i32x4 (&qf)[2][D / 32]) {
+                                       i32x4 (&qf)[kQB][D / 32]) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++) {
+  for (int qb = 0; qb < kQB; qb++) {
     const int row = qbase + 32 * qb + l32;
     const bool ok = row < N;
     const int8_t* p = Q + (static_cast<int64_t>(g) * N + (ok ? row : 0)) * D + 16 * h;
@@ -195,13 +203,13 @@ __device__ __forceinline__ float rows_max(float x) {
 }
 
 template <int D, int BQ, int BK>
-__global__ __launch_bounds__(BQ) void fwd_i8_kernel(
+__global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
     const int8_t* __restrict__ Q, const float* __restrict__ sQ, const int8_t* __restrict__ K,
     const float* __restrict__ sK, const int8_t* __restrict__ V, const float* __restrict__ sV,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
     int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
     float scale_log2) {
-  constexpr int NW = BQ / 64;
+  constexpr int NW = BQ / kRowsPerWave;
   constexpr int NB = BK / 32;
   using L = L8<D, BK, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[3][L::TB];
@@ -212,13 +220,13 @@ __global__ __launch_bounds__(BQ) void fwd_i8_kernel(
   if (!head_sync_tile(blockIdx.x, nq, g, i)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int qbase = i * BQ + w * 64;
+  const int qbase = i * BQ + w * kRowsPerWave;
 
   Stage8<D, BK, NW> sg;
   sg.init();
   const uint32_t kread = k_read_off<D>(), vread = v_read_off<D>();
 
-  i32x4 qf[2][D / 32];
+  i32x4 qf[kQB][D / 32];
   load_q<D>(Q, g, qbase, N, qf);
   const float sq = sQ[static_cast<int64_t>(g) * nq + i] * scale_log2;
 
@@ -236,10 +244,12 @@ __global__ __launch_bounds__(BQ) void fwd_i8_kernel(
     return static_cast<unsigned>(j) < static_cast<unsigned>(nk) ? j * BK : 0;
   };
 
-  float m[2] = {kRefInit, kRefInit}, l[2] = {0.0f, 0.0f};
-  f32x16 o[2][D / 32];
+  float m[kQB], l[kQB];
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++)
+  for (int qb = 0; qb < kQB; qb++) { m[qb] = kRefInit; l[qb] = 0.0f; }
+  f32x16 o[kQB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < kQB; qb++)
 #pragma unroll
     for (int db = 0; db < D / 32; db++) o[qb][db] = f32x16{};
 
@@ -259,12 +269,12 @@ __global__ __launch_bounds__(BQ) void fwd_i8_kernel(
       const float svj = jvalid ? sV[static_cast<int64_t>(g) * nk + j] : 0.0f;
 
       // ---- scores and the exact running maximum of every row
-      i32x16 s[2][NB];
+      i32x16 s[kQB][NB];
       qk_i8<D, BK>(kbuf[t % 3], kread, qf, s);
-      float x_max[2];
+      float x_max[kQB];
       if (!masked) {
 #pragma unroll
-        for (int qb = 0; qb < 2; qb++) {
+        for (int qb = 0; qb < kQB; qb++) {
           int im = s[qb][0][0];
 #pragma unroll
           for (int b = 0; b < NB; b++)
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(BQ) void fwd_i8_kernel(
         }
       } else {
 #pragma unroll
-        for (int qb = 0; qb < 2; qb++) {
+        for (int qb = 0; qb < kQB; qb++) {
           float xm = -INFINITY;
 #pragma unroll
           for (int b = 0; b < NB; b++)
@@ -291,9 +301,9 @@ __global__ __launch_bounds__(BQ) void fwd_i8_kernel(
           x_max[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
       }
-      float alpha[2], dmax = -INFINITY;
+      float alpha[kQB], dmax = -INFINITY;
 #pragma unroll
-      for (int qb = 0; qb < 2; qb++) {
+      for (int qb = 0; qb < kQB; qb++) {
         const float mn = fmaxf(m[qb], x_max[qb]);
         alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mn);
         m[qb] = mn;
@@ -316,9 +326,9 @@ __global__ __launch_bounds__(BQ) void fwd_i8_kernel(
       // ---- P8 = rint(Pt * 127 / mP), mP = 2^dm; l sums Pt = y * mP / 127
       const bool any = dm > -INFINITY;
       const float mp127 = any ? __builtin_amdgcn_exp2f(dm - kLog2_127) : 0.0f;  // mP / 127
-      i32x4 pf[2][NB];
+      i32x4 pf[kQB][NB];
 #pragma unroll
-      for (int qb = 0; qb < 2; qb++) {
+      for (int qb = 0; qb < kQB; qb++) {
         const float off = any ? m[qb] + dm - kLog2_127 : 0.0f;
         float ys = 0.0f;
 #pragma unroll
@@ -347,9 +357,12 @@ __global__ __launch_bounds__(BQ) void fwd_i8_kernel(
 
       // ---- O = O * alpha + (mP/127) sV_j (P8 . V8), one channel block at a time
       const float cv = mp127 * svj;
-      if (__ballot(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0ull) {
+      bool resc = false;
 #pragma unroll
-        for (int qb = 0; qb < 2; qb++)
+      for (int qb = 0; qb < kQB; qb++) resc = resc || alpha[qb] != 1.0f;
+      if (__ballot(resc) != 0ull) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; qb++)
 #pragma unroll
           for (int db = 0; db < D / 32; db++)
 #pragma unroll
@@ -357,19 +370,19 @@ __global__ __launch_bounds__(BQ) void fwd_i8_kernel(
       }
 #pragma unroll
       for (int db = 0; db < D / 32; db++) {
-        i32x16 ov0, ov1;
-        pv_block<D, BK>(vbuf[t & 1], vread, pf, db, ov0, ov1);
+        i32x16 ov[kQB];
+        pv_block<D, BK>(vbuf[t & 1], vread, pf, db, ov);
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          o[0][db][r] = __builtin_fmaf(static_cast<float>(ov0[r]), cv, o[0][db][r]);
-          o[1][db][r] = __builtin_fmaf(static_cast<float>(ov1[r]), cv, o[1][db][r]);
-        }
+        for (int qb = 0; qb < kQB; qb++)
+#pragma unroll
+          for (int r = 0; r < 16; r++)
+            o[qb][db][r] = __builtin_fmaf(static_cast<float>(ov[qb][r]), cv, o[qb][db][r]);
       }
     }
   }
 
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++) {
+  for (int qb = 0; qb < kQB; qb++) {
     const float lt = l[qb] + __shfl_xor(l[qb], 32);
     const int row = qbase + 32 * qb + l32;
     if (row < N) {
@@ -397,11 +410,11 @@ __global__ __launch_bounds__(BQ) void fwd_i8_kernel(
 // Debug entry points: the forward kernel's own staging and int8 tile
 // routines on chosen tiles, writing exact int32 products.
 template <int D, int BQ, int BK>
-__global__ __launch_bounds__(BQ) void dbg_qk_kernel(const int8_t* __restrict__ Q,
+__global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void dbg_qk_kernel(const int8_t* __restrict__ Q,
                                                     const int8_t* __restrict__ K, int G, int N,
                                                     int nq, int nk, const int32_t* __restrict__ gij,
                                                     int32_t* __restrict__ S) {
-  constexpr int NW = BQ / 64;
+  constexpr int NW = BQ / kRowsPerWave;
   using L = L8<D, BK, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t kt[1][L::TB];
   const int t = blockIdx.x;
@@ -418,16 +431,16 @@ __global__ __launch_bounds__(BQ) void dbg_qk_kernel(const int8_t* __restrict__ Q
   sg.init();
   const int nrec = jvalid ? N * D : 0;
   L::stage(K + static_cast<int64_t>(g) * N * D, nrec, sg.k, jvalid ? j * BK : 0, kt[0]);
-  i32x4 qf[2][D / 32];
-  load_q<D>(Q, g, i * BQ + w * 64, N, qf);
+  i32x4 qf[kQB][D / 32];
+  load_q<D>(Q, g, i * BQ + w * kRowsPerWave, N, qf);
   wait_loads();
   __syncthreads();
-  i32x16 s[2][BK / 32];
+  i32x16 s[kQB][BK / 32];
   qk_i8<D, BK>(kt[0], k_read_off<D>(), qf, s);
   int32_t* out = S + static_cast<int64_t>(t) * BQ * BK;
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++) {
-    const int qr = w * 64 + 32 * qb + l32;
+  for (int qb = 0; qb < kQB; qb++) {
+    const int qr = w * kRowsPerWave + 32 * qb + l32;
 #pragma unroll
     for (int b = 0; b < BK / 32; b++)
 #pragma unroll
@@ -436,11 +449,11 @@ __global__ __launch_bounds__(BQ) void dbg_qk_kernel(const int8_t* __restrict__ Q
 }
 
 template <int D, int BQ, int BK>
-__global__ __launch_bounds__(BQ) void dbg_pv_kernel(const int8_t* __restrict__ P8,
+__global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void dbg_pv_kernel(const int8_t* __restrict__ P8,
                                                     const int8_t* __restrict__ V, int G, int N,
                                                     int nk, const int32_t* __restrict__ gj,
                                                     int32_t* __restrict__ OV) {
-  constexpr int NW = BQ / 64;
+  constexpr int NW = BQ / kRowsPerWave;
   using L = L8<D, BK, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t vt[1][L::TB];
   const int t = blockIdx.x;
@@ -455,10 +468,10 @@ __global__ __launch_bounds__(BQ) void dbg_pv_kernel(const int8_t* __restrict__ P
   const int nrec = jvalid ? N * D : 0;
   L::stage(V + static_cast<int64_t>(g) * N * D, nrec, sg.v, jvalid ? j * BK : 0, vt[0]);
   // P8 operand: slot s of lane half h carries kv 8(s/4) + 4h + s%4
-  i32x4 pf[2][BK / 32];
+  i32x4 pf[kQB][BK / 32];
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++) {
-    const int8_t* prow = P8 + (static_cast<int64_t>(t) * BQ + w * 64 + 32 * qb + l32) * BK;
+  for (int qb = 0; qb < kQB; qb++) {
+    const int8_t* prow = P8 + (static_cast<int64_t>(t) * BQ + w * kRowsPerWave + 32 * qb + l32) * BK;
 #pragma unroll
     for (int b = 0; b < BK / 32; b++)
 #pragma unroll
@@ -477,11 +490,11 @@ __global__ __launch_bounds__(BQ) void dbg_pv_kernel(const int8_t* __restrict__ P
   const uint32_t vread = v_read_off<D>();
 #pragma unroll
   for (int db = 0; db < D / 32; db++) {
-    i32x16 ov[2];
-    pv_block<D, BK>(vt[0], vread, pf, db, ov[0], ov[1]);
+    i32x16 ov[kQB];
+    pv_block<D, BK>(vt[0], vread, pf, db, ov);
 #pragma unroll
-    for (int qb = 0; qb < 2; qb++) {
-      const int qr = w * 64 + 32 * qb + l32;
+    for (int qb = 0; qb < kQB; qb++) {
+      const int qr = w * kRowsPerWave + 32 * qb + l32;
 #pragma unroll
       for (int r = 0; r < 16; r++) out[qr * D + 32 * db + acc_row(r, h)] = ov[qb][r];
     }
@@ -515,7 +528,7 @@ struct LaunchI8 {
   static hipError_t run(const AttnArgs& a, hipStream_t s) {
     const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
     const uint32_t nwg = static_cast<uint32_t>(a.G) * kNumXcd * ((nq + kNumXcd - 1) / kNumXcd);
-    fwd_i8_kernel<D, BQ, BK><<<nwg, BQ, 0, s>>>(
+    fwd_i8_kernel<D, BQ, BK><<<nwg, BQ / kRowsPerWave * kWave, 0, s>>>(
         static_cast<const int8_t*>(a.Q), a.sQ, static_cast<const int8_t*>(a.K), a.sK,
         static_cast<const int8_t*>(a.V), a.sV, a.row_ptr, a.col_idx, a.col_len, a.mask_G, a.O,
         a.lse, a.N, nq, nk, scale_log2_of(a));
@@ -528,7 +541,7 @@ struct LaunchDbgQk {
   static hipError_t run(const int8_t* Q, const int8_t* K, int G, int N, const int32_t* gij, int n,
                         int32_t* S, hipStream_t s) {
     const int nq = (N + BQ - 1) / BQ, nk = (N + BK - 1) / BK;
-    dbg_qk_kernel<D, BQ, BK><<<n, BQ, 0, s>>>(Q, K, G, N, nq, nk, gij, S);
+    dbg_qk_kernel<D, BQ, BK><<<n, BQ / kRowsPerWave * kWave, 0, s>>>(Q, K, G, N, nq, nk, gij, S);
     return hipGetLastError();
   }
 };
@@ -538,7 +551,7 @@ struct LaunchDbgPv {
   static hipError_t run(const int8_t* P8, const int8_t* V, int G, int N, const int32_t* gj, int n,
                         int32_t* OV, hipStream_t s) {
     const int nk = (N + BK - 1) / BK;
-    dbg_pv_kernel<D, BQ, BK><<<n, BQ, 0, s>>>(P8, V, G, N, nk, gj, OV);
+    dbg_pv_kernel<D, BQ, BK><<<n, BQ / kRowsPerWave * kWave, 0, s>>>(P8, V, G, N, nk, gj, OV);
     return hipGetLastError();
   }
 };
