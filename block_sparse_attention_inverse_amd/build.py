@@ -35,7 +35,11 @@ HIPCC_FLAGS = [
 # per-source extra flags.  The bf16 attention kernel takes no NaN inputs into
 # account (a NaN in Q, K or V gives unspecified output), which lets its row
 # maxima fuse into v_max3 without quieting every operand first.
-EXTRA_FLAGS = {"attn_bf16.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {
+    "attn_bf16.hip": ["-fno-honor-nans"],
+    # the INT8 kernel reads its MFMA results with VALU ops: keep them in VGPRs
+    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _hipcc():

@@ -202,6 +202,44 @@ __device__ __forceinline__ float rows_max(float x) {
   return x;
 }
 
+// P8 = rint(Pt * 127 / mP) for the wave's rows (mP = 2^dm, the tile maximum
+// of Pt), l = l * alpha + sum Pt.  The exponential argument folds the
+// quantisation scale in: y = Pt * 127 / mP = 2^(x - m - dm + log2 127).
+// MASK: columns outside the tile and a tile without real rows give zero.
+template <bool MASK, int NB>
+__device__ __forceinline__ void quantize_tile(const i32x16 (&s)[kQB][NB], float f, const float (&m)[kQB],
+                                              float dm, bool any, int kv0, bool jvalid, int N,
+                                              float mp127, const float (&alpha)[kQB], float (&l)[kQB],
+                                              i32x4 (&pf)[kQB][NB]) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int qb = 0; qb < kQB; qb++) {
+    const float off = any ? m[qb] + dm - kLog2_127 : 0.0f;
+    float ys = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int r = 4 * q4 + e;
+          float y = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[qb][b][r]), f, -off));
+          if constexpr (MASK) {
+            const int kv = kv0 + 32 * b + acc_row(r, h);
+            if (!any || !jvalid || kv >= N) y = 0.0f;
+          }
+          ys += y;
+          // v_cvt_pk_u8_f32 rounds half to even (checked against rintf on
+          // every quarter step of 0..255 and next to every .5)
+          word = __builtin_amdgcn_cvt_pk_u8_f32(y, e, word);
+        }
+        pf[qb][b][q4] = static_cast<int>(word);
+      }
+    l[qb] = l[qb] * alpha[qb] + ys * mp127;
+  }
+}
+
 template <int D, int BQ, int BK>
 __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
     const int8_t* __restrict__ Q, const float* __restrict__ sQ, const int8_t* __restrict__ K,
@@ -327,33 +365,12 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
       const bool any = dm > -INFINITY;
       const float mp127 = any ? __builtin_amdgcn_exp2f(dm - kLog2_127) : 0.0f;  // mP / 127
       i32x4 pf[kQB][NB];
-#pragma unroll
-      for (int qb = 0; qb < kQB; qb++) {
-        const float off = any ? m[qb] + dm - kLog2_127 : 0.0f;
-        float ys = 0.0f;
-#pragma unroll
-        for (int b = 0; b < NB; b++)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; q4++) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-              const int r = 4 * q4 + e;
-              float y = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[qb][b][r]), f, -off));
-              if (masked) {
-                const int kv = kv0 + 32 * b + acc_row(r, h);
-                if (!jvalid || kv >= N) y = 0.0f;
-              }
-              if (!any) y = 0.0f;
-              ys += y;
-              // v_cvt_pk_u8_f32 rounds half to even (checked against rintf on
-              // every quarter step of 0..255 and next to every .5)
-              word = __builtin_amdgcn_cvt_pk_u8_f32(y, e, word);
-            }
-            pf[qb][b][q4] = static_cast<int>(word);
-          }
-        l[qb] = l[qb] * alpha[qb] + ys * mp127;
-      }
+      // masked columns (ragged tail, invalid block) and a tile without real
+      // rows take the checked variant
+      if (masked || !any)
+        quantize_tile<true>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
+      else
+        quantize_tile<false>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
 
       // ---- O = O * alpha + (mP/127) sV_j (P8 . V8), one channel block at a time
       const float cv = mp127 * svj;
