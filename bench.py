@@ -3,9 +3,11 @@
 One step = one pass of the bf16 layer chain over one synthetic batch:
 reorder Q, K, V -> build the block mask (pooled DOT scores, per-row top-k,
 diagonal) -> bf16 block-sparse flash attention -> inverse reorder of O.
-The INT8 chain (reorder -> mask -> quantise Q, K, V -> INT8 attention ->
+The INT8 chain (reorder with quantisation -> mask -> INT8 attention ->
 inverse reorder) is timed in the same run, over the same number of steps,
-and reported under "int8".
+and reported under "int8"; the long-clip layer (118,800 tokens, mask rebuilt
+every step from COSINE block scores with a temporal window) under
+"long_clip".
 
 Workload: the 720p-shaped DiT layer, F=21, H=45, W=80 (75,600 tokens),
 40 heads, d=128, 128x64 blocks, 30% density; inputs resident in HBM.
@@ -120,6 +122,79 @@ def cpu_baseline(cfg, Qn, Kn, Vn, orders, p, budget_s=12.0):
     }
 
 
+def long_clip(args, timed_steps):
+    """The long-clip layer, F=33, H=45, W=80 (118,800 tokens), 24 heads, d=128,
+    128x128 blocks: per step the mask is rebuilt from the current Q and K
+    (COSINE of block sums, top-k at 15 % plus diagonal and temporal window),
+    then bf16 attention; reorder and inverse reorder as in the main chain."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_inverse_amd as bsa
+    from block_sparse_attention_inverse_amd import synth
+
+    cfg = synth.config(5)
+    F, H, W, G, d, N = cfg["F"], cfg["H"], cfg["W"], cfg["G"], cfg["d"], cfg["N"]
+    seed = synth.seed_of(5)
+    orders = synth.make_orders(cfg, seed)
+    log(f"[bench] long clip: generating N={N} G={G} d={d}")
+    Q, K, V = synth.cast_inputs(cfg, *synth.make_qkv(cfg, orders, seed, device="cuda"))
+    od = torch.from_numpy(orders).cuda()
+    p = bsa.mask_params(cfg["Bq"], cfg["Bk"], 1, cfg["rho"], True, cfg["win_T"], cfg["win_r0"])
+    plan = bsa.LayerPlan(G, F, H, W, d, "cuda", p, fused=True)
+
+    def step(ev=None):
+        plan.reorder_fused(Q, K, V, od)
+        if ev:
+            ev[0].record()
+        plan.build_mask_from_sums(od)
+        if ev:
+            ev[1].record()
+        bsa.forward(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk,
+                    out=plan.Op, lse=plan.lse)
+        if ev:
+            ev[2].record()
+        bsa.permute(plan.Op, od, F, H, W, 1, out=plan.O)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    steps = max(3, timed_steps // 2)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        evs[k][0].record()
+        step(evs[k][1:])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    seg = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(3)] for k in range(steps)])
+    seg = seg.mean(axis=0)
+    rp = plan.row_ptr.cpu().numpy()
+    nnz = int(plan.nnz.item())
+    ci = plan.col_idx[:nnz].cpu().numpy()
+    nq, nk = -(-N // p.Bq), -(-N // p.Bk)
+    fl = kept_flops(rp, ci, G, N, p.Bq, p.Bk, d)
+    dense = 4.0 * N * N * d * G
+    log(f"[bench] long clip: {wall * 1e3:.3f} ms/step; segments (ms) {seg}")
+    return {
+        "workload": "long clip: F=33,H=45,W=80 (118800 tokens), 24 heads, d=128, 128x128 blocks, "
+                    "COSINE top-k 15% + diagonal + temporal window (T=2, r0=4), mask rebuilt per step",
+        "steps": steps,
+        "ms_per_step": wall * 1e3,
+        "dense_equiv_tflops": dense / wall / 1e12,
+        "block_density": nnz / (G * nq * nk),
+        "kept_tflop": fl / 1e12,
+        "breakdown_ms": {
+            "reorder_qkv_with_qk_block_sums": float(seg[0]),
+            "build_mask_from_sums": float(seg[1]),
+            "attention": float(seg[2]),
+            "inverse_reorder_and_gaps": float(wall * 1e3 - seg.sum()),
+        },
+        "attention_kept_tflops": fl / (seg[2] / 1e3) / 1e12,
+        "attention_frac_bf16_peak": fl / (seg[2] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +202,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
+    ap.add_argument("--no-long-clip", action="store_true",
+                    help="skip the long-clip layer (dynamic COSINE mask rebuilt every step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 3 plain device copies of 2 GiB (reference dispatches for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -304,6 +381,8 @@ def main():
             "frac_int8_peak": fl_kept / t8 / 1e12 / PEAK_INT8_TOPS,
             "frac_bf16_peak": fl_kept / t8 / 1e12 / PEAK_BF16_TFLOPS,
         }
+    if not args.no_long_clip:
+        result["long_clip"] = long_clip(args, timed_steps=args.steps)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(cfg, Q, K, V, orders, p)
