@@ -54,12 +54,16 @@ COPY_BYTES = 1 << 31  # plain device copy used to calibrate the HBM byte counter
 
 
 def source_hash():
-    """Hash of the bf16 attention kernel's sources: a traffic figure taken on
-    other sources is stale and is not reported."""
+    """Hash of the bf16 attention kernel's sources with comments and blank
+    lines dropped: a traffic figure taken on other code is stale and is not
+    reported (an edit to comments alone keeps it)."""
     h = hashlib.sha256()
     for name in ATTN_SOURCES:
-        with open(os.path.join(ROOT, "block_sparse_attention_inverse_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "block_sparse_attention_inverse_amd", "csrc", name)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -10,14 +10,12 @@
 // read from LDS feeds two MFMAs.  One wave per SIMD (two workgroups per CU).
 //
 // Products (v_mfma_f32_32x32x16_bf16), per 32-row kv half-tile u:
-//   S_u^T = K_u . Qc^T - m   A = K rows from LDS, B = Q fragments held in
-//                            registers, pre-scaled by c = sm_scale*log2(e);
-//                            the accumulator starts at -m (the row's running
-//                            reference), so the scores arrive in log2 units
-//                            relative to m: P = exp2(S) needs no VALU op
-//                            besides the exponential.  Every lane holds one
-//                            query row; lane half h, slot r carries kv
-//                            8(r/4) + 4h + r%4 of the half.
+//   S_u^T = K_u . Q^T - m    A = K rows from LDS, B = Q fragments held in
+//                            AGPRs; the accumulator starts at -m (the row's
+//                            reference), so each probability is one multiply
+//                            by c = sm_scale*log2(e) and one exp2.  Every
+//                            lane holds one query row; lane half h, slot r
+//                            carries kv 8(r/4) + 4h + r%4 of the half.
 //   O^T += V_u^T . P_u^T     A = V^T read with ds_read_b64_tr_b16 (the
 //                            transposing LDS read) from row-major V, B = P
 //                            converted to bf16 in registers: slots 8s..8s+7
@@ -31,13 +29,14 @@
 // so the exponentials are spread over both products.  Two S and two P
 // register sets alternate between steps.
 //
-// Reference m: the first half-tile of a row sets it to the exact row maximum;
-// afterwards it only moves when a half-tile's row sum exceeds 2^16 (scores
-// rose far above m), in a rare uniform branch that raises m to the exact
-// maximum, redoes that half's exponentials, and rescales O and l.  O = acc / l
-// does not depend on m, so the only requirement on m is that no exponent
-// overflows.  The first half-tile of a row whose columns are all masked
-// leaves m unset until a real column arrives.
+// Reference m: the first half-tile of a row sets it to that half-tile's
+// exact row maximum and it never moves afterwards.  O = acc / l does not
+// depend on m, so the only requirement is that no exponential overflows: a
+// half-tile row sum above 2^96 (later scores far above m), or a row that ends
+// with no weight, raises a flag, and a workgroup with the flag set recomputes
+// its rows on an exact two-pass path (row maxima over every kept column
+// first, then O and l against them).  The first half-tile of a row whose
+// columns are all masked leaves m at 0.
 //
 // K and V move HBM -> LDS in 64-row sub-tiles with 16-byte buffer loads that
 // write LDS directly, double-buffered (64 KB per workgroup).  LDS chunk c of
