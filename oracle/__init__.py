@@ -53,6 +53,9 @@ def _load():
         "oracle_int8_qk_tile": (_I, [_P, _P, _I, _L, _I, _I, _I, _L, _L, _P]),
         "oracle_int8_pv_tile": (_I, [_P, _P, _I, _L, _I, _I, _I, _L, _P]),
         "oracle_sics_scores": (_I, [_P, _I, _L, _L, _I, _I, _I, _I, _I, _I, _P]),
+        "oracle_block_stats": (_I, [_P, _P, _I, _L, _I, _I, _D, _D, _D, _P, _P, _P, _P, _P]),
+        "oracle_paro_metric": (_I, [_P, _P, _P, _I, _L, _I, _I, _I, _D, _P]),
+        "oracle_mass_select": (_I, [_P, _I, _L, _I, _I, ctypes.c_float, _I, _P, _P, _L, _P]),
         "oracle_num_threads": (_I, []),
     }
     for name, (res, args) in sig.items():
@@ -306,3 +309,74 @@ def int8_pv_tile(P8, Vq, g, j, Bq, Bk):
     OV = np.empty((Bq, d), dtype=np.int32)
     _check(_load().oracle_int8_pv_tile(_ptr(P8), _ptr(Vq), g, N, d, Bq, Bk, j, _ptr(OV)), "pv")
     return OV
+
+
+def block_stats(Qp, Kp, B, eps, sm_scale=None, delta=1e-3):
+    """Block statistics of the dense fp64 post-softmax map of reordered bf16
+    Qp, Kp [G][N][d] (PAROAttention calibration): dict of cnt (entries
+    below eps), cnt_lo / cnt_hi (below eps*(1 -/+ delta)), sum, max, each
+    [G][nb][nb]."""
+    Qp = np.ascontiguousarray(Qp, dtype=np.uint16)
+    Kp = np.ascontiguousarray(Kp, dtype=np.uint16)
+    G, N, d = Qp.shape
+    nb = (N + B - 1) // B
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = {k: np.empty((G, nb, nb), dtype=np.int32) for k in ("cnt", "cnt_lo", "cnt_hi")}
+    out["sum"] = np.empty((G, nb, nb), dtype=np.float64)
+    out["max"] = np.empty((G, nb, nb), dtype=np.float64)
+    _check(_load().oracle_block_stats(_ptr(Qp), _ptr(Kp), G, N, d, B, float(sm_scale), float(eps),
+                                      float(delta), _ptr(out["cnt"]), _ptr(out["cnt_lo"]),
+                                      _ptr(out["cnt_hi"]), _ptr(out["sum"]), _ptr(out["max"])),
+           "block_stats")
+    return out
+
+
+def paro_metric(cnt, bsum, bmax, N, B, sigma_num, sigma_den, alpha):
+    """Per head (M, r, Ibar) in fp64 from one order's block statistics
+    (cnt int32, sum and max fp32, [G][nb][nb]): r = share of sparse blocks,
+    Ibar = mean block incoherence, M = (1 - r) + alpha*Ibar."""
+    cnt = np.ascontiguousarray(cnt, dtype=np.int32)
+    bsum = np.ascontiguousarray(bsum, dtype=np.float32)
+    bmax = np.ascontiguousarray(bmax, dtype=np.float32)
+    G = cnt.shape[0]
+    out = np.empty((G, 3), dtype=np.float64)
+    _check(_load().oracle_paro_metric(_ptr(cnt), _ptr(bsum), _ptr(bmax), G, N, B, sigma_num,
+                                      sigma_den, float(alpha), _ptr(out)), "paro_metric")
+    return out
+
+
+def paro_select(metric):
+    """Per head, the order code with the smallest M (metric [G][6]); ties go
+    to the lowest code."""
+    return np.argmin(np.asarray(metric), axis=1).astype(np.uint8)
+
+
+def mass_select(keys, N, Bq, Bk, mass, force_diag=1):
+    """Static mask by block-sum thresholding: keys fp32 [G][nq][nk] (block
+    sums); returns (row_ptr, col_idx) int32."""
+    keys = np.ascontiguousarray(keys, dtype=np.float32)
+    G, nq, nk = keys.shape
+    row_ptr = np.empty(G * nq + 1, dtype=np.int32)
+    cap = G * nq * nk
+    col_idx = np.empty(max(cap, 1), dtype=np.int32)
+    nnz = ctypes.c_int64(0)
+    _check(_load().oracle_mass_select(_ptr(keys), G, N, Bq, Bk, ctypes.c_float(mass), force_diag,
+                                      _ptr(row_ptr), _ptr(col_idx), cap, ctypes.byref(nnz)),
+           "mass_select")
+    return row_ptr, col_idx[: nnz.value].copy()
+
+
+def bits_to_csr(bits, nk):
+    """CSR of a block bitmask: bits uint64 [R][words], bit j % 64 of word
+    j // 64 set keeps kv-block j; bits at j >= nk are ignored.  The kept
+    indices of each row in ascending order."""
+    bits = np.asarray(bits, dtype=np.uint64)
+    R = bits.shape[0]
+    row_ptr = np.zeros(R + 1, dtype=np.int32)
+    cols = []
+    for r in range(R):
+        row = [j for j in range(nk) if (int(bits[r, j // 64]) >> (j % 64)) & 1]
+        cols.extend(row)
+        row_ptr[r + 1] = row_ptr[r] + len(row)
+    return row_ptr, np.asarray(cols, dtype=np.int32)

@@ -66,3 +66,26 @@ def window_sets(order, F, H, W, Bq, Bk, T, r0):
                 row.append(j)
         out.append(row)
     return out
+
+
+def block_stats(Q, K, B, eps, scale):
+    """Dense softmax map of one head (Q, K: lists of rows) cut into B x B
+    blocks: returns (cnt, sum, max) as nested lists [nb][nb], with every row
+    normalised by an exactly rounded sum."""
+    N = len(Q)
+    nb = -(-N // B)
+    cnt = [[0] * nb for _ in range(nb)]
+    sm = [[[] for _ in range(nb)] for _ in range(nb)]
+    mx = [[0.0] * nb for _ in range(nb)]
+    for r in range(N):
+        s = [scale * math.fsum(a * b for a, b in zip(Q[r], K[c])) for c in range(N)]
+        top = max(s)
+        e = [math.exp(x - top) for x in s]
+        tot = math.fsum(e)
+        for c in range(N):
+            a = e[c] / tot
+            i, j = r // B, c // B
+            cnt[i][j] += a < eps
+            sm[i][j].append(a)
+            mx[i][j] = max(mx[i][j], a)
+    return cnt, [[math.fsum(v) for v in row] for row in sm], mx

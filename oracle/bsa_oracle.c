@@ -713,6 +713,172 @@ int oracle_int8_pv_tile(const int8_t *P8, const int8_t *Vq, int g, int64_t N, in
   return 0;
 }
 
+/* ------------------------------------------------------------------------
+ * Offline calibration, part 1: block statistics of the dense post-softmax
+ * map.  [PARO] key machinery: the axis order is chosen offline from the
+ * post-softmax attention map, by how many of its blocks are mostly below a
+ * small threshold (sparsifiability) and by each block's quantisation
+ * incoherence (largest over mean |A| inside the block); referee minor
+ * comment on Eq. (1): n^{<eps}_{ij} counts the entries of block (i, j)
+ * below eps.  For head g of reordered bf16 Qp, Kp [G][N][d], in fp64:
+ *   A[r][c] = exp(s*q_r.k_c) / sum over all N columns c' of exp(s*q_r.k_c')
+ * and for the B x B block (i, j), over its real rows and columns:
+ *   cnt = #{A < eps},  sum = sum of A,  max = max of A.
+ * cnt_lo / cnt_hi (either may be NULL) count A < eps*(1-delta) and
+ * A < eps*(1+delta): a count taken in lower precision lies between them.
+ * Outputs [G][nb][nb], nb = ceil(N/B).
+ * ---------------------------------------------------------------------- */
+int oracle_block_stats(const uint16_t *Qp, const uint16_t *Kp, int G, int64_t N, int d, int B,
+                       double sm_scale, double eps, double delta, int32_t *cnt, int32_t *cnt_lo,
+                       int32_t *cnt_hi, double *bsum, double *bmax) {
+  if (!Qp || !Kp || !cnt || !bsum || !bmax || G <= 0 || N <= 0 || d <= 0 || B <= 0) return -1;
+  const int64_t nb = (N + B - 1) / B;
+  const double lo = eps * (1.0 - delta), hi = eps * (1.0 + delta);
+  for (int g = 0; g < G; g++) {
+    const uint16_t *Q = Qp + (int64_t)g * N * d, *K = Kp + (int64_t)g * N * d;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t i = 0; i < nb; i++) {
+      double *srow = (double *)malloc(sizeof(double) * (size_t)N);
+      double *qv = (double *)malloc(sizeof(double) * (size_t)d);
+      const int64_t base = ((int64_t)g * nb + i) * nb;
+      for (int64_t j = 0; j < nb; j++) {
+        cnt[base + j] = 0;
+        if (cnt_lo) cnt_lo[base + j] = 0;
+        if (cnt_hi) cnt_hi[base + j] = 0;
+        bsum[base + j] = 0.0;
+        bmax[base + j] = 0.0;
+      }
+      const int64_t r1 = (i + 1) * B < N ? (i + 1) * B : N;
+      for (int64_t r = i * B; r < r1; r++) {
+        for (int c = 0; c < d; c++) qv[c] = bf16_to_f32(Q[r * d + c]);
+        double mx = -INFINITY;
+        for (int64_t m = 0; m < N; m++) {
+          double acc = 0.0;
+          for (int c = 0; c < d; c++) acc += qv[c] * (double)bf16_to_f32(K[m * d + c]);
+          srow[m] = sm_scale * acc;
+          if (srow[m] > mx) mx = srow[m];
+        }
+        double l = 0.0;
+        for (int64_t m = 0; m < N; m++) l += exp(srow[m] - mx);
+        for (int64_t m = 0; m < N; m++) {
+          const double a = exp(srow[m] - mx) / l;
+          const int64_t t = base + m / B;
+          cnt[t] += a < eps;
+          if (cnt_lo) cnt_lo[t] += a < lo;
+          if (cnt_hi) cnt_hi[t] += a < hi;
+          bsum[t] += a;
+          if (a > bmax[t]) bmax[t] = a;
+        }
+      }
+      free(srow); free(qv);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Offline calibration, part 2: the order metric.  [PARO] key machinery and
+ * the referee's major comment on Sec. 4.1 Eq. (3): the metric balances
+ * block sparsifiability against quantisation incoherence with a weight
+ * alpha whose value the pages do not give; the pages' example thresholds
+ * are eps = 1e-3 and sigma = 90 %.  Reading taken here, per head, from the
+ * block statistics of one order (fp32 cnt/sum/max as a kernel emits them):
+ *   block (i, j) is sparse iff cnt * sigma_den >= sigma_num * area
+ *     (area = real rows x real columns; exact integers);
+ *   r    = (number of sparse blocks) / nb^2;
+ *   inc  = max * area / sum for a block with sum > 0, else 1;
+ *   Ibar = mean of inc over all nb^2 blocks;
+ *   M    = (1 - r) + alpha * Ibar            (lower is better).
+ * out [G][3] = (M, r, Ibar), fp64.
+ * ---------------------------------------------------------------------- */
+int oracle_paro_metric(const int32_t *cnt, const float *bsum, const float *bmax, int G,
+                       int64_t N, int B, int sigma_num, int sigma_den, double alpha,
+                       double *out) {
+  if (!cnt || !bsum || !bmax || !out || G <= 0 || N <= 0 || B <= 0) return -1;
+  if (sigma_den <= 0 || sigma_num < 0) return -1;
+  const int64_t nb = (N + B - 1) / B;
+  for (int g = 0; g < G; g++) {
+    int64_t nsparse = 0;
+    double isum = 0.0;
+    for (int64_t i = 0; i < nb; i++)
+      for (int64_t j = 0; j < nb; j++) {
+        const int64_t t = ((int64_t)g * nb + i) * nb + j;
+        const int64_t area = block_len(i, B, N) * block_len(j, B, N);
+        if ((int64_t)cnt[t] * sigma_den >= (int64_t)sigma_num * area) nsparse++;
+        isum += bsum[t] > 0.0f ? (double)bmax[t] * (double)area / (double)bsum[t] : 1.0;
+      }
+    const double nblk = (double)nb * (double)nb;
+    const double r = (double)nsparse / nblk, ibar = isum / nblk;
+    out[3 * g + 0] = (1.0 - r) + alpha * ibar;
+    out[3 * g + 1] = r;
+    out[3 * g + 2] = ibar;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Offline calibration, part 3: the static mask by block-sum thresholding.
+ * [PARO] key machinery and core discovery: the static block mask keeps
+ * blocks selected by thresholding the block sums of the post-softmax map.
+ * Reading taken here (the threshold as a share of each row's mass): for
+ * q-block row i of head g, the kv-blocks in (key descending, index
+ * ascending) order, keys = block sums with anything not > 0 taken as +0;
+ * P_k = fp32 running sum of the first k keys (sequential adds from +0);
+ * total = P_nk; t = total * mass (one fp32 multiply); k* = the smallest
+ * k >= 1 with P_k >= t.  The row keeps the first k* blocks and, with
+ * force_diag, every kv-block overlapping the q-block's rows; CSR ascending.
+ * keys fp32 [G][nq][nk].  Returns -3 when cap is too small.
+ * ---------------------------------------------------------------------- */
+static float canon_key(float x) { return x > 0.0f ? x : 0.0f; }
+
+int oracle_mass_select(const float *keys, int G, int64_t N, int Bq, int Bk, float mass,
+                       int force_diag, int32_t *row_ptr, int32_t *col_idx, int64_t cap,
+                       int64_t *nnz_out) {
+  if (!keys || !row_ptr || G <= 0 || N <= 0 || Bq <= 0 || Bk <= 0) return -1;
+  const int64_t nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+  float *ck = (float *)malloc(sizeof(float) * (size_t)nk);
+  int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)nk);
+  uint8_t *keep = (uint8_t *)malloc((size_t)nk);
+  if (!ck || !idx || !keep) { free(ck); free(idx); free(keep); return -2; }
+  int64_t pos = 0;
+  int rc = 0;
+  for (int64_t row = 0; row < (int64_t)G * nq; row++) {
+    const int64_t i = row % nq;
+    for (int64_t j = 0; j < nk; j++) { ck[j] = canon_key(keys[row * nk + j]); idx[j] = (int32_t)j; }
+    g_sort_keys = ck;
+    qsort(idx, (size_t)nk, sizeof(int32_t), cmp_key_desc_idx_asc);
+    float total = 0.0f;
+    for (int64_t t = 0; t < nk; t++) total += ck[idx[t]];
+    const float thr = total * mass;
+    int64_t kstar = nk;
+    float run = 0.0f;
+    for (int64_t t = 0; t < nk; t++) {
+      run += ck[idx[t]];
+      if (run >= thr) { kstar = t + 1; break; }
+    }
+    memset(keep, 0, (size_t)nk);
+    for (int64_t t = 0; t < kstar; t++) keep[idx[t]] = 1;
+    if (force_diag) {
+      const int64_t q0 = i * Bq, q1 = (q0 + Bq < N ? q0 + Bq : N);
+      for (int64_t j = 0; j < nk; j++) {
+        const int64_t k0 = j * Bk, k1 = (k0 + Bk < N ? k0 + Bk : N);
+        if (k0 < q1 && q0 < k1) keep[j] = 1;
+      }
+    }
+    row_ptr[row] = (int32_t)pos;
+    for (int64_t j = 0; j < nk; j++)
+      if (keep[j]) {
+        if (col_idx && pos < cap) col_idx[pos] = (int32_t)j;
+        else rc = -3;
+        pos++;
+      }
+  }
+  row_ptr[(int64_t)G * nq] = (int32_t)pos;
+  if (nnz_out) *nnz_out = pos;
+  free(ck); free(idx); free(keep);
+  return rc;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -666,3 +666,207 @@ def test_int8_p_quantisation_error_bound(orc):
             bound = (1.0 / 254.0) * vsum  # per channel
             assert np.all(np.abs(O8[bi, r_] - Oe[bi, r_]) <= bound + 1e-12)
     assert np.max(np.abs(O8 - Oe)) > 0  # the quantisation does act
+
+
+# ------------------------------------------------- offline calibration (PARO)
+def _bf16_pair(seed, G, N, d, scale=1.0):
+    r = rng(seed)
+    q = to_bf16_bits(scale * r.standard_normal((G, N, d)).astype(np.float32))
+    k = to_bf16_bits(scale * r.standard_normal((G, N, d)).astype(np.float32))
+    return q, k
+
+
+@pytest.mark.parametrize("N,B", [(200, 64), (130, 32), (96, 96)])
+def test_block_stats_rows_sum_to_one(orc, N, B):
+    """Every softmax row sums to 1, so the block sums of q-block row i add up
+    to its number of real rows; counts and maxima stay in range."""
+    G, d = 2, 64
+    q, k = _bf16_pair(31, G, N, d, 1.5)
+    st = orc.block_stats(q, k, B, 1e-3)
+    nb = -(-N // B)
+    lens = np.array([min(B, N - i * B) for i in range(nb)])
+    assert np.allclose(st["sum"].sum(axis=2), lens[None, :], rtol=0, atol=1e-12)
+    area = lens[:, None] * lens[None, :]
+    assert np.all((st["cnt"] >= 0) & (st["cnt"] <= area))
+    assert np.all((st["cnt_lo"] <= st["cnt"]) & (st["cnt"] <= st["cnt_hi"]))
+    assert np.all(st["max"] <= 1.0) and np.all(st["max"] * area >= st["sum"] * (1 - 1e-12))
+
+
+@pytest.mark.parametrize("eps,all_below", [(1e-3, False), (1e-2, True)])
+def test_block_stats_uniform_map(orc, eps, all_below):
+    """Identical keys give every row the uniform distribution 1/N: block
+    sums area/N, maxima 1/N, and every entry below eps iff 1/N < eps."""
+    G, N, d, B = 1, 200, 64, 64
+    q, _ = _bf16_pair(32, G, N, d)
+    k = np.repeat(q[:, :1, :], N, axis=1)
+    st = orc.block_stats(q, k, B, eps)
+    nb = -(-N // B)
+    lens = np.array([min(B, N - i * B) for i in range(nb)])
+    area = lens[:, None] * lens[None, :]
+    assert np.allclose(st["sum"][0], area / N, rtol=1e-12, atol=0)
+    assert np.allclose(st["max"][0], 1.0 / N, rtol=1e-12, atol=0)
+    assert np.array_equal(st["cnt"][0], area if all_below else np.zeros_like(area))
+
+
+def _cluster_case(N, d, B, v):
+    """Tokens of block b carry the value v in channel b only (Q = K), so the
+    score is s*v^2 inside a block and 0 across blocks."""
+    x = np.zeros((1, N, d), np.float32)
+    for n in range(N):
+        x[0, n, n // B] = v
+    return to_bf16_bits(x)
+
+
+def test_block_stats_block_diagonal_closed_form(orc):
+    """Within-block score a = v^2/sqrt(d), cross-block 0: the row of a token
+    in a block of length L is e^a / (L e^a + N - L) inside its block and
+    1 / (L e^a + N - L) elsewhere."""
+    N, d, B, v = 200, 64, 64, 4.0
+    x = _cluster_case(N, d, B, v)
+    a = v * v / math.sqrt(d)
+    eps = 1e-3
+    st = orc.block_stats(x, x, B, eps)
+    nb = -(-N // B)
+    lens = [min(B, N - i * B) for i in range(nb)]
+    for i in range(nb):
+        den = lens[i] * math.exp(a) + (N - lens[i])
+        pin, pout = math.exp(a) / den, 1.0 / den
+        for j in range(nb):
+            p = pin if i == j else pout
+            area = lens[i] * lens[j]
+            assert st["sum"][0, i, j] == pytest.approx(area * p, rel=1e-12)
+            assert st["max"][0, i, j] == pytest.approx(p, rel=1e-12)
+            assert st["cnt"][0, i, j] == (area if p < eps else 0)
+
+
+def test_block_stats_brute_force(orc):
+    """Tiny dense maps against the pure-Python reading (exact sums)."""
+    N, d, B = 11, 8, 3
+    q, k = _bf16_pair(33, 1, N, d, 2.0)
+    st = orc.block_stats(q, k, B, 0.02, sm_scale=0.5)
+    Q = bits_to_f64(q[0]).tolist()
+    K = bits_to_f64(k[0]).tolist()
+    cnt, sm, mx = brute.block_stats(Q, K, B, 0.02, 0.5)
+    assert st["cnt"][0].tolist() == cnt
+    assert np.allclose(st["sum"][0], np.array(sm), rtol=1e-13, atol=1e-16)
+    assert np.allclose(st["max"][0], np.array(mx), rtol=1e-13, atol=0)
+
+
+def test_paro_metric_worked_example(orc):
+    """The hand-derived example in golden/paro_metric_example.txt."""
+    rows, expect = [], {}
+    with open(os.path.join(GOLDEN, "paro_metric_example.txt")) as f:
+        for line in f:
+            t = line.split()
+            if not t or t[0].startswith("#"):
+                continue
+            if t[0] == "expect":
+                expect[t[1]] = float(t[2])
+            else:
+                rows.append(t)
+    cnt = np.zeros((1, 2, 2), np.int32)
+    bs = np.zeros((1, 2, 2), np.float32)
+    bm = np.zeros((1, 2, 2), np.float32)
+    for i, j, c, s_, m_ in rows:
+        cnt[0, int(i), int(j)], bs[0, int(i), int(j)], bm[0, int(i), int(j)] = int(c), float(s_), float(m_)
+    for alpha in (0.0, 0.25, 3.0):
+        M, r, ib = orc.paro_metric(cnt, bs, bm, 4, 2, 3, 4, alpha)[0]
+        assert r == expect["r"] and ib == expect["ibar"]
+        assert M == (1 - expect["r"]) + alpha * expect["ibar"]
+
+
+def test_paro_metric_special_maps(orc):
+    """Uniform map: every block has incoherence 1; all blocks sparse (r = 1)
+    when 1/N < eps, none otherwise.  Block-diagonal map with eps between
+    the two levels: exactly the off-diagonal blocks are sparse."""
+    G, N, d, B = 1, 256, 64, 64
+    q, _ = _bf16_pair(34, G, N, d)
+    k = np.repeat(q[:, :1, :], N, axis=1)
+    nb = N // B
+    for eps, r_want in ((1e-2, 1.0), (1e-3, 0.0)):
+        st = orc.block_stats(q, k, B, eps)
+        M, r, ib = orc.paro_metric(st["cnt"], st["sum"].astype(np.float32),
+                                   st["max"].astype(np.float32), N, B, 9, 10, 0.5)[0]
+        assert r == r_want and ib == pytest.approx(1.0, rel=1e-6)
+        assert M == pytest.approx(1 - r_want + 0.5, rel=1e-6)
+    x = _cluster_case(N, d, B, 8.0)  # levels e^8/190976 ~ 1.6e-2 and 1/190976 ~ 5.2e-6
+    st = orc.block_stats(x, x, B, 1e-3)
+    M, r, ib = orc.paro_metric(st["cnt"], st["sum"].astype(np.float32),
+                               st["max"].astype(np.float32), N, B, 9, 10, 0.0)[0]
+    assert r == (nb * nb - nb) / (nb * nb) and M == pytest.approx(1 - r, abs=1e-15)
+    assert ib == pytest.approx(1.0, rel=1e-6)
+
+
+def test_paro_metric_sigma_boundary(orc):
+    """sigma compares exact integers: cnt = 0.9*area is sparse, one less is not."""
+    cnt = np.array([[[3686, 3685]]], np.int32)  # area 64*64 = 4096, 0.9*4096 = 3686.4
+    one = np.ones((1, 1, 2), np.float32)
+    # N = 128 with B = 64 would be 2 x 2; use N = 64, B = 64 -> one block row, cols sliced
+    r = orc.paro_metric(cnt[:, :, :1], one[:, :, :1], one[:, :, :1], 64, 64, 9, 10, 0)[0, 1]
+    assert r == 0.0  # 3686*10 = 36860 < 9*4096 = 36864
+    cnt2 = np.array([[[3687]]], np.int32)
+    assert orc.paro_metric(cnt2, one[:, :, :1], one[:, :, :1], 64, 64, 9, 10, 0)[0, 1] == 1.0
+    cnt3 = np.array([[[4096]]], np.int32)  # sigma = 1 needs every entry
+    assert orc.paro_metric(cnt3, one[:, :, :1], one[:, :, :1], 64, 64, 1, 1, 0)[0, 1] == 1.0
+
+
+def test_paro_select_ties_lowest(orc):
+    m = np.array([[3.0, 1.0, 1.0, 2.0, 5.0, 1.5], [0.1] * 6], np.float64)
+    assert orc.paro_select(m).tolist() == [1, 0]
+
+
+def test_mass_select_worked_examples(orc):
+    """Hand-derived rows in golden/mass_select_examples.txt (one q-block row
+    each, nk = len(keys), no forced blocks)."""
+    with open(os.path.join(GOLDEN, "mass_select_examples.txt")) as f:
+        cases = [l for l in f if l.strip() and not l.startswith("#")]
+    assert len(cases) == 9
+    for line in cases:
+        mass, keys, kept = (p.strip() for p in line.split("|"))
+        keys = np.array([float(x) for x in keys.split()], np.float32)
+        nk = len(keys)
+        rp, ci = orc.mass_select(keys[None, None, :], nk, nk, 1, float(mass), force_diag=0)
+        assert ci.tolist() == [int(x) for x in kept.split()], line
+
+
+def test_mass_select_cover_and_minimal(orc):
+    """On random block sums (multiples of 2^-20, so every fp32 sum below is
+    exact): the kept blocks carry at least mass * total, dropping the
+    smallest kept block falls short, and the diagonal is added on top."""
+    r = rng(35)
+    G, N, B = 2, 640, 64
+    nb = N // B
+    keys = (r.integers(0, 1 << 12, size=(G, nb, nb)) / float(1 << 20)).astype(np.float32)
+    for mass in (0.3, 0.75, 0.95, 1.0):
+        rp, ci = orc.mass_select(keys, N, B, B, mass, force_diag=0)
+        rpd, cid = orc.mass_select(keys, N, B, B, mass, force_diag=1)
+        t32 = np.float32(mass)
+        for row in range(G * nb):
+            kk = keys.reshape(G * nb, nb)[row].astype(np.float64)
+            kept = ci[rp[row]:rp[row + 1]]
+            thr = float(np.float32(np.float32(kk.sum()) * t32))
+            assert kk[kept].sum() >= thr
+            assert kk[kept].sum() - kk[kept].min() < thr or len(kept) == 1
+            # no unkept block beats a kept one
+            rest = np.setdiff1d(np.arange(nb), kept)
+            if len(rest):
+                assert kk[rest].max() <= kk[kept].min()
+            i = row % nb
+            assert cid[rpd[row]:rpd[row + 1]].tolist() == sorted(set(kept.tolist()) | {i})
+
+
+def test_bits_to_csr_round_trip(orc):
+    """A random CSR packed into 64-bit words (bit j % 64 of word j // 64)
+    comes back unchanged; bits past nk are ignored."""
+    r = rng(36)
+    R, nk = 9, 150
+    words = -(-nk // 64)
+    sets = [sorted(r.choice(nk, size=int(r.integers(0, nk + 1)), replace=False).tolist()) for _ in range(R)]
+    bits = np.zeros((R, words), np.uint64)
+    for row, s_ in enumerate(sets):
+        for j in s_:
+            bits[row, j // 64] |= np.uint64(1) << np.uint64(j % 64)
+    bits[:, -1] |= np.uint64(1) << np.uint64(63)  # j = 191 >= nk
+    rp, ci = orc.bits_to_csr(bits, nk)
+    for row, s_ in enumerate(sets):
+        assert ci[rp[row]:rp[row + 1]].tolist() == s_
