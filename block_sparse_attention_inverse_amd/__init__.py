@@ -4,13 +4,18 @@ Public surface (Python names mirror the C ABI in include/bsa.h):
 ``permute``, ``mask_capacity``, ``mask_workspace``, ``build_mask``,
 ``permute_pool``, ``build_mask_pooled``, ``order_workspace``,
 ``order_scores``, ``select_orders``, ``quantize_int8``, ``forward``,
-``forward_int8``, ``debug_int8_qk``, ``debug_int8_pv``, plus ``LayerPlan`` / ``layer_forward`` which chain them.
+``forward_int8``, ``debug_int8_qk``, ``debug_int8_pv``, the offline calibration
+``attn_block_stats``, ``paro_metric``, ``paro_select`` (chained by
+``paro_calibrate``), the static masks ``mask_from_block_sums`` and
+``mask_from_bits``, plus ``LayerPlan`` / ``layer_forward`` which chain the
+per-step calls.
 The HIP library is loaded on first use and must be built; there is no
 fallback path.  ``synth`` holds the seeded synthetic workload generators.
 """
 from .api import (  # noqa: F401
     LayerPlan,
     abi_version,
+    attn_block_stats,
     build_mask,
     build_mask_pooled,
     debug_int8_pv,
@@ -20,10 +25,15 @@ from .api import (  # noqa: F401
     last_error,
     layer_forward,
     mask_capacity,
+    mask_from_bits,
+    mask_from_block_sums,
     mask_params,
     mask_workspace,
     order_scores,
     order_workspace,
+    paro_calibrate,
+    paro_metric,
+    paro_select,
     permute,
     permute_pool,
     quantize_int8,

@@ -50,6 +50,13 @@ SIGNATURES = {
                               _F, _P]),
     "bsa_debug_int8_qk": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P]),
     "bsa_debug_int8_pv": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P]),
+    "bsa_attn_block_stats": (_I, [_P, _P, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P]),
+    "bsa_paro_metric": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
+    "bsa_paro_select": (_I, [_P, _I, _P, _P]),
+    "bsa_mask_sums_workspace": (_L, [_I, _I, _I, _I]),
+    "bsa_mask_from_block_sums": (_I, [_P, _I, _I, _I, _I, _F, _I, _P, _P, _L, _P, _P, _L, _P]),
+    "bsa_mask_bits_workspace": (_L, [_I]),
+    "bsa_mask_from_bits": (_I, [_P, _I, _I, _P, _P, _L, _P, _P, _L, _P]),
 }
 
 _lib = None

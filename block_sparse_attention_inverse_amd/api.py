@@ -232,6 +232,127 @@ def select_orders(scores_a, scores_b=None, out=None):
     return out
 
 
+def attn_block_stats(Qp, Kp, B, eps=1e-3, sm_scale=0.0, out=None):
+    """bsa_attn_block_stats: per-block statistics of the dense post-softmax
+    map of reordered bf16 Qp, Kp [G][N][d].  Returns (cnt int32, bsum fp32,
+    bmax fp32), each [G][nb][nb] with nb = ceil(N/B)."""
+    _dev(Qp, Kp)
+    G, N, d = Qp.shape
+    if Kp.shape != Qp.shape or Qp.dtype != torch.bfloat16 or Kp.dtype != torch.bfloat16:
+        raise ValueError("Qp and Kp must be bf16 [G][N][d] of one shape")
+    if not (Qp.is_contiguous() and Kp.is_contiguous()):
+        raise ValueError("Qp and Kp must be contiguous")
+    nb = (N + B - 1) // B
+    if out is None:
+        out = (torch.empty((G, nb, nb), dtype=torch.int32, device=Qp.device),
+               torch.empty((G, nb, nb), dtype=torch.float32, device=Qp.device),
+               torch.empty((G, nb, nb), dtype=torch.float32, device=Qp.device))
+    cnt, bsum, bmax = out
+    for t, dt in ((cnt, torch.int32), (bsum, torch.float32), (bmax, torch.float32)):
+        if t.shape != (G, nb, nb) or t.dtype != dt or not t.is_contiguous():
+            raise ValueError("outputs must be contiguous [G][nb][nb] (int32, fp32, fp32)")
+    _dev(cnt, bsum, bmax)
+    check(_lib.load().bsa_attn_block_stats(_ptr(Qp), _ptr(Kp), G, N, d, B, float(sm_scale),
+                                           float(eps), _ptr(cnt), _ptr(bsum), _ptr(bmax), _stream()))
+    return cnt, bsum, bmax
+
+
+def paro_metric(cnt, bsum, bmax, N, B, order, sigma=(9, 10), alpha=0.0, stats=None):
+    """bsa_paro_metric: writes stats[g][order] = (M, r, Ibar) from one
+    order's block statistics.  ``stats``: fp32 [G][6][3] (new if None)."""
+    G = cnt.shape[0]
+    if stats is None:
+        stats = torch.full((G, 6, 3), float("nan"), dtype=torch.float32, device=cnt.device)
+    if stats.shape != (G, 6, 3) or stats.dtype != torch.float32 or not stats.is_contiguous():
+        raise ValueError("stats must be contiguous fp32 [G][6][3]")
+    nb = (N + B - 1) // B
+    for t in (cnt, bsum, bmax):
+        if t.shape != (G, nb, nb) or not t.is_contiguous():
+            raise ValueError("block statistics must be contiguous [G][nb][nb]")
+    if cnt.dtype != torch.int32 or bsum.dtype != torch.float32 or bmax.dtype != torch.float32:
+        raise ValueError("block statistics must be (int32, fp32, fp32)")
+    _dev(cnt, bsum, bmax, stats)
+    check(_lib.load().bsa_paro_metric(_ptr(cnt), _ptr(bsum), _ptr(bmax), G, N, B, int(sigma[0]),
+                                      int(sigma[1]), float(alpha), int(order), _ptr(stats), _stream()))
+    return stats
+
+
+def paro_select(stats, out=None):
+    """bsa_paro_select: per head, the order with the smallest M.  uint8 [G]."""
+    G = stats.shape[0]
+    if stats.shape != (G, 6, 3) or stats.dtype != torch.float32 or not stats.is_contiguous():
+        raise ValueError("stats must be contiguous fp32 [G][6][3]")
+    if out is None:
+        out = torch.empty(G, dtype=torch.uint8, device=stats.device)
+    _dev(stats, out)
+    check(_lib.load().bsa_paro_select(_ptr(stats), G, _ptr(out), _stream()))
+    return out
+
+
+def paro_calibrate(Q, K, F, H, W, B=64, eps=1e-3, sigma=(9, 10), alpha=0.0, sm_scale=0.0):
+    """Offline order choice for natural Q, K [N][G][d]: for each of the six
+    axis orders, reorder (bsa_permute), take the dense map's block
+    statistics and the order metric; then pick the argmin per head.
+    Returns (axis_order uint8 [G], stats fp32 [G][6][3])."""
+    G = Q.shape[1]
+    stats = torch.full((G, 6, 3), float("nan"), dtype=torch.float32, device=Q.device)
+    for o in range(6):
+        orders = torch.full((G,), o, dtype=torch.uint8, device=Q.device)
+        Qp = permute(Q, orders, F, H, W)
+        Kp = permute(K, orders, F, H, W)
+        cnt, bsum, bmax = attn_block_stats(Qp, Kp, B, eps, sm_scale)
+        paro_metric(cnt, bsum, bmax, F * H * W, B, o, sigma, alpha, stats)
+    return paro_select(stats), stats
+
+
+def mask_from_block_sums(keys, N, Bq, Bk, mass, force_diag=True, workspace=None):
+    """bsa_mask_from_block_sums: static mask keeping, per q-block row, the
+    fewest largest blocks whose fp32 running sum reaches mass * row total
+    (plus the diagonal).  keys fp32 [G][Nq][Nkv].  Returns (row_ptr, col_idx
+    view of length nnz, nnz)."""
+    G, nq, nk = keys.shape
+    if keys.dtype != torch.float32 or not keys.is_contiguous():
+        raise ValueError("keys must be contiguous fp32 [G][Nq][Nkv]")
+    if nq != (N + Bq - 1) // Bq or nk != (N + Bk - 1) // Bk:
+        raise ValueError("keys shape does not match N, Bq, Bk")
+    ws = int(_lib.load().bsa_mask_sums_workspace(G, N, Bq, Bk))
+    if ws < 0:
+        raise ValueError("bsa_mask_sums_workspace: unsupported sizes")
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=keys.device)
+    row_ptr = torch.empty(G * nq + 1, dtype=torch.int32, device=keys.device)
+    col_idx = torch.empty(G * nq * nk, dtype=torch.int32, device=keys.device)
+    nnz = torch.empty(1, dtype=torch.int32, device=keys.device)
+    _dev(keys, workspace)
+    check(_lib.load().bsa_mask_from_block_sums(_ptr(keys), G, N, Bq, Bk, float(mass),
+                                               1 if force_diag else 0, _ptr(row_ptr), _ptr(col_idx),
+                                               col_idx.numel(), _ptr(nnz), _ptr(workspace),
+                                               workspace.numel(), _stream()))
+    n = int(nnz.item())
+    return row_ptr, col_idx[:n], n
+
+
+def mask_from_bits(bits, nk, workspace=None):
+    """bsa_mask_from_bits: CSR of a block bitmask, bits int64/uint64
+    [rows][ceil(nk/64)] (bit j % 64 of word j // 64 keeps kv-block j).
+    Returns (row_ptr, col_idx view of length nnz, nnz)."""
+    rows, words = bits.shape
+    if words != (nk + 63) // 64 or bits.element_size() != 8 or not bits.is_contiguous():
+        raise ValueError("bits must be contiguous 64-bit [rows][ceil(nk/64)]")
+    ws = int(_lib.load().bsa_mask_bits_workspace(rows))
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=bits.device)
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=bits.device)
+    col_idx = torch.empty(rows * nk, dtype=torch.int32, device=bits.device)
+    nnz = torch.empty(1, dtype=torch.int32, device=bits.device)
+    _dev(bits, workspace)
+    check(_lib.load().bsa_mask_from_bits(_ptr(bits), rows, nk, _ptr(row_ptr), _ptr(col_idx),
+                                         col_idx.numel(), _ptr(nnz), _ptr(workspace),
+                                         workspace.numel(), _stream()))
+    n = int(nnz.item())
+    return row_ptr, col_idx[:n], n
+
+
 def quantize_int8(Xp, B, out=None):
     """bsa_quantize_int8: bf16 [G][N][d] -> (int8 [G][N][d], fp32 scales
     [G][ceil(N/B)]); ``out`` = (q, scale) reuses preallocated tensors."""

@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libbsa.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = [
     "capi.hip", "permute.hip", "mask.hip", "fused.hip", "order.hip", "quant.hip", "attn.hip",
-    "attn_bf16.hip",
+    "attn_bf16.hip", "calib.hip",
 ]
 ARCH = "gfx950"
 

@@ -39,6 +39,25 @@ hipError_t launch_build_mask_pooled(const MaskGeom& m, const float* sums_q, cons
                                     const uint8_t* orders, int32_t* row_ptr, int32_t* col_idx,
                                     int64_t col_capacity, int32_t* nnz, char* ws, hipStream_t s);
 
+// bitmask rows [R][ceil(nk/64)] -> counts (scratch, R ints) -> CSR; bits at
+// kv-block >= nk are ignored
+hipError_t launch_bits_to_csr(const unsigned long long* bits, int R, int nk, int32_t* counts,
+                              int32_t* row_ptr, int32_t* col_idx, int64_t cap, int32_t* nnz,
+                              hipStream_t s);
+
+// ---- calib.hip -------------------------------------------------------------
+hipError_t launch_block_stats(const uint16_t* Qp, const uint16_t* Kp, int G, int N, int d, int B,
+                              float sm_scale, float eps, int32_t* cnt, float* bsum, float* bmax,
+                              hipStream_t s);
+hipError_t launch_paro_metric(const int32_t* cnt, const float* bsum, const float* bmax, int G,
+                              int N, int B, int sigma_num, int sigma_den, float alpha, int order,
+                              float* stats, hipStream_t s);
+hipError_t launch_paro_select(const float* stats, int G, uint8_t* orders, hipStream_t s);
+size_t mass_select_workspace_bytes(int G, int nq, int nk);
+hipError_t launch_mass_select(const float* keys, int G, int N, int Bq, int Bk, float mass,
+                              int force_diag, int32_t* row_ptr, int32_t* col_idx, int64_t cap,
+                              int32_t* nnz, void* ws, hipStream_t s);
+
 // ---- fused.hip -------------------------------------------------------------
 hipError_t launch_permute_pool(const void* src, int src_dt, uint16_t* dst, int64_t stride_g,
                                int64_t stride_n, int G, int F, int H, int W, int d,

@@ -1,0 +1,382 @@
+// calib.hip — offline calibration of the static path: statistics of the dense
+// post-softmax map per block, the order metric built from them, the argmin
+// over the six axis orders, and the static mask by block-sum thresholding.
+//
+// PAROAttention machine verdict (pith.science, arXiv 2506.16054), key
+// machinery: each head's axis order is picked offline from its post-softmax
+// attention map by a metric that weighs block sparsifiability (the share of
+// blocks whose entries are mostly below a small threshold) against the
+// blocks' quantisation incoherence (largest over mean |A| inside a block);
+// the static mask keeps blocks chosen by thresholding block sums.  Referee
+// minor comment on Eq. (1): n^{<eps}_{ij} counts block (i, j)'s entries
+// below eps; referee major comment on Sec. 4.1 Eq. (3): the weight alpha is
+// not given.
+//
+// Block statistics kernel (dense, two passes over every key):
+//   S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: A = 32 key rows, B = 32
+//   query rows, both loaded straight from HBM/L2 as the 16-byte k-chunks the
+//   operands want (every lane holds one query column and 16 keys of it).
+//   Pass 1 keeps a per-lane running maximum and sum in log2 units and
+//   merges the two lane halves: lse2 = m + log2(l) per query row.
+//   Pass 2 recomputes S, forms A = exp2(S*c - lse2) and accumulates count
+//   below eps, sum and maximum per (q-block, kv-block), reduced over the
+//   wave (and, for 128-row blocks, over the two waves of the q-block through
+//   LDS).  Each wave owns 64 query rows as two 32-row halves, so each K
+//   operand feeds two MFMAs; a workgroup of four waves covers 256 rows.
+#include <algorithm>
+
+#include "bsa_device.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kStatRows = 256;  // query rows per workgroup (4 waves x 64)
+
+__device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// S^T for 32 keys x (2 x 32) queries: acc[qb] lane L holds query 32qb + L%32,
+// slot e holds key 8(e/4) + 4(L/32) + e%4 of the 32.
+template <int KS>
+__device__ __forceinline__ void s_tile(const bf16x8 (&kop)[KS], const bf16x8 (&qop)[2][KS],
+                                       f32x16 (&acc)[2]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    acc[qb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+      acc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[qb][ks], acc[qb], 0, 0, 0);
+  }
+}
+
+template <int KS>
+__device__ __forceinline__ void load_k(const uint16_t* K, int N, int key0, int lane,
+                                       bf16x8 (&kop)[KS]) {
+  const int row = min(key0 + lane % 32, N - 1);
+  const uint16_t* p = K + static_cast<int64_t>(row) * (KS * 16) + 8 * (lane / 32);
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) kop[ks] = load8(p + 16 * ks);
+}
+
+__device__ __forceinline__ int key_of(int slot, int lane) {
+  return 8 * (slot / 4) + 4 * (lane / 32) + slot % 4;
+}
+
+template <int D, int B>
+__global__ __launch_bounds__(256) void block_stats_kernel(
+    const uint16_t* __restrict__ Qp, const uint16_t* __restrict__ Kp, int N, float c, float eps,
+    int32_t* __restrict__ cnt, float* __restrict__ bsum, float* __restrict__ bmax) {
+  constexpr int KS = D / 16;
+  constexpr int SUBS = B / 32;  // 32-key sub-tiles per kv-block
+  __shared__ float part[2][4][3];
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int r0 = blockIdx.x * kStatRows + 64 * w;  // this wave's first query row
+  const int nb = (N + B - 1) / B;
+  const uint16_t* Q = Qp + static_cast<int64_t>(g) * N * D;
+  const uint16_t* K = Kp + static_cast<int64_t>(g) * N * D;
+
+  bf16x8 qop[2][KS];
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    const int row = min(r0 + 32 * qb + lane % 32, N - 1);
+    const uint16_t* p = Q + static_cast<int64_t>(row) * D + 8 * (lane / 32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) qop[qb][ks] = load8(p + 16 * ks);
+  }
+
+  // ---- pass 1: row log-sum-exp (log2 units), per lane over its keys
+  const int nt = (N + 31) / 32;
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+  bf16x8 kop[KS], knx[KS];
+  load_k<KS>(K, N, 0, lane, kop);
+  for (int t = 0; t < nt; t++) {
+    if (t + 1 < nt) load_k<KS>(K, N, 32 * (t + 1), lane, knx);
+    f32x16 acc[2];
+    s_tile<KS>(kop, qop, acc);
+    const bool tail = 32 * t + 32 > N;
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+      float x[16], tm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        x[e] = acc[qb][e] * c;
+        if (tail && 32 * t + key_of(e, lane) >= N) x[e] = -INFINITY;
+        tm = fmaxf(tm, x[e]);
+      }
+      const float mn = fmaxf(m[qb], tm);
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; e++) s += __builtin_amdgcn_exp2f(x[e] - mn);
+      // mn is finite: every sub-tile holds at least one real key
+      l[qb] = l[qb] * __builtin_amdgcn_exp2f(m[qb] - mn) + s;
+      m[qb] = mn;
+    }
+    if (t + 1 < nt) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) kop[ks] = knx[ks];
+    }
+  }
+  float lse2[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    const float mo = __shfl_xor(m[qb], 32), lo = __shfl_xor(l[qb], 32);
+    const float mm = fmaxf(m[qb], mo);
+    const float lt = l[qb] * __builtin_amdgcn_exp2f(m[qb] - mm) + lo * __builtin_amdgcn_exp2f(mo - mm);
+    lse2[qb] = mm + __log2f(lt);
+  }
+
+  // ---- pass 2: statistics per (q-block, kv-block)
+  const bool rv[2] = {r0 + lane % 32 < N, r0 + 32 + lane % 32 < N};
+  const int qblk = r0 / B;  // the wave's 64 rows lie in one q-block
+  load_k<KS>(K, N, 0, lane, kop);
+  for (int j = 0; j < nb; j++) {
+    int ccount = 0;
+    float csum = 0.0f, cmax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < SUBS; u++) {
+      const int t = j * SUBS + u;
+      if (32 * t >= N) break;
+      const bool more = 32 * (t + 1) < N;
+      if (more) load_k<KS>(K, N, 32 * (t + 1), lane, knx);
+      f32x16 acc[2];
+      s_tile<KS>(kop, qop, acc);
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++) {
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const bool real = rv[qb] && 32 * t + key_of(e, lane) < N;
+          const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[qb][e], c, -lse2[qb]));
+          ccount += (real && a < eps) ? 1 : 0;
+          csum += real ? a : 0.0f;
+          cmax = fmaxf(cmax, real ? a : 0.0f);
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) kop[ks] = knx[ks];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      ccount += __shfl_xor(ccount, o);
+      csum += __shfl_xor(csum, o);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, o));
+    }
+    if constexpr (B == 64) {
+      if (lane == 0 && r0 < N) {
+        const int64_t o = (static_cast<int64_t>(g) * nb + qblk) * nb + j;
+        cnt[o] = ccount;
+        bsum[o] = csum;
+        bmax[o] = cmax;
+      }
+    } else {
+      // the two waves of a 128-row q-block meet in LDS (double-buffered by j)
+      float* slot = part[j & 1][w];
+      if (lane == 0) {
+        slot[0] = __int_as_float(ccount);
+        slot[1] = csum;
+        slot[2] = cmax;
+      }
+      __syncthreads();
+      if ((w & 1) == 0 && lane == 0 && r0 < N) {
+        const float* other = part[j & 1][w + 1];
+        const int64_t o = (static_cast<int64_t>(g) * nb + qblk) * nb + j;
+        cnt[o] = ccount + __float_as_int(other[0]);
+        bsum[o] = csum + other[1];
+        bmax[o] = fmaxf(cmax, other[2]);
+      }
+    }
+  }
+}
+
+// ---- order metric: one workgroup per head
+constexpr int kMetThreads = 256;
+
+__global__ __launch_bounds__(kMetThreads) void paro_metric_kernel(
+    const int32_t* __restrict__ cnt, const float* __restrict__ bsum, const float* __restrict__ bmax,
+    int N, int B, int sigma_num, int sigma_den, float alpha, int order, float* __restrict__ stats) {
+  __shared__ int s_n[kMetThreads / kWave];
+  __shared__ float s_i[kMetThreads / kWave];
+  const int g = blockIdx.x, t = threadIdx.x;
+  const int nb = (N + B - 1) / B;
+  const int64_t nblk = static_cast<int64_t>(nb) * nb;
+  const int64_t base = static_cast<int64_t>(g) * nblk;
+  int nsp = 0;
+  float isum = 0.0f;
+  for (int64_t e = t; e < nblk; e += kMetThreads) {
+    const int i = static_cast<int>(e / nb), j = static_cast<int>(e % nb);
+    const int li = min(B, N - i * B), lj = min(B, N - j * B);
+    const int64_t area = static_cast<int64_t>(li) * lj;
+    nsp += static_cast<int64_t>(cnt[base + e]) * sigma_den >= static_cast<int64_t>(sigma_num) * area;
+    const float s = bsum[base + e];
+    isum += s > 0.0f ? bmax[base + e] * static_cast<float>(area) / s : 1.0f;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    nsp += __shfl_xor(nsp, o);
+    isum += __shfl_xor(isum, o);
+  }
+  if (t % kWave == 0) { s_n[t / kWave] = nsp; s_i[t / kWave] = isum; }
+  __syncthreads();
+  if (t == 0) {
+    int ns = 0;
+    float is = 0.0f;
+    for (int w = 0; w < kMetThreads / kWave; w++) { ns += s_n[w]; is += s_i[w]; }
+    const float nf = static_cast<float>(nblk);
+    const float r = static_cast<float>(ns) / nf, ib = is / nf;
+    float* out = stats + (static_cast<int64_t>(g) * 6 + order) * 3;
+    out[0] = (1.0f - r) + alpha * ib;
+    out[1] = r;
+    out[2] = ib;
+  }
+}
+
+__global__ void paro_select_kernel(const float* __restrict__ stats, int G, uint8_t* __restrict__ orders) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= G) return;
+  int best = 0;
+  float bv = stats[static_cast<int64_t>(g) * 18];
+  for (int o = 1; o < 6; o++) {
+    const float v = stats[(static_cast<int64_t>(g) * 6 + o) * 3];
+    if (v < bv || (bv != bv && v == v)) { bv = v; best = o; }  // a NaN never wins
+  }
+  orders[g] = static_cast<uint8_t>(best);
+}
+
+// ---- static mask by block-sum thresholding: one workgroup per q-block row.
+// Keys (anything not > 0 taken as +0) sorted by (key descending, index
+// ascending) as 64-bit images (~key bits : index) with a bitonic sort in LDS;
+// one lane forms the fp32 running sums in that order; k* is the first
+// position whose running sum reaches total*mass.
+constexpr int kMassThreads = 256;
+
+__global__ __launch_bounds__(kMassThreads) void mass_select_kernel(
+    const float* __restrict__ keys, int N, int Bq, int Bk, int nq, int nk, int p2, int words,
+    float mass, int force_diag, unsigned long long* __restrict__ bits) {
+  extern __shared__ unsigned long long srt[];  // [p2] images, then [nk] fp32 prefix sums
+  float* pre = reinterpret_cast<float*>(srt + p2);
+  __shared__ uint32_t keep[2 * 128];            // bitmask words (nk <= 8192)
+  __shared__ int s_k;
+  const int row = blockIdx.x, t = threadIdx.x;
+  const float* kr = keys + static_cast<int64_t>(row) * nk;
+  for (int e = t; e < p2; e += kMassThreads) {
+    unsigned long long img = ~0ull;
+    if (e < nk) {
+      const float k = kr[e];
+      const uint32_t kb = k > 0.0f ? __float_as_uint(k) : 0u;
+      img = (static_cast<unsigned long long>(~kb) << 32) | static_cast<uint32_t>(e);
+    }
+    srt[e] = img;
+  }
+  for (int e = t; e < 2 * words; e += kMassThreads) keep[e] = 0u;
+  if (t == 0) s_k = nk;
+  __syncthreads();
+  for (int k = 2; k <= p2; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int e = t; e < p2; e += kMassThreads) {
+        const int o = e ^ jj;
+        if (o > e) {
+          const unsigned long long a = srt[e], b = srt[o];
+          const bool up = (e & k) == 0;
+          if ((a > b) == up) { srt[e] = b; srt[o] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  if (t == 0) {
+    float run = 0.0f;
+    for (int p = 0; p < nk; p++) {
+      run += __uint_as_float(~static_cast<uint32_t>(srt[p] >> 32));
+      pre[p] = run;
+    }
+  }
+  __syncthreads();
+  const float thr = pre[nk - 1] * mass;
+  for (int p = t; p < nk; p += kMassThreads)
+    if (pre[p] >= thr && (p == 0 || pre[p - 1] < thr)) s_k = p + 1;
+  __syncthreads();
+  const int kstar = s_k;
+  for (int p = t; p < kstar; p += kMassThreads) {
+    const uint32_t j = static_cast<uint32_t>(srt[p]);
+    atomicOr(&keep[j / 32], 1u << (j % 32));
+  }
+  if (force_diag) {
+    const int i = row % nq;
+    const int q0 = i * Bq, q1 = min(q0 + Bq, N);
+    for (int j = t; j < nk; j += kMassThreads) {
+      const int k0 = j * Bk, k1 = min(k0 + Bk, N);
+      if (k0 < q1 && q0 < k1) atomicOr(&keep[j / 32], 1u << (j % 32));
+    }
+  }
+  __syncthreads();
+  for (int wd = t; wd < words; wd += kMassThreads)
+    bits[static_cast<int64_t>(row) * words + wd] =
+        static_cast<unsigned long long>(keep[2 * wd]) | (static_cast<unsigned long long>(keep[2 * wd + 1]) << 32);
+}
+
+}  // namespace
+
+hipError_t launch_block_stats(const uint16_t* Qp, const uint16_t* Kp, int G, int N, int d, int B,
+                              float sm_scale, float eps, int32_t* cnt, float* bsum, float* bmax,
+                              hipStream_t s) {
+  const dim3 grid((N + kStatRows - 1) / kStatRows, G);
+  const float c = sm_scale * kLog2e;
+  if (d == 128 && B == 64)
+    block_stats_kernel<128, 64><<<grid, 256, 0, s>>>(Qp, Kp, N, c, eps, cnt, bsum, bmax);
+  else if (d == 128)
+    block_stats_kernel<128, 128><<<grid, 256, 0, s>>>(Qp, Kp, N, c, eps, cnt, bsum, bmax);
+  else if (B == 64)
+    block_stats_kernel<64, 64><<<grid, 256, 0, s>>>(Qp, Kp, N, c, eps, cnt, bsum, bmax);
+  else
+    block_stats_kernel<64, 128><<<grid, 256, 0, s>>>(Qp, Kp, N, c, eps, cnt, bsum, bmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_paro_metric(const int32_t* cnt, const float* bsum, const float* bmax, int G,
+                              int N, int B, int sigma_num, int sigma_den, float alpha, int order,
+                              float* stats, hipStream_t s) {
+  paro_metric_kernel<<<G, kMetThreads, 0, s>>>(cnt, bsum, bmax, N, B, sigma_num, sigma_den, alpha,
+                                               order, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_paro_select(const float* stats, int G, uint8_t* orders, hipStream_t s) {
+  paro_select_kernel<<<(G + 63) / 64, 64, 0, s>>>(stats, G, orders);
+  return hipGetLastError();
+}
+
+size_t mass_select_workspace_bytes(int G, int nq, int nk) {
+  const size_t R = static_cast<size_t>(G) * nq;
+  const size_t words = (static_cast<size_t>(nk) + 63) / 64;
+  return R * words * 8 + ((R * 4 + 255) & ~static_cast<size_t>(255));
+}
+
+hipError_t launch_mass_select(const float* keys, int G, int N, int Bq, int Bk, float mass,
+                              int force_diag, int32_t* row_ptr, int32_t* col_idx, int64_t cap,
+                              int32_t* nnz, void* ws, hipStream_t s) {
+  const int nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+  const int words = (nk + 63) / 64;
+  const int R = G * nq;
+  int p2 = 1;
+  while (p2 < nk) p2 <<= 1;
+  auto* bits = static_cast<unsigned long long*>(ws);
+  auto* counts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + static_cast<size_t>(R) * words * 8);
+  const size_t lds = sizeof(unsigned long long) * p2 + sizeof(float) * nk;
+  if (lds > 65536) {
+    const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&mass_select_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(lds));
+    if (a != hipSuccess) return a;
+  }
+  mass_select_kernel<<<R, kMassThreads, lds, s>>>(keys, N, Bq, Bk, nq, nk, p2, words, mass,
+                                                  force_diag, bits);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_bits_to_csr(bits, R, nk, counts, row_ptr, col_idx, cap, nnz, s);
+}
+
+}  // namespace bsa

@@ -361,4 +361,118 @@ int bsa_debug_int8_pv(const int8_t* P8, const int8_t* Vq, int32_t G, int32_t N, 
   });
 }
 
+
+// ---- offline calibration and static masks ---------------------------------
+
+int bsa_attn_block_stats(const void* Qp, const void* Kp, int32_t G, int32_t N, int32_t d, int32_t B,
+                         float sm_scale, float eps, int32_t* cnt, float* bsum, float* bmax,
+                         void* stream) {
+  return guarded([&]() -> int {
+    if (!Qp || !Kp || !cnt || !bsum || !bmax) return fail(BSA_EINVAL, "NULL pointer");
+    if (G <= 0 || N <= 0) return fail(BSA_EINVAL, "G and N must be positive");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    if (!block_ok(B)) return fail(BSA_EUNSUPPORTED, "B must be 64 or 128");
+    if (G > 65535) return fail(BSA_EUNSUPPORTED, "G must be <= 65535");
+    if (static_cast<int64_t>(N) * d >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "N*d must be < 2^31");
+    if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(BSA_EINVAL, "eps must be positive and finite");
+    if (!aligned(Qp, 16) || !aligned(Kp, 16)) return fail(BSA_EINVAL, "Qp and Kp must be 16-byte aligned");
+    if (!aligned(cnt, 4) || !aligned(bsum, 4) || !aligned(bmax, 4))
+      return fail(BSA_EINVAL, "outputs must be 4-byte aligned");
+    const float sc = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(static_cast<float>(d));
+    return hip_status(bsa::launch_block_stats(static_cast<const uint16_t*>(Qp),
+                                              static_cast<const uint16_t*>(Kp), G, N, d, B, sc, eps,
+                                              cnt, bsum, bmax, as_stream(stream)),
+                      "bsa_attn_block_stats");
+  });
+}
+
+int bsa_paro_metric(const int32_t* cnt, const float* bsum, const float* bmax, int32_t G, int32_t N,
+                    int32_t B, int32_t sigma_num, int32_t sigma_den, float alpha, int32_t order,
+                    float* stats, void* stream) {
+  return guarded([&]() -> int {
+    if (!cnt || !bsum || !bmax || !stats) return fail(BSA_EINVAL, "NULL pointer");
+    if (G <= 0 || N <= 0) return fail(BSA_EINVAL, "G and N must be positive");
+    if (!block_ok(B)) return fail(BSA_EUNSUPPORTED, "B must be 64 or 128");
+    if (sigma_den <= 0 || sigma_num < 0 || sigma_num > sigma_den)
+      return fail(BSA_EINVAL, "0 <= sigma_num <= sigma_den, sigma_den > 0 required");
+    if (!(alpha >= 0.0f) || !std::isfinite(alpha)) return fail(BSA_EINVAL, "alpha must be >= 0 and finite");
+    if (order < 0 || order > 5) return fail(BSA_EINVAL, "order must be 0..5");
+    if (G > 65535) return fail(BSA_EUNSUPPORTED, "G must be <= 65535");
+    return hip_status(bsa::launch_paro_metric(cnt, bsum, bmax, G, N, B, sigma_num, sigma_den, alpha,
+                                              order, stats, as_stream(stream)),
+                      "bsa_paro_metric");
+  });
+}
+
+int bsa_paro_select(const float* stats, int32_t G, uint8_t* axis_order, void* stream) {
+  return guarded([&]() -> int {
+    if (!stats || !axis_order) return fail(BSA_EINVAL, "NULL pointer");
+    if (G <= 0) return fail(BSA_EINVAL, "G must be positive");
+    return hip_status(bsa::launch_paro_select(stats, G, axis_order, as_stream(stream)),
+                      "bsa_paro_select");
+  });
+}
+
+int64_t bsa_mask_sums_workspace(int32_t G, int32_t N, int32_t Bq, int32_t Bk) {
+  if (G <= 0 || N <= 0 || !block_ok(Bq) || !block_ok(Bk)) return -1;
+  const int nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+  if (nk > 8192 || static_cast<int64_t>(G) * nq >= (1ll << 31)) return -1;
+  return static_cast<int64_t>(bsa::mass_select_workspace_bytes(G, nq, nk));
+}
+
+int bsa_mask_from_block_sums(const float* keys, int32_t G, int32_t N, int32_t Bq, int32_t Bk,
+                             float mass, int32_t force_diag, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_capacity, int32_t* nnz, void* workspace, int64_t ws_bytes,
+                             void* stream) {
+  return guarded([&]() -> int {
+    if (!keys || !row_ptr || !col_idx || !nnz || !workspace) return fail(BSA_EINVAL, "NULL pointer");
+    if (G <= 0 || N <= 0) return fail(BSA_EINVAL, "G and N must be positive");
+    if (!block_ok(Bq) || !block_ok(Bk)) return fail(BSA_EUNSUPPORTED, "Bq, Bk must be 64 or 128");
+    if (!(mass > 0.0f && mass <= 1.0f)) return fail(BSA_EINVAL, "mass must be in (0, 1]");
+    const int64_t nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+    if (nk > 8192) return fail(BSA_EUNSUPPORTED, "Nkv = %lld exceeds 8192", (long long)nk);
+    if (G * nq >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "too many rows");
+    const int64_t need_cols = G * nq * nk;
+    if (col_capacity < need_cols)
+      return fail(BSA_ECAPACITY, "col_capacity %lld < G*Nq*Nkv = %lld", (long long)col_capacity,
+                  (long long)need_cols);
+    const int64_t need = bsa_mask_sums_workspace(G, N, Bq, Bk);
+    if (!aligned(workspace, 256)) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+      return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
+    return hip_status(bsa::launch_mass_select(keys, G, N, Bq, Bk, mass, force_diag != 0, row_ptr,
+                                              col_idx, col_capacity, nnz, workspace,
+                                              as_stream(stream)),
+                      "bsa_mask_from_block_sums");
+  });
+}
+
+int64_t bsa_mask_bits_workspace(int32_t rows) {
+  if (rows <= 0) return -1;
+  return (static_cast<int64_t>(rows) * 4 + 255) & ~static_cast<int64_t>(255);
+}
+
+int bsa_mask_from_bits(const uint64_t* bits, int32_t rows, int32_t nk, int32_t* row_ptr,
+                       int32_t* col_idx, int64_t col_capacity, int32_t* nnz, void* workspace,
+                       int64_t ws_bytes, void* stream) {
+  return guarded([&]() -> int {
+    if (!bits || !row_ptr || !col_idx || !nnz || !workspace) return fail(BSA_EINVAL, "NULL pointer");
+    if (rows <= 0 || nk <= 0) return fail(BSA_EINVAL, "rows and nk must be positive");
+    if (!aligned(bits, 8) || !aligned(workspace, 4)) return fail(BSA_EINVAL, "bits 8-byte, workspace 4-byte alignment required");
+    const int64_t need_cols = static_cast<int64_t>(rows) * nk;
+    if (need_cols >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "rows*nk must be < 2^31");
+    if (col_capacity < need_cols)
+      return fail(BSA_ECAPACITY, "col_capacity %lld < rows*nk = %lld", (long long)col_capacity,
+                  (long long)need_cols);
+    if (ws_bytes < bsa_mask_bits_workspace(rows))
+      return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes,
+                  (long long)bsa_mask_bits_workspace(rows));
+    return hip_status(bsa::launch_bits_to_csr(reinterpret_cast<const unsigned long long*>(bits), rows,
+                                              nk, static_cast<int32_t*>(workspace), row_ptr, col_idx,
+                                              col_capacity, nnz, as_stream(stream)),
+                      "bsa_mask_from_bits");
+  });
+}
+
 }  // extern "C"

@@ -358,10 +358,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
   }
 }
 
-// one wave per row, 4 rows per workgroup
+// bits of word w that address kv-blocks below nk
+__device__ __forceinline__ unsigned long long live_bits(int w, int nk) {
+  const int rem = nk - 64 * w;
+  return rem >= 64 ? ~0ull : (rem <= 0 ? 0ull : (1ull << rem) - 1ull);
+}
+
+// one wave per row, 4 rows per workgroup; bits at kv-block >= nk are ignored
 __global__ __launch_bounds__(256) void emit_kernel(const unsigned long long* __restrict__ bits,
                                                    const int32_t* __restrict__ row_ptr, int R,
-                                                   int words, int32_t* __restrict__ col_idx,
+                                                   int words, int nk, int32_t* __restrict__ col_idx,
                                                    int64_t cap) {
   const int lane = threadIdx.x % kWave;
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -369,7 +375,8 @@ __global__ __launch_bounds__(256) void emit_kernel(const unsigned long long* __r
   int64_t pos = row_ptr[row];
   for (int w0 = 0; w0 < words; w0 += kWave) {
     const int w = w0 + lane;
-    const unsigned long long b = w < words ? bits[static_cast<int64_t>(row) * words + w] : 0ull;
+    const unsigned long long b =
+        w < words ? bits[static_cast<int64_t>(row) * words + w] & live_bits(w, nk) : 0ull;
     const int c = __popcll(b);
     int x = c;
 #pragma unroll
@@ -387,6 +394,21 @@ __global__ __launch_bounds__(256) void emit_kernel(const unsigned long long* __r
     }
     pos += __shfl(x, kWave - 1);
   }
+}
+
+// kept blocks per row of a bitmask (one wave per row, 4 rows per workgroup)
+__global__ __launch_bounds__(256) void count_kernel(const unsigned long long* __restrict__ bits,
+                                                    int R, int words, int nk,
+                                                    int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (row >= R) return;
+  int c = 0;
+  for (int w = lane; w < words; w += kWave)
+    c += __popcll(bits[static_cast<int64_t>(row) * words + w] & live_bits(w, nk));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 0) counts[row] = c;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -436,11 +458,21 @@ hipError_t select_and_emit(const MaskGeom& m, const uint8_t* orders, int32_t* ro
                                                      m.score, m.k, m.force_diag, m.win_T, m.win_r0,
                                                      rpw, counts, bits);
   scan_kernel<<<1, kScanThreads, 0, s>>>(counts, R, row_ptr, nnz);
-  emit_kernel<<<(R + 3) / 4, 256, 0, s>>>(bits, row_ptr, R, m.words, col_idx, col_capacity);
+  emit_kernel<<<(R + 3) / 4, 256, 0, s>>>(bits, row_ptr, R, m.words, m.nk, col_idx, col_capacity);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_bits_to_csr(const unsigned long long* bits, int R, int nk, int32_t* counts,
+                              int32_t* row_ptr, int32_t* col_idx, int64_t cap, int32_t* nnz,
+                              hipStream_t s) {
+  const int words = (nk + 63) / 64;
+  count_kernel<<<(R + 3) / 4, 256, 0, s>>>(bits, R, words, nk, counts);
+  scan_kernel<<<1, kScanThreads, 0, s>>>(counts, R, row_ptr, nnz);
+  emit_kernel<<<(R + 3) / 4, 256, 0, s>>>(bits, row_ptr, R, words, nk, col_idx, cap);
+  return hipGetLastError();
+}
 
 hipError_t launch_build_mask(const MaskGeom& m, const uint16_t* Qp, const uint16_t* Kp,
                              const uint8_t* orders, int32_t* row_ptr, int32_t* col_idx,

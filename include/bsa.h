@@ -273,6 +273,91 @@ int bsa_debug_int8_pv(const int8_t *P8, const int8_t *Vq, int32_t G, int32_t N, 
                       int32_t Bq, int32_t Bk, const int32_t *gj, int32_t n, int32_t *OV,
                       void *stream);
 
+/* ---- offline calibration of the static path ------------------------------
+ * PAROAttention verdict, key machinery: each head's axis order is chosen
+ * offline from its post-softmax attention map by a metric that weighs block
+ * sparsifiability (the share of blocks whose entries are mostly below a
+ * small threshold) against block quantisation incoherence (largest over
+ * mean |A| inside a block), and the static mask keeps blocks chosen by
+ * thresholding block sums.  Referee minor comment on Eq. (1): n^{<eps}_{ij}
+ * counts the entries of block (i, j) below eps; referee major comment on
+ * Sec. 4.1 Eq. (3): the weight alpha is not given (the example thresholds
+ * are eps = 1e-3 and sigma = 90 %). */
+
+/* bsa_attn_block_stats — statistics of the dense post-softmax map of each
+ * head.  Qp, Kp: reordered bf16 [G][N][d] (16-byte aligned).  With
+ * A[r][c] = exp(s*q_r.k_c) / sum over all N columns c' of exp(s*q_r.k_c')
+ * (s = sm_scale, <= 0 selects 1/sqrt(d); fp32 arithmetic), for every B x B
+ * block (i, j) over its real rows and columns:
+ *   cnt[g][i][j]  int32  number of entries A < eps,
+ *   bsum[g][i][j] fp32   sum of A,
+ *   bmax[g][i][j] fp32   maximum of A,
+ * all [G][nb][nb], nb = ceil(N/B).  Dense work: 4*N^2*d FLOP per head (two
+ * passes of S).  d in {64, 128}, B in {64, 128}, eps > 0.
+ * Errors: EINVAL, EUNSUPPORTED, EHIP. */
+int bsa_attn_block_stats(const void *Qp, const void *Kp, int32_t G, int32_t N, int32_t d,
+                         int32_t B, float sm_scale, float eps, int32_t *cnt, float *bsum,
+                         float *bmax, void *stream);
+
+/* bsa_paro_metric — the order metric of one axis order from its block
+ * statistics (as bsa_attn_block_stats emits them, blocks B x B over N
+ * tokens), per head g, in fp32:
+ *   block (i, j) is sparse iff cnt*sigma_den >= sigma_num*area, with area =
+ *     real rows x real columns (exact integers);
+ *   r    = (sparse blocks) / nb^2;
+ *   inc  = bmax*area/bsum for a block with bsum > 0, else 1;
+ *   Ibar = mean of inc over the nb^2 blocks (summation order unspecified);
+ *   M    = (1 - r) + alpha*Ibar   (lower is better).
+ * Writes stats[g][order][0..2] = (M, r, Ibar) of a caller-owned fp32
+ * [G][6][3] array; the other orders' entries are left alone.
+ * 0 <= sigma_num <= sigma_den, sigma_den > 0; alpha >= 0; order 0..5.
+ * Errors: EINVAL, EUNSUPPORTED, EHIP. */
+int bsa_paro_metric(const int32_t *cnt, const float *bsum, const float *bmax, int32_t G,
+                    int32_t N, int32_t B, int32_t sigma_num, int32_t sigma_den, float alpha,
+                    int32_t order, float *stats, void *stream);
+
+/* bsa_paro_select — axis_order[g] (device uint8) = the order o with the
+ * smallest stats[g][o][0] (M of bsa_paro_metric); ties go to the lowest
+ * code, a NaN never wins.  Errors: EINVAL, EHIP. */
+int bsa_paro_select(const float *stats, int32_t G, uint8_t *axis_order, void *stream);
+
+/* bsa_mask_sums_workspace — device workspace bytes for
+ * bsa_mask_from_block_sums, or -1 for unsupported sizes. */
+int64_t bsa_mask_sums_workspace(int32_t G, int32_t N, int32_t Bq, int32_t Bk);
+
+/* bsa_mask_from_block_sums — the static mask by block-sum thresholding,
+ * the threshold being a share `mass` of each q-block row's total.  keys:
+ * fp32 [G][Nq][Nkv] (e.g. bsum of bsa_attn_block_stats averaged over
+ * calibration inputs); a key that is not > 0 counts as +0.  Per row: the
+ * kv-blocks in (key descending, index ascending) order, P_k = fp32 running
+ * sum of the first k keys (sequential adds from +0), total = P_Nkv,
+ * t = total*mass (one fp32 multiply), k* = the smallest k >= 1 with
+ * P_k >= t; the row keeps those k* blocks and, with force_diag, every
+ * kv-block overlapping the q-block's rows.  Outputs as bsa_build_mask:
+ * row_ptr int32[G*Nq + 1], col_idx int32 (ascending per row), nnz int32[1].
+ * 0 < mass <= 1; Nkv <= 8192; col_capacity >= G*Nq*Nkv (ECAPACITY
+ * otherwise); workspace 256-byte aligned, >= bsa_mask_sums_workspace bytes.
+ * Errors: EINVAL, EUNSUPPORTED, ECAPACITY, EHIP. */
+int bsa_mask_from_block_sums(const float *keys, int32_t G, int32_t N, int32_t Bq, int32_t Bk,
+                             float mass, int32_t force_diag, int32_t *row_ptr, int32_t *col_idx,
+                             int64_t col_capacity, int32_t *nnz, void *workspace, int64_t ws_bytes,
+                             void *stream);
+
+/* bsa_mask_bits_workspace — device workspace bytes for bsa_mask_from_bits
+ * (4 bytes a row, rounded up to 256), or -1. */
+int64_t bsa_mask_bits_workspace(int32_t rows);
+
+/* bsa_mask_from_bits — CSR of a block mask stored as bits (PAROAttention
+ * verdict, key machinery: the static masks are kept as bitmasks).  bits:
+ * uint64 [rows][ceil(nk/64)]; bit j % 64 of word j / 64 of a row keeps
+ * kv-block j; bits at j >= nk are ignored.  Rows are CSR rows (g*Nq + i).
+ * Outputs as bsa_build_mask.  col_capacity >= rows*nk (ECAPACITY
+ * otherwise); bits 8-byte aligned; workspace >= bsa_mask_bits_workspace.
+ * Errors: EINVAL, EUNSUPPORTED, ECAPACITY, EHIP. */
+int bsa_mask_from_bits(const uint64_t *bits, int32_t rows, int32_t nk, int32_t *row_ptr,
+                       int32_t *col_idx, int64_t col_capacity, int32_t *nnz, void *workspace,
+                       int64_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

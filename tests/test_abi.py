@@ -36,7 +36,9 @@ def test_header_lists_the_entry_points():
               "bsa_quantize_int8", "bsa_mask_capacity", "bsa_mask_workspace",
               "bsa_debug_int8_qk", "bsa_debug_int8_pv", "bsa_abi_version", "bsa_last_error",
               "bsa_permute_pool", "bsa_build_mask_pooled", "bsa_order_workspace",
-              "bsa_order_scores", "bsa_select_orders"):
+              "bsa_order_scores", "bsa_select_orders", "bsa_attn_block_stats",
+              "bsa_paro_metric", "bsa_paro_select", "bsa_mask_sums_workspace",
+              "bsa_mask_from_block_sums", "bsa_mask_bits_workspace", "bsa_mask_from_bits"):
         assert n in names
 
 
@@ -139,3 +141,47 @@ def test_fused_and_order_argument_errors(lib):
     assert b"workspace" in lib.bsa_last_error()
     assert lib.bsa_order_scores(fake, 2, 8, 64, 1, 2, 4, 8, 64, 64, fake, fake, 1 << 20, None) == -2
     assert lib.bsa_select_orders(None, None, 4, fake, None) == -1
+
+
+def test_calibration_and_static_mask_argument_errors(lib):
+    """Host checks of the offline calibration and static-mask calls; none of
+    these reaches HIP."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    F = ctypes.c_float
+    # block stats: bad d, bad B, non-positive eps, misaligned Q
+    assert lib.bsa_attn_block_stats(fake, fake, 1, 256, 96, 64, F(0), F(1e-3), fake, fake, fake,
+                                    None) == -2
+    assert lib.bsa_attn_block_stats(fake, fake, 1, 256, 128, 32, F(0), F(1e-3), fake, fake, fake,
+                                    None) == -2
+    assert lib.bsa_attn_block_stats(fake, fake, 1, 256, 128, 64, F(0), F(0), fake, fake, fake,
+                                    None) == -1
+    assert b"eps" in lib.bsa_last_error()
+    assert lib.bsa_attn_block_stats(P(0x1008), fake, 1, 256, 128, 64, F(0), F(1e-3), fake, fake,
+                                    fake, None) == -1
+    # metric: sigma out of range, order out of range, negative alpha
+    assert lib.bsa_paro_metric(fake, fake, fake, 1, 256, 64, 11, 10, F(0), 0, fake, None) == -1
+    assert lib.bsa_paro_metric(fake, fake, fake, 1, 256, 64, 9, 10, F(0), 6, fake, None) == -1
+    assert lib.bsa_paro_metric(fake, fake, fake, 1, 256, 64, 9, 10, F(-1), 0, fake, None) == -1
+    assert lib.bsa_paro_select(None, 4, fake, None) == -1
+    # static mask from block sums: workspace size, mass range, capacity, workspace short
+    ws = lib.bsa_mask_sums_workspace(2, 1000, 64, 64)
+    R, nk = 2 * 16, 16
+    assert ws == R * 1 * 8 + ((R * 4 + 255) // 256) * 256
+    assert lib.bsa_mask_sums_workspace(2, 1000, 64, 96) == -1
+    args = (fake, 2, 1000, 64, 64)
+    assert lib.bsa_mask_from_block_sums(*args, F(0.0), 1, fake, fake, R * nk, fake, P(0x1000), ws,
+                                        None) == -1
+    assert lib.bsa_mask_from_block_sums(*args, F(1.5), 1, fake, fake, R * nk, fake, P(0x1000), ws,
+                                        None) == -1
+    assert lib.bsa_mask_from_block_sums(*args, F(0.9), 1, fake, fake, R * nk - 1, fake,
+                                        P(0x1000), ws, None) == -3
+    assert b"col_capacity" in lib.bsa_last_error()
+    assert lib.bsa_mask_from_block_sums(*args, F(0.9), 1, fake, fake, R * nk, fake, P(0x1000),
+                                        ws - 1, None) == -3
+    # bitmask -> CSR: workspace size, capacity, alignment
+    assert lib.bsa_mask_bits_workspace(10) == 256
+    assert lib.bsa_mask_bits_workspace(0) == -1
+    assert lib.bsa_mask_from_bits(fake, 10, 100, fake, fake, 999, fake, fake, 256, None) == -3
+    assert lib.bsa_mask_from_bits(P(0x1004), 10, 100, fake, fake, 1000, fake, fake, 256,
+                                  None) == -1

@@ -1,0 +1,250 @@
+"""GPU parity of the offline calibration (block statistics of the dense
+post-softmax map, the order metric, the argmin over orders) and of the
+static masks (block-sum thresholding, bitmask input), through the C ABI
+against the CPU oracle on the same seeded inputs.
+
+Bars: the mask CSRs are integer outputs of a fixed fp32 sequence and must
+match bit for bit.  The block statistics come from fp32 exponentials of
+fp32 MFMA scores against the oracle's fp64, so each count must lie between
+the oracle's counts at eps*(1 -/+ 1e-3) and sums / maxima within 2e-4
+relative.  The metric, fed the same statistics on both sides, must give
+the sparse share exactly and the mean incoherence within 1e-5 relative
+(fp32 summation order).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_inverse_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _qk(seed, G, N, d, scale):
+    """Reordered bf16 Q, K [G][N][d] on the GPU and their bit patterns."""
+    gen = torch.Generator().manual_seed(seed)
+    q = (scale * torch.randn((G, N, d), generator=gen)).to(torch.bfloat16)
+    k = (scale * torch.randn((G, N, d), generator=gen)).to(torch.bfloat16)
+    return q.cuda(), k.cuda(), synth.bf16_bits(q), synth.bf16_bits(k)
+
+
+STAT_CASES = [
+    # (N, d, B, scale): ragged tails, both head dims, both block sizes
+    (200, 64, 64, 1.0),
+    (1000, 128, 64, 1.0),
+    (1000, 128, 128, 1.5),
+    (777, 64, 128, 2.0),
+    (31, 128, 64, 1.0),
+    (4096, 128, 64, 1.2),
+]
+
+
+@pytest.mark.parametrize("N,d,B,scale", STAT_CASES)
+def test_block_stats_parity(bsa_gpu, orc, N, d, B, scale):
+    G, eps = 2, 1e-3
+    _say(f"[block_stats N={N} d={d} B={B} scale={scale}]")
+    q, k, qb, kb = _qk(40 + N + d + B, G, N, d, scale)
+    cnt, bsum, bmax = bsa_gpu.attn_block_stats(q, k, B, eps)
+    torch.cuda.synchronize()
+    want = orc.block_stats(qb, kb, B, eps, delta=1e-3)
+    c = cnt.cpu().numpy()
+    assert np.all(want["cnt_lo"] <= c) and np.all(c <= want["cnt_hi"])
+    # exact wherever no entry lies within the bracket
+    sure = want["cnt_lo"] == want["cnt_hi"]
+    assert np.array_equal(c[sure], want["cnt"][sure])
+    s = bsum.cpu().numpy().astype(np.float64)
+    m = bmax.cpu().numpy().astype(np.float64)
+    assert np.allclose(s, want["sum"], rtol=2e-4, atol=1e-9)
+    assert np.allclose(m, want["max"], rtol=2e-4, atol=1e-12)
+    # and the counts do vary between blocks in these cases (the test bites)
+    if N >= 1000:
+        assert c.min() < c.max()
+
+
+def test_block_stats_custom_scale(bsa_gpu, orc):
+    G, N, d, B = 1, 512, 64, 64
+    q, k, qb, kb = _qk(47, G, N, d, 1.0)
+    cnt, bsum, bmax = bsa_gpu.attn_block_stats(q, k, B, 5e-3, sm_scale=0.3)
+    torch.cuda.synchronize()
+    want = orc.block_stats(qb, kb, B, 5e-3, sm_scale=0.3)
+    c = cnt.cpu().numpy()
+    assert np.all(want["cnt_lo"] <= c) and np.all(c <= want["cnt_hi"])
+    assert np.allclose(bsum.cpu().numpy(), want["sum"], rtol=2e-4, atol=1e-9)
+
+
+def _stats_inputs(orc, seed, G, N, d, B, scale):
+    """Block statistics from the oracle (fp64 rounded to the kernel's output
+    types): the common input of both metric implementations."""
+    _, _, qb, kb = _qk(seed, G, N, d, scale)
+    st = orc.block_stats(qb, kb, B, 1e-3)
+    return st["cnt"], st["sum"].astype(np.float32), st["max"].astype(np.float32)
+
+
+@pytest.mark.parametrize("N,B", [(1000, 64), (700, 128)])
+def test_paro_metric_parity(bsa_gpu, orc, N, B):
+    G, d = 3, 64
+    _say(f"[paro_metric N={N} B={B}]")
+    cnt, bs, bm = _stats_inputs(orc, 50 + N, G, N, d, B, 1.3)
+    tc, ts, tm = (torch.from_numpy(a).cuda() for a in (cnt, bs, bm))
+    stats = None
+    for order, sigma, alpha in ((2, (9, 10), 0.0), (5, (1, 2), 0.01), (0, (3, 4), 1.0)):
+        stats = bsa_gpu.paro_metric(tc, ts, tm, N, B, order, sigma, alpha, stats)
+        torch.cuda.synchronize()
+        got = stats.cpu().numpy()[:, order, :].astype(np.float64)
+        want = orc.paro_metric(cnt, bs, bm, N, B, sigma[0], sigma[1], alpha)
+        assert np.allclose(got[:, 1], want[:, 1], rtol=0, atol=1e-7)  # r: exact ratio in fp32
+        assert np.allclose(got[:, 2], want[:, 2], rtol=1e-5)
+        assert np.allclose(got[:, 0], want[:, 0], rtol=1e-5, atol=1e-7)
+    untouched = stats.cpu().numpy()[:, [1, 3, 4], :]
+    assert np.all(np.isnan(untouched))
+
+
+def test_paro_select_parity(bsa_gpu):
+    r = rng(60)
+    G = 130
+    M = r.integers(0, 5, size=(G, 6)).astype(np.float32) / 4  # many exact ties
+    M[7, :] = np.nan
+    M[8, 0] = np.nan
+    stats = np.zeros((G, 6, 3), np.float32)
+    stats[:, :, 0] = M
+    got = bsa_gpu.paro_select(torch.from_numpy(stats).cuda()).cpu().numpy()
+    want = np.argmin(np.where(np.isnan(M), np.inf, M), axis=1)
+    want[7] = 0
+    assert np.array_equal(got, want.astype(np.uint8))
+
+
+def test_paro_calibrate_end_to_end(bsa_gpu, orc):
+    """Natural Q, K with a planted local axis per head: the chosen order is
+    (within the fp32 metric's resolution) the argmin of the oracle's metric
+    over all six orders."""
+    cfg = synth.config(2, G=2)
+    F, H, W, G, d = cfg["F"], cfg["H"], cfg["W"], cfg["G"], cfg["d"]
+    N = F * H * W
+    B, alpha = 64, 0.02
+    planted = np.array([3, 4], np.uint8)
+    Qn, Kn, _ = synth.make_qkv(cfg, planted, synth.seed_of(2))
+    Qb, Kb = Qn.to(torch.bfloat16), Kn.to(torch.bfloat16)
+    _say("[paro_calibrate cfg 2, 2 heads]")
+    orders, stats = bsa_gpu.paro_calibrate(Qb.cuda(), Kb.cuda(), F, H, W, B, 1e-3, (9, 10), alpha)
+    torch.cuda.synchronize()
+    got = orders.cpu().numpy()
+    Mo = np.zeros((G, 6))
+    qn, kn = synth.bf16_bits(Qb), synth.bf16_bits(Kb)
+    for o in range(6):
+        qp = orc.permute(0, qn, np.uint16, G, F, H, W, d, np.full(G, o, np.uint8))
+        kp = orc.permute(0, kn, np.uint16, G, F, H, W, d, np.full(G, o, np.uint8))
+        st = orc.block_stats(qp, kp, B, 1e-3)
+        Mo[:, o] = orc.paro_metric(st["cnt"], st["sum"].astype(np.float32),
+                                   st["max"].astype(np.float32), N, B, 9, 10, alpha)[:, 0]
+    for g in range(G):
+        assert Mo[g, got[g]] <= Mo[g].min() + 1e-4 * abs(Mo[g].min()) + 1e-6
+    s = stats.cpu().numpy()
+    assert np.allclose(s[:, :, 0], Mo, rtol=1e-3, atol=1e-3)
+
+
+MASS_CASES = [
+    # (G, N, Bq, Bk, mass, force_diag, kind)
+    (2, 1000, 64, 64, 0.9, 1, "stats"),
+    (1, 2048, 128, 64, 0.5, 0, "ties"),
+    (3, 4000, 64, 128, 1.0, 1, "ties"),
+    (1, 300, 64, 64, 0.75, 0, "zeros"),
+    (2, 64 * 75, 64, 64, 0.95, 1, "special"),
+    (1, 128 * 40, 128, 64, 0.3, 1, "ties"),
+]
+
+
+def _mass_keys(orc, kind, G, N, Bq, Bk, seed):
+    nq, nk = -(-N // Bq), -(-N // Bk)
+    r = rng(seed)
+    if kind == "stats":
+        _, _, qb, kb = _qk(seed, G, N, 64, 1.5)
+        return orc.block_stats(qb, kb, Bq, 1e-3)["sum"].astype(np.float32)
+    if kind == "ties":
+        return (r.integers(0, 8, size=(G, nq, nk)) / 8).astype(np.float32)
+    if kind == "zeros":
+        k = r.random((G, nq, nk), dtype=np.float32)
+        k[:, ::2, :] = 0.0
+        return k
+    k = r.random((G, nq, nk), dtype=np.float32)
+    k[:, :, ::7] = -1.0
+    k[:, :, 3::11] = np.nan
+    k[:, :, 5::13] = -0.0
+    return k
+
+
+@pytest.mark.parametrize("G,N,Bq,Bk,mass,fd,kind", MASS_CASES)
+def test_mask_from_block_sums_parity(bsa_gpu, orc, G, N, Bq, Bk, mass, fd, kind):
+    _say(f"[mass_select G={G} N={N} Bq={Bq} Bk={Bk} mass={mass} diag={fd} {kind}]")
+    keys = _mass_keys(orc, kind, G, N, Bq, Bk, 70 + N)
+    rp, ci, n = bsa_gpu.mask_from_block_sums(torch.from_numpy(keys).cuda(), N, Bq, Bk, mass, fd)
+    torch.cuda.synchronize()
+    wrp, wci = orc.mass_select(keys, N, Bq, Bk, mass, fd)
+    assert np.array_equal(rp.cpu().numpy(), wrp)
+    assert n == len(wci) and np.array_equal(ci.cpu().numpy(), wci)
+
+
+def test_mask_from_block_sums_widest_row(bsa_gpu, orc):
+    """Nkv = 8192 (the limit): the 96 KB sort buffer; a few hundred rows."""
+    G, Bq, Bk = 1, 128, 64
+    N = 8192 * Bk
+    nq = N // Bq
+    r = rng(80)
+    keys = (r.integers(0, 64, size=(G, nq, 8192)) / 64).astype(np.float32)
+    keys = keys[:, :256, :]  # rows are independent: N sets nk, the first 256 rows are checked
+    _say("[mass_select widest row nk=8192]")
+    # the call needs all nq rows; pad the rest with zeros (each keeps 1 block + diagonal)
+    full = np.zeros((G, nq, 8192), np.float32)
+    full[:, :256, :] = keys
+    rp, ci, n = bsa_gpu.mask_from_block_sums(torch.from_numpy(full).cuda(), N, Bq, Bk, 0.6, 1)
+    torch.cuda.synchronize()
+    wrp, wci = orc.mass_select(full, N, Bq, Bk, 0.6, 1)
+    assert np.array_equal(rp.cpu().numpy(), wrp)
+    assert np.array_equal(ci.cpu().numpy(), wci)
+
+
+@pytest.mark.parametrize("rows,nk", [(300, 150), (40, 64), (17, 1), (5, 8192)])
+def test_mask_from_bits_parity(bsa_gpu, orc, rows, nk):
+    _say(f"[mask_from_bits rows={rows} nk={nk}]")
+    r = rng(90 + nk)
+    words = -(-nk // 64)
+    dens = r.random((rows, 1))
+    keep = r.random((rows, words * 64)) < dens  # includes bits past nk
+    bits = np.zeros((rows, words), np.uint64)
+    for b in range(64):
+        bits |= keep[:, b::64].astype(np.uint64) << np.uint64(b)
+    rp, ci, n = bsa_gpu.mask_from_bits(torch.from_numpy(bits.view(np.int64)).cuda(), nk)
+    torch.cuda.synchronize()
+    wrp, wci = orc.bits_to_csr(bits, nk)
+    assert np.array_equal(rp.cpu().numpy(), wrp)
+    assert n == len(wci) and np.array_equal(ci.cpu().numpy(), wci)
+
+
+def test_bitmask_mask_drives_forward(bsa_gpu, orc):
+    """A static mask given as bits runs the bf16 forward exactly as the same
+    mask given as CSR (same kernel inputs, same outputs bit for bit)."""
+    G, N, d, B = 2, 1000, 128, 64
+    nq = -(-N // B)
+    r = rng(95)
+    sets = [sorted(set(r.choice(nq, size=5, replace=False).tolist()) | {i % nq})
+            for i in range(G * nq)]
+    bits = np.zeros((G * nq, 1), np.uint64)
+    for row, s in enumerate(sets):
+        for j in s:
+            bits[row, 0] |= np.uint64(1) << np.uint64(j)
+    rp, ci, _ = bsa_gpu.mask_from_bits(torch.from_numpy(bits.view(np.int64)).cuda(), nq)
+    rp2 = torch.tensor(np.cumsum([0] + [len(s) for s in sets]), dtype=torch.int32).cuda()
+    ci2 = torch.tensor([j for s in sets for j in s], dtype=torch.int32).cuda()
+    q, k, _, _ = _qk(96, G, N, d, 1.0)
+    v = torch.randn((G, N, d), generator=torch.Generator().manual_seed(97)).to(torch.bfloat16).cuda()
+    o1, l1 = bsa_gpu.forward(q, k, v, rp, ci, B, B)
+    o2, l2 = bsa_gpu.forward(q, k, v, rp2, ci2, B, B)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
