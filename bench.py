@@ -7,7 +7,8 @@ The INT8 chain (reorder with quantisation -> mask -> INT8 attention ->
 inverse reorder) is timed in the same run, over the same number of steps,
 and reported under "int8"; the long-clip layer (118,800 tokens, mask rebuilt
 every step from COSINE block scores with a temporal window) under
-"long_clip".
+"long_clip"; the offline order calibration (dense-map block statistics for
+all six axis orders, metric, argmin, static mask) under "calibration".
 
 Workload: the 720p-shaped DiT layer, F=21, H=45, W=80 (75,600 tokens),
 40 heads, d=128, 128x64 blocks, 30% density; inputs resident in HBM.
@@ -199,6 +200,88 @@ def long_clip(args, timed_steps):
     }
 
 
+def calibration(args):
+    """Offline order calibration on the 480p-shaped layer (F=21, H=30, W=52,
+    32,760 tokens, 12 heads, d=128, 64x64 blocks): for each of the six axis
+    orders reorder Q and K, take the dense post-softmax map's block
+    statistics (two MFMA passes over every score) and the order metric, then
+    pick the argmin; then the static mask from the chosen order's block sums
+    (90 % of each row's mass plus the diagonal)."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_inverse_amd as bsa
+    from block_sparse_attention_inverse_amd import synth
+
+    cfg = synth.config(3)
+    F, H, W, G, d, N = cfg["F"], cfg["H"], cfg["W"], cfg["G"], cfg["d"], cfg["N"]
+    B = 64
+    seed = synth.seed_of(3)
+    orders = synth.make_orders(cfg, seed)
+    log(f"[bench] calibration: generating N={N} G={G} d={d}")
+    Q, K, _ = synth.cast_inputs(cfg, *synth.make_qkv(cfg, orders, seed, device="cuda"))
+    nb = (N + B - 1) // B
+    stats = torch.empty((G, 6, 3), dtype=torch.float32, device="cuda")
+    cnt = torch.empty((G, nb, nb), dtype=torch.int32, device="cuda")
+    bsum = torch.empty((G, nb, nb), dtype=torch.float32, device="cuda")
+    bmax = torch.empty((G, nb, nb), dtype=torch.float32, device="cuda")
+    Qp = torch.empty((G, N, d), dtype=torch.bfloat16, device="cuda")
+    Kp = torch.empty_like(Qp)
+    ods = [torch.full((G,), o, dtype=torch.uint8, device="cuda") for o in range(6)]
+
+    def step(ev=None):
+        for o in range(6):
+            bsa.permute(Q, ods[o], F, H, W, out=Qp)
+            bsa.permute(K, ods[o], F, H, W, out=Kp)
+            if ev:
+                ev[2 * o].record()
+            bsa.attn_block_stats(Qp, Kp, B, 1e-3, out=(cnt, bsum, bmax))
+            if ev:
+                ev[2 * o + 1].record()
+            bsa.paro_metric(cnt, bsum, bmax, N, B, o, (9, 10), 0.02, stats)
+        return bsa.paro_select(stats)
+
+    for _ in range(max(1, args.warmup)):
+        chosen = step()
+    torch.cuda.synchronize()
+    steps = max(2, args.steps // 10)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        chosen = step(evs[k])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    t_stats = np.mean([[evs[k][2 * o].elapsed_time(evs[k][2 * o + 1]) for o in range(6)]
+                       for k in range(steps)]) / 1e3
+    # the static mask from the chosen orders' block sums
+    Qp2 = bsa.permute(Q, chosen, F, H, W)
+    Kp2 = bsa.permute(K, chosen, F, H, W)
+    _, keys, _ = bsa.attn_block_stats(Qp2, Kp2, B, 1e-3)
+    bsa.mask_from_block_sums(keys, N, B, B, 0.9)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        rp, ci, nnz = bsa.mask_from_block_sums(keys, N, B, B, 0.9)
+    e1.record()
+    torch.cuda.synchronize()
+    t_mask = e0.elapsed_time(e1) / steps
+    fl = 4.0 * N * N * d * G  # two passes of S = Q.K^T over every (query, key)
+    log(f"[bench] calibration: {wall * 1e3:.2f} ms for six orders; block stats {t_stats * 1e3:.3f} ms "
+        f"({fl / t_stats / 1e12:.1f} TFLOP/s); static mask {t_mask:.3f} ms")
+    return {
+        "workload": "480p layer: F=21,H=30,W=52 (32760 tokens), 12 heads, d=128, 64x64 blocks; "
+                    "six axis orders, eps=1e-3, sigma=90%, alpha=0.02; static mask at 90% row mass",
+        "ms_six_orders": wall * 1e3,
+        "block_stats_ms": t_stats * 1e3,
+        "block_stats_tflops": fl / t_stats / 1e12,
+        "block_stats_frac_bf16_peak": fl / t_stats / 1e12 / PEAK_BF16_TFLOPS,
+        "static_mask_ms": t_mask,
+        "static_mask_density": nnz / (G * nb * nb),
+        "chosen_orders": chosen.cpu().tolist(),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +289,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip the offline order calibration timing")
     ap.add_argument("--no-long-clip", action="store_true",
                     help="skip the long-clip layer (dynamic COSINE mask rebuilt every step)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -387,6 +472,8 @@ def main():
         }
     if not args.no_long_clip:
         result["long_clip"] = long_clip(args, timed_steps=args.steps)
+    if not args.no_calib:
+        result["calibration"] = calibration(args)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(cfg, Q, K, V, orders, p)

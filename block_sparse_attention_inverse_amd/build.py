@@ -39,6 +39,8 @@ EXTRA_FLAGS = {
     "attn_bf16.hip": ["-fno-honor-nans"],
     # the INT8 kernel reads its MFMA results with VALU ops: keep them in VGPRs
     "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the dense block-statistics kernel reads every score with VALU ops too
+    "calib.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

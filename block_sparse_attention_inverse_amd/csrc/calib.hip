@@ -13,9 +13,10 @@
 // not given.
 //
 // Block statistics kernel (dense, two passes over every key):
-//   S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: A = 32 key rows, B = 32
-//   query rows, both loaded straight from HBM/L2 as the 16-byte k-chunks the
-//   operands want (every lane holds one query column and 16 keys of it).
+//   S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: A = 32 key rows read from
+//   LDS (64-key tiles staged once per workgroup, double-buffered), B = 32
+//   query rows held in registers (every lane holds one query column and 16
+//   keys of it).
 //   Pass 1 keeps a per-lane running maximum and sum in log2 units and
 //   merges the two lane halves: lse2 = m + log2(l) per query row.
 //   Pass 2 recomputes S, forms A = exp2(S*c - lse2) and accumulates count
@@ -38,35 +39,64 @@ __device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-// S^T for 32 keys x (2 x 32) queries: acc[qb] lane L holds query 32qb + L%32,
-// slot e holds key 8(e/4) + 4(L/32) + e%4 of the 32.
-template <int KS>
-__device__ __forceinline__ void s_tile(const bf16x8 (&kop)[KS], const bf16x8 (&qop)[2][KS],
-                                       f32x16 (&acc)[2]) {
+// K staging: 64-key tiles pass HBM/L2 -> registers -> LDS once per
+// workgroup (four waves share them).  16-byte chunk c of tile row r sits at
+// chunk position c ^ (r mod CH), so that the operand reads (32 rows, one
+// chunk each per half-wave) hit distinct banks.
+template <int D>
+struct KStage {
+  static constexpr int CH = D / 8;                 // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;               // bytes per row
+  static constexpr int TILEB = 64 * ROWB;          // bytes per 64-key tile
+  static constexpr int PER = TILEB / 16 / 256;     // chunks per thread per tile
+  uint4 r[PER];
+  __device__ __forceinline__ void load(const uint16_t* K, int N, int key0, int t) {
 #pragma unroll
-  for (int qb = 0; qb < 2; qb++) {
-    acc[qb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++)
-      acc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[qb][ks], acc[qb], 0, 0, 0);
+    for (int q = 0; q < PER; q++) {
+      const int e = q * 256 + t, row = e / CH, ch = e % CH;
+      const int kr = min(key0 + row, N - 1);
+      r[q] = *reinterpret_cast<const uint4*>(K + static_cast<int64_t>(kr) * D + ch * 8);
+    }
   }
-}
-
-template <int KS>
-__device__ __forceinline__ void load_k(const uint16_t* K, int N, int key0, int lane,
-                                       bf16x8 (&kop)[KS]) {
-  const int row = min(key0 + lane % 32, N - 1);
-  const uint16_t* p = K + static_cast<int64_t>(row) * (KS * 16) + 8 * (lane / 32);
+  __device__ __forceinline__ void store(uint8_t* lds, int t) const {
 #pragma unroll
-  for (int ks = 0; ks < KS; ks++) kop[ks] = load8(p + 16 * ks);
+    for (int q = 0; q < PER; q++) {
+      const int e = q * 256 + t, row = e / CH, ch = e % CH;
+      *reinterpret_cast<uint4*>(lds + row * ROWB + ((ch ^ (row % CH)) * 16)) = r[q];
+    }
+  }
+};
+
+// S^T of sub-tile u (keys 32u .. 32u+31 of the LDS tile) against the
+// wave's 2 x 32 queries.  A operand of k-step ks: lane L takes tile row
+// 32u + L%32, channels 16ks + 8(L/32) .. +7; each operand is read right
+// before the two MFMAs that use it, which keeps few K registers live.
+template <int D>
+__device__ __forceinline__ void s_tile_lds(const uint8_t* lds, int u, int lane,
+                                           const bf16x8 (&qop)[2][D / 16], f32x16 (&acc)[2]) {
+  constexpr int CH = D / 8, ROWB = D * 2;
+  const int row = 32 * u + lane % 32;
+  const uint8_t* base = lds + row * ROWB;
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ks++) {
+    const int ch = 2 * ks + lane / 32;
+    const bf16x8 kop =
+        __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(base + ((ch ^ (row % CH)) * 16)));
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[0][ks], acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[1][ks], acc[1], 0, 0, 0);
+  }
 }
 
 __device__ __forceinline__ int key_of(int slot, int lane) {
   return 8 * (slot / 4) + 4 * (lane / 32) + slot % 4;
 }
 
+// three waves per SIMD (168 VGPRs): the kernel is latency-bound, and more
+// resident waves hide the MFMA-to-VALU and LDS latencies
 template <int D, int B>
-__global__ __launch_bounds__(256) void block_stats_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void block_stats_kernel(
     const uint16_t* __restrict__ Qp, const uint16_t* __restrict__ Kp, int N, float c, float eps,
     int32_t* __restrict__ cnt, float* __restrict__ bsum, float* __restrict__ bmax) {
   constexpr int KS = D / 16;
@@ -89,36 +119,50 @@ __global__ __launch_bounds__(256) void block_stats_kernel(
   }
 
   // ---- pass 1: row log-sum-exp (log2 units), per lane over its keys
-  const int nt = (N + 31) / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][KStage<D>::TILEB];
+  const int tid = threadIdx.x;
+  const int nt = (N + 31) / 32;       // 32-key sub-tiles
+  const int ntile = (N + 63) / 64;    // 64-key LDS tiles
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
-  bf16x8 kop[KS], knx[KS];
-  load_k<KS>(K, N, 0, lane, kop);
-  for (int t = 0; t < nt; t++) {
-    if (t + 1 < nt) load_k<KS>(K, N, 32 * (t + 1), lane, knx);
+  KStage<D> st;
+  auto lse_sub = [&](int t, const uint8_t* lds, int u) {
     f32x16 acc[2];
-    s_tile<KS>(kop, qop, acc);
-    const bool tail = 32 * t + 32 > N;
+    s_tile_lds<D>(lds, u, lane, qop, acc);
+    if (32 * t + 32 > N) {
+      // keys past N take no weight
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+        for (int e = 0; e < 16; e++)
+          if (32 * t + key_of(e, lane) >= N) acc[qb][e] = -INFINITY;
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
-      float x[16], tm = -INFINITY;
+      float tm = acc[qb][0];
 #pragma unroll
-      for (int e = 0; e < 16; e++) {
-        x[e] = acc[qb][e] * c;
-        if (tail && 32 * t + key_of(e, lane) >= N) x[e] = -INFINITY;
-        tm = fmaxf(tm, x[e]);
-      }
-      const float mn = fmaxf(m[qb], tm);
+      for (int e = 1; e < 16; e++) tm = fmaxf(tm, acc[qb][e]);
+      // c > 0, so the scaled maximum is the maximum of the scaled scores;
+      // mn is finite: every sub-tile holds at least one real key
+      const float mn = fmaxf(m[qb], tm * c);
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; e++) s += __builtin_amdgcn_exp2f(x[e] - mn);
-      // mn is finite: every sub-tile holds at least one real key
+      for (int e = 0; e < 16; e++) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[qb][e], c, -mn));
       l[qb] = l[qb] * __builtin_amdgcn_exp2f(m[qb] - mn) + s;
       m[qb] = mn;
     }
-    if (t + 1 < nt) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ks++) kop[ks] = knx[ks];
-    }
+  };
+  // one barrier per tile: in step T the waves read buffer T&1, then write
+  // tile T+1 into the other buffer, which every wave finished reading in
+  // step T-1 (before the barrier that ended it)
+  st.load(K, N, 0, tid);
+  st.store(kt[0], tid);
+  __syncthreads();
+  for (int T = 0; T < ntile; T++) {
+    if (T + 1 < ntile) st.load(K, N, 64 * (T + 1), tid);
+    lse_sub(2 * T, kt[T & 1], 0);
+    if (2 * T + 1 < nt) lse_sub(2 * T + 1, kt[T & 1], 1);
+    if (T + 1 < ntile) st.store(kt[(T + 1) & 1], tid);
+    __syncthreads();
   }
   float lse2[2];
 #pragma unroll
@@ -129,46 +173,54 @@ __global__ __launch_bounds__(256) void block_stats_kernel(
     lse2[qb] = mm + __log2f(lt);
   }
 
-  // ---- pass 2: statistics per (q-block, kv-block)
+  // ---- pass 2: statistics per (q-block, kv-block); a 64-key tile never
+  // straddles two kv-blocks
   const bool rv[2] = {r0 + lane % 32 < N, r0 + 32 + lane % 32 < N};
+  const bool rows_full = r0 + 64 <= N;
   const int qblk = r0 / B;  // the wave's 64 rows lie in one q-block
-  load_k<KS>(K, N, 0, lane, kop);
-  for (int j = 0; j < nb; j++) {
-    int ccount = 0;
-    float csum = 0.0f, cmax = 0.0f;
+  int ccount = 0;
+  float csum = 0.0f, xmax = -INFINITY;  // maximum exponent; the block maximum is exp2(xmax)
+  auto stat_sub = [&](int t, const uint8_t* lds, int u) {
+    f32x16 acc[2];
+    s_tile_lds<D>(lds, u, lane, qop, acc);
+    if (rows_full && 32 * t + 32 <= N) {
 #pragma unroll
-    for (int u = 0; u < SUBS; u++) {
-      const int t = j * SUBS + u;
-      if (32 * t >= N) break;
-      const bool more = 32 * (t + 1) < N;
-      if (more) load_k<KS>(K, N, 32 * (t + 1), lane, knx);
-      f32x16 acc[2];
-      s_tile<KS>(kop, qop, acc);
+      for (int qb = 0; qb < 2; qb++) {
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const float x = __builtin_fmaf(acc[qb][e], c, -lse2[qb]);
+          const float a = __builtin_amdgcn_exp2f(x);
+          ccount += a < eps ? 1 : 0;
+          csum += a;
+          xmax = fmaxf(xmax, x);
+        }
+      }
+    } else {
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) {
 #pragma unroll
         for (int e = 0; e < 16; e++) {
           const bool real = rv[qb] && 32 * t + key_of(e, lane) < N;
-          const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[qb][e], c, -lse2[qb]));
+          const float x = real ? __builtin_fmaf(acc[qb][e], c, -lse2[qb]) : -INFINITY;
+          const float a = __builtin_amdgcn_exp2f(x);
           ccount += (real && a < eps) ? 1 : 0;
-          csum += real ? a : 0.0f;
-          cmax = fmaxf(cmax, real ? a : 0.0f);
+          csum += a;
+          xmax = fmaxf(xmax, x);
         }
       }
-      if (more) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++) kop[ks] = knx[ks];
-      }
     }
+  };
+  auto flush = [&](int j) {
+    float cmax = __builtin_amdgcn_exp2f(xmax);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       ccount += __shfl_xor(ccount, o);
       csum += __shfl_xor(csum, o);
       cmax = fmaxf(cmax, __shfl_xor(cmax, o));
     }
+    const int64_t o = (static_cast<int64_t>(g) * nb + qblk) * nb + j;
     if constexpr (B == 64) {
       if (lane == 0 && r0 < N) {
-        const int64_t o = (static_cast<int64_t>(g) * nb + qblk) * nb + j;
         cnt[o] = ccount;
         bsum[o] = csum;
         bmax[o] = cmax;
@@ -184,12 +236,27 @@ __global__ __launch_bounds__(256) void block_stats_kernel(
       __syncthreads();
       if ((w & 1) == 0 && lane == 0 && r0 < N) {
         const float* other = part[j & 1][w + 1];
-        const int64_t o = (static_cast<int64_t>(g) * nb + qblk) * nb + j;
         cnt[o] = ccount + __float_as_int(other[0]);
         bsum[o] = csum + other[1];
         bmax[o] = fmaxf(cmax, other[2]);
       }
     }
+    ccount = 0;
+    csum = 0.0f;
+    xmax = -INFINITY;
+  };
+  st.load(K, N, 0, tid);
+  st.store(kt[0], tid);
+  __syncthreads();
+  for (int T = 0; T < ntile; T++) {
+    if (T + 1 < ntile) st.load(K, N, 64 * (T + 1), tid);
+    stat_sub(2 * T, kt[T & 1], 0);
+    if (2 * T + 1 < nt) stat_sub(2 * T + 1, kt[T & 1], 1);
+    // the tile ends kv-block T*64/B when it is the block's last tile or the
+    // last tile of all
+    if ((64 * (T + 1)) % B == 0 || T + 1 == ntile) flush((64 * T) / B);
+    if (T + 1 < ntile) st.store(kt[(T + 1) & 1], tid);
+    __syncthreads();
   }
 }
 
