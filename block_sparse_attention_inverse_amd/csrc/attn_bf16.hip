@@ -149,8 +149,11 @@ struct Stage {
   static constexpr int NVK = L::RW >= L::CH ? 1 : L::CH / L::RW;
   static constexpr int NVV = 2 * L::RW >= L::CH ? 1 : L::CH / (2 * L::RW);
   uint32_t k[NVK], v[NVV];
+  uint32_t wb;  // this wave's byte offset inside a staged tile (wave-uniform, kept in an SGPR)
   __device__ __forceinline__ void init() {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    wb = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(w) * 1024u);
+    asm volatile("" : "+s"(wb));  // computed once, not re-derived from the thread id per load
     const int rw = w * L::RPI + lane / L::CH, p = lane % L::CH;
 #pragma unroll
     for (int a = 0; a < NVK; a++) {
@@ -175,17 +178,19 @@ struct Stage {
 
 template <int D, int NW>
 __device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int win, int q,
-                                         uint8_t* tile) {
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+                                         uint8_t* tile, uint32_t wb) {
   const uint32_t soff = static_cast<uint32_t>(win * Ly<D, NW>::ROWB + q * NW * 1024);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(tile + (q * NW + w) * 1024), 16, voff,
+  // opaque per load, so the LDS address is one add here instead of a
+  // register per (buffer, q) held across the loop
+  asm volatile("" : "+s"(wb));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(tile + q * NW * 1024 + wb), 16, voff,
                                            soff, 0, 0);
 }
 // load q of the staging of a K (ISV false) or V sub-tile whose window starts at row win
 template <int D, int NW, bool ISV, bool SMALLN>
 __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, const Stage<D, NW>& sg, int N,
                                          int win, int q, uint8_t* tile) {
-  load_raw<D, NW>(rsrc, sg.template lane_off<ISV, SMALLN>(q, N), win, q, tile);
+  load_raw<D, NW>(rsrc, sg.template lane_off<ISV, SMALLN>(q, N), win, q, tile, sg.wb);
 }
 
 template <int D, int NW, bool SMALLN>
