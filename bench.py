@@ -279,6 +279,10 @@ def calibration(args):
         "static_mask_ms": t_mask,
         "static_mask_density": nnz / (G * nb * nb),
         "chosen_orders": chosen.cpu().tolist(),
+        # the synthetic inputs carry a local component along each head's
+        # planted axis order: how often the calibration finds it
+        "planted_orders": [int(o) for o in orders],
+        "heads_matching_planted": int(sum(int(a) == int(b) for a, b in zip(chosen.cpu().tolist(), orders))),
     }
 
 
