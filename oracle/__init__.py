@@ -54,6 +54,8 @@ def _load():
         "oracle_int8_pv_tile": (_I, [_P, _P, _I, _L, _I, _I, _I, _L, _P]),
         "oracle_sics_scores": (_I, [_P, _I, _L, _L, _I, _I, _I, _I, _I, _I, _P]),
         "oracle_block_stats": (_I, [_P, _P, _I, _L, _I, _I, _D, _D, _D, _P, _P, _P, _P, _P]),
+        "oracle_block_stats_rows": (_I, [_P, _P, _I, _L, _I, _I, _D, _D, _D, _P, _L, _P, _P, _P,
+                                         _P, _P]),
         "oracle_paro_metric": (_I, [_P, _P, _P, _I, _L, _I, _I, _I, _D, _P]),
         "oracle_mass_select": (_I, [_P, _I, _L, _I, _I, ctypes.c_float, _I, _P, _P, _L, _P]),
         "oracle_num_threads": (_I, []),
@@ -329,6 +331,28 @@ def block_stats(Qp, Kp, B, eps, sm_scale=None, delta=1e-3):
                                       float(delta), _ptr(out["cnt"]), _ptr(out["cnt_lo"]),
                                       _ptr(out["cnt_hi"]), _ptr(out["sum"]), _ptr(out["max"])),
            "block_stats")
+    return out
+
+
+def block_stats_rows(Qp, Kp, B, eps, blocks, sm_scale=None, delta=1e-3):
+    """block_stats for chosen (head, q-block) rows only: blocks int [n][2]
+    of (g, i); returns the same dict with arrays [n][nb]."""
+    Qp = np.ascontiguousarray(Qp, dtype=np.uint16)
+    Kp = np.ascontiguousarray(Kp, dtype=np.uint16)
+    G, N, d = Qp.shape
+    nb = (N + B - 1) // B
+    blocks = np.ascontiguousarray(blocks, dtype=np.int64)
+    n = blocks.shape[0]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = {k: np.empty((n, nb), dtype=np.int32) for k in ("cnt", "cnt_lo", "cnt_hi")}
+    out["sum"] = np.empty((n, nb), dtype=np.float64)
+    out["max"] = np.empty((n, nb), dtype=np.float64)
+    _check(_load().oracle_block_stats_rows(_ptr(Qp), _ptr(Kp), G, N, d, B, float(sm_scale),
+                                           float(eps), float(delta), _ptr(blocks), n,
+                                           _ptr(out["cnt"]), _ptr(out["cnt_lo"]),
+                                           _ptr(out["cnt_hi"]), _ptr(out["sum"]),
+                                           _ptr(out["max"])), "block_stats_rows")
     return out
 
 

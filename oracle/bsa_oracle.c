@@ -728,6 +728,44 @@ int oracle_int8_pv_tile(const int8_t *P8, const int8_t *Vq, int g, int64_t N, in
  * A < eps*(1+delta): a count taken in lower precision lies between them.
  * Outputs [G][nb][nb], nb = ceil(N/B).
  * ---------------------------------------------------------------------- */
+/* One q-block row (head g, q-block i) of the statistics above: outputs
+ * [nb] at cnt etc. (cnt_lo / cnt_hi may be NULL). */
+static void block_stats_row(const uint16_t *Q, const uint16_t *K, int64_t N, int d, int B,
+                            int64_t i, double sm_scale, double eps, double lo, double hi,
+                            int32_t *cnt, int32_t *cnt_lo, int32_t *cnt_hi, double *bsum,
+                            double *bmax, double *srow, double *qv) {
+  const int64_t nb = (N + B - 1) / B;
+  for (int64_t j = 0; j < nb; j++) {
+    cnt[j] = 0;
+    if (cnt_lo) cnt_lo[j] = 0;
+    if (cnt_hi) cnt_hi[j] = 0;
+    bsum[j] = 0.0;
+    bmax[j] = 0.0;
+  }
+  const int64_t r1 = (i + 1) * B < N ? (i + 1) * B : N;
+  for (int64_t r = i * B; r < r1; r++) {
+    for (int c = 0; c < d; c++) qv[c] = bf16_to_f32(Q[r * d + c]);
+    double mx = -INFINITY;
+    for (int64_t m = 0; m < N; m++) {
+      double acc = 0.0;
+      for (int c = 0; c < d; c++) acc += qv[c] * (double)bf16_to_f32(K[m * d + c]);
+      srow[m] = sm_scale * acc;
+      if (srow[m] > mx) mx = srow[m];
+    }
+    double l = 0.0;
+    for (int64_t m = 0; m < N; m++) l += exp(srow[m] - mx);
+    for (int64_t m = 0; m < N; m++) {
+      const double a = exp(srow[m] - mx) / l;
+      const int64_t t = m / B;
+      cnt[t] += a < eps;
+      if (cnt_lo) cnt_lo[t] += a < lo;
+      if (cnt_hi) cnt_hi[t] += a < hi;
+      bsum[t] += a;
+      if (a > bmax[t]) bmax[t] = a;
+    }
+  }
+}
+
 int oracle_block_stats(const uint16_t *Qp, const uint16_t *Kp, int G, int64_t N, int d, int B,
                        double sm_scale, double eps, double delta, int32_t *cnt, int32_t *cnt_lo,
                        int32_t *cnt_hi, double *bsum, double *bmax) {
@@ -741,37 +779,38 @@ int oracle_block_stats(const uint16_t *Qp, const uint16_t *Kp, int G, int64_t N,
       double *srow = (double *)malloc(sizeof(double) * (size_t)N);
       double *qv = (double *)malloc(sizeof(double) * (size_t)d);
       const int64_t base = ((int64_t)g * nb + i) * nb;
-      for (int64_t j = 0; j < nb; j++) {
-        cnt[base + j] = 0;
-        if (cnt_lo) cnt_lo[base + j] = 0;
-        if (cnt_hi) cnt_hi[base + j] = 0;
-        bsum[base + j] = 0.0;
-        bmax[base + j] = 0.0;
-      }
-      const int64_t r1 = (i + 1) * B < N ? (i + 1) * B : N;
-      for (int64_t r = i * B; r < r1; r++) {
-        for (int c = 0; c < d; c++) qv[c] = bf16_to_f32(Q[r * d + c]);
-        double mx = -INFINITY;
-        for (int64_t m = 0; m < N; m++) {
-          double acc = 0.0;
-          for (int c = 0; c < d; c++) acc += qv[c] * (double)bf16_to_f32(K[m * d + c]);
-          srow[m] = sm_scale * acc;
-          if (srow[m] > mx) mx = srow[m];
-        }
-        double l = 0.0;
-        for (int64_t m = 0; m < N; m++) l += exp(srow[m] - mx);
-        for (int64_t m = 0; m < N; m++) {
-          const double a = exp(srow[m] - mx) / l;
-          const int64_t t = base + m / B;
-          cnt[t] += a < eps;
-          if (cnt_lo) cnt_lo[t] += a < lo;
-          if (cnt_hi) cnt_hi[t] += a < hi;
-          bsum[t] += a;
-          if (a > bmax[t]) bmax[t] = a;
-        }
-      }
+      block_stats_row(Q, K, N, d, B, i, sm_scale, eps, lo, hi, cnt + base,
+                      cnt_lo ? cnt_lo + base : NULL, cnt_hi ? cnt_hi + base : NULL, bsum + base,
+                      bmax + base, srow, qv);
       free(srow); free(qv);
     }
+  }
+  return 0;
+}
+
+/* The same statistics for chosen (head, q-block) rows only: blocks holds
+ * nblk pairs (g, i); outputs [nblk][nb].  For full-size inputs, where the
+ * whole map is out of reach on the CPU. */
+int oracle_block_stats_rows(const uint16_t *Qp, const uint16_t *Kp, int G, int64_t N, int d, int B,
+                            double sm_scale, double eps, double delta, const int64_t *blocks,
+                            int64_t nblk, int32_t *cnt, int32_t *cnt_lo, int32_t *cnt_hi,
+                            double *bsum, double *bmax) {
+  if (!Qp || !Kp || !blocks || !cnt || !bsum || !bmax || G <= 0 || N <= 0 || d <= 0 || B <= 0)
+    return -1;
+  const int64_t nb = (N + B - 1) / B;
+  for (int64_t t = 0; t < nblk; t++)
+    if (blocks[2 * t] < 0 || blocks[2 * t] >= G || blocks[2 * t + 1] < 0 || blocks[2 * t + 1] >= nb)
+      return -1;
+  const double lo = eps * (1.0 - delta), hi = eps * (1.0 + delta);
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t t = 0; t < nblk; t++) {
+    double *srow = (double *)malloc(sizeof(double) * (size_t)N);
+    double *qv = (double *)malloc(sizeof(double) * (size_t)d);
+    const int64_t g = blocks[2 * t], i = blocks[2 * t + 1];
+    block_stats_row(Qp + g * N * d, Kp + g * N * d, N, d, B, i, sm_scale, eps, lo, hi,
+                    cnt + t * nb, cnt_lo ? cnt_lo + t * nb : NULL, cnt_hi ? cnt_hi + t * nb : NULL,
+                    bsum + t * nb, bmax + t * nb, srow, qv);
+    free(srow); free(qv);
   }
   return 0;
 }

@@ -248,3 +248,37 @@ def test_bitmask_mask_drives_forward(bsa_gpu, orc):
     o2, l2 = bsa_gpu.forward(q, k, v, rp2, ci2, B, B)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.slow
+def test_block_stats_full_size_sampled(bsa_gpu, orc):
+    """The timed calibration shape: the 480p layer (32,760 tokens, 12 heads,
+    d = 128, 64 x 64 blocks), reordered by one axis order, in the same
+    launch the benchmark times; sampled (head, q-block) rows, including the
+    ragged last one, against the oracle."""
+    cfg = synth.config(3)
+    F, H, W, G, d, N = cfg["F"], cfg["H"], cfg["W"], cfg["G"], cfg["d"], cfg["N"]
+    B = 64
+    orders = synth.make_orders(cfg, synth.seed_of(3))
+    Qn, Kn, _ = synth.cast_inputs(cfg, *synth.make_qkv(cfg, orders, synth.seed_of(3)))
+    od = torch.full((G,), 1, dtype=torch.uint8).cuda()
+    Qp = bsa_gpu.permute(Qn.cuda(), od, F, H, W)
+    Kp = bsa_gpu.permute(Kn.cuda(), od, F, H, W)
+    _say("[block_stats full size 480p]")
+    cnt, bsum, bmax = bsa_gpu.attn_block_stats(Qp, Kp, B, 1e-3)
+    torch.cuda.synchronize()
+    nb = -(-N // B)
+    r = rng(98)
+    blocks = np.array([[0, 0], [G - 1, nb - 1], [5, nb // 2]] +
+                      [[int(r.integers(G)), int(r.integers(nb))] for _ in range(5)], np.int64)
+    qb, kb = synth.bf16_bits(Qp.cpu()), synth.bf16_bits(Kp.cpu())
+    want = orc.block_stats_rows(qb, kb, B, 1e-3, blocks)
+    c, s, m = (t.cpu().numpy() for t in (cnt, bsum, bmax))
+    for t, (g, i) in enumerate(blocks):
+        assert np.all(want["cnt_lo"][t] <= c[g, i]) and np.all(c[g, i] <= want["cnt_hi"][t])
+        assert np.allclose(s[g, i], want["sum"][t], rtol=2e-4, atol=1e-9)
+        assert np.allclose(m[g, i], want["max"][t], rtol=2e-4, atol=1e-12)
+    # every row of the map sums to one: the block sums of a q-block row add
+    # up to its rows, on every row of every head
+    lens = np.minimum(B, N - B * np.arange(nb))
+    assert np.allclose(s.astype(np.float64).sum(axis=2), lens[None, :], rtol=1e-4)

@@ -870,3 +870,15 @@ def test_bits_to_csr_round_trip(orc):
     rp, ci = orc.bits_to_csr(bits, nk)
     for row, s_ in enumerate(sets):
         assert ci[rp[row]:rp[row + 1]].tolist() == s_
+
+
+def test_block_stats_rows_match_whole_map(orc):
+    """The sampled-row entry computes exactly the rows of the whole map."""
+    G, N, d, B = 2, 300, 64, 64
+    q, k = _bf16_pair(37, G, N, d, 1.3)
+    full = orc.block_stats(q, k, B, 1e-3)
+    blocks = np.array([[0, 4], [1, 0], [1, 3], [0, 0]], np.int64)
+    part = orc.block_stats_rows(q, k, B, 1e-3, blocks)
+    for t, (g, i) in enumerate(blocks):
+        for key in ("cnt", "cnt_lo", "cnt_hi", "sum", "max"):
+            assert np.array_equal(part[key][t], full[key][g, i]), key
