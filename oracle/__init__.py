@@ -58,6 +58,9 @@ def _load():
                                          _P, _P]),
         "oracle_paro_metric": (_I, [_P, _P, _P, _I, _L, _I, _I, _I, _D, _P]),
         "oracle_mass_select": (_I, [_P, _I, _L, _I, _I, ctypes.c_float, _I, _P, _P, _L, _P]),
+        "oracle_perturb_keys": (None, [_P, _P, ctypes.c_float, _L, _P]),
+        "oracle_select_topp": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_float, ctypes.c_float,
+                                    _I, _I, _I, _P, _P, _L, _P, _P, _P]),
         "oracle_num_threads": (_I, []),
     }
     for name, (res, args) in sig.items():
@@ -332,6 +335,35 @@ def block_stats(Qp, Kp, B, eps, sm_scale=None, delta=1e-3):
                                       _ptr(out["cnt_hi"]), _ptr(out["sum"]), _ptr(out["max"])),
            "block_stats")
     return out
+
+
+def perturb_keys(keys, noise, scale):
+    """Seeded stochastic scoring: key' = fmaf(noise, scale, key) in fp32
+    (noise None: key unchanged); the random draws come in as ``noise``."""
+    keys = np.ascontiguousarray(keys, dtype=np.float32)
+    out = np.empty_like(keys)
+    nz = None if noise is None else np.ascontiguousarray(noise, dtype=np.float32)
+    _load().oracle_perturb_keys(_ptr(keys), _ptr(nz), ctypes.c_float(scale), keys.size, _ptr(out))
+    return out
+
+
+def select_topp(keys, G, F, H, W, Bq, Bk, orders, top_p, temp, force_diag=1, win_T=-1, win_r0=0):
+    """Top-P selection on fp32 keys [G][nq][nk]: returns (row_ptr, col_idx,
+    kstar [G*nq], cum [G*nq][nk] fp64 running weights in sorted order)."""
+    keys = np.ascontiguousarray(keys, dtype=np.float32)
+    orders = np.ascontiguousarray(orders, dtype=np.uint8)
+    nq, nk = keys.shape[1], keys.shape[2]
+    row_ptr = np.empty(G * nq + 1, dtype=np.int32)
+    cap = G * nq * nk
+    col_idx = np.empty(cap, dtype=np.int32)
+    kstar = np.empty(G * nq, dtype=np.int32)
+    cum = np.empty((G * nq, nk), dtype=np.float64)
+    nnz = ctypes.c_int64(0)
+    _check(_load().oracle_select_topp(_ptr(keys), G, F, H, W, Bq, Bk, _ptr(orders),
+                                      ctypes.c_float(top_p), ctypes.c_float(temp), force_diag, win_T,
+                                      win_r0, _ptr(row_ptr), _ptr(col_idx), cap, ctypes.byref(nnz),
+                                      _ptr(kstar), _ptr(cum)), "select_topp")
+    return row_ptr, col_idx[: nnz.value].copy(), kstar, cum
 
 
 def block_stats_rows(Qp, Kp, B, eps, blocks, sm_scale=None, delta=1e-3):

@@ -236,6 +236,31 @@ static int cmp_key_desc_idx_asc(const void *pa, const void *pb) {
   return (ia > ib) - (ia < ib);
 }
 
+/* The forced part of a row (q-block i): with force_diag every kv-block
+ * overlapping the q-block's rows; with win_T >= 0 the temporal window on
+ * block centres (perm: the head's reordered -> natural map). */
+static void mark_forced(uint8_t *keep, int64_t i, int64_t N, int Bq, int Bk, int64_t nk,
+                        int force_diag, int win_T, int win_r0, const int32_t *perm, int W,
+                        int64_t HW) {
+  const int64_t q0 = i * Bq, q1 = (q0 + Bq < N ? q0 + Bq : N); /* [q0, q1) */
+  if (force_diag)
+    for (int64_t j = 0; j < nk; j++) {
+      const int64_t k0 = j * Bk, k1 = (k0 + Bk < N ? k0 + Bk : N);
+      if (k0 < q1 && q0 < k1) keep[j] = 1;
+    }
+  if (win_T >= 0) {
+    const int64_t ci = q0 + (block_len(i, Bq, N) - 1) / 2;
+    const int64_t ni = perm[ci], fi = ni / HW, oi = ni % HW;
+    for (int64_t j = 0; j < nk; j++) {
+      const int64_t cj = j * Bk + (block_len(j, Bk, N) - 1) / 2;
+      const int64_t nj = perm[cj], fj = nj / HW, oj = nj % HW;
+      const int64_t df = fi > fj ? fi - fj : fj - fi;
+      const int64_t dox = oi > oj ? oi - oj : oj - oi;
+      if (df <= win_T && dox <= (((int64_t)win_r0 * W) >> df)) keep[j] = 1;
+    }
+  }
+}
+
 int64_t oracle_select_k(int64_t nk, int rho_num, int rho_den) {
   if (rho_den <= 0 || rho_num < 0) return -1;
   int64_t k = (2 * (int64_t)rho_num * nk + rho_den) / (2 * (int64_t)rho_den);
@@ -273,24 +298,92 @@ int oracle_select(const float *keys, int G, int F, int H, int W, int Bq, int Bk,
       g_sort_keys = krow;
       qsort(idx, (size_t)nk, sizeof(int32_t), cmp_key_desc_idx_asc);
       for (int64_t t = 0; t < k; t++) keep[idx[t]] = 1;
-      const int64_t q0 = i * Bq, q1 = (q0 + Bq < N ? q0 + Bq : N); /* [q0, q1) */
-      if (force_diag)
-        for (int64_t j = 0; j < nk; j++) {
-          const int64_t k0 = j * Bk, k1 = (k0 + Bk < N ? k0 + Bk : N);
-          if (k0 < q1 && q0 < k1) keep[j] = 1;
-        }
-      if (win_T >= 0) {
-        const int64_t ci = q0 + (block_len(i, Bq, N) - 1) / 2;
-        const int64_t ni = perm[ci], fi = ni / HW, oi = ni % HW;
-        for (int64_t j = 0; j < nk; j++) {
-          const int64_t cj = j * Bk + (block_len(j, Bk, N) - 1) / 2;
-          const int64_t nj = perm[cj], fj = nj / HW, oj = nj % HW;
-          const int64_t df = fi > fj ? fi - fj : fj - fi;
-          const int64_t dox = oi > oj ? oi - oj : oj - oi;
-          if (df <= win_T && dox <= (((int64_t)win_r0 * W) >> df)) keep[j] = 1;
-        }
-      }
+      mark_forced(keep, i, N, Bq, Bk, nk, force_diag, win_T, win_r0, perm, W, HW);
       row_ptr[(int64_t)g * nq + i] = (int32_t)pos;
+      for (int64_t j = 0; j < nk; j++)
+        if (keep[j]) {
+          if (col_idx && pos < cap) col_idx[pos] = (int32_t)j;
+          else rc = -3;
+          pos++;
+        }
+    }
+    if (rc == -1) break;
+  }
+  row_ptr[(int64_t)G * nq] = (int32_t)pos;
+  if (nnz_out) *nnz_out = pos;
+  free(idx); free(keep); free(perm);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Seeded stochastic scoring.  [PASA] (review of arXiv 2604.12219): a
+ * stochastic bias in the block routing softens the selection boundary
+ * (temperature-scaled Gumbel perturbation of the block scores).  The random
+ * draws are an input here: key' = fmaf(noise, scale, key), one fp32 fma per
+ * score (noise NULL: key' = key).
+ * ---------------------------------------------------------------------- */
+void oracle_perturb_keys(const float *keys, const float *noise, float scale, int64_t n,
+                         float *out) {
+  for (int64_t t = 0; t < n; t++) out[t] = noise ? fmaf(noise[t], scale, keys[t]) : keys[t];
+}
+
+/* ------------------------------------------------------------------------
+ * Top-P selection.  [SPADE] key machinery: the kept blocks pass a
+ * head-wise Top-K / Top-P filter.  Reading taken here: per q-block row, the
+ * kv-blocks in (key descending, index ascending) order carry the weights
+ * w_p = exp2((key_p - key_0) * temp) (fp32: one subtract, one multiply,
+ * exp2f), i.e. the softmax of the block scores at inverse temperature
+ * temp (log2 units); P_k = fp32 running sum of the first k weights;
+ * t = P_nk * top_p; k* = the smallest k >= 1 with P_k >= t.  The row keeps
+ * those k* blocks plus the forced set (diagonal, window) of oracle_select.
+ * Also writes kstar[row] (may be NULL) and, for a tolerance check of a
+ * lower-precision exponential, cum[row][p] (may be NULL) = the fp64
+ * running sum of exp2((double)(key_p - key_0) * temp) over sorted
+ * positions 0..p.
+ * ---------------------------------------------------------------------- */
+int oracle_select_topp(const float *keys, int G, int F, int H, int W, int Bq, int Bk,
+                       const uint8_t *orders, float top_p, float temp, int force_diag, int win_T,
+                       int win_r0, int32_t *row_ptr, int32_t *col_idx, int64_t cap,
+                       int64_t *nnz_out, int32_t *kstar, double *cum) {
+  const int64_t N = (int64_t)F * H * W;
+  if (!keys || !orders || !row_ptr || G <= 0 || Bq <= 0 || Bk <= 0) return -1;
+  const int64_t nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+  int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)nk);
+  uint8_t *keep = (uint8_t *)malloc((size_t)nk);
+  int32_t *perm = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+  if (!idx || !keep || !perm) { free(idx); free(keep); free(perm); return -2; }
+  int64_t pos = 0;
+  int rc = 0;
+  const int64_t HW = (int64_t)H * W;
+  for (int g = 0; g < G; g++) {
+    if (oracle_perm(orders[g], F, H, W, perm)) { rc = -1; break; }
+    for (int64_t i = 0; i < nq; i++) {
+      const int64_t row = (int64_t)g * nq + i;
+      const float *krow = keys + row * nk;
+      for (int64_t j = 0; j < nk; j++) idx[j] = (int32_t)j;
+      g_sort_keys = krow;
+      qsort(idx, (size_t)nk, sizeof(int32_t), cmp_key_desc_idx_asc);
+      const float top = krow[idx[0]];
+      float total = 0.0f;
+      double c64 = 0.0;
+      for (int64_t t = 0; t < nk; t++) {
+        const float dlt = krow[idx[t]] - top;
+        total += exp2f(dlt * temp);
+        c64 += exp2((double)dlt * (double)temp);
+        if (cum) cum[row * nk + t] = c64;
+      }
+      const float thr = total * top_p;
+      int64_t ks = nk;
+      float run = 0.0f;
+      for (int64_t t = 0; t < nk; t++) {
+        run += exp2f((krow[idx[t]] - top) * temp);
+        if (run >= thr) { ks = t + 1; break; }
+      }
+      if (kstar) kstar[row] = (int32_t)ks;
+      memset(keep, 0, (size_t)nk);
+      for (int64_t t = 0; t < ks; t++) keep[idx[t]] = 1;
+      mark_forced(keep, i, N, Bq, Bk, nk, force_diag, win_T, win_r0, perm, W, HW);
+      row_ptr[row] = (int32_t)pos;
       for (int64_t j = 0; j < nk; j++)
         if (keep[j]) {
           if (col_idx && pos < cap) col_idx[pos] = (int32_t)j;

@@ -882,3 +882,79 @@ def test_block_stats_rows_match_whole_map(orc):
     for t, (g, i) in enumerate(blocks):
         for key in ("cnt", "cnt_lo", "cnt_hi", "sum", "max"):
             assert np.array_equal(part[key][t], full[key][g, i]), key
+
+
+# ------------------------------------------- Top-P and stochastic scoring
+def test_select_topp_worked_examples(orc):
+    """Hand-derived rows in golden/topp_examples.txt (one q-block covering
+    the whole sequence, 64-token kv-blocks, no forced blocks)."""
+    with open(os.path.join(GOLDEN, "topp_examples.txt")) as f:
+        cases = [l for l in f if l.strip() and not l.startswith("#")]
+    assert len(cases) == 8
+    for line in cases:
+        head, keys, kept = (p.strip() for p in line.split("|"))
+        top_p, temp = (float(x) for x in head.split())
+        keys = np.array([float(x) for x in keys.split()], np.float32)
+        nk = len(keys)
+        N = 64 * nk
+        rp, ci, ks, _ = orc.select_topp(keys[None, None, :], 1, 1, 1, N, N, 64, np.zeros(1, np.uint8),
+                                        top_p, temp, force_diag=0)
+        assert ci.tolist() == [int(x) for x in kept.split()], line
+        assert ks[0] == len(ci)
+
+
+def test_select_topp_is_minimal_softmax_cover(orc):
+    """On random keys: the kept (unforced) set is the top-k* by key, its fp64
+    softmax mass reaches top_p (to rounding) and one block fewer does not."""
+    r = rng(38)
+    G, F, H, W, B = 2, 1, 8, 80, 64
+    N = F * H * W
+    nb = N // B
+    keys = (3 * r.standard_normal((G, nb, nb))).astype(np.float32)
+    for top_p, temp in ((0.5, 1.0), (0.9, 0.7), (0.99, 2.0)):
+        rp, ci, ks, cum = orc.select_topp(keys, G, F, H, W, B, B, np.zeros(G, np.uint8), top_p, temp,
+                                          force_diag=0)
+        for row in range(G * nb):
+            kk = keys.reshape(G * nb, nb)[row]
+            order = sorted(range(nb), key=lambda j: (-kk[j], j))
+            kept = ci[rp[row]:rp[row + 1]].tolist()
+            assert kept == sorted(order[:ks[row]])
+            w = np.exp2((kk.astype(np.float64) - kk.max()) * temp)
+            w = w[order]
+            c = np.cumsum(w) / w.sum()
+            assert c[ks[row] - 1] >= top_p - 1e-5
+            assert ks[row] == 1 or c[ks[row] - 2] < top_p + 1e-5
+            assert np.allclose(cum[row], np.cumsum(w), rtol=1e-6)  # cum uses the fp32 difference
+
+
+def test_perturbed_top1_samples_the_softmax(orc):
+    """Gumbel-max: with keys = ln p and standard Gumbel noise at scale 1, the
+    top-1 block is a draw from p (checked by frequency over 4000 seeded
+    draws, each within 4.5 standard deviations)."""
+    p = np.array([0.05, 0.4, 0.15, 0.3, 0.1])
+    keys = np.log(p).astype(np.float32)[None, None, :]
+    r = rng(39)
+    T = 4000
+    counts = np.zeros(5)
+    noise = r.gumbel(size=(T, 5)).astype(np.float32)
+    for t in range(T):
+        kp = orc.perturb_keys(keys, noise[t][None, None, :], 1.0)
+        counts[int(np.argmax(kp[0, 0]))] += 1
+    sd = np.sqrt(T * p * (1 - p))
+    assert np.all(np.abs(counts - T * p) < 4.5 * sd)
+
+
+def test_perturb_keys_is_one_fma(orc):
+    """key' = fmaf(noise, scale, key) (noise None or scale 0: key itself);
+    checked against an exact rational evaluation rounded once to fp32."""
+    from fractions import Fraction
+    r = rng(40)
+    k = r.standard_normal(64).astype(np.float32)
+    n = r.standard_normal(64).astype(np.float32)
+    out = orc.perturb_keys(k, n, 0.37)
+    s32 = float(np.float32(0.37))
+    for a, b, o in zip(k, n, out):
+        exact = Fraction(float(b)) * Fraction(s32) + Fraction(float(a))
+        assert o == np.float32(float(exact))
+    assert np.array_equal(orc.perturb_keys(k, None, 5.0), k)
+    assert np.array_equal(orc.perturb_keys(k, n, 0.0), k)
