@@ -7,7 +7,8 @@ Public surface (Python names mirror the C ABI in include/bsa.h):
 ``forward_int8``, ``debug_int8_qk``, ``debug_int8_pv``, the offline calibration
 ``attn_block_stats``, ``paro_metric``, ``paro_select`` (chained by
 ``paro_calibrate``), the static masks ``mask_from_block_sums`` and
-``mask_from_bits``, plus ``LayerPlan`` / ``layer_forward`` which chain the
+``mask_from_bits``, the Top-K / Top-P / noise-perturbed selection
+``block_scores`` + ``mask_from_scores``, plus ``LayerPlan`` / ``layer_forward`` which chain the
 per-step calls.
 The HIP library is loaded on first use and must be built; there is no
 fallback path.  ``synth`` holds the seeded synthetic workload generators.
@@ -16,6 +17,7 @@ from .api import (  # noqa: F401
     LayerPlan,
     abi_version,
     attn_block_stats,
+    block_scores,
     build_mask,
     build_mask_pooled,
     debug_int8_pv,
@@ -27,6 +29,7 @@ from .api import (  # noqa: F401
     mask_capacity,
     mask_from_bits,
     mask_from_block_sums,
+    mask_from_scores,
     mask_params,
     mask_workspace,
     order_scores,

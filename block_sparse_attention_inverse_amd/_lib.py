@@ -57,6 +57,11 @@ SIGNATURES = {
     "bsa_mask_from_block_sums": (_I, [_P, _I, _I, _I, _I, _F, _I, _P, _P, _L, _P, _P, _L, _P]),
     "bsa_mask_bits_workspace": (_L, [_I]),
     "bsa_mask_from_bits": (_I, [_P, _I, _I, _P, _P, _L, _P, _P, _L, _P]),
+    "bsa_block_scores": (_I, [_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MaskParams), _P, _P, _L,
+                              _P]),
+    "bsa_scores_select_workspace": (_L, [_I, _I, _I, _I, _I, _I]),
+    "bsa_mask_from_scores": (_I, [_P, _P, _F, _I, _I, _I, _I, _P, ctypes.POINTER(MaskParams), _I,
+                                  _F, _F, _P, _P, _L, _P, _P, _L, _P]),
 }
 
 _lib = None

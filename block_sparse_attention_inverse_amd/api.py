@@ -185,6 +185,65 @@ def build_mask_pooled(sums_q, sums_k, axis_order, F, H, W, params: MaskParams, w
     return row_ptr, col_idx, nnz
 
 
+def block_scores(sums_q, sums_k, F, H, W, params: MaskParams, out=None, workspace=None):
+    """bsa_block_scores: fp32 [G][Nq][Nkv] scores of every (q-block, kv-block)
+    pair from per-block channel sums (the keys the mask build ranks)."""
+    _dev(sums_q, sums_k)
+    G, _, d = sums_q.shape
+    N = F * H * W
+    nq, nk = (N + params.Bq - 1) // params.Bq, (N + params.Bk - 1) // params.Bk
+    for t, nb in ((sums_q, nq), (sums_k, nk)):
+        if t.shape != (G, nb, d) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("sums must be contiguous fp32 [G][ceil(N/B)][d] (Bq for Q, Bk for K)")
+    if out is None:
+        out = torch.empty((G, nq, nk), dtype=torch.float32, device=sums_q.device)
+    if out.shape != (G, nq, nk) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [G][Nq][Nkv]")
+    ws_bytes = mask_workspace(G, F, H, W, d, params)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=sums_q.device)
+    check(_lib.load().bsa_block_scores(_ptr(sums_q), _ptr(sums_k), G, F, H, W, d,
+                                       ctypes.byref(params), _ptr(out), _ptr(workspace),
+                                       workspace.numel(), _stream()))
+    return out
+
+
+def mask_from_scores(scores, axis_order, F, H, W, params: MaskParams, top_p=None, temp=1.0,
+                     noise=None, noise_scale=1.0, workspace=None):
+    """bsa_mask_from_scores: Top-K (top_p None: the budget of ``params``) or
+    Top-P (top_p in (0, 1], weights exp2((score - max) * temp)) per q-block
+    row of scores fp32 [G][Nq][Nkv], optionally perturbed by ``noise`` (same
+    shape; score' = fma(noise, noise_scale, score)), plus the forced
+    diagonal / window of ``params``.  Returns (row_ptr, col_idx, nnz) with
+    col_idx the full-capacity buffer and nnz a device int32 [1]."""
+    G, nq, nk = scores.shape
+    N = F * H * W
+    if nq != (N + params.Bq - 1) // params.Bq or nk != (N + params.Bk - 1) // params.Bk:
+        raise ValueError("scores shape does not match the grid and blocks")
+    for t in (scores, noise):
+        if t is not None and (t.shape != scores.shape or t.dtype != torch.float32
+                              or not t.is_contiguous()):
+            raise ValueError("scores / noise must be contiguous fp32 [G][Nq][Nkv]")
+    _dev(scores, axis_order, *(t for t in (noise,) if t is not None))
+    mode = 0 if top_p is None else 1
+    cap = mask_capacity(G, F, H, W, params) if mode == 0 else G * nq * nk
+    ws_bytes = int(_lib.load().bsa_scores_select_workspace(G, F, H, W, params.Bq, params.Bk))
+    if ws_bytes < 0:
+        raise ValueError("bsa_scores_select_workspace: unsupported sizes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
+    row_ptr = torch.empty(G * nq + 1, dtype=torch.int32, device=scores.device)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=scores.device)
+    nnz = torch.empty(1, dtype=torch.int32, device=scores.device)
+    check(_lib.load().bsa_mask_from_scores(_ptr(scores), _ptr(noise) if noise is not None else None,
+                                           float(noise_scale), G, F, H, W, _ptr(axis_order),
+                                           ctypes.byref(params), mode,
+                                           float(top_p) if top_p is not None else 0.0, float(temp),
+                                           _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(nnz),
+                                           _ptr(workspace), workspace.numel(), _stream()))
+    return row_ptr, col_idx, nnz
+
+
 def order_workspace(G, F, H, W, B) -> int:
     v = int(_lib.load().bsa_order_workspace(G, F, H, W, B))
     if v < 0:

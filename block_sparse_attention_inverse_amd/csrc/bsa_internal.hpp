@@ -45,6 +45,21 @@ hipError_t launch_bits_to_csr(const unsigned long long* bits, int R, int nk, int
                               int32_t* row_ptr, int32_t* col_idx, int64_t cap, int32_t* nnz,
                               hipStream_t s);
 
+// score matrix [G][nq][nk] of every (q-block, kv-block) pair from per-block
+// channel sums (same fp32 sequence as the select step)
+hipError_t launch_block_scores(const MaskGeom& m, const float* sums_q, const float* sums_k,
+                               float* scores, char* ws, hipStream_t s);
+// selection from a score matrix by sorting each row: mode 0 top-k (k),
+// 1 top-p (frac, temp), 2 block-sum mass (frac); optional noise (key' =
+// fmaf(noise, nscale, key)); forced diagonal / window; CSR.  orders may be
+// null when win_T < 0.  Workspace: sorted_select_workspace_bytes.
+size_t sorted_select_workspace_bytes(int G, int nq, int nk);
+hipError_t launch_sorted_select(int mode, const float* keys, const float* noise, float nscale,
+                                const uint8_t* orders, int G, int F, int H, int W, int Bq, int Bk,
+                                int k, float frac, float temp, int force_diag, int win_T,
+                                int win_r0, int32_t* row_ptr, int32_t* col_idx, int64_t cap,
+                                int32_t* nnz, void* ws, hipStream_t s);
+
 // ---- calib.hip -------------------------------------------------------------
 hipError_t launch_block_stats(const uint16_t* Qp, const uint16_t* Kp, int G, int N, int d, int B,
                               float sm_scale, float eps, int32_t* cnt, float* bsum, float* bmax,
@@ -53,10 +68,6 @@ hipError_t launch_paro_metric(const int32_t* cnt, const float* bsum, const float
                               int N, int B, int sigma_num, int sigma_den, float alpha, int order,
                               float* stats, hipStream_t s);
 hipError_t launch_paro_select(const float* stats, int G, uint8_t* orders, hipStream_t s);
-size_t mass_select_workspace_bytes(int G, int nq, int nk);
-hipError_t launch_mass_select(const float* keys, int G, int N, int Bq, int Bk, float mass,
-                              int force_diag, int32_t* row_ptr, int32_t* col_idx, int64_t cap,
-                              int32_t* nnz, void* ws, hipStream_t s);
 
 // ---- fused.hip -------------------------------------------------------------
 hipError_t launch_permute_pool(const void* src, int src_dt, uint16_t* dst, int64_t stride_g,

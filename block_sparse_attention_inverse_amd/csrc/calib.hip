@@ -1,6 +1,7 @@
 // calib.hip — offline calibration of the static path: statistics of the dense
-// post-softmax map per block, the order metric built from them, the argmin
-// over the six axis orders, and the static mask by block-sum thresholding.
+// post-softmax map per block, the order metric built from them, and the
+// argmin over the six axis orders (the static mask by block-sum
+// thresholding is the mass mode of the sorted selection in mask.hip).
 //
 // PAROAttention machine verdict (pith.science, arXiv 2506.16054), key
 // machinery: each head's axis order is picked offline from its post-softmax
@@ -314,77 +315,6 @@ __global__ void paro_select_kernel(const float* __restrict__ stats, int G, uint8
   orders[g] = static_cast<uint8_t>(best);
 }
 
-// ---- static mask by block-sum thresholding: one workgroup per q-block row.
-// Keys (anything not > 0 taken as +0) sorted by (key descending, index
-// ascending) as 64-bit images (~key bits : index) with a bitonic sort in LDS;
-// one lane forms the fp32 running sums in that order; k* is the first
-// position whose running sum reaches total*mass.
-constexpr int kMassThreads = 256;
-
-__global__ __launch_bounds__(kMassThreads) void mass_select_kernel(
-    const float* __restrict__ keys, int N, int Bq, int Bk, int nq, int nk, int p2, int words,
-    float mass, int force_diag, unsigned long long* __restrict__ bits) {
-  extern __shared__ unsigned long long srt[];  // [p2] images, then [nk] fp32 prefix sums
-  float* pre = reinterpret_cast<float*>(srt + p2);
-  __shared__ uint32_t keep[2 * 128];            // bitmask words (nk <= 8192)
-  __shared__ int s_k;
-  const int row = blockIdx.x, t = threadIdx.x;
-  const float* kr = keys + static_cast<int64_t>(row) * nk;
-  for (int e = t; e < p2; e += kMassThreads) {
-    unsigned long long img = ~0ull;
-    if (e < nk) {
-      const float k = kr[e];
-      const uint32_t kb = k > 0.0f ? __float_as_uint(k) : 0u;
-      img = (static_cast<unsigned long long>(~kb) << 32) | static_cast<uint32_t>(e);
-    }
-    srt[e] = img;
-  }
-  for (int e = t; e < 2 * words; e += kMassThreads) keep[e] = 0u;
-  if (t == 0) s_k = nk;
-  __syncthreads();
-  for (int k = 2; k <= p2; k <<= 1)
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int e = t; e < p2; e += kMassThreads) {
-        const int o = e ^ jj;
-        if (o > e) {
-          const unsigned long long a = srt[e], b = srt[o];
-          const bool up = (e & k) == 0;
-          if ((a > b) == up) { srt[e] = b; srt[o] = a; }
-        }
-      }
-      __syncthreads();
-    }
-  if (t == 0) {
-    float run = 0.0f;
-    for (int p = 0; p < nk; p++) {
-      run += __uint_as_float(~static_cast<uint32_t>(srt[p] >> 32));
-      pre[p] = run;
-    }
-  }
-  __syncthreads();
-  const float thr = pre[nk - 1] * mass;
-  for (int p = t; p < nk; p += kMassThreads)
-    if (pre[p] >= thr && (p == 0 || pre[p - 1] < thr)) s_k = p + 1;
-  __syncthreads();
-  const int kstar = s_k;
-  for (int p = t; p < kstar; p += kMassThreads) {
-    const uint32_t j = static_cast<uint32_t>(srt[p]);
-    atomicOr(&keep[j / 32], 1u << (j % 32));
-  }
-  if (force_diag) {
-    const int i = row % nq;
-    const int q0 = i * Bq, q1 = min(q0 + Bq, N);
-    for (int j = t; j < nk; j += kMassThreads) {
-      const int k0 = j * Bk, k1 = min(k0 + Bk, N);
-      if (k0 < q1 && q0 < k1) atomicOr(&keep[j / 32], 1u << (j % 32));
-    }
-  }
-  __syncthreads();
-  for (int wd = t; wd < words; wd += kMassThreads)
-    bits[static_cast<int64_t>(row) * words + wd] =
-        static_cast<unsigned long long>(keep[2 * wd]) | (static_cast<unsigned long long>(keep[2 * wd + 1]) << 32);
-}
-
 }  // namespace
 
 hipError_t launch_block_stats(const uint16_t* Qp, const uint16_t* Kp, int G, int N, int d, int B,
@@ -414,36 +344,6 @@ hipError_t launch_paro_metric(const int32_t* cnt, const float* bsum, const float
 hipError_t launch_paro_select(const float* stats, int G, uint8_t* orders, hipStream_t s) {
   paro_select_kernel<<<(G + 63) / 64, 64, 0, s>>>(stats, G, orders);
   return hipGetLastError();
-}
-
-size_t mass_select_workspace_bytes(int G, int nq, int nk) {
-  const size_t R = static_cast<size_t>(G) * nq;
-  const size_t words = (static_cast<size_t>(nk) + 63) / 64;
-  return R * words * 8 + ((R * 4 + 255) & ~static_cast<size_t>(255));
-}
-
-hipError_t launch_mass_select(const float* keys, int G, int N, int Bq, int Bk, float mass,
-                              int force_diag, int32_t* row_ptr, int32_t* col_idx, int64_t cap,
-                              int32_t* nnz, void* ws, hipStream_t s) {
-  const int nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
-  const int words = (nk + 63) / 64;
-  const int R = G * nq;
-  int p2 = 1;
-  while (p2 < nk) p2 <<= 1;
-  auto* bits = static_cast<unsigned long long*>(ws);
-  auto* counts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + static_cast<size_t>(R) * words * 8);
-  const size_t lds = sizeof(unsigned long long) * p2 + sizeof(float) * nk;
-  if (lds > 65536) {
-    const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&mass_select_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(lds));
-    if (a != hipSuccess) return a;
-  }
-  mass_select_kernel<<<R, kMassThreads, lds, s>>>(keys, N, Bq, Bk, nq, nk, p2, words, mass,
-                                                  force_diag, bits);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_bits_to_csr(bits, R, nk, counts, row_ptr, col_idx, cap, nnz, s);
 }
 
 }  // namespace bsa

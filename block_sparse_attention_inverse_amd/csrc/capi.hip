@@ -418,7 +418,7 @@ int64_t bsa_mask_sums_workspace(int32_t G, int32_t N, int32_t Bq, int32_t Bk) {
   if (G <= 0 || N <= 0 || !block_ok(Bq) || !block_ok(Bk)) return -1;
   const int nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
   if (nk > 8192 || static_cast<int64_t>(G) * nq >= (1ll << 31)) return -1;
-  return static_cast<int64_t>(bsa::mass_select_workspace_bytes(G, nq, nk));
+  return static_cast<int64_t>(bsa::sorted_select_workspace_bytes(G, nq, nk));
 }
 
 int bsa_mask_from_block_sums(const float* keys, int32_t G, int32_t N, int32_t Bq, int32_t Bk,
@@ -441,9 +441,12 @@ int bsa_mask_from_block_sums(const float* keys, int32_t G, int32_t N, int32_t Bq
     if (!aligned(workspace, 256)) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
     if (ws_bytes < need)
       return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
-    return hip_status(bsa::launch_mass_select(keys, G, N, Bq, Bk, mass, force_diag != 0, row_ptr,
-                                              col_idx, col_capacity, nnz, workspace,
-                                              as_stream(stream)),
+    // the block-sum mass mode of the sorted selection (no window: the
+    // token grid only matters for it, so the sequence is passed as 1 x 1 x N)
+    return hip_status(bsa::launch_sorted_select(2, keys, nullptr, 0.0f, nullptr, G, 1, 1, N, Bq, Bk,
+                                                0, mass, 0.0f, force_diag != 0, -1, 0, row_ptr,
+                                                col_idx, col_capacity, nnz, workspace,
+                                                as_stream(stream)),
                       "bsa_mask_from_block_sums");
   });
 }
@@ -472,6 +475,67 @@ int bsa_mask_from_bits(const uint64_t* bits, int32_t rows, int32_t nk, int32_t* 
                                               nk, static_cast<int32_t*>(workspace), row_ptr, col_idx,
                                               col_capacity, nnz, as_stream(stream)),
                       "bsa_mask_from_bits");
+  });
+}
+
+int bsa_block_scores(const float* sums_q, const float* sums_k, int32_t G, int32_t F, int32_t H,
+                     int32_t W, int32_t d, const bsa_mask_params* p_host, float* scores,
+                     void* workspace, int64_t ws_bytes, void* stream) {
+  return guarded([&]() -> int {
+    bsa::MaskGeom m{};
+    const int rc = mask_geom(G, F, H, W, d, p_host, m);
+    if (rc != BSA_OK) return rc;
+    if (!sums_q || !sums_k || !scores || !workspace) return fail(BSA_EINVAL, "NULL pointer");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    if (!aligned(sums_k, 16) || !aligned(workspace, 256))
+      return fail(BSA_EINVAL, "sums_k 16-byte, workspace 256-byte alignment required");
+    const int64_t need = static_cast<int64_t>(bsa::mask_workspace_layout(m).total);
+    if (ws_bytes < need)
+      return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
+    return hip_status(bsa::launch_block_scores(m, sums_q, sums_k, scores, static_cast<char*>(workspace),
+                                               as_stream(stream)),
+                      "bsa_block_scores");
+  });
+}
+
+int64_t bsa_scores_select_workspace(int32_t G, int32_t F, int32_t H, int32_t W, int32_t Bq,
+                                    int32_t Bk) {
+  if (G <= 0 || F <= 0 || H <= 0 || W <= 0 || !block_ok(Bq) || !block_ok(Bk)) return -1;
+  const int64_t N = static_cast<int64_t>(F) * H * W;
+  if (N >= (1ll << 31)) return -1;
+  const int64_t nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+  if (nk > 8192 || G * nq >= (1ll << 31)) return -1;
+  return static_cast<int64_t>(bsa::sorted_select_workspace_bytes(G, static_cast<int>(nq),
+                                                                 static_cast<int>(nk)));
+}
+
+int bsa_mask_from_scores(const float* scores, const float* noise, float noise_scale, int32_t G,
+                         int32_t F, int32_t H, int32_t W, const uint8_t* axis_order,
+                         const bsa_mask_params* p_host, int32_t mode, float top_p, float temp,
+                         int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* nnz,
+                         void* workspace, int64_t ws_bytes, void* stream) {
+  return guarded([&]() -> int {
+    bsa::MaskGeom m{};
+    const int rc = mask_geom(G, F, H, W, 64, p_host, m);
+    if (rc != BSA_OK) return rc;
+    if (!scores || !row_ptr || !col_idx || !nnz || !workspace) return fail(BSA_EINVAL, "NULL pointer");
+    if (m.win_T >= 0 && !axis_order) return fail(BSA_EINVAL, "axis_order is required with a window");
+    if (mode != 0 && mode != 1) return fail(BSA_EINVAL, "mode must be 0 (top-k) or 1 (top-p)");
+    if (mode == 1 && !(top_p > 0.0f && top_p <= 1.0f)) return fail(BSA_EINVAL, "top_p must be in (0, 1]");
+    if (mode == 1 && !(temp >= 0.0f && std::isfinite(temp))) return fail(BSA_EINVAL, "temp must be >= 0 and finite");
+    if (noise && !std::isfinite(noise_scale)) return fail(BSA_EINVAL, "noise_scale must be finite");
+    const int64_t need_cols = mode == 0 ? capacity_of(m) : static_cast<int64_t>(G) * m.nq * m.nk;
+    if (col_capacity < need_cols)
+      return fail(BSA_ECAPACITY, "col_capacity %lld < %lld", (long long)col_capacity, (long long)need_cols);
+    const int64_t need = bsa_scores_select_workspace(G, F, H, W, m.Bq, m.Bk);
+    if (!aligned(workspace, 256)) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+      return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
+    return hip_status(bsa::launch_sorted_select(mode, scores, noise, noise_scale, axis_order, G, F, H, W,
+                                                m.Bq, m.Bk, m.k, top_p, temp, m.force_diag, m.win_T,
+                                                m.win_r0, row_ptr, col_idx, col_capacity, nnz,
+                                                workspace, as_stream(stream)),
+                      "bsa_mask_from_scores");
   });
 }
 

@@ -322,6 +322,142 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// scores_kernel: the key of every (q-block, kv-block) pair written out, by
+// the same fp32 sequence as select_kernel (fma chain over the channels in
+// order; COSINE: one correctly rounded divide by the product of the norms).
+// One workgroup per q-block row.
+template <int D>
+__global__ __launch_bounds__(kSelThreads) void scores_kernel(
+    const float* __restrict__ sum_q, const float* __restrict__ sum_k,
+    const float* __restrict__ norm_q, const float* __restrict__ norm_k, int nq, int nk, int score,
+    float* __restrict__ out) {
+  __shared__ float a[D];
+  const int row = blockIdx.x, g = row / nq, t = threadIdx.x;
+  for (int c = t; c < D; c += kSelThreads) a[c] = sum_q[static_cast<int64_t>(row) * D + c];
+  __syncthreads();
+  const float nqv = score == 1 ? norm_q[row] : 0.0f;
+  for (int j = t; j < nk; j += kSelThreads) {
+    const float4* bj = reinterpret_cast<const float4*>(sum_k + (static_cast<int64_t>(g) * nk + j) * D);
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int c4 = 0; c4 < D / 4; c4++) {
+      const float4 v = bj[c4];
+      acc = __builtin_fmaf(a[4 * c4 + 0], v.x, acc);
+      acc = __builtin_fmaf(a[4 * c4 + 1], v.y, acc);
+      acc = __builtin_fmaf(a[4 * c4 + 2], v.z, acc);
+      acc = __builtin_fmaf(a[4 * c4 + 3], v.w, acc);
+    }
+    float key = acc;
+    if (score == 1) {
+      const float den = nqv * norm_k[static_cast<int64_t>(g) * nk + j];
+      key = (den == 0.0f) ? 0.0f : div_rn(acc, den);
+    }
+    out[static_cast<int64_t>(row) * nk + j] = key;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// sorted_select_kernel: selection from a score matrix by sorting each row.
+// One workgroup per q-block row.  Scores, perturbed by an optional noise
+// input (key' = fmaf(noise, scale, key)), are sorted by (key' descending,
+// index ascending) as 64-bit images (~order bits : index) with a bitonic
+// sort in LDS.  The row keeps the first k* of that order:
+//   SEL_TOPK  k* = k;
+//   SEL_TOPP  weights w = exp2f((key'_p - key'_0) * temp), fp32 running sums
+//             P_p in sorted order (one lane), k* = the first p with
+//             P_p >= frac * P_last (plus one);
+//   SEL_MASS  the same with w = key' itself (keys not > 0 taken as +0);
+// plus the forced set (diagonal overlap, temporal window) of select_kernel.
+enum { SEL_TOPK = 0, SEL_TOPP = 1, SEL_MASS = 2 };
+
+__device__ __forceinline__ float key_from_order_bits(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kSelThreads) void sorted_select_kernel(
+    const float* __restrict__ keys, const float* __restrict__ noise, float nscale,
+    const uint8_t* __restrict__ orders, int N, int F, int H, int W, int Bq, int Bk, int nq, int nk,
+    int p2, int words, int k, float frac, float temp, int force_diag, int win_T, int win_r0,
+    unsigned long long* __restrict__ bits) {
+  extern __shared__ unsigned long long srt[];  // [p2] images, then [nk] fp32 running sums
+  float* pre = reinterpret_cast<float*>(srt + p2);
+  __shared__ uint32_t keep[2 * 128];           // row bitmask (nk <= 8192)
+  __shared__ int s_k;
+  const int row = blockIdx.x, g = row / nq, i = row % nq, t = threadIdx.x;
+  const int64_t base = static_cast<int64_t>(row) * nk;
+  for (int e = t; e < p2; e += kSelThreads) {
+    unsigned long long img = ~0ull;
+    if (e < nk) {
+      float x = keys[base + e];
+      if (noise != nullptr) x = __builtin_fmaf(noise[base + e], nscale, x);
+      if (MODE == SEL_MASS) x = x > 0.0f ? x : 0.0f;
+      img = (static_cast<unsigned long long>(~key_order_bits(x)) << 32) | static_cast<uint32_t>(e);
+    }
+    srt[e] = img;
+  }
+  for (int e = t; e < 2 * words; e += kSelThreads) keep[e] = 0u;
+  if (t == 0) s_k = MODE == SEL_TOPK ? min(k, nk) : nk;
+  __syncthreads();
+  for (int kk = 2; kk <= p2; kk <<= 1)
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int e = t; e < p2; e += kSelThreads) {
+        const int o = e ^ jj;
+        if (o > e) {
+          const unsigned long long a = srt[e], b = srt[o];
+          const bool up = (e & kk) == 0;
+          if ((a > b) == up) { srt[e] = b; srt[o] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  if constexpr (MODE != SEL_TOPK) {
+    if (t == 0) {
+      const float top = key_from_order_bits(~static_cast<uint32_t>(srt[0] >> 32));
+      float run = 0.0f;
+      for (int p = 0; p < nk; p++) {
+        const float x = key_from_order_bits(~static_cast<uint32_t>(srt[p] >> 32));
+        run += MODE == SEL_MASS ? x : exp2f((x - top) * temp);
+        pre[p] = run;
+      }
+    }
+    __syncthreads();
+    const float thr = pre[nk - 1] * frac;
+    for (int p = t; p < nk; p += kSelThreads)
+      if (pre[p] >= thr && (p == 0 || pre[p - 1] < thr)) s_k = p + 1;
+    __syncthreads();
+  }
+  const int kstar = s_k;
+  for (int p = t; p < kstar; p += kSelThreads) {
+    const uint32_t j = static_cast<uint32_t>(srt[p]);
+    atomicOr(&keep[j / 32], 1u << (j % 32));
+  }
+  const int q0 = i * Bq, q1 = min(q0 + Bq, N);
+  const int order = win_T >= 0 ? orders[g] : 0;
+  int fi = 0, oi = 0;
+  if (win_T >= 0) block_centre(order, i, Bq, N, F, H, W, fi, oi);
+  for (int j = t; j < nk; j += kSelThreads) {
+    bool f = false;
+    if (force_diag) {
+      const int k0 = j * Bk, k1 = min(k0 + Bk, N);
+      f = k0 < q1 && q0 < k1;
+    }
+    if (!f && win_T >= 0) {
+      int fj, oj;
+      block_centre(order, j, Bk, N, F, H, W, fj, oj);
+      const int df = abs(fi - fj), dox = abs(oi - oj);
+      f = df <= win_T && static_cast<int64_t>(dox) <= ((static_cast<int64_t>(win_r0) * W) >> df);
+    }
+    if (f) atomicOr(&keep[j / 32], 1u << (j % 32));
+  }
+  __syncthreads();
+  for (int wd = t; wd < words; wd += kSelThreads)
+    bits[static_cast<int64_t>(row) * words + wd] =
+        static_cast<unsigned long long>(keep[2 * wd]) |
+        (static_cast<unsigned long long>(keep[2 * wd + 1]) << 32);
+}
+
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ counts,
                                                             int R, int32_t* __restrict__ row_ptr,
                                                             int32_t* __restrict__ nnz) {
@@ -513,6 +649,74 @@ hipError_t launch_build_mask_pooled(const MaskGeom& m, const float* sums_q, cons
     finish_pool_kernel<64><<<total_blocks, 64, 0, s>>>(sums_q, sums_k, m.G, N, m.Bq, m.Bk, m.nq,
                                                        m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
   return select_and_emit(m, orders, row_ptr, col_idx, col_capacity, nnz, ws, s);
+}
+
+}  // namespace bsa
+
+namespace bsa {
+
+hipError_t launch_block_scores(const MaskGeom& m, const float* sums_q, const float* sums_k,
+                               float* scores, char* ws, hipStream_t s) {
+  const MaskWs L = mask_workspace_layout(m);
+  float* sum_q = reinterpret_cast<float*>(ws + L.sum_q);
+  float* sum_k = reinterpret_cast<float*>(ws + L.sum_k);
+  float* norm_q = reinterpret_cast<float*>(ws + L.norm_q);
+  float* norm_k = reinterpret_cast<float*>(ws + L.norm_k);
+  const int N = static_cast<int>(m.N);
+  const uint32_t total_blocks = static_cast<uint32_t>(static_cast<int64_t>(m.G) * (m.nq + m.nk));
+  const uint32_t rows = static_cast<uint32_t>(m.G) * m.nq;
+  if (m.d == 128) {
+    finish_pool_kernel<128><<<total_blocks, 128, 0, s>>>(sums_q, sums_k, m.G, N, m.Bq, m.Bk, m.nq,
+                                                         m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
+    scores_kernel<128><<<rows, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, m.nq, m.nk, m.score,
+                                                    scores);
+  } else {
+    finish_pool_kernel<64><<<total_blocks, 64, 0, s>>>(sums_q, sums_k, m.G, N, m.Bq, m.Bk, m.nq,
+                                                       m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
+    scores_kernel<64><<<rows, kSelThreads, 0, s>>>(sum_q, sum_k, norm_q, norm_k, m.nq, m.nk, m.score,
+                                                   scores);
+  }
+  return hipGetLastError();
+}
+
+size_t sorted_select_workspace_bytes(int G, int nq, int nk) {
+  const size_t R = static_cast<size_t>(G) * nq;
+  const size_t words = (static_cast<size_t>(nk) + 63) / 64;
+  return align256(R * words * 8) + align256(R * 4);
+}
+
+hipError_t launch_sorted_select(int mode, const float* keys, const float* noise, float nscale,
+                                const uint8_t* orders, int G, int F, int H, int W, int Bq, int Bk,
+                                int k, float frac, float temp, int force_diag, int win_T,
+                                int win_r0, int32_t* row_ptr, int32_t* col_idx, int64_t cap,
+                                int32_t* nnz, void* ws, hipStream_t s) {
+  const int N = F * H * W;
+  const int nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+  const int words = (nk + 63) / 64;
+  const int R = G * nq;
+  int p2 = 1;
+  while (p2 < nk) p2 <<= 1;
+  auto* bits = static_cast<unsigned long long*>(ws);
+  auto* counts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                            align256(static_cast<size_t>(R) * words * 8));
+  const size_t lds = sizeof(unsigned long long) * p2 + sizeof(float) * nk;
+  auto run = [&](auto kern) -> hipError_t {
+    if (lds > 65536) {
+      const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(lds));
+      if (a != hipSuccess) return a;
+    }
+    kern<<<R, kSelThreads, lds, s>>>(keys, noise, nscale, orders, N, F, H, W, Bq, Bk, nq, nk, p2,
+                                     words, k, frac, temp, force_diag, win_T, win_r0, bits);
+    return hipGetLastError();
+  };
+  hipError_t e;
+  if (mode == SEL_TOPK) e = run(sorted_select_kernel<SEL_TOPK>);
+  else if (mode == SEL_TOPP) e = run(sorted_select_kernel<SEL_TOPP>);
+  else e = run(sorted_select_kernel<SEL_MASS>);
+  if (e != hipSuccess) return e;
+  return launch_bits_to_csr(bits, R, nk, counts, row_ptr, col_idx, cap, nnz, s);
 }
 
 }  // namespace bsa

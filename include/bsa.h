@@ -273,6 +273,54 @@ int bsa_debug_int8_pv(const int8_t *P8, const int8_t *Vq, int32_t G, int32_t N, 
                       int32_t Bq, int32_t Bk, const int32_t *gj, int32_t n, int32_t *OV,
                       void *stream);
 
+/* ---- selection from a score matrix: Top-K, Top-P, stochastic scoring ------
+ * SPADE verdict, key machinery: the kept blocks pass a head-wise Top-K /
+ * Top-P filter and a local window.  PASA review (arXiv 2604.12219): a
+ * stochastic selection bias (temperature-scaled Gumbel perturbation of the
+ * block scores) softens the selection boundary; the random draws come in
+ * as an input (`noise`), so a seeded caller reproduces every mask. */
+
+/* bsa_block_scores — the block score of every (q-block, kv-block) pair,
+ * scores fp32 [G][Nq][Nkv], from per-block channel sums (as
+ * bsa_permute_pool emits them), by the fixed fp32 sequence of
+ * bsa_build_mask (DOT of means or COSINE of sums, p_host->score): the keys
+ * bsa_build_mask_pooled ranks, bit for bit.  workspace: >=
+ * bsa_mask_workspace bytes, 256-byte aligned.  sums_k 16-byte aligned.
+ * Errors: EINVAL, EUNSUPPORTED, ECAPACITY, EHIP. */
+int bsa_block_scores(const float *sums_q, const float *sums_k, int32_t G, int32_t F, int32_t H,
+                     int32_t W, int32_t d, const bsa_mask_params *p_host, float *scores,
+                     void *workspace, int64_t ws_bytes, void *stream);
+
+/* bsa_scores_select_workspace — device workspace bytes for
+ * bsa_mask_from_scores, or -1 for unsupported sizes. */
+int64_t bsa_scores_select_workspace(int32_t G, int32_t F, int32_t H, int32_t W, int32_t Bq,
+                                    int32_t Bk);
+
+/* bsa_mask_from_scores — per q-block row of scores fp32 [G][Nq][Nkv]:
+ *   key' = fmaf(noise, noise_scale, key) when noise (fp32, same shape) is
+ *          given, else key;
+ *   kv-blocks in (key' descending, index ascending) order;
+ *   mode 0 (Top-K): keep the first k = max(1, min(Nkv, floor(rho*Nkv+1/2)))
+ *          (p_host->rho_num / rho_den);
+ *   mode 1 (Top-P): weights w_p = exp2f((key'_p - key'_0) * temp) (the
+ *          softmax of the scores at inverse temperature temp, log2 units),
+ *          fp32 running sums P_k in that order, keep the first k* = the
+ *          smallest k >= 1 with P_k >= top_p * P_Nkv (exp2f is the device's;
+ *          a k* next to the threshold can differ from another exp2f's);
+ * plus the forced set of bsa_build_mask (diagonal overlap with force_diag,
+ * the temporal window with win_T >= 0, which needs axis_order).  With
+ * noise NULL, mode 0 on bsa_block_scores' output equals
+ * bsa_build_mask_pooled bit for bit.  Outputs as bsa_build_mask;
+ * col_capacity >= bsa_mask_capacity (mode 0) or G*Nq*Nkv (mode 1); Nkv
+ * <= 8192; workspace 256-byte aligned, >= bsa_scores_select_workspace.
+ * A NaN score or noise gives an unspecified (but valid) selection.
+ * Errors: EINVAL, EUNSUPPORTED, ECAPACITY, EHIP. */
+int bsa_mask_from_scores(const float *scores, const float *noise, float noise_scale, int32_t G,
+                         int32_t F, int32_t H, int32_t W, const uint8_t *axis_order,
+                         const bsa_mask_params *p_host, int32_t mode, float top_p, float temp,
+                         int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity, int32_t *nnz,
+                         void *workspace, int64_t ws_bytes, void *stream);
+
 /* ---- offline calibration of the static path ------------------------------
  * PAROAttention verdict, key machinery: each head's axis order is chosen
  * offline from its post-softmax attention map by a metric that weighs block

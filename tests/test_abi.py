@@ -38,7 +38,8 @@ def test_header_lists_the_entry_points():
               "bsa_permute_pool", "bsa_build_mask_pooled", "bsa_order_workspace",
               "bsa_order_scores", "bsa_select_orders", "bsa_attn_block_stats",
               "bsa_paro_metric", "bsa_paro_select", "bsa_mask_sums_workspace",
-              "bsa_mask_from_block_sums", "bsa_mask_bits_workspace", "bsa_mask_from_bits"):
+              "bsa_mask_from_block_sums", "bsa_mask_bits_workspace", "bsa_mask_from_bits",
+              "bsa_block_scores", "bsa_scores_select_workspace", "bsa_mask_from_scores"):
         assert n in names
 
 
@@ -185,3 +186,38 @@ def test_calibration_and_static_mask_argument_errors(lib):
     assert lib.bsa_mask_from_bits(fake, 10, 100, fake, fake, 999, fake, fake, 256, None) == -3
     assert lib.bsa_mask_from_bits(P(0x1004), 10, 100, fake, fake, 1000, fake, fake, 256,
                                   None) == -1
+
+
+def test_scores_selection_argument_errors(lib):
+    """Host checks of the score-matrix selection; none reaches HIP."""
+    from block_sparse_attention_inverse_amd._lib import MaskParams
+
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    F = ctypes.c_float
+    p = MaskParams(64, 64, 0, 30, 100, 1, -1, 0)
+    pw = MaskParams(64, 64, 0, 30, 100, 1, 2, 4)  # with a temporal window
+    ws = lib.bsa_scores_select_workspace(2, 2, 8, 40, 64, 64)
+    assert ws > 0 and lib.bsa_scores_select_workspace(2, 2, 8, 40, 64, 96) == -1
+    big = 1 << 30
+    args = (fake, None, F(0), 2, 2, 8, 40)
+    # bad mode, top_p out of range, negative temperature, window without orders
+    assert lib.bsa_mask_from_scores(*args, fake, ctypes.byref(p), 2, F(0.5), F(1), fake, fake, big,
+                                    fake, P(0x1000), ws, None) == -1
+    assert lib.bsa_mask_from_scores(*args, fake, ctypes.byref(p), 1, F(0.0), F(1), fake, fake, big,
+                                    fake, P(0x1000), ws, None) == -1
+    assert lib.bsa_mask_from_scores(*args, fake, ctypes.byref(p), 1, F(0.5), F(-1), fake, fake, big,
+                                    fake, P(0x1000), ws, None) == -1
+    assert lib.bsa_mask_from_scores(*args, None, ctypes.byref(pw), 0, F(0), F(0), fake, fake, big,
+                                    fake, P(0x1000), ws, None) == -1
+    assert b"axis_order" in lib.bsa_last_error()
+    # capacity: top-p needs G*Nq*Nkv; a short workspace
+    assert lib.bsa_mask_from_scores(*args, fake, ctypes.byref(p), 1, F(0.5), F(1), fake, fake,
+                                    2 * 10 * 10 - 1, fake, P(0x1000), ws, None) == -3
+    assert lib.bsa_mask_from_scores(*args, fake, ctypes.byref(p), 0, F(0), F(0), fake, fake, big,
+                                    fake, P(0x1000), ws - 1, None) == -3
+    # block scores: bad d, short workspace
+    assert lib.bsa_block_scores(fake, fake, 2, 2, 8, 40, 96, ctypes.byref(p), fake, P(0x1000), big,
+                                None) == -2
+    assert lib.bsa_block_scores(fake, fake, 2, 2, 8, 40, 64, ctypes.byref(p), fake, P(0x1000), 16,
+                                None) == -3
