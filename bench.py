@@ -180,7 +180,31 @@ def long_clip(args, timed_steps):
     nq, nk = -(-N // p.Bq), -(-N // p.Bk)
     fl = kept_flops(rp, ci, G, N, p.Bq, p.Bk, d)
     dense = 4.0 * N * N * d * G
-    log(f"[bench] long clip: {wall * 1e3:.3f} ms/step; segments (ms) {seg}")
+    # the same rebuild with Top-P in place of Top-K: block scores from the
+    # fused sums, then the per-row sorted Top-P cut (80 % of the softmax of
+    # the COSINE scores at inverse temperature 16, log2 units; about the
+    # Top-K density here) + forced blocks
+    nq, nk = -(-N // p.Bq), -(-N // p.Bk)
+    sc = torch.empty((G, nq, nk), dtype=torch.float32, device="cuda")
+    ws_sc = torch.empty(bsa.mask_workspace(G, F, H, W, d, p), dtype=torch.uint8, device="cuda")
+    ws_sel = torch.empty(bsa.scores_select_workspace(G, F, H, W, p.Bq, p.Bk), dtype=torch.uint8,
+                         device="cuda")
+
+    def topp_mask():
+        bsa.block_scores(plan.sums_q, plan.sums_k, F, H, W, p, out=sc, workspace=ws_sc)
+        return bsa.mask_from_scores(sc, od, F, H, W, p, top_p=0.8, temp=16.0, workspace=ws_sel)
+
+    topp_mask()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        _, _, tnnz = topp_mask()
+    e1.record()
+    torch.cuda.synchronize()
+    t_topp = e0.elapsed_time(e1) / steps
+    topp_density = int(tnnz.item()) / (G * nq * nk)
+    log(f"[bench] long clip: {wall * 1e3:.3f} ms/step; segments (ms) {seg}; top-p mask {t_topp:.3f} ms")
     return {
         "workload": "long clip: F=33,H=45,W=80 (118800 tokens), 24 heads, d=128, 128x128 blocks, "
                     "COSINE top-k 15% + diagonal + temporal window (T=2, r0=4), mask rebuilt per step",
@@ -197,6 +221,9 @@ def long_clip(args, timed_steps):
         },
         "attention_kept_tflops": fl / (seg[2] / 1e3) / 1e12,
         "attention_frac_bf16_peak": fl / (seg[2] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "topp_mask_ms": t_topp,
+        "topp_mask_density": topp_density,
+        "topp_mask_policy": "top_p 0.8 of softmax(COSINE score * 16, base 2) + diagonal + window",
     }
 
 

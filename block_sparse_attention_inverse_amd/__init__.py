@@ -40,6 +40,7 @@ from .api import (  # noqa: F401
     permute,
     permute_pool,
     quantize_int8,
+    scores_select_workspace,
     select_orders,
 )
 from ._lib import BsaError, MaskParams  # noqa: F401

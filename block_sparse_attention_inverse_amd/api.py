@@ -208,6 +208,13 @@ def block_scores(sums_q, sums_k, F, H, W, params: MaskParams, out=None, workspac
     return out
 
 
+def scores_select_workspace(G, F, H, W, Bq, Bk) -> int:
+    v = int(_lib.load().bsa_scores_select_workspace(G, F, H, W, Bq, Bk))
+    if v < 0:
+        raise ValueError("bsa_scores_select_workspace: unsupported sizes")
+    return v
+
+
 def mask_from_scores(scores, axis_order, F, H, W, params: MaskParams, top_p=None, temp=1.0,
                      noise=None, noise_scale=1.0, workspace=None):
     """bsa_mask_from_scores: Top-K (top_p None: the budget of ``params``) or
@@ -227,9 +234,7 @@ def mask_from_scores(scores, axis_order, F, H, W, params: MaskParams, top_p=None
     _dev(scores, axis_order, *(t for t in (noise,) if t is not None))
     mode = 0 if top_p is None else 1
     cap = mask_capacity(G, F, H, W, params) if mode == 0 else G * nq * nk
-    ws_bytes = int(_lib.load().bsa_scores_select_workspace(G, F, H, W, params.Bq, params.Bk))
-    if ws_bytes < 0:
-        raise ValueError("bsa_scores_select_workspace: unsupported sizes")
+    ws_bytes = scores_select_workspace(G, F, H, W, params.Bq, params.Bk)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
     row_ptr = torch.empty(G * nq + 1, dtype=torch.int32, device=scores.device)
