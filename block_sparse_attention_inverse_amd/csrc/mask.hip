@@ -325,34 +325,52 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 // scores_kernel: the key of every (q-block, kv-block) pair written out, by
 // the same fp32 sequence as select_kernel (fma chain over the channels in
 // order; COSINE: one correctly rounded divide by the product of the norms).
-// One workgroup per q-block row.
+// kSelRows consecutive q-block rows of one head per workgroup, so each kv
+// summary is read once for all of them.
 template <int D>
 __global__ __launch_bounds__(kSelThreads) void scores_kernel(
     const float* __restrict__ sum_q, const float* __restrict__ sum_k,
     const float* __restrict__ norm_q, const float* __restrict__ norm_k, int nq, int nk, int score,
     float* __restrict__ out) {
-  __shared__ float a[D];
-  const int row = blockIdx.x, g = row / nq, t = threadIdx.x;
-  for (int c = t; c < D; c += kSelThreads) a[c] = sum_q[static_cast<int64_t>(row) * D + c];
+  __shared__ float a[kSelRows][D];
+  const int gpr = (nq + kSelRows - 1) / kSelRows;
+  const int g = blockIdx.x / gpr, i0 = (blockIdx.x % gpr) * kSelRows;
+  const int nr = min(kSelRows, nq - i0);
+  const int t = threadIdx.x;
+  for (int e = t; e < kSelRows * D; e += kSelThreads) {
+    const int r = e / D, c = e % D;
+    a[r][c] = r < nr ? sum_q[(static_cast<int64_t>(g) * nq + i0 + r) * D + c] : 0.0f;
+  }
   __syncthreads();
-  const float nqv = score == 1 ? norm_q[row] : 0.0f;
   for (int j = t; j < nk; j += kSelThreads) {
     const float4* bj = reinterpret_cast<const float4*>(sum_k + (static_cast<int64_t>(g) * nk + j) * D);
-    float acc = 0.0f;
+    float acc[kSelRows];
+#pragma unroll
+    for (int r = 0; r < kSelRows; r++) acc[r] = 0.0f;
 #pragma unroll 4
     for (int c4 = 0; c4 < D / 4; c4++) {
       const float4 v = bj[c4];
-      acc = __builtin_fmaf(a[4 * c4 + 0], v.x, acc);
-      acc = __builtin_fmaf(a[4 * c4 + 1], v.y, acc);
-      acc = __builtin_fmaf(a[4 * c4 + 2], v.z, acc);
-      acc = __builtin_fmaf(a[4 * c4 + 3], v.w, acc);
+#pragma unroll
+      for (int r = 0; r < kSelRows; r++) {
+        acc[r] = __builtin_fmaf(a[r][4 * c4 + 0], v.x, acc[r]);
+        acc[r] = __builtin_fmaf(a[r][4 * c4 + 1], v.y, acc[r]);
+        acc[r] = __builtin_fmaf(a[r][4 * c4 + 2], v.z, acc[r]);
+        acc[r] = __builtin_fmaf(a[r][4 * c4 + 3], v.w, acc[r]);
+      }
     }
-    float key = acc;
-    if (score == 1) {
-      const float den = nqv * norm_k[static_cast<int64_t>(g) * nk + j];
-      key = (den == 0.0f) ? 0.0f : div_rn(acc, den);
+    const float nkj = score == 1 ? norm_k[static_cast<int64_t>(g) * nk + j] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < kSelRows; r++) {
+      if (r < nr) {
+        const int64_t row = static_cast<int64_t>(g) * nq + i0 + r;
+        float key = acc[r];
+        if (score == 1) {
+          const float den = norm_q[row] * nkj;
+          key = (den == 0.0f) ? 0.0f : div_rn(acc[r], den);
+        }
+        out[row * nk + j] = key;
+      }
     }
-    out[static_cast<int64_t>(row) * nk + j] = key;
   }
 }
 
@@ -412,12 +430,33 @@ __global__ __launch_bounds__(kSelThreads) void sorted_select_kernel(
       __syncthreads();
     }
   if constexpr (MODE != SEL_TOPK) {
+    // the weights in parallel, then one lane adds them in sorted order (the
+    // fp32 summation order is part of the result)
+    const float top = key_from_order_bits(~static_cast<uint32_t>(srt[0] >> 32));
+    for (int p = t; p < nk; p += kSelThreads) {
+      const float x = key_from_order_bits(~static_cast<uint32_t>(srt[p] >> 32));
+      pre[p] = MODE == SEL_MASS ? x : exp2f((x - top) * temp);
+    }
+    __syncthreads();
     if (t == 0) {
-      const float top = key_from_order_bits(~static_cast<uint32_t>(srt[0] >> 32));
       float run = 0.0f;
-      for (int p = 0; p < nk; p++) {
-        const float x = key_from_order_bits(~static_cast<uint32_t>(srt[p] >> 32));
-        run += MODE == SEL_MASS ? x : exp2f((x - top) * temp);
+      int p = 0;
+      // pre starts 8*p2 bytes into the buffer: 16-byte aligned when p2 >= 2,
+      // and p2 == 1 (nk == 1) never enters the vector loop
+#pragma unroll 4
+      for (; p + 4 <= nk; p += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(pre + p);
+        run += v.x;
+        pre[p] = run;
+        run += v.y;
+        pre[p + 1] = run;
+        run += v.z;
+        pre[p + 2] = run;
+        run += v.w;
+        pre[p + 3] = run;
+      }
+      for (; p < nk; p++) {
+        run += pre[p];
         pre[p] = run;
       }
     }
@@ -664,7 +703,7 @@ hipError_t launch_block_scores(const MaskGeom& m, const float* sums_q, const flo
   float* norm_k = reinterpret_cast<float*>(ws + L.norm_k);
   const int N = static_cast<int>(m.N);
   const uint32_t total_blocks = static_cast<uint32_t>(static_cast<int64_t>(m.G) * (m.nq + m.nk));
-  const uint32_t rows = static_cast<uint32_t>(m.G) * m.nq;
+  const uint32_t rows = static_cast<uint32_t>(m.G) * ((m.nq + kSelRows - 1) / kSelRows);
   if (m.d == 128) {
     finish_pool_kernel<128><<<total_blocks, 128, 0, s>>>(sums_q, sums_k, m.G, N, m.Bq, m.Bk, m.nq,
                                                          m.nk, m.score, sum_q, sum_k, norm_q, norm_k);
