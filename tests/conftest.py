@@ -10,7 +10,7 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs the HIP kernels)")
-    config.addinivalue_line("markers", "slow: full-size configuration (GPU box only)")
+    config.addinivalue_line("markers", "slow: full-size configuration (needs a GPU)")
 
 
 @pytest.fixture(scope="session")
