@@ -50,6 +50,13 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_127 = 6.988684686772166f;
+// Score bias: the forward's Q.K^T accumulators start at the bit pattern of
+// 1.5 * 2^23.  Every |q8.k8| <= 127^2 * 128 < 2^22, so the int32 result,
+// read as an fp32, is exactly 1.5 * 2^23 + q8.k8: the scores reach the
+// VALU as floats without a conversion, and the offset folds into the
+// exponent's fma.
+constexpr int kSBias = 0x4B400000;
+constexpr float kSBiasF = 12582912.0f;
 constexpr float kRefInit = -1.0e30f;  // running maximum before any score: finite, below all
 // 32-row halves per wave: one, so a 128-row q-block is four waves and two
 // workgroups give every SIMD two waves whose products and softmax interleave
@@ -137,13 +144,13 @@ __device__ __forceinline__ uint32_t v_read_off() {
 }
 
 // S^T = K . Q^T for the wave's two row halves: s[qb][b] covers kv 32b..32b+31
-template <int D, int BK>
+template <int D, int BK, int BIAS = 0>
 __device__ __forceinline__ void qk_i8(const uint8_t* kt, uint32_t kread,
                                       const i32x4 (&qf)[kQB][D / 32], i32x16 (&s)[kQB][BK / 32]) {
 #pragma unroll
   for (int b = 0; b < BK / 32; b++)
 #pragma unroll
-    for (int qb = 0; qb < kQB; qb++) s[qb][b] = i32x16{};
+    for (int qb = 0; qb < kQB; qb++) s[qb][b] = BIAS;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ks++)
 #pragma unroll
@@ -214,7 +221,9 @@ __device__ __forceinline__ void quantize_tile(const i32x16 (&s)[kQB][NB], float 
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++) {
-    const float off = any ? m[qb] + dm - kLog2_127 : 0.0f;
+    // exponent (q8.k8) * f - off, with the score read as biased fp32:
+    // fma(score, f, -(off + bias * f)), one rounding of the folded offset
+    const float off = __builtin_fmaf(kSBiasF, f, any ? m[qb] + dm - kLog2_127 : 0.0f);
     float ys = 0.0f;
 #pragma unroll
     for (int b = 0; b < NB; b++)
@@ -224,7 +233,7 @@ __device__ __forceinline__ void quantize_tile(const i32x16 (&s)[kQB][NB], float 
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int r = 4 * q4 + e;
-          float y = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[qb][b][r]), f, -off));
+          float y = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[qb][b][r]), f, -off));
           if constexpr (MASK) {
             const int kv = kv0 + 32 * b + acc_row(r, h);
             if (!any || !jvalid || kv >= N) y = 0.0f;
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
 
       // ---- scores and the exact running maximum of every row
       i32x16 s[kQB][NB];
-      qk_i8<D, BK>(kbuf[t % 3], kread, qf, s);
+      qk_i8<D, BK, kSBias>(kbuf[t % 3], kread, qf, s);
       float x_max[kQB];
       if (!masked) {
 #pragma unroll
@@ -321,7 +330,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
           const auto sw = __builtin_amdgcn_permlane32_swap(im, im, false, false);
           im = static_cast<int>(sw[0]) > static_cast<int>(sw[1]) ? static_cast<int>(sw[0])
                                                                  : static_cast<int>(sw[1]);
-          x_max[qb] = static_cast<float>(im) * f;
+          x_max[qb] = static_cast<float>(im - kSBias) * f;
         }
       } else {
 #pragma unroll
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
 #pragma unroll
             for (int r = 0; r < 16; r++) {
               const int kv = kv0 + 32 * b + acc_row(r, h);
-              if (jvalid && kv < N) xm = fmaxf(xm, static_cast<float>(s[qb][b][r]) * f);
+              if (jvalid && kv < N) xm = fmaxf(xm, static_cast<float>(s[qb][b][r] - kSBias) * f);
             }
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(xm), __float_as_uint(xm),
                                                            false, false);
