@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 }
 
 // ---- order metric: one workgroup per head
-constexpr int kMetThreads = 256;
+constexpr int kMetThreads = 1024;
 
 __global__ __launch_bounds__(kMetThreads) void paro_metric_kernel(
     const int32_t* __restrict__ cnt, const float* __restrict__ bsum, const float* __restrict__ bmax,
@@ -275,13 +275,16 @@ __global__ __launch_bounds__(kMetThreads) void paro_metric_kernel(
   const int64_t base = static_cast<int64_t>(g) * nblk;
   int nsp = 0;
   float isum = 0.0f;
-  for (int64_t e = t; e < nblk; e += kMetThreads) {
-    const int i = static_cast<int>(e / nb), j = static_cast<int>(e % nb);
-    const int li = min(B, N - i * B), lj = min(B, N - j * B);
-    const int64_t area = static_cast<int64_t>(li) * lj;
-    nsp += static_cast<int64_t>(cnt[base + e]) * sigma_den >= static_cast<int64_t>(sigma_num) * area;
-    const float s = bsum[base + e];
-    isum += s > 0.0f ? bmax[base + e] * static_cast<float>(area) / s : 1.0f;
+  for (int i = 0; i < nb; i++) {
+    const int li = min(B, N - i * B);
+    const int64_t rb = base + static_cast<int64_t>(i) * nb;
+    for (int j = t; j < nb; j += kMetThreads) {
+      const int lj = min(B, N - j * B);
+      const int64_t area = static_cast<int64_t>(li) * lj;
+      nsp += static_cast<int64_t>(cnt[rb + j]) * sigma_den >= static_cast<int64_t>(sigma_num) * area;
+      const float s = bsum[rb + j];
+      isum += s > 0.0f ? bmax[rb + j] * static_cast<float>(area) / s : 1.0f;
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
