@@ -71,7 +71,7 @@ constexpr float kSumBound = 0x1p96f;    // half-tile row sum that flags overflow
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 #ifndef BSA_PF
-#define BSA_PF 2
+#define BSA_PF 4
 #endif
 constexpr int kPf = BSA_PF;             // LDS operand prefetch distance (operands)
 #ifndef BSA_QSCALE
