@@ -4,7 +4,7 @@ Public surface (Python names mirror the C ABI in include/bsa.h):
 ``permute``, ``mask_capacity``, ``mask_workspace``, ``build_mask``,
 ``permute_pool``, ``build_mask_pooled``, ``order_workspace``,
 ``order_scores``, ``select_orders``, ``quantize_int8``, ``forward``,
-``forward_int8``, ``debug_int8_qk``, ``debug_int8_pv``, the offline calibration
+``forward_int8``, ``forward_natural``, ``forward_int8_natural``, ``debug_int8_qk``, ``debug_int8_pv``, the offline calibration
 ``attn_block_stats``, ``paro_metric``, ``paro_select`` (chained by
 ``paro_calibrate``), the static masks ``mask_from_block_sums`` and
 ``mask_from_bits``, the Top-K / Top-P / noise-perturbed selection
@@ -24,6 +24,8 @@ from .api import (  # noqa: F401
     debug_int8_qk,
     forward,
     forward_int8,
+    forward_int8_natural,
+    forward_natural,
     last_error,
     layer_forward,
     mask_capacity,

@@ -57,6 +57,10 @@ SIGNATURES = {
     "bsa_mask_from_block_sums": (_I, [_P, _I, _I, _I, _I, _F, _I, _P, _P, _L, _P, _P, _L, _P]),
     "bsa_mask_bits_workspace": (_L, [_I]),
     "bsa_mask_from_bits": (_I, [_P, _I, _I, _P, _P, _L, _P, _P, _L, _P]),
+    "bsa_forward_natural": (_I, [_P, _P, _P, _P, _P, _L, _I, _P, _I, _I, _I, _P, _L, _L, _P, _I, _I,
+                                 _I, _I, _F, _P]),
+    "bsa_forward_int8_natural": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _L, _I, _P, _I, _I, _I, _P, _L,
+                                      _L, _P, _I, _I, _I, _I, _F, _P]),
     "bsa_block_scores": (_I, [_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MaskParams), _P, _P, _L,
                               _P]),
     "bsa_scores_select_workspace": (_L, [_I, _I, _I, _I, _I, _I]),

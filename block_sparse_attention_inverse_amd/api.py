@@ -467,6 +467,55 @@ def forward_int8(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, Bq, Bk, mask_G=None, 
     return out, lse
 
 
+def _natural_out(out, G, N, d, dev):
+    if out is None:
+        out = torch.empty((N, G, d), dtype=torch.bfloat16, device=dev)
+    if out.dim() != 3 or out.shape != (N, G, d) or out.stride(2) != 1 or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bf16 [N][G][d] (any strides with unit channel stride)")
+    return out
+
+
+def forward_natural(Qp, Kp, Vp, row_ptr, col_idx, Bq, Bk, axis_order, F, H, W, mask_G=None,
+                    sm_scale=0.0, out=None, lse=None, want_lse=True, col_len=None):
+    """bsa_forward_natural: bsa_forward with the inverse reorder fused into
+    its epilogue.  Returns (O bf16 natural [N][G][d] (``out`` may be a
+    strided view), lse fp32 [G][N] by natural token or None)."""
+    _dev(Qp, Kp, Vp, row_ptr, col_idx, axis_order)
+    G, N, d = Qp.shape
+    if N != F * H * W:
+        raise ValueError("N must equal F*H*W")
+    out = _natural_out(out, G, N, d, Qp.device)
+    if lse is None and want_lse:
+        lse = torch.empty((G, N), dtype=torch.float32, device=Qp.device)
+    rc = _lib.load().bsa_forward_natural(_ptr(Qp), _ptr(Kp), _ptr(Vp), _ptr(row_ptr), _ptr(col_idx),
+                                         col_idx.numel() if col_len is None else col_len,
+                                         G if mask_G is None else mask_G, _ptr(axis_order), F, H, W,
+                                         _ptr(out), out.stride(1), out.stride(0), _ptr(lse), G, d, Bq,
+                                         Bk, float(sm_scale), _stream())
+    check(rc)
+    return out, lse
+
+
+def forward_int8_natural(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, Bq, Bk, axis_order, F, H, W,
+                         mask_G=None, sm_scale=0.0, out=None, lse=None, want_lse=True,
+                         col_len=None):
+    """bsa_forward_int8_natural: bsa_forward_int8 writing O in natural order."""
+    _dev(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, axis_order)
+    G, N, d = Qq.shape
+    if N != F * H * W:
+        raise ValueError("N must equal F*H*W")
+    out = _natural_out(out, G, N, d, Qq.device)
+    if lse is None and want_lse:
+        lse = torch.empty((G, N), dtype=torch.float32, device=Qq.device)
+    rc = _lib.load().bsa_forward_int8_natural(
+        _ptr(Qq), _ptr(sQ), _ptr(Kq), _ptr(sK), _ptr(Vq), _ptr(sV), _ptr(row_ptr), _ptr(col_idx),
+        col_idx.numel() if col_len is None else col_len, G if mask_G is None else mask_G,
+        _ptr(axis_order), F, H, W, _ptr(out), out.stride(1), out.stride(0), _ptr(lse), G, d, Bq, Bk,
+        float(sm_scale), _stream())
+    check(rc)
+    return out, lse
+
+
 def debug_int8_qk(Qq, Kq, gij, Bq, Bk):
     """bsa_debug_int8_qk: exact int32 Q.K^T tiles for gij int32 [n][3] of (g, i, j)."""
     _dev(Qq, Kq, gij)
@@ -573,8 +622,9 @@ def layer_forward(plan: LayerPlan, Q, K, V, axis_order):
     """One pass of the whole path on natural-order Q, K, V [N][G][d]:
     reorder (x3) -> [build mask] -> [quantize (x3)] -> block-sparse attention
     -> inverse reorder.  With ``plan.fused`` the reorder, the block pooling
-    and the INT8 quantisation share one pass per tensor.  Returns the
-    natural-order output [N][G][d] (bf16)."""
+    and the INT8 quantisation share one pass per tensor, and the inverse
+    reorder is the attention's own epilogue (``plan.lse`` is then indexed by
+    natural token).  Returns the natural-order output [N][G][d] (bf16)."""
     F, H, W = plan.F, plan.H, plan.W
     p = plan.params
     if plan.fused:
@@ -589,6 +639,15 @@ def layer_forward(plan: LayerPlan, Q, K, V, axis_order):
             plan.build_mask(axis_order)
         if plan.int8:
             plan.quantize()
+    if plan.fused:
+        if plan.int8:
+            forward_int8_natural(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq, plan.sV, plan.row_ptr,
+                                 plan.col_idx, p.Bq, p.Bk, axis_order, F, H, W, out=plan.O,
+                                 lse=plan.lse)
+        else:
+            forward_natural(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk,
+                            axis_order, F, H, W, out=plan.O, lse=plan.lse)
+        return plan.O
     if plan.int8:
         forward_int8(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq, plan.sV, plan.row_ptr,
                      plan.col_idx, p.Bq, p.Bk, out=plan.Op, lse=plan.lse)

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
     const float* __restrict__ sK, const int8_t* __restrict__ V, const float* __restrict__ sV,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
     int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
-    float scale_log2) {
+    float scale_log2, OutMap om) {
   constexpr int NW = BQ / kRowsPerWave;
   constexpr int NB = BK / 32;
   using L = L8<D, BK, NW>;
@@ -413,7 +413,8 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
     const int row = qbase + 32 * qb + l32;
     if (row < N) {
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      uint16_t* op = O + (static_cast<int64_t>(g) * N + row) * D;
+      int64_t li;
+      uint16_t* op = out_row<D>(O, om.orders, om.F, om.H, om.W, om.sg, om.sn, g, N, row, li);
 #pragma unroll
       for (int db = 0; db < D / 32; db++)
 #pragma unroll
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
           *reinterpret_cast<uint2*>(op + d0) = pk;
         }
       if (lse != nullptr && h == 0)
-        lse[static_cast<int64_t>(g) * N + row] = lt > 0.0f ? m[qb] * kLn2 + logf(lt) : -INFINITY;
+        lse[li] = lt > 0.0f ? m[qb] * kLn2 + logf(lt) : -INFINITY;
     }
   }
 }
@@ -557,7 +558,7 @@ struct LaunchI8 {
     fwd_i8_kernel<D, BQ, BK><<<nwg, BQ / kRowsPerWave * kWave, 0, s>>>(
         static_cast<const int8_t*>(a.Q), a.sQ, static_cast<const int8_t*>(a.K), a.sK,
         static_cast<const int8_t*>(a.V), a.sV, a.row_ptr, a.col_idx, a.col_len, a.mask_G, a.O,
-        a.lse, a.N, nq, nk, scale_log2_of(a));
+        a.lse, a.N, nq, nk, scale_log2_of(a), a.out);
     return hipGetLastError();
   }
 };

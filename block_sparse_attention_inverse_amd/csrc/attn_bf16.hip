@@ -453,7 +453,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
     int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
-    float c) {
+    float c, OutMap om) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int NW = BQ / 64;
   constexpr int SUB = BK / KT;
@@ -675,7 +675,8 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
     const int row = qbase + 32 * qb + l32;
     if (row < N) {
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      uint16_t* op = O + (static_cast<int64_t>(g) * N + row) * D;
+      int64_t li;
+      uint16_t* op = out_row<D>(O, om.orders, om.F, om.H, om.W, om.sg, om.sn, g, N, row, li);
 #pragma unroll
       for (int db = 0; db < D / 32; db++)
 #pragma unroll
@@ -689,7 +690,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
           *reinterpret_cast<uint2*>(op + d0) = pk;
         }
       if (lse != nullptr && h == 0)
-        lse[static_cast<int64_t>(g) * N + row] = lt > 0.0f ? (BSA_QSCALE ? m[qb] : m[qb] * c) * kLn2 + logf(lt) : -INFINITY;
+        lse[li] = lt > 0.0f ? (BSA_QSCALE ? m[qb] : m[qb] * c) * kLn2 + logf(lt) : -INFINITY;
     }
   }
 }
@@ -702,7 +703,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
   auto kern = a.N >= KT ? fwd_bf16_kernel<D, BQ, BK, false> : fwd_bf16_kernel<D, BQ, BK, true>;
   kern<<<nwg, BQ, 0, s>>>(static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                           static_cast<const uint16_t*>(a.V), a.row_ptr, a.col_idx, a.col_len,
-                          a.mask_G, a.O, a.lse, a.N, nq, nk, sm * kLog2e);
+                          a.mask_G, a.O, a.lse, a.N, nq, nk, sm * kLog2e, a.out);
   return hipGetLastError();
 }
 

@@ -72,6 +72,23 @@ __device__ __forceinline__ bool head_sync_tile(uint32_t bid, int nq, int& g, int
   return i < nq;
 }
 
+// Output row of reordered position r of head g under an OutMap-like
+// description: reordered [G][N][D] when orders is null, else the natural
+// token n = perm_g(r) at n*sn + g*sg; lse_idx receives the matching
+// [G][N] index (g*N + r, or g*N + n).
+template <int D>
+__device__ __forceinline__ uint16_t* out_row(uint16_t* O, const uint8_t* orders, int F, int H, int W,
+                                             int64_t sg, int64_t sn, int g, int N, int r,
+                                             int64_t& lse_idx) {
+  if (orders == nullptr) {
+    lse_idx = static_cast<int64_t>(g) * N + r;
+    return O + lse_idx * D;
+  }
+  const uint32_t n = natural_index(orders[g], static_cast<uint32_t>(r), F, H, W);
+  lse_idx = static_cast<int64_t>(g) * N + n;
+  return O + static_cast<int64_t>(n) * sn + static_cast<int64_t>(g) * sg;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll

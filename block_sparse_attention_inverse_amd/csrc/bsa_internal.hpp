@@ -88,6 +88,15 @@ hipError_t launch_quantize_int8(const uint16_t* X, int8_t* Xq, float* scale, int
                                 int B, hipStream_t s);
 
 // ---- attn.hip --------------------------------------------------------------
+// Where a forward writes O (and lse): orders == nullptr -> reordered
+// [G][N][d] (lse [G][N]); else the natural token order, row (n, g) at
+// n*sn + g*sg elements (lse[g*N + n]), n = the natural index of reordered
+// position r under orders[g] on an F x H x W grid.
+struct OutMap {
+  const uint8_t* orders;
+  int F, H, W;
+  int64_t sg, sn;
+};
 struct AttnArgs {
   const void* Q;  // bf16 or int8 [G][N][d]
   const void* K;
@@ -103,6 +112,7 @@ struct AttnArgs {
   float* lse;   // [G][N] or nullptr
   int G, N, d, Bq, Bk;
   float sm_scale;
+  OutMap out;   // out.orders == nullptr: reordered output
 };
 hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_forward_int8(const AttnArgs& a, hipStream_t s);

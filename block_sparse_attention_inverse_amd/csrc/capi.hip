@@ -83,6 +83,27 @@ int64_t capacity_of(const bsa::MaskGeom& m) {
   return per * m.G * static_cast<int64_t>(m.nq);
 }
 
+// Validation of a natural-order output (the inverse reorder fused into the
+// forward's epilogue); fills the output map.
+int natural_out(const uint8_t* axis_order, int32_t F, int32_t H, int32_t W, int32_t G, int32_t d,
+                int64_t sg, int64_t sn, bsa::OutMap& om, int32_t& N) {
+  if (!axis_order) return fail(BSA_EINVAL, "axis_order is NULL");
+  if (F <= 0 || H <= 0 || W <= 0) return fail(BSA_EINVAL, "F, H, W must be positive");
+  const int64_t n64 = static_cast<int64_t>(F) * H * W;
+  if (n64 >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "N = F*H*W must be < 2^31");
+  if (sg < 0 || sn < 0 || sg % 8 || sn % 8)
+    return fail(BSA_EINVAL, "natural strides must be non-negative multiples of 8");
+  // rows (n, g) of d elements must not overlap: [N][G][d]-like or [G][N][d]-like strides
+  const bool ng = sg >= d && sn >= static_cast<int64_t>(G) * sg;
+  const bool gn = sn >= d && sg >= n64 * sn;
+  if (!ng && !gn) return fail(BSA_EINVAL, "natural strides make output rows overlap");
+  om.orders = axis_order;
+  om.F = F; om.H = H; om.W = W;
+  om.sg = sg; om.sn = sn;
+  N = static_cast<int32_t>(n64);
+  return BSA_OK;
+}
+
 int attn_common(const void* Q, const void* K, const void* V, const int32_t* row_ptr,
                 const int32_t* col_idx, int64_t col_len, int32_t mask_G, void* Op, int32_t G,
                 int32_t N, int32_t d, int32_t Bq, int32_t Bk) {
@@ -536,6 +557,50 @@ int bsa_mask_from_scores(const float* scores, const float* noise, float noise_sc
                                                 m.win_r0, row_ptr, col_idx, col_capacity, nnz,
                                                 workspace, as_stream(stream)),
                       "bsa_mask_from_scores");
+  });
+}
+
+int bsa_forward_natural(const void* Qp, const void* Kp, const void* Vp, const int32_t* row_ptr,
+                        const int32_t* col_idx, int64_t col_len, int32_t mask_G,
+                        const uint8_t* axis_order, int32_t F, int32_t H, int32_t W, void* O,
+                        int64_t nat_stride_g, int64_t nat_stride_n, float* lse, int32_t G, int32_t d,
+                        int32_t Bq, int32_t Bk, float sm_scale, void* stream) {
+  return guarded([&]() -> int {
+    bsa::AttnArgs a{};
+    int32_t N = 0;
+    int rc = natural_out(axis_order, F, H, W, G, d, nat_stride_g, nat_stride_n, a.out, N);
+    if (rc != BSA_OK) return rc;
+    rc = attn_common(Qp, Kp, Vp, row_ptr, col_idx, col_len, mask_G, O, G, N, d, Bq, Bk);
+    if (rc != BSA_OK) return rc;
+    if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");
+    a.Q = Qp; a.K = Kp; a.V = Vp;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.col_len = col_len; a.mask_G = mask_G;
+    a.O = static_cast<uint16_t*>(O); a.lse = lse;
+    a.G = G; a.N = N; a.d = d; a.Bq = Bq; a.Bk = Bk; a.sm_scale = sm_scale;
+    return hip_status(bsa::launch_forward_bf16(a, as_stream(stream)), "bsa_forward_natural");
+  });
+}
+
+int bsa_forward_int8_natural(const int8_t* Qq, const float* sQ, const int8_t* Kq, const float* sK,
+                             const int8_t* Vq, const float* sV, const int32_t* row_ptr,
+                             const int32_t* col_idx, int64_t col_len, int32_t mask_G,
+                             const uint8_t* axis_order, int32_t F, int32_t H, int32_t W, void* O,
+                             int64_t nat_stride_g, int64_t nat_stride_n, float* lse, int32_t G,
+                             int32_t d, int32_t Bq, int32_t Bk, float sm_scale, void* stream) {
+  return guarded([&]() -> int {
+    bsa::AttnArgs a{};
+    int32_t N = 0;
+    int rc = natural_out(axis_order, F, H, W, G, d, nat_stride_g, nat_stride_n, a.out, N);
+    if (rc != BSA_OK) return rc;
+    rc = attn_common(Qq, Kq, Vq, row_ptr, col_idx, col_len, mask_G, O, G, N, d, Bq, Bk);
+    if (rc != BSA_OK) return rc;
+    if (!sQ || !sK || !sV) return fail(BSA_EINVAL, "NULL scale pointer");
+    if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");
+    a.Q = Qq; a.K = Kq; a.V = Vq; a.sQ = sQ; a.sK = sK; a.sV = sV;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.col_len = col_len; a.mask_G = mask_G;
+    a.O = static_cast<uint16_t*>(O); a.lse = lse;
+    a.G = G; a.N = N; a.d = d; a.Bq = Bq; a.Bk = Bk; a.sm_scale = sm_scale;
+    return hip_status(bsa::launch_forward_int8(a, as_stream(stream)), "bsa_forward_int8_natural");
   });
 }
 

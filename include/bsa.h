@@ -256,6 +256,34 @@ int bsa_forward_int8(const int8_t *Qq, const float *sQ, const int8_t *Kq, const 
                      int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk, float sm_scale,
                      void *stream);
 
+/* bsa_forward_natural — bsa_forward with the inverse reorder fused into its
+ * epilogue (PAROAttention verdict, key machinery: the permutation is fused
+ * into the neighbouring kernels so that it costs almost nothing): every
+ * output row is written straight to its natural token position.  Inputs
+ * and the mask as bsa_forward, with N = F*H*W; the output row of head g
+ * and reordered position r goes to natural token n = perm_g(r) (axis_order
+ * device uint8[G], as bsa_permute), at O + n*nat_stride_n + g*nat_stride_g
+ * (elements; e.g. [N][G][d]: nat_stride_g = d, nat_stride_n = G*d).  lse
+ * (nullable) is fp32 [G][N] indexed by natural token.  The result equals
+ * bsa_forward followed by bsa_permute(direction 1) bit for bit.  O 16-byte
+ * aligned, strides non-negative multiples of 8 that keep rows disjoint.
+ * Errors: EINVAL, EUNSUPPORTED, EHIP. */
+int bsa_forward_natural(const void *Qp, const void *Kp, const void *Vp, const int32_t *row_ptr,
+                        const int32_t *col_idx, int64_t col_len, int32_t mask_G,
+                        const uint8_t *axis_order, int32_t F, int32_t H, int32_t W, void *O,
+                        int64_t nat_stride_g, int64_t nat_stride_n, float *lse, int32_t G, int32_t d,
+                        int32_t Bq, int32_t Bk, float sm_scale, void *stream);
+
+/* bsa_forward_int8_natural — bsa_forward_int8 with the output written in
+ * natural token order, exactly as bsa_forward_natural does for bsa_forward.
+ * Errors: EINVAL, EUNSUPPORTED, EHIP. */
+int bsa_forward_int8_natural(const int8_t *Qq, const float *sQ, const int8_t *Kq, const float *sK,
+                             const int8_t *Vq, const float *sV, const int32_t *row_ptr,
+                             const int32_t *col_idx, int64_t col_len, int32_t mask_G,
+                             const uint8_t *axis_order, int32_t F, int32_t H, int32_t W, void *O,
+                             int64_t nat_stride_g, int64_t nat_stride_n, float *lse, int32_t G,
+                             int32_t d, int32_t Bq, int32_t Bk, float sm_scale, void *stream);
+
 /* bsa_debug_int8_qk — runs bsa_forward_int8's own Q.K^T tile routine on n
  * chosen tiles and writes the exact int32 products.  gij: device
  * int32[n][3] of (g, i, j); S: int32[n][Bq][Bk], S[t][r][c] =

@@ -39,7 +39,8 @@ def test_header_lists_the_entry_points():
               "bsa_order_scores", "bsa_select_orders", "bsa_attn_block_stats",
               "bsa_paro_metric", "bsa_paro_select", "bsa_mask_sums_workspace",
               "bsa_mask_from_block_sums", "bsa_mask_bits_workspace", "bsa_mask_from_bits",
-              "bsa_block_scores", "bsa_scores_select_workspace", "bsa_mask_from_scores"):
+              "bsa_block_scores", "bsa_scores_select_workspace", "bsa_mask_from_scores",
+              "bsa_forward_natural", "bsa_forward_int8_natural"):
         assert n in names
 
 
@@ -221,3 +222,25 @@ def test_scores_selection_argument_errors(lib):
                                 None) == -2
     assert lib.bsa_block_scores(fake, fake, 2, 2, 8, 40, 64, ctypes.byref(p), fake, P(0x1000), 16,
                                 None) == -3
+
+
+def test_forward_natural_argument_errors(lib):
+    """Host checks of the forwards that write natural order; none reaches HIP."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    F = ctypes.c_float
+    G, d = 4, 128
+    Fr, Hr, Wr = 2, 8, 40
+    N = Fr * Hr * Wr
+    ok = (d, G * d)  # [N][G][d]
+    def call(orders=fake, grid=(Fr, Hr, Wr), strides=ok):
+        return lib.bsa_forward_natural(fake, fake, fake, fake, fake, 100, G, orders, *grid, fake,
+                                       strides[0], strides[1], None, G, d, 128, 64, F(0), None)
+    assert call(orders=None) == -1
+    assert call(grid=(0, Hr, Wr)) == -1
+    assert call(strides=(d, d)) == -1            # rows of different heads overlap
+    assert b"overlap" in lib.bsa_last_error()
+    assert call(strides=(d + 4, G * (d + 4))) == -1  # not a multiple of 8
+    assert lib.bsa_forward_int8_natural(fake, fake, fake, fake, fake, fake, fake, fake, 100, G, None,
+                                        Fr, Hr, Wr, fake, d, G * d, None, G, d, 128, 64, F(0),
+                                        None) == -1

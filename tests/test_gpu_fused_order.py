@@ -169,3 +169,45 @@ def test_order_scores_small_and_ragged(bsa_gpu, orc, d, B, N3):
         host = _bits(x) if dt == torch.bfloat16 else X
         want = orc.sics_scores(host, G, F, H, W, d, B)
         assert np.array_equal(_np(s).view(np.uint32), want.view(np.uint32)), (dt, N3)
+
+
+# ------------------------------------------- inverse reorder in the epilogue
+@pytest.mark.parametrize("cid,int8,layout", [(2, False, "NGd"), (2, True, "NGd"), (3, False, "GNd"),
+                                             (3, True, "NGd"), (5, False, "NGd")])
+def test_forward_natural_equals_forward_then_scatter(bsa_gpu, orc, cid, int8, layout):
+    """The forward with the inverse reorder fused into its epilogue gives,
+    bit for bit, the reordered forward followed by bsa_permute(direction 1),
+    for natural [N][G][d] and strided [G][N][d] outputs; lse lands at the
+    natural token index."""
+    c = case(cid)
+    cfg = c["cfg"]
+    G, F, H, W, d = cfg["G"], cfg["F"], cfg["H"], cfg["W"], cfg["d"]
+    N = F * H * W
+    p = mask_params(bsa_gpu, cfg) if cfg["mask"] != "static" else bsa_gpu.mask_params(
+        cfg["Bq"], cfg["Bk"], 0, (30, 100), True)
+    _say(f"[forward natural cfg {cid} int8={int8} {layout}]")
+    plan = bsa_gpu.LayerPlan(G, F, H, W, d, "cuda", p, int8=int8, fused=True)
+    plan.reorder_fused(c["Q"], c["K"], c["V"], c["orders_dev"])
+    plan.build_mask_from_sums(c["orders_dev"])
+    if layout == "NGd":
+        out_nat = torch.empty((N, G, d), dtype=torch.bfloat16, device="cuda")
+    else:
+        out_nat = torch.empty((G, N, d), dtype=torch.bfloat16, device="cuda").transpose(0, 1)
+    if int8:
+        o_r, l_r = bsa_gpu.forward_int8(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq, plan.sV,
+                                        plan.row_ptr, plan.col_idx, p.Bq, p.Bk)
+        o_n, l_n = bsa_gpu.forward_int8_natural(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq,
+                                                plan.sV, plan.row_ptr, plan.col_idx, p.Bq, p.Bk,
+                                                c["orders_dev"], F, H, W, out=out_nat)
+    else:
+        o_r, l_r = bsa_gpu.forward(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk)
+        o_n, l_n = bsa_gpu.forward_natural(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx,
+                                           p.Bq, p.Bk, c["orders_dev"], F, H, W, out=out_nat)
+    want = bsa_gpu.permute(o_r, c["orders_dev"], F, H, W, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(o_n.view(torch.int16), want.view(torch.int16))
+    # lse: reordered position r of head g -> natural token perm_g(r)
+    lr, ln = _np(l_r), _np(l_n)
+    for g in range(G):
+        pm = orc.perm(int(c["orders"][g]), F, H, W)
+        assert np.array_equal(ln[g, pm], lr[g])
