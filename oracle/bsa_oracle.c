@@ -25,6 +25,19 @@
  * sequence for the same reason.  Build with -ffp-contract=off and without
  * -ffast-math: no reassociation, no implicit contraction.
  *
+ * Parity unpinned by the pages (each is pinned against its written
+ * reading by worked examples, closed forms or bounds in the tests, but the
+ * pages themselves do not fix the reading):
+ *   - the INT8 post-softmax quantisation per tile relative to the running
+ *     maximum, with l summing the unquantised values (oracle_attention_int8);
+ *   - the combination M = (1 - r) + alpha * Ibar of the order metric's
+ *     ingredients (oracle_paro_metric);
+ *   - the block-sum threshold as a share of each row's mass
+ *     (oracle_mass_select);
+ *   - Top-P as a softmax of the block scores at a caller temperature
+ *     (oracle_select_topp) and the additive form of the stochastic bias
+ *     (oracle_perturb_keys).
+ *
  * Every pointer is a host pointer.  Functions return 0 on success and a
  * negative value on a bad argument.
  */
