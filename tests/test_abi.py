@@ -244,3 +244,19 @@ def test_forward_natural_argument_errors(lib):
     assert lib.bsa_forward_int8_natural(fake, fake, fake, fake, fake, fake, fake, fake, 100, G, None,
                                         Fr, Hr, Wr, fake, d, G * d, None, G, d, 128, 64, F(0),
                                         None) == -1
+
+
+def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """With libbsa.so absent the binding raises; nothing falls back to a CPU
+    or PyTorch implementation."""
+    from block_sparse_attention_inverse_amd import _lib
+    import block_sparse_attention_inverse_amd as bsa
+
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libbsa.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()
+    with pytest.raises(ImportError):
+        bsa.abi_version()
+    with pytest.raises(ImportError):
+        bsa.mask_capacity(1, 2, 8, 8, bsa.mask_params())
