@@ -416,3 +416,80 @@ def test_forward_first_half_tile_masked(bsa_gpu, orc):
     rp = np.array([0, 2, 3], np.int32)
     ci = np.array([0, 1, 1], np.int32)
     _forward_reordered_case(bsa_gpu, orc, Q, K, V, rp, ci, F, H, W, Bq, Bk, "masked first half")
+
+
+# ------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("N,d", [(40, 64), (40, 128), (1, 128), (63, 64)])
+def test_forward_fewer_tokens_than_a_sub_tile(bsa_gpu, orc, N, d):
+    """N below the 64-row staging window (the clamped-row variant of the
+    kernel): one q-block, one kv-block, every row against the oracle."""
+    r = np.random.Generator(np.random.PCG64(40 + N + d))
+    G = 2
+    Q, K, V = (r.standard_normal((N, G, d)) for _ in range(3))
+    rp = np.array([0, 1, 2], np.int32)
+    ci = np.array([0, 0], np.int32)
+    _forward_reordered_case(bsa_gpu, orc, Q, K, V, rp, ci, 1, 1, N, 64, 64, f"N={N} d={d}")
+
+
+def test_forward_empty_rows_and_out_of_range_entries(bsa_gpu, orc):
+    """Rows with no kept block give O = 0 and lse = -inf; CSR entries outside
+    [0, Nkv) are skipped."""
+    r = np.random.Generator(np.random.PCG64(41))
+    F, H, W, G, d, B = 1, 4, 64, 2, 128, 64
+    N = F * H * W
+    Q, K, V = (r.standard_normal((N, G, d)) for _ in range(3))
+    nq = N // B
+    # head 0: rows 0 and 2 empty; head 1: row 1 keeps an out-of-range entry only
+    rows_sets = [[], [0, 1], [], [3], [0, 2], [99], [1, 3], [-5, 2]]
+    rp = np.cumsum([0] + [len(s) for s in rows_sets]).astype(np.int32)
+    ci = np.array([j for s in rows_sets for j in s], np.int32)
+    od = torch.zeros(G, dtype=torch.uint8).cuda()
+    dev = [torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda() for x in (Q, K, V)]
+    Qp, Kp, Vp = (bsa_gpu.permute(x, od, F, H, W, 0) for x in dev)
+    Op, lse = bsa_gpu.forward(Qp, Kp, Vp, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(),
+                              B, B)
+    torch.cuda.synchronize()
+    o, l = _np(Op.float()), _np(lse)
+    host = [_bits(x) for x in dev]
+    rows = np.array([(g, n) for g in range(G) for n in range(N)], np.int64)
+    Ow, Lw = orc.attention_rows(*host, G, F, H, W, d, np.zeros(G, np.uint8), rows, B, B, rp, ci)
+    got = o[rows[:, 0], rows[:, 1]]
+    empty = ~np.isfinite(Lw)
+    assert empty.sum() == 3 * B  # rows 0 and 2 of head 0, row 1 of head 1
+    assert np.all(got[empty] == 0.0) and np.all(np.isneginf(l[rows[empty, 0], rows[empty, 1]]))
+    _compare(got[~empty], Ow[~empty], tag="non-empty rows")
+
+
+def test_forward_mask_shared_across_heads(bsa_gpu, orc):
+    """mask_G < G: head g reads CSR rows (g % mask_G) * Nq + i (batch copies
+    sharing one mask), for the bf16 and the INT8 forward."""
+    r = np.random.Generator(np.random.PCG64(42))
+    F, H, W, G, d, B, mG = 1, 8, 64, 4, 64, 64, 2
+    N = F * H * W
+    nq = N // B
+    Q, K, V = (r.standard_normal((N, G, d)) for _ in range(3))
+    sets = [sorted(set(r.choice(nq, size=3, replace=False).tolist()) | {i % nq})
+            for i in range(mG * nq)]
+    rp = np.cumsum([0] + [len(s) for s in sets]).astype(np.int32)
+    ci = np.array([j for s in sets for j in s], np.int32)
+    od = torch.zeros(G, dtype=torch.uint8).cuda()
+    dev = [torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda() for x in (Q, K, V)]
+    Qp, Kp, Vp = (bsa_gpu.permute(x, od, F, H, W, 0) for x in dev)
+    grp, gci = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    Op, lse = bsa_gpu.forward(Qp, Kp, Vp, grp, gci, B, B, mask_G=mG)
+    torch.cuda.synchronize()
+    host = [_bits(x) for x in dev]
+    rows = np.array([(g, n) for g in range(G) for n in range(N)], np.int64)
+    Ow, Lw = orc.attention_rows(*host, G, F, H, W, d, np.zeros(G, np.uint8), rows, B, B, rp, ci,
+                                mask_G=mG)
+    _compare(_np(Op.float())[rows[:, 0], rows[:, 1]], Ow, heads=rows[:, 0], tag="shared mask")
+    # INT8: the same sharing against the INT8 emulation
+    (qq, sq), (kq, sk), (vq, sv) = (bsa_gpu.quantize_int8(x, B) for x in (Qp, Kp, Vp))
+    O8, _ = bsa_gpu.forward_int8(qq, sq, kq, sk, vq, sv, grp, gci, B, B, mask_G=mG)
+    torch.cuda.synchronize()
+    blocks = np.array([(g, i) for g in range(G) for i in range(nq)], np.int64)
+    W8, _ = orc.attention_int8(_np(qq), _np(sq), _np(kq), _np(sk), _np(vq), _np(sv), B, B, rp, ci,
+                               blocks, mask_G=mG)
+    o8 = _np(O8.float())
+    got8 = np.concatenate([o8[g, i * B:(i + 1) * B] for g, i in blocks])
+    _compare(got8, W8.reshape(-1, d), tag="shared mask int8")
