@@ -493,3 +493,27 @@ def test_forward_mask_shared_across_heads(bsa_gpu, orc):
     o8 = _np(O8.float())
     got8 = np.concatenate([o8[g, i * B:(i + 1) * B] for g, i in blocks])
     _compare(got8, W8.reshape(-1, d), tag="shared mask int8")
+
+
+@pytest.mark.parametrize("N,d,Bq,Bk", [(40, 64, 64, 64), (1, 128, 128, 64), (100, 128, 128, 128)])
+def test_forward_int8_short_sequences(bsa_gpu, orc, N, d, Bq, Bk):
+    """INT8 forward when the sequence is shorter than a tile (rows and
+    columns past N read as zero and are masked) against the INT8 emulation."""
+    r = np.random.Generator(np.random.PCG64(43 + N))
+    G = 2
+    x = [torch.from_numpy(r.standard_normal((G, N, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+         for _ in range(3)]
+    (qq, sq), (kq, sk), (vq, sv) = (bsa_gpu.quantize_int8(t, B) for t, B in zip(x, (Bq, Bk, Bk)))
+    nq, nk = -(-N // Bq), -(-N // Bk)
+    rp = np.arange(0, G * nq * nk + 1, nk, dtype=np.int32)
+    ci = np.tile(np.arange(nk, dtype=np.int32), G * nq)
+    O8, _ = bsa_gpu.forward_int8(qq, sq, kq, sk, vq, sv, torch.from_numpy(rp).cuda(),
+                                 torch.from_numpy(ci).cuda(), Bq, Bk)
+    torch.cuda.synchronize()
+    blocks = np.array([(g, i) for g in range(G) for i in range(nq)], np.int64)
+    W8, _ = orc.attention_int8(_np(qq), _np(sq), _np(kq), _np(sk), _np(vq), _np(sv), Bq, Bk, rp, ci,
+                               blocks)
+    o8 = _np(O8.float())
+    got = np.concatenate([o8[g, i * Bq:min((i + 1) * Bq, N)] for g, i in blocks])
+    want = np.concatenate([W8[t, :min(Bq, N - i * Bq)] for t, (g, i) in enumerate(blocks)])
+    _compare(got, want, tag=f"int8 N={N}")
