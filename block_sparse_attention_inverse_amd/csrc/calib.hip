@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const bool rv[2] = {r0 + lane % 32 < N, r0 + 32 + lane % 32 < N};
   const bool rows_full = r0 + 64 <= N;
   const int qblk = r0 / B;  // the wave's 64 rows lie in one q-block
-  int ccount = 0;
+  int ccount = 0;  // wave-uniform: each element's test is counted once per wave via a ballot
   float csum = 0.0f, xmax = -INFINITY;  // maximum exponent; the block maximum is exp2(xmax)
   auto stat_sub = [&](int t, const uint8_t* lds, int u) {
     f32x16 acc[2];
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         for (int e = 0; e < 16; e++) {
           const float x = __builtin_fmaf(acc[qb][e], c, -lse2[qb]);
           const float a = __builtin_amdgcn_exp2f(x);
-          ccount += a < eps ? 1 : 0;
+          ccount += __popcll(__ballot(a < eps));
           csum += a;
           xmax = fmaxf(xmax, x);
         }
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
           const bool real = rv[qb] && 32 * t + key_of(e, lane) < N;
           const float x = real ? __builtin_fmaf(acc[qb][e], c, -lse2[qb]) : -INFINITY;
           const float a = __builtin_amdgcn_exp2f(x);
-          ccount += (real && a < eps) ? 1 : 0;
+          ccount += __popcll(__ballot(real && a < eps));
           csum += a;
           xmax = fmaxf(xmax, x);
         }
@@ -215,7 +215,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     float cmax = __builtin_amdgcn_exp2f(xmax);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      ccount += __shfl_xor(ccount, o);
       csum += __shfl_xor(csum, o);
       cmax = fmaxf(cmax, __shfl_xor(cmax, o));
     }
