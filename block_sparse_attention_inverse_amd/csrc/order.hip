@@ -31,74 +31,116 @@
 namespace bsa {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kMaxB = 128;
+constexpr int kThreads = kMaxB;  // one thread per row in the norm phase, per channel in the sum phase
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// one workgroup per (block b, order o, head g): q_b into part[g][o][b]
+// one workgroup per (block b, order o, head g): q_b into part[g][o][b].
+// bf16 rows are staged in LDS as 16-byte chunks, chunk c of row r stored at
+// c ^ (r mod 16) within the row, so that both the row-wise reads of the norm
+// phase and the column-wise reads of the sum phase are free of bank
+// conflicts; fp32 rows are read from global memory in both phases.
 template <bool F32, int D>
 __global__ __launch_bounds__(kThreads) void sics_block_kernel(
     const void* __restrict__ src, int64_t stride_g, int64_t stride_n, uint32_t N, uint32_t F,
     uint32_t H, uint32_t W, int B, int nb, float* __restrict__ part) {
-  __shared__ float tile[kMaxB][D + 1];
+  constexpr int CPR = D / 8;                   // 16-byte chunks per bf16 row
+  constexpr int SW = CPR - 1 < 15 ? CPR - 1 : 15;
+  __shared__ u32x4 xs[F32 ? 1 : kMaxB * CPR];
   __shared__ float inv[kMaxB];
-  __shared__ float u[D];
+  __shared__ __align__(16) float u[D];
+  __shared__ int64_t roff[kMaxB];  // element offset of the block's row r, channel 0
   const int b = blockIdx.x, o = blockIdx.y, g = blockIdx.z;
   const int t = threadIdx.x;
   const int r0 = b * B;
   const int len = min(B, static_cast<int>(N) - r0);
-  // gather the block's rows as fp32 (bf16 widens exactly), 8 channels a load
-  constexpr int CPR = D / 8;
-  for (int e = t; e < len * CPR; e += kThreads) {
-    const int r = e / CPR, c8 = (e % CPR) * 8;
-    const uint32_t n = natural_index(o, static_cast<uint32_t>(r0 + r), F, H, W);
-    const int64_t off = static_cast<int64_t>(n) * stride_n + static_cast<int64_t>(g) * stride_g + c8;
-    float x[8];
-    if constexpr (F32) {
-      const u32x4* sp = reinterpret_cast<const u32x4*>(static_cast<const float*>(src) + off);
-      const u32x4 lo = sp[0], hi = sp[1];
-      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-      for (int q = 0; q < 8; q++) x[q] = __uint_as_float(w[q]);
-    } else {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + off);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        x[2 * q] = bf16_bits_to_f32(w[q] & 0xffffu);
-        x[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 8; q++) tile[r][c8 + q] = x[q];
+  if (t < len) {
+    const uint32_t n = natural_index(o, static_cast<uint32_t>(r0 + t), F, H, W);
+    roff[t] = static_cast<int64_t>(n) * stride_n + static_cast<int64_t>(g) * stride_g;
   }
   __syncthreads();
+  auto row_off = [&](int r) -> int64_t { return roff[r]; };
+  if constexpr (!F32) {
+    const uint16_t* s16 = static_cast<const uint16_t*>(src);
+    for (int e = t; e < len * CPR; e += kThreads) {
+      const int r = e / CPR, ch = e % CPR;
+      xs[r * CPR + (ch ^ (r & SW))] = *reinterpret_cast<const u32x4*>(s16 + row_off(r) + ch * 8);
+    }
+    __syncthreads();
+  }
+  // row norms, channels in order (bf16 widens exactly)
   if (t < len) {
     float nr = 0.0f;
-    for (int c = 0; c < D; c++) nr = __builtin_fmaf(tile[t][c], tile[t][c], nr);
+    if constexpr (F32) {
+      const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const float*>(src) + row_off(t));
+      for (int c4 = 0; c4 < D / 4; c4++) {
+        const u32x4 v = xr[c4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) nr = __builtin_fmaf(__uint_as_float(v[q]), __uint_as_float(v[q]), nr);
+      }
+    } else {
+#pragma unroll 4
+      for (int ch = 0; ch < CPR; ch++) {
+        const u32x4 v = xs[t * CPR + (ch ^ (t & SW))];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const float lo = bf16_bits_to_f32(v[q] & 0xffffu), hi = bf16_bits_to_f32(v[q] >> 16);
+          nr = __builtin_fmaf(lo, lo, nr);
+          nr = __builtin_fmaf(hi, hi, nr);
+        }
+      }
+    }
     inv[t] = nr > 0.0f ? 1.0f / __builtin_sqrtf(nr) : 0.0f;
   }
   __syncthreads();
+  // per-channel sums of the unit rows, rows in order
   if (t < D) {
     float a = 0.0f;
-    for (int r = 0; r < len; r++) a = __builtin_fmaf(tile[r][t], inv[r], a);
+    if constexpr (F32) {
+      const float* s32 = static_cast<const float*>(src);
+      for (int r = 0; r < len; r++) a = __builtin_fmaf(s32[row_off(r) + t], inv[r], a);
+    } else {
+      const uint16_t* xe = reinterpret_cast<const uint16_t*>(xs);
+      const int ch = t / 8, q = t % 8;
+#pragma unroll 8
+      for (int r = 0; r < len; r++)
+        a = __builtin_fmaf(bf16_bits_to_f32(xe[(r * CPR + (ch ^ (r & SW))) * 8 + q]), inv[r], a);
+    }
     u[t] = a;
   }
   __syncthreads();
   if (t == 0) {
     float q = 0.0f;
-    for (int c = 0; c < D; c++) q = __builtin_fmaf(u[c], u[c], q);
+    const float4* u4 = reinterpret_cast<const float4*>(u);
+#pragma unroll 8
+    for (int c4 = 0; c4 < D / 4; c4++) {
+      const float4 v = u4[c4];
+      q = __builtin_fmaf(v.x, v.x, q);
+      q = __builtin_fmaf(v.y, v.y, q);
+      q = __builtin_fmaf(v.z, v.z, q);
+      q = __builtin_fmaf(v.w, v.w, q);
+    }
     part[(static_cast<int64_t>(g) * 6 + o) * nb + b] = q;
   }
 }
 
-// score[g][o] = sum of part[g][o][0..nb) in order: one thread per (g, o)
+// score[g][o] = sum of part[g][o][0..nb) in order: one thread per (g, o);
+// loads are issued sixteen at a time ahead of the sequential adds
 __global__ void sics_sum_kernel(const float* __restrict__ part, int nb, int n,
                                 float* __restrict__ scores) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  const float* p = part + static_cast<int64_t>(i) * nb;
   float s = 0.0f;
-  for (int b = 0; b < nb; b++) s = s + part[static_cast<int64_t>(i) * nb + b];
+  int b = 0;
+  for (; b + 16 <= nb; b += 16) {
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; e++) v[e] = p[b + e];
+#pragma unroll
+    for (int e = 0; e < 16; e++) s = s + v[e];
+  }
+  for (; b < nb; b++) s = s + p[b];
   scores[i] = s;
 }
 
