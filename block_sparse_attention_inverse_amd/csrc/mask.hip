@@ -18,9 +18,10 @@
 // Kernels (all on one stream, no host round trip):
 //   pool_kernel    per (head, block, channel) sequential fp32 sums -> means
 //                  (DOT) or sums + norms (COSINE)              [HBM-bound]
-//   select_kernel  one workgroup per (head, q-block): keys in LDS, exact
-//                  k-th-largest by 4-pass radix select, ties by index,
-//                  union with diagonal / window, 64-bit row bitmask + count
+//   select_kernel  one workgroup per run of q-blocks of a head: keys in LDS,
+//                  then one wave per row: exact k-th-largest by 4-pass radix
+//                  select, ties by index, union with diagonal / window,
+//                  64-bit row bitmask + count
 //   scan_kernel    exclusive scan of the row counts -> row_ptr, nnz
 //   emit_kernel    one wave per row: bitmask -> ascending col_idx
 #pragma clang fp contract(off)
@@ -42,6 +43,15 @@ constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ float div_rn(float x, float y) { return x / y; }  // correctly rounded build
 __device__ __forceinline__ float sqrt_rn(float x) { return __builtin_sqrtf(x); }
+
+// Orders the LDS accesses of a wave's lanes around it (the hardware performs
+// one wave's LDS instructions in issue order; this keeps the compiler from
+// moving accesses across the point).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Ordered-integer image of an fp32 key: larger key <-> larger image, and
 // -0 maps like +0 so that IEEE-equal keys tie.
@@ -171,12 +181,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int nk, int words, int score, int k, int force_diag, int win_T, int win_r0, int rows_per_wg,
     int32_t* __restrict__ counts, unsigned long long* __restrict__ bits) {
   extern __shared__ uint32_t ukeys[];  // [rows_per_wg][nk] ordered key images
-  __shared__ float a[kSelRows][D];
-  __shared__ int hist[256];
-  __shared__ uint32_t s_prefix, s_mask;
-  __shared__ int s_krem;
-  __shared__ int s_wave[kSelWaves];
-  __shared__ int s_count;
+  __shared__ int hist[kSelWaves][256];
 
   // rows_per_wg consecutive q-blocks of one head: each kv-block summary is
   // read once for all of them
@@ -185,13 +190,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int nr = min(rows_per_wg, nq - i0);
   const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
 
-  for (int e = t; e < kSelRows * D; e += kSelThreads) {
-    const int r = e / D, c = e % D;
-    a[r][c] = r < nr ? sum_q[(static_cast<int64_t>(g) * nq + i0 + r) * D + c] : 0.0f;
-  }
-  __syncthreads();
-
-  // keys: for every (row, j) one fp32 fma chain over the channels in order
+  // keys: for every (row, j) one fp32 fma chain over the channels in order.
+  // The q-block summaries are the same for every lane and arrive through
+  // scalar loads (rows past the last q-block repeat it; their keys are not
+  // stored).
+  const float* aq[kSelRows];
+#pragma unroll
+  for (int r = 0; r < kSelRows; r++)
+    aq[r] = sum_q + (static_cast<int64_t>(g) * nq + min(i0 + r, nq - 1)) * D;
   for (int j = t; j < nk; j += kSelThreads) {
     const float4* bj = reinterpret_cast<const float4*>(sum_k + (static_cast<int64_t>(g) * nk + j) * D);
     float acc[kSelRows];
@@ -202,10 +208,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       const float4 v = bj[c4];
 #pragma unroll
       for (int r = 0; r < kSelRows; r++) {
-        acc[r] = __builtin_fmaf(a[r][4 * c4 + 0], v.x, acc[r]);
-        acc[r] = __builtin_fmaf(a[r][4 * c4 + 1], v.y, acc[r]);
-        acc[r] = __builtin_fmaf(a[r][4 * c4 + 2], v.z, acc[r]);
-        acc[r] = __builtin_fmaf(a[r][4 * c4 + 3], v.w, acc[r]);
+        const float4 q = reinterpret_cast<const float4*>(aq[r])[c4];
+        acc[r] = __builtin_fmaf(q.x, v.x, acc[r]);
+        acc[r] = __builtin_fmaf(q.y, v.y, acc[r]);
+        acc[r] = __builtin_fmaf(q.z, v.z, acc[r]);
+        acc[r] = __builtin_fmaf(q.w, v.w, acc[r]);
       }
     }
     const float nkj = score == 1 ? norm_k[static_cast<int64_t>(g) * nk + j] : 0.0f;
@@ -223,55 +230,67 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
   __syncthreads();
 
-  for (int r = 0; r < nr; r++) {
+  // each wave selects its own rows (w, w + 4, ...) with no workgroup
+  // barrier: a wave's LDS accesses take effect in issue order, so its
+  // histogram needs no synchronisation beyond the wave
+  int* wh = hist[wv];
+  for (int r = wv; r < nr; r += kSelWaves) {
     const uint32_t* ukey = ukeys + r * nk;
     const int i = i0 + r, row = g * nq + i;
-    if (t == 0) { s_prefix = 0; s_mask = 0; s_krem = k; s_count = 0; }
-    __syncthreads();
 
     // exact k-th largest image by MSB-first radix select (8-bit digits)
+    uint32_t pre = 0, msk = 0;
+    int krem = k;
     for (int pass = 0; pass < 4; pass++) {
       const int shift = 24 - 8 * pass;
-      for (int e = t; e < 256; e += kSelThreads) hist[e] = 0;
-      __syncthreads();
-      const uint32_t pre = s_prefix, msk = s_mask;
-      for (int j = t; j < nk; j += kSelThreads) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) wh[4 * lane + q] = 0;
+      wave_sync();
+      int j = lane;
+      for (; j + 3 * kWave < nk; j += 4 * kWave) {  // four key reads in flight
+        uint32_t u[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) u[q] = ukey[j + q * kWave];
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          if ((u[q] & msk) == pre) atomicAdd(&wh[(u[q] >> shift) & 255u], 1);
+      }
+      for (; j < nk; j += kWave) {
         const uint32_t u = ukey[j];
-        if ((u & msk) == pre) atomicAdd(&hist[(u >> shift) & 255u], 1);
+        if ((u & msk) == pre) atomicAdd(&wh[(u >> shift) & 255u], 1);
       }
-      __syncthreads();
-      if (wv == 0) {
-        // the digit: the highest bin at which the count from the top reaches
-        // krem (bin 0 if none does); lane l holds bins 255-4l .. 252-4l
-        int hb[4], sl = 0;
+      wave_sync();
+      // the digit: the highest bin at which the count from the top reaches
+      // krem (bin 0 if none does); lane l holds bins 255-4l .. 252-4l
+      int hb[4], sl = 0;
 #pragma unroll
-        for (int q = 0; q < 4; q++) { hb[q] = hist[255 - 4 * lane - q]; sl += hb[q]; }
-        int x = sl;
+      for (int q = 0; q < 4; q++) { hb[q] = wh[255 - 4 * lane - q]; sl += hb[q]; }
+      wave_sync();
+      int x = sl;
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int y = __shfl_up(x, o);
-          if (lane >= o) x += y;
-        }
-        const int krem = s_krem;
-        const unsigned long long reach = __ballot(x >= krem);
-        const int L = reach ? __builtin_ctzll(reach) : kWave - 1;
-        if (lane == L) {
-          int cum = x - sl, dg = 0;
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const int b = 255 - 4 * lane - q;
-            if (b == 0 || cum + hb[q] >= krem) { dg = b; break; }
-            cum += hb[q];
-          }
-          s_krem = krem - cum;
-          s_prefix = pre | (static_cast<uint32_t>(dg) << shift);
-          s_mask = msk | (255u << shift);
-        }
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
       }
-      __syncthreads();
+      const unsigned long long reach = __ballot(x >= krem);
+      const int L = reach ? __builtin_ctzll(reach) : kWave - 1;
+      int cum = x - sl, dg = 0;
+      bool found = false;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int b = 255 - 4 * lane - q;
+        if (!found && (b == 0 || cum + hb[q] >= krem)) { dg = b; found = true; }
+        if (!found) cum += hb[q];
+      }
+      // lane L's digit and count above it, for the whole wave
+      dg = __shfl(dg, L);
+      cum = __shfl(cum, L);
+      krem -= cum;
+      pre |= static_cast<uint32_t>(dg) << shift;
+      msk |= 255u << shift;
     }
-    const uint32_t T = s_prefix;
-    const int take_eq = s_krem;  // how many keys equal to T are kept (lowest indices first)
+    const uint32_t T = pre;
+    const int take_eq = krem;  // how many keys equal to T are kept (lowest indices first)
 
     // q-block geometry for the forced sets
     const int q0 = i * Bq, q1 = min(q0 + Bq, N);
@@ -279,23 +298,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int fi = 0, oi = 0;
     if (win_T >= 0) block_centre(order, i, Bq, N, F, H, W, fi, oi);
 
-    int eq_carry = 0, my_count = 0;
-    const int chunks = (nk + kSelThreads - 1) / kSelThreads;
-    for (int ch = 0; ch < chunks; ch++) {
-      const int j = ch * kSelThreads + t;
+    // one 64-key chunk per bitmask word, equal keys ranked by index
+    int eq_before = 0, count = 0;
+    for (int word = 0; word < words; word++) {
+      const int j = word * kWave + lane;
       const bool inr = j < nk;
       const uint32_t u = inr ? ukey[j] : 0u;
       const bool eq = inr && u == T;
-      // rank of this element among the equal ones, in ascending index order
       const unsigned long long eb = __ballot(eq);
       const int below = __popcll(eb & ((1ull << lane) - 1ull));
-      if (lane == 0) s_wave[wv] = __popcll(eb);
-      __syncthreads();
-      int before = eq_carry;
-      for (int w = 0; w < wv; w++) before += s_wave[w];
-      int chunk_total = 0;
-      for (int w = 0; w < kSelWaves; w++) chunk_total += s_wave[w];
-      bool keep = inr && (u > T || (eq && before + below < take_eq));
+      bool keep = inr && (u > T || (eq && eq_before + below < take_eq));
+      eq_before += __popcll(eb);
       if (inr && force_diag) {
         const int k0 = j * Bk, k1 = min(k0 + Bk, N);
         keep = keep || (k0 < q1 && q0 < k1);
@@ -307,17 +320,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         keep = df <= win_T && static_cast<int64_t>(dox) <= ((static_cast<int64_t>(win_r0) * W) >> df);
       }
       const unsigned long long kb = __ballot(keep);
-      const int word = (ch * kSelThreads + wv * kWave) / 64;
-      if (lane == 0 && word < words) {
-        bits[static_cast<int64_t>(row) * words + word] = kb;
-        my_count += __popcll(kb);
-      }
-      eq_carry += chunk_total;
-      __syncthreads();  // s_wave reuse
+      if (lane == 0) bits[static_cast<int64_t>(row) * words + word] = kb;
+      count += __popcll(kb);
     }
-    if (lane == 0) atomicAdd(&s_count, my_count);
-    __syncthreads();
-    if (t == 0) counts[row] = s_count;
+    if (lane == 0) counts[row] = count;
   }
 }
 
