@@ -173,6 +173,36 @@ __device__ __forceinline__ void block_centre(int order, int b, int B, int N, int
   offs = static_cast<int>(n % hw);
 }
 
+// The fp32 dot products of kSelRows consecutive q-block summaries of head g
+// (rows i0, i0+1, ...; rows past the last q-block repeat it, and callers
+// drop them) with kv-block j's summary: one fma chain per row over the
+// channels in order.  The q-block summaries are the same for every lane and
+// arrive through scalar loads.
+template <int D>
+__device__ __forceinline__ void row_dots(const float* __restrict__ sum_q,
+                                         const float* __restrict__ sum_k, int g, int nq, int nk,
+                                         int i0, int j, float (&acc)[kSelRows]) {
+  const float* aq[kSelRows];
+#pragma unroll
+  for (int r = 0; r < kSelRows; r++) {
+    aq[r] = sum_q + (static_cast<int64_t>(g) * nq + min(i0 + r, nq - 1)) * D;
+    acc[r] = 0.0f;
+  }
+  const float4* bj = reinterpret_cast<const float4*>(sum_k + (static_cast<int64_t>(g) * nk + j) * D);
+#pragma unroll 4
+  for (int c4 = 0; c4 < D / 4; c4++) {
+    const float4 v = bj[c4];
+#pragma unroll
+    for (int r = 0; r < kSelRows; r++) {
+      const float4 q = reinterpret_cast<const float4*>(aq[r])[c4];
+      acc[r] = __builtin_fmaf(q.x, v.x, acc[r]);
+      acc[r] = __builtin_fmaf(q.y, v.y, acc[r]);
+      acc[r] = __builtin_fmaf(q.z, v.z, acc[r]);
+      acc[r] = __builtin_fmaf(q.w, v.w, acc[r]);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ sum_q, const float* __restrict__ sum_k,
@@ -190,31 +220,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int nr = min(rows_per_wg, nq - i0);
   const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
 
-  // keys: for every (row, j) one fp32 fma chain over the channels in order.
-  // The q-block summaries are the same for every lane and arrive through
-  // scalar loads (rows past the last q-block repeat it; their keys are not
-  // stored).
-  const float* aq[kSelRows];
-#pragma unroll
-  for (int r = 0; r < kSelRows; r++)
-    aq[r] = sum_q + (static_cast<int64_t>(g) * nq + min(i0 + r, nq - 1)) * D;
+  // keys of the workgroup's rows against every kv-block
   for (int j = t; j < nk; j += kSelThreads) {
-    const float4* bj = reinterpret_cast<const float4*>(sum_k + (static_cast<int64_t>(g) * nk + j) * D);
     float acc[kSelRows];
-#pragma unroll
-    for (int r = 0; r < kSelRows; r++) acc[r] = 0.0f;
-#pragma unroll 4
-    for (int c4 = 0; c4 < D / 4; c4++) {
-      const float4 v = bj[c4];
-#pragma unroll
-      for (int r = 0; r < kSelRows; r++) {
-        const float4 q = reinterpret_cast<const float4*>(aq[r])[c4];
-        acc[r] = __builtin_fmaf(q.x, v.x, acc[r]);
-        acc[r] = __builtin_fmaf(q.y, v.y, acc[r]);
-        acc[r] = __builtin_fmaf(q.z, v.z, acc[r]);
-        acc[r] = __builtin_fmaf(q.w, v.w, acc[r]);
-      }
-    }
+    row_dots<D>(sum_q, sum_k, g, nq, nk, i0, j, acc);
     const float nkj = score == 1 ? norm_k[static_cast<int64_t>(g) * nk + j] : 0.0f;
 #pragma unroll
     for (int r = 0; r < kSelRows; r++) {
@@ -338,32 +347,13 @@ __global__ __launch_bounds__(kSelThreads) void scores_kernel(
     const float* __restrict__ sum_q, const float* __restrict__ sum_k,
     const float* __restrict__ norm_q, const float* __restrict__ norm_k, int nq, int nk, int score,
     float* __restrict__ out) {
-  __shared__ float a[kSelRows][D];
   const int gpr = (nq + kSelRows - 1) / kSelRows;
   const int g = blockIdx.x / gpr, i0 = (blockIdx.x % gpr) * kSelRows;
   const int nr = min(kSelRows, nq - i0);
   const int t = threadIdx.x;
-  for (int e = t; e < kSelRows * D; e += kSelThreads) {
-    const int r = e / D, c = e % D;
-    a[r][c] = r < nr ? sum_q[(static_cast<int64_t>(g) * nq + i0 + r) * D + c] : 0.0f;
-  }
-  __syncthreads();
   for (int j = t; j < nk; j += kSelThreads) {
-    const float4* bj = reinterpret_cast<const float4*>(sum_k + (static_cast<int64_t>(g) * nk + j) * D);
     float acc[kSelRows];
-#pragma unroll
-    for (int r = 0; r < kSelRows; r++) acc[r] = 0.0f;
-#pragma unroll 4
-    for (int c4 = 0; c4 < D / 4; c4++) {
-      const float4 v = bj[c4];
-#pragma unroll
-      for (int r = 0; r < kSelRows; r++) {
-        acc[r] = __builtin_fmaf(a[r][4 * c4 + 0], v.x, acc[r]);
-        acc[r] = __builtin_fmaf(a[r][4 * c4 + 1], v.y, acc[r]);
-        acc[r] = __builtin_fmaf(a[r][4 * c4 + 2], v.z, acc[r]);
-        acc[r] = __builtin_fmaf(a[r][4 * c4 + 3], v.w, acc[r]);
-      }
-    }
+    row_dots<D>(sum_q, sum_k, g, nq, nk, i0, j, acc);
     const float nkj = score == 1 ? norm_k[static_cast<int64_t>(g) * nk + j] : 0.0f;
 #pragma unroll
     for (int r = 0; r < kSelRows; r++) {
@@ -423,6 +413,9 @@ __global__ __launch_bounds__(kSelThreads) void sorted_select_kernel(
   for (int e = t; e < 2 * words; e += kSelThreads) keep[e] = 0u;
   if (t == 0) s_k = MODE == SEL_TOPK ? min(k, nk) : nk;
   __syncthreads();
+  // thread t handles elements t + 256m, so a stage whose partner distance
+  // jj is below 64 stays inside each wave's own 64-element groups; the
+  // workgroup synchronises only around stages that cross waves
   for (int kk = 2; kk <= p2; kk <<= 1)
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
       for (int e = t; e < p2; e += kSelThreads) {
@@ -433,7 +426,9 @@ __global__ __launch_bounds__(kSelThreads) void sorted_select_kernel(
           if ((a > b) == up) { srt[e] = b; srt[o] = a; }
         }
       }
-      __syncthreads();
+      const int next_jj = jj > 1 ? jj >> 1 : kk;
+      if (jj >= kWave || next_jj >= kWave || (kk == p2 && jj == 1)) __syncthreads();
+      else wave_sync();
     }
   if constexpr (MODE != SEL_TOPK) {
     // the weights in parallel, then one lane adds them in sorted order (the
