@@ -31,85 +31,106 @@
 namespace bsa {
 namespace {
 
-constexpr int kMaxB = 128;
-constexpr int kThreads = kMaxB;  // one thread per row in the norm phase, per channel in the sum phase
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// one workgroup per (block b, order o, head g): q_b into part[g][o][b].
-// bf16 rows are staged in LDS as 16-byte chunks, chunk c of row r stored at
-// c ^ (r mod 16) within the row, so that both the row-wise reads of the norm
-// phase and the column-wise reads of the sum phase are free of bank
-// conflicts; fp32 rows are read from global memory in both phases.
+// inv[g][n] = 1 / sqrt(fmaf chain over channels of x^2) for every token n
+// of head g (0 for an all-zero token); a token's norm does not depend on
+// the order, so it is computed once for all six.  One thread per token.
 template <bool F32, int D>
-__global__ __launch_bounds__(kThreads) void sics_block_kernel(
+__global__ __launch_bounds__(256) void sics_inv_kernel(const void* __restrict__ src,
+                                                       int64_t stride_g, int64_t stride_n,
+                                                       uint32_t N, int G, float* __restrict__ inv) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // g * N + n
+  if (idx >= static_cast<int64_t>(G) * N) return;
+  const int64_t g = idx / N, n = idx % N;
+  const int64_t off = n * stride_n + g * stride_g;
+  float nr = 0.0f;
+  if constexpr (F32) {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const float*>(src) + off);
+#pragma unroll
+    for (int c4 = 0; c4 < D / 4; c4++) {
+      const u32x4 v = xr[c4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) nr = __builtin_fmaf(__uint_as_float(v[q]), __uint_as_float(v[q]), nr);
+    }
+  } else {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + off);
+#pragma unroll
+    for (int c8 = 0; c8 < D / 8; c8++) {
+      const u32x4 v = xr[c8];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const float lo = bf16_bits_to_f32(v[q] & 0xffffu), hi = bf16_bits_to_f32(v[q] >> 16);
+        nr = __builtin_fmaf(lo, lo, nr);
+        nr = __builtin_fmaf(hi, hi, nr);
+      }
+    }
+  }
+  inv[idx] = nr > 0.0f ? 1.0f / __builtin_sqrtf(nr) : 0.0f;
+}
+
+// One wave per (block b, order o, head g): q_b into part[g][o][b].  Lane l
+// owns channels l*CPL .. l*CPL+CPL-1 and runs their chains over the block's
+// rows in order, reading each row straight from global memory (one
+// coalesced access per row); row r's natural index comes from the lane
+// that computed it, its inverse norm from the per-token table.
+template <bool F32, int D>
+__global__ __launch_bounds__(kWave) void sics_block_kernel(
     const void* __restrict__ src, int64_t stride_g, int64_t stride_n, uint32_t N, uint32_t F,
-    uint32_t H, uint32_t W, int B, int nb, float* __restrict__ part) {
-  constexpr int CPR = D / 8;                   // 16-byte chunks per bf16 row
-  constexpr int SW = CPR - 1 < 15 ? CPR - 1 : 15;
-  __shared__ u32x4 xs[F32 ? 1 : kMaxB * CPR];
-  __shared__ float inv[kMaxB];
+    uint32_t H, uint32_t W, int B, int nb, const float* __restrict__ inv, float* __restrict__ part) {
+  constexpr int CPL = D / kWave;  // channels per lane
   __shared__ __align__(16) float u[D];
-  __shared__ int64_t roff[kMaxB];  // element offset of the block's row r, channel 0
   const int b = blockIdx.x, o = blockIdx.y, g = blockIdx.z;
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x;
   const int r0 = b * B;
-  const int len = min(B, static_cast<int>(N) - r0);
-  if (t < len) {
-    const uint32_t n = natural_index(o, static_cast<uint32_t>(r0 + t), F, H, W);
-    roff[t] = static_cast<int64_t>(n) * stride_n + static_cast<int64_t>(g) * stride_g;
-  }
-  __syncthreads();
-  auto row_off = [&](int r) -> int64_t { return roff[r]; };
-  if constexpr (!F32) {
-    const uint16_t* s16 = static_cast<const uint16_t*>(src);
-    for (int e = t; e < len * CPR; e += kThreads) {
-      const int r = e / CPR, ch = e % CPR;
-      xs[r * CPR + (ch ^ (r & SW))] = *reinterpret_cast<const u32x4*>(s16 + row_off(r) + ch * 8);
-    }
-    __syncthreads();
-  }
-  // row norms, channels in order (bf16 widens exactly)
-  if (t < len) {
-    float nr = 0.0f;
-    if constexpr (F32) {
-      const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const float*>(src) + row_off(t));
-      for (int c4 = 0; c4 < D / 4; c4++) {
-        const u32x4 v = xr[c4];
+  const int len = min(B, static_cast<int>(N) - r0);  // B <= 2 * kWave
+  const uint32_t n_lo = lane < len ? natural_index(o, static_cast<uint32_t>(r0 + lane), F, H, W) : 0u;
+  const uint32_t n_hi =
+      lane + kWave < len ? natural_index(o, static_cast<uint32_t>(r0 + kWave + lane), F, H, W) : 0u;
+  const float* invg = inv + static_cast<int64_t>(g) * N;
+  const int64_t gofs = static_cast<int64_t>(g) * stride_g + lane * CPL;
+  float a[CPL];
 #pragma unroll
-        for (int q = 0; q < 4; q++) nr = __builtin_fmaf(__uint_as_float(v[q]), __uint_as_float(v[q]), nr);
-      }
-    } else {
-#pragma unroll 4
-      for (int ch = 0; ch < CPR; ch++) {
-        const u32x4 v = xs[t * CPR + (ch ^ (t & SW))];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const float lo = bf16_bits_to_f32(v[q] & 0xffffu), hi = bf16_bits_to_f32(v[q] >> 16);
-          nr = __builtin_fmaf(lo, lo, nr);
-          nr = __builtin_fmaf(hi, hi, nr);
-        }
-      }
-    }
-    inv[t] = nr > 0.0f ? 1.0f / __builtin_sqrtf(nr) : 0.0f;
-  }
-  __syncthreads();
-  // per-channel sums of the unit rows, rows in order
-  if (t < D) {
-    float a = 0.0f;
+  for (int k = 0; k < CPL; k++) a[k] = 0.0f;
+  // row r: its natural index from the lane that computed it, its inverse
+  // norm, and this lane's channels of it
+  auto fetch = [&](int r, float& ir, float (&x)[CPL]) {
+    const uint32_t n = __builtin_amdgcn_readlane(r < kWave ? n_lo : n_hi, r & (kWave - 1));
+    ir = invg[n];
+    const int64_t off = static_cast<int64_t>(n) * stride_n + gofs;
     if constexpr (F32) {
-      const float* s32 = static_cast<const float*>(src);
-      for (int r = 0; r < len; r++) a = __builtin_fmaf(s32[row_off(r) + t], inv[r], a);
+      const float* xp = static_cast<const float*>(src) + off;
+#pragma unroll
+      for (int k = 0; k < CPL; k++) x[k] = xp[k];
+    } else if constexpr (CPL == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(src) + off);
+      x[0] = bf16_bits_to_f32(w & 0xffffu);
+      x[1] = bf16_bits_to_f32(w >> 16);
     } else {
-      const uint16_t* xe = reinterpret_cast<const uint16_t*>(xs);
-      const int ch = t / 8, q = t % 8;
-#pragma unroll 8
-      for (int r = 0; r < len; r++)
-        a = __builtin_fmaf(bf16_bits_to_f32(xe[(r * CPR + (ch ^ (r & SW))) * 8 + q]), inv[r], a);
+      x[0] = bf16_bits_to_f32(static_cast<const uint16_t*>(src)[off]);
     }
-    u[t] = a;
+  };
+  constexpr int kRun = 16;  // rows whose loads are in flight together
+  int r = 0;
+  for (; r + kRun <= len; r += kRun) {
+    float ir[kRun], x[kRun][CPL];
+#pragma unroll
+    for (int e = 0; e < kRun; e++) fetch(r + e, ir[e], x[e]);
+#pragma unroll
+    for (int e = 0; e < kRun; e++)
+#pragma unroll
+      for (int k = 0; k < CPL; k++) a[k] = __builtin_fmaf(x[e][k], ir[e], a[k]);
   }
+  for (; r < len; r++) {
+    float ir, x[CPL];
+    fetch(r, ir, x);
+#pragma unroll
+    for (int k = 0; k < CPL; k++) a[k] = __builtin_fmaf(x[k], ir, a[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < CPL; k++) u[lane * CPL + k] = a[k];
   __syncthreads();
-  if (t == 0) {
+  if (lane == 0) {
     float q = 0.0f;
     const float4* u4 = reinterpret_cast<const float4*>(u);
 #pragma unroll 8
@@ -160,9 +181,14 @@ __global__ void select_orders_kernel(const float* __restrict__ a, const float* _
 
 }  // namespace
 
-size_t order_workspace_bytes(int G, int N, int B) {
+// workspace: part [G][6][nb] fp32, then (256-byte aligned) inv [G][N] fp32
+static size_t part_bytes(int G, int N, int B) {
   const size_t nb = static_cast<size_t>((N + B - 1) / B);
-  return sizeof(float) * static_cast<size_t>(G) * 6 * nb;
+  return (sizeof(float) * static_cast<size_t>(G) * 6 * nb + 255) & ~static_cast<size_t>(255);
+}
+
+size_t order_workspace_bytes(int G, int N, int B) {
+  return part_bytes(G, N, B) + sizeof(float) * static_cast<size_t>(G) * static_cast<size_t>(N);
 }
 
 hipError_t launch_order_scores(const void* src, int src_dt, int64_t stride_g, int64_t stride_n,
@@ -171,14 +197,20 @@ hipError_t launch_order_scores(const void* src, int src_dt, int64_t stride_g, in
   const uint32_t N = static_cast<uint32_t>(F) * H * W;
   const int nb = static_cast<int>((N + B - 1) / B);
   float* part = static_cast<float*>(ws);
+  float* inv = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes(G, static_cast<int>(N), B));
+  const uint32_t inv_grid = static_cast<uint32_t>((static_cast<int64_t>(G) * N + 255) / 256);
   const dim3 grid(nb, 6, G);
+  auto run = [&](auto inv_kern, auto blk_kern) {
+    inv_kern<<<inv_grid, 256, 0, s>>>(src, stride_g, stride_n, N, G, inv);
+    blk_kern<<<grid, kWave, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, inv, part);
+  };
   const bool f32 = src_dt == 0;
   if (d == 128) {
-    if (f32) sics_block_kernel<true, 128><<<grid, kThreads, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, part);
-    else sics_block_kernel<false, 128><<<grid, kThreads, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, part);
+    if (f32) run(sics_inv_kernel<true, 128>, sics_block_kernel<true, 128>);
+    else run(sics_inv_kernel<false, 128>, sics_block_kernel<false, 128>);
   } else {
-    if (f32) sics_block_kernel<true, 64><<<grid, kThreads, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, part);
-    else sics_block_kernel<false, 64><<<grid, kThreads, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, part);
+    if (f32) run(sics_inv_kernel<true, 64>, sics_block_kernel<true, 64>);
+    else run(sics_inv_kernel<false, 64>, sics_block_kernel<false, 64>);
   }
   const int n = G * 6;
   sics_sum_kernel<<<(n + 255) / 256, 256, 0, s>>>(part, nb, n, scores);

@@ -175,7 +175,9 @@ int bsa_permute_pool(const void *src, int32_t src_dt, void *dst, int64_t nat_str
                      void *stream);
 
 /* bsa_order_workspace — bytes of device workspace bsa_order_scores needs
- * for G heads, an F x H x W grid and B-row blocks: 4 * G * 6 * ceil(N/B).
+ * for G heads, an F x H x W grid and B-row blocks: the per-block terms,
+ * 4 * G * 6 * ceil(N/B) rounded up to a multiple of 256, then the per-token
+ * inverse norms, 4 * G * N.
  * Returns -1 for non-positive sizes, B not in {64, 128} or N >= 2^31. */
 int64_t bsa_order_workspace(int32_t G, int32_t F, int32_t H, int32_t W, int32_t B);
 
