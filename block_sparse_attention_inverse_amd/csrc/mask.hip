@@ -501,15 +501,28 @@ __global__ __launch_bounds__(kSelThreads) void sorted_select_kernel(
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ counts,
                                                             int R, int32_t* __restrict__ row_ptr,
                                                             int32_t* __restrict__ nnz) {
+  // runs of 4 * kScanThreads rows in order, four consecutive rows per
+  // thread; the next run's counts are loaded while the current one is scanned
+  constexpr int kPer = 4, kRun = kPer * kScanThreads;
   __shared__ int s_w[kScanThreads / kWave];
   __shared__ int s_carry;
   const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
+  auto load = [&](int base, int (&v)[kPer]) {
+#pragma unroll
+    for (int q = 0; q < kPer; q++) {
+      const int idx = base + kPer * t + q;
+      v[q] = idx < R ? counts[idx] : 0;
+    }
+  };
   if (t == 0) s_carry = 0;
+  int v[kPer];
+  load(0, v);
   __syncthreads();
-  for (int base = 0; base < R; base += kScanThreads) {
-    const int idx = base + t;
-    const int v = idx < R ? counts[idx] : 0;
-    int x = v;  // inclusive wave scan
+  for (int base = 0; base < R; base += kRun) {
+    int vn[kPer];
+    load(base + kRun, vn);
+    const int own = v[0] + v[1] + v[2] + v[3];
+    int x = own;  // inclusive wave scan of the threads' totals
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const int y = __shfl_up(x, o);
@@ -523,10 +536,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
       tot += s_w[w];
     }
     const int carry = s_carry;
-    if (idx < R) row_ptr[idx] = carry + wbase + x - v;
+    int run = carry + wbase + x - own;
+#pragma unroll
+    for (int q = 0; q < kPer; q++) {
+      const int idx = base + kPer * t + q;
+      if (idx < R) row_ptr[idx] = run;
+      run += v[q];
+    }
     __syncthreads();
     if (t == 0) s_carry = carry + tot;
     __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPer; q++) v[q] = vn[q];
   }
   if (t == 0) {
     row_ptr[R] = s_carry;
@@ -540,7 +561,10 @@ __device__ __forceinline__ unsigned long long live_bits(int w, int nk) {
   return rem >= 64 ? ~0ull : (rem <= 0 ? 0ull : (1ull << rem) - 1ull);
 }
 
-// one wave per row, 4 rows per workgroup; bits at kv-block >= nk are ignored
+// one wave per row, 4 rows per workgroup; bits at kv-block >= nk are ignored.
+// The row's words are loaded one per lane; then for each word every lane
+// tests its own bit, so the indices of a word are written by one coalesced
+// store.
 __global__ __launch_bounds__(256) void emit_kernel(const unsigned long long* __restrict__ bits,
                                                    const int32_t* __restrict__ row_ptr, int R,
                                                    int words, int nk, int32_t* __restrict__ col_idx,
@@ -549,26 +573,22 @@ __global__ __launch_bounds__(256) void emit_kernel(const unsigned long long* __r
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   if (row >= R) return;
   int64_t pos = row_ptr[row];
+  const unsigned long long below = (1ull << lane) - 1ull;
   for (int w0 = 0; w0 < words; w0 += kWave) {
-    const int w = w0 + lane;
-    const unsigned long long b =
-        w < words ? bits[static_cast<int64_t>(row) * words + w] & live_bits(w, nk) : 0ull;
-    const int c = __popcll(b);
-    int x = c;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
+    const int wl = w0 + lane;
+    const unsigned long long mine =
+        wl < words ? bits[static_cast<int64_t>(row) * words + wl] & live_bits(wl, nk) : 0ull;
+    const int nw = min(kWave, words - w0);
+    for (int k = 0; k < nw; k++) {
+      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine), k);
+      const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(mine >> 32), k);
+      const unsigned long long b = (static_cast<unsigned long long>(hi) << 32) | lo;
+      if ((b >> lane) & 1ull) {
+        const int64_t p = pos + __popcll(b & below);
+        if (p < cap) col_idx[p] = (w0 + k) * 64 + lane;
+      }
+      pos += __popcll(b);
     }
-    int64_t p = pos + (x - c);
-    unsigned long long m = b;
-    while (m) {
-      const int bit = __builtin_ctzll(m);
-      m &= m - 1ull;
-      if (p < cap) col_idx[p] = w * 64 + bit;
-      p++;
-    }
-    pos += __shfl(x, kWave - 1);
   }
 }
 

@@ -145,24 +145,34 @@ __global__ __launch_bounds__(kWave) void sics_block_kernel(
   }
 }
 
-// score[g][o] = sum of part[g][o][0..nb) in order: one thread per (g, o);
-// loads are issued sixteen at a time ahead of the sequential adds
-__global__ void sics_sum_kernel(const float* __restrict__ part, int nb, int n,
-                                float* __restrict__ scores) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+// score[g][o] = sum of part[g][o][0..nb) in order: one workgroup per
+// (g, o) stages the terms through LDS in coalesced runs, one lane adds them
+constexpr int kSumThreads = 256;
+constexpr int kSumRun = 4096;
+__global__ __launch_bounds__(kSumThreads) void sics_sum_kernel(const float* __restrict__ part,
+                                                               int nb, float* __restrict__ scores) {
+  __shared__ __align__(16) float run[kSumRun];
+  const int i = blockIdx.x, t = threadIdx.x;
   const float* p = part + static_cast<int64_t>(i) * nb;
   float s = 0.0f;
-  int b = 0;
-  for (; b + 16 <= nb; b += 16) {
-    float v[16];
-#pragma unroll
-    for (int e = 0; e < 16; e++) v[e] = p[b + e];
-#pragma unroll
-    for (int e = 0; e < 16; e++) s = s + v[e];
+  for (int b0 = 0; b0 < nb; b0 += kSumRun) {
+    const int n = min(kSumRun, nb - b0);
+    for (int e = t; e < n; e += kSumThreads) run[e] = p[b0 + e];
+    __syncthreads();
+    if (t == 0) {
+      int e = 0;
+      for (; e + 4 <= n; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(run + e);
+        s = s + v.x;
+        s = s + v.y;
+        s = s + v.z;
+        s = s + v.w;
+      }
+      for (; e < n; e++) s = s + run[e];
+    }
+    __syncthreads();
   }
-  for (; b < nb; b++) s = s + p[b];
-  scores[i] = s;
+  if (t == 0) scores[i] = s;
 }
 
 __global__ void select_orders_kernel(const float* __restrict__ a, const float* __restrict__ b,
@@ -213,7 +223,7 @@ hipError_t launch_order_scores(const void* src, int src_dt, int64_t stride_g, in
     else run(sics_inv_kernel<false, 64>, sics_block_kernel<false, 64>);
   }
   const int n = G * 6;
-  sics_sum_kernel<<<(n + 255) / 256, 256, 0, s>>>(part, nb, n, scores);
+  sics_sum_kernel<<<n, kSumThreads, 0, s>>>(part, nb, scores);
   return hipGetLastError();
 }
 
