@@ -48,6 +48,31 @@ __device__ __forceinline__ uint32_t natural_index(int order, uint32_t p, uint32_
   return (f * H + h) * W + w;
 }
 
+// The same map as natural_index, split into the order's extents and the
+// natural strides of its axes (outermost, middle, innermost), so that a
+// kernel mapping many positions resolves the order once:
+//   n = (p / (d1*d2)) * s0 + ((p / d2) % d1) * s1 + (p % d2) * s2.
+struct OrderMap {
+  uint32_t d1, d2, s0, s1, s2;
+  __device__ __forceinline__ uint32_t operator()(uint32_t p) const {
+    const uint32_t q = p / d2;
+    return (q / d1) * s0 + (q % d1) * s1 + (p % d2) * s2;
+  }
+};
+
+__device__ __forceinline__ OrderMap order_map(int order, uint32_t F, uint32_t H, uint32_t W) {
+  const uint32_t sf = H * W, sh = W, sw = 1;
+  switch (order) {
+    default:
+    case 0: return {H, W, sf, sh, sw};  // F H W
+    case 1: return {W, H, sf, sw, sh};  // F W H
+    case 2: return {F, W, sh, sf, sw};  // H F W
+    case 3: return {W, F, sh, sw, sf};  // H W F
+    case 4: return {F, H, sw, sf, sh};  // W F H
+    case 5: return {H, F, sw, sh, sf};  // W H F
+  }
+}
+
 // Workgroup id -> logical tile id so that each XCD (which receives every
 // 8th workgroup) owns one contiguous range of logical tiles; neighbouring
 // tiles of one head then share that XCD's L2.

@@ -38,40 +38,56 @@ __global__ __launch_bounds__(kThreads) void permute_pool_kernel(
   const int len = min(B, static_cast<int>(N) - r0);
   const int order = orders[g];
 
-  // ---- gather, convert, write the reordered rows and keep them in LDS
-  float amax = 0.0f;
-  for (int c = t; c < len * CPR; c += kThreads) {
+  // ---- gather (all of the thread's loads issued before the first use),
+  // convert, write the reordered rows and keep them in LDS for the sums
+  constexpr int MAXC = 128 * CPR / kThreads;  // chunks per thread in a 128-row block
+  const int nc = len * CPR;
+  const OrderMap nat_of = order_map(order, F, H, W);
+  u32x4 o[MAXC];
+#pragma unroll
+  for (int m = 0; m < MAXC; m++) {
+    // chunks past the block reload its last chunk (no branch around the
+    // load) and are not used
+    const int c = min(t + m * kThreads, nc - 1);
     const int r = c / CPR, c8 = (c % CPR) * 8;
-    const uint32_t p = static_cast<uint32_t>(r0 + r);
-    const uint32_t n = natural_index(order, p, F, H, W);
+    const uint32_t n = nat_of(static_cast<uint32_t>(r0 + r));
     const int64_t nat = static_cast<int64_t>(n) * stride_n + static_cast<int64_t>(g) * stride_g + c8;
-    u32x4 o;
     if constexpr (F32) {
       const u32x4* sp = reinterpret_cast<const u32x4*>(static_cast<const float*>(src) + nat);
       const u32x4 lo = __builtin_nontemporal_load(sp), hi = __builtin_nontemporal_load(sp + 1);
       auto cv = [](uint32_t x, uint32_t y) {
         return f32_to_bf16_bits(__uint_as_float(x)) | (f32_to_bf16_bits(__uint_as_float(y)) << 16);
       };
-      o = u32x4{cv(lo.x, lo.y), cv(lo.z, lo.w), cv(hi.x, hi.y), cv(hi.z, hi.w)};
+      o[m] = u32x4{cv(lo.x, lo.y), cv(lo.z, lo.w), cv(hi.x, hi.y), cv(hi.z, hi.w)};
     } else {
-      o = __builtin_nontemporal_load(
+      o[m] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + nat));
     }
-    if (dst != nullptr)
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + (static_cast<int64_t>(g) * N + p) * D + c8));
-    *reinterpret_cast<u32x4*>(tile + r * D + c8) = o;
-    const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+  }
+  float amax = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xffffu)));
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
+  for (int m = 0; m < MAXC; m++) {
+    const int c = t + m * kThreads;
+    if (c < nc) {
+      const int r = c / CPR, c8 = (c % CPR) * 8;
+      if (dst != nullptr)
+        __builtin_nontemporal_store(
+            o[m], reinterpret_cast<u32x4*>(dst + (static_cast<int64_t>(g) * N + r0 + r) * D + c8));
+      if (sums != nullptr) *reinterpret_cast<u32x4*>(tile + r * D + c8) = o[m];
+      const uint32_t w[4] = {o[m].x, o[m].y, o[m].z, o[m].w};
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xffffu)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
+      }
     }
   }
-  __syncthreads();
+  if (sums != nullptr) __syncthreads();  // (uniform) the tile is complete
 
   // ---- per-channel sums, rows in increasing order
   if (sums != nullptr && t < D) {
     float a = 0.0f;
+#pragma unroll 8
     for (int r = 0; r < len; r++) a = a + bf16_bits_to_f32(tile[r * D + t]);
     sums[(static_cast<int64_t>(g) * nb + b) * D + t] = a;
   }
@@ -87,10 +103,13 @@ __global__ __launch_bounds__(kThreads) void permute_pool_kernel(
     const float sc = amax == 0.0f ? 0.0f : amax / 127.0f;
     const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
     if (t == 0) scale[static_cast<int64_t>(g) * nb + b] = sc;
-    for (int c = t; c < len * CPR; c += kThreads) {
+    // the thread's own chunks, still in registers
+#pragma unroll
+    for (int m = 0; m < MAXC; m++) {
+      const int c = t + m * kThreads;
+      if (c >= nc) break;
       const int r = c / CPR, c8 = (c % CPR) * 8;
-      const u32x4 o = *reinterpret_cast<const u32x4*>(tile + r * D + c8);
-      const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+      const uint32_t w[4] = {o[m].x, o[m].y, o[m].z, o[m].w};
       uint32_t packed[2] = {0u, 0u};
 #pragma unroll
       for (int q = 0; q < 4; q++)
