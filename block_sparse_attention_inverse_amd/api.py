@@ -599,7 +599,7 @@ class LayerPlan:
         if self.int8:
             permute_pool(V, axis_order, F, H, W, p.Bk, int8=v8, reordered=False)
         else:
-            permute(V, axis_order, F, H, W, 0, out=self.Vp)
+            permute_pool(V, axis_order, F, H, W, p.Bk, out=self.Vp)
 
     def build_mask_from_sums(self, axis_order):
         lib = _lib.load()
