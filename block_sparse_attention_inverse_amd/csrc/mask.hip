@@ -413,18 +413,18 @@ __global__ __launch_bounds__(kSelThreads) void sorted_select_kernel(
   for (int e = t; e < 2 * words; e += kSelThreads) keep[e] = 0u;
   if (t == 0) s_k = MODE == SEL_TOPK ? min(k, nk) : nk;
   __syncthreads();
-  // thread t handles elements t + 256m, so a stage whose partner distance
-  // jj is below 64 stays inside each wave's own 64-element groups; the
-  // workgroup synchronises only around stages that cross waves
+  // thread t handles the compare-exchange pairs t + 256m (pair pi joins
+  // element e, pi with a zero bit inserted at jj, and e + jj), so every lane
+  // works in every stage.  In a stage with jj below 64, pairs [32q, 32q+32)
+  // touch only elements [64q, 64q+64), which belong to one wave: such
+  // stages synchronise the wave only, the others the workgroup.
   for (int kk = 2; kk <= p2; kk <<= 1)
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int e = t; e < p2; e += kSelThreads) {
-        const int o = e ^ jj;
-        if (o > e) {
-          const unsigned long long a = srt[e], b = srt[o];
-          const bool up = (e & kk) == 0;
-          if ((a > b) == up) { srt[e] = b; srt[o] = a; }
-        }
+      for (int pi = t; pi < p2 / 2; pi += kSelThreads) {
+        const int e = ((pi & ~(jj - 1)) << 1) | (pi & (jj - 1)), o = e + jj;
+        const unsigned long long a = srt[e], b = srt[o];
+        const bool up = (e & kk) == 0;
+        if ((a > b) == up) { srt[e] = b; srt[o] = a; }
       }
       const int next_jj = jj > 1 ? jj >> 1 : kk;
       if (jj >= kWave || next_jj >= kWave || (kk == p2 && jj == 1)) __syncthreads();
