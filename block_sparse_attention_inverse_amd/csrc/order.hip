@@ -35,7 +35,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // inv[g][n] = 1 / sqrt(fmaf chain over channels of x^2) for every token n
 // of head g (0 for an all-zero token); a token's norm does not depend on
-// the order, so it is computed once for all six.  One thread per token.
+// the order, so it is computed once for all six.  One thread per token
+// (used for fp32 input; bf16 input takes the staged variant below).
 template <bool F32, int D>
 __global__ __launch_bounds__(256) void sics_inv_kernel(const void* __restrict__ src,
                                                        int64_t stride_g, int64_t stride_n,
@@ -67,6 +68,56 @@ __global__ __launch_bounds__(256) void sics_inv_kernel(const void* __restrict__ 
     }
   }
   inv[idx] = nr > 0.0f ? 1.0f / __builtin_sqrtf(nr) : 0.0f;
+}
+
+// bf16 variant of the same table: a workgroup stages 128 consecutive
+// tokens of one head through LDS (each token's row read by 16 lanes as one
+// coalesced 256-byte access at d = 128), chunk c of token r stored at
+// c ^ (r mod 16) within the row, then thread r runs token r's chain over the
+// channels in order.
+constexpr int kInvRows = 128;
+template <int D>
+__global__ __launch_bounds__(256) void sics_inv_bf16_kernel(const uint16_t* __restrict__ src,
+                                                            int64_t stride_g, int64_t stride_n,
+                                                            uint32_t N, float* __restrict__ inv) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  constexpr int SW = CPR - 1 < 15 ? CPR - 1 : 15;
+  constexpr int PER = kInvRows * CPR / 256;
+  __shared__ u32x4 xs[kInvRows * CPR];
+  const int g = blockIdx.y, t = threadIdx.x;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kInvRows;
+  const int len = static_cast<int>(min(static_cast<int64_t>(kInvRows), static_cast<int64_t>(N) - n0));
+  const int nc = len * CPR;
+  u32x4 v[PER];
+#pragma unroll
+  for (int m = 0; m < PER; m++) {
+    const int c = min(t + 256 * m, nc - 1);  // past the last token: reload it, unused
+    const int r = c / CPR, ch = c % CPR;
+    v[m] = *reinterpret_cast<const u32x4*>(src + (n0 + r) * stride_n + g * stride_g + ch * 8);
+  }
+#pragma unroll
+  for (int m = 0; m < PER; m++) {
+    const int c = t + 256 * m;
+    if (c < nc) {
+      const int r = c / CPR, ch = c % CPR;
+      xs[r * CPR + (ch ^ (r & SW))] = v[m];
+    }
+  }
+  __syncthreads();
+  if (t < len) {
+    float nr = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < CPR; ch++) {
+      const u32x4 w = xs[t * CPR + (ch ^ (t & SW))];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const float lo = bf16_bits_to_f32(w[q] & 0xffffu), hi = bf16_bits_to_f32(w[q] >> 16);
+        nr = __builtin_fmaf(lo, lo, nr);
+        nr = __builtin_fmaf(hi, hi, nr);
+      }
+    }
+    inv[static_cast<int64_t>(g) * N + n0 + t] = nr > 0.0f ? 1.0f / __builtin_sqrtf(nr) : 0.0f;
+  }
 }
 
 // One wave per (block b, order o, head g): q_b into part[g][o][b].  Lane l
@@ -210,17 +261,19 @@ hipError_t launch_order_scores(const void* src, int src_dt, int64_t stride_g, in
   float* inv = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes(G, static_cast<int>(N), B));
   const uint32_t inv_grid = static_cast<uint32_t>((static_cast<int64_t>(G) * N + 255) / 256);
   const dim3 grid(nb, 6, G);
-  auto run = [&](auto inv_kern, auto blk_kern) {
-    inv_kern<<<inv_grid, 256, 0, s>>>(src, stride_g, stride_n, N, G, inv);
-    blk_kern<<<grid, kWave, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, inv, part);
-  };
+  const dim3 inv16_grid((N + kInvRows - 1) / kInvRows, G);
+  const uint16_t* s16 = static_cast<const uint16_t*>(src);
   const bool f32 = src_dt == 0;
   if (d == 128) {
-    if (f32) run(sics_inv_kernel<true, 128>, sics_block_kernel<true, 128>);
-    else run(sics_inv_kernel<false, 128>, sics_block_kernel<false, 128>);
+    if (f32) sics_inv_kernel<true, 128><<<inv_grid, 256, 0, s>>>(src, stride_g, stride_n, N, G, inv);
+    else sics_inv_bf16_kernel<128><<<inv16_grid, 256, 0, s>>>(s16, stride_g, stride_n, N, inv);
+    if (f32) sics_block_kernel<true, 128><<<grid, kWave, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, inv, part);
+    else sics_block_kernel<false, 128><<<grid, kWave, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, inv, part);
   } else {
-    if (f32) run(sics_inv_kernel<true, 64>, sics_block_kernel<true, 64>);
-    else run(sics_inv_kernel<false, 64>, sics_block_kernel<false, 64>);
+    if (f32) sics_inv_kernel<true, 64><<<inv_grid, 256, 0, s>>>(src, stride_g, stride_n, N, G, inv);
+    else sics_inv_bf16_kernel<64><<<inv16_grid, 256, 0, s>>>(s16, stride_g, stride_n, N, inv);
+    if (f32) sics_block_kernel<true, 64><<<grid, kWave, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, inv, part);
+    else sics_block_kernel<false, 64><<<grid, kWave, 0, s>>>(src, stride_g, stride_n, N, F, H, W, B, nb, inv, part);
   }
   const int n = G * 6;
   sics_sum_kernel<<<n, kSumThreads, 0, s>>>(part, nb, scores);
