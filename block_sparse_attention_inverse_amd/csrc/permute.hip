@@ -6,9 +6,9 @@
 // contiguous.  The permutation is never stored: each thread derives the
 // natural index of its reordered row from the order code by div/mod.
 //
-// HBM-bound gather/scatter.  One thread moves 8 channels (16 B of bf16 or
-// 32 B of fp32); d/8 consecutive threads cover one row, so every wave reads
-// and writes whole rows contiguously on both sides.
+// HBM-bound gather/scatter.  A chunk is 8 channels (16 B of bf16 or 32 B of
+// fp32); d/8 consecutive threads cover one row, so every wave reads and
+// writes whole rows contiguously on both sides.
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
 
@@ -60,25 +60,38 @@ __device__ __forceinline__ void store8(void* base, int64_t off, const u32x4& lo,
   }
 }
 
-// grid: (ceil(N*d/8 / kThreads), G).  direction 0 gathers natural -> reordered,
-// direction 1 scatters reordered -> natural.
+// grid: (ceil(N*d/8 / (kThreads*kChunks)), G).  direction 0 gathers
+// natural -> reordered, direction 1 scatters reordered -> natural.  Each
+// thread moves kChunks 8-channel chunks, kThreads apart, with all of its
+// loads issued before its first store; the order is resolved once.
+constexpr int kChunks = 4;
 template <bool SRC_F32, bool DST_F32, bool GATHER>
 __global__ __launch_bounds__(kThreads) void permute_kernel(
     const void* __restrict__ src, void* __restrict__ dst, int64_t stride_g, int64_t stride_n,
     uint32_t N, uint32_t F, uint32_t H, uint32_t W, uint32_t chunks_per_row,
     const uint8_t* __restrict__ orders) {
   const uint32_t g = blockIdx.y;
-  const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t p = t / chunks_per_row;
-  if (p >= N) return;
-  const uint32_t c8 = (t - p * chunks_per_row) * 8;
+  const OrderMap nat_of = order_map(orders[g], F, H, W);
+  const uint64_t total = static_cast<uint64_t>(N) * chunks_per_row;
   const int d = static_cast<int>(chunks_per_row * 8);
-  const uint32_t n = natural_index(orders[g], p, F, H, W);
-  const int64_t nat = static_cast<int64_t>(n) * stride_n + static_cast<int64_t>(g) * stride_g + c8;
-  const int64_t red = (static_cast<int64_t>(g) * N + p) * d + c8;
-  u32x4 lo, hi;
-  load8<SRC_F32>(src, GATHER ? nat : red, lo, hi);
-  store8<SRC_F32, DST_F32>(dst, GATHER ? red : nat, lo, hi);
+  const uint64_t c0 = static_cast<uint64_t>(blockIdx.x) * kThreads * kChunks + threadIdx.x;
+  u32x4 lo[kChunks], hi[kChunks];
+  int64_t to[kChunks];
+#pragma unroll
+  for (int m = 0; m < kChunks; m++) {
+    // chunks past the end reload the last one (no branch around the load)
+    const uint64_t c = c0 + static_cast<uint64_t>(m) * kThreads;
+    const uint64_t cc = c < total ? c : total - 1;
+    const uint32_t p = static_cast<uint32_t>(cc / chunks_per_row);
+    const uint32_t c8 = static_cast<uint32_t>(cc - static_cast<uint64_t>(p) * chunks_per_row) * 8;
+    const int64_t nat = static_cast<int64_t>(nat_of(p)) * stride_n + static_cast<int64_t>(g) * stride_g + c8;
+    const int64_t red = (static_cast<int64_t>(g) * N + p) * d + c8;
+    load8<SRC_F32>(src, GATHER ? nat : red, lo[m], hi[m]);
+    to[m] = GATHER ? red : nat;
+  }
+#pragma unroll
+  for (int m = 0; m < kChunks; m++)
+    if (c0 + static_cast<uint64_t>(m) * kThreads < total) store8<SRC_F32, DST_F32>(dst, to[m], lo[m], hi[m]);
 }
 
 template <bool S32, bool D32>
@@ -88,7 +101,7 @@ hipError_t launch_typed(int direction, const void* src, void* dst, int64_t strid
   const uint32_t N = static_cast<uint32_t>(F) * H * W;
   const uint32_t cpr = static_cast<uint32_t>(d / 8);
   const uint64_t threads = static_cast<uint64_t>(N) * cpr;
-  dim3 grid(static_cast<uint32_t>((threads + kThreads - 1) / kThreads), G);
+  dim3 grid(static_cast<uint32_t>((threads + kThreads * kChunks - 1) / (kThreads * kChunks)), G);
   if (direction == 0)
     permute_kernel<S32, D32, true><<<grid, kThreads, 0, s>>>(src, dst, stride_g, stride_n, N, F,
                                                              H, W, cpr, orders);
