@@ -668,6 +668,41 @@ def test_int8_p_quantisation_error_bound(orc):
     assert np.max(np.abs(O8 - Oe)) > 0  # the quantisation does act
 
 
+def _read_golden_kv(name):
+    from fractions import Fraction
+
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            key, *rest = line.split()
+            vals[key] = [Fraction(x) for x in rest]
+    return vals
+
+
+def test_int8_p_tile_worked_example(orc):
+    """Hand-derived golden/int8_ptile_example.txt: two q-blocks over two
+    tiles each, with scores that make every unquantised Pt an exact power
+    of two.  The codes separate rint from floor, the tile maximum from a
+    fixed 1/127 scale, l over unquantised Pt from l over codes, and the
+    rescale when a row's maximum moves; O and LSE are exact rationals."""
+    g = _read_golden_kv("int8_ptile_example.txt")
+    N, d, Bq, Bk = (int(g[k][0]) for k in ("N", "d", "Bq", "Bk"))
+    arr = lambda k, dt: np.array([int(x) for x in g[k]], dt)
+    q8, k8, v8 = (arr(k, np.int8).reshape(1, N, d) for k in ("q8", "k8", "v8"))
+    sQ, sK, sV = (np.array([[float(x) for x in g[k]]], np.float32) for k in ("sQ", "sK", "sV"))
+    rp, ci = arr("row_ptr", np.int32), arr("col_idx", np.int32)
+    nq = N // Bq
+    blocks = np.array([(0, i) for i in range(nq)], np.int64)
+    O, L = orc.attention_int8(q8, sQ, k8, sK, v8, sV, Bq, Bk, rp, ci, blocks,
+                              sm_scale=math.log(2.0))
+    want_o = np.array([float(x) for x in g["O"]])
+    want_l = np.array([math.log(float(x)) for x in g["expLSE"]])
+    assert np.allclose(O.reshape(-1), want_o, rtol=1e-14, atol=0)
+    assert np.allclose(L.reshape(-1), want_l, rtol=1e-14, atol=0)
+
+
 # ------------------------------------------------- offline calibration (PARO)
 def _bf16_pair(seed, G, N, d, scale=1.0):
     r = rng(seed)
