@@ -420,8 +420,15 @@ def mask_from_bits(bits, nk, workspace=None):
 def quantize_int8(Xp, B, out=None):
     """bsa_quantize_int8: bf16 [G][N][d] -> (int8 [G][N][d], fp32 scales
     [G][ceil(N/B)]); ``out`` = (q, scale) reuses preallocated tensors."""
-    _dev(Xp)
+    if Xp.dim() != 3 or Xp.dtype != torch.bfloat16 or not Xp.is_contiguous():
+        raise ValueError("Xp must be contiguous bf16 [G][N][d]")
     G, N, d = Xp.shape
+    if out is not None:
+        q, s = out
+        if (q.dtype != torch.int8 or tuple(q.shape) != (G, N, d) or not q.is_contiguous()
+                or s.dtype != torch.float32 or not s.is_contiguous() or s.numel() < G * -(-N // B)):
+            raise ValueError("out must be (int8 [G][N][d], fp32 [G][ceil(N/B)]), contiguous")
+    _dev(Xp, *(out or ()))
     if out is None:
         q = torch.empty((G, N, d), dtype=torch.int8, device=Xp.device)
         s = torch.empty((G, (N + B - 1) // B), dtype=torch.float32, device=Xp.device)
@@ -431,20 +438,80 @@ def quantize_int8(Xp, B, out=None):
     return q, s
 
 
+def _attn_inputs(Q, K, V, row_ptr, col_idx, Bq, Bk, mask_G, col_len, dtype, scales=None):
+    """Host checks of a forward's inputs that the C ABI cannot make (it sees
+    raw pointers): shapes, dtypes, contiguity and lengths, so that no kernel
+    reads past an allocation.  Returns (G, N, d, mask_G, col_len)."""
+    if Q.dim() != 3:
+        raise ValueError("Q must be [G][N][d]")
+    G, N, d = Q.shape
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}")
+        if tuple(t.shape) != (G, N, d):
+            raise ValueError(f"{name} must have Q's shape {(G, N, d)}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [G][N][d]")
+    if Bq not in (64, 128) or Bk not in (64, 128):
+        raise ValueError("Bq and Bk must be 64 or 128")
+    nq, nk = -(-N // Bq), -(-N // Bk)
+    mask_G = G if mask_G is None else int(mask_G)
+    if not 1 <= mask_G <= G:
+        raise ValueError("mask_G must be in [1, G]")
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-D int32 tensor")
+    if row_ptr.numel() < mask_G * nq + 1:
+        raise ValueError(f"row_ptr needs mask_G*Nq + 1 = {mask_G * nq + 1} entries "
+                         f"(Bq = {Bq}), got {row_ptr.numel()}")
+    col_len = col_idx.numel() if col_len is None else int(col_len)
+    if not 0 <= col_len <= col_idx.numel():
+        raise ValueError("col_len must be in [0, col_idx.numel()]")
+    if scales is not None:
+        for name, t, n in zip(("sQ", "sK", "sV"), scales, (G * nq, G * nk, G * nk)):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < n:
+                raise ValueError(f"{name} must be contiguous fp32 with at least {n} entries")
+    return G, N, d, mask_G, col_len
+
+
+def _check_lse(lse, G, N):
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.numel() != G * N):
+        raise ValueError("lse must be contiguous fp32 with G*N entries")
+
+
+def _lse_out(lse, want_lse, G, N, dev):
+    if lse is None and want_lse:
+        lse = torch.empty((G, N), dtype=torch.float32, device=dev)
+    return lse
+
+
+def _check_reordered_out(out, G, N, d):
+    if out is not None and (tuple(out.shape) != (G, N, d) or out.dtype != torch.bfloat16
+                            or not out.is_contiguous()):
+        raise ValueError("out must be contiguous bf16 [G][N][d]")
+
+
+def _reordered_out(out, G, N, d, dev):
+    if out is None:
+        out = torch.empty((G, N, d), dtype=torch.bfloat16, device=dev)
+    return out
+
+
 def forward(Qp, Kp, Vp, row_ptr, col_idx, Bq, Bk, mask_G=None, sm_scale=0.0, out=None,
             lse=None, want_lse=True, col_len=None):
     """bsa_forward: bf16 block-sparse attention on reordered tensors.
     Returns (O bf16 [G][N][d], lse fp32 [G][N] or None)."""
-    _dev(Qp, Kp, Vp, row_ptr, col_idx)
-    G, N, d = Qp.shape
-    if out is None:
-        out = torch.empty_like(Qp)
-    if lse is None and want_lse:
-        lse = torch.empty((G, N), dtype=torch.float32, device=Qp.device)
+    G, N, d, mask_G, col_len = _attn_inputs(Qp, Kp, Vp, row_ptr, col_idx, Bq, Bk, mask_G, col_len,
+                                            torch.bfloat16)
+    _check_reordered_out(out, G, N, d)
+    _check_lse(lse, G, N)
+    _dev(Qp, Kp, Vp, row_ptr, col_idx, out, lse)
+    out = _reordered_out(out, G, N, d, Qp.device)
+    lse = _lse_out(lse, want_lse, G, N, Qp.device)
     rc = _lib.load().bsa_forward(_ptr(Qp), _ptr(Kp), _ptr(Vp), _ptr(row_ptr), _ptr(col_idx),
-                                 col_idx.numel() if col_len is None else col_len,
-                                 G if mask_G is None else mask_G, _ptr(out), _ptr(lse), G, N, d, Bq,
-                                 Bk, float(sm_scale), _stream())
+                                 col_len, mask_G, _ptr(out), _ptr(lse), G, N, d, Bq, Bk,
+                                 float(sm_scale), _stream())
     check(rc)
     return out, lse
 
@@ -452,26 +519,34 @@ def forward(Qp, Kp, Vp, row_ptr, col_idx, Bq, Bk, mask_G=None, sm_scale=0.0, out
 def forward_int8(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, Bq, Bk, mask_G=None, sm_scale=0.0,
                  out=None, lse=None, want_lse=True, col_len=None):
     """bsa_forward_int8 on int8 reordered tensors with per-block scales."""
-    _dev(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx)
-    G, N, d = Qq.shape
-    if out is None:
-        out = torch.empty((G, N, d), dtype=torch.bfloat16, device=Qq.device)
-    if lse is None and want_lse:
-        lse = torch.empty((G, N), dtype=torch.float32, device=Qq.device)
+    G, N, d, mask_G, col_len = _attn_inputs(Qq, Kq, Vq, row_ptr, col_idx, Bq, Bk, mask_G, col_len,
+                                            torch.int8, (sQ, sK, sV))
+    _check_reordered_out(out, G, N, d)
+    _check_lse(lse, G, N)
+    _dev(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, out, lse)
+    out = _reordered_out(out, G, N, d, Qq.device)
+    lse = _lse_out(lse, want_lse, G, N, Qq.device)
     rc = _lib.load().bsa_forward_int8(_ptr(Qq), _ptr(sQ), _ptr(Kq), _ptr(sK), _ptr(Vq), _ptr(sV),
-                                      _ptr(row_ptr), _ptr(col_idx),
-                                      col_idx.numel() if col_len is None else col_len,
-                                      G if mask_G is None else mask_G, _ptr(out), _ptr(lse), G, N,
-                                      d, Bq, Bk, float(sm_scale), _stream())
+                                      _ptr(row_ptr), _ptr(col_idx), col_len, mask_G, _ptr(out),
+                                      _ptr(lse), G, N, d, Bq, Bk, float(sm_scale), _stream())
     check(rc)
     return out, lse
+
+
+def _orders_ok(axis_order, G):
+    if axis_order.dtype != torch.uint8 or axis_order.numel() < G:
+        raise ValueError("axis_order must be a uint8 tensor with G entries")
+
+
+def _check_natural_out(out, G, N, d):
+    if out is not None and (out.dim() != 3 or out.shape != (N, G, d) or out.stride(2) != 1
+                            or out.dtype != torch.bfloat16):
+        raise ValueError("out must be bf16 [N][G][d] (any strides with unit channel stride)")
 
 
 def _natural_out(out, G, N, d, dev):
     if out is None:
         out = torch.empty((N, G, d), dtype=torch.bfloat16, device=dev)
-    if out.dim() != 3 or out.shape != (N, G, d) or out.stride(2) != 1 or out.dtype != torch.bfloat16:
-        raise ValueError("out must be bf16 [N][G][d] (any strides with unit channel stride)")
     return out
 
 
@@ -480,18 +555,20 @@ def forward_natural(Qp, Kp, Vp, row_ptr, col_idx, Bq, Bk, axis_order, F, H, W, m
     """bsa_forward_natural: bsa_forward with the inverse reorder fused into
     its epilogue.  Returns (O bf16 natural [N][G][d] (``out`` may be a
     strided view), lse fp32 [G][N] by natural token or None)."""
-    _dev(Qp, Kp, Vp, row_ptr, col_idx, axis_order)
-    G, N, d = Qp.shape
+    G, N, d, mask_G, col_len = _attn_inputs(Qp, Kp, Vp, row_ptr, col_idx, Bq, Bk, mask_G, col_len,
+                                            torch.bfloat16)
     if N != F * H * W:
         raise ValueError("N must equal F*H*W")
+    _orders_ok(axis_order, G)
+    _check_natural_out(out, G, N, d)
+    _check_lse(lse, G, N)
+    _dev(Qp, Kp, Vp, row_ptr, col_idx, axis_order, out, lse)
     out = _natural_out(out, G, N, d, Qp.device)
-    if lse is None and want_lse:
-        lse = torch.empty((G, N), dtype=torch.float32, device=Qp.device)
+    lse = _lse_out(lse, want_lse, G, N, Qp.device)
     rc = _lib.load().bsa_forward_natural(_ptr(Qp), _ptr(Kp), _ptr(Vp), _ptr(row_ptr), _ptr(col_idx),
-                                         col_idx.numel() if col_len is None else col_len,
-                                         G if mask_G is None else mask_G, _ptr(axis_order), F, H, W,
-                                         _ptr(out), out.stride(1), out.stride(0), _ptr(lse), G, d, Bq,
-                                         Bk, float(sm_scale), _stream())
+                                         col_len, mask_G, _ptr(axis_order), F, H, W, _ptr(out),
+                                         out.stride(1), out.stride(0), _ptr(lse), G, d, Bq, Bk,
+                                         float(sm_scale), _stream())
     check(rc)
     return out, lse
 
@@ -500,18 +577,20 @@ def forward_int8_natural(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, Bq, Bk, axis_
                          mask_G=None, sm_scale=0.0, out=None, lse=None, want_lse=True,
                          col_len=None):
     """bsa_forward_int8_natural: bsa_forward_int8 writing O in natural order."""
-    _dev(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, axis_order)
-    G, N, d = Qq.shape
+    G, N, d, mask_G, col_len = _attn_inputs(Qq, Kq, Vq, row_ptr, col_idx, Bq, Bk, mask_G, col_len,
+                                            torch.int8, (sQ, sK, sV))
     if N != F * H * W:
         raise ValueError("N must equal F*H*W")
+    _orders_ok(axis_order, G)
+    _check_natural_out(out, G, N, d)
+    _check_lse(lse, G, N)
+    _dev(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, axis_order, out, lse)
     out = _natural_out(out, G, N, d, Qq.device)
-    if lse is None and want_lse:
-        lse = torch.empty((G, N), dtype=torch.float32, device=Qq.device)
+    lse = _lse_out(lse, want_lse, G, N, Qq.device)
     rc = _lib.load().bsa_forward_int8_natural(
         _ptr(Qq), _ptr(sQ), _ptr(Kq), _ptr(sK), _ptr(Vq), _ptr(sV), _ptr(row_ptr), _ptr(col_idx),
-        col_idx.numel() if col_len is None else col_len, G if mask_G is None else mask_G,
-        _ptr(axis_order), F, H, W, _ptr(out), out.stride(1), out.stride(0), _ptr(lse), G, d, Bq, Bk,
-        float(sm_scale), _stream())
+        col_len, mask_G, _ptr(axis_order), F, H, W, _ptr(out), out.stride(1), out.stride(0),
+        _ptr(lse), G, d, Bq, Bk, float(sm_scale), _stream())
     check(rc)
     return out, lse
 

@@ -58,6 +58,10 @@ constexpr float kLog2_127 = 6.988684686772166f;
 constexpr int kSBias = 0x4B400000;
 constexpr float kSBiasF = 12582912.0f;
 constexpr float kRefInit = -1.0e30f;  // running maximum before any score: finite, below all
+// Largest score scale f (log2 units per integer score unit) for the biased
+// exponent: bias*f < 1.5*2^12, so the folded offset is rounded by at most
+// 2^-12 (log2 units) and y = Pt*127/mP stays below 127.02 (code <= 127).
+constexpr float kNarrowF = 0x1p-11f;
 // 32-row halves per wave: one, so a 128-row q-block is four waves and two
 // workgroups give every SIMD two waves whose products and softmax interleave
 constexpr int kQB = 1;
@@ -213,7 +217,12 @@ __device__ __forceinline__ float rows_max(float x) {
 // of Pt), l = l * alpha + sum Pt.  The exponential argument folds the
 // quantisation scale in: y = Pt * 127 / mP = 2^(x - m - dm + log2 127).
 // MASK: columns outside the tile and a tile without real rows give zero.
-template <bool MASK, int NB>
+// WIDE: a score scale f above kNarrowF, where the biased fp32 score would
+// lose too many bits of the offset bias*f (an exponent error of ulp(bias*f)/2
+// could lift the tile maximum's y past 127.5 and its code to 128, which the
+// signed MFMA reads as -128); the integer score is converted exactly instead,
+// and y is clamped to 127 so the code stays in [0, 127] for any input.
+template <bool MASK, bool WIDE, int NB>
 __device__ __forceinline__ void quantize_tile(const i32x16 (&s)[kQB][NB], float f, const float (&m)[kQB],
                                               float dm, bool any, int kv0, bool jvalid, int N,
                                               float mp127, const float (&alpha)[kQB], float (&l)[kQB],
@@ -221,9 +230,11 @@ __device__ __forceinline__ void quantize_tile(const i32x16 (&s)[kQB][NB], float 
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++) {
-    // exponent (q8.k8) * f - off, with the score read as biased fp32:
-    // fma(score, f, -(off + bias * f)), one rounding of the folded offset
-    const float off = __builtin_fmaf(kSBiasF, f, any ? m[qb] + dm - kLog2_127 : 0.0f);
+    // exponent (q8.k8) * f - off.  Narrow: the score read as biased fp32,
+    // fma(score, f, -(off + bias * f)), one rounding of the folded offset.
+    // Wide: fma(float(q8.k8), f, -off), the integer converted exactly.
+    const float off0 = any ? m[qb] + dm - kLog2_127 : 0.0f;
+    const float off = WIDE ? off0 : __builtin_fmaf(kSBiasF, f, off0);
     float ys = 0.0f;
 #pragma unroll
     for (int b = 0; b < NB; b++)
@@ -233,7 +244,14 @@ __device__ __forceinline__ void quantize_tile(const i32x16 (&s)[kQB][NB], float 
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int r = 4 * q4 + e;
-          float y = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[qb][b][r]), f, -off));
+          float y;
+          if constexpr (WIDE) {
+            y = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(static_cast<float>(s[qb][b][r] - kSBias), f, -off));
+            y = fminf(y, 127.0f);
+          } else {
+            y = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[qb][b][r]), f, -off));
+          }
           if constexpr (MASK) {
             const int kv = kv0 + 32 * b + acc_row(r, h);
             if (!any || !jvalid || kv >= N) y = 0.0f;
@@ -376,10 +394,12 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
       i32x4 pf[kQB][NB];
       // masked columns (ragged tail, invalid block) and a tile without real
       // rows take the checked variant
-      if (masked || !any)
-        quantize_tile<true>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
+      if (f > kNarrowF)
+        quantize_tile<true, true>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
+      else if (masked || !any)
+        quantize_tile<true, false>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
       else
-        quantize_tile<false>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
+        quantize_tile<false, false>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
 
       // ---- O = O * alpha + (mP/127) sV_j (P8 . V8), one channel block at a time
       const float cv = mp127 * svj;

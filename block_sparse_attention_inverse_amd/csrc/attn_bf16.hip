@@ -70,13 +70,7 @@ constexpr int KT = 64;                  // kv rows per staged sub-tile
 constexpr float kSumBound = 0x1p96f;    // half-tile row sum that flags overflow
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-#ifndef BSA_PF
-#define BSA_PF 4
-#endif
-constexpr int kPf = BSA_PF;             // LDS operand prefetch distance (operands)
-#ifndef BSA_QSCALE
-#define BSA_QSCALE 0
-#endif
+constexpr int kPf = 4;                  // LDS operand prefetch distance (operands)
 
 template <int D, int NW>
 struct Ly {
@@ -286,12 +280,7 @@ struct Ex {
 __device__ __forceinline__ void exp_issue(const f32x16 (&s)[2], int e, Ex& ex, float cs) {
   const int qb = e >> 4, r = e & 15;
   float x;
-#if BSA_QSCALE
-  (void)cs;
-  asm volatile("v_exp_f32 %0, %1" : "=v"(x) : "v"(s[qb][r]));
-#else
   asm volatile("v_mul_f32 %0, %2, %1\n\tv_exp_f32 %0, %0" : "=&v"(x) : "v"(s[qb][r]), "s"(cs));
-#endif
   ex.y[e & 3] = x;
 }
 __device__ __forceinline__ void exp_retire(int e, Ex& ex, float (&sum)[2], u32x4 (&p)[2][2]) {
@@ -424,10 +413,9 @@ __device__ __forceinline__ void row_max(const f32x16 (&s)[2], float (&mx)[2]) {
 }
 
 // Q fragments of the wave's rows qbase + 32qb + l32 (rows past N read as
-// zero); k-step ks holds channels 16ks + 8h .. +7.  With BSA_QSCALE the
-// fragments are pre-scaled by c (bf16, round to nearest).
+// zero); k-step ks holds channels 16ks + 8h .. +7.
 template <int D>
-__device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, int g, int N, int qbase, float c,
+__device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, int g, int N, int qbase,
                                        bf16x8 (&qf)[2][D / 16]) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
 #pragma unroll
@@ -439,10 +427,7 @@ __device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, int g, in
     for (int ks = 0; ks < D / 16; ks++) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (ok) v = *reinterpret_cast<const uint4*>(qp + 16 * ks);
-      const bf16x8 raw = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-      for (int e = 0; e < 8; e++)
-        qf[qb][ks][e] = BSA_QSCALE ? static_cast<__bf16>(static_cast<float>(raw[e]) * c) : raw[e];
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, v);
       asm volatile("" : "+a"(qf[qb][ks]));  // held in AGPRs: only MFMAs read it
     }
   }
@@ -475,7 +460,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
   ad.init();
 
   bf16x8 qf[2][D / 16];
-  load_q<D>(Q, g, N, qbase, c, qf);
+  load_q<D>(Q, g, N, qbase, qf);
 
   const int64_t rbase = static_cast<int64_t>(g % mask_G) * nq + i;
   int64_t e0 = row_ptr[rbase], e1 = row_ptr[rbase + 1];
@@ -614,7 +599,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
   if (ovf) {
     // Exact path, one sub-tile at a time: the row maxima over every kept
     // column, then O and l against them (every score <= 0).
-    load_q<D>(Q, g, N, qbase, c, qf);
+    load_q<D>(Q, g, N, qbase, qf);
     f32x16 sA[2];
     u32x4 pA[2][2];
     float mx[2] = {-INFINITY, -INFINITY};
@@ -690,7 +675,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
           *reinterpret_cast<uint2*>(op + d0) = pk;
         }
       if (lse != nullptr && h == 0)
-        lse[li] = lt > 0.0f ? (BSA_QSCALE ? m[qb] : m[qb] * c) * kLn2 + logf(lt) : -INFINITY;
+        lse[li] = lt > 0.0f ? m[qb] * c * kLn2 + logf(lt) : -INFINITY;
     }
   }
 }

@@ -104,9 +104,12 @@ int natural_out(const uint8_t* axis_order, int32_t F, int32_t H, int32_t W, int3
   return BSA_OK;
 }
 
+// elem: bytes per K / V element (2 bf16, 1 int8).  The kernels address one
+// head's K and V through 32-bit buffer resources, so N*d*elem must stay
+// below 2^31.
 int attn_common(const void* Q, const void* K, const void* V, const int32_t* row_ptr,
                 const int32_t* col_idx, int64_t col_len, int32_t mask_G, void* Op, int32_t G,
-                int32_t N, int32_t d, int32_t Bq, int32_t Bk) {
+                int32_t N, int32_t d, int32_t Bq, int32_t Bk, int elem) {
   if (!Q || !K || !V || !row_ptr || !Op) return fail(BSA_EINVAL, "NULL tensor pointer");
   if (col_len < 0 || (col_len > 0 && !col_idx)) return fail(BSA_EINVAL, "bad col_idx / col_len");
   if (G <= 0 || N <= 0) return fail(BSA_EINVAL, "G and N must be positive");
@@ -118,6 +121,9 @@ int attn_common(const void* Q, const void* K, const void* V, const int32_t* row_
   const int64_t nq = (static_cast<int64_t>(N) + Bq - 1) / Bq;
   if (static_cast<int64_t>(G) * nq >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "grid too large");
   if (static_cast<int64_t>(G) * N * d >= (1ll << 40)) return fail(BSA_EUNSUPPORTED, "tensor too large");
+  if (static_cast<int64_t>(N) * d * elem >= (1ll << 31))
+    return fail(BSA_EUNSUPPORTED, "one head's K/V must be < 2^31 bytes (N*d*%d = %lld)", elem,
+                static_cast<long long>(N) * d * elem);
   return BSA_OK;
 }
 
@@ -323,7 +329,7 @@ int bsa_forward(const void* Qp, const void* Kp, const void* Vp, const int32_t* r
                 int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk, float sm_scale,
                 void* stream) {
   return guarded([&]() -> int {
-    const int rc = attn_common(Qp, Kp, Vp, row_ptr, col_idx, col_len, mask_G, Op, G, N, d, Bq, Bk);
+    const int rc = attn_common(Qp, Kp, Vp, row_ptr, col_idx, col_len, mask_G, Op, G, N, d, Bq, Bk, 2);
     if (rc != BSA_OK) return rc;
     if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");
     bsa::AttnArgs a{};
@@ -341,7 +347,7 @@ int bsa_forward_int8(const int8_t* Qq, const float* sQ, const int8_t* Kq, const 
                      int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk, float sm_scale,
                      void* stream) {
   return guarded([&]() -> int {
-    const int rc = attn_common(Qq, Kq, Vq, row_ptr, col_idx, col_len, mask_G, Op, G, N, d, Bq, Bk);
+    const int rc = attn_common(Qq, Kq, Vq, row_ptr, col_idx, col_len, mask_G, Op, G, N, d, Bq, Bk, 1);
     if (rc != BSA_OK) return rc;
     if (!sQ || !sK || !sV) return fail(BSA_EINVAL, "NULL scale pointer");
     if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");
@@ -570,7 +576,7 @@ int bsa_forward_natural(const void* Qp, const void* Kp, const void* Vp, const in
     int32_t N = 0;
     int rc = natural_out(axis_order, F, H, W, G, d, nat_stride_g, nat_stride_n, a.out, N);
     if (rc != BSA_OK) return rc;
-    rc = attn_common(Qp, Kp, Vp, row_ptr, col_idx, col_len, mask_G, O, G, N, d, Bq, Bk);
+    rc = attn_common(Qp, Kp, Vp, row_ptr, col_idx, col_len, mask_G, O, G, N, d, Bq, Bk, 2);
     if (rc != BSA_OK) return rc;
     if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");
     a.Q = Qp; a.K = Kp; a.V = Vp;
@@ -592,7 +598,7 @@ int bsa_forward_int8_natural(const int8_t* Qq, const float* sQ, const int8_t* Kq
     int32_t N = 0;
     int rc = natural_out(axis_order, F, H, W, G, d, nat_stride_g, nat_stride_n, a.out, N);
     if (rc != BSA_OK) return rc;
-    rc = attn_common(Qq, Kq, Vq, row_ptr, col_idx, col_len, mask_G, O, G, N, d, Bq, Bk);
+    rc = attn_common(Qq, Kq, Vq, row_ptr, col_idx, col_len, mask_G, O, G, N, d, Bq, Bk, 1);
     if (rc != BSA_OK) return rc;
     if (!sQ || !sK || !sV) return fail(BSA_EINVAL, "NULL scale pointer");
     if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");

@@ -377,12 +377,35 @@ __global__ __launch_bounds__(kSelThreads) void scores_kernel(
 // index ascending) as 64-bit images (~order bits : index) with a bitonic
 // sort in LDS.  The row keeps the first k* of that order:
 //   SEL_TOPK  k* = k;
-//   SEL_TOPP  weights w = exp2f((key'_p - key'_0) * temp), fp32 running sums
+//   SEL_TOPP  weights w = exp2_fixed((key'_p - key'_0) * temp), fp32 running sums
 //             P_p in sorted order (one lane), k* = the first p with
 //             P_p >= frac * P_last (plus one);
 //   SEL_MASS  the same with w = key' itself (keys not > 0 taken as +0);
 // plus the forced set (diagonal overlap, temporal window) of select_kernel.
 enum { SEL_TOPK = 0, SEL_TOPP = 1, SEL_MASS = 2 };
+
+// 2^a as a fixed fp32 sequence (the Top-P weights are defined by it, so the
+// selection is reproducible bit for bit): n = rint(a), f = a - n (exact),
+// 2^f by its degree-7 Taylor polynomial in f ln 2 (coefficients (ln 2)^k/k!
+// to the nearest fp32) with one fma per coefficient, highest first, times
+// 2^n built from its exponent bits (exact: the result is normal).  Below
+// -125: +0; above 127: +inf; NaN stays NaN.
+__device__ __forceinline__ float exp2_fixed(float a) {
+  if (a != a) return a;
+  if (a < -125.0f) return 0.0f;
+  if (a > 127.0f) return INFINITY;
+  const float n = __builtin_rintf(a);
+  const float f = a - n;
+  float p = 0x1.ffcbfcp-17f;
+  p = __builtin_fmaf(p, f, 0x1.430912p-13f);
+  p = __builtin_fmaf(p, f, 0x1.5d87fep-10f);
+  p = __builtin_fmaf(p, f, 0x1.3b2ab6p-7f);
+  p = __builtin_fmaf(p, f, 0x1.c6b08ep-5f);
+  p = __builtin_fmaf(p, f, 0x1.ebfbep-3f);
+  p = __builtin_fmaf(p, f, 0x1.62e43p-1f);
+  p = __builtin_fmaf(p, f, 1.0f);
+  return p * __uint_as_float(static_cast<uint32_t>(static_cast<int>(n) + 127) << 23);
+}
 
 __device__ __forceinline__ float key_from_order_bits(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
@@ -436,7 +459,7 @@ __global__ __launch_bounds__(kSelThreads) void sorted_select_kernel(
     const float top = key_from_order_bits(~static_cast<uint32_t>(srt[0] >> 32));
     for (int p = t; p < nk; p += kSelThreads) {
       const float x = key_from_order_bits(~static_cast<uint32_t>(srt[p] >> 32));
-      pre[p] = MODE == SEL_MASS ? x : exp2f((x - top) * temp);
+      pre[p] = MODE == SEL_MASS ? x : exp2_fixed((x - top) * temp);
     }
     __syncthreads();
     if (t == 0) {

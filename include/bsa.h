@@ -233,8 +233,10 @@ int bsa_quantize_int8(const void *Xp, int8_t *Xq, float *scale, int32_t G, int32
  * visited in CSR order; entries outside [0, Nkv) are skipped, and CSR
  * offsets are clamped to [0, col_len).  An empty row gives O = 0 and
  * lse = -inf.  sm_scale <= 0 selects 1/sqrt(d).  Rows past N are never
- * written.  d in {64, 128}; (Bq, Bk) in {64,128} x {64,128}.
- * Errors: EINVAL, EUNSUPPORTED, EHIP. */
+ * written.  d in {64, 128}; (Bq, Bk) in {64,128} x {64,128}.  Limits: one
+ * head's K (and V) must be < 2^31 bytes, N*d*2 < 2^31 (N < 8388608 at
+ * d = 128); G*Nq < 2^31; G*N*d < 2^40.  Beyond them: EUNSUPPORTED, nothing
+ * launched.  Errors: EINVAL, EUNSUPPORTED, EHIP. */
 int bsa_forward(const void *Qp, const void *Kp, const void *Vp, const int32_t *row_ptr,
                 const int32_t *col_idx, int64_t col_len, int32_t mask_G, void *Op, float *lse,
                 int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk, float sm_scale,
@@ -251,7 +253,8 @@ int bsa_forward(const void *Qp, const void *Kp, const void *Vp, const int32_t *r
  *   Pt is quantised per tile: mP = max of Pt over the tile's real rows and
  *   columns, P8 = rint(Pt*127/mP) in [0, 127], sP = mP/127;
  *   acc = acc*exp(m - m') + sP*sV_j*(P8.v8) with an exact integer product.
- * Outputs as bsa_forward.  Errors: EINVAL, EUNSUPPORTED, EHIP. */
+ * Outputs as bsa_forward.  Limits as bsa_forward with one byte per element:
+ * N*d < 2^31.  Errors: EINVAL, EUNSUPPORTED, EHIP. */
 int bsa_forward_int8(const int8_t *Qq, const float *sQ, const int8_t *Kq, const float *sK,
                      const int8_t *Vq, const float *sV, const int32_t *row_ptr,
                      const int32_t *col_idx, int64_t col_len, int32_t mask_G, void *Op, float *lse,

@@ -58,6 +58,7 @@ def _load():
                                          _P, _P]),
         "oracle_paro_metric": (_I, [_P, _P, _P, _I, _L, _I, _I, _I, _D, _P]),
         "oracle_mass_select": (_I, [_P, _I, _L, _I, _I, ctypes.c_float, _I, _P, _P, _L, _P]),
+        "oracle_exp2_fixed": (ctypes.c_float, [ctypes.c_float]),
         "oracle_perturb_keys": (None, [_P, _P, ctypes.c_float, _L, _P]),
         "oracle_select_topp": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_float, ctypes.c_float,
                                     _I, _I, _I, _P, _P, _L, _P, _P, _P]),
@@ -345,6 +346,11 @@ def perturb_keys(keys, noise, scale):
     nz = None if noise is None else np.ascontiguousarray(noise, dtype=np.float32)
     _load().oracle_perturb_keys(_ptr(keys), _ptr(nz), ctypes.c_float(scale), keys.size, _ptr(out))
     return out
+
+
+def exp2_fixed(a: float) -> float:
+    """The fixed fp32 2^a that defines the Top-P weights (one fp32 value)."""
+    return float(_load().oracle_exp2_fixed(float(np.float32(a))))
 
 
 def select_topp(keys, G, F, H, W, Bq, Bk, orders, top_p, temp, force_diag=1, win_T=-1, win_r0=0):

@@ -341,12 +341,39 @@ void oracle_perturb_keys(const float *keys, const float *noise, float scale, int
 }
 
 /* ------------------------------------------------------------------------
+ * 2^a as a fixed fp32 operation sequence (the Top-P weights are defined by
+ * it, so that the selection does not hang on a library's exp2f).  Range
+ * reduction to the nearest integer exponent, as in Cody and Waite's
+ * exponential (exact here, the argument being in base 2): n = rint(a),
+ * f = a - n in [-1/2, 1/2].  Then 2^f = e^(f ln 2) by its Taylor series to
+ * degree 7, c_k = (ln 2)^k / k! rounded to fp32 (truncation error below
+ * 1e-8 on the interval), evaluated by Horner's rule with one fmaf per
+ * coefficient, highest first; the result p * 2^n is exact (a normal number
+ * for -125 <= a <= 127).  a < -125 gives +0, a > 127 +inf, NaN stays NaN.
+ * ---------------------------------------------------------------------- */
+float oracle_exp2_fixed(float a) {
+  if (a != a) return a;
+  if (a < -125.0f) return 0.0f;
+  if (a > 127.0f) return INFINITY;
+  /* (ln 2)^k / k!, k = 0..7, each the nearest fp32 */
+  static const float c[8] = {0x1p+0f,        0x1.62e43p-1f,  0x1.ebfbep-3f,  0x1.c6b08ep-5f,
+                             0x1.3b2ab6p-7f, 0x1.5d87fep-10f, 0x1.430912p-13f, 0x1.ffcbfcp-17f};
+  const float n = rintf(a);
+  const float f = a - n;
+  float p = c[7];
+  for (int k = 6; k >= 0; k--) p = fmaf(p, f, c[k]);
+  union { uint32_t u; float x; } sc;
+  sc.u = (uint32_t)((int32_t)n + 127) << 23;
+  return p * sc.x;
+}
+
+/* ------------------------------------------------------------------------
  * Top-P selection.  [SPADE] key machinery: the kept blocks pass a
  * head-wise Top-K / Top-P filter.  Reading taken here: per q-block row, the
  * kv-blocks in (key descending, index ascending) order carry the weights
- * w_p = exp2((key_p - key_0) * temp) (fp32: one subtract, one multiply,
- * exp2f), i.e. the softmax of the block scores at inverse temperature
- * temp (log2 units); P_k = fp32 running sum of the first k weights;
+ * w_p = 2^((key_p - key_0) * temp) (fp32: one subtract, one multiply,
+ * oracle_exp2_fixed), i.e. the softmax of the block scores at inverse
+ * temperature temp (log2 units); P_k = fp32 running sum of the first k weights;
  * t = P_nk * top_p; k* = the smallest k >= 1 with P_k >= t.  The row keeps
  * those k* blocks plus the forced set (diagonal, window) of oracle_select.
  * Also writes kstar[row] (may be NULL) and, for a tolerance check of a
@@ -381,7 +408,7 @@ int oracle_select_topp(const float *keys, int G, int F, int H, int W, int Bq, in
       double c64 = 0.0;
       for (int64_t t = 0; t < nk; t++) {
         const float dlt = krow[idx[t]] - top;
-        total += exp2f(dlt * temp);
+        total += oracle_exp2_fixed(dlt * temp);
         c64 += exp2((double)dlt * (double)temp);
         if (cum) cum[row * nk + t] = c64;
       }
@@ -389,7 +416,7 @@ int oracle_select_topp(const float *keys, int G, int F, int H, int W, int Bq, in
       int64_t ks = nk;
       float run = 0.0f;
       for (int64_t t = 0; t < nk; t++) {
-        run += exp2f((krow[idx[t]] - top) * temp);
+        run += oracle_exp2_fixed((krow[idx[t]] - top) * temp);
         if (run >= thr) { ks = t + 1; break; }
       }
       if (kstar) kstar[row] = (int32_t)ks;

@@ -260,3 +260,71 @@ def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):
         bsa.abi_version()
     with pytest.raises(ImportError):
         bsa.mask_capacity(1, 2, 8, 8, bsa.mask_params())
+
+
+def test_forward_rejects_heads_too_long_for_32_bit_addressing(lib):
+    """One head's K / V is addressed through 32-bit buffer resources: a head
+    of 2^31 bytes or more is refused before any launch (bf16: N*d*2, INT8:
+    N*d)."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    F = ctypes.c_float
+    N = 1 << 23  # N*128*2 = 2^31 bytes per bf16 head
+    assert lib.bsa_forward(fake, fake, fake, fake, fake, 10, 1, fake, None, 1, N, 128, 128, 64,
+                           F(0), None) == -2
+    assert b"2^31 bytes" in lib.bsa_last_error()
+    assert lib.bsa_forward_int8(fake, fake, fake, fake, fake, fake, fake, fake, 10, 1, fake, None, 1,
+                                2 * N, 128, 128, 64, F(0), None) == -2
+    assert b"2^31 bytes" in lib.bsa_last_error()
+    # natural-order output: the same limit with N = F*H*W
+    assert lib.bsa_forward_natural(fake, fake, fake, fake, fake, 10, 1, fake, 8, 1024, 1024, fake,
+                                   128, 128, None, 1, 128, 128, 64, F(0), None) == -2
+
+
+def test_forward_bindings_check_inputs_before_any_launch():
+    """The Python forwards refuse inputs the C ABI cannot see through raw
+    pointers (mismatched shapes, dtypes, strides, short row_ptr or scales)
+    with ValueError, before any device check or launch."""
+    import torch
+    import block_sparse_attention_inverse_amd as bsa
+
+    G, N, d, B = 2, 256, 64, 64
+    nq = N // B
+    Q = torch.zeros((G, N, d), dtype=torch.bfloat16)
+    rp = torch.zeros(G * nq + 1, dtype=torch.int32)
+    ci = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="shape"):
+        bsa.forward(Q, Q[:, :128], Q, rp, ci, B, B)
+    with pytest.raises(ValueError, match="bfloat16"):
+        bsa.forward(Q, Q.float(), Q, rp, ci, B, B)
+    with pytest.raises(ValueError, match="contiguous"):
+        bsa.forward(Q, Q, Q.transpose(0, 1).contiguous().transpose(0, 1), rp, ci, B, B)
+    with pytest.raises(ValueError, match="row_ptr needs"):
+        bsa.forward(Q, Q, Q, rp[:nq], ci, B, B)
+    with pytest.raises(ValueError, match="row_ptr needs"):  # a mask built with Bq = 128
+        bsa.forward(Q, Q, Q, torch.zeros(G * N // 128 + 1, dtype=torch.int32), ci, B, B)
+    with pytest.raises(ValueError, match="int32"):
+        bsa.forward(Q, Q, Q, rp.long(), ci, B, B)
+    with pytest.raises(ValueError, match="col_len"):
+        bsa.forward(Q, Q, Q, rp, ci, B, B, col_len=5)
+    with pytest.raises(ValueError, match="mask_G"):
+        bsa.forward(Q, Q, Q, rp, ci, B, B, mask_G=3)
+    with pytest.raises(ValueError, match="out must be"):
+        bsa.forward(Q, Q, Q, rp, ci, B, B, out=torch.zeros((G, N, d + 8), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU"):
+        bsa.forward(Q, Q, Q, rp, ci, B, B)
+    q8 = torch.zeros((G, N, d), dtype=torch.int8)
+    s = torch.zeros(G * nq, dtype=torch.float32)
+    with pytest.raises(ValueError, match="sK must be"):
+        bsa.forward_int8(q8, s, q8, s[:1], q8, s, rp, ci, B, B)
+    with pytest.raises(ValueError, match="int8"):
+        bsa.forward_int8(q8, s, Q, s, q8, s, rp, ci, B, B)
+    with pytest.raises(ValueError, match="GPU"):
+        bsa.forward_int8(q8, s, q8, s, q8, s, rp, ci, B, B)
+    orders = torch.zeros(G, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="F\\*H\\*W"):
+        bsa.forward_natural(Q, Q, Q, rp, ci, B, B, orders, 2, 2, 2)
+    with pytest.raises(ValueError, match="axis_order"):
+        bsa.forward_natural(Q, Q, Q, rp, ci, B, B, orders[:1], 4, 8, 8)
+    with pytest.raises(ValueError, match="Xp must be"):
+        bsa.quantize_int8(Q.float(), B)

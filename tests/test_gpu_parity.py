@@ -111,7 +111,7 @@ def sample_rows(cfg, orders, orc, n_rand, seed):
 
 
 # ------------------------------------------------------------ reordering
-@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_permute_bit_exact(bsa_gpu, orc, cid):
     c = case(cid)
     cfg = c["cfg"]
@@ -320,22 +320,23 @@ def test_forward_int8_2k(bsa_gpu, orc):
     _int8_parity(bsa_gpu, orc, c, rp, ci, blocks, "int8 cfg2")
 
 
-@pytest.mark.parametrize("cid", [3, 4])
-def test_forward_int8_full_size(bsa_gpu, orc, cid):
+@pytest.mark.parametrize("cid,rho,nb", [(3, None, 8), (4, None, 16), (4, (20, 100), 16)])
+def test_forward_int8_full_size(bsa_gpu, orc, cid, rho, nb):
     c = case(cid)
     cfg = c["cfg"]
     F, H, W = cfg["F"], cfg["H"], cfg["W"]
-    p = mask_params(bsa_gpu, cfg)
+    p = mask_params(bsa_gpu, cfg, rho)
     rp, ci = orc.build_mask(oracle_reorder(orc, c, "Q"), oracle_reorder(orc, c, "K"), F, H, W,
                             c["orders"], p.Bq, p.Bk, p.score, p.rho_num, p.rho_den, p.force_diag,
                             p.win_T, p.win_r0)
     nq = -(-cfg["N"] // cfg["Bq"])
     r = np.random.Generator(np.random.PCG64(c["seed"] + 11))
-    blocks = [(int(r.integers(cfg["G"])), int(r.integers(nq))) for _ in range(6)]
-    blocks += [(0, 0), (cfg["G"] - 1, nq - 1)]  # first and ragged last q-block
+    blocks = [(int(r.integers(cfg["G"])), int(r.integers(nq))) for _ in range(nb - 3)]
+    # first and ragged last q-block of the first and last head
+    blocks += [(0, 0), (0, nq - 1), (cfg["G"] - 1, nq - 1)]
     blocks = np.array(blocks, np.int64)
-    _say(f"[int8 cfg {cid}] {len(blocks)} sampled q-blocks")
-    _int8_parity(bsa_gpu, orc, c, rp, ci, blocks, f"int8 cfg{cid}")
+    _say(f"[int8 cfg {cid} rho={p.rho_num}/{p.rho_den}] {len(blocks)} sampled q-blocks")
+    _int8_parity(bsa_gpu, orc, c, rp, ci, blocks, f"int8 cfg{cid} rho={p.rho_num}")
 
 
 @pytest.mark.parametrize("d,Bq,Bk", [(128, 128, 64), (128, 128, 128), (64, 64, 64), (64, 128, 64),
@@ -483,13 +484,17 @@ def test_forward_mask_shared_across_heads(bsa_gpu, orc):
     Ow, Lw = orc.attention_rows(*host, G, F, H, W, d, np.zeros(G, np.uint8), rows, B, B, rp, ci,
                                 mask_G=mG)
     _compare(_np(Op.float())[rows[:, 0], rows[:, 1]], Ow, heads=rows[:, 0], tag="shared mask")
-    # INT8: the same sharing against the INT8 emulation
+    # INT8: the same sharing against the INT8 emulation (the oracle quantises
+    # the same bf16 inputs with its own quantiser)
     (qq, sq), (kq, sk), (vq, sv) = (bsa_gpu.quantize_int8(x, B) for x in (Qp, Kp, Vp))
     O8, _ = bsa_gpu.forward_int8(qq, sq, kq, sk, vq, sv, grp, gci, B, B, mask_G=mG)
     torch.cuda.synchronize()
     blocks = np.array([(g, i) for g in range(G) for i in range(nq)], np.int64)
-    W8, _ = orc.attention_int8(_np(qq), _np(sq), _np(kq), _np(sk), _np(vq), _np(sv), B, B, rp, ci,
-                               blocks, mask_G=mG)
+    # identity order: the reordered tensors are the natural ones, head-major
+    oq = [orc.quantize_int8(np.ascontiguousarray(h.reshape(N, G, d).transpose(1, 0, 2)), B)
+          for h in host]
+    W8, _ = orc.attention_int8(oq[0][0], oq[0][1], oq[1][0], oq[1][1], oq[2][0], oq[2][1], B, B,
+                               rp, ci, blocks, mask_G=mG)
     o8 = _np(O8.float())
     got8 = np.concatenate([o8[g, i * B:(i + 1) * B] for g, i in blocks])
     _compare(got8, W8.reshape(-1, d), tag="shared mask int8")
@@ -511,8 +516,10 @@ def test_forward_int8_short_sequences(bsa_gpu, orc, N, d, Bq, Bk):
                                  torch.from_numpy(ci).cuda(), Bq, Bk)
     torch.cuda.synchronize()
     blocks = np.array([(g, i) for g in range(G) for i in range(nq)], np.int64)
-    W8, _ = orc.attention_int8(_np(qq), _np(sq), _np(kq), _np(sk), _np(vq), _np(sv), Bq, Bk, rp, ci,
-                               blocks)
+    # the oracle quantises the same bf16 inputs with its own quantiser
+    oq = [orc.quantize_int8(_bits(t), B) for t, B in zip(x, (Bq, Bk, Bk))]
+    W8, _ = orc.attention_int8(oq[0][0], oq[0][1], oq[1][0], oq[1][1], oq[2][0], oq[2][1], Bq, Bk,
+                               rp, ci, blocks)
     o8 = _np(O8.float())
     got = np.concatenate([o8[g, i * Bq:min((i + 1) * Bq, N)] for g, i in blocks])
     want = np.concatenate([W8[t, :min(Bq, N - i * Bq)] for t, (g, i) in enumerate(blocks)])

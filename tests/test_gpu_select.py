@@ -2,12 +2,11 @@
 (with and without seeded noise perturbing the scores) and Top-P, through the
 C ABI against the CPU oracle on the same seeded inputs.
 
-Bars: scores and Top-K CSRs are outputs of a fixed fp32 sequence and match
-bit for bit.  Top-P decides its cut with an fp32 exponential, whose device
-and host implementations may round differently: rows must match the
-oracle's exactly except where the oracle's fp64 running weight at the cut
-lies within 1e-5 (relative) of the threshold, and such a row must still be
-a top-k' prefix (plus the forced set) for a k' next to the oracle's.
+Bars: scores, Top-K and Top-P CSRs are outputs of fixed fp32 sequences and
+match bit for bit.  Top-P weighs the sorted scores with a fixed fp32 2^x
+(range reduction to the nearest integer, a degree-7 Taylor polynomial by
+fma, an exact power-of-two scale) that the kernel and the oracle each
+implement, and adds the weights in sorted order on both sides.
 """
 import numpy as np
 import pytest
@@ -89,39 +88,19 @@ def test_topk_with_noise_bit_exact(bsa_gpu, orc, cid, scale):
 
 def _topp_compare(orc, got_rp, got_ci, keys, G, F, H, W, p, orders, top_p, temp, noise=None,
                   scale=0.0):
+    """Top-P CSR bit for bit: both sides weigh the sorted scores with the same
+    fixed fp32 2^x sequence and add the weights in the same order."""
     kp = keys if noise is None else orc.perturb_keys(keys, noise, scale)
     wrp, wci, kstar, cum = orc.select_topp(kp, G, F, H, W, p.Bq, p.Bk, orders, top_p, temp,
                                            p.force_diag, p.win_T, p.win_r0)
-    R = G * kp.shape[1]
-    nk = kp.shape[2]
-    bad = 0
-    for row in range(R):
-        got = got_ci[got_rp[row]:got_rp[row + 1]].tolist()
-        want = wci[wrp[row]:wrp[row + 1]].tolist()
-        if got == want:
-            continue
-        bad += 1
-        ks = int(kstar[row])
-        tot = cum[row, -1]
-        # a genuine near-tie at the cut: the oracle's fp64 running weight at
-        # k* - 1 or k* sits next to the threshold
-        near = [abs(cum[row, k - 1] / tot - top_p) < 1e-5 for k in (ks - 1, ks, ks + 1)
-                if 1 <= k <= nk]
-        assert any(near), f"row {row} differs away from the threshold"
-        ok = False
-        for k2 in (ks - 1, ks + 1):
-            if 1 <= k2 <= nk:
-                alt = orc.select(kp, G, F, H, W, p.Bq, p.Bk, orders, k2, nk, p.force_diag, p.win_T,
-                                 p.win_r0)
-                arp, aci = alt
-                ok = ok or got == aci[arp[row]:arp[row + 1]].tolist()
-        assert ok, f"row {row} is not a top-k prefix next to the oracle's cut"
-    assert bad <= max(2, R // 200)
+    assert np.array_equal(got_rp, wrp)
+    assert np.array_equal(got_ci, wci)
     return wrp, wci
 
 
-@pytest.mark.parametrize("cid,top_p,temp", [(2, 0.9, 1.0), (3, 0.5, 4.0), (3, 0.95, 0.25),
-                                            (5, 0.8, 8.0), (4, 0.9, 2.0)])
+@pytest.mark.parametrize("cid,top_p,temp", [(2, 0.9, 1.0), (2, 0.99, 16.0), (3, 0.5, 4.0),
+                                            (3, 0.95, 0.25), (5, 0.8, 8.0), (5, 0.3, 0.5),
+                                            (4, 0.9, 2.0)])
 def test_topp_parity(bsa_gpu, orc, cid, top_p, temp):
     c = case(cid)
     cfg = c["cfg"]

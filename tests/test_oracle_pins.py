@@ -668,6 +668,26 @@ def test_int8_p_quantisation_error_bound(orc):
     assert np.max(np.abs(O8 - Oe)) > 0  # the quantisation does act
 
 
+def test_exp2_fixed_accuracy_and_special_values(orc):
+    """The fixed fp32 2^a behind the Top-P weights: exact powers of two at
+    integer arguments; within one fp32 ulp of the fp64 exp2 everywhere on
+    [-125, 127] (dense random grid); +0 below -125, +inf above 127, NaN
+    kept."""
+    f = orc.exp2_fixed
+    for n in range(-125, 128):
+        assert f(n) == 2.0 ** n
+    r = rng(71)
+    a = np.concatenate([r.uniform(-125.0, 127.0, 20000), r.uniform(-1.0, 1.0, 20000),
+                        r.uniform(-0.5, 0.5, 5000) + 0.5]).astype(np.float32)
+    got = np.array([f(float(x)) for x in a], np.float64)
+    ref = np.exp2(a.astype(np.float64))
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert np.max(np.abs(got - ref) / ulp) <= 1.0
+    assert f(-125.0001) == 0.0 and f(-math.inf) == 0.0 and f(-300.0) == 0.0
+    assert f(127.5) == math.inf and f(math.inf) == math.inf
+    assert math.isnan(f(math.nan))
+
+
 def _read_golden_kv(name):
     from fractions import Fraction
 
