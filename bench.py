@@ -88,6 +88,18 @@ def read_traffic(flops_per_launch):
         return None
 
 
+def cpu_model():
+    """The host CPU's model string from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, Qn, Kn, Vn, orders, p, budget_s=12.0):
     """Oracle on head 0 (reorder, mask build, masked attention on sampled
     rows), extrapolated to the whole layer (all heads, all rows)."""
@@ -123,6 +135,9 @@ def cpu_baseline(cfg, Qn, Kn, Vn, orders, p, budget_s=12.0):
         "unit": "TFLOPS",
         "cores": oracle.num_threads(),
         "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "os_cpu_count": os.cpu_count(),
+        "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
         "sample": (f"head 0 of {G}: reorder Q/K/V + mask build ({t_head:.2f} s) and fp64 masked "
                    f"attention on {nrows} of {N} rows ({t_rows:.2f} s); layer time extrapolated "
                    f"as {G} x (head + rows*N/{nrows}) = {t_layer:.0f} s"),
@@ -317,6 +332,125 @@ def calibration(args):
     }
 
 
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def event_ms(fn, reps):
+    """Mean duration (ms) of fn() over reps launches, HIP events on the
+    current stream around the whole loop."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def reorder_bandwidth(plan, Q, od, F, H, W, reps):
+    """The reorder judged by achieved GB/s: algorithmic bytes = read + write
+    of one bf16 tensor (2*N*G*d*2; indices are computed, not read), against
+    the HBM peak and against a plain device copy of the same size timed in
+    the same run.  The fused pass (reorder + fp32 block sums) adds its sums
+    to the written bytes."""
+    import torch
+
+    import block_sparse_attention_inverse_amd as bsa
+
+    G, N, d = plan.G, plan.N, plan.d
+    nbytes = N * G * d * 2
+    p = plan.params
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = event_ms(lambda: dst.copy_(src), reps)
+    del src, dst
+    t_gather = event_ms(lambda: bsa.permute(Q, od, F, H, W, 0, out=plan.Qp), reps)
+    t_scatter = event_ms(lambda: bsa.permute(plan.Qp, od, F, H, W, 1, out=plan.O), reps)
+    t_fused = event_ms(lambda: bsa.permute_pool(Q, od, F, H, W, p.Bq, out=plan.Qp, sums=plan.sums_q),
+                       reps)
+    sums_bytes = G * -(-N // p.Bq) * d * 4
+
+    def gbs(byt, ms):
+        return byt / (ms / 1e3) / 1e9
+
+    out = {
+        "tensor": f"one bf16 tensor [N][G][d] = {nbytes} bytes",
+        "algorithmic_bytes": 2 * nbytes,
+        "device_copy_ms": t_copy,
+        "device_copy_gbs": gbs(2 * nbytes, t_copy),
+        "gather_ms": t_gather,
+        "gather_gbs": gbs(2 * nbytes, t_gather),
+        "scatter_ms": t_scatter,
+        "scatter_gbs": gbs(2 * nbytes, t_scatter),
+        "fused_gather_with_block_sums_ms": t_fused,
+        "fused_gather_with_block_sums_gbs": gbs(2 * nbytes + sums_bytes, t_fused),
+        "peak_gbs": HBM_PEAK_GBS,
+    }
+    out["gather_frac_peak"] = out["gather_gbs"] / HBM_PEAK_GBS
+    out["gather_vs_copy"] = out["gather_gbs"] / out["device_copy_gbs"]
+    out["fused_frac_peak"] = out["fused_gather_with_block_sums_gbs"] / HBM_PEAK_GBS
+    out["copy_frac_peak"] = out["device_copy_gbs"] / HBM_PEAK_GBS
+    return out
+
+
+def density_sweep(plan, plan8, Q, K, V, od, F, H, W, reps, rhos=((30, 100), (20, 100))):
+    """bf16 and INT8 attention (natural-order output) at several densities on
+    the same reordered inputs, with the relative L2 difference between the
+    INT8 and the bf16 outputs (whole tensor, fp32)."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_inverse_amd as bsa
+
+    G, N, d = plan.G, plan.N, plan.d
+    p0 = plan.params
+    plan.reorder_fused(Q, K, V, od)
+    if plan8 is not None:
+        plan8.reorder_fused(Q, K, V, od)
+    res = {}
+    for rn, rd in rhos:
+        p = bsa.mask_params(p0.Bq, p0.Bk, 0, (rn, rd), True)
+        rp, ci, nnz = bsa.build_mask_pooled(plan.sums_q, plan.sums_k, od, F, H, W, p)
+        n = int(nnz.item())
+        fl = kept_flops(rp.cpu().numpy(), ci[:n].cpu().numpy(), G, N, p.Bq, p.Bk, d)
+        nq, nk = -(-N // p.Bq), -(-N // p.Bk)
+        Ob = torch.empty((N, G, d), dtype=torch.bfloat16, device="cuda")
+        t_b = event_ms(lambda: bsa.forward_natural(plan.Qp, plan.Kp, plan.Vp, rp, ci, p.Bq, p.Bk,
+                                                   od, F, H, W, out=Ob, want_lse=False), reps)
+        r = {
+            "block_density": n / (G * nq * nk),
+            "kept_tflop": fl / 1e12,
+            "bf16_attention_ms": t_b,
+            "bf16_kept_tflops": fl / (t_b / 1e3) / 1e12,
+            "bf16_frac_peak": fl / (t_b / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        }
+        if plan8 is not None:
+            O8 = torch.empty_like(Ob)
+            t_8 = event_ms(lambda: bsa.forward_int8_natural(
+                plan8.Qq, plan8.sQ, plan8.Kq, plan8.sK, plan8.Vq, plan8.sV, rp, ci, p.Bq, p.Bk, od,
+                F, H, W, out=O8, want_lse=False), reps)
+            diff = 0.0
+            ref = 0.0
+            for g in range(G):  # per head in fp32, to bound the temporary memory
+                a = O8[:, g].float()
+                b = Ob[:, g].float()
+                diff += float(torch.sum((a - b) ** 2))
+                ref += float(torch.sum(b * b))
+            r.update({
+                "int8_attention_ms": t_8,
+                "int8_kept_tops": fl / (t_8 / 1e3) / 1e12,
+                "int8_frac_int8_peak": fl / (t_8 / 1e3) / 1e12 / PEAK_INT8_TOPS,
+                "int8_vs_bf16_rel_l2": float(np.sqrt(diff / max(ref, 1e-30))),
+            })
+        res[f"rho_{rn}"] = r
+        log(f"[bench] density {rn}/{rd}: {r}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +462,8 @@ def main():
                     help="skip the offline order calibration timing")
     ap.add_argument("--no-long-clip", action="store_true",
                     help="skip the long-clip layer (dynamic COSINE mask rebuilt every step)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the reorder bandwidth and the 30 %% / 20 %% density sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 3 plain device copies of 2 GiB (reference dispatches for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -506,6 +642,12 @@ def main():
             "frac_int8_peak": fl_kept / t8 / 1e12 / PEAK_INT8_TOPS,
             "frac_bf16_peak": fl_kept / t8 / 1e12 / PEAK_BF16_TFLOPS,
         }
+    if not args.no_extras:
+        log("[bench] reorder bandwidth")
+        result["permute"] = reorder_bandwidth(plan, Q, od, F, H, W, reps=max(5, args.steps // 2))
+        log("[bench] density sweep (30 % and 20 %)")
+        result["density"] = density_sweep(plan, plan8, Q, K, V, od, F, H, W,
+                                          reps=max(3, args.steps // 4))
     if not args.no_long_clip:
         result["long_clip"] = long_clip(args, timed_steps=args.steps)
     if not args.no_calib:
