@@ -2,7 +2,8 @@
 
 Public surface (Python names mirror the C ABI in include/bsa.h):
 ``permute``, ``mask_capacity``, ``mask_workspace``, ``build_mask``,
-``permute_pool``, ``build_mask_pooled``, ``order_workspace``,
+``permute_pool``, ``build_mask_pooled``, ``build_mask_pooled_noalloc`` (no
+device allocation: a fixed scratch inside the library), ``order_workspace``,
 ``order_scores``, ``select_orders``, ``quantize_int8``, ``forward``,
 ``forward_int8``, ``forward_natural``, ``forward_int8_natural``, ``debug_int8_qk``, ``debug_int8_pv``, the offline calibration
 ``attn_block_stats``, ``paro_metric``, ``paro_select`` (chained by
@@ -20,6 +21,7 @@ from .api import (  # noqa: F401
     block_scores,
     build_mask,
     build_mask_pooled,
+    build_mask_pooled_noalloc,
     debug_int8_pv,
     debug_int8_qk,
     forward,

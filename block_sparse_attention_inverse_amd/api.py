@@ -185,6 +185,29 @@ def build_mask_pooled(sums_q, sums_k, axis_order, F, H, W, params: MaskParams, w
     return row_ptr, col_idx, nnz
 
 
+def build_mask_pooled_noalloc(sums_q, sums_k, axis_order, F, H, W, params: MaskParams, row_ptr,
+                              col_idx, nnz):
+    """bsa_build_mask_pooled_noalloc: as :func:`build_mask_pooled` into the
+    caller's row_ptr (int32 [G*Nq+1]), col_idx (int32, >= mask_capacity) and
+    nnz (int32 [1]), with the library's fixed device scratch in place of a
+    workspace; neither this call nor the library allocates device memory."""
+    G, _, d = sums_q.shape
+    N = F * H * W
+    for t, B in ((sums_q, params.Bq), (sums_k, params.Bk)):
+        if (t.shape != (G, (N + B - 1) // B, d) or t.dtype != torch.float32
+                or not t.is_contiguous()):
+            raise ValueError("sums must be contiguous fp32 [G][ceil(N/B)][d] (Bq for Q, Bk for K)")
+    nq = (N + params.Bq - 1) // params.Bq
+    for name, t, n in (("row_ptr", row_ptr, G * nq + 1), ("nnz", nnz, 1), ("col_idx", col_idx, 0)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < n:
+            raise ValueError(f"{name} must be contiguous int32 with at least {n} entries")
+    _dev(sums_q, sums_k, axis_order, row_ptr, col_idx, nnz)
+    check(_lib.load().bsa_build_mask_pooled_noalloc(
+        _ptr(sums_q), _ptr(sums_k), G, F, H, W, d, _ptr(axis_order), ctypes.byref(params),
+        _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(nnz), _stream()))
+    return row_ptr, col_idx, nnz
+
+
 def block_scores(sums_q, sums_k, F, H, W, params: MaskParams, out=None, workspace=None):
     """bsa_block_scores: fp32 [G][Nq][Nkv] scores of every (q-block, kv-block)
     pair from per-block channel sums (the keys the mask build ranks)."""

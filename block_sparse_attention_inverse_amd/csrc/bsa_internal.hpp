@@ -39,6 +39,12 @@ hipError_t launch_build_mask_pooled(const MaskGeom& m, const float* sums_q, cons
                                     const uint8_t* orders, int32_t* row_ptr, int32_t* col_idx,
                                     int64_t col_capacity, int32_t* nnz, char* ws, hipStream_t s);
 
+// the fixed device scratch of the mask build (file-scope array in mask.hip):
+// its size, and its device address on the current device (looked up once
+// per device with hipGetSymbolAddress)
+size_t mask_scratch_bytes();
+hipError_t mask_scratch_ptr(void** out);
+
 // bitmask rows [R][ceil(nk/64)] -> counts (scratch, R ints) -> CSR; bits at
 // kv-block >= nk are ignored
 hipError_t launch_bits_to_csr(const unsigned long long* bits, int R, int nk, int32_t* counts,

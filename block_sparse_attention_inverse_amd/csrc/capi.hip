@@ -267,6 +267,38 @@ int bsa_build_mask_pooled(const float* sums_q, const float* sums_k, int32_t G, i
   });
 }
 
+int bsa_build_mask_pooled_noalloc(const float* sums_q, const float* sums_k, int32_t G, int32_t F,
+                                  int32_t H, int32_t W, int32_t d, const uint8_t* axis_order,
+                                  const bsa_mask_params* p_host, int32_t* row_ptr, int32_t* col_idx,
+                                  int64_t col_capacity, int32_t* nnz, void* stream) {
+  return guarded([&]() -> int {
+    if (!sums_q || !sums_k || !axis_order || !row_ptr || !col_idx || !nnz)
+      return fail(BSA_EINVAL, "NULL pointer");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    bsa::MaskGeom m{};
+    const int rc = mask_geom(G, F, H, W, d, p_host, m);
+    if (rc != BSA_OK) return rc;
+    const int64_t cap = capacity_of(m);
+    if (cap >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "mask capacity %lld exceeds int32", (long long)cap);
+    if (col_capacity < cap)
+      return fail(BSA_ECAPACITY, "col_capacity %lld < required bound %lld", (long long)col_capacity,
+                  (long long)cap);
+    const size_t need = bsa::mask_workspace_layout(m).total;
+    if (need > bsa::mask_scratch_bytes())
+      return fail(BSA_ECAPACITY,
+                  "this mask build needs %zu bytes of scratch; the fixed scratch holds %zu "
+                  "(use bsa_build_mask_pooled with a caller workspace)",
+                  need, bsa::mask_scratch_bytes());
+    void* ws = nullptr;
+    const int st = hip_status(bsa::mask_scratch_ptr(&ws), "bsa_build_mask_pooled_noalloc: scratch address");
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_build_mask_pooled(m, sums_q, sums_k, axis_order, row_ptr, col_idx,
+                                                    col_capacity, nnz, static_cast<char*>(ws),
+                                                    as_stream(stream)),
+                      "bsa_build_mask_pooled_noalloc");
+  });
+}
+
 int64_t bsa_order_workspace(int32_t G, int32_t F, int32_t H, int32_t W, int32_t B) {
   if (G <= 0 || F <= 0 || H <= 0 || W <= 0 || !block_ok(B)) return -1;
   const int64_t N = static_cast<int64_t>(F) * H * W;

@@ -27,6 +27,7 @@
 #pragma clang fp contract(off)
 
 #include <algorithm>
+#include <mutex>
 
 #include "bsa_device.hpp"
 #include "bsa_internal.hpp"
@@ -800,6 +801,42 @@ hipError_t launch_sorted_select(int mode, const float* keys, const float* noise,
   else e = run(sorted_select_kernel<SEL_MASS>);
   if (e != hipSuccess) return e;
   return launch_bits_to_csr(bits, R, nk, counts, row_ptr, col_idx, cap, nnz, s);
+}
+
+// ---------------------------------------------------------------------------
+// The mask build's workspace as a file-scope device array, for callers that
+// cannot allocate (bsa_build_mask_pooled_noalloc).  Each GPU holds its own
+// copy until the process ends; its host-side name is only a stand-in, so the
+// device address is looked up once per device with hipGetSymbolAddress and
+// kept.  Every region of the workspace is written before it is read within
+// one build (pooled summaries, per-row counts, bitmask words), so nothing
+// has to be cleared between calls.
+constexpr size_t kScratchBytes = size_t{48} << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t mask_scratch_bytes() { return kScratchBytes; }
+
+hipError_t mask_scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace bsa

@@ -154,6 +154,26 @@ int bsa_build_mask_pooled(const float *sums_q, const float *sums_k, int32_t G, i
                           int64_t col_capacity, int32_t *nnz, void *workspace, int64_t ws_bytes,
                           void *stream);
 
+/* bsa_build_mask_pooled_noalloc — bsa_build_mask_pooled without a workspace
+ * argument and without any device allocation, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation.  The scratch is a fixed
+ * device array inside the library, 48 MiB (50331648 bytes) per GPU, held
+ * until the process ends (the 720p layer at 128x64 blocks needs 38.4 MiB,
+ * the long clip at 128x128 24.6 MiB).  A call whose
+ * bsa_mask_workspace(G, F, H, W, d, p_host) exceeds it returns ECAPACITY
+ * and launches nothing.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (concurrent streams, or threads) race and
+ * must be serialised by the caller; successive calls on one stream are
+ * safe (the scratch keeps the last call's contents, and every region is
+ * written before it is read, so nothing needs clearing).  The device used
+ * is the one current on the calling thread.  Inputs, outputs, result (the
+ * same CSR bit for bit) and the other errors as bsa_build_mask_pooled. */
+int bsa_build_mask_pooled_noalloc(const float *sums_q, const float *sums_k, int32_t G, int32_t F,
+                                  int32_t H, int32_t W, int32_t d, const uint8_t *axis_order,
+                                  const bsa_mask_params *p_host, int32_t *row_ptr, int32_t *col_idx,
+                                  int64_t col_capacity, int32_t *nnz, void *stream);
+
 /* bsa_permute_pool — the reordering of bsa_permute (direction 0) fused with
  * block pooling and, optionally, INT8 quantisation (PAROAttention verdict,
  * key machinery: the permutation fused into neighbouring kernels; SPADE

@@ -328,3 +328,23 @@ def test_forward_bindings_check_inputs_before_any_launch():
         bsa.forward_natural(Q, Q, Q, rp, ci, B, B, orders[:1], 4, 8, 8)
     with pytest.raises(ValueError, match="Xp must be"):
         bsa.quantize_int8(Q.float(), B)
+
+
+def test_noalloc_mask_refuses_shapes_beyond_its_scratch(lib):
+    """The mask build without allocation has a fixed 48 MiB scratch: a shape
+    whose workspace exceeds it is refused (ECAPACITY, nothing launched), with
+    a message naming both sizes."""
+    from block_sparse_attention_inverse_amd._lib import MaskParams
+
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    p = MaskParams(64, 64, 0, 30, 100, 1, -1, 0)  # 720p, 40 heads, 64x64: 53.6 MiB
+    need = lib.bsa_mask_workspace(40, 21, 45, 80, 128, ctypes.byref(p))
+    assert need > 48 << 20
+    cap = lib.bsa_mask_capacity(40, 21, 45, 80, ctypes.byref(p))
+    assert lib.bsa_build_mask_pooled_noalloc(fake, fake, 40, 21, 45, 80, 128, fake, ctypes.byref(p),
+                                             fake, fake, cap, fake, None) == -3
+    msg = lib.bsa_last_error()
+    assert b"scratch" in msg and str(need).encode() in msg and b"50331648" in msg
+    assert lib.bsa_build_mask_pooled_noalloc(None, fake, 40, 21, 45, 80, 128, fake, ctypes.byref(p),
+                                             fake, fake, cap, fake, None) == -1
