@@ -62,6 +62,10 @@ constexpr float kRefInit = -1.0e30f;  // running maximum before any score: finit
 // exponent: bias*f < 1.5*2^12, so the folded offset is rounded by at most
 // 2^-12 (log2 units) and y = Pt*127/mP stays below 127.02 (code <= 127).
 constexpr float kNarrowF = 0x1p-11f;
+// O and l follow the running row maximum lazily: their reference moves only
+// when the maximum has risen more than this (log2 units) above it, so the
+// per-tile contributions carry a factor of at most 2^kLazy
+constexpr float kLazy = 8.0f;
 // 32-row halves per wave: one, so a 128-row q-block is four waves and two
 // workgroups give every SIMD two waves whose products and softmax interleave
 constexpr int kQB = 1;
@@ -167,13 +171,14 @@ __device__ __forceinline__ void qk_i8(const uint8_t* kt, uint32_t kread,
 }
 
 // One channel block of O^T (int32, this tile only) = V^T . P8^T for the
-// wave's row halves: ov[qb] covers channels 32db..32db+31 of half qb
+// wave's row halves: ov[qb] covers channels 32db..32db+31 of half qb.  The
+// first product takes its accumulator from zacc, a register block that holds
+// zeros for the whole kernel (the product writes ov, not zacc), so no
+// per-tile clearing of ov is issued.
 template <int D, int BK>
 __device__ __forceinline__ void pv_block(const uint8_t* vt, uint32_t vread, const i32x4 (&pf)[kQB][BK / 32],
-                                         int db, i32x16 (&ov)[kQB]) {
+                                         int db, const i32x16& zacc, i32x16 (&ov)[kQB]) {
   const uint32_t vhi = (vread ^ ((D / 32) << 4)) + 8 * D;  // rows +8: the swizzle flips CH/2
-#pragma unroll
-  for (int qb = 0; qb < kQB; qb++) ov[qb] = i32x16{};
 #pragma unroll
   for (int b = 0; b < BK / 32; b++) {
     const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -182,7 +187,8 @@ __device__ __forceinline__ void pv_block(const uint8_t* vt, uint32_t vread, cons
         (LDS_AS i32x2*)(vt + b * 32 * D + (vhi ^ (db << 5))));
     const i32x4 a = (i32x4){lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-    for (int qb = 0; qb < kQB; qb++) ov[qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[qb][b], ov[qb], 0, 0, 0);
+    for (int qb = 0; qb < kQB; qb++)
+      ov[qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[qb][b], b == 0 ? zacc : ov[qb], 0, 0, 0);
   }
 }
 
@@ -214,8 +220,9 @@ __device__ __forceinline__ float rows_max(float x) {
 }
 
 // P8 = rint(Pt * 127 / mP) for the wave's rows (mP = 2^dm, the tile maximum
-// of Pt), l = l * alpha + sum Pt.  The exponential argument folds the
-// quantisation scale in: y = Pt * 127 / mP = 2^(x - m - dm + log2 127).
+// of Pt), l += lsc * sum y (lsc = mP/127 times the row's frame factor: l
+// sums Pt).  The exponential argument folds the quantisation scale in:
+// y = Pt * 127 / mP = 2^(x - m - dm + log2 127).
 // MASK: columns outside the tile and a tile without real rows give zero.
 // WIDE: a score scale f above kNarrowF, where the biased fp32 score would
 // lose too many bits of the offset bias*f (an exponent error of ulp(bias*f)/2
@@ -225,7 +232,7 @@ __device__ __forceinline__ float rows_max(float x) {
 template <bool MASK, bool WIDE, int NB>
 __device__ __forceinline__ void quantize_tile(const i32x16 (&s)[kQB][NB], float f, const float (&m)[kQB],
                                               float dm, bool any, int kv0, bool jvalid, int N,
-                                              float mp127, const float (&alpha)[kQB], float (&l)[kQB],
+                                              const float (&lsc)[kQB], float (&l)[kQB],
                                               i32x4 (&pf)[kQB][NB]) {
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
@@ -263,7 +270,7 @@ __device__ __forceinline__ void quantize_tile(const i32x16 (&s)[kQB][NB], float 
         }
         pf[qb][b][q4] = static_cast<int>(word);
       }
-    l[qb] = l[qb] * alpha[qb] + ys * mp127;
+    l[qb] = __builtin_fmaf(ys, lsc[qb], l[qb]);
   }
 }
 
@@ -309,9 +316,14 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
     return static_cast<unsigned>(j) < static_cast<unsigned>(nk) ? j * BK : 0;
   };
 
-  float m[kQB], l[kQB];
+  // m: the exact running row maximum (the P quantisation is relative to
+  // it); O and l are kept relative to an older reference mf <= m and only
+  // moved to the running maximum when it has risen more than kLazy above mf
+  float m[kQB], mf[kQB], l[kQB];
 #pragma unroll
-  for (int qb = 0; qb < kQB; qb++) { m[qb] = kRefInit; l[qb] = 0.0f; }
+  for (int qb = 0; qb < kQB; qb++) { m[qb] = kRefInit; mf[qb] = kRefInit; l[qb] = 0.0f; }
+  i32x16 zacc = {};
+  asm volatile("" : "+v"(zacc));  // zeros kept in registers (see pv_block)
   f32x16 o[kQB][D / 32];
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++)
@@ -366,14 +378,30 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
           x_max[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
       }
-      float alpha[kQB], dmax = -INFINITY;
+      float dmax = -INFINITY;
+      bool resc = false;
 #pragma unroll
       for (int qb = 0; qb < kQB; qb++) {
         const float mn = fmaxf(m[qb], x_max[qb]);
-        alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mn);
         m[qb] = mn;
+        resc = resc || mn - mf[qb] > kLazy;
         // largest log2 Pt of this row in the tile (real rows only)
         if (qbase + 32 * qb + l32 < N) dmax = fmaxf(dmax, x_max[qb] - mn);
+      }
+      // the running maximum rose far above the reference of O and l: move
+      // them to it (rows that did not rise keep factor 1)
+      if (__ballot(resc) != 0ull) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; qb++) {
+          const bool up = m[qb] - mf[qb] > kLazy;
+          const float alpha = up ? __builtin_amdgcn_exp2f(mf[qb] - m[qb]) : 1.0f;
+          mf[qb] = up ? m[qb] : mf[qb];
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; db++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) o[qb][db][r] *= alpha;
+        }
       }
       dmax = rows_max(dmax);
       if (lane == 0) tile_max[t & 1][w] = dmax;
@@ -388,41 +416,36 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
 #pragma unroll
       for (int ww = 1; ww < NW; ww++) dm = fmaxf(dm, tile_max[t & 1][ww]);
 
-      // ---- P8 = rint(Pt * 127 / mP), mP = 2^dm; l sums Pt = y * mP / 127
+      // ---- P8 = rint(Pt * 127 / mP), mP = 2^dm; l sums Pt = y * mP / 127,
+      // expressed relative to mf: times the row's frame factor 2^(m - mf)
       const bool any = dm > -INFINITY;
       const float mp127 = any ? __builtin_amdgcn_exp2f(dm - kLog2_127) : 0.0f;  // mP / 127
+      float lsc[kQB], cv[kQB];
+#pragma unroll
+      for (int qb = 0; qb < kQB; qb++) {
+        lsc[qb] = mp127 * __builtin_amdgcn_exp2f(m[qb] - mf[qb]);
+        cv[qb] = lsc[qb] * svj;
+      }
       i32x4 pf[kQB][NB];
       // masked columns (ragged tail, invalid block) and a tile without real
       // rows take the checked variant
       if (f > kNarrowF)
-        quantize_tile<true, true>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
+        quantize_tile<true, true>(s, f, m, dm, any, kv0, jvalid, N, lsc, l, pf);
       else if (masked || !any)
-        quantize_tile<true, false>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
+        quantize_tile<true, false>(s, f, m, dm, any, kv0, jvalid, N, lsc, l, pf);
       else
-        quantize_tile<false, false>(s, f, m, dm, any, kv0, jvalid, N, mp127, alpha, l, pf);
+        quantize_tile<false, false>(s, f, m, dm, any, kv0, jvalid, N, lsc, l, pf);
 
-      // ---- O = O * alpha + (mP/127) sV_j (P8 . V8), one channel block at a time
-      const float cv = mp127 * svj;
-      bool resc = false;
-#pragma unroll
-      for (int qb = 0; qb < kQB; qb++) resc = resc || alpha[qb] != 1.0f;
-      if (__ballot(resc) != 0ull) {
-#pragma unroll
-        for (int qb = 0; qb < kQB; qb++)
-#pragma unroll
-          for (int db = 0; db < D / 32; db++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) o[qb][db][r] *= alpha[qb];
-      }
+      // ---- O += (mP/127) sV_j 2^(m - mf) (P8 . V8), one channel block at a time
 #pragma unroll
       for (int db = 0; db < D / 32; db++) {
         i32x16 ov[kQB];
-        pv_block<D, BK>(vbuf[t & 1], vread, pf, db, ov);
+        pv_block<D, BK>(vbuf[t & 1], vread, pf, db, zacc, ov);
 #pragma unroll
         for (int qb = 0; qb < kQB; qb++)
 #pragma unroll
           for (int r = 0; r < 16; r++)
-            o[qb][db][r] = __builtin_fmaf(static_cast<float>(ov[qb][r]), cv, o[qb][db][r]);
+            o[qb][db][r] = __builtin_fmaf(static_cast<float>(ov[qb][r]), cv[qb], o[qb][db][r]);
       }
     }
   }
@@ -448,7 +471,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
           *reinterpret_cast<uint2*>(op + d0) = pk;
         }
       if (lse != nullptr && h == 0)
-        lse[li] = lt > 0.0f ? m[qb] * kLn2 + logf(lt) : -INFINITY;
+        lse[li] = lt > 0.0f ? mf[qb] * kLn2 + logf(lt) : -INFINITY;
     }
   }
 }
@@ -535,10 +558,12 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void dbg_pv_kernel(const
   __syncthreads();
   int32_t* out = OV + static_cast<int64_t>(t) * BQ * D;
   const uint32_t vread = v_read_off<D>();
+  i32x16 zacc = {};
+  asm volatile("" : "+v"(zacc));
 #pragma unroll
   for (int db = 0; db < D / 32; db++) {
     i32x16 ov[kQB];
-    pv_block<D, BK>(vt[0], vread, pf, db, ov);
+    pv_block<D, BK>(vt[0], vread, pf, db, zacc, ov);
 #pragma unroll
     for (int qb = 0; qb < kQB; qb++) {
       const int qr = w * kRowsPerWave + 32 * qb + l32;
