@@ -437,7 +437,7 @@ template <int D, int BQ, int BK, bool SMALLN>
 __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
-    int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
+    int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int G, int N, int nq, int nk,
     float c, OutMap om) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int NW = BQ / 64;
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t vb1[L::TB];
 
   int g, i;
-  if (!head_sync_tile(blockIdx.x, nq, g, i)) return;
+  if (!xcd_range_tile(blockIdx.x, nq, G, g, i)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int qbase = i * BQ + w * 64;
@@ -683,12 +683,12 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
 template <int D, int BQ, int BK>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
   const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
-  const uint32_t nwg = static_cast<uint32_t>(a.G) * kNumXcd * ((nq + kNumXcd - 1) / kNumXcd);
+  const uint32_t nwg = kNumXcd * static_cast<uint32_t>((static_cast<int64_t>(a.G) * nq + kNumXcd - 1) / kNumXcd);
   const float sm = a.sm_scale > 0.0f ? a.sm_scale : 1.0f / sqrtf(static_cast<float>(a.d));
   auto kern = a.N >= KT ? fwd_bf16_kernel<D, BQ, BK, false> : fwd_bf16_kernel<D, BQ, BK, true>;
   kern<<<nwg, BQ, 0, s>>>(static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                           static_cast<const uint16_t*>(a.V), a.row_ptr, a.col_idx, a.col_len,
-                          a.mask_G, a.O, a.lse, a.N, nq, nk, sm * kLog2e, a.out);
+                          a.mask_G, a.O, a.lse, a.G, a.N, nq, nk, sm * kLog2e, a.out);
   return hipGetLastError();
 }
 

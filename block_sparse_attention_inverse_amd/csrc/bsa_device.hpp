@@ -97,6 +97,22 @@ __device__ __forceinline__ bool head_sync_tile(uint32_t bid, int nq, int& g, int
   return i < nq;
 }
 
+// XCD-contiguous tile order for (head, row-block) grids: the G*nq tiles in
+// head-major order are cut into 8 contiguous ranges of T = ceil(G*nq/8), and
+// XCD x (which receives workgroups bid with bid % 8 == x) runs range x in
+// order.  The workgroups resident on one XCD then belong to one head almost
+// all the time, so its L2 serves a single head's K/V instead of two.  Grid
+// size must be 8 * T; returns false for the padding slots.
+__device__ __forceinline__ bool xcd_range_tile(uint32_t bid, int nq, int G, int& g, int& i) {
+  const int64_t total = static_cast<int64_t>(G) * nq;
+  const int64_t T = (total + kNumXcd - 1) / kNumXcd;
+  const int64_t item = (bid % kNumXcd) * T + bid / kNumXcd;
+  if (item >= total) return false;
+  g = static_cast<int>(item / nq);
+  i = static_cast<int>(item % nq);
+  return true;
+}
+
 // Output row of reordered position r of head g under an OutMap-like
 // description: reordered [G][N][D] when orders is null, else the natural
 // token n = perm_g(r) at n*sn + g*sg; lse_idx receives the matching
