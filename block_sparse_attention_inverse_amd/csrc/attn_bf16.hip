@@ -50,10 +50,11 @@
 // as the 64-row window that ends at row N (all rows real) and its columns
 // outside the sub-tile are masked.
 //
-// Grid order: workgroup b runs on XCD b mod 8; XCD x takes q-blocks
-// [x*per, (x+1)*per) of every head, heads in order, so all XCDs work on one
-// head at a time (its K/V stays in the shared last-level cache) while each
-// XCD's L2 serves neighbouring q-blocks.
+// Grid order: workgroup b runs on XCD b mod 8; XCD x takes one contiguous
+// range of the head-major (head, q-block) tiles, so the workgroups resident
+// on an XCD belong to one head at almost any time and its 4 MB L2 serves a
+// single head's K/V (at 720p this halves the fetches that miss the L2,
+// against an order that spreads every head over all eight XCDs).
 #include <utility>
 
 #include "bsa_device.hpp"
