@@ -71,8 +71,9 @@ def source_hash():
 
 
 def read_traffic(flops_per_launch):
-    """HBM bytes per launch of the bf16 attention kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    """Bytes per launch of the bf16 attention kernel beyond its L2 (FETCH_SIZE
+    + WRITE_SIZE, copy-calibrated) from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -83,7 +84,7 @@ def read_traffic(flops_per_launch):
     if kv.get("attn_source_sha256_16") != source_hash():
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["l2_miss_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 

@@ -59,6 +59,8 @@ def _load():
         "oracle_paro_metric": (_I, [_P, _P, _P, _I, _L, _I, _I, _I, _D, _P]),
         "oracle_mass_select": (_I, [_P, _I, _L, _I, _I, ctypes.c_float, _I, _P, _P, _L, _P]),
         "oracle_exp2_fixed": (ctypes.c_float, [ctypes.c_float]),
+        "oracle_attention_rows_fo": (_I, [_P, _P, _P, _I, _L, _L, _I, _I, _I, _I, _I, _P, _I, _I,
+                                          _P, _P, _I, _D, _P, _L, _P, _P]),
         "oracle_perturb_keys": (None, [_P, _P, ctypes.c_float, _L, _P]),
         "oracle_select_topp": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, ctypes.c_float, ctypes.c_float,
                                     _I, _I, _I, _P, _P, _L, _P, _P, _P]),
@@ -270,6 +272,33 @@ def attention_rows(Q, K, V, G, F, H, W, d, orders, rows, Bq=64, Bk=64, row_ptr=N
         0 if dense else mask_G, 1 if dense else 0, float(sm_scale), _ptr(rows), R, _ptr(O),
         _ptr(lse))
     _check(rc, "attention_rows")
+    return O, lse
+
+
+def attention_rows_fo(Q, K, V, G, F, H, W, d, orders, rows, Bq, Bk, row_ptr, col_idx,
+                      mask_G=None, sm_scale=None, stride_g=None, stride_n=None):
+    """fp64 masked attention plus the first-order compensation of each
+    q-block row's skipped keys (one expansion point, their mean), for
+    natural-order rows; arguments as :func:`attention_rows` (mask required).
+    Returns (O [R][d], lse [R])."""
+    Q, K, V = (np.ascontiguousarray(x) for x in (Q, K, V))
+    assert Q.dtype == K.dtype == V.dtype
+    if stride_g is None:
+        stride_g, stride_n = d, G * d
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
+    orders = np.ascontiguousarray(orders, dtype=np.uint8)
+    R = rows.shape[0]
+    O = np.zeros((R, d), dtype=np.float64)
+    lse = np.zeros(R, dtype=np.float64)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
+    rc = _load().oracle_attention_rows_fo(
+        _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), stride_g, stride_n, G, F, H, W, d,
+        _ptr(orders), Bq, Bk, _ptr(row_ptr), _ptr(col_idx), G if mask_G is None else mask_G,
+        float(sm_scale), _ptr(rows), R, _ptr(O), _ptr(lse))
+    _check(rc, "attention_rows_fo")
     return O, lse
 
 

@@ -36,7 +36,9 @@
  *     (oracle_mass_select);
  *   - Top-P as a softmax of the block scores at a caller temperature
  *     (oracle_select_topp) and the additive form of the stochastic bias
- *     (oracle_perturb_keys).
+ *     (oracle_perturb_keys);
+ *   - first-order compensation with one expansion point per q-block row,
+ *     the mean of all its skipped keys (oracle_attention_rows_fo).
  *
  * Every pointer is a host pointer.  Functions return 0 on success and a
  * negative value on a bad argument.
@@ -697,6 +699,135 @@ int oracle_attention_rows(const void *Q, const void *K, const void *V, int dt, i
         lse[t] = mx + log(l);
       }
       free(kept); free(s); free(qv);
+    }
+  }
+  free(perm); free(pos);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Block-sparse attention with first-order compensation of the skipped keys.
+ * [PASA] Figure 2 caption: grouped first-order compensation for the blocks
+ * outside the selected set; section 3.3 (title only): a Taylor expansion
+ * approximating the sparse attention.  Reading taken here (the pages give
+ * neither the groups nor the expansion point): the group is everything a
+ * q-block row skips.  For q-block i of head g, U = the real tokens of the
+ * kv-blocks not in its CSR row, n = |U|, and in fp64
+ *   kbar = (1/n) sum_{c in U} k_c,   Vhat = sum_{c in U} v_c,
+ *   M    = sum_{c in U} (k_c - kbar) v_c^T        (d x d),
+ * exp(s q.k_c) ~ exp(s q.kbar) (1 + s q.(k_c - kbar)) summed over U gives,
+ * for every real row r of the q-block (a = s q_r.kbar):
+ *   num = sum_{c in A(r)} exp(s q_r.k_c) v_c + exp(a) (Vhat + s M^T q_r)
+ *   den = sum_{c in A(r)} exp(s q_r.k_c)     + exp(a) n
+ * (the first-order term of den is s q_r.sum_U (k_c - kbar) = 0), O = num/den,
+ * lse = ln den (both with a common reference subtracted).  n = 0 leaves the
+ * masked attention unchanged.  Interface as oracle_attention_rows (a mask
+ * is required).
+ * ---------------------------------------------------------------------- */
+int oracle_attention_rows_fo(const void *Q, const void *K, const void *V, int dt, int64_t stride_g,
+                             int64_t stride_n, int G, int F, int H, int W, int d,
+                             const uint8_t *orders, int Bq, int Bk, const int32_t *row_ptr,
+                             const int32_t *col_idx, int mask_G, double sm_scale,
+                             const int64_t *rows, int64_t nrows, double *O, double *lse) {
+  const int64_t N = (int64_t)F * H * W;
+  if (!Q || !K || !V || !orders || !rows || !O || !lse || G <= 0 || N <= 0 || d <= 0) return -1;
+  if (!row_ptr || !col_idx || mask_G <= 0 || Bq <= 0 || Bk <= 0) return -1;
+  if (dt != OR_F32 && dt != OR_BF16 && dt != OR_F64) return -1;
+  const int64_t nq = (N + Bq - 1) / Bq, nk = (N + Bk - 1) / Bk;
+  int32_t *perm = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+  int32_t *pos = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+  if (!perm || !pos) { free(perm); free(pos); return -2; }
+  int rc = 0;
+  for (int g = 0; g < G && !rc; g++) {
+    int any = 0;
+    for (int64_t t = 0; t < nrows; t++) any |= rows[2 * t] == g;
+    if (!any) continue;
+    if (oracle_perm(orders[g], F, H, W, perm)) { rc = -1; break; }
+    for (int64_t p = 0; p < N; p++) pos[perm[p]] = (int32_t)p;
+    /* one pass per q-block that holds a requested row */
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t i = 0; i < nq; i++) {
+      int want = 0;
+      for (int64_t t = 0; t < nrows; t++)
+        if (rows[2 * t] == g && pos[rows[2 * t + 1]] / Bq == i) { want = 1; break; }
+      if (!want) continue;
+      uint8_t *kept = (uint8_t *)calloc((size_t)nk, 1);
+      double *kbar = (double *)calloc((size_t)d, sizeof(double));
+      double *vhat = (double *)calloc((size_t)d, sizeof(double));
+      double *Mt = (double *)calloc((size_t)d * d, sizeof(double)); /* M[a][b] at a*d + b */
+      double *s = (double *)malloc(sizeof(double) * (size_t)N);
+      double *qv = (double *)malloc(sizeof(double) * (size_t)d);
+      double *mq = (double *)malloc(sizeof(double) * (size_t)d);
+      const int64_t row = (int64_t)(g % mask_G) * nq + i;
+      for (int64_t e = row_ptr[row]; e < row_ptr[row + 1]; e++)
+        if (col_idx[e] >= 0 && col_idx[e] < nk) kept[col_idx[e]] = 1;
+      /* moments of the skipped set U */
+      int64_t nu = 0;
+      for (int64_t m = 0; m < N; m++) {
+        if (kept[pos[m] / Bk]) continue;
+        nu++;
+        const int64_t b = m * stride_n + (int64_t)g * stride_g;
+        for (int c = 0; c < d; c++) {
+          kbar[c] += load_elem(K, dt, b + c);
+          vhat[c] += load_elem(V, dt, b + c);
+        }
+      }
+      if (nu > 0) {
+        for (int c = 0; c < d; c++) kbar[c] /= (double)nu;
+        for (int64_t m = 0; m < N; m++) {
+          if (kept[pos[m] / Bk]) continue;
+          const int64_t b = m * stride_n + (int64_t)g * stride_g;
+          for (int a = 0; a < d; a++) {
+            const double ka = load_elem(K, dt, b + a) - kbar[a];
+            for (int c = 0; c < d; c++) Mt[(int64_t)a * d + c] += ka * load_elem(V, dt, b + c);
+          }
+        }
+      }
+      for (int64_t t = 0; t < nrows; t++) {
+        if (rows[2 * t] != g) continue;
+        const int64_t n = rows[2 * t + 1];
+        if (pos[n] / Bq != i) continue;
+        double *o = O + t * d;
+        for (int c = 0; c < d; c++) qv[c] = load_elem(Q, dt, n * stride_n + (int64_t)g * stride_g + c);
+        double mx = -INFINITY;
+        for (int64_t m = 0; m < N; m++) {
+          if (!kept[pos[m] / Bk]) { s[m] = -INFINITY; continue; }
+          double acc = 0.0;
+          const int64_t kb = m * stride_n + (int64_t)g * stride_g;
+          for (int c = 0; c < d; c++) acc += qv[c] * load_elem(K, dt, kb + c);
+          s[m] = sm_scale * acc;
+          if (s[m] > mx) mx = s[m];
+        }
+        double a = 0.0;
+        if (nu > 0) {
+          for (int c = 0; c < d; c++) a += qv[c] * kbar[c];
+          a *= sm_scale;
+          if (a > mx) mx = a;
+        }
+        for (int c = 0; c < d; c++) o[c] = 0.0;
+        if (mx == -INFINITY) { lse[t] = -INFINITY; continue; }
+        double l = 0.0;
+        for (int64_t m = 0; m < N; m++) {
+          if (s[m] == -INFINITY) continue;
+          const double p = exp(s[m] - mx);
+          l += p;
+          const int64_t vb = m * stride_n + (int64_t)g * stride_g;
+          for (int c = 0; c < d; c++) o[c] += p * load_elem(V, dt, vb + c);
+        }
+        if (nu > 0) {
+          const double ea = exp(a - mx);
+          for (int c = 0; c < d; c++) {
+            double acc = 0.0;
+            for (int x = 0; x < d; x++) acc += Mt[(int64_t)x * d + c] * qv[x];
+            mq[c] = acc;
+          }
+          for (int c = 0; c < d; c++) o[c] += ea * (vhat[c] + sm_scale * mq[c]);
+          l += ea * (double)nu;
+        }
+        for (int c = 0; c < d; c++) o[c] /= l;
+        lse[t] = mx + log(l);
+      }
+      free(kept); free(kbar); free(vhat); free(Mt); free(s); free(qv); free(mq);
     }
   }
   free(perm); free(pos);

@@ -495,6 +495,75 @@ def test_attention_full_density_equals_dense(orc):
     assert np.max(np.abs(lse - Lt[rows[:, 1], rows[:, 0]])) < 1e-12
 
 
+def _fo_case(r, t, head_orders=(3, 0)):
+    """Keys: the kv-block that every q-block row keeps (reordered block 0) is
+    random; every other key is one vector k* plus t * delta.  Rows keep
+    block 0 and their own diagonal block; everything else is skipped."""
+    F, H, W, G, d, B = 2, 4, 32, 2, 32, 64
+    N = F * H * W
+    orders = np.array(head_orders, np.uint8)
+    Q = r.standard_normal((N, G, d))
+    V = r.standard_normal((N, G, d))
+    kstar = r.standard_normal((G, d))
+    delta = r.standard_normal((N, G, d))
+    K = kstar[None, :, :] + t * delta
+    for g in range(G):  # reordered block 0 of each head: free keys
+        pm = brute.perm(int(orders[g]), F, H, W)
+        K[pm[:B], g, :] = r.standard_normal((B, d))
+    nb = N // B
+    sets = [[0] if i == 0 else [0, i] for _ in range(G) for i in range(nb)]
+    rp = np.cumsum([0] + [len(x) for x in sets]).astype(np.int32)
+    ci = np.array([j for x in sets for j in x], np.int32)
+    return F, H, W, G, d, B, N, orders, Q, K, V, rp, ci
+
+
+def test_first_order_compensation_exact_for_identical_skipped_keys(orc):
+    """When every skipped key equals the same vector, the expansion point is
+    that vector and the first-order term vanishes: masked attention plus
+    compensation equals dense attention over all keys (fp64 textbook)."""
+    F, H, W, G, d, B, N, orders, Q, K, V, rp, ci = _fo_case(rng(91), 0.0)
+    rows = _all_rows(N, G)
+    O, L = orc.attention_rows_fo(Q, K, V, G, F, H, W, d, orders, rows, B, B, rp, ci)
+    Ot, Lt = _dense_ref(Q, K, V, 1 / np.sqrt(d))
+    assert np.max(np.abs(O - Ot[rows[:, 1], rows[:, 0]])) < 1e-12
+    assert np.max(np.abs(L - Lt[rows[:, 1], rows[:, 0]])) < 1e-12
+    # the masked attention alone is far from it (the compensation matters)
+    Om, _ = orc.attention_rows(Q, K, V, G, F, H, W, d, orders, rows, B, B, rp, ci)
+    assert np.max(np.abs(Om - Ot[rows[:, 1], rows[:, 0]])) > 1e-2
+
+
+def test_first_order_compensation_error_is_second_order(orc):
+    """Skipped keys k* + t*delta: the compensation keeps the value and the
+    slope in t of the exact skipped sums, so its error against dense
+    attention falls four-fold when t halves (a missing or wrongly signed
+    first-order term leaves an error linear in t, falling two-fold)."""
+    errs = []
+    for t in (0.02, 0.01, 0.005):
+        F, H, W, G, d, B, N, orders, Q, K, V, rp, ci = _fo_case(rng(92), t)
+        rows = _all_rows(N, G)
+        O, _ = orc.attention_rows_fo(Q, K, V, G, F, H, W, d, orders, rows, B, B, rp, ci)
+        Ot, _ = _dense_ref(Q, K, V, 1 / np.sqrt(d))
+        errs.append(np.max(np.abs(O - Ot[rows[:, 1], rows[:, 0]])))
+    assert errs[0] > 1e-8
+    assert 0.2 < errs[1] / errs[0] < 0.3 and 0.2 < errs[2] / errs[1] < 0.3, errs
+
+
+def test_first_order_compensation_without_skipped_keys_is_masked_attention(orc):
+    """A row that keeps every kv-block has nothing to compensate."""
+    r = rng(93)
+    F, H, W, G, d, B = 1, 2, 96, 2, 16, 64
+    N = F * H * W
+    Q, K, V = (r.standard_normal((N, G, d)) for _ in range(3))
+    orders = np.array([1, 4], np.uint8)
+    nb = -(-N // B)
+    rp = (np.arange(G * nb + 1) * nb).astype(np.int32)
+    ci = np.tile(np.arange(nb, dtype=np.int32), G * nb)
+    rows = _all_rows(N, G)
+    O, L = orc.attention_rows_fo(Q, K, V, G, F, H, W, d, orders, rows, B, B, rp, ci)
+    Om, Lm = orc.attention_rows(Q, K, V, G, F, H, W, d, orders, rows, B, B, rp, ci)
+    assert np.max(np.abs(O - Om)) < 1e-14 and np.max(np.abs(L - Lm)) < 1e-14
+
+
 def test_attention_diagonal_only_is_per_block(orc):
     """Diagonal-only mask with Bq = Bk: each reordered block attends to
     itself only — independent per-block attention."""
