@@ -452,6 +452,43 @@ def density_sweep(plan, plan8, Q, K, V, od, F, H, W, reps, rhos=((30, 100), (20,
     return res
 
 
+def compensation(plan, od, F, H, W, reps):
+    """First-order compensation of the skipped keys on the 720p layer, after
+    the bf16 forward with its natural-order output (the mask and the
+    reordered tensors of the last bf16 step): its time beside the attention's,
+    and its dominant product (the skip-mask GEMM over per-kv-block moments,
+    2 * Nq * Nkv * (d^2 + 2d + 1) flops per head) against the bf16 peak."""
+    import torch
+
+    import block_sparse_attention_inverse_amd as bsa
+
+    G, N, d, p = plan.G, plan.N, plan.d, plan.params
+    ws = torch.empty(bsa.fo_workspace(G, N, d, p.Bq, p.Bk), dtype=torch.uint8, device="cuda")
+    O = torch.empty((N, G, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((G, N), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        bsa.forward_natural(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk, od,
+                            F, H, W, out=O, lse=lse)
+
+    def comp():
+        bsa.fo_compensate(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk, O, lse,
+                          od, F, H, W, workspace=ws)
+
+    fwd()
+    t_comp = event_ms(comp, reps)
+    nq, nk = -(-N // p.Bq), -(-N // p.Bk)
+    fl = 2.0 * nq * nk * (d * d + 2 * d + 1) * G
+    return {
+        "ms": t_comp,
+        "workspace_gib": ws.numel() / 2**30,
+        "skip_gemm_tflop": fl / 1e12,
+        "skip_gemm_tflops_if_whole_time": fl / (t_comp / 1e3) / 1e12,
+        "policy": "one expansion point per q-block row (the mean of its skipped keys), "
+                  "first-order Taylor term of exp(s q.k) summed over the skipped set",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -649,6 +686,10 @@ def main():
         log("[bench] density sweep (30 % and 20 %)")
         result["density"] = density_sweep(plan, plan8, Q, K, V, od, F, H, W,
                                           reps=max(3, args.steps // 4))
+        log("[bench] first-order compensation")
+        step_bf16()
+        result["compensation"] = compensation(plan, od, F, H, W, reps=max(3, args.steps // 4))
+        log(f"[bench] compensation: {result['compensation']}")
     if not args.no_long_clip:
         result["long_clip"] = long_clip(args, timed_steps=args.steps)
     if not args.no_calib:

@@ -9,7 +9,8 @@ device allocation: a fixed scratch inside the library), ``order_workspace``,
 ``attn_block_stats``, ``paro_metric``, ``paro_select`` (chained by
 ``paro_calibrate``), the static masks ``mask_from_block_sums`` and
 ``mask_from_bits``, the Top-K / Top-P / noise-perturbed selection
-``block_scores`` + ``mask_from_scores``, plus ``LayerPlan`` / ``layer_forward`` which chain the
+``block_scores`` + ``mask_from_scores``, the first-order compensation of skipped
+keys ``fo_compensate`` (``fo_workspace``), plus ``LayerPlan`` / ``layer_forward`` which chain the
 per-step calls.
 The HIP library is loaded on first use and must be built; there is no
 fallback path.  ``synth`` holds the seeded synthetic workload generators.
@@ -24,6 +25,8 @@ from .api import (  # noqa: F401
     build_mask_pooled_noalloc,
     debug_int8_pv,
     debug_int8_qk,
+    fo_compensate,
+    fo_workspace,
     forward,
     forward_int8,
     forward_int8_natural,

@@ -40,6 +40,9 @@ SIGNATURES = {
                             _L, _P, _P, _L, _P]),
     "bsa_build_mask_pooled": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, ctypes.POINTER(MaskParams), _P,
                                    _P, _L, _P, _P, _L, _P]),
+    "bsa_fo_workspace": (_L, [_I, _I, _I, _I, _I]),
+    "bsa_fo_compensate": (_I, [_P, _P, _P, _P, _P, _L, _I, _P, _I, _I, _I, _P, _L, _L, _P, _I, _I,
+                               _I, _I, _F, _P, _L, _P]),
     "bsa_build_mask_pooled_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _P,
                                            ctypes.POINTER(MaskParams), _P, _P, _L, _P, _P]),
     "bsa_permute_pool": (_I, [_P, _I, _P, _L, _L, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),

@@ -618,6 +618,48 @@ def forward_int8_natural(Qq, sQ, Kq, sK, Vq, sV, row_ptr, col_idx, Bq, Bk, axis_
     return out, lse
 
 
+def fo_workspace(G, N, d, Bq, Bk) -> int:
+    v = int(_lib.load().bsa_fo_workspace(G, N, d, Bq, Bk))
+    if v < 0:
+        check(v)
+    return v
+
+
+def fo_compensate(Qp, Kp, Vp, row_ptr, col_idx, Bq, Bk, O, lse, axis_order=None, F=None, H=None,
+                  W=None, mask_G=None, sm_scale=0.0, workspace=None, col_len=None):
+    """bsa_fo_compensate: adds the first-order compensation of each q-block
+    row's skipped keys to a forward's output, in place.  ``O``, ``lse`` as
+    :func:`forward` wrote them (``axis_order`` None: reordered [G][N][d] and
+    [G][N]) or as :func:`forward_natural` did (``axis_order`` given: natural
+    [N][G][d], any strides with unit channel stride, lse by natural token).
+    Returns (O, lse)."""
+    G, N, d, mask_G, col_len = _attn_inputs(Qp, Kp, Vp, row_ptr, col_idx, Bq, Bk, mask_G, col_len,
+                                            torch.bfloat16)
+    if F is None:
+        F, H, W = 1, 1, N
+    if F * H * W != N:
+        raise ValueError("N must equal F*H*W")
+    if lse is None:
+        raise ValueError("lse is required")
+    _check_lse(lse, G, N)
+    if axis_order is None:
+        _check_reordered_out(O, G, N, d)
+        sg, sn = 0, 0
+    else:
+        _orders_ok(axis_order, G)
+        _check_natural_out(O, G, N, d)
+        sg, sn = O.stride(1), O.stride(0)
+    need = fo_workspace(G, N, d, Bq, Bk)
+    _dev(Qp, Kp, Vp, row_ptr, col_idx, O, lse, axis_order, workspace)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Qp.device)
+    check(_lib.load().bsa_fo_compensate(
+        _ptr(Qp), _ptr(Kp), _ptr(Vp), _ptr(row_ptr), _ptr(col_idx), col_len, mask_G,
+        _ptr(axis_order), F, H, W, _ptr(O), sg, sn, _ptr(lse), G, d, Bq, Bk, float(sm_scale),
+        _ptr(workspace), workspace.numel(), _stream()))
+    return O, lse
+
+
 def debug_int8_qk(Qq, Kq, gij, Bq, Bk):
     """bsa_debug_int8_qk: exact int32 Q.K^T tiles for gij int32 [n][3] of (g, i, j)."""
     _dev(Qq, Kq, gij)

@@ -121,6 +121,23 @@ struct AttnArgs {
   OutMap out;   // out.orders == nullptr: reordered output
 };
 hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s);
+
+// ---- comp.hip --------------------------------------------------------------
+// Workspace of the first-order compensation: per-kv-block moments X (bf16
+// [G][nkp][Lp]), skip mask S (bf16 [G][nqp][nkp]), sums over the skipped set
+// C (fp32 [G][nqp][Lp]); byte offsets 256-aligned.
+struct FoLayout {
+  int nq, nk, nqp, nkp, Lp;
+  size_t x, s, c, total;
+};
+FoLayout fo_layout(int G, int N, int d, int Bq, int Bk);
+// O (bf16) and lse (fp32) as a forward wrote them (reordered, or natural
+// through om) are updated in place.
+hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
+                                int mask_G, int G, int N, int d, int Bq, int Bk, float sm_scale,
+                                uint16_t* O, float* lse, const OutMap& om, char* ws,
+                                hipStream_t s);
 hipError_t launch_forward_int8(const AttnArgs& a, hipStream_t s);
 hipError_t launch_debug_int8_qk(const int8_t* Qq, const int8_t* Kq, int G, int N, int d, int Bq,
                                 int Bk, const int32_t* gij, int n, int32_t* S, hipStream_t s);

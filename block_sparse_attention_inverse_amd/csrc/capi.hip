@@ -36,8 +36,10 @@ bool block_ok(int b) { return b == 64 || b == 128; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// runs f, turning any C++ exception into BSA_EHIP; the return type is f's
+// (int for the calls, int64_t for the size queries)
 template <typename F>
-int guarded(F&& f) {
+auto guarded(F&& f) -> decltype(f()) {
   try {
     return f();
   } catch (...) {
@@ -595,6 +597,60 @@ int bsa_mask_from_scores(const float* scores, const float* noise, float noise_sc
                                                 m.win_r0, row_ptr, col_idx, col_capacity, nnz,
                                                 workspace, as_stream(stream)),
                       "bsa_mask_from_scores");
+  });
+}
+
+int64_t bsa_fo_workspace(int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk) {
+  return guarded([&]() -> int64_t {
+    if (G <= 0 || N <= 0) return fail(BSA_EINVAL, "G and N must be positive");
+    if (d != 64 && d != 128) return fail(BSA_EUNSUPPORTED, "d must be 64 or 128");
+    if (!block_ok(Bq) || !block_ok(Bk)) return fail(BSA_EUNSUPPORTED, "Bq, Bk must be 64 or 128");
+    const int64_t nk = (static_cast<int64_t>(N) + Bk - 1) / Bk;
+    if (nk > 32768) return fail(BSA_EUNSUPPORTED, "Nkv = %lld exceeds 32768", (long long)nk);
+    return static_cast<int64_t>(bsa::fo_layout(G, N, d, Bq, Bk).total);
+  });
+}
+
+int bsa_fo_compensate(const void* Qp, const void* Kp, const void* Vp, const int32_t* row_ptr,
+                      const int32_t* col_idx, int64_t col_len, int32_t mask_G,
+                      const uint8_t* axis_order, int32_t F, int32_t H, int32_t W, void* O,
+                      int64_t nat_stride_g, int64_t nat_stride_n, float* lse, int32_t G, int32_t d,
+                      int32_t Bq, int32_t Bk, float sm_scale, void* workspace, int64_t ws_bytes,
+                      void* stream) {
+  return guarded([&]() -> int {
+    bsa::OutMap om{};
+    int32_t N = 0;
+    if (axis_order != nullptr) {
+      const int rc = natural_out(axis_order, F, H, W, G, d, nat_stride_g, nat_stride_n, om, N);
+      if (rc != BSA_OK) return rc;
+    } else {
+      if (F <= 0 || H <= 0 || W <= 0) return fail(BSA_EINVAL, "F, H, W must be positive");
+      const int64_t n64 = static_cast<int64_t>(F) * H * W;
+      if (n64 >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "N = F*H*W must be < 2^31");
+      N = static_cast<int32_t>(n64);
+    }
+    int rc = attn_common(Qp, Kp, Vp, row_ptr, col_idx, col_len, mask_G, O, G, N, d, Bq, Bk, 2);
+    if (rc != BSA_OK) return rc;
+    if (!lse) return fail(BSA_EINVAL, "lse is required (the forward's log-sum-exp is updated)");
+    if (!aligned(lse, 4)) return fail(BSA_EINVAL, "lse must be 4-byte aligned");
+    if (!std::isfinite(sm_scale)) return fail(BSA_EINVAL, "sm_scale must be finite");
+    const int64_t need = bsa_fo_workspace(G, N, d, Bq, Bk);
+    if (need < 0) return static_cast<int>(need);
+    if (!workspace) return fail(BSA_EINVAL, "NULL workspace");
+    if (!aligned(workspace, 256)) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+      return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
+    const bsa::FoLayout L = bsa::fo_layout(G, N, d, Bq, Bk);
+    if (static_cast<int64_t>(G) * (L.nqp / 64) * (L.Lp / 256) >= (1ll << 31) ||
+        static_cast<int64_t>(G) * L.nkp >= (1ll << 31))
+      return fail(BSA_EUNSUPPORTED, "grid too large");
+    return hip_status(bsa::launch_fo_compensate(static_cast<const uint16_t*>(Qp),
+                                                static_cast<const uint16_t*>(Kp),
+                                                static_cast<const uint16_t*>(Vp), row_ptr, col_idx,
+                                                col_len, mask_G, G, N, d, Bq, Bk, sm_scale,
+                                                static_cast<uint16_t*>(O), lse, om,
+                                                static_cast<char*>(workspace), as_stream(stream)),
+                      "bsa_fo_compensate");
   });
 }
 

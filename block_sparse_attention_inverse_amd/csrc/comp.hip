@@ -1,0 +1,351 @@
+// comp.hip — first-order compensation of the skipped keys, applied to the
+// output of a block-sparse forward.
+//
+// PASA review (pith.science, arXiv 2604.12219), Figure 2 caption: grouped
+// first-order compensation for the blocks outside the selected set; the
+// keys outside a query's selected set are skipped with coarse
+// approximations.  The pages give neither the groups nor the expansion
+// point; here the group is everything a q-block row skips.  For q-block i
+// of head g, U = the real tokens of the kv-blocks not in its CSR row,
+// n = |U|, kbar = sum_U k / n, Vhat = sum_U v, M = sum_U (k - kbar) v^T.  The
+// first-order expansion of exp(s q.k) around kbar adds, for every real row
+// r of the q-block, exp(s q_r.kbar) (Vhat + s M^T q_r) to the numerator and
+// exp(s q_r.kbar) n to the denominator of its softmax (the first-order term
+// of the denominator vanishes).  The forward already wrote O = num/den and
+// lse = ln den of the kept blocks; the update reads them back:
+//   mu  = max(lse, a + ln n),  a = s q_r.kbar
+//   den = exp(lse - mu) + n exp(a - mu)
+//   O'  = (O exp(lse - mu) + exp(a - mu) (Vhat + s M^T q_r)) / den,
+//   lse' = mu + ln den.
+//
+// Four steps:
+//   1. kv_moments_kernel: per kv-block j, X_j = [sum k v^T (d x d, row-major)
+//      | sum k | sum v | rows | 0...], bf16, one row of length Lp;
+//   2. skip_mask_kernel: S[i][j] = 1 for the kv-blocks row i skips, else 0
+//      (bf16; rows padded to a multiple of 64, columns to one of 32, with zeros);
+//   3. skip_gemm_kernel: C = S . X per head (bf16 MFMA, fp32 accumulation):
+//      row i of C holds the sums over U_i, so M_i = C_kv - kbar Vhat^T;
+//   4. apply_kernel: one workgroup per q-block, the update above.
+// Step 3 is the only heavy one: 2 * nq * nk * Lp flops per head.
+#include "bsa_device.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+namespace {
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kCompThreads = 256;
+constexpr int kTileI = 64;   // C rows (q-blocks) per GEMM workgroup
+constexpr int kTileC = 256;  // C columns per GEMM workgroup (64 per wave)
+constexpr int kStageJ = 32;  // kv-blocks per LDS stage
+constexpr int kPitchX = kStageJ + 8;  // bf16 per transposed X row in LDS (16-byte aligned rows)
+constexpr int kPitchS = kStageJ + 8;
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return static_cast<uint16_t>(f32_to_bf16_bits(x)); }
+
+// 1. per kv-block moments.  Tokens are taken 64 at a time through LDS; thread
+// (ta, tb) owns a (D/16) x (D/16) block of sum k v^T.
+template <int D>
+__global__ __launch_bounds__(kCompThreads) void kv_moments_kernel(const uint16_t* __restrict__ K,
+                                                                  const uint16_t* __restrict__ V,
+                                                                  int N, int Bk, int nk, int nkp,
+                                                                  int Lp, uint16_t* __restrict__ X) {
+  constexpr int RB = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t kl[64][D];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[64][D];
+  const int g = blockIdx.x / nkp, j = blockIdx.x % nkp;
+  const int t = threadIdx.x;
+  uint16_t* xr = X + (static_cast<int64_t>(g) * nkp + j) * Lp;
+  if (j >= nk) {
+    for (int c = t; c < Lp; c += kCompThreads) xr[c] = 0;
+    return;
+  }
+  const int r0 = j * Bk, r1 = min(N, r0 + Bk);
+  const uint16_t* kh = K + static_cast<int64_t>(g) * N * D;
+  const uint16_t* vh = V + static_cast<int64_t>(g) * N * D;
+  const int ta = t / 16, tb = t % 16;
+  float acc[RB][RB];
+#pragma unroll
+  for (int a = 0; a < RB; a++)
+#pragma unroll
+    for (int b = 0; b < RB; b++) acc[a][b] = 0.0f;
+  float ks = 0.0f, vs = 0.0f;  // thread t < D: sum k[.][t]; D <= t < 2D: sum v[.][t - D]
+  for (int c0 = r0; c0 < r1; c0 += 64) {
+    const int nr = min(64, r1 - c0);
+    __syncthreads();
+    for (int e = t; e < nr * D; e += kCompThreads) {
+      const int rr = e / D, cc = e % D;
+      kl[rr][cc] = kh[static_cast<int64_t>(c0 + rr) * D + cc];
+      vl[rr][cc] = vh[static_cast<int64_t>(c0 + rr) * D + cc];
+    }
+    __syncthreads();
+    for (int rr = 0; rr < nr; rr++) {
+      float kv[RB], vv[RB];
+#pragma unroll
+      for (int a = 0; a < RB; a++) kv[a] = bf16_bits_to_f32(kl[rr][RB * ta + a]);
+#pragma unroll
+      for (int b = 0; b < RB; b++) vv[b] = bf16_bits_to_f32(vl[rr][RB * tb + b]);
+#pragma unroll
+      for (int a = 0; a < RB; a++)
+#pragma unroll
+        for (int b = 0; b < RB; b++) acc[a][b] = __builtin_fmaf(kv[a], vv[b], acc[a][b]);
+      if (t < D) ks += bf16_bits_to_f32(kl[rr][t]);
+      else if (t < 2 * D) vs += bf16_bits_to_f32(vl[rr][t - D]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < RB; a++)
+#pragma unroll
+    for (int b = 0; b < RB; b++) xr[(RB * ta + a) * D + RB * tb + b] = bf16_bits(acc[a][b]);
+  if (t < D) xr[D * D + t] = bf16_bits(ks);
+  else if (t < 2 * D) xr[D * D + t] = bf16_bits(vs);  // D*D + D + (t - D)
+  if (t == 0) xr[D * D + 2 * D] = bf16_bits(static_cast<float>(r1 - r0));
+  for (int c = D * D + 2 * D + 1 + t; c < Lp; c += kCompThreads) xr[c] = 0;
+}
+
+// 2. S[g][i][j] = 1 for the kv-blocks q-block row i skips (padding: 0)
+__global__ __launch_bounds__(kCompThreads) void skip_mask_kernel(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
+    int mask_G, int nq, int nk, int nqp, int nkp, uint16_t* __restrict__ S) {
+  extern __shared__ uint16_t srow[];  // [nkp]
+  const int g = blockIdx.x / nqp, i = blockIdx.x % nqp;
+  const int t = threadIdx.x;
+  const uint16_t one = 0x3F80;
+  for (int j = t; j < nkp; j += kCompThreads) srow[j] = (i < nq && j < nk) ? one : 0;
+  __syncthreads();
+  if (i < nq) {
+    const int64_t r = static_cast<int64_t>(g % mask_G) * nq + i;
+    int64_t e0 = row_ptr[r], e1 = row_ptr[r + 1];
+    e0 = e0 < 0 ? 0 : (e0 > col_len ? col_len : e0);
+    e1 = e1 < e0 ? e0 : (e1 > col_len ? col_len : e1);
+    for (int64_t e = e0 + t; e < e1; e += kCompThreads) {
+      const int j = col_idx[e];
+      if (static_cast<unsigned>(j) < static_cast<unsigned>(nk)) srow[j] = 0;
+    }
+  }
+  __syncthreads();
+  uint16_t* out = S + (static_cast<int64_t>(g) * nqp + i) * nkp;
+  for (int j = t; j < nkp; j += kCompThreads) out[j] = srow[j];
+}
+
+// 3. C[g][i][c] = sum_j S[g][i][j] X[g][j][c].  Products C^T = X^T . S^T on
+// v_mfma_f32_32x32x16_bf16: A = X^T (32 columns x 16 kv-blocks) read from a
+// transposed LDS copy, B = S^T (16 kv-blocks x 32 rows).  Wave w owns
+// columns [64w, 64w + 64) of the tile and all 64 rows: 2 x 2 accumulators;
+// lane l of an accumulator holds row ib + l%32 and columns
+// cb + 8(r/4) + 4(l/32) + r%4.
+__global__ __launch_bounds__(kCompThreads) void skip_gemm_kernel(const uint16_t* __restrict__ S,
+                                                                 const uint16_t* __restrict__ X,
+                                                                 int nqp, int nkp, int Lp,
+                                                                 int tiles_i, int tiles_c,
+                                                                 float* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) uint16_t xt[kTileC][kPitchX];
+  __shared__ __attribute__((aligned(16))) uint16_t sl[kTileI][kPitchS];
+  const int per_head = tiles_i * tiles_c;
+  const int g = blockIdx.x / per_head, rem = blockIdx.x % per_head;
+  const int ti = rem / tiles_c, tc = rem % tiles_c;
+  const int i0 = ti * kTileI, c0 = tc * kTileC;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const uint16_t* Sg = S + static_cast<int64_t>(g) * nqp * nkp;
+  const uint16_t* Xg = X + static_cast<int64_t>(g) * nkp * Lp;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++) acc[a][b] = f32x16{};
+  for (int j0 = 0; j0 < nkp; j0 += kStageJ) {
+    __syncthreads();
+    {
+      // X rows j0..j0+31, columns c0..c0+255: thread t takes row t/8 and
+      // 32 columns, stored transposed
+      const int jr = t / 8, cc = (t % 8) * 32;
+      const uint16_t* src = Xg + static_cast<int64_t>(j0 + jr) * Lp + c0 + cc;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * q);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          xt[cc + 8 * q + 2 * e][jr] = static_cast<uint16_t>(wv[e] & 0xFFFFu);
+          xt[cc + 8 * q + 2 * e + 1][jr] = static_cast<uint16_t>(wv[e] >> 16);
+        }
+      }
+      // S rows i0..i0+63, kv-blocks j0..j0+31: 16 bytes per thread
+      const int ir = t / 4, jc = (t % 4) * 8;
+      *reinterpret_cast<uint4*>(&sl[ir][jc]) =
+          *reinterpret_cast<const uint4*>(Sg + static_cast<int64_t>(i0 + ir) * nkp + j0 + jc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kStageJ / 16; ks++) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int cbk = 0; cbk < 2; cbk++)
+        a[cbk] = *reinterpret_cast<const bf16x8*>(&xt[64 * w + 32 * cbk + l32][16 * ks + 8 * h]);
+#pragma unroll
+      for (int ib = 0; ib < 2; ib++)
+        b[ib] = *reinterpret_cast<const bf16x8*>(&sl[32 * ib + l32][16 * ks + 8 * h]);
+#pragma unroll
+      for (int cbk = 0; cbk < 2; cbk++)
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++)
+          acc[cbk][ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cbk], b[ib], acc[cbk][ib], 0, 0, 0);
+    }
+  }
+  float* Cg = C + static_cast<int64_t>(g) * nqp * Lp;
+#pragma unroll
+  for (int cbk = 0; cbk < 2; cbk++)
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++) {
+      const int i = i0 + 32 * ib + l32;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const int c = c0 + 64 * w + 32 * cbk + 8 * r4 + 4 * h;
+        float4 v;
+        v.x = acc[cbk][ib][4 * r4 + 0];
+        v.y = acc[cbk][ib][4 * r4 + 1];
+        v.z = acc[cbk][ib][4 * r4 + 2];
+        v.w = acc[cbk][ib][4 * r4 + 3];
+        *reinterpret_cast<float4*>(Cg + static_cast<int64_t>(i) * Lp + c) = v;
+      }
+    }
+}
+
+// 4. the update of O and lse, one workgroup per (head, q-block).  Per row
+// (thread t < rows): a = s q.kbar, the weights of the old and the new terms,
+// and the new lse; then thread t owns output channel b = t % D of rows
+// t / D, t / D + 256/D, ...: y = M^T q (M[a][b] = C_kv[a][b] - kbar_a Vhat_b,
+// read from C), and O' = O wo' + wc' (Vhat + s y) with the weights divided
+// by the new denominator.
+template <int D>
+__global__ __launch_bounds__(kCompThreads) void apply_kernel(
+    const uint16_t* __restrict__ Q, const float* __restrict__ C, int N, int Bq, int nq, int nqp,
+    int Lp, float sm, uint16_t* __restrict__ O, float* __restrict__ lse, OutMap om) {
+  constexpr int RG = kCompThreads / D;  // row groups
+  constexpr int kMaxR = 128 / RG;       // rows per thread (Bq <= 128)
+  __shared__ float kbar[D], vhat[D];
+  __shared__ __attribute__((aligned(16))) uint16_t ql[128][D];
+  __shared__ float w_old[128], w_new[128];
+  __shared__ float s_n;
+  const int g = blockIdx.x / nq, i = blockIdx.x % nq;
+  const int t = threadIdx.x;
+  const float* Ci = C + (static_cast<int64_t>(g) * nqp + i) * Lp;
+  const int r0 = i * Bq, nr = min(Bq, N - r0);
+  if (t == 0) s_n = Ci[D * D + 2 * D];
+  __syncthreads();
+  const float n = s_n;
+  if (!(n > 0.5f)) return;  // nothing skipped: O and lse stay as they are
+  if (t < D) {
+    kbar[t] = Ci[D * D + t] / n;
+    vhat[t] = Ci[D * D + D + t];
+  }
+  for (int e = t; e < nr * (D / 8); e += kCompThreads) {
+    const int rr = e / (D / 8), cc = 8 * (e % (D / 8));
+    *reinterpret_cast<uint4*>(&ql[rr][cc]) =
+        *reinterpret_cast<const uint4*>(Q + (static_cast<int64_t>(g) * N + r0 + rr) * D + cc);
+  }
+  __syncthreads();
+  const float ln_n = logf(n);
+  for (int rr = t; rr < nr; rr += kCompThreads) {
+    float a = 0.0f;
+    for (int c = 0; c < D; c++) a = __builtin_fmaf(bf16_bits_to_f32(ql[rr][c]), kbar[c], a);
+    a *= sm;
+    int64_t li;
+    (void)out_row<D>(O, om.orders, om.F, om.H, om.W, om.sg, om.sn, g, N, r0 + rr, li);
+    const float lo = lse[li];
+    const float mu = fmaxf(lo, a + ln_n);
+    const float wo = lo > -INFINITY ? expf(lo - mu) : 0.0f;
+    const float wc = expf(a - mu);
+    const float den = wo + wc * n;
+    w_old[rr] = wo / den;
+    w_new[rr] = wc / den;
+    lse[li] = mu + logf(den);  // only this thread touches lse[li]
+  }
+  __syncthreads();
+  const int b = t % D, rg = t / D;
+  float y[kMaxR];
+#pragma unroll
+  for (int k = 0; k < kMaxR; k++) y[k] = 0.0f;
+  const float vb = vhat[b];
+  for (int a0 = 0; a0 < D; a0 += 8) {
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) m[e] = Ci[(a0 + e) * D + b] - kbar[a0 + e] * vb;
+#pragma unroll
+    for (int k = 0; k < kMaxR; k++) {
+      const int rr = rg + RG * k;
+      if (rr < nr) {
+        const uint4 qv = *reinterpret_cast<const uint4*>(&ql[rr][a0]);
+        const uint32_t wv[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          y[k] = __builtin_fmaf(m[2 * e], bf16_bits_to_f32(wv[e] & 0xFFFFu), y[k]);
+          y[k] = __builtin_fmaf(m[2 * e + 1], bf16_bits_to_f32(wv[e] >> 16), y[k]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxR; k++) {
+    const int rr = rg + RG * k;
+    if (rr >= nr) continue;
+    int64_t li;
+    uint16_t* op = out_row<D>(O, om.orders, om.F, om.H, om.W, om.sg, om.sn, g, N, r0 + rr, li);
+    const float old = bf16_bits_to_f32(op[b]);
+    op[b] = bf16_bits(__builtin_fmaf(old, w_old[rr], w_new[rr] * __builtin_fmaf(sm, y[k], vb)));
+  }
+}
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+FoLayout fo_layout(int G, int N, int d, int Bq, int Bk) {
+  FoLayout L{};
+  L.nq = (N + Bq - 1) / Bq;
+  L.nk = (N + Bk - 1) / Bk;
+  L.nqp = round_up(L.nq, kTileI);
+  L.nkp = round_up(L.nk, kStageJ);
+  L.Lp = round_up(d * d + 2 * d + 1, kTileC);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 255) & ~static_cast<size_t>(255);
+    return o;
+  };
+  L.x = take(sizeof(uint16_t) * static_cast<size_t>(G) * L.nkp * L.Lp);
+  L.s = take(sizeof(uint16_t) * static_cast<size_t>(G) * L.nqp * L.nkp);
+  L.c = take(sizeof(float) * static_cast<size_t>(G) * L.nqp * L.Lp);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
+                                int mask_G, int G, int N, int d, int Bq, int Bk, float sm_scale,
+                                uint16_t* O, float* lse, const OutMap& om, char* ws,
+                                hipStream_t s) {
+  const FoLayout L = fo_layout(G, N, d, Bq, Bk);
+  auto* X = reinterpret_cast<uint16_t*>(ws + L.x);
+  auto* S = reinterpret_cast<uint16_t*>(ws + L.s);
+  auto* C = reinterpret_cast<float*>(ws + L.c);
+  const float sm = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d));
+  const uint32_t gm = static_cast<uint32_t>(G) * L.nkp;
+  if (d == 128) kv_moments_kernel<128><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
+  else kv_moments_kernel<64><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
+  skip_mask_kernel<<<static_cast<uint32_t>(G) * L.nqp, kCompThreads, sizeof(uint16_t) * L.nkp, s>>>(
+      row_ptr, col_idx, col_len, mask_G, L.nq, L.nk, L.nqp, L.nkp, S);
+  const int ti = L.nqp / kTileI, tc = L.Lp / kTileC;
+  skip_gemm_kernel<<<static_cast<uint32_t>(G) * ti * tc, kCompThreads, 0, s>>>(S, X, L.nqp, L.nkp, L.Lp,
+                                                                             ti, tc, C);
+  const uint32_t ga = static_cast<uint32_t>(G) * L.nq;
+  if (d == 128)
+    apply_kernel<128><<<ga, kCompThreads, 0, s>>>(Q, C, N, Bq, L.nq, L.nqp, L.Lp, sm, O, lse, om);
+  else
+    apply_kernel<64><<<ga, kCompThreads, 0, s>>>(Q, C, N, Bq, L.nq, L.nqp, L.Lp, sm, O, lse, om);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

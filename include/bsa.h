@@ -309,6 +309,38 @@ int bsa_forward_int8_natural(const int8_t *Qq, const float *sQ, const int8_t *Kq
                              int64_t nat_stride_g, int64_t nat_stride_n, float *lse, int32_t G,
                              int32_t d, int32_t Bq, int32_t Bk, float sm_scale, void *stream);
 
+/* bsa_fo_workspace — bytes of device workspace bsa_fo_compensate needs
+ * (per-kv-block moments, the skip mask and the sums over each q-block
+ * row's skipped set: about G*Nkv*d*d*2 + G*Nq*d*d*4 bytes), or a negative
+ * status (d not in {64, 128}, B not in {64, 128}, Nkv > 32768). */
+int64_t bsa_fo_workspace(int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk);
+
+/* bsa_fo_compensate — first-order compensation of the skipped keys (PASA
+ * review, Figure 2 caption: grouped first-order compensation for the blocks
+ * outside the selected set), applied to what bsa_forward (axis_order NULL:
+ * O and lse reordered [G][N][d], [G][N]) or bsa_forward_natural (axis_order
+ * given: natural-order O at n*nat_stride_n + g*nat_stride_g, lse [G][N] by
+ * natural token) wrote with the same Qp, Kp, Vp and mask; N = F*H*W.  The
+ * group is everything a q-block row skips: for q-block i, U = the real
+ * tokens of the kv-blocks not in its CSR row, n = |U|, kbar = sum_U k / n,
+ * Vhat = sum_U v, M = sum_U (k - kbar) v^T.  Every real row r of the
+ * q-block gains exp(a) (Vhat + s M^T q_r) in the numerator and exp(a) n in
+ * the denominator of its softmax, a = s q_r.kbar (the first-order Taylor
+ * term of exp(s q.k) around kbar, summed over U), i.e. with the forward's
+ * O, lse:  mu = max(lse, a + ln n), den = exp(lse - mu) + n exp(a - mu),
+ *   O <- (O exp(lse - mu) + exp(a - mu) (Vhat + s M^T q_r)) / den,
+ *   lse <- mu + ln den.
+ * A row whose q-block skips nothing is left unchanged.  The sums over U use
+ * per-kv-block moments rounded to bf16 and accumulated in fp32.  lse must
+ * not be NULL.  workspace: >= bsa_fo_workspace(...), 256-byte aligned.
+ * Errors: EINVAL, EUNSUPPORTED, ECAPACITY (workspace), EHIP. */
+int bsa_fo_compensate(const void *Qp, const void *Kp, const void *Vp, const int32_t *row_ptr,
+                      const int32_t *col_idx, int64_t col_len, int32_t mask_G,
+                      const uint8_t *axis_order, int32_t F, int32_t H, int32_t W, void *O,
+                      int64_t nat_stride_g, int64_t nat_stride_n, float *lse, int32_t G, int32_t d,
+                      int32_t Bq, int32_t Bk, float sm_scale, void *workspace, int64_t ws_bytes,
+                      void *stream);
+
 /* bsa_debug_int8_qk — runs bsa_forward_int8's own Q.K^T tile routine on n
  * chosen tiles and writes the exact int32 products.  gij: device
  * int32[n][3] of (g, i, j); S: int32[n][Bq][Bk], S[t][r][c] =
