@@ -348,3 +348,23 @@ def test_noalloc_mask_refuses_shapes_beyond_its_scratch(lib):
     assert b"scratch" in msg and str(need).encode() in msg and b"50331648" in msg
     assert lib.bsa_build_mask_pooled_noalloc(None, fake, 40, 21, 45, 80, 128, fake, ctypes.byref(p),
                                              fake, fake, cap, fake, None) == -1
+
+
+def test_compensation_argument_errors(lib):
+    """Host checks of the first-order compensation; none reaches HIP."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    F = ctypes.c_float
+    G, d, Fr, Hr, Wr = 2, 128, 1, 4, 64
+    N = Fr * Hr * Wr
+    need = lib.bsa_fo_workspace(G, N, d, 128, 64)
+    assert need > 0
+    assert lib.bsa_fo_workspace(G, N, 96, 128, 64) == -2
+    def call(lse=fake, ws_bytes=need, ws=fake, orders=None):
+        return lib.bsa_fo_compensate(fake, fake, fake, fake, fake, 10, G, orders, Fr, Hr, Wr, fake,
+                                     d, G * d, lse, G, d, 128, 64, F(0), ws, ws_bytes, None)
+    assert call(lse=None) == -1
+    assert b"lse is required" in lib.bsa_last_error()
+    assert call(ws_bytes=need - 1) == -3
+    assert call(ws=P(0x1010)) == -1  # not 256-byte aligned
+    assert call(orders=fake, ws_bytes=need - 1) == -3
