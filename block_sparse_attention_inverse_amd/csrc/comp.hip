@@ -38,9 +38,7 @@ namespace {
 constexpr int kCompThreads = 256;
 constexpr int kTileI = 64;   // C rows (q-blocks) per GEMM workgroup
 constexpr int kTileC = 256;  // C columns per GEMM workgroup (64 per wave)
-constexpr int kStageJ = 32;  // kv-blocks per LDS stage
-constexpr int kPitchX = kStageJ + 8;  // bf16 per transposed X row in LDS (16-byte aligned rows)
-constexpr int kPitchS = kStageJ + 8;
+constexpr int kStageJ = 64;  // kv-block padding (the GEMM's stage)
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return static_cast<uint16_t>(f32_to_bf16_bits(x)); }
 
@@ -130,18 +128,71 @@ __global__ __launch_bounds__(kCompThreads) void skip_mask_kernel(
 }
 
 // 3. C[g][i][c] = sum_j S[g][i][j] X[g][j][c].  Products C^T = X^T . S^T on
-// v_mfma_f32_32x32x16_bf16: A = X^T (32 columns x 16 kv-blocks) read from a
-// transposed LDS copy, B = S^T (16 kv-blocks x 32 rows).  Wave w owns
-// columns [64w, 64w + 64) of the tile and all 64 rows: 2 x 2 accumulators;
-// lane l of an accumulator holds row ib + l%32 and columns
+// v_mfma_f32_32x32x16_bf16: A = X^T (32 columns x 16 kv-blocks), B = S^T
+// (16 kv-blocks x 32 rows).  X is row-major (kv-block j, column c), so each
+// stage of 64 kv-blocks x 256 columns is transposed on its way into LDS: a
+// thread loads an 8 x 8 block (8 rows, 16 bytes each), transposes it in
+// registers and writes 8 columns of 8 kv-blocks (16 bytes each).  The next
+// stage's loads are issued before the current stage's products.  Wave w
+// owns columns [64w, 64w + 64) of the tile and all 64 rows: 2 x 2
+// accumulators; lane l of an accumulator holds row ib + l%32 and columns
 // cb + 8(r/4) + 4(l/32) + r%4.
+constexpr int kGemmJ = 64;              // kv-blocks per stage
+constexpr int kPitchG = kGemmJ + 8;     // bf16 per LDS row (16-byte aligned, staggered banks)
+
+struct GemmStage {
+  uint4 x[8];  // rows 8*(t/32) .. +7, columns 8*(t%32) .. +7 of the X stage
+  uint4 s[2];  // row t/4, kv-blocks 16*(t%4) .. +15 of the S stage
+};
+
+__device__ __forceinline__ void gemm_load(const uint16_t* Xg, const uint16_t* Sg, int Lp, int nkp,
+                                          int i0, int c0, int j0, GemmStage& st) {
+  const int t = threadIdx.x;
+  const int jr = 8 * (t / 32), cc = 8 * (t % 32);
+#pragma unroll
+  for (int r = 0; r < 8; r++)
+    st.x[r] = *reinterpret_cast<const uint4*>(Xg + static_cast<int64_t>(j0 + jr + r) * Lp + c0 + cc);
+  const uint16_t* sp = Sg + static_cast<int64_t>(i0 + t / 4) * nkp + j0 + 16 * (t % 4);
+  st.s[0] = *reinterpret_cast<const uint4*>(sp);
+  st.s[1] = *reinterpret_cast<const uint4*>(sp + 8);
+}
+
+// word w of column e after the transpose holds rows 2w, 2w + 1 of column e
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t word(const uint4& v, int w) {
+  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ void gemm_store(const GemmStage& st, uint16_t (*xt)[kPitchG],
+                                           uint16_t (*sl)[kPitchG]) {
+  const int t = threadIdx.x;
+  const int jr = 8 * (t / 32), cc = 8 * (t % 32);
+#pragma unroll
+  for (int wc = 0; wc < 4; wc++) {  // input word wc holds columns 2wc, 2wc + 1
+    uint4 lo, hi;
+    lo.x = lo_pair(word(st.x[0], wc), word(st.x[1], wc));
+    lo.y = lo_pair(word(st.x[2], wc), word(st.x[3], wc));
+    lo.z = lo_pair(word(st.x[4], wc), word(st.x[5], wc));
+    lo.w = lo_pair(word(st.x[6], wc), word(st.x[7], wc));
+    hi.x = hi_pair(word(st.x[0], wc), word(st.x[1], wc));
+    hi.y = hi_pair(word(st.x[2], wc), word(st.x[3], wc));
+    hi.z = hi_pair(word(st.x[4], wc), word(st.x[5], wc));
+    hi.w = hi_pair(word(st.x[6], wc), word(st.x[7], wc));
+    *reinterpret_cast<uint4*>(&xt[cc + 2 * wc][jr]) = lo;
+    *reinterpret_cast<uint4*>(&xt[cc + 2 * wc + 1][jr]) = hi;
+  }
+  *reinterpret_cast<uint4*>(&sl[t / 4][16 * (t % 4)]) = st.s[0];
+  *reinterpret_cast<uint4*>(&sl[t / 4][16 * (t % 4) + 8]) = st.s[1];
+}
+
 __global__ __launch_bounds__(kCompThreads) void skip_gemm_kernel(const uint16_t* __restrict__ S,
                                                                  const uint16_t* __restrict__ X,
                                                                  int nqp, int nkp, int Lp,
                                                                  int tiles_i, int tiles_c,
                                                                  float* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) uint16_t xt[kTileC][kPitchX];
-  __shared__ __attribute__((aligned(16))) uint16_t sl[kTileI][kPitchS];
+  __shared__ __attribute__((aligned(16))) uint16_t xt[kTileC][kPitchG];
+  __shared__ __attribute__((aligned(16))) uint16_t sl[kTileI][kPitchG];
   const int per_head = tiles_i * tiles_c;
   const int g = blockIdx.x / per_head, rem = blockIdx.x % per_head;
   const int ti = rem / tiles_c, tc = rem % tiles_c;
@@ -155,31 +206,15 @@ __global__ __launch_bounds__(kCompThreads) void skip_gemm_kernel(const uint16_t*
   for (int a = 0; a < 2; a++)
 #pragma unroll
     for (int b = 0; b < 2; b++) acc[a][b] = f32x16{};
-  for (int j0 = 0; j0 < nkp; j0 += kStageJ) {
+  GemmStage st;
+  gemm_load(Xg, Sg, Lp, nkp, i0, c0, 0, st);
+  for (int j0 = 0; j0 < nkp; j0 += kGemmJ) {
+    __syncthreads();  // the previous stage's operand reads are done
+    gemm_store(st, xt, sl);
     __syncthreads();
-    {
-      // X rows j0..j0+31, columns c0..c0+255: thread t takes row t/8 and
-      // 32 columns, stored transposed
-      const int jr = t / 8, cc = (t % 8) * 32;
-      const uint16_t* src = Xg + static_cast<int64_t>(j0 + jr) * Lp + c0 + cc;
+    if (j0 + kGemmJ < nkp) gemm_load(Xg, Sg, Lp, nkp, i0, c0, j0 + kGemmJ, st);
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * q);
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          xt[cc + 8 * q + 2 * e][jr] = static_cast<uint16_t>(wv[e] & 0xFFFFu);
-          xt[cc + 8 * q + 2 * e + 1][jr] = static_cast<uint16_t>(wv[e] >> 16);
-        }
-      }
-      // S rows i0..i0+63, kv-blocks j0..j0+31: 16 bytes per thread
-      const int ir = t / 4, jc = (t % 4) * 8;
-      *reinterpret_cast<uint4*>(&sl[ir][jc]) =
-          *reinterpret_cast<const uint4*>(Sg + static_cast<int64_t>(i0 + ir) * nkp + j0 + jc);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < kStageJ / 16; ks++) {
+    for (int ks = 0; ks < kGemmJ / 16; ks++) {
       bf16x8 a[2], b[2];
 #pragma unroll
       for (int cbk = 0; cbk < 2; cbk++)
@@ -213,26 +248,32 @@ __global__ __launch_bounds__(kCompThreads) void skip_gemm_kernel(const uint16_t*
     }
 }
 
-// 4. the update of O and lse, one workgroup per (head, q-block).  Per row
-// (thread t < rows): a = s q.kbar, the weights of the old and the new terms,
-// and the new lse; then thread t owns output channel b = t % D of rows
-// t / D, t / D + 256/D, ...: y = M^T q (M[a][b] = C_kv[a][b] - kbar_a Vhat_b,
-// read from C), and O' = O wo' + wc' (Vhat + s y) with the weights divided
-// by the new denominator.
+// 4. the update of O and lse, one workgroup per (head, q-block).
+//   a. per row (thread t < rows): a = s q.kbar, the old and new terms'
+//      weights divided by the new denominator, the new lse;
+//   b. M^T (bf16, [b][a]) into LDS: M[a][b] = C_kv[a][b] - kbar_a Vhat_b;
+//   c. Y = Q_i M on v_mfma_f32_32x32x16_bf16: wave w takes rows 32w..32w+31
+//      (A = Q rows from global memory, B = M^T rows from LDS); lane l of
+//      accumulator bb holds channel b = 32bb + l%32 of rows
+//      32w + 8(r/4) + 4(l/32) + r%4;
+//   d. O' = O w_old + w_new (Vhat + s y), written where the forward wrote O.
 template <int D>
-__global__ __launch_bounds__(kCompThreads) void apply_kernel(
+__global__ __launch_bounds__(kCompThreads, 2) void apply_kernel(
     const uint16_t* __restrict__ Q, const float* __restrict__ C, int N, int Bq, int nq, int nqp,
     int Lp, float sm, uint16_t* __restrict__ O, float* __restrict__ lse, OutMap om) {
-  constexpr int RG = kCompThreads / D;  // row groups
-  constexpr int kMaxR = 128 / RG;       // rows per thread (Bq <= 128)
+  constexpr int NB = D / 32;      // 32-channel blocks of the output
+  constexpr int PM = D + 8;       // bf16 per LDS row of M^T
   __shared__ float kbar[D], vhat[D];
-  __shared__ __attribute__((aligned(16))) uint16_t ql[128][D];
+  __shared__ __attribute__((aligned(16))) uint16_t mt[D][PM];
   __shared__ float w_old[128], w_new[128];
+  __shared__ int64_t row_off[128];  // element offset of each row's output
   __shared__ float s_n;
   const int g = blockIdx.x / nq, i = blockIdx.x % nq;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
   const float* Ci = C + (static_cast<int64_t>(g) * nqp + i) * Lp;
   const int r0 = i * Bq, nr = min(Bq, N - r0);
+  const uint16_t* Qi = Q + (static_cast<int64_t>(g) * N + r0) * D;
   if (t == 0) s_n = Ci[D * D + 2 * D];
   __syncthreads();
   const float n = s_n;
@@ -241,19 +282,23 @@ __global__ __launch_bounds__(kCompThreads) void apply_kernel(
     kbar[t] = Ci[D * D + t] / n;
     vhat[t] = Ci[D * D + D + t];
   }
-  for (int e = t; e < nr * (D / 8); e += kCompThreads) {
-    const int rr = e / (D / 8), cc = 8 * (e % (D / 8));
-    *reinterpret_cast<uint4*>(&ql[rr][cc]) =
-        *reinterpret_cast<const uint4*>(Q + (static_cast<int64_t>(g) * N + r0 + rr) * D + cc);
-  }
   __syncthreads();
+  // a. per-row weights and the new lse
   const float ln_n = logf(n);
   for (int rr = t; rr < nr; rr += kCompThreads) {
     float a = 0.0f;
-    for (int c = 0; c < D; c++) a = __builtin_fmaf(bf16_bits_to_f32(ql[rr][c]), kbar[c], a);
+    for (int c0 = 0; c0 < D; c0 += 8) {
+      const uint4 qv = *reinterpret_cast<const uint4*>(Qi + static_cast<int64_t>(rr) * D + c0);
+      const uint32_t wv[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        a = __builtin_fmaf(bf16_bits_to_f32(wv[e] & 0xFFFFu), kbar[c0 + 2 * e], a);
+        a = __builtin_fmaf(bf16_bits_to_f32(wv[e] >> 16), kbar[c0 + 2 * e + 1], a);
+      }
+    }
     a *= sm;
     int64_t li;
-    (void)out_row<D>(O, om.orders, om.F, om.H, om.W, om.sg, om.sn, g, N, r0 + rr, li);
+    row_off[rr] = out_row<D>(O, om.orders, om.F, om.H, om.W, om.sg, om.sn, g, N, r0 + rr, li) - O;
     const float lo = lse[li];
     const float mu = fmaxf(lo, a + ln_n);
     const float wo = lo > -INFINITY ? expf(lo - mu) : 0.0f;
@@ -263,38 +308,59 @@ __global__ __launch_bounds__(kCompThreads) void apply_kernel(
     w_new[rr] = wc / den;
     lse[li] = mu + logf(den);  // only this thread touches lse[li]
   }
+  // b. M^T into LDS, 8 consecutive a per 16-byte write
+  for (int e = t; e < D * (D / 8); e += kCompThreads) {
+    const int b = e % D, a0 = 8 * (e / D);
+    const float vb = vhat[b];
+    uint32_t pk[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float m0 = Ci[(a0 + 2 * q) * D + b] - kbar[a0 + 2 * q] * vb;
+      const float m1 = Ci[(a0 + 2 * q + 1) * D + b] - kbar[a0 + 2 * q + 1] * vb;
+      pk[q] = f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);
+    }
+    *reinterpret_cast<uint4*>(&mt[b][a0]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
   __syncthreads();
-  const int b = t % D, rg = t / D;
-  float y[kMaxR];
+  // c. Y = Q_i M for the wave's 32 rows
+  const int rb = 32 * w;
+  if (rb >= nr) return;  // no later barrier
+  f32x16 acc[NB];
 #pragma unroll
-  for (int k = 0; k < kMaxR; k++) y[k] = 0.0f;
-  const float vb = vhat[b];
-  for (int a0 = 0; a0 < D; a0 += 8) {
-    float m[8];
+  for (int bb = 0; bb < NB; bb++) acc[bb] = f32x16{};
+  const int qrow = rb + l32;
 #pragma unroll
-    for (int e = 0; e < 8; e++) m[e] = Ci[(a0 + e) * D + b] - kbar[a0 + e] * vb;
+  for (int ks = 0; ks < D / 16; ks++) {
+    uint4 qv = make_uint4(0u, 0u, 0u, 0u);
+    if (qrow < nr) qv = *reinterpret_cast<const uint4*>(Qi + static_cast<int64_t>(qrow) * D + 16 * ks + 8 * h);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, qv);
 #pragma unroll
-    for (int k = 0; k < kMaxR; k++) {
-      const int rr = rg + RG * k;
-      if (rr < nr) {
-        const uint4 qv = *reinterpret_cast<const uint4*>(&ql[rr][a0]);
-        const uint32_t wv[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          y[k] = __builtin_fmaf(m[2 * e], bf16_bits_to_f32(wv[e] & 0xFFFFu), y[k]);
-          y[k] = __builtin_fmaf(m[2 * e + 1], bf16_bits_to_f32(wv[e] >> 16), y[k]);
-        }
-      }
+    for (int bb = 0; bb < NB; bb++) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&mt[32 * bb + l32][16 * ks + 8 * h]);
+      acc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[bb], 0, 0, 0);
     }
   }
+  // d. the update: every old value is loaded before the first store (the
+  // stores could alias the loads as far as the compiler knows)
+  uint16_t oldv[16][NB];
 #pragma unroll
-  for (int k = 0; k < kMaxR; k++) {
-    const int rr = rg + RG * k;
+  for (int r = 0; r < 16; r++) {
+    const int rr = rb + 8 * (r / 4) + 4 * h + (r % 4);
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) oldv[r][bb] = rr < nr ? O[row_off[rr] + 32 * bb + l32] : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int rr = rb + 8 * (r / 4) + 4 * h + (r % 4);
     if (rr >= nr) continue;
-    int64_t li;
-    uint16_t* op = out_row<D>(O, om.orders, om.F, om.H, om.W, om.sg, om.sn, g, N, r0 + rr, li);
-    const float old = bf16_bits_to_f32(op[b]);
-    op[b] = bf16_bits(__builtin_fmaf(old, w_old[rr], w_new[rr] * __builtin_fmaf(sm, y[k], vb)));
+    const float wo = w_old[rr], wn = w_new[rr];
+    uint16_t* op = O + row_off[rr];
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) {
+      const int b = 32 * bb + l32;
+      const float y = __builtin_fmaf(sm, acc[bb][r], vhat[b]);
+      op[b] = bf16_bits(__builtin_fmaf(bf16_bits_to_f32(oldv[r][bb]), wo, wn * y));
+    }
   }
 }
 
