@@ -489,6 +489,79 @@ def compensation(plan, od, F, H, W, reps):
     }
 
 
+def smi_sample():
+    """One reading of the GPU's socket power (W) and its per-XCD graphics
+    clocks (MHz) from amd-smi, or None where the tool is not there."""
+    import re
+    import subprocess
+
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", "0"], capture_output=True,
+                           text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
+    clk = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", r.stdout)]
+    if pw is None or not clk:
+        return None
+    return float(pw.group(1)), clk
+
+
+def power_probe(fns, seconds):
+    """Socket power and graphics clocks while each workload runs back to back
+    for about `seconds` (amd-smi sampled from a second thread, readings in the
+    first and last half second dropped), beside the workload's own time per
+    launch.  The first sample is taken idle."""
+    import math
+    import threading
+
+    import torch
+
+    idle = smi_sample()
+    if idle is None:
+        return None
+    out = {"idle_socket_w": idle[0], "idle_gfx_mhz_mean": sum(idle[1]) / len(idle[1]),
+           "tool": "amd-smi metric -p -c (SOCKET_POWER, GFX_n CLK)"}
+    for name, fn, est_ms, flop in fns:
+        n = max(3, math.ceil(seconds * 1e3 / est_ms))
+        fn()
+        torch.cuda.synchronize()
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                t = time.perf_counter()
+                r = smi_sample()
+                if r is not None:
+                    samples.append((t, r))
+                stop.wait(0.25)
+
+        th = threading.Thread(target=sampler)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        th.start()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stop.set()
+        th.join()
+        ms = e0.elapsed_time(e1) / n
+        keep = [r for t, r in samples if t0 + 0.5 <= t <= t1 - 0.5]
+        rec = {"launches": n, "ms_per_launch": ms, "tflops": flop / (ms / 1e3) / 1e12, "samples": len(keep)}
+        if keep:
+            rec["socket_w_mean"] = sum(r[0] for r in keep) / len(keep)
+            clks = [c for r in keep for c in r[1]]
+            rec["gfx_mhz_mean"] = sum(clks) / len(clks)
+            rec["gfx_mhz_min"] = min(clks)
+            rec["gfx_mhz_max"] = max(clks)
+        out[name] = rec
+        log(f"[bench] power {name}: {rec}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -502,6 +575,9 @@ def main():
                     help="skip the long-clip layer (dynamic COSINE mask rebuilt every step)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the reorder bandwidth and the 30 %% / 20 %% density sweep")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the power and clock readings (amd-smi) under the attention kernels "
+                         "and a vendor bf16 GEMM")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 3 plain device copies of 2 GiB (reference dispatches for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -690,6 +766,24 @@ def main():
         step_bf16()
         result["compensation"] = compensation(plan, od, F, H, W, reps=max(3, args.steps // 4))
         log(f"[bench] compensation: {result['compensation']}")
+    if not args.no_power:
+        log("[bench] power and clocks")
+        gm = 8192
+        ga = torch.randn(gm, gm, device="cuda", dtype=torch.bfloat16)
+        gb = torch.randn(gm, gm, device="cuda", dtype=torch.bfloat16)
+        gc = torch.empty(gm, gm, device="cuda", dtype=torch.bfloat16)
+        fns = [("bf16_attention", lambda: bsa.forward_natural(
+                    plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk, od, F, H, W,
+                    out=plan.O, lse=plan.lse), seg[2], fl_kept)]
+        if not args.no_int8:
+            fns.append(("int8_attention", lambda: bsa.forward_int8_natural(
+                plan8.Qq, plan8.sQ, plan8.Kq, plan8.sK, plan8.Vq, plan8.sV, plan8.row_ptr,
+                plan8.col_idx, p.Bq, p.Bk, od, F, H, W, out=plan8.O, lse=plan8.lse),
+                result["int8"]["attention_ms"], fl_kept))
+        fns.append(("torch_mm_bf16_8192", lambda: torch.mm(ga, gb, out=gc), 0.8, 2.0 * gm ** 3))
+        step_bf16()
+        result["power"] = power_probe(fns, seconds=4.0)
+        del ga, gb, gc
     if not args.no_long_clip:
         result["long_clip"] = long_clip(args, timed_steps=args.steps)
     if not args.no_calib:
