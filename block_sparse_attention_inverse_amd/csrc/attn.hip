@@ -212,11 +212,20 @@ __device__ __forceinline__ void load_q(const int8_t* __restrict__ Q, int g, int 
   }
 }
 
-// max over the lanes that carry real rows; both lane halves of a row agree
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// max over the 32 rows of a wave (lanes l and l + 32 carry the same row), in
+// VALU cross-lane moves only: within quads, 8-lane and 16-lane rows by DPP,
+// then the two 16-lane rows of each half by permlane16_swap
 __device__ __forceinline__ float rows_max(float x) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // P8 = rint(Pt * 127 / mP) for the wave's rows (mP = 2^dm, the tile maximum
@@ -311,10 +320,9 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
   const int head_bytes = N * L::ROWB;
   const int8_t* kh = K + static_cast<int64_t>(g) * N * D;
   const int8_t* vh = V + static_cast<int64_t>(g) * N * D;
-  auto kv0_of = [&](int t) {
-    const int j = col_idx[e0 + t];
-    return static_cast<unsigned>(j) < static_cast<unsigned>(nk) ? j * BK : 0;
-  };
+  // kv-block index of tile t (0 past the list), its first row (0 when out of range)
+  auto col_of = [&](int t) { return t < nt ? col_idx[e0 + t] : 0; };
+  auto kv0_of = [&](int j) { return static_cast<unsigned>(j) < static_cast<unsigned>(nk) ? j * BK : 0; };
 
   // m: the exact running row maximum (the P quantisation is relative to
   // it); O and l are kept relative to an older reference mf <= m and only
@@ -332,18 +340,30 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
 
   if (nt > 0) {
     // prologue: K(0), K(1), V(0)
-    L::stage(kh, head_bytes, sg.k, kv0_of(0), kbuf[0]);
-    if (nt > 1) L::stage(kh, head_bytes, sg.k, kv0_of(1), kbuf[1]);
-    L::stage(vh, head_bytes, sg.v, kv0_of(0), vbuf[0]);
+    // indices of tiles t, t+1, t+2 and the scales of tile t, each read one
+    // tile before its use so no scalar load is waited on inside a tile
+    int j0 = col_of(0), j1 = col_of(1), j2 = col_of(2);
+    auto sk_of = [&](int j) {
+      return static_cast<unsigned>(j) < static_cast<unsigned>(nk) ? sK[static_cast<int64_t>(g) * nk + j] : 0.0f;
+    };
+    auto sv_of = [&](int j) {
+      return static_cast<unsigned>(j) < static_cast<unsigned>(nk) ? sV[static_cast<int64_t>(g) * nk + j] : 0.0f;
+    };
+    float sk0 = sk_of(j0), sv0 = sv_of(j0);
+    L::stage(kh, head_bytes, sg.k, kv0_of(j0), kbuf[0]);
+    if (nt > 1) L::stage(kh, head_bytes, sg.k, kv0_of(j1), kbuf[1]);
+    L::stage(vh, head_bytes, sg.v, kv0_of(j0), vbuf[0]);
     wait_loads();
     __syncthreads();
     for (int t = 0; t < nt; t++) {
-      const int j = col_idx[e0 + t];
+      const int j = j0;
       const bool jvalid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
       const int kv0 = jvalid ? j * BK : 0;
       const bool masked = !jvalid || kv0 + BK > N;
-      const float f = jvalid ? sq * sK[static_cast<int64_t>(g) * nk + j] : 0.0f;
-      const float svj = jvalid ? sV[static_cast<int64_t>(g) * nk + j] : 0.0f;
+      const float f = sq * sk0, svj = sv0;
+      // next tile's scales and the index of tile t+3, consumed one tile later
+      const int j3 = col_of(t + 3);
+      const float sk1 = sk_of(j1), sv1 = sv_of(j1);
 
       // ---- scores and the exact running maximum of every row
       i32x16 s[kQB][NB];
@@ -410,8 +430,8 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
       // maximum of every wave is visible
       wait_loads();
       __syncthreads();
-      if (t + 2 < nt) L::stage(kh, head_bytes, sg.k, kv0_of(t + 2), kbuf[(t + 2) % 3]);
-      if (t + 1 < nt) L::stage(vh, head_bytes, sg.v, kv0_of(t + 1), vbuf[(t + 1) & 1]);
+      if (t + 2 < nt) L::stage(kh, head_bytes, sg.k, kv0_of(j2), kbuf[(t + 2) % 3]);
+      if (t + 1 < nt) L::stage(vh, head_bytes, sg.v, kv0_of(j1), vbuf[(t + 1) & 1]);
       float dm = tile_max[t & 1][0];
 #pragma unroll
       for (int ww = 1; ww < NW; ww++) dm = fmaxf(dm, tile_max[t & 1][ww]);
@@ -447,6 +467,8 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
           for (int r = 0; r < 16; r++)
             o[qb][db][r] = __builtin_fmaf(static_cast<float>(ov[qb][r]), cv[qb], o[qb][db][r]);
       }
+      j0 = j1; j1 = j2; j2 = j3;
+      sk0 = sk1; sv0 = sv1;
     }
   }
 
