@@ -607,6 +607,8 @@ int64_t bsa_fo_workspace(int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk
     if (!block_ok(Bq) || !block_ok(Bk)) return fail(BSA_EUNSUPPORTED, "Bq, Bk must be 64 or 128");
     const int64_t nk = (static_cast<int64_t>(N) + Bk - 1) / Bk;
     if (nk > 32768) return fail(BSA_EUNSUPPORTED, "Nkv = %lld exceeds 32768", (long long)nk);
+    const int64_t nq = (static_cast<int64_t>(N) + Bq - 1) / Bq;
+    if (nq > 32768) return fail(BSA_EUNSUPPORTED, "Nq = %lld exceeds 32768", (long long)nq);
     return static_cast<int64_t>(bsa::fo_layout(G, N, d, Bq, Bk).total);
   });
 }

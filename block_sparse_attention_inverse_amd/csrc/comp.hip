@@ -129,99 +129,110 @@ __global__ __launch_bounds__(kCompThreads) void skip_mask_kernel(
 
 // 3. C[g][i][c] = sum_j S[g][i][j] X[g][j][c].  Products C^T = X^T . S^T on
 // v_mfma_f32_32x32x16_bf16: A = X^T (32 columns x 16 kv-blocks), B = S^T
-// (16 kv-blocks x 32 rows).  X is row-major (kv-block j, column c), so each
-// stage of 64 kv-blocks x 256 columns is transposed on its way into LDS: a
-// thread loads an 8 x 8 block (8 rows, 16 bytes each), transposes it in
-// registers and writes 8 columns of 8 kv-blocks (16 bytes each).  The next
-// stage's loads are issued before the current stage's products.  Wave w
-// owns columns [64w, 64w + 64) of the tile and all 64 rows: 2 x 2
-// accumulators; lane l of an accumulator holds row ib + l%32 and columns
-// cb + 8(r/4) + 4(l/32) + r%4.
-constexpr int kGemmJ = 64;              // kv-blocks per stage
-constexpr int kPitchG = kGemmJ + 8;     // bf16 per LDS row (16-byte aligned, staggered banks)
+// (16 kv-blocks x 32 rows).  A workgroup owns 64 rows i and 256 columns c;
+// each stage of 64 kv-blocks moves global -> LDS with 16-byte buffer loads
+// that write LDS directly (double-buffered, the next stage in flight under
+// the current one's products, one barrier per stage):
+//   X stage: two 64 x 128 sub-tiles (256-byte rows), chunk p of row r at
+//            p ^ (2r mod 16); A operands come out of ds_read_b64_tr_b16, two
+//            reads per operand, which give a lane half h the kv-blocks
+//            16ks + 4h + (0..3) and 16ks + 8 + 4h + (0..3) of k-step ks;
+//   S stage: 64 x 64 (128-byte rows), chunk p of row r at p ^ ((r/2) mod 8);
+//            B operands are two 8-byte reads in the same kv-block order.
+// Wave w owns columns [64w, 64w + 64) (sub-tile w/2, channel blocks
+// 2(w%2), 2(w%2)+1) and all 64 rows: 2 x 2 accumulators; lane l of an
+// accumulator holds row ib + l%32 and columns cb + 8(r/4) + 4(l/32) + r%4.
+// Tiles go to XCDs in contiguous ranges ordered (head, column tile, row
+// tile), so the row tiles that share an X stage run together on one L2.
+constexpr int kGemmJ = 64;       // kv-blocks per stage
+constexpr int kXSub = 64 * 256;  // bytes of one X sub-tile (64 rows x 128 columns)
+constexpr int kSTile = 64 * 128; // bytes of one S stage (64 rows x 64 kv-blocks)
 
-struct GemmStage {
-  uint4 x[8];  // rows 8*(t/32) .. +7, columns 8*(t%32) .. +7 of the X stage
-  uint4 s[2];  // row t/4, kv-blocks 16*(t%4) .. +15 of the S stage
-};
-
-__device__ __forceinline__ void gemm_load(const uint16_t* Xg, const uint16_t* Sg, int Lp, int nkp,
-                                          int i0, int c0, int j0, GemmStage& st) {
-  const int t = threadIdx.x;
-  const int jr = 8 * (t / 32), cc = 8 * (t % 32);
-#pragma unroll
-  for (int r = 0; r < 8; r++)
-    st.x[r] = *reinterpret_cast<const uint4*>(Xg + static_cast<int64_t>(j0 + jr + r) * Lp + c0 + cc);
-  const uint16_t* sp = Sg + static_cast<int64_t>(i0 + t / 4) * nkp + j0 + 16 * (t % 4);
-  st.s[0] = *reinterpret_cast<const uint4*>(sp);
-  st.s[1] = *reinterpret_cast<const uint4*>(sp + 8);
-}
-
-// word w of column e after the transpose holds rows 2w, 2w + 1 of column e
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-__device__ __forceinline__ uint32_t word(const uint4& v, int w) {
-  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
-}
-
-__device__ __forceinline__ void gemm_store(const GemmStage& st, uint16_t (*xt)[kPitchG],
-                                           uint16_t (*sl)[kPitchG]) {
-  const int t = threadIdx.x;
-  const int jr = 8 * (t / 32), cc = 8 * (t % 32);
-#pragma unroll
-  for (int wc = 0; wc < 4; wc++) {  // input word wc holds columns 2wc, 2wc + 1
-    uint4 lo, hi;
-    lo.x = lo_pair(word(st.x[0], wc), word(st.x[1], wc));
-    lo.y = lo_pair(word(st.x[2], wc), word(st.x[3], wc));
-    lo.z = lo_pair(word(st.x[4], wc), word(st.x[5], wc));
-    lo.w = lo_pair(word(st.x[6], wc), word(st.x[7], wc));
-    hi.x = hi_pair(word(st.x[0], wc), word(st.x[1], wc));
-    hi.y = hi_pair(word(st.x[2], wc), word(st.x[3], wc));
-    hi.z = hi_pair(word(st.x[4], wc), word(st.x[5], wc));
-    hi.w = hi_pair(word(st.x[6], wc), word(st.x[7], wc));
-    *reinterpret_cast<uint4*>(&xt[cc + 2 * wc][jr]) = lo;
-    *reinterpret_cast<uint4*>(&xt[cc + 2 * wc + 1][jr]) = hi;
-  }
-  *reinterpret_cast<uint4*>(&sl[t / 4][16 * (t % 4)]) = st.s[0];
-  *reinterpret_cast<uint4*>(&sl[t / 4][16 * (t % 4) + 8]) = st.s[1];
-}
-
-__global__ __launch_bounds__(kCompThreads) void skip_gemm_kernel(const uint16_t* __restrict__ S,
-                                                                 const uint16_t* __restrict__ X,
-                                                                 int nqp, int nkp, int Lp,
-                                                                 int tiles_i, int tiles_c,
-                                                                 float* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) uint16_t xt[kTileC][kPitchG];
-  __shared__ __attribute__((aligned(16))) uint16_t sl[kTileI][kPitchG];
-  const int per_head = tiles_i * tiles_c;
-  const int g = blockIdx.x / per_head, rem = blockIdx.x % per_head;
-  const int ti = rem / tiles_c, tc = rem % tiles_c;
-  const int i0 = ti * kTileI, c0 = tc * kTileC;
+__global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16_t* __restrict__ S,
+                                                                    const uint16_t* __restrict__ X,
+                                                                    int G, int nqp, int nkp, int Lp,
+                                                                    int tiles_i, int tiles_c,
+                                                                    float* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[2][2][kXSub];
+  __shared__ __attribute__((aligned(1024))) uint8_t ss[2][kSTile];
+  int g, item;
+  if (!xcd_range_tile(blockIdx.x, tiles_i * tiles_c, G, g, item)) return;
+  const int tc = item / tiles_i, ti = item % tiles_i;
+  const int i0 = ti * 64, c0 = tc * 256;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const uint16_t* Sg = S + static_cast<int64_t>(g) * nqp * nkp;
   const uint16_t* Xg = X + static_cast<int64_t>(g) * nkp * Lp;
+  const uint16_t* Sg = S + static_cast<int64_t>(g) * nqp * nkp;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Xg), 0, static_cast<int>(static_cast<int64_t>(nkp) * Lp * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Sg), 0, static_cast<int>(static_cast<int64_t>(nqp) * nkp * 2), 0x00020000);
+  // staging lane offsets: X load q of wave w fills rows 16q + 4w + lane/16,
+  // S load q rows 32q + 8w + lane/8 (the swizzle depends on lane and w only)
+  const uint32_t vx_ld = static_cast<uint32_t>((4 * w + (lane >> 4)) * (Lp * 2) +
+                                               (((lane & 15) ^ ((8 * w + 2 * (lane >> 4)) & 15)) << 4));
+  const uint32_t vs_ld = static_cast<uint32_t>((8 * w + (lane >> 3)) * (nkp * 2) +
+                                               (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4));
+  const uint32_t wb = static_cast<uint32_t>(w) * 1024u;
+  auto stage = [&](int j0, int buf) {
+#pragma unroll
+    for (int sb = 0; sb < 2; sb++)
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (LDS_AS void*)(&xs[buf][sb][q * 4096 + wb]), 16, vx_ld,
+            static_cast<uint32_t>((j0 + 16 * q) * Lp * 2 + (c0 + 128 * sb) * 2), 0, 0);
+#pragma unroll
+    for (int q = 0; q < 2; q++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (LDS_AS void*)(&ss[buf][q * 4096 + wb]), 16, vs_ld,
+          static_cast<uint32_t>((i0 + 32 * q) * nkp * 2 + j0 * 2), 0, 0);
+  };
+  // operand read offsets
+  const int rsub = (lane & 15) >> 2;
+  const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int sv = (2 * (4 * h + rsub)) & 15;
+  const uint32_t vread = static_cast<uint32_t>((4 * h + rsub) * 256 + ((cl ^ sv) << 4) + (lane & 1) * 8);
+  uint32_t ax[2];
+#pragma unroll
+  for (int cbk = 0; cbk < 2; cbk++) ax[cbk] = vread ^ static_cast<uint32_t>((2 * (w & 1) + cbk) << 6);
+  uint32_t bx[2];
+#pragma unroll
+  for (int ib = 0; ib < 2; ib++) {
+    const int i = 32 * ib + l32;
+    bx[ib] = static_cast<uint32_t>(i * 128 + 8 * h);
+  }
+  const int bsw = (l32 >> 1) & 7;  // same for both row blocks (32ib + l32)
   f32x16 acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; a++)
 #pragma unroll
     for (int b = 0; b < 2; b++) acc[a][b] = f32x16{};
-  GemmStage st;
-  gemm_load(Xg, Sg, Lp, nkp, i0, c0, 0, st);
-  for (int j0 = 0; j0 < nkp; j0 += kGemmJ) {
-    __syncthreads();  // the previous stage's operand reads are done
-    gemm_store(st, xt, sl);
+  const int nst = nkp / kGemmJ;
+  stage(0, 0);
+  for (int st = 0; st < nst; st++) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j0 + kGemmJ < nkp) gemm_load(Xg, Sg, Lp, nkp, i0, c0, j0 + kGemmJ, st);
+    if (st + 1 < nst) stage((st + 1) * kGemmJ, (st + 1) & 1);
+    const uint8_t* xt = xs[st & 1][w >> 1];
+    const uint8_t* sl = ss[st & 1];
 #pragma unroll
     for (int ks = 0; ks < kGemmJ / 16; ks++) {
       bf16x8 a[2], b[2];
 #pragma unroll
-      for (int cbk = 0; cbk < 2; cbk++)
-        a[cbk] = *reinterpret_cast<const bf16x8*>(&xt[64 * w + 32 * cbk + l32][16 * ks + 8 * h]);
+      for (int cbk = 0; cbk < 2; cbk++) {
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s4*)(xt + 16 * ks * 256 + ax[cbk]));
+        const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s4*)(xt + (16 * ks + 8) * 256 + ax[cbk]));
+        a[cbk] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                                lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
 #pragma unroll
-      for (int ib = 0; ib < 2; ib++)
-        b[ib] = *reinterpret_cast<const bf16x8*>(&sl[32 * ib + l32][16 * ks + 8 * h]);
+      for (int ib = 0; ib < 2; ib++) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(sl + bx[ib] + (((2 * ks) ^ bsw) << 4));
+        const uint2 hi = *reinterpret_cast<const uint2*>(sl + bx[ib] + (((2 * ks + 1) ^ bsw) << 4));
+        b[ib] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      }
 #pragma unroll
       for (int cbk = 0; cbk < 2; cbk++)
 #pragma unroll
@@ -404,8 +415,9 @@ hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint
   skip_mask_kernel<<<static_cast<uint32_t>(G) * L.nqp, kCompThreads, sizeof(uint16_t) * L.nkp, s>>>(
       row_ptr, col_idx, col_len, mask_G, L.nq, L.nk, L.nqp, L.nkp, S);
   const int ti = L.nqp / kTileI, tc = L.Lp / kTileC;
-  skip_gemm_kernel<<<static_cast<uint32_t>(G) * ti * tc, kCompThreads, 0, s>>>(S, X, L.nqp, L.nkp, L.Lp,
-                                                                             ti, tc, C);
+  const int64_t tiles = static_cast<int64_t>(G) * ti * tc;
+  const uint32_t ng = kNumXcd * static_cast<uint32_t>((tiles + kNumXcd - 1) / kNumXcd);
+  skip_gemm_kernel<<<ng, kCompThreads, 0, s>>>(S, X, G, L.nqp, L.nkp, L.Lp, ti, tc, C);
   const uint32_t ga = static_cast<uint32_t>(G) * L.nq;
   if (d == 128)
     apply_kernel<128><<<ga, kCompThreads, 0, s>>>(Q, C, N, Bq, L.nq, L.nqp, L.Lp, sm, O, lse, om);

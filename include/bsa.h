@@ -312,7 +312,7 @@ int bsa_forward_int8_natural(const int8_t *Qq, const float *sQ, const int8_t *Kq
 /* bsa_fo_workspace — bytes of device workspace bsa_fo_compensate needs
  * (per-kv-block moments, the skip mask and the sums over each q-block
  * row's skipped set: about G*Nkv*d*d*2 + G*Nq*d*d*4 bytes), or a negative
- * status (d not in {64, 128}, B not in {64, 128}, Nkv > 32768). */
+ * status (d not in {64, 128}, B not in {64, 128}, Nq or Nkv > 32768). */
 int64_t bsa_fo_workspace(int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk);
 
 /* bsa_fo_compensate — first-order compensation of the skipped keys (PASA
