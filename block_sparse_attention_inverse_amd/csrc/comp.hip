@@ -42,62 +42,110 @@ constexpr int kStageJ = 64;  // kv-block padding (the GEMM's stage)
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return static_cast<uint16_t>(f32_to_bf16_bits(x)); }
 
-// 1. per kv-block moments.  Tokens are taken 64 at a time through LDS; thread
-// (ta, tb) owns a (D/16) x (D/16) block of sum k v^T.
+// 1. per kv-block moments on v_mfma_f32_32x32x16_bf16, one workgroup per
+// (head, kv-block).  K and V move global -> LDS in 64-row sub-tiles with
+// 16-byte buffer loads that write LDS directly (rows past N read as zero),
+// chunk p of row r at p ^ (2r mod CH); both operands of
+// sum_r k_r v_r^T = K^T V come out of ds_read_b64_tr_b16 (A = K^T: a lane
+// holds one channel a of K over 8 rows; B = V: one channel b over the same
+// 8 rows).  sum k and sum v are the same products against a bf16 ones
+// operand.  Wave w takes the KV tiles w*TPW .. w*TPW+TPW-1 (32 x 32 each)
+// and SPW of the 2*D/32 sum blocks (k blocks first, then v blocks).
 template <int D>
 __global__ __launch_bounds__(kCompThreads) void kv_moments_kernel(const uint16_t* __restrict__ K,
                                                                   const uint16_t* __restrict__ V,
                                                                   int N, int Bk, int nk, int nkp,
                                                                   int Lp, uint16_t* __restrict__ X) {
-  constexpr int RB = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t kl[64][D];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[64][D];
+  constexpr int ROWB = 2 * D, CH = ROWB / 16, RPI = 1024 / ROWB;
+  constexpr int TB = 64 * ROWB;              // bytes of a 64-row sub-tile
+  constexpr int NI = TB / 1024 / 4;          // staging loads per wave per sub-tile
+  constexpr int DB = D / 32;
+  constexpr int TPW = DB * DB / 4, SPW = 2 * DB / 4;
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef short s8 __attribute__((ext_vector_type(8)));
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[2][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt[2][TB];
   const int g = blockIdx.x / nkp, j = blockIdx.x % nkp;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
   uint16_t* xr = X + (static_cast<int64_t>(g) * nkp + j) * Lp;
   if (j >= nk) {
     for (int c = t; c < Lp; c += kCompThreads) xr[c] = 0;
     return;
   }
   const int r0 = j * Bk, r1 = min(N, r0 + Bk);
-  const uint16_t* kh = K + static_cast<int64_t>(g) * N * D;
-  const uint16_t* vh = V + static_cast<int64_t>(g) * N * D;
-  const int ta = t / 16, tb = t % 16;
-  float acc[RB][RB];
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(K + static_cast<int64_t>(g) * N * D), 0, N * ROWB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(V + static_cast<int64_t>(g) * N * D), 0, N * ROWB, 0x00020000);
+  // load q of wave w fills rows RPI*(4q + w) + lane/CH; the swizzle does not depend on q
+  const int rl = RPI * w + lane / CH;
+  const uint32_t voff = static_cast<uint32_t>(rl * ROWB + (((lane % CH) ^ ((2 * rl) & (CH - 1))) << 4));
+  const int nsub = Bk / 64;
+  for (int u = 0; u < nsub; u++)
 #pragma unroll
-  for (int a = 0; a < RB; a++)
-#pragma unroll
-    for (int b = 0; b < RB; b++) acc[a][b] = 0.0f;
-  float ks = 0.0f, vs = 0.0f;  // thread t < D: sum k[.][t]; D <= t < 2D: sum v[.][t - D]
-  for (int c0 = r0; c0 < r1; c0 += 64) {
-    const int nr = min(64, r1 - c0);
-    __syncthreads();
-    for (int e = t; e < nr * D; e += kCompThreads) {
-      const int rr = e / D, cc = e % D;
-      kl[rr][cc] = kh[static_cast<int64_t>(c0 + rr) * D + cc];
-      vl[rr][cc] = vh[static_cast<int64_t>(c0 + rr) * D + cc];
+    for (int q = 0; q < NI; q++) {
+      const uint32_t so = static_cast<uint32_t>((r0 + 64 * u + 4 * RPI * q) * ROWB);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(&kt[u][(4 * q + w) * 1024]), 16, voff, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(&vt[u][(4 * q + w) * 1024]), 16, voff, so, 0, 0);
     }
-    __syncthreads();
-    for (int rr = 0; rr < nr; rr++) {
-      float kv[RB], vv[RB];
+  // transposed-read offsets (channel block x: xor x << 6)
+  const int rsub = (lane & 15) >> 2;
+  const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int sv = (2 * (4 * h + rsub)) & (CH - 1);
+  const uint32_t vread = static_cast<uint32_t>((4 * h + rsub) * ROWB + ((cl ^ sv) << 4) + (lane & 1) * 8);
+  auto tr = [&](const uint8_t* base, int ks, int blk) {
+    const uint32_t o = vread ^ static_cast<uint32_t>(blk << 6);
+    const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s4*)(base + 16 * ks * ROWB + o));
+    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s4*)(base + (16 * ks + 8) * ROWB + o));
+    return __builtin_bit_cast(bf16x8, (s8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, (s8){0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80});
+  f32x16 kv[TPW], sm[SPW];
 #pragma unroll
-      for (int a = 0; a < RB; a++) kv[a] = bf16_bits_to_f32(kl[rr][RB * ta + a]);
+  for (int x = 0; x < TPW; x++) kv[x] = f32x16{};
 #pragma unroll
-      for (int b = 0; b < RB; b++) vv[b] = bf16_bits_to_f32(vl[rr][RB * tb + b]);
+  for (int y = 0; y < SPW; y++) sm[y] = f32x16{};
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int u = 0; u < nsub; u++)
 #pragma unroll
-      for (int a = 0; a < RB; a++)
+    for (int ks = 0; ks < 4; ks++) {
 #pragma unroll
-        for (int b = 0; b < RB; b++) acc[a][b] = __builtin_fmaf(kv[a], vv[b], acc[a][b]);
-      if (t < D) ks += bf16_bits_to_f32(kl[rr][t]);
-      else if (t < 2 * D) vs += bf16_bits_to_f32(vl[rr][t - D]);
+      for (int x = 0; x < TPW; x++) {
+        const int k = w * TPW + x, ab = k / DB, bb = k % DB;
+        kv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr(kt[u], ks, ab), tr(vt[u], ks, bb), kv[x], 0, 0, 0);
+      }
+#pragma unroll
+      for (int y = 0; y < SPW; y++) {
+        const int sb = w * SPW + y;
+        if (sb < DB) sm[y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr(kt[u], ks, sb), ones, sm[y], 0, 0, 0);
+        else sm[y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, tr(vt[u], ks, sb - DB), sm[y], 0, 0, 0);
+      }
+    }
+  // KV tile: lane holds channel b = 32bb + l32 of rows a = 32ab + 8(r/4) + 4h + r%4
+#pragma unroll
+  for (int x = 0; x < TPW; x++) {
+    const int k = w * TPW + x, ab = k / DB, bb = k % DB;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int a = 32 * ab + 8 * (r / 4) + 4 * h + (r % 4);
+      xr[a * D + 32 * bb + l32] = bf16_bits(kv[x][r]);
     }
   }
+  // sum k (rows of the product, every column alike: column 0 writes) and
+  // sum v (columns, every row alike: row slot 0 of lane half 0 writes)
 #pragma unroll
-  for (int a = 0; a < RB; a++)
+  for (int y = 0; y < SPW; y++) {
+    const int sb = w * SPW + y;
+    if (sb < DB) {
+      if (l32 == 0)
 #pragma unroll
-    for (int b = 0; b < RB; b++) xr[(RB * ta + a) * D + RB * tb + b] = bf16_bits(acc[a][b]);
-  if (t < D) xr[D * D + t] = bf16_bits(ks);
-  else if (t < 2 * D) xr[D * D + t] = bf16_bits(vs);  // D*D + D + (t - D)
+        for (int r = 0; r < 16; r++) xr[D * D + 32 * sb + 8 * (r / 4) + 4 * h + (r % 4)] = bf16_bits(sm[y][r]);
+    } else if (h == 0) {
+      xr[D * D + D + 32 * (sb - DB) + l32] = bf16_bits(sm[y][0]);
+    }
+  }
   if (t == 0) xr[D * D + 2 * D] = bf16_bits(static_cast<float>(r1 - r0));
   for (int c = D * D + 2 * D + 1 + t; c < Lp; c += kCompThreads) xr[c] = 0;
 }
@@ -260,9 +308,10 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
 }
 
 // 4. the update of O and lse, one workgroup per (head, q-block).
-//   a. per row (thread t < rows): a = s q.kbar, the old and new terms'
+//   a. M^T (bf16, [b][a]) into LDS: M[a][b] = C_kv[a][b] - kbar_a Vhat_b
+//      (every read of C is issued first, all in flight together);
+//   b. per row (thread t < rows): a = s q.kbar, the old and new terms'
 //      weights divided by the new denominator, the new lse;
-//   b. M^T (bf16, [b][a]) into LDS: M[a][b] = C_kv[a][b] - kbar_a Vhat_b;
 //   c. Y = Q_i M on v_mfma_f32_32x32x16_bf16: wave w takes rows 32w..32w+31
 //      (A = Q rows from global memory, B = M^T rows from LDS); lane l of
 //      accumulator bb holds channel b = 32bb + l%32 of rows
@@ -278,23 +327,43 @@ __global__ __launch_bounds__(kCompThreads, 2) void apply_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t mt[D][PM];
   __shared__ float w_old[128], w_new[128];
   __shared__ int64_t row_off[128];  // element offset of each row's output
-  __shared__ float s_n;
   const int g = blockIdx.x / nq, i = blockIdx.x % nq;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const float* Ci = C + (static_cast<int64_t>(g) * nqp + i) * Lp;
   const int r0 = i * Bq, nr = min(Bq, N - r0);
   const uint16_t* Qi = Q + (static_cast<int64_t>(g) * N + r0) * D;
-  if (t == 0) s_n = Ci[D * D + 2 * D];
-  __syncthreads();
-  const float n = s_n;
-  if (!(n > 0.5f)) return;  // nothing skipped: O and lse stay as they are
-  if (t < D) {
-    kbar[t] = Ci[D * D + t] / n;
-    vhat[t] = Ci[D * D + D + t];
+  // every read of C first: the d x d block (thread t takes the 8 x 1 column
+  // pieces e = t + 256k of step a), the sums of k and v, the skipped count
+  constexpr int KM = D * (D / 8) / kCompThreads;
+  float cm[KM][8];
+#pragma unroll
+  for (int k = 0; k < KM; k++) {
+    const int e = t + kCompThreads * k, b = e % D, a0 = 8 * (e / D);
+#pragma unroll
+    for (int q = 0; q < 8; q++) cm[k][q] = Ci[(a0 + q) * D + b];
   }
+  const float sums = t < 2 * D ? Ci[D * D + t] : 0.0f;
+  const float n = Ci[D * D + 2 * D];
+  if (!(n > 0.5f)) return;  // nothing skipped (the same for the whole workgroup): O and lse stay
+  if (t < D) kbar[t] = sums / n;
+  else if (t < 2 * D) vhat[t - D] = sums;
   __syncthreads();
-  // a. per-row weights and the new lse
+  // a. M^T into LDS, 8 consecutive a per 16-byte write
+#pragma unroll
+  for (int k = 0; k < KM; k++) {
+    const int e = t + kCompThreads * k, b = e % D, a0 = 8 * (e / D);
+    const float vb = vhat[b];
+    uint32_t pk[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float m0 = cm[k][2 * q] - kbar[a0 + 2 * q] * vb;
+      const float m1 = cm[k][2 * q + 1] - kbar[a0 + 2 * q + 1] * vb;
+      pk[q] = f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);
+    }
+    *reinterpret_cast<uint4*>(&mt[b][a0]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+  // b. per-row weights and the new lse
   const float ln_n = logf(n);
   for (int rr = t; rr < nr; rr += kCompThreads) {
     float a = 0.0f;
@@ -318,19 +387,6 @@ __global__ __launch_bounds__(kCompThreads, 2) void apply_kernel(
     w_old[rr] = wo / den;
     w_new[rr] = wc / den;
     lse[li] = mu + logf(den);  // only this thread touches lse[li]
-  }
-  // b. M^T into LDS, 8 consecutive a per 16-byte write
-  for (int e = t; e < D * (D / 8); e += kCompThreads) {
-    const int b = e % D, a0 = 8 * (e / D);
-    const float vb = vhat[b];
-    uint32_t pk[4];
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const float m0 = Ci[(a0 + 2 * q) * D + b] - kbar[a0 + 2 * q] * vb;
-      const float m1 = Ci[(a0 + 2 * q + 1) * D + b] - kbar[a0 + 2 * q + 1] * vb;
-      pk[q] = f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);
-    }
-    *reinterpret_cast<uint4*>(&mt[b][a0]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   }
   __syncthreads();
   // c. Y = Q_i M for the wave's 32 rows
