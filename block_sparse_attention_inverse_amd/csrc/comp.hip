@@ -307,21 +307,25 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
     }
 }
 
-// 4. the update of O and lse, one workgroup per (head, q-block).
-//   a. M^T (bf16, [b][a]) into LDS: M[a][b] = C_kv[a][b] - kbar_a Vhat_b
-//      (every read of C is issued first, all in flight together);
-//   b. per row (thread t < rows): a = s q.kbar, the old and new terms'
+// 4. the update of O and lse, one workgroup per (head, q-block); wave w
+// owns rows 32w..32w+31 (lane l and l+32 share row 32w + l%32).
+//   a. every read of C first (the d x d block: thread t takes the 8 x 1
+//      column pieces e = t + 256k; the sums of k and v; the skipped count),
+//      and the wave's Q fragments (the A operand of step d);
+//   b. M^T (bf16, [b][a]) into LDS: M[a][b] = C_kv[a][b] - kbar_a Vhat_b;
+//   c. per row, from the Q fragments: a = s q.kbar, the old and new terms'
 //      weights divided by the new denominator, the new lse;
-//   c. Y = Q_i M on v_mfma_f32_32x32x16_bf16: wave w takes rows 32w..32w+31
-//      (A = Q rows from global memory, B = M^T rows from LDS); lane l of
-//      accumulator bb holds channel b = 32bb + l%32 of rows
+//   d. Y = Q_i M on v_mfma_f32_32x32x16_bf16 (B = M^T rows from LDS); lane l
+//      of accumulator bb holds channel b = 32bb + l%32 of rows
 //      32w + 8(r/4) + 4(l/32) + r%4;
-//   d. O' = O w_old + w_new (Vhat + s y), written where the forward wrote O.
+//   e. O' = O w_old + w_new (Vhat + s y), written where the forward wrote O
+//      (the old values are read before the products).
 template <int D>
 __global__ __launch_bounds__(kCompThreads, 2) void apply_kernel(
     const uint16_t* __restrict__ Q, const float* __restrict__ C, int N, int Bq, int nq, int nqp,
     int Lp, float sm, uint16_t* __restrict__ O, float* __restrict__ lse, OutMap om) {
   constexpr int NB = D / 32;      // 32-channel blocks of the output
+  constexpr int KS = D / 16;      // k-steps of Y = Q M
   constexpr int PM = D + 8;       // bf16 per LDS row of M^T
   __shared__ float kbar[D], vhat[D];
   __shared__ __attribute__((aligned(16))) uint16_t mt[D][PM];
@@ -333,8 +337,8 @@ __global__ __launch_bounds__(kCompThreads, 2) void apply_kernel(
   const float* Ci = C + (static_cast<int64_t>(g) * nqp + i) * Lp;
   const int r0 = i * Bq, nr = min(Bq, N - r0);
   const uint16_t* Qi = Q + (static_cast<int64_t>(g) * N + r0) * D;
-  // every read of C first: the d x d block (thread t takes the 8 x 1 column
-  // pieces e = t + 256k of step a), the sums of k and v, the skipped count
+  const int rb = 32 * w, qrow = rb + l32;
+  // a. reads
   constexpr int KM = D * (D / 8) / kCompThreads;
   float cm[KM][8];
 #pragma unroll
@@ -345,11 +349,17 @@ __global__ __launch_bounds__(kCompThreads, 2) void apply_kernel(
   }
   const float sums = t < 2 * D ? Ci[D * D + t] : 0.0f;
   const float n = Ci[D * D + 2 * D];
+  uint4 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    qf[ks] = make_uint4(0u, 0u, 0u, 0u);
+    if (qrow < nr) qf[ks] = *reinterpret_cast<const uint4*>(Qi + static_cast<int64_t>(qrow) * D + 16 * ks + 8 * h);
+  }
   if (!(n > 0.5f)) return;  // nothing skipped (the same for the whole workgroup): O and lse stay
   if (t < D) kbar[t] = sums / n;
   else if (t < 2 * D) vhat[t - D] = sums;
   __syncthreads();
-  // a. M^T into LDS, 8 consecutive a per 16-byte write
+  // b. M^T into LDS, 8 consecutive a per 16-byte write
 #pragma unroll
   for (int k = 0; k < KM; k++) {
     const int e = t + kCompThreads * k, b = e % D, a0 = 8 * (e / D);
@@ -363,52 +373,38 @@ __global__ __launch_bounds__(kCompThreads, 2) void apply_kernel(
     }
     *reinterpret_cast<uint4*>(&mt[b][a0]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   }
-  // b. per-row weights and the new lse
-  const float ln_n = logf(n);
-  for (int rr = t; rr < nr; rr += kCompThreads) {
-    float a = 0.0f;
-    for (int c0 = 0; c0 < D; c0 += 8) {
-      const uint4 qv = *reinterpret_cast<const uint4*>(Qi + static_cast<int64_t>(rr) * D + c0);
-      const uint32_t wv[4] = {qv.x, qv.y, qv.z, qv.w};
+  // c. per-row weights and the new lse: this lane's half of q.kbar (channels
+  // 16ks + 8h .. +7), the halves added across the wave
+  if (rb < nr) {
+    float part = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const uint32_t wv[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        a = __builtin_fmaf(bf16_bits_to_f32(wv[e] & 0xFFFFu), kbar[c0 + 2 * e], a);
-        a = __builtin_fmaf(bf16_bits_to_f32(wv[e] >> 16), kbar[c0 + 2 * e + 1], a);
+        part = __builtin_fmaf(bf16_bits_to_f32(wv[e] & 0xFFFFu), kbar[16 * ks + 8 * h + 2 * e], part);
+        part = __builtin_fmaf(bf16_bits_to_f32(wv[e] >> 16), kbar[16 * ks + 8 * h + 2 * e + 1], part);
       }
     }
-    a *= sm;
-    int64_t li;
-    row_off[rr] = out_row<D>(O, om.orders, om.F, om.H, om.W, om.sg, om.sn, g, N, r0 + rr, li) - O;
-    const float lo = lse[li];
-    const float mu = fmaxf(lo, a + ln_n);
-    const float wo = lo > -INFINITY ? expf(lo - mu) : 0.0f;
-    const float wc = expf(a - mu);
-    const float den = wo + wc * n;
-    w_old[rr] = wo / den;
-    w_new[rr] = wc / den;
-    lse[li] = mu + logf(den);  // only this thread touches lse[li]
-  }
-  __syncthreads();
-  // c. Y = Q_i M for the wave's 32 rows
-  const int rb = 32 * w;
-  if (rb >= nr) return;  // no later barrier
-  f32x16 acc[NB];
-#pragma unroll
-  for (int bb = 0; bb < NB; bb++) acc[bb] = f32x16{};
-  const int qrow = rb + l32;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ks++) {
-    uint4 qv = make_uint4(0u, 0u, 0u, 0u);
-    if (qrow < nr) qv = *reinterpret_cast<const uint4*>(Qi + static_cast<int64_t>(qrow) * D + 16 * ks + 8 * h);
-    const bf16x8 a = __builtin_bit_cast(bf16x8, qv);
-#pragma unroll
-    for (int bb = 0; bb < NB; bb++) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&mt[32 * bb + l32][16 * ks + 8 * h]);
-      acc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[bb], 0, 0, 0);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    const float a = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * sm;
+    if (h == 0 && qrow < nr) {
+      int64_t li;
+      row_off[qrow] = out_row<D>(O, om.orders, om.F, om.H, om.W, om.sg, om.sn, g, N, r0 + qrow, li) - O;
+      const float lo = lse[li];
+      const float mu = fmaxf(lo, a + logf(n));
+      const float wo = lo > -INFINITY ? expf(lo - mu) : 0.0f;
+      const float wc = expf(a - mu);
+      const float den = wo + wc * n;
+      w_old[qrow] = wo / den;
+      w_new[qrow] = wc / den;
+      lse[li] = mu + logf(den);  // only this lane touches lse[li]
     }
   }
-  // d. the update: every old value is loaded before the first store (the
-  // stores could alias the loads as far as the compiler knows)
+  __syncthreads();
+  if (rb >= nr) return;  // no later barrier
+  // e (first half). the old values of this lane's 16 rows, read before the
+  // products (the stores below could alias them as far as the compiler knows)
   uint16_t oldv[16][NB];
 #pragma unroll
   for (int r = 0; r < 16; r++) {
@@ -416,6 +412,20 @@ __global__ __launch_bounds__(kCompThreads, 2) void apply_kernel(
 #pragma unroll
     for (int bb = 0; bb < NB; bb++) oldv[r][bb] = rr < nr ? O[row_off[rr] + 32 * bb + l32] : 0;
   }
+  // d. Y = Q_i M for the wave's 32 rows
+  f32x16 acc[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; bb++) acc[bb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, qf[ks]);
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&mt[32 * bb + l32][16 * ks + 8 * h]);
+      acc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[bb], 0, 0, 0);
+    }
+  }
+  // e. the update
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int rr = rb + 8 * (r / 4) + 4 * h + (r % 4);
