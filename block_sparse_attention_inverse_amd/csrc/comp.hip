@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
 //   e. O' = O w_old + w_new (Vhat + s y), written where the forward wrote O
 //      (the old values are read before the products).
 template <int D>
-__global__ __launch_bounds__(kCompThreads, 2) void apply_kernel(
+__global__ __launch_bounds__(kCompThreads, 3) void apply_kernel(
     const uint16_t* __restrict__ Q, const float* __restrict__ C, int N, int Bq, int nq, int nqp,
     int Lp, float sm, uint16_t* __restrict__ O, float* __restrict__ lse, OutMap om) {
   constexpr int NB = D / 32;      // 32-channel blocks of the output
