@@ -36,8 +36,8 @@ namespace {
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kCompThreads = 256;
-constexpr int kTileI = 64;   // C rows (q-blocks) per GEMM workgroup
-constexpr int kTileC = 256;  // C columns per GEMM workgroup (64 per wave)
+constexpr int kTileI = 128;  // C rows (q-blocks) per GEMM workgroup
+constexpr int kTileC = 128;  // C columns per GEMM workgroup
 constexpr int kStageJ = 64;  // kv-block padding (the GEMM's stage)
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return static_cast<uint16_t>(f32_to_bf16_bits(x)); }
@@ -177,37 +177,38 @@ __global__ __launch_bounds__(kCompThreads) void skip_mask_kernel(
 
 // 3. C[g][i][c] = sum_j S[g][i][j] X[g][j][c].  Products C^T = X^T . S^T on
 // v_mfma_f32_32x32x16_bf16: A = X^T (32 columns x 16 kv-blocks), B = S^T
-// (16 kv-blocks x 32 rows).  A workgroup owns 64 rows i and 256 columns c;
+// (16 kv-blocks x 32 rows).  A workgroup owns 128 rows i and 128 columns c;
 // each stage of 64 kv-blocks moves global -> LDS with 16-byte buffer loads
 // that write LDS directly (double-buffered, the next stage in flight under
 // the current one's products, one barrier per stage):
-//   X stage: two 64 x 128 sub-tiles (256-byte rows), chunk p of row r at
+//   X stage: 64 x 128 (256-byte rows), chunk p of row r at
 //            p ^ (2r mod 16); A operands come out of ds_read_b64_tr_b16, two
 //            reads per operand, which give a lane half h the kv-blocks
 //            16ks + 4h + (0..3) and 16ks + 8 + 4h + (0..3) of k-step ks;
-//   S stage: 64 x 64 (128-byte rows), chunk p of row r at p ^ ((r/2) mod 8);
+//   S stage: 128 x 64 (128-byte rows), chunk p of row r at p ^ ((r/2) mod 8);
 //            B operands are two 8-byte reads in the same kv-block order.
-// Wave w owns columns [64w, 64w + 64) (sub-tile w/2, channel blocks
-// 2(w%2), 2(w%2)+1) and all 64 rows: 2 x 2 accumulators; lane l of an
-// accumulator holds row ib + l%32 and columns cb + 8(r/4) + 4(l/32) + r%4.
+// Wave w owns rows [64(w/2), +64) and columns [64(w%2), +64) (channel
+// blocks 2(w%2), 2(w%2)+1): 2 x 2 accumulators; lane l of an accumulator
+// holds row ib + l%32 and columns cb + 8(r/4) + 4(l/32) + r%4.
 // Tiles go to XCDs in contiguous ranges ordered (head, column tile, row
 // tile), so the row tiles that share an X stage run together on one L2.
 constexpr int kGemmJ = 64;       // kv-blocks per stage
-constexpr int kXSub = 64 * 256;  // bytes of one X sub-tile (64 rows x 128 columns)
-constexpr int kSTile = 64 * 128; // bytes of one S stage (64 rows x 64 kv-blocks)
+constexpr int kXSub = 64 * 256;   // bytes of one X stage (64 rows x 128 columns)
+constexpr int kSTile = 128 * 128; // bytes of one S stage (128 rows x 64 kv-blocks)
 
 __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16_t* __restrict__ S,
                                                                     const uint16_t* __restrict__ X,
                                                                     int G, int nqp, int nkp, int Lp,
                                                                     int tiles_i, int tiles_c,
                                                                     float* __restrict__ C) {
-  __shared__ __attribute__((aligned(1024))) uint8_t xs[2][2][kXSub];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[2][kXSub];
   __shared__ __attribute__((aligned(1024))) uint8_t ss[2][kSTile];
   int g, item;
   if (!xcd_range_tile(blockIdx.x, tiles_i * tiles_c, G, g, item)) return;
   const int tc = item / tiles_i, ti = item % tiles_i;
-  const int i0 = ti * 64, c0 = tc * 256;
+  const int i0 = ti * kTileI, c0 = tc * kTileC;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wr = w >> 1, wc = w & 1;
   const int l32 = lane & 31, h = lane >> 5;
   const uint16_t* Xg = X + static_cast<int64_t>(g) * nkp * Lp;
   const uint16_t* Sg = S + static_cast<int64_t>(g) * nqp * nkp;
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Sg), 0, static_cast<int>(static_cast<int64_t>(nqp) * nkp * 2), 0x00020000);
   // staging lane offsets: X load q of wave w fills rows 16q + 4w + lane/16,
-  // S load q rows 32q + 8w + lane/8 (the swizzle depends on lane and w only)
+  // S load q rows 32q + 8w + lane/8 (the swizzles depend on lane and w only)
   const uint32_t vx_ld = static_cast<uint32_t>((4 * w + (lane >> 4)) * (Lp * 2) +
                                                (((lane & 15) ^ ((8 * w + 2 * (lane >> 4)) & 15)) << 4));
   const uint32_t vs_ld = static_cast<uint32_t>((8 * w + (lane >> 3)) * (nkp * 2) +
@@ -224,14 +225,12 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
   const uint32_t wb = static_cast<uint32_t>(w) * 1024u;
   auto stage = [&](int j0, int buf) {
 #pragma unroll
-    for (int sb = 0; sb < 2; sb++)
+    for (int q = 0; q < 4; q++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (LDS_AS void*)(&xs[buf][q * 4096 + wb]), 16, vx_ld,
+          static_cast<uint32_t>((j0 + 16 * q) * Lp * 2 + c0 * 2), 0, 0);
 #pragma unroll
-      for (int q = 0; q < 4; q++)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (LDS_AS void*)(&xs[buf][sb][q * 4096 + wb]), 16, vx_ld,
-            static_cast<uint32_t>((j0 + 16 * q) * Lp * 2 + (c0 + 128 * sb) * 2), 0, 0);
-#pragma unroll
-    for (int q = 0; q < 2; q++)
+    for (int q = 0; q < 4; q++)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (LDS_AS void*)(&ss[buf][q * 4096 + wb]), 16, vs_ld,
           static_cast<uint32_t>((i0 + 32 * q) * nkp * 2 + j0 * 2), 0, 0);
@@ -243,14 +242,14 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
   const uint32_t vread = static_cast<uint32_t>((4 * h + rsub) * 256 + ((cl ^ sv) << 4) + (lane & 1) * 8);
   uint32_t ax[2];
 #pragma unroll
-  for (int cbk = 0; cbk < 2; cbk++) ax[cbk] = vread ^ static_cast<uint32_t>((2 * (w & 1) + cbk) << 6);
+  for (int cbk = 0; cbk < 2; cbk++) ax[cbk] = vread ^ static_cast<uint32_t>((2 * wc + cbk) << 6);
   uint32_t bx[2];
 #pragma unroll
   for (int ib = 0; ib < 2; ib++) {
-    const int i = 32 * ib + l32;
+    const int i = 64 * wr + 32 * ib + l32;
     bx[ib] = static_cast<uint32_t>(i * 128 + 8 * h);
   }
-  const int bsw = (l32 >> 1) & 7;  // same for both row blocks (32ib + l32)
+  const int bsw = (l32 >> 1) & 7;  // the same for every row block (64wr + 32ib + l32)
   f32x16 acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; a++)
@@ -262,7 +261,7 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (st + 1 < nst) stage((st + 1) * kGemmJ, (st + 1) & 1);
-    const uint8_t* xt = xs[st & 1][w >> 1];
+    const uint8_t* xt = xs[st & 1];
     const uint8_t* sl = ss[st & 1];
 #pragma unroll
     for (int ks = 0; ks < kGemmJ / 16; ks++) {
@@ -293,10 +292,10 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
   for (int cbk = 0; cbk < 2; cbk++)
 #pragma unroll
     for (int ib = 0; ib < 2; ib++) {
-      const int i = i0 + 32 * ib + l32;
+      const int i = i0 + 64 * wr + 32 * ib + l32;
 #pragma unroll
       for (int r4 = 0; r4 < 4; r4++) {
-        const int c = c0 + 64 * w + 32 * cbk + 8 * r4 + 4 * h;
+        const int c = c0 + 64 * wc + 32 * cbk + 8 * r4 + 4 * h;
         float4 v;
         v.x = acc[cbk][ib][4 * r4 + 0];
         v.y = acc[cbk][ib][4 * r4 + 1];
