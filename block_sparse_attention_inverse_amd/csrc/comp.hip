@@ -22,7 +22,7 @@
 //   1. kv_moments_kernel: per kv-block j, X_j = [sum k v^T (d x d, row-major)
 //      | sum k | sum v | rows | 0...], bf16, one row of length Lp;
 //   2. skip_mask_kernel: S[i][j] = 1 for the kv-blocks row i skips, else 0
-//      (bf16; rows padded to a multiple of 64, columns to one of 32, with zeros);
+//      (bf16; rows padded to a multiple of 128, columns to one of 64, with zeros);
 //   3. skip_gemm_kernel: C = S . X per head (bf16 MFMA, fp32 accumulation):
 //      row i of C holds the sums over U_i, so M_i = C_kv - kbar Vhat^T;
 //   4. apply_kernel: one workgroup per q-block, the update above.
