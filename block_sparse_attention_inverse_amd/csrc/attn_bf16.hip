@@ -50,11 +50,12 @@
 // as the 64-row window that ends at row N (all rows real) and its columns
 // outside the sub-tile are masked.
 //
-// Grid order: workgroup b runs on XCD b mod 8; XCD x takes one contiguous
-// range of the head-major (head, q-block) tiles, so the workgroups resident
-// on an XCD belong to one head at almost any time and its 4 MB L2 serves a
-// single head's K/V (at 720p this halves the fetches that miss the L2,
-// against an order that spreads every head over all eight XCDs).
+// Grid order: workgroup b runs on XCD b mod 8; the XCDs work in two groups
+// of four, each group on one head at a time with every XCD of the group on
+// a contiguous quarter of that head's q-blocks, so the workgroups resident
+// on an XCD are neighbouring q-blocks of one head (its 4 MB L2 serves a
+// single head's K/V) and only two heads' K/V (78 MB at 720p) are in flight
+// in the last-level cache.
 #include <utility>
 
 #include "bsa_device.hpp"
@@ -450,7 +451,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t vb1[L::TB];
 
   int g, i;
-  if (!xcd_range_tile(blockIdx.x, nq, G, g, i)) return;
+  if (!xcd_group_tile(blockIdx.x, nq, G, g, i)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int qbase = i * BQ + w * 64;
@@ -684,7 +685,7 @@ __global__ __launch_bounds__(BQ) void fwd_bf16_kernel(
 template <int D, int BQ, int BK>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
   const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
-  const uint32_t nwg = kNumXcd * static_cast<uint32_t>((static_cast<int64_t>(a.G) * nq + kNumXcd - 1) / kNumXcd);
+  const uint32_t nwg = xcd_group_grid(nq, a.G);
   const float sm = a.sm_scale > 0.0f ? a.sm_scale : 1.0f / sqrtf(static_cast<float>(a.d));
   auto kern = a.N >= KT ? fwd_bf16_kernel<D, BQ, BK, false> : fwd_bf16_kernel<D, BQ, BK, true>;
   kern<<<nwg, BQ, 0, s>>>(static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),

@@ -113,6 +113,29 @@ __device__ __forceinline__ bool xcd_range_tile(uint32_t bid, int nq, int G, int&
   return true;
 }
 
+// Grouped tile order for (head, row-block) grids: the 8 XCDs form groups of
+// kXcdGroup; group p takes heads [p*hpg, (p+1)*hpg) in order, and within a
+// head XCD member m of the group takes the contiguous rows [m*per,
+// (m+1)*per).  Two heads are in flight at a time (their K/V stay resident in
+// the last-level cache) and each XCD's concurrent workgroups are neighbouring
+// rows of one head (which share K/V in its L2).  Grid size:
+// xcd_group_grid(nq, G); returns false for the padding slots.
+constexpr int kXcdGroup = 4;
+inline uint32_t xcd_group_grid(int nq, int G) {
+  constexpr int groups = kNumXcd / kXcdGroup;
+  const int64_t hpg = (G + groups - 1) / groups, per = (nq + kXcdGroup - 1) / kXcdGroup;
+  return static_cast<uint32_t>(kNumXcd * hpg * per);
+}
+__device__ __forceinline__ bool xcd_group_tile(uint32_t bid, int nq, int G, int& g, int& i) {
+  constexpr int groups = kNumXcd / kXcdGroup;
+  const int x = static_cast<int>(bid % kNumXcd), k = static_cast<int>(bid / kNumXcd);
+  const int hpg = (G + groups - 1) / groups, per = (nq + kXcdGroup - 1) / kXcdGroup;
+  const int hl = k / per;
+  g = (x / kXcdGroup) * hpg + hl;
+  i = (x % kXcdGroup) * per + k % per;
+  return hl < hpg && g < G && i < nq;
+}
+
 // Output row of reordered position r of head g under an OutMap-like
 // description: reordered [G][N][D] when orders is null, else the natural
 // token n = perm_g(r) at n*sn + g*sg; lse_idx receives the matching
