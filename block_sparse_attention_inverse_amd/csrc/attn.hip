@@ -18,7 +18,8 @@
 // and O = acc / l, LSE = (m + log2 l) * ln 2.
 //
 // Work split: one workgroup per (head g, q-block i); Bq/32 waves of 32 query
-// rows.  Two workgroups per CU put two waves on every SIMD, so one wave's
+// rows; XCD x runs a contiguous range of the head-major (head, q-block) tiles
+// (its L2 serves one head's INT8 K/V at a time).  Two workgroups per CU put two waves on every SIMD, so one wave's
 // v_mfma_i32_32x32x32_i8 products run under the other's softmax, quantising
 // and rescaling work (each wave needs at most 256 registers).  A tile is one
 // kv-block (the quantisation unit of P).
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
     const int8_t* __restrict__ Q, const float* __restrict__ sQ, const int8_t* __restrict__ K,
     const float* __restrict__ sK, const int8_t* __restrict__ V, const float* __restrict__ sV,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
-    int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int N, int nq, int nk,
+    int mask_G, uint16_t* __restrict__ O, float* __restrict__ lse, int G, int N, int nq, int nk,
     float scale_log2, OutMap om) {
   constexpr int NW = BQ / kRowsPerWave;
   constexpr int NB = BK / 32;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
   __shared__ float tile_max[2][NW];
 
   int g, i;
-  if (!head_sync_tile(blockIdx.x, nq, g, i)) return;
+  if (!xcd_range_tile(blockIdx.x, nq, G, g, i)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int qbase = i * BQ + w * kRowsPerWave;
@@ -621,11 +622,11 @@ template <int D, int BQ, int BK>
 struct LaunchI8 {
   static hipError_t run(const AttnArgs& a, hipStream_t s) {
     const int nq = (a.N + BQ - 1) / BQ, nk = (a.N + BK - 1) / BK;
-    const uint32_t nwg = static_cast<uint32_t>(a.G) * kNumXcd * ((nq + kNumXcd - 1) / kNumXcd);
+    const uint32_t nwg = kNumXcd * static_cast<uint32_t>((static_cast<int64_t>(a.G) * nq + kNumXcd - 1) / kNumXcd);
     fwd_i8_kernel<D, BQ, BK><<<nwg, BQ / kRowsPerWave * kWave, 0, s>>>(
         static_cast<const int8_t*>(a.Q), a.sQ, static_cast<const int8_t*>(a.K), a.sK,
         static_cast<const int8_t*>(a.V), a.sV, a.row_ptr, a.col_idx, a.col_len, a.mask_G, a.O,
-        a.lse, a.N, nq, nk, scale_log2_of(a), a.out);
+        a.lse, a.G, a.N, nq, nk, scale_log2_of(a), a.out);
     return hipGetLastError();
   }
 };

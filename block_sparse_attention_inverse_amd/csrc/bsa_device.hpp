@@ -73,30 +73,6 @@ __device__ __forceinline__ OrderMap order_map(int order, uint32_t F, uint32_t H,
   }
 }
 
-// Workgroup id -> logical tile id so that each XCD (which receives every
-// 8th workgroup) owns one contiguous range of logical tiles; neighbouring
-// tiles of one head then share that XCD's L2.
-__device__ __forceinline__ uint32_t xcd_swizzle(uint32_t bid, uint32_t nwg) {
-  const uint32_t q = nwg / kNumXcd, r = nwg % kNumXcd;
-  const uint32_t x = bid % kNumXcd, local = bid / kNumXcd;
-  return x * q + (x < r ? x : r) + local;
-}
-
-// Head-synchronous tile order for (head, row-block) grids: workgroup `bid`
-// runs on XCD bid % 8 as that XCD's (bid / 8)-th workgroup.  XCD x takes
-// rows [x*per, (x+1)*per) of every head, heads in order, so all XCDs work
-// on the same head at the same time (one head's K/V stays resident in the
-// shared last-level cache) while each XCD's L2 serves neighbouring rows.
-// Grid size must be 8 * per * G with per = ceil(nq / 8); returns false for
-// the padding slots (i >= nq).
-__device__ __forceinline__ bool head_sync_tile(uint32_t bid, int nq, int& g, int& i) {
-  const int per = (nq + kNumXcd - 1) / kNumXcd;
-  const int x = static_cast<int>(bid % kNumXcd), k = static_cast<int>(bid / kNumXcd);
-  g = k / per;
-  i = x * per + k % per;
-  return i < nq;
-}
-
 // XCD-contiguous tile order for (head, row-block) grids: the G*nq tiles in
 // head-major order are cut into 8 contiguous ranges of T = ceil(G*nq/8), and
 // XCD x (which receives workgroups bid with bid % 8 == x) runs range x in
