@@ -511,12 +511,14 @@ def power_probe(fns, seconds):
     """Socket power and graphics clocks while each workload runs back to back
     for about `seconds` (amd-smi sampled from a second thread, readings in the
     first and last half second dropped), beside the workload's own time per
-    launch.  The first sample is taken idle."""
+    launch.  The first sample is taken idle, 3 s after the preceding work."""
     import math
     import threading
 
     import torch
 
+    torch.cuda.synchronize()
+    time.sleep(3.0)  # let the averaged power reading settle after the preceding legs
     idle = smi_sample()
     if idle is None:
         return None
