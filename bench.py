@@ -524,7 +524,7 @@ def power_probe(fns, seconds):
         return None
     out = {"idle_socket_w": idle[0], "idle_gfx_mhz_mean": sum(idle[1]) / len(idle[1]),
            "tool": "amd-smi metric -p -c (SOCKET_POWER, GFX_n CLK)"}
-    for name, fn, est_ms, flop in fns:
+    for name, fn, est_ms, flop, peak in fns:
         n = max(3, math.ceil(seconds * 1e3 / est_ms))
         fn()
         torch.cuda.synchronize()
@@ -559,6 +559,9 @@ def power_probe(fns, seconds):
             rec["gfx_mhz_mean"] = sum(clks) / len(clks)
             rec["gfx_mhz_min"] = min(clks)
             rec["gfx_mhz_max"] = max(clks)
+            if peak is not None:
+                # the nominal peak holds at 2.4 GHz; scaled to the clock measured under this load
+                rec["frac_of_peak_at_measured_clock"] = rec["tflops"] / (peak * rec["gfx_mhz_mean"] / 2400.0)
         out[name] = rec
         log(f"[bench] power {name}: {rec}")
     return out
@@ -667,6 +670,8 @@ def main():
         bsa.order_scores(K, F, H, W, p.Bk, out=sk_buf, workspace=sics_ws)
         bsa.select_orders(sq_buf, sk_buf)
 
+    seg_stats = {}
+
     def timed(step, nev, label):
         for _ in range(args.warmup):
             step()
@@ -683,6 +688,7 @@ def main():
         seg = np.array([[evs[s][k].elapsed_time(evs[s][k + 1]) for k in range(nev)]
                         for s in range(args.steps)])
         log(f"[bench] {label}: {wall * 1e3:.3f} ms/step; segments (ms) {seg.mean(axis=0)}")
+        seg_stats[label] = seg
         return wall, seg.mean(axis=0)
 
     log("[bench] bf16 chain")
@@ -737,6 +743,12 @@ def main():
             "attention": float(seg[2]),
             "gaps": float(wall * 1e3 - seg.sum()),
         },
+        "attention_ms_median": float(np.median(seg_stats["bf16"][:, 2])),
+        "attention_ms_min": float(np.min(seg_stats["bf16"][:, 2])),
+        "overhead_share_of_step": {
+            "reorder_qkv_with_qk_block_sums": float(seg[0]) / (wall * 1e3),
+            "build_mask_from_sums": float(seg[1]) / (wall * 1e3),
+        },
         "unfused_ms": {
             "step": wall_u * 1e3,
             "reorder_qkv": float(seg_u[0]),
@@ -776,13 +788,14 @@ def main():
         gc = torch.empty(gm, gm, device="cuda", dtype=torch.bfloat16)
         fns = [("bf16_attention", lambda: bsa.forward_natural(
                     plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk, od, F, H, W,
-                    out=plan.O, lse=plan.lse), seg[2], fl_kept)]
+                    out=plan.O, lse=plan.lse), seg[2], fl_kept, PEAK_BF16_TFLOPS)]
         if not args.no_int8:
             fns.append(("int8_attention", lambda: bsa.forward_int8_natural(
                 plan8.Qq, plan8.sQ, plan8.Kq, plan8.sK, plan8.Vq, plan8.sV, plan8.row_ptr,
                 plan8.col_idx, p.Bq, p.Bk, od, F, H, W, out=plan8.O, lse=plan8.lse),
-                result["int8"]["attention_ms"], fl_kept))
-        fns.append(("torch_mm_bf16_8192", lambda: torch.mm(ga, gb, out=gc), 0.8, 2.0 * gm ** 3))
+                result["int8"]["attention_ms"], fl_kept, PEAK_INT8_TOPS))
+        fns.append(("torch_mm_bf16_8192", lambda: torch.mm(ga, gb, out=gc), 0.8, 2.0 * gm ** 3,
+                    PEAK_BF16_TFLOPS))
         step_bf16()
         result["power"] = power_probe(fns, seconds=4.0)
         del ga, gb, gc
