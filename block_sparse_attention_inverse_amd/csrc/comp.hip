@@ -196,7 +196,7 @@ constexpr int kGemmJ = 64;       // kv-blocks per stage
 constexpr int kXSub = 64 * 256;   // bytes of one X stage (64 rows x 128 columns)
 constexpr int kSTile = 128 * 128; // bytes of one S stage (128 rows x 64 kv-blocks)
 
-__global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16_t* __restrict__ S,
+__global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __restrict__ S,
                                                                     const uint16_t* __restrict__ X,
                                                                     int G, int nqp, int nkp, int Lp,
                                                                     int tiles_i, int tiles_c,
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
   const int tc = item / tiles_i, ti = item % tiles_i;
   const int i0 = ti * kTileI, c0 = tc * kTileC;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wr = w >> 1, wc = w & 1;
+  const int wr = w >> 1, wc = w & 1;  // 32-row quarter, 64-column half
   const int l32 = lane & 31, h = lane >> 5;
   const uint16_t* Xg = X + static_cast<int64_t>(g) * nkp * Lp;
   const uint16_t* Sg = S + static_cast<int64_t>(g) * nqp * nkp;
@@ -225,15 +225,15 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
   const uint32_t wb = static_cast<uint32_t>(w) * 1024u;
   auto stage = [&](int j0, int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; q++)
+    for (int q = 0; q < 2; q++)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (LDS_AS void*)(&xs[buf][q * 4096 + wb]), 16, vx_ld,
-          static_cast<uint32_t>((j0 + 16 * q) * Lp * 2 + c0 * 2), 0, 0);
+          rx, (LDS_AS void*)(&xs[buf][q * 8192 + wb]), 16, vx_ld,
+          static_cast<uint32_t>((j0 + 32 * q) * Lp * 2 + c0 * 2), 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; q++)
+    for (int q = 0; q < 2; q++)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (LDS_AS void*)(&ss[buf][q * 4096 + wb]), 16, vs_ld,
-          static_cast<uint32_t>((i0 + 32 * q) * nkp * 2 + j0 * 2), 0, 0);
+          rs, (LDS_AS void*)(&ss[buf][q * 8192 + wb]), 16, vs_ld,
+          static_cast<uint32_t>((i0 + 64 * q) * nkp * 2 + j0 * 2), 0, 0);
   };
   // operand read offsets
   const int rsub = (lane & 15) >> 2;
@@ -243,18 +243,12 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
   uint32_t ax[2];
 #pragma unroll
   for (int cbk = 0; cbk < 2; cbk++) ax[cbk] = vread ^ static_cast<uint32_t>((2 * wc + cbk) << 6);
-  uint32_t bx[2];
-#pragma unroll
-  for (int ib = 0; ib < 2; ib++) {
-    const int i = 64 * wr + 32 * ib + l32;
-    bx[ib] = static_cast<uint32_t>(i * 128 + 8 * h);
-  }
+  uint32_t bx[1];
+  bx[0] = static_cast<uint32_t>((32 * wr + l32) * 128 + 8 * h);
   const int bsw = (l32 >> 1) & 7;  // the same for every row block (64wr + 32ib + l32)
-  f32x16 acc[2][2];
+  f32x16 acc[2][1];
 #pragma unroll
-  for (int a = 0; a < 2; a++)
-#pragma unroll
-    for (int b = 0; b < 2; b++) acc[a][b] = f32x16{};
+  for (int a = 0; a < 2; a++) acc[a][0] = f32x16{};
   const int nst = nkp / kGemmJ;
   stage(0, 0);
   for (int st = 0; st < nst; st++) {
@@ -265,7 +259,7 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
     const uint8_t* sl = ss[st & 1];
 #pragma unroll
     for (int ks = 0; ks < kGemmJ / 16; ks++) {
-      bf16x8 a[2], b[2];
+      bf16x8 a[2], b[1];
 #pragma unroll
       for (int cbk = 0; cbk < 2; cbk++) {
         typedef short s4 __attribute__((ext_vector_type(4)));
@@ -275,24 +269,22 @@ __global__ __launch_bounds__(kCompThreads, 2) void skip_gemm_kernel(const uint16
                                                 lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
 #pragma unroll
-      for (int ib = 0; ib < 2; ib++) {
+      for (int ib = 0; ib < 1; ib++) {
         const uint2 lo = *reinterpret_cast<const uint2*>(sl + bx[ib] + (((2 * ks) ^ bsw) << 4));
         const uint2 hi = *reinterpret_cast<const uint2*>(sl + bx[ib] + (((2 * ks + 1) ^ bsw) << 4));
         b[ib] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
 #pragma unroll
       for (int cbk = 0; cbk < 2; cbk++)
-#pragma unroll
-        for (int ib = 0; ib < 2; ib++)
-          acc[cbk][ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cbk], b[ib], acc[cbk][ib], 0, 0, 0);
+        acc[cbk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cbk], b[0], acc[cbk][0], 0, 0, 0);
     }
   }
   float* Cg = C + static_cast<int64_t>(g) * nqp * Lp;
 #pragma unroll
   for (int cbk = 0; cbk < 2; cbk++)
 #pragma unroll
-    for (int ib = 0; ib < 2; ib++) {
-      const int i = i0 + 64 * wr + 32 * ib + l32;
+    for (int ib = 0; ib < 1; ib++) {
+      const int i = i0 + 32 * wr + l32;
 #pragma unroll
       for (int r4 = 0; r4 < 4; r4++) {
         const int c = c0 + 64 * wc + 32 * cbk + 8 * r4 + 4 * h;
@@ -482,7 +474,7 @@ hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint
   const int ti = L.nqp / kTileI, tc = L.Lp / kTileC;
   const int64_t tiles = static_cast<int64_t>(G) * ti * tc;
   const uint32_t ng = kNumXcd * static_cast<uint32_t>((tiles + kNumXcd - 1) / kNumXcd);
-  skip_gemm_kernel<<<ng, kCompThreads, 0, s>>>(S, X, G, L.nqp, L.nkp, L.Lp, ti, tc, C);
+  skip_gemm_kernel<<<ng, 512, 0, s>>>(S, X, G, L.nqp, L.nkp, L.Lp, ti, tc, C);
   const uint32_t ga = static_cast<uint32_t>(G) * L.nq;
   if (d == 128)
     apply_kernel<128><<<ga, kCompThreads, 0, s>>>(Q, C, N, Bq, L.nq, L.nqp, L.Lp, sm, O, lse, om);
