@@ -187,9 +187,9 @@ __global__ __launch_bounds__(kCompThreads) void skip_mask_kernel(
 //            16ks + 4h + (0..3) and 16ks + 8 + 4h + (0..3) of k-step ks;
 //   S stage: 128 x 64 (128-byte rows), chunk p of row r at p ^ ((r/2) mod 8);
 //            B operands are two 8-byte reads in the same kv-block order.
-// Wave w owns rows [64(w/2), +64) and columns [64(w%2), +64) (channel
-// blocks 2(w%2), 2(w%2)+1): 2 x 2 accumulators; lane l of an accumulator
-// holds row ib + l%32 and columns cb + 8(r/4) + 4(l/32) + r%4.
+// Eight waves: wave w owns rows [32(w/2), +32) and columns [64(w%2), +64)
+// (channel blocks 2(w%2), 2(w%2)+1): two accumulators; lane l of an
+// accumulator holds row 32(w/2) + l%32 and columns cb + 8(r/4) + 4(l/32) + r%4.
 // Tiles go to XCDs in contiguous ranges ordered (head, column tile, row
 // tile), so the row tiles that share an X stage run together on one L2.
 constexpr int kGemmJ = 64;       // kv-blocks per stage
@@ -216,8 +216,8 @@ __global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __res
       const_cast<uint16_t*>(Xg), 0, static_cast<int>(static_cast<int64_t>(nkp) * Lp * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Sg), 0, static_cast<int>(static_cast<int64_t>(nqp) * nkp * 2), 0x00020000);
-  // staging lane offsets: X load q of wave w fills rows 16q + 4w + lane/16,
-  // S load q rows 32q + 8w + lane/8 (the swizzles depend on lane and w only)
+  // staging lane offsets: X load q of wave w fills rows 32q + 4w + lane/16,
+  // S load q rows 64q + 8w + lane/8 (the swizzles depend on lane and w only)
   const uint32_t vx_ld = static_cast<uint32_t>((4 * w + (lane >> 4)) * (Lp * 2) +
                                                (((lane & 15) ^ ((8 * w + 2 * (lane >> 4)) & 15)) << 4));
   const uint32_t vs_ld = static_cast<uint32_t>((8 * w + (lane >> 3)) * (nkp * 2) +
