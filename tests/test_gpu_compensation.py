@@ -151,3 +151,41 @@ def test_compensation_reaches_dense_attention_when_skipped_keys_agree(bsa_gpu):
     err0 = np.linalg.norm(O0.cpu().numpy() - ref) / np.linalg.norm(ref)
     _say(f"  compensated rel_l2 vs dense {err:.3e} (masked only {err0:.3e})")
     assert err < 1e-2 and err0 > 5e-2
+
+
+def test_compensation_shared_mask_strided_output_and_scale(bsa_gpu, orc):
+    """Batch copies sharing one mask (mask_G = 2 of G = 4 heads), the
+    natural-order output written into a strided [G][N][d] buffer viewed as
+    [N][G][d], and an explicit softmax scale: every row against the oracle."""
+    from block_sparse_attention_inverse_amd import synth
+
+    F, H, W, G, d, B = 2, 6, 21, 4, 64, 64
+    N = F * H * W
+    mask_G = 2
+    sm = 0.21
+    r = np.random.Generator(np.random.PCG64(4242))
+    orders = np.array([3, 1, 4, 0], np.uint8)
+    nat = [torch.from_numpy(r.standard_normal((N, G, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+           for _ in range(3)]
+    rp, ci = synth.static_mask(mask_G, N, B, B, 2, 4343)
+    od = torch.from_numpy(orders).cuda()
+    Qp, Kp, Vp = (bsa_gpu.permute(x, od, F, H, W, 0) for x in nat)
+    grp, gci = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    base = torch.full((G, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Ov = base.transpose(0, 1)  # [N][G][d] view, strides (d, N*d, 1)
+    _, lse = bsa_gpu.forward_natural(Qp, Kp, Vp, grp, gci, B, B, od, F, H, W, mask_G=mask_G,
+                                     sm_scale=sm, out=Ov)
+    bsa_gpu.fo_compensate(Qp, Kp, Vp, grp, gci, B, B, Ov, lse, od, F, H, W, mask_G=mask_G,
+                          sm_scale=sm)
+    torch.cuda.synchronize()
+    _say("[compensation shared mask, strided output, sm_scale 0.21]")
+    host = {k: _bits(x) for k, x in zip("QKV", nat)}
+    rows = np.array([(g, n) for g in range(G) for n in range(N)], np.int64)
+    Ow, Lw = orc.attention_rows_fo(host["Q"], host["K"], host["V"], G, F, H, W, d, orders, rows, B, B,
+                                   rp, ci, mask_G=mask_G, sm_scale=sm)
+    got = _np(Ov.float())[rows[:, 1], rows[:, 0]]
+    _compare(got, Ow, heads=rows[:, 0], tag="fo shared mask strided")
+    lg = _np(lse)[rows[:, 0], rows[:, 1]]
+    err = np.abs(lg - Lw)
+    _say(f"  lse max_abs={err.max():.3e}")
+    assert np.all(err <= LSE_ABS + 2.0 ** -21 * np.abs(Lw))
