@@ -40,31 +40,35 @@ __device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-// K staging: 64-key tiles pass HBM/L2 -> registers -> LDS once per
-// workgroup (four waves share them).  16-byte chunk c of tile row r sits at
-// chunk position c ^ (r mod CH), so that the operand reads (32 rows, one
-// chunk each per half-wave) hit distinct banks.
+// K staging: 64-key tiles move global -> LDS once per workgroup (four waves
+// share them) with 16-byte buffer loads that write LDS directly; rows past N
+// read as zero (their keys are masked).  16-byte chunk c of tile row r sits
+// at chunk position c ^ (r mod CH), so that the operand reads (32 rows, one
+// chunk each per half-wave) hit distinct banks; the swizzle is realised by
+// the chunk each lane fetches.
 template <int D>
 struct KStage {
   static constexpr int CH = D / 8;                 // 16-byte chunks per row
   static constexpr int ROWB = D * 2;               // bytes per row
   static constexpr int TILEB = 64 * ROWB;          // bytes per 64-key tile
-  static constexpr int PER = TILEB / 16 / 256;     // chunks per thread per tile
-  uint4 r[PER];
-  __device__ __forceinline__ void load(const uint16_t* K, int N, int key0, int t) {
-#pragma unroll
-    for (int q = 0; q < PER; q++) {
-      const int e = q * 256 + t, row = e / CH, ch = e % CH;
-      const int kr = min(key0 + row, N - 1);
-      r[q] = *reinterpret_cast<const uint4*>(K + static_cast<int64_t>(kr) * D + ch * 8);
-    }
+  static constexpr int RPL = 1024 / ROWB;          // rows per 1 KB wave-load
+  static constexpr int NL = TILEB / 1024 / 4;      // loads per wave per tile
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff;  // load q of wave w fills rows RPL*(4q + w) + lane/CH; the swizzle is q-independent
+  uint32_t wb;
+  __device__ __forceinline__ void init(const uint16_t* K, int N, int t) {
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K), 0, N * ROWB, 0x00020000);
+    const int lane = t & 63, w = t >> 6;
+    const int r = RPL * w + lane / CH, p = lane % CH;
+    voff = static_cast<uint32_t>(r * ROWB + ((p ^ (r % CH)) << 4));
+    wb = static_cast<uint32_t>(w) * 1024u;
   }
-  __device__ __forceinline__ void store(uint8_t* lds, int t) const {
+  __device__ __forceinline__ void load(uint8_t* lds, int key0) const {
 #pragma unroll
-    for (int q = 0; q < PER; q++) {
-      const int e = q * 256 + t, row = e / CH, ch = e % CH;
-      *reinterpret_cast<uint4*>(lds + row * ROWB + ((ch ^ (row % CH)) * 16)) = r[q];
-    }
+    for (int q = 0; q < NL; q++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds + q * 4096 + wb), 16, voff,
+          static_cast<uint32_t>((key0 + 4 * RPL * q) * ROWB), 0, 0);
   }
 };
 
@@ -126,6 +130,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int ntile = (N + 63) / 64;    // 64-key LDS tiles
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
   KStage<D> st;
+  st.init(K, N, tid);
   auto lse_sub = [&](int t, const uint8_t* lds, int u) {
     f32x16 acc[2];
     s_tile_lds<D>(lds, u, lane, qop, acc);
@@ -155,14 +160,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   // one barrier per tile: in step T the waves read buffer T&1, then write
   // tile T+1 into the other buffer, which every wave finished reading in
   // step T-1 (before the barrier that ended it)
-  st.load(K, N, 0, tid);
-  st.store(kt[0], tid);
+  st.load(kt[0], 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int T = 0; T < ntile; T++) {
-    if (T + 1 < ntile) st.load(K, N, 64 * (T + 1), tid);
+    // the other buffer was last read in tile T-1, before the barrier that ended it
+    if (T + 1 < ntile) st.load(kt[(T + 1) & 1], 64 * (T + 1));
     lse_sub(2 * T, kt[T & 1], 0);
     if (2 * T + 1 < nt) lse_sub(2 * T + 1, kt[T & 1], 1);
-    if (T + 1 < ntile) st.store(kt[(T + 1) & 1], tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   float lse2[2];
@@ -245,17 +251,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     csum = 0.0f;
     xmax = -INFINITY;
   };
-  st.load(K, N, 0, tid);
-  st.store(kt[0], tid);
+  st.load(kt[0], 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int T = 0; T < ntile; T++) {
-    if (T + 1 < ntile) st.load(K, N, 64 * (T + 1), tid);
+    if (T + 1 < ntile) st.load(kt[(T + 1) & 1], 64 * (T + 1));
     stat_sub(2 * T, kt[T & 1], 0);
     if (2 * T + 1 < nt) stat_sub(2 * T + 1, kt[T & 1], 1);
     // the tile ends kv-block T*64/B when it is the block's last tile or the
     // last tile of all
     if ((64 * (T + 1)) % B == 0 || T + 1 == ntile) flush((64 * T) / B);
-    if (T + 1 < ntile) st.store(kt[(T + 1) & 1], tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 }
