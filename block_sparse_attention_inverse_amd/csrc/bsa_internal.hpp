@@ -128,6 +128,7 @@ hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s);
 // C (fp32 [G][nqp][Lp]); byte offsets 256-aligned.
 struct FoLayout {
   int nq, nk, nqp, nkp, Lp;
+  int64_t gemm_tiles;  // skip-mask GEMM workgroups over all heads
   size_t x, s, c, total;
 };
 FoLayout fo_layout(int G, int N, int d, int Bq, int Bk);

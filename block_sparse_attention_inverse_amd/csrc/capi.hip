@@ -643,8 +643,8 @@ int bsa_fo_compensate(const void* Qp, const void* Kp, const void* Vp, const int3
     if (ws_bytes < need)
       return fail(BSA_ECAPACITY, "workspace %lld bytes < required %lld", (long long)ws_bytes, (long long)need);
     const bsa::FoLayout L = bsa::fo_layout(G, N, d, Bq, Bk);
-    if (static_cast<int64_t>(G) * (L.nqp / 64) * (L.Lp / 256) >= (1ll << 31) ||
-        static_cast<int64_t>(G) * L.nkp >= (1ll << 31))
+    if (L.gemm_tiles >= (1ll << 31) || static_cast<int64_t>(G) * L.nkp >= (1ll << 31) ||
+        static_cast<int64_t>(G) * L.nqp >= (1ll << 31))
       return fail(BSA_EUNSUPPORTED, "grid too large");
     return hip_status(bsa::launch_fo_compensate(static_cast<const uint16_t*>(Qp),
                                                 static_cast<const uint16_t*>(Kp),

@@ -443,6 +443,7 @@ FoLayout fo_layout(int G, int N, int d, int Bq, int Bk) {
   L.nqp = round_up(L.nq, kTileI);
   L.nkp = round_up(L.nk, kStageJ);
   L.Lp = round_up(d * d + 2 * d + 1, kTileC);
+  L.gemm_tiles = static_cast<int64_t>(G) * (L.nqp / kTileI) * (L.Lp / kTileC);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -472,8 +473,7 @@ hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint
   skip_mask_kernel<<<static_cast<uint32_t>(G) * L.nqp, kCompThreads, sizeof(uint16_t) * L.nkp, s>>>(
       row_ptr, col_idx, col_len, mask_G, L.nq, L.nk, L.nqp, L.nkp, S);
   const int ti = L.nqp / kTileI, tc = L.Lp / kTileC;
-  const int64_t tiles = static_cast<int64_t>(G) * ti * tc;
-  const uint32_t ng = kNumXcd * static_cast<uint32_t>((tiles + kNumXcd - 1) / kNumXcd);
+  const uint32_t ng = kNumXcd * static_cast<uint32_t>((L.gemm_tiles + kNumXcd - 1) / kNumXcd);
   skip_gemm_kernel<<<ng, 512, 0, s>>>(S, X, G, L.nqp, L.nkp, L.Lp, ti, tc, C);
   const uint32_t ga = static_cast<uint32_t>(G) * L.nq;
   if (d == 128)
