@@ -452,7 +452,7 @@ def density_sweep(plan, plan8, Q, K, V, od, F, H, W, reps, rhos=((30, 100), (20,
     return res
 
 
-def compensation(plan, od, F, H, W, reps):
+def compensation(plan, od, F, H, W, reps, Qn, Kn, Vn):
     """First-order compensation of the skipped keys on the 720p layer, after
     the bf16 forward with its natural-order output (the mask and the
     reordered tensors of the last bf16 step): its time beside the attention's,
@@ -479,6 +479,28 @@ def compensation(plan, od, F, H, W, reps):
     t_comp = event_ms(comp, reps)
     nq, nk = -(-N // p.Bq), -(-N // p.Bk)
     fl = 2.0 * nq * nk * (d * d + 2 * d + 1) * G
+    # what the compensation buys: on sampled rows of a few heads, the relative
+    # L2 distance of the block-sparse output to dense softmax attention (fp32
+    # on the GPU, from the same bf16 inputs) without and with it
+    fwd()
+    O_masked = O.clone()
+    comp()
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(7)
+    rows = torch.randint(0, N, (1024,), generator=gen).cuda()
+    sm = 1.0 / float(d) ** 0.5
+    num_m = num_c = den = 0.0
+    heads = [0, G // 3, (2 * G) // 3, G - 1]
+    for g in heads:
+        kg = Kn[:, g, :].float().contiguous()
+        vg = Vn[:, g, :].float().contiguous()
+        qs = Qn[rows, g, :].float().contiguous()
+        s = torch.mm(qs, kg.t().contiguous()) * sm
+        ref = torch.mm(torch.softmax(s, dim=1), vg)
+        num_m += float(torch.sum((O_masked[rows, g, :].float() - ref) ** 2))
+        num_c += float(torch.sum((O[rows, g, :].float() - ref) ** 2))
+        den += float(torch.sum(ref ** 2))
+        del s
     return {
         "ms": t_comp,
         "workspace_gib": ws.numel() / 2**30,
@@ -486,6 +508,11 @@ def compensation(plan, od, F, H, W, reps):
         "skip_gemm_tflops_if_whole_time": fl / (t_comp / 1e3) / 1e12,
         "policy": "one expansion point per q-block row (the mean of its skipped keys), "
                   "first-order Taylor term of exp(s q.k) summed over the skipped set",
+        "vs_dense_rel_l2": {
+            "rows": f"1024 random tokens of heads {heads}, dense softmax attention in fp32 on the GPU",
+            "block_sparse": (num_m / den) ** 0.5,
+            "block_sparse_compensated": (num_c / den) ** 0.5,
+        },
     }
 
 
@@ -778,7 +805,8 @@ def main():
                                           reps=max(3, args.steps // 4))
         log("[bench] first-order compensation")
         step_bf16()
-        result["compensation"] = compensation(plan, od, F, H, W, reps=max(3, args.steps // 4))
+        result["compensation"] = compensation(plan, od, F, H, W, reps=max(3, args.steps // 4),
+                                              Qn=Q, Kn=K, Vn=V)
         log(f"[bench] compensation: {result['compensation']}")
     if not args.no_power:
         log("[bench] power and clocks")
