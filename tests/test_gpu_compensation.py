@@ -189,3 +189,39 @@ def test_compensation_shared_mask_strided_output_and_scale(bsa_gpu, orc):
     err = np.abs(lg - Lw)
     _say(f"  lse max_abs={err.max():.3e}")
     assert np.all(err <= LSE_ABS + 2.0 ** -21 * np.abs(Lw))
+
+
+def test_compensation_leaves_rows_without_skipped_keys_unchanged(bsa_gpu):
+    """Every kv-block kept (100 % density, nothing skipped): O and lse come
+    back bit for bit; with one row of q-blocks empty instead (nothing kept),
+    that row's output becomes the compensation alone and stays finite."""
+    F, H, W, G, d, B = 1, 5, 40, 2, 128, 64
+    N = F * H * W
+    nq = nk = -(-N // B)
+    r = np.random.Generator(np.random.PCG64(515))
+    od = torch.zeros(G, dtype=torch.uint8).cuda()
+    nat = [torch.from_numpy(r.standard_normal((N, G, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+           for _ in range(3)]
+    Qp, Kp, Vp = (bsa_gpu.permute(x, od, F, H, W, 0) for x in nat)
+    rp = np.arange(0, G * nq * nk + 1, nk, dtype=np.int32)
+    ci = np.tile(np.arange(nk, dtype=np.int32), G * nq)
+    grp, gci = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    O, lse = bsa_gpu.forward_natural(Qp, Kp, Vp, grp, gci, B, B, od, F, H, W)
+    O0, L0 = O.clone(), lse.clone()
+    bsa_gpu.fo_compensate(Qp, Kp, Vp, grp, gci, B, B, O, lse, od, F, H, W)
+    torch.cuda.synchronize()
+    _say("[compensation, nothing skipped]")
+    assert torch.equal(O.view(torch.int16), O0.view(torch.int16))
+    assert torch.equal(lse, L0)
+    # q-block 0 of every head keeps nothing: its rows get the compensation alone
+    sets = [[] if i == 0 else list(range(nk)) for _ in range(G) for i in range(nq)]
+    rp2 = np.cumsum([0] + [len(x) for x in sets]).astype(np.int32)
+    ci2 = np.array([j for x in sets for j in x], np.int32)
+    grp2, gci2 = torch.from_numpy(rp2).cuda(), torch.from_numpy(ci2).cuda()
+    O2, l2 = bsa_gpu.forward_natural(Qp, Kp, Vp, grp2, gci2, B, B, od, F, H, W)
+    torch.cuda.synchronize()
+    assert torch.all(O2[:B].float() == 0) and torch.all(torch.isinf(l2[:, :B]))
+    bsa_gpu.fo_compensate(Qp, Kp, Vp, grp2, gci2, B, B, O2, l2, od, F, H, W)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(O2.float())) and torch.all(torch.isfinite(l2))
+    assert float(O2[:B].float().abs().sum()) > 0
