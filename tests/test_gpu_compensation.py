@@ -191,10 +191,11 @@ def test_compensation_shared_mask_strided_output_and_scale(bsa_gpu, orc):
     assert np.all(err <= LSE_ABS + 2.0 ** -21 * np.abs(Lw))
 
 
-def test_compensation_leaves_rows_without_skipped_keys_unchanged(bsa_gpu):
+def test_compensation_leaves_rows_without_skipped_keys_unchanged(bsa_gpu, orc):
     """Every kv-block kept (100 % density, nothing skipped): O and lse come
     back bit for bit; with one row of q-blocks empty instead (nothing kept),
-    that row's output becomes the compensation alone and stays finite."""
+    that row's output becomes the compensation alone, finite and equal to the
+    oracle's."""
     F, H, W, G, d, B = 1, 5, 40, 2, 128, 64
     N = F * H * W
     nq = nk = -(-N // B)
@@ -225,3 +226,12 @@ def test_compensation_leaves_rows_without_skipped_keys_unchanged(bsa_gpu):
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(O2.float())) and torch.all(torch.isfinite(l2))
     assert float(O2[:B].float().abs().sum()) > 0
+    host = {k: _bits(x) for k, x in zip("QKV", nat)}
+    rows = np.array([(g, n) for g in range(G) for n in range(B)], np.int64)
+    Ow, Lw = orc.attention_rows_fo(host["Q"], host["K"], host["V"], G, F, H, W, d,
+                                   np.zeros(G, np.uint8), rows, B, B, rp2, ci2)
+    got = _np(O2.float())[rows[:, 1], rows[:, 0]]
+    _compare(got, Ow, heads=rows[:, 0], tag="fo empty rows")
+    err = np.abs(_np(l2)[rows[:, 0], rows[:, 1]] - Lw)
+    _say(f"  lse max_abs={err.max():.3e}")
+    assert np.all(err <= LSE_ABS + 2.0 ** -21 * np.abs(Lw))
