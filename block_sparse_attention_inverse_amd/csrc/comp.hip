@@ -123,14 +123,19 @@ __global__ __launch_bounds__(kCompThreads) void kv_moments_kernel(const uint16_t
         else sm[y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, tr(vt[u], ks, sb - DB), sm[y], 0, 0, 0);
       }
     }
-  // KV tile: lane holds channel b = 32bb + l32 of rows a = 32ab + 8(r/4) + 4h + r%4
+  // KV tile: lane holds channel b = 32bb + l32 of rows a = 32ab + 8(r/4) + 4h + r%4.
+  // The tiles go through LDS (over the staged K, which every wave has
+  // finished reading) so that the row is written with 16-byte stores.
+  static_assert(2 * TB >= D * D * 2, "the K staging area holds the d x d block");
+  __syncthreads();
+  uint16_t* ot = reinterpret_cast<uint16_t*>(&kt[0][0]);
 #pragma unroll
   for (int x = 0; x < TPW; x++) {
     const int k = w * TPW + x, ab = k / DB, bb = k % DB;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int a = 32 * ab + 8 * (r / 4) + 4 * h + (r % 4);
-      xr[a * D + 32 * bb + l32] = bf16_bits(kv[x][r]);
+      ot[a * D + 32 * bb + l32] = bf16_bits(kv[x][r]);
     }
   }
   // sum k (rows of the product, every column alike: column 0 writes) and
@@ -148,6 +153,10 @@ __global__ __launch_bounds__(kCompThreads) void kv_moments_kernel(const uint16_t
   }
   if (t == 0) xr[D * D + 2 * D] = bf16_bits(static_cast<float>(r1 - r0));
   for (int c = D * D + 2 * D + 1 + t; c < Lp; c += kCompThreads) xr[c] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int c = t; c < D * D / 8; c += kCompThreads)
+    *reinterpret_cast<uint4*>(xr + 8 * c) = *reinterpret_cast<const uint4*>(ot + 8 * c);
 }
 
 // 2. S[g][i][j] = 1 for the kv-blocks q-block row i skips (padding: 0)
