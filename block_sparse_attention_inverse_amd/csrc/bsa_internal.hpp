@@ -128,8 +128,9 @@ hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s);
 // C (fp32 [G][nqp][Lp]); byte offsets 256-aligned.
 struct FoLayout {
   int nq, nk, nqp, nkp, Lp;
+  int Lt;              // columns of C past the d x d block (sums of k and v, count, padding)
   int64_t gemm_tiles;  // skip-mask GEMM workgroups over all heads
-  size_t x, s, c, total;
+  size_t x, s, ckv, ct, total;  // moments, skip mask, C's d x d block (bf16), C's tail (fp32)
 };
 FoLayout fo_layout(int G, int N, int d, int Bq, int Bk);
 // O (bf16) and lse (fp32) as a forward wrote them (reordered, or natural

@@ -24,7 +24,8 @@
 //   2. skip_mask_kernel: S[i][j] = 1 for the kv-blocks row i skips, else 0
 //      (bf16; rows padded to a multiple of 128, columns to one of 64, with zeros);
 //   3. skip_gemm_kernel: C = S . X per head (bf16 MFMA, fp32 accumulation):
-//      row i of C holds the sums over U_i, so M_i = C_kv - kbar Vhat^T;
+//      row i of C holds the sums over U_i, so M_i = C_kv - kbar Vhat^T (the
+//      d x d block C_kv stored as bf16, the sums and the count as fp32);
 //   4. apply_kernel: one workgroup per q-block, the update above.
 // Step 3 is the only heavy one: 2 * nq * nk * Lp flops per head.
 #include "bsa_device.hpp"
@@ -208,8 +209,9 @@ constexpr int kSTile = 128 * 128; // bytes of one S stage (128 rows x 64 kv-bloc
 __global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __restrict__ S,
                                                                     const uint16_t* __restrict__ X,
                                                                     int G, int nqp, int nkp, int Lp,
-                                                                    int tiles_i, int tiles_c,
-                                                                    float* __restrict__ C) {
+                                                                    int dd, int tiles_i, int tiles_c,
+                                                                    uint16_t* __restrict__ Ckv,
+                                                                    float* __restrict__ Ct) {
   __shared__ __attribute__((aligned(1024))) uint8_t xs[2][kXSub];
   __shared__ __attribute__((aligned(1024))) uint8_t ss[2][kSTile];
   int g, item;
@@ -288,21 +290,25 @@ __global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __res
         acc[cbk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cbk], b[0], acc[cbk][0], 0, 0, 0);
     }
   }
-  float* Cg = C + static_cast<int64_t>(g) * nqp * Lp;
+  // C's d x d block is stored as bf16 (it becomes the bf16 M^T operand of the
+  // update), the sums and the count as fp32; a tile lies wholly on one side
+  const int i = i0 + 32 * wr + l32;
+  const int64_t row = static_cast<int64_t>(g) * nqp + i;
+  const int Lt = Lp - dd;
 #pragma unroll
   for (int cbk = 0; cbk < 2; cbk++)
 #pragma unroll
-    for (int ib = 0; ib < 1; ib++) {
-      const int i = i0 + 32 * wr + l32;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; r4++) {
-        const int c = c0 + 64 * wc + 32 * cbk + 8 * r4 + 4 * h;
-        float4 v;
-        v.x = acc[cbk][ib][4 * r4 + 0];
-        v.y = acc[cbk][ib][4 * r4 + 1];
-        v.z = acc[cbk][ib][4 * r4 + 2];
-        v.w = acc[cbk][ib][4 * r4 + 3];
-        *reinterpret_cast<float4*>(Cg + static_cast<int64_t>(i) * Lp + c) = v;
+    for (int r4 = 0; r4 < 4; r4++) {
+      const int c = c0 + 64 * wc + 32 * cbk + 8 * r4 + 4 * h;
+      const float v[4] = {acc[cbk][0][4 * r4], acc[cbk][0][4 * r4 + 1], acc[cbk][0][4 * r4 + 2],
+                          acc[cbk][0][4 * r4 + 3]};
+      if (c0 < dd) {
+        uint2 pk;
+        pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        *reinterpret_cast<uint2*>(Ckv + row * dd + c) = pk;
+      } else {
+        *reinterpret_cast<float4*>(Ct + row * Lt + (c - dd)) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
 }
@@ -322,8 +328,9 @@ __global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __res
 //      (the old values are read before the products).
 template <int D>
 __global__ __launch_bounds__(kCompThreads, 3) void apply_kernel(
-    const uint16_t* __restrict__ Q, const float* __restrict__ C, int N, int Bq, int nq, int nqp,
-    int Lp, float sm, uint16_t* __restrict__ O, float* __restrict__ lse, OutMap om) {
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Ckv, const float* __restrict__ Ct,
+    int N, int Bq, int nq, int nqp, int Lt, float sm, uint16_t* __restrict__ O, float* __restrict__ lse,
+    OutMap om) {
   constexpr int NB = D / 32;      // 32-channel blocks of the output
   constexpr int KS = D / 16;      // k-steps of Y = Q M
   constexpr int PM = D + 8;       // bf16 per LDS row of M^T
@@ -334,21 +341,22 @@ __global__ __launch_bounds__(kCompThreads, 3) void apply_kernel(
   const int g = blockIdx.x / nq, i = blockIdx.x % nq;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const float* Ci = C + (static_cast<int64_t>(g) * nqp + i) * Lp;
+  const uint16_t* Ci = Ckv + (static_cast<int64_t>(g) * nqp + i) * D * D;  // sums over U of k v^T
+  const float* Cs = Ct + (static_cast<int64_t>(g) * nqp + i) * Lt;          // sum k, sum v, count
   const int r0 = i * Bq, nr = min(Bq, N - r0);
   const uint16_t* Qi = Q + (static_cast<int64_t>(g) * N + r0) * D;
   const int rb = 32 * w, qrow = rb + l32;
   // a. reads
   constexpr int KM = D * (D / 8) / kCompThreads;
-  float cm[KM][8];
+  uint16_t cm[KM][8];
 #pragma unroll
   for (int k = 0; k < KM; k++) {
     const int e = t + kCompThreads * k, b = e % D, a0 = 8 * (e / D);
 #pragma unroll
     for (int q = 0; q < 8; q++) cm[k][q] = Ci[(a0 + q) * D + b];
   }
-  const float sums = t < 2 * D ? Ci[D * D + t] : 0.0f;
-  const float n = Ci[D * D + 2 * D];
+  const float sums = t < 2 * D ? Cs[t] : 0.0f;
+  const float n = Cs[2 * D];
   uint4 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ks++) {
@@ -367,8 +375,8 @@ __global__ __launch_bounds__(kCompThreads, 3) void apply_kernel(
     uint32_t pk[4];
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const float m0 = cm[k][2 * q] - kbar[a0 + 2 * q] * vb;
-      const float m1 = cm[k][2 * q + 1] - kbar[a0 + 2 * q + 1] * vb;
+      const float m0 = bf16_bits_to_f32(cm[k][2 * q]) - kbar[a0 + 2 * q] * vb;
+      const float m1 = bf16_bits_to_f32(cm[k][2 * q + 1]) - kbar[a0 + 2 * q + 1] * vb;
       pk[q] = f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);
     }
     *reinterpret_cast<uint4*>(&mt[b][a0]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
@@ -461,7 +469,9 @@ FoLayout fo_layout(int G, int N, int d, int Bq, int Bk) {
   };
   L.x = take(sizeof(uint16_t) * static_cast<size_t>(G) * L.nkp * L.Lp);
   L.s = take(sizeof(uint16_t) * static_cast<size_t>(G) * L.nqp * L.nkp);
-  L.c = take(sizeof(float) * static_cast<size_t>(G) * L.nqp * L.Lp);
+  L.Lt = L.Lp - d * d;
+  L.ckv = take(sizeof(uint16_t) * static_cast<size_t>(G) * L.nqp * d * d);
+  L.ct = take(sizeof(float) * static_cast<size_t>(G) * L.nqp * L.Lt);
   L.total = off;
   return L;
 }
@@ -474,7 +484,8 @@ hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint
   const FoLayout L = fo_layout(G, N, d, Bq, Bk);
   auto* X = reinterpret_cast<uint16_t*>(ws + L.x);
   auto* S = reinterpret_cast<uint16_t*>(ws + L.s);
-  auto* C = reinterpret_cast<float*>(ws + L.c);
+  auto* Ckv = reinterpret_cast<uint16_t*>(ws + L.ckv);
+  auto* Ct = reinterpret_cast<float*>(ws + L.ct);
   const float sm = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d));
   const uint32_t gm = static_cast<uint32_t>(G) * L.nkp;
   if (d == 128) kv_moments_kernel<128><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
@@ -483,12 +494,12 @@ hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint
       row_ptr, col_idx, col_len, mask_G, L.nq, L.nk, L.nqp, L.nkp, S);
   const int ti = L.nqp / kTileI, tc = L.Lp / kTileC;
   const uint32_t ng = kNumXcd * static_cast<uint32_t>((L.gemm_tiles + kNumXcd - 1) / kNumXcd);
-  skip_gemm_kernel<<<ng, 512, 0, s>>>(S, X, G, L.nqp, L.nkp, L.Lp, ti, tc, C);
+  skip_gemm_kernel<<<ng, 512, 0, s>>>(S, X, G, L.nqp, L.nkp, L.Lp, d * d, ti, tc, Ckv, Ct);
   const uint32_t ga = static_cast<uint32_t>(G) * L.nq;
   if (d == 128)
-    apply_kernel<128><<<ga, kCompThreads, 0, s>>>(Q, C, N, Bq, L.nq, L.nqp, L.Lp, sm, O, lse, om);
+    apply_kernel<128><<<ga, kCompThreads, 0, s>>>(Q, Ckv, Ct, N, Bq, L.nq, L.nqp, L.Lt, sm, O, lse, om);
   else
-    apply_kernel<64><<<ga, kCompThreads, 0, s>>>(Q, C, N, Bq, L.nq, L.nqp, L.Lp, sm, O, lse, om);
+    apply_kernel<64><<<ga, kCompThreads, 0, s>>>(Q, Ckv, Ct, N, Bq, L.nq, L.nqp, L.Lt, sm, O, lse, om);
   return hipGetLastError();
 }
 
