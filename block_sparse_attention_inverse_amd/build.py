@@ -3,6 +3,11 @@
 Each translation unit is compiled separately with hipcc and linked into one
 shared library that lives next to this file (in-tree, so that it travels
 with the source tree).  Usage: ``python -m block_sparse_attention_inverse_amd.build``.
+
+``--sanitize-host`` builds the host code (argument checks, launch set-up)
+with AddressSanitizer and UndefinedBehaviorSanitizer; the device code is
+unchanged.  Load it with clang's ASan runtime preloaded (see the README) and
+run the host-only ABI tests; build again without the flag afterwards.
 """
 import os
 import subprocess
@@ -51,9 +56,15 @@ def _hipcc():
     return "hipcc"
 
 
-def _compile(src, verbose):
+# host-only sanitizers: each -fsanitize goes to the host pass alone
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize=function", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src, verbose, sanitize=False):
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *(HOST_SANITIZE if sanitize else []),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,11 +77,12 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 6) -> str:
+def build(verbose: bool = False, jobs: int = 6, sanitize_host: bool = False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize_host), SOURCES))
+    san = ["-shared-libsan", "-Xarch_host", "-fsanitize=address,undefined"] if sanitize_host else []
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *san, "-o", LIB + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -79,4 +91,4 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize_host="--sanitize-host" in sys.argv))
