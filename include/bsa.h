@@ -330,9 +330,13 @@ int64_t bsa_fo_workspace(int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk
  * O, lse:  mu = max(lse, a + ln n), den = exp(lse - mu) + n exp(a - mu),
  *   O <- (O exp(lse - mu) + exp(a - mu) (Vhat + s M^T q_r)) / den,
  *   lse <- mu + ln den.
- * A row whose q-block skips nothing is left unchanged.  The sums over U use
- * per-kv-block moments rounded to bf16 and accumulated in fp32.  lse must
- * not be NULL.  workspace: >= bsa_fo_workspace(...), 256-byte aligned.
+ * A row whose q-block skips nothing is left unchanged; a row whose q-block
+ * keeps nothing (O = 0, lse = -inf from the forward) gets the compensation
+ * alone.  The sums over U use per-kv-block moments rounded to bf16 and
+ * accumulated in fp32; sum_U k v^T and M are rounded to bf16 (M feeds a bf16
+ * product), the sums of k and v and n stay fp32.  lse must not be NULL.
+ * workspace: >= bsa_fo_workspace(...), 256-byte aligned; its contents on
+ * return are scratch.  Calls that share a workspace must not overlap.
  * Errors: EINVAL, EUNSUPPORTED, ECAPACITY (workspace), EHIP. */
 int bsa_fo_compensate(const void *Qp, const void *Kp, const void *Vp, const int32_t *row_ptr,
                       const int32_t *col_idx, int64_t col_len, int32_t mask_G,
