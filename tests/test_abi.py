@@ -360,6 +360,12 @@ def test_compensation_argument_errors(lib):
     need = lib.bsa_fo_workspace(G, N, d, 128, 64)
     assert need > 0
     assert lib.bsa_fo_workspace(G, N, 96, 128, 64) == -2
+    # the skip mask is addressed with 32-bit buffer ranges: Nq and Nkv at most 32768
+    assert lib.bsa_fo_workspace(1, 32768 * 64, 64, 64, 64) > 0
+    assert lib.bsa_fo_workspace(1, 32768 * 64 + 1, 64, 64, 128) == -2
+    assert b"Nq" in lib.bsa_last_error()
+    assert lib.bsa_fo_workspace(1, 32768 * 64 + 1, 64, 128, 64) == -2
+    assert b"Nkv" in lib.bsa_last_error()
     def call(lse=fake, ws_bytes=need, ws=fake, orders=None):
         return lib.bsa_fo_compensate(fake, fake, fake, fake, fake, 10, G, orders, Fr, Hr, Wr, fake,
                                      d, G * d, lse, G, d, 128, 64, F(0), ws, ws_bytes, None)
