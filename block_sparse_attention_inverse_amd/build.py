@@ -42,8 +42,10 @@ HIPCC_FLAGS = [
 # maxima fuse into v_max3 without quieting every operand first.
 EXTRA_FLAGS = {
     "attn_bf16.hip": ["-fno-honor-nans"],
-    # the INT8 kernel reads its MFMA results with VALU ops: keep them in VGPRs
-    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the INT8 kernel reads its MFMA results with VALU ops: keep them in VGPRs.
+    # Its scales are finite for finite inputs (a NaN scale gives unspecified
+    # output), so its maxima need no NaN quieting either.
+    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     # the dense block-statistics kernel reads every score with VALU ops too
     "calib.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }

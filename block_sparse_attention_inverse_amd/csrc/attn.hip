@@ -141,9 +141,11 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 
 // LDS read offsets of this lane's operands
 template <int D>
-__device__ __forceinline__ uint32_t k_read_off() {
+__device__ __forceinline__ void k_offsets(uint32_t (&kx)[D / 32]) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
-  return static_cast<uint32_t>(l32 * D + ((h ^ swz<D>(l32)) << 4));
+  const uint32_t base = static_cast<uint32_t>(l32 * D + ((h ^ swz<D>(l32)) << 4));
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ks++) kx[ks] = base ^ (ks << 5);
 }
 template <int D>
 __device__ __forceinline__ uint32_t v_read_off() {
@@ -154,7 +156,7 @@ __device__ __forceinline__ uint32_t v_read_off() {
 
 // S^T = K . Q^T for the wave's two row halves: s[qb][b] covers kv 32b..32b+31
 template <int D, int BK, int BIAS = 0>
-__device__ __forceinline__ void qk_i8(const uint8_t* kt, uint32_t kread,
+__device__ __forceinline__ void qk_i8(const uint8_t* kt, const uint32_t (&kx)[D / 32],
                                       const i32x4 (&qf)[kQB][D / 32], i32x16 (&s)[kQB][BK / 32]) {
 #pragma unroll
   for (int b = 0; b < BK / 32; b++)
@@ -164,7 +166,7 @@ __device__ __forceinline__ void qk_i8(const uint8_t* kt, uint32_t kread,
   for (int ks = 0; ks < D / 32; ks++)
 #pragma unroll
     for (int b = 0; b < BK / 32; b++) {
-      const i32x4 a = *reinterpret_cast<const i32x4*>(kt + b * 32 * D + (kread ^ (ks << 5)));
+      const i32x4 a = *reinterpret_cast<const i32x4*>(kt + b * 32 * D + kx[ks]);
 #pragma unroll
       for (int qb = 0; qb < kQB; qb++)
         s[qb][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[qb][ks], s[qb][b], 0, 0, 0);
@@ -215,7 +217,9 @@ __device__ __forceinline__ void load_q(const int8_t* __restrict__ Q, int g, int 
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+  // every lane has a source under the controls used here; bound_ctrl lets
+  // the move fold into the consuming v_max_f32 as its DPP operand
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 // max over the 32 rows of a wave (lanes l and l + 32 carry the same row), in
 // VALU cross-lane moves only: within quads, 8-lane and 16-lane rows by DPP,
@@ -273,7 +277,7 @@ __device__ __forceinline__ void quantize_tile(const i32x16 (&s)[kQB][NB], float 
             const int kv = kv0 + 32 * b + acc_row(r, h);
             if (!any || !jvalid || kv >= N) y = 0.0f;
           }
-          ys += y;
+          ys = b == 0 && r == 0 ? y : ys + y;
           // v_cvt_pk_u8_f32 rounds half to even (checked against rintf on
           // every quarter step of 0..255 and next to every .5)
           word = __builtin_amdgcn_cvt_pk_u8_f32(y, e, word);
@@ -306,7 +310,9 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
 
   Stage8<D, BK, NW> sg;
   sg.init();
-  const uint32_t kread = k_read_off<D>(), vread = v_read_off<D>();
+  const uint32_t vread = v_read_off<D>();
+  uint32_t kx[D / 32];  // this lane's K operand offsets, one per k-step
+  k_offsets<D>(kx);
 
   i32x4 qf[kQB][D / 32];
   load_q<D>(Q, g, qbase, N, qf);
@@ -356,6 +362,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
     L::stage(vh, head_bytes, sg.v, kv0_of(j0), vbuf[0]);
     wait_loads();
     __syncthreads();
+    int kb = 0;  // K buffer of tile t (t mod 3)
     for (int t = 0; t < nt; t++) {
       const int j = j0;
       const bool jvalid = static_cast<unsigned>(j) < static_cast<unsigned>(nk);
@@ -368,7 +375,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
 
       // ---- scores and the exact running maximum of every row
       i32x16 s[kQB][NB];
-      qk_i8<D, BK, kSBias>(kbuf[t % 3], kread, qf, s);
+      qk_i8<D, BK, kSBias>(kbuf[kb], kx, qf, s);
       float x_max[kQB];
       if (!masked) {
 #pragma unroll
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
       // maximum of every wave is visible
       wait_loads();
       __syncthreads();
-      if (t + 2 < nt) L::stage(kh, head_bytes, sg.k, kv0_of(j2), kbuf[(t + 2) % 3]);
+      if (t + 2 < nt) L::stage(kh, head_bytes, sg.k, kv0_of(j2), kbuf[kb == 0 ? 2 : kb - 1]);
       if (t + 1 < nt) L::stage(vh, head_bytes, sg.v, kv0_of(j1), vbuf[(t + 1) & 1]);
       float dm = tile_max[t & 1][0];
 #pragma unroll
@@ -469,6 +476,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
             o[qb][db][r] = __builtin_fmaf(static_cast<float>(ov[qb][r]), cv[qb], o[qb][db][r]);
       }
       j0 = j1; j1 = j2; j2 = j3;
+      kb = kb == 2 ? 0 : kb + 1;
       sk0 = sk1; sv0 = sv1;
     }
   }
@@ -529,7 +537,9 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void dbg_qk_kernel(const
   wait_loads();
   __syncthreads();
   i32x16 s[kQB][BK / 32];
-  qk_i8<D, BK>(kt[0], k_read_off<D>(), qf, s);
+  uint32_t kx[D / 32];
+  k_offsets<D>(kx);
+  qk_i8<D, BK>(kt[0], kx, qf, s);
   int32_t* out = S + static_cast<int64_t>(t) * BQ * BK;
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++) {
