@@ -15,7 +15,8 @@
 //   mP  = max of Pt over the tile's real rows and columns (whole workgroup)
 //   P8  = rint(Pt * 127 / mP) in [0, 127]
 //   acc = acc * 2^(m - m') + (mP / 127) * sV_j * (P8 . v8) (exact int32)
-// and O = acc / l, LSE = (m + log2 l) * ln 2.
+// and O = acc / l, LSE = (m + log2 l) * ln 2.  The integer tile product
+// reaches acc through a biased fp32 read (see kPBias).
 //
 // Work split: one workgroup per (head g, q-block i); Bq/32 waves of 32 query
 // rows; XCD x runs a contiguous range of the head-major (head, q-block) tiles
@@ -67,6 +68,19 @@ constexpr float kNarrowF = 0x1p-11f;
 // when the maximum has risen more than this (log2 units) above it, so the
 // per-tile contributions carry a factor of at most 2^kLazy
 constexpr float kLazy = 8.0f;
+// Product bias: each tile's P8.V8 products start from the bit pattern of
+// 2^23 + 2^20 (Bk = 64) or 2^23 + 2^21 (Bk = 128); every |p8.v8| over the
+// tile is below 2^20 (2^21), so the int32 result read as an fp32 is exactly
+// that bias plus the integer product and enters O's fma without a
+// conversion.  O then carries bias * (the tile's scale) per tile, the same
+// for every element of a row; a per-row scalar keeps that offset and is
+// taken out of O every kFold tiles, so the offset never exceeds kFold tiles'
+// worth (each fma rounds at most ulp(|O| + kFold * bias * scale) / 2).
+template <int BK>
+constexpr int kPBias = BK == 64 ? 0x4B100000 : 0x4B200000;
+template <int BK>
+constexpr float kPBiasF = BK == 64 ? 9437184.0f : 10485760.0f;
+constexpr int kFold = 4;
 // 32-row halves per wave: one, so a 128-row q-block is four waves and two
 // workgroups give every SIMD two waves whose products and softmax interleave
 constexpr int kQB = 1;
@@ -175,12 +189,13 @@ __device__ __forceinline__ void qk_i8(const uint8_t* kt, const uint32_t (&kx)[D 
 
 // One channel block of O^T (int32, this tile only) = V^T . P8^T for the
 // wave's row halves: ov[qb] covers channels 32db..32db+31 of half qb.  The
-// first product takes its accumulator from zacc, a register block that holds
-// zeros for the whole kernel (the product writes ov, not zacc), so no
-// per-tile clearing of ov is issued.
+// first product takes its accumulator from acc0, a register block that holds
+// its start value for the whole kernel (zeros, or the forward's product
+// bias; the product writes ov, not acc0), so no per-tile clearing of ov is
+// issued.
 template <int D, int BK>
 __device__ __forceinline__ void pv_block(const uint8_t* vt, uint32_t vread, const i32x4 (&pf)[kQB][BK / 32],
-                                         int db, const i32x16& zacc, i32x16 (&ov)[kQB]) {
+                                         int db, const i32x16& acc0, i32x16 (&ov)[kQB]) {
   const uint32_t vhi = (vread ^ ((D / 32) << 4)) + 8 * D;  // rows +8: the swizzle flips CH/2
 #pragma unroll
   for (int b = 0; b < BK / 32; b++) {
@@ -191,7 +206,7 @@ __device__ __forceinline__ void pv_block(const uint8_t* vt, uint32_t vread, cons
     const i32x4 a = (i32x4){lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
     for (int qb = 0; qb < kQB; qb++)
-      ov[qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[qb][b], b == 0 ? zacc : ov[qb], 0, 0, 0);
+      ov[qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, pf[qb][b], b == 0 ? acc0 : ov[qb], 0, 0, 0);
   }
 }
 
@@ -334,11 +349,13 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
   // m: the exact running row maximum (the P quantisation is relative to
   // it); O and l are kept relative to an older reference mf <= m and only
   // moved to the running maximum when it has risen more than kLazy above mf
-  float m[kQB], mf[kQB], l[kQB];
+  float m[kQB], mf[kQB], l[kQB], pend[kQB];
 #pragma unroll
-  for (int qb = 0; qb < kQB; qb++) { m[qb] = kRefInit; mf[qb] = kRefInit; l[qb] = 0.0f; }
-  i32x16 zacc = {};
-  asm volatile("" : "+v"(zacc));  // zeros kept in registers (see pv_block)
+  for (int qb = 0; qb < kQB; qb++) { m[qb] = kRefInit; mf[qb] = kRefInit; l[qb] = 0.0f; pend[qb] = 0.0f; }
+  i32x16 pacc;
+#pragma unroll
+  for (int r = 0; r < 16; r++) pacc[r] = kPBias<BK>;
+  asm volatile("" : "+v"(pacc));  // the product bias kept in registers (see pv_block)
   f32x16 o[kQB][D / 32];
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++)
@@ -425,6 +442,7 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
           const float alpha = up ? __builtin_amdgcn_exp2f(mf[qb] - m[qb]) : 1.0f;
           mf[qb] = up ? m[qb] : mf[qb];
           l[qb] *= alpha;
+          pend[qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < D / 32; db++)
 #pragma unroll
@@ -468,12 +486,24 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
 #pragma unroll
       for (int db = 0; db < D / 32; db++) {
         i32x16 ov[kQB];
-        pv_block<D, BK>(vbuf[t & 1], vread, pf, db, zacc, ov);
+        pv_block<D, BK>(vbuf[t & 1], vread, pf, db, pacc, ov);
 #pragma unroll
         for (int qb = 0; qb < kQB; qb++)
 #pragma unroll
           for (int r = 0; r < 16; r++)
-            o[qb][db][r] = __builtin_fmaf(static_cast<float>(ov[qb][r]), cv[qb], o[qb][db][r]);
+            o[qb][db][r] = __builtin_fmaf(__int_as_float(ov[qb][r]), cv[qb], o[qb][db][r]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < kQB; qb++) pend[qb] = __builtin_fmaf(cv[qb], kPBiasF<BK>, pend[qb]);
+      if (t % kFold == kFold - 1) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; qb++) {
+#pragma unroll
+          for (int db = 0; db < D / 32; db++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) o[qb][db][r] -= pend[qb];
+          pend[qb] = 0.0f;
+        }
       }
       j0 = j1; j1 = j2; j2 = j3;
       kb = kb == 2 ? 0 : kb + 1;
@@ -483,6 +513,11 @@ __global__ __launch_bounds__(BQ / kRowsPerWave * kWave) void fwd_i8_kernel(
 
 #pragma unroll
   for (int qb = 0; qb < kQB; qb++) {
+    // the offset of the last tiles since the previous fold
+#pragma unroll
+    for (int db = 0; db < D / 32; db++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) o[qb][db][r] -= pend[qb];
     const float lt = l[qb] + __shfl_xor(l[qb], 32);
     const int row = qbase + 32 * qb + l32;
     if (row < N) {
