@@ -80,6 +80,7 @@ template <int BK>
 constexpr int kPBias = BK == 64 ? 0x4B100000 : 0x4B200000;
 template <int BK>
 constexpr float kPBiasF = BK == 64 ? 9437184.0f : 10485760.0f;
+static_assert(64 * 127 * 127 < (1 << 20) && 128 * 127 * 127 < (1 << 21), "product range of a tile");
 constexpr int kFold = 4;
 // 32-row halves per wave: one, so a 128-row q-block is four waves and two
 // workgroups give every SIMD two waves whose products and softmax interleave
