@@ -3,7 +3,8 @@
 * every (d, Bq, Bk) forward instantiation the C ABI accepts, bf16 and INT8,
   on a short sequence with a ragged tail, against the oracle;
 * INT8 with large score scales (wide Q / K ranges and single outliers), where
-  the tile maximum's code must stay at 127;
+  the tile maximum's code must stay at 127, and at the largest integer tile
+  products (every code at its bound);
 * run-to-run bitwise equality of both forwards at the 480p shape;
 * guard regions around every output buffer (O natural and reordered, lse,
   row_ptr, col_idx, nnz, INT8 codes and scales, block sums), which must be
@@ -154,6 +155,32 @@ def test_int8_large_score_scales(bsa_gpu, orc, kind, scale):
     ci = np.tile(np.arange(nk, dtype=np.int32), G * nq)
     _say(f"[int8 large scales {kind} x{scale}]")
     _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, f"int8 {kind} x{scale}")
+
+
+# ------------------------------------------------- INT8 at the product bound
+@pytest.mark.parametrize("Bk", [64, 128])
+def test_int8_extreme_tile_products(bsa_gpu, orc, Bk):
+    """Every code at its largest magnitude: Q = 0 makes every score 0, so
+    every P8 code is 127, and V is +0.5 in one head and -0.5 in the other, so
+    every V8 code is +-127.  Each full tile's integer product then reaches
+    +-Bk * 127 * 127, the bound the kernel's biased fp32 read of the product
+    tiles relies on, and every output element must be +-0.5 (the last,
+    ragged kv-block has fewer real columns)."""
+    G, N, d, Bq = 2, 500, 128, 128
+    r = np.random.Generator(np.random.PCG64(900 + Bk))
+    Q = np.zeros((G, N, d), np.float32)
+    K = r.standard_normal((G, N, d)).astype(np.float32)
+    V = np.empty((G, N, d), np.float32)
+    V[0], V[1] = 0.5, -0.5
+    Qp, Kp, Vp = (_bf16(x) for x in (Q, K, V))
+    nq, nk = -(-N // Bq), -(-N // Bk)
+    rp = np.arange(0, G * nq * nk + 1, nk, dtype=np.int32)
+    ci = np.tile(np.arange(nk, dtype=np.int32), G * nq)
+    _say(f"[int8 extreme products Bk={Bk}]")
+    O8 = _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, f"int8 extreme Bk={Bk}")
+    o8 = _np(O8.float())
+    assert np.array_equal(o8[0], np.full((N, d), 0.5, np.float32))
+    assert np.array_equal(o8[1], np.full((N, d), -0.5, np.float32))
 
 
 # ------------------------------------------------- determinism
