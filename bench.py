@@ -357,7 +357,10 @@ def reorder_bandwidth(plan, Q, od, F, H, W, reps):
     of one bf16 tensor (2*N*G*d*2; indices are computed, not read), against
     the HBM peak and against a plain device copy of the same size timed in
     the same run.  The fused pass (reorder + fp32 block sums) adds its sums
-    to the written bytes."""
+    to the written bytes.  The INT8 quantiser is judged the same way: read
+    bf16, write int8 codes and fp32 scales, standalone on the reordered
+    tensor and fused into the reorder (codes, scales and block sums from the
+    natural tensor, no bf16 copy)."""
     import torch
 
     import block_sparse_attention_inverse_amd as bsa
@@ -374,6 +377,14 @@ def reorder_bandwidth(plan, Q, od, F, H, W, reps):
     t_fused = event_ms(lambda: bsa.permute_pool(Q, od, F, H, W, p.Bq, out=plan.Qp, sums=plan.sums_q),
                        reps)
     sums_bytes = G * -(-N // p.Bq) * d * 4
+    nb = -(-N // p.Bq)
+    codes = torch.empty((G, N, d), dtype=torch.int8, device="cuda")
+    scales = torch.empty((G, nb), dtype=torch.float32, device="cuda")
+    t_quant = event_ms(lambda: bsa.quantize_int8(plan.Qp, p.Bq, out=(codes, scales)), reps)
+    t_fused8 = event_ms(lambda: bsa.permute_pool(Q, od, F, H, W, p.Bq, sums=plan.sums_q,
+                                                 int8=(codes, scales), reordered=False), reps)
+    del codes, scales
+    quant_bytes = nbytes + nbytes // 2 + G * nb * 4  # bf16 read, int8 written, scales
 
     def gbs(byt, ms):
         return byt / (ms / 1e3) / 1e9
@@ -389,12 +400,17 @@ def reorder_bandwidth(plan, Q, od, F, H, W, reps):
         "scatter_gbs": gbs(2 * nbytes, t_scatter),
         "fused_gather_with_block_sums_ms": t_fused,
         "fused_gather_with_block_sums_gbs": gbs(2 * nbytes + sums_bytes, t_fused),
+        "quantize_int8_ms": t_quant,
+        "quantize_int8_gbs": gbs(quant_bytes, t_quant),
+        "fused_quantize_with_block_sums_ms": t_fused8,
+        "fused_quantize_with_block_sums_gbs": gbs(quant_bytes + sums_bytes, t_fused8),
         "peak_gbs": HBM_PEAK_GBS,
     }
     out["gather_frac_peak"] = out["gather_gbs"] / HBM_PEAK_GBS
     out["gather_vs_copy"] = out["gather_gbs"] / out["device_copy_gbs"]
     out["fused_frac_peak"] = out["fused_gather_with_block_sums_gbs"] / HBM_PEAK_GBS
     out["copy_frac_peak"] = out["device_copy_gbs"] / HBM_PEAK_GBS
+    out["quantize_frac_peak"] = out["quantize_int8_gbs"] / HBM_PEAK_GBS
     return out
 
 
