@@ -12,7 +12,9 @@ on the same seeded inputs:
 * the first-order compensation applied to that output, against the oracle's
   compensated attention on every second row;
 * the INT8 forward on the same mask, every q-block, against the oracle's INT8
-  emulation on its own quantisation of the same bf16 values.
+  emulation on its own quantisation of the same bf16 values;
+* the order choice (SICS scores, bit for bit) and the calibration's block
+  statistics of the dense map.
 """
 import numpy as np
 import pytest
@@ -87,3 +89,42 @@ def test_random_shape(bsa_gpu, orc, k):
 
     # INT8 forward on the same mask
     _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, wrp, wci, Bq, Bk, f"int8 case {k}")
+
+
+@pytest.mark.parametrize("k", range(NCASES))
+def test_random_shape_order_choice_and_calibration(bsa_gpu, orc, k):
+    """The same draws through the order choice and the offline calibration:
+    SICS scores of Q and K over the six axis orders bit for bit and the same
+    chosen orders; block statistics of the dense map (block = Bq) with each
+    count inside the oracle's bracket at eps(1 -+ 1e-3) and equal where no
+    entry lies in it, sums and maxima within 2e-4 relative."""
+    c = _draw(k)
+    F, H, W, N, G, d, B = c["F"], c["H"], c["W"], c["N"], c["G"], c["d"], c["Bq"]
+    orders = c["orders"][:G].copy()
+    _say(f"[random shape {k}: order choice and calibration] N={N} G={G} d={d} B={B}")
+    r = np.random.Generator(np.random.PCG64(c["seed"]))
+    nat = [r.standard_normal((N, G, d)).astype(np.float32) for _ in range(3)]
+    dev = [_bf16(x) for x in nat[:2]]
+    host = [_bits(x) for x in dev]
+
+    sq = bsa_gpu.order_scores(dev[0], F, H, W, B)
+    sk = bsa_gpu.order_scores(dev[1], F, H, W, B)
+    chosen = bsa_gpu.select_orders(sq, sk)
+    torch.cuda.synchronize()
+    wq = orc.sics_scores(host[0], G, F, H, W, d, B)
+    wk = orc.sics_scores(host[1], G, F, H, W, d, B)
+    assert np.array_equal(_np(sq).view(np.uint32), wq.view(np.uint32))
+    assert np.array_equal(_np(sk).view(np.uint32), wk.view(np.uint32))
+    assert np.array_equal(_np(chosen), orc.select_orders(wq, wk))
+
+    od = torch.from_numpy(orders).cuda()
+    Qp, Kp = (bsa_gpu.permute(x, od, F, H, W, 0) for x in dev)
+    cnt, bsum, bmax = bsa_gpu.attn_block_stats(Qp, Kp, B, 1e-3)
+    torch.cuda.synchronize()
+    want = orc.block_stats(_bits(Qp), _bits(Kp), B, 1e-3, delta=1e-3)
+    cn = _np(cnt)
+    assert np.all(want["cnt_lo"] <= cn) and np.all(cn <= want["cnt_hi"])
+    sure = want["cnt_lo"] == want["cnt_hi"]
+    assert np.array_equal(cn[sure], want["cnt"][sure])
+    assert np.allclose(_np(bsum).astype(np.float64), want["sum"], rtol=2e-4, atol=1e-9)
+    assert np.allclose(_np(bmax).astype(np.float64), want["max"], rtol=2e-4, atol=1e-12)
