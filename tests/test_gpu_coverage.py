@@ -62,16 +62,18 @@ def _bf16(x):
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).cuda()
 
 
-def _int8_all_blocks(bsa, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, tag):
+def _int8_all_blocks(bsa, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, tag, host_p):
     """GPU: quantise reordered bf16 Qp/Kp/Vp [G][N][d] and run the INT8
-    forward; oracle: its own quantiser on the same bf16 values, then the
-    INT8 emulation on every q-block.  Returns the GPU output."""
+    forward; oracle: its own quantiser on host_p, the same bf16 values in the
+    same [G][N][d] order held on the host (the inputs themselves, or the
+    oracle's own reorder of them), then the INT8 emulation on every q-block.
+    Returns the GPU output."""
     G, N, d = Qp.shape
     (qq, sq), (kq, sk), (vq, sv) = (bsa.quantize_int8(x, B) for x, B in ((Qp, Bq), (Kp, Bk), (Vp, Bk)))
     O8, L8 = bsa.forward_int8(qq, sq, kq, sk, vq, sv, torch.from_numpy(rp).cuda(),
                               torch.from_numpy(ci).cuda(), Bq, Bk)
     torch.cuda.synchronize()
-    oq = [orc.quantize_int8(_bits(x), B) for x, B in ((Qp, Bq), (Kp, Bk), (Vp, Bk))]
+    oq = [orc.quantize_int8(x, B) for x, B in zip(host_p, (Bq, Bk, Bk))]
     nq = -(-N // Bq)
     blocks = np.array([(g, i) for g in range(G) for i in range(nq)], np.int64)
     Ow, Lw = orc.attention_int8(oq[0][0], oq[0][1], oq[1][0], oq[1][1], oq[2][0], oq[2][1], Bq, Bk,
@@ -125,8 +127,9 @@ def test_forward_every_instantiation(bsa_gpu, orc, d, Bq, Bk):
     _compare(_np(O.float())[rows[:, 1], rows[:, 0]], Ow, f"bf16 d={d} {Bq}x{Bk}", heads=rows[:, 0])
     lg = _np(lse)[rows[:, 0], rows[:, 1]]
     assert np.max(np.abs(lg - Lw)) <= LSE_ABS
-    # INT8 on the reordered tensors
-    _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, f"int8 d={d} {Bq}x{Bk}")
+    # INT8 on the reordered tensors (the oracle reorders the host bits itself)
+    host_p = [orc.permute(0, h, np.uint16, G, F, H, W, d, orders) for h in host]
+    _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, f"int8 d={d} {Bq}x{Bk}", host_p)
 
 
 # ------------------------------------------------- INT8 with large score scales
@@ -150,11 +153,12 @@ def test_int8_large_score_scales(bsa_gpu, orc, kind, scale):
             for b0 in range(0, N, B):
                 X[:, b0 + int(r.integers(min(B, N - b0))), int(r.integers(d))] = scale
     Qp, Kp, Vp = (_bf16(x) for x in (Q, K, V))
+    host_p = [orc.f32_to_bf16(x) for x in (Q, K, V)]
     nq, nk = -(-N // Bq), -(-N // Bk)
     rp = np.arange(0, G * nq * nk + 1, nk, dtype=np.int32)
     ci = np.tile(np.arange(nk, dtype=np.int32), G * nq)
     _say(f"[int8 large scales {kind} x{scale}]")
-    _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, f"int8 {kind} x{scale}")
+    _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, f"int8 {kind} x{scale}", host_p)
 
 
 # ------------------------------------------------- INT8 at the product bound
@@ -173,11 +177,12 @@ def test_int8_extreme_tile_products(bsa_gpu, orc, Bk):
     V = np.empty((G, N, d), np.float32)
     V[0], V[1] = 0.5, -0.5
     Qp, Kp, Vp = (_bf16(x) for x in (Q, K, V))
+    host_p = [orc.f32_to_bf16(x) for x in (Q, K, V)]
     nq, nk = -(-N // Bq), -(-N // Bk)
     rp = np.arange(0, G * nq * nk + 1, nk, dtype=np.int32)
     ci = np.tile(np.arange(nk, dtype=np.int32), G * nq)
     _say(f"[int8 extreme products Bk={Bk}]")
-    O8 = _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, f"int8 extreme Bk={Bk}")
+    O8 = _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, rp, ci, Bq, Bk, f"int8 extreme Bk={Bk}", host_p)
     o8 = _np(O8.float())
     assert np.array_equal(o8[0], np.full((N, d), 0.5, np.float32))
     assert np.array_equal(o8[1], np.full((N, d), -0.5, np.float32))

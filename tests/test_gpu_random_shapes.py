@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 import torch
 
-from test_gpu_coverage import _bf16, _bits, _compare, _int8_all_blocks, _np, _say
+from test_gpu_coverage import _bf16, _compare, _int8_all_blocks, _np, _say
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +57,9 @@ def test_random_shape(bsa_gpu, orc, k):
     p = bsa_gpu.mask_params(Bq, Bk, c["score"], c["rho"], c["force_diag"], c["win_T"], c["win_r0"])
     grp, gci, gnnz = bsa_gpu.build_mask(Qp, Kp, od, F, H, W, p)
     torch.cuda.synchronize()
-    wrp, wci = orc.build_mask(_bits(Qp), _bits(Kp), F, H, W, orders, Bq, Bk, c["score"], c["rho"][0],
+    host = [orc.f32_to_bf16(x) for x in nat]  # the same bf16 values, converted by the oracle
+    host_p = [orc.permute(0, h, np.uint16, G, F, H, W, d, orders) for h in host]
+    wrp, wci = orc.build_mask(host_p[0], host_p[1], F, H, W, orders, Bq, Bk, c["score"], c["rho"][0],
                               c["rho"][1], int(c["force_diag"]), c["win_T"], c["win_r0"])
     n = int(_np(gnnz)[0])
     assert n == int(wrp[-1])
@@ -67,7 +69,6 @@ def test_random_shape(bsa_gpu, orc, k):
     # bf16 forward, natural-order output, every row
     O, lse = bsa_gpu.forward_natural(Qp, Kp, Vp, grp, gci, Bq, Bk, od, F, H, W)
     torch.cuda.synchronize()
-    host = [_bits(x) for x in dev]
     rows = np.array([(g, t) for g in range(G) for t in range(N)], np.int64)
     Ow, Lw = orc.attention_rows(*host, G, F, H, W, d, orders, rows, Bq, Bk, wrp, wci)
     _compare(_np(O.float())[rows[:, 1], rows[:, 0]], Ow, f"bf16 case {k}", heads=rows[:, 0])
@@ -88,7 +89,7 @@ def test_random_shape(bsa_gpu, orc, k):
     assert np.all(np.abs(lg[fin] - Lc[fin]) <= LSE_ABS + 2.0 ** -21 * np.abs(Lc[fin]))
 
     # INT8 forward on the same mask
-    _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, wrp, wci, Bq, Bk, f"int8 case {k}")
+    _int8_all_blocks(bsa_gpu, orc, Qp, Kp, Vp, wrp, wci, Bq, Bk, f"int8 case {k}", host_p)
 
 
 @pytest.mark.parametrize("k", range(NCASES))
@@ -105,7 +106,7 @@ def test_random_shape_order_choice_and_calibration(bsa_gpu, orc, k):
     r = np.random.Generator(np.random.PCG64(c["seed"]))
     nat = [r.standard_normal((N, G, d)).astype(np.float32) for _ in range(3)]
     dev = [_bf16(x) for x in nat[:2]]
-    host = [_bits(x) for x in dev]
+    host = [orc.f32_to_bf16(x) for x in nat[:2]]
 
     sq = bsa_gpu.order_scores(dev[0], F, H, W, B)
     sk = bsa_gpu.order_scores(dev[1], F, H, W, B)
@@ -121,7 +122,8 @@ def test_random_shape_order_choice_and_calibration(bsa_gpu, orc, k):
     Qp, Kp = (bsa_gpu.permute(x, od, F, H, W, 0) for x in dev)
     cnt, bsum, bmax = bsa_gpu.attn_block_stats(Qp, Kp, B, 1e-3)
     torch.cuda.synchronize()
-    want = orc.block_stats(_bits(Qp), _bits(Kp), B, 1e-3, delta=1e-3)
+    host_p = [orc.permute(0, h, np.uint16, G, F, H, W, d, orders) for h in host]
+    want = orc.block_stats(host_p[0], host_p[1], B, 1e-3, delta=1e-3)
     cn = _np(cnt)
     assert np.all(want["cnt_lo"] <= cn) and np.all(cn <= want["cnt_hi"])
     sure = want["cnt_lo"] == want["cnt_hi"]

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from test_gpu_parity import _np, _say, case, mask_params
+from test_gpu_parity import _np, _say, case, mask_params, oracle_reorder
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +23,16 @@ def _sums(bsa, c, p):
     _, sq, _ = bsa.permute_pool(c["Q"], c["orders_dev"], F, H, W, p.Bq, sums=True, reordered=False)
     _, sk, _ = bsa.permute_pool(c["K"], c["orders_dev"], F, H, W, p.Bk, sums=True, reordered=False)
     return sq, sk
+
+
+def _oracle_keys(orc, c, p):
+    """The oracle's block keys from the host inputs: its own reorder, block
+    sums and keys (nothing taken from the GPU)."""
+    cfg = c["cfg"]
+    G, N = cfg["G"], cfg["F"] * cfg["H"] * cfg["W"]
+    sq = orc.block_sums(oracle_reorder(orc, c, "Q"), p.Bq)
+    sk = orc.block_sums(oracle_reorder(orc, c, "K"), p.Bk)
+    return np.stack([orc.block_keys(sq[g], sk[g], N, p.Bq, p.Bk, p.score) for g in range(G)])
 
 
 SCORE_CASES = [
@@ -48,8 +58,7 @@ def test_block_scores_and_topk_bit_exact(bsa_gpu, orc, cid, over, rho):
     rp, ci, nnz = bsa_gpu.mask_from_scores(sc, c["orders_dev"], F, H, W, p)
     rp2, ci2, nnz2 = bsa_gpu.build_mask_pooled(sq, sk, c["orders_dev"], F, H, W, p)
     torch.cuda.synchronize()
-    N = F * H * W
-    want = np.stack([orc.block_keys(_np(sq)[g], _np(sk)[g], N, p.Bq, p.Bk, p.score) for g in range(G)])
+    want = _oracle_keys(orc, c, p)
     assert np.array_equal(_np(sc).view(np.uint32), want.view(np.uint32))
     n = int(_np(nnz)[0])
     assert n == int(_np(nnz2)[0])
@@ -75,7 +84,9 @@ def test_topk_with_noise_bit_exact(bsa_gpu, orc, cid, scale):
     rp, ci, nnz = bsa_gpu.mask_from_scores(sc, c["orders_dev"], F, H, W, p,
                                            noise=torch.from_numpy(noise).cuda(), noise_scale=scale)
     torch.cuda.synchronize()
-    kp = orc.perturb_keys(_np(sc), noise, scale)
+    want = _oracle_keys(orc, c, p)
+    assert np.array_equal(_np(sc).view(np.uint32), want.view(np.uint32))
+    kp = orc.perturb_keys(want, noise, scale)
     wrp, wci = orc.select(kp, G, F, H, W, p.Bq, p.Bk, c["orders"], p.rho_num, p.rho_den,
                           p.force_diag, p.win_T, p.win_r0)
     n = int(_np(nnz)[0])
@@ -112,7 +123,9 @@ def test_topp_parity(bsa_gpu, orc, cid, top_p, temp):
     rp, ci, nnz = bsa_gpu.mask_from_scores(sc, c["orders_dev"], F, H, W, p, top_p=top_p, temp=temp)
     torch.cuda.synchronize()
     n = int(_np(nnz)[0])
-    _topp_compare(orc, _np(rp), _np(ci)[:n], _np(sc), G, F, H, W, p, c["orders"], top_p, temp)
+    want = _oracle_keys(orc, c, p)
+    assert np.array_equal(_np(sc).view(np.uint32), want.view(np.uint32))
+    _topp_compare(orc, _np(rp), _np(ci)[:n], want, G, F, H, W, p, c["orders"], top_p, temp)
 
 
 def test_topp_with_noise_and_exact_weights(bsa_gpu, orc):
