@@ -144,7 +144,7 @@ def test_order_scores_planted_axis(bsa_gpu, orc, axis):
     s = bsa_gpu.order_scores(x, F, H, W, B)
     o = bsa_gpu.select_orders(s)
     torch.cuda.synchronize()
-    host = _bits(x)
+    host = orc.f32_to_bf16(X)
     want = orc.sics_scores(host, G, F, H, W, d, B)
     assert np.array_equal(_np(s).view(np.uint32), want.view(np.uint32))
     winners = [i for i, nm in enumerate(["FHW", "FWH", "HFW", "HWF", "WFH", "WHF"])
@@ -166,7 +166,7 @@ def test_order_scores_small_and_ragged(bsa_gpu, orc, d, B, N3):
         x = torch.from_numpy(X).cuda().to(dt)
         s = bsa_gpu.order_scores(x, F, H, W, B)
         torch.cuda.synchronize()
-        host = _bits(x) if dt == torch.bfloat16 else X
+        host = orc.f32_to_bf16(X) if dt == torch.bfloat16 else X
         want = orc.sics_scores(host, G, F, H, W, d, B)
         assert np.array_equal(_np(s).view(np.uint32), want.view(np.uint32)), (dt, N3)
 
