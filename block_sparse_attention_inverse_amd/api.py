@@ -685,16 +685,20 @@ def debug_int8_pv(P8, Vq, gj, Bq, Bk):
 class LayerPlan:
     """Buffers for one attention layer over natural-order [N][G][d] tensors:
     reordered copies, mask CSR, INT8 copies and the output, allocated once
-    and reused by :func:`layer_forward`."""
+    and reused by :func:`layer_forward`.  ``compensate=True`` adds the
+    first-order compensation of the skipped keys after the forward (its
+    workspace allocated here; it reads the bf16 reordered Q, K, V, which the
+    INT8 chain then also writes)."""
 
     def __init__(self, G, F, H, W, d, device, params: MaskParams, int8=False, dynamic_mask=True,
-                 fused=False):
+                 fused=False, compensate=False):
         N = F * H * W
         self.G, self.F, self.H, self.W, self.d, self.N = G, F, H, W, d, N
         self.params = params
         self.int8 = int8
         self.dynamic_mask = dynamic_mask
         self.fused = fused
+        self.compensate = compensate
         e = dict(device=device)
         self.Qp = torch.empty((G, N, d), dtype=torch.bfloat16, **e)
         self.Kp = torch.empty_like(self.Qp)
@@ -712,6 +716,9 @@ class LayerPlan:
             nk = (N + params.Bk - 1) // params.Bk
             self.sums_q = torch.empty((G, nq, d), dtype=torch.float32, **e)
             self.sums_k = torch.empty((G, nk, d), dtype=torch.float32, **e)
+        if compensate:
+            self.fo_ws = torch.empty(fo_workspace(G, N, d, params.Bq, params.Bk), dtype=torch.uint8,
+                                     **e)
         if int8:
             nk = (N + params.Bk - 1) // params.Bk
             self.Qq = torch.empty((G, N, d), dtype=torch.int8, **e)
@@ -735,13 +742,14 @@ class LayerPlan:
         k8 = (self.Kq, self.sK) if self.int8 else None
         v8 = (self.Vq, self.sV) if self.int8 else None
         F, H, W = self.F, self.H, self.W
-        bf = not self.int8  # the INT8 attention reads only the codes
+        # the INT8 attention reads only the codes; the compensation reads bf16
+        bf = not self.int8 or self.compensate
         permute_pool(Q, axis_order, F, H, W, p.Bq, out=self.Qp, sums=self.sums_q, int8=q8,
                      reordered=bf)
         permute_pool(K, axis_order, F, H, W, p.Bk, out=self.Kp, sums=self.sums_k, int8=k8,
                      reordered=bf)
         if self.int8:
-            permute_pool(V, axis_order, F, H, W, p.Bk, int8=v8, reordered=False)
+            permute_pool(V, axis_order, F, H, W, p.Bk, out=self.Vp, int8=v8, reordered=bf)
         else:
             permute_pool(V, axis_order, F, H, W, p.Bk, out=self.Vp)
 
@@ -768,7 +776,9 @@ def layer_forward(plan: LayerPlan, Q, K, V, axis_order):
     -> inverse reorder.  With ``plan.fused`` the reorder, the block pooling
     and the INT8 quantisation share one pass per tensor, and the inverse
     reorder is the attention's own epilogue (``plan.lse`` is then indexed by
-    natural token).  Returns the natural-order output [N][G][d] (bf16)."""
+    natural token).  With ``plan.compensate`` the first-order compensation
+    of the skipped keys follows the attention.  Returns the natural-order
+    output [N][G][d] (bf16)."""
     F, H, W = plan.F, plan.H, plan.W
     p = plan.params
     if plan.fused:
@@ -791,6 +801,9 @@ def layer_forward(plan: LayerPlan, Q, K, V, axis_order):
         else:
             forward_natural(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk,
                             axis_order, F, H, W, out=plan.O, lse=plan.lse)
+        if plan.compensate:
+            fo_compensate(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk, plan.O,
+                          plan.lse, axis_order, F, H, W, workspace=plan.fo_ws)
         return plan.O
     if plan.int8:
         forward_int8(plan.Qq, plan.sQ, plan.Kq, plan.sK, plan.Vq, plan.sV, plan.row_ptr,
@@ -798,5 +811,8 @@ def layer_forward(plan: LayerPlan, Q, K, V, axis_order):
     else:
         forward(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk, out=plan.Op,
                 lse=plan.lse)
+    if plan.compensate:
+        fo_compensate(plan.Qp, plan.Kp, plan.Vp, plan.row_ptr, plan.col_idx, p.Bq, p.Bk, plan.Op,
+                      plan.lse, F=F, H=H, W=W, workspace=plan.fo_ws)
     permute(plan.Op, axis_order, F, H, W, 1, out=plan.O)
     return plan.O

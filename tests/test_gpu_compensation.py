@@ -235,3 +235,33 @@ def test_compensation_leaves_rows_without_skipped_keys_unchanged(bsa_gpu, orc):
     err = np.abs(_np(l2)[rows[:, 0], rows[:, 1]] - Lw)
     _say(f"  lse max_abs={err.max():.3e}")
     assert np.all(err <= LSE_ABS + 2.0 ** -21 * np.abs(Lw))
+
+
+@pytest.mark.parametrize("int8,fused", [(False, True), (True, True), (False, False)])
+def test_layer_forward_with_compensation(bsa_gpu, int8, fused):
+    """layer_forward with compensate=True gives, bit for bit, the same chain
+    without it followed by bsa_fo_compensate on its output (480p layer, mask
+    built from the sums or from Qp and Kp)."""
+    c = case(3)
+    cfg = c["cfg"]
+    G, F, H, W, d = cfg["G"], cfg["F"], cfg["H"], cfg["W"], cfg["d"]
+    p = mask_params(bsa_gpu, cfg)
+    od = c["orders_dev"]
+    _say(f"[layer_forward compensate int8={int8} fused={fused}]")
+    plan = bsa_gpu.LayerPlan(G, F, H, W, d, "cuda", p, int8=int8, fused=fused, compensate=True)
+    got = bsa_gpu.layer_forward(plan, c["Q"], c["K"], c["V"], od).clone()
+    got_lse = plan.lse.clone()
+    ref = bsa_gpu.LayerPlan(G, F, H, W, d, "cuda", p, int8=int8, fused=fused)
+    out = bsa_gpu.layer_forward(ref, c["Q"], c["K"], c["V"], od)
+    # the bf16 reordered inputs the compensation reads (the INT8 chain skips them)
+    Qp, Kp, Vp = (bsa_gpu.permute(c[x], od, F, H, W, 0) for x in ("Q", "K", "V"))
+    if fused:
+        bsa_gpu.fo_compensate(Qp, Kp, Vp, ref.row_ptr, ref.col_idx, p.Bq, p.Bk, out, ref.lse, od,
+                              F, H, W)
+    else:
+        bsa_gpu.fo_compensate(Qp, Kp, Vp, ref.row_ptr, ref.col_idx, p.Bq, p.Bk, ref.Op, ref.lse,
+                              F=F, H=H, W=W)
+        out = bsa_gpu.permute(ref.Op, od, F, H, W, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(got_lse, ref.lse)
