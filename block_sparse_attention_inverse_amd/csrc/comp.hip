@@ -321,11 +321,12 @@ __global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __res
 //   b. M^T (bf16, [b][a]) into LDS: M[a][b] = C_kv[a][b] - kbar_a Vhat_b;
 //   c. per row, from the Q fragments: a = s q.kbar, the old and new terms'
 //      weights divided by the new denominator, the new lse;
-//   d. Y = Q_i M on v_mfma_f32_32x32x16_bf16 (B = M^T rows from LDS); lane l
-//      of accumulator bb holds channel b = 32bb + l%32 of rows
-//      32w + 8(r/4) + 4(l/32) + r%4;
-//   e. O' = O w_old + w_new (Vhat + s y), written where the forward wrote O
-//      (the old values are read before the products).
+//   d. Y^T = M^T Q_i^T on v_mfma_f32_32x32x16_bf16 (A = M^T rows from LDS,
+//      B = the Q fragments); lane l of accumulator bb holds row 32w + l%32
+//      and channels 32bb + 8(r/4) + 4(l/32) + r%4;
+//   e. O' = O w_old + w_new (Vhat + s y), written where the forward wrote O,
+//      four consecutive channels of the lane's own row per 8-byte access
+//      (every old value is read before the first store).
 template <int D>
 __global__ __launch_bounds__(kCompThreads, 3) void apply_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Ckv, const float* __restrict__ Ct,
@@ -334,7 +335,8 @@ __global__ __launch_bounds__(kCompThreads, 3) void apply_kernel(
   constexpr int NB = D / 32;      // 32-channel blocks of the output
   constexpr int KS = D / 16;      // k-steps of Y = Q M
   constexpr int PM = D + 8;       // bf16 per LDS row of M^T
-  __shared__ float kbar[D], vhat[D];
+  __shared__ __attribute__((aligned(16))) float kbar[D];
+  __shared__ __attribute__((aligned(16))) float vhat[D];
   __shared__ __attribute__((aligned(16))) uint16_t mt[D][PM];
   __shared__ float w_old[128], w_new[128];
   __shared__ int64_t row_off[128];  // element offset of each row's output
@@ -411,41 +413,48 @@ __global__ __launch_bounds__(kCompThreads, 3) void apply_kernel(
   }
   __syncthreads();
   if (rb >= nr) return;  // no later barrier
-  // e (first half). the old values of this lane's 16 rows, read before the
-  // products (the stores below could alias them as far as the compiler knows)
-  uint16_t oldv[16][NB];
-#pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int rr = rb + 8 * (r / 4) + 4 * h + (r % 4);
-#pragma unroll
-    for (int bb = 0; bb < NB; bb++) oldv[r][bb] = rr < nr ? O[row_off[rr] + 32 * bb + l32] : 0;
-  }
-  // d. Y = Q_i M for the wave's 32 rows
+  // d. Y^T = M^T Q_i^T for the wave's 32 rows: lane l of accumulator bb holds
+  // query row rb + l%32 and channels 32bb + 8(r/4) + 4(l/32) + r%4, so each
+  // lane updates four consecutive channels of its own row per (bb, r/4)
   f32x16 acc[NB];
 #pragma unroll
   for (int bb = 0; bb < NB; bb++) acc[bb] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < KS; ks++) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, qf[ks]);
+    const bf16x8 b = __builtin_bit_cast(bf16x8, qf[ks]);
 #pragma unroll
     for (int bb = 0; bb < NB; bb++) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&mt[32 * bb + l32][16 * ks + 8 * h]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&mt[32 * bb + l32][16 * ks + 8 * h]);
       acc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[bb], 0, 0, 0);
     }
   }
-  // e. the update
+  // e. the update, 8-byte reads and writes of this lane's row
+  if (qrow < nr) {
+    const float wo = w_old[qrow], wn = w_new[qrow];
+    uint16_t* op = O + row_off[qrow];
+    uint2 old[NB][4];  // every old value first (the stores below could alias them as far as the compiler knows)
 #pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int rr = rb + 8 * (r / 4) + 4 * h + (r % 4);
-    if (rr >= nr) continue;
-    const float wo = w_old[rr], wn = w_new[rr];
-    uint16_t* op = O + row_off[rr];
+    for (int bb = 0; bb < NB; bb++)
 #pragma unroll
-    for (int bb = 0; bb < NB; bb++) {
-      const int b = 32 * bb + l32;
-      const float y = __builtin_fmaf(sm, acc[bb][r], vhat[b]);
-      op[b] = bf16_bits(__builtin_fmaf(bf16_bits_to_f32(oldv[r][bb]), wo, wn * y));
-    }
+      for (int r4 = 0; r4 < 4; r4++) old[bb][r4] = *reinterpret_cast<const uint2*>(op + 32 * bb + 8 * r4 + 4 * h);
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const int b0 = 32 * bb + 8 * r4 + 4 * h;
+        const uint2 ov = old[bb][r4];
+        const float4 vh = *reinterpret_cast<const float4*>(&vhat[b0]);
+        const float y0 = __builtin_fmaf(sm, acc[bb][4 * r4 + 0], vh.x);
+        const float y1 = __builtin_fmaf(sm, acc[bb][4 * r4 + 1], vh.y);
+        const float y2 = __builtin_fmaf(sm, acc[bb][4 * r4 + 2], vh.z);
+        const float y3 = __builtin_fmaf(sm, acc[bb][4 * r4 + 3], vh.w);
+        uint2 nv;
+        nv.x = f32_to_bf16_bits(__builtin_fmaf(bf16_bits_to_f32(ov.x & 0xFFFFu), wo, wn * y0)) |
+               (f32_to_bf16_bits(__builtin_fmaf(bf16_bits_to_f32(ov.x >> 16), wo, wn * y1)) << 16);
+        nv.y = f32_to_bf16_bits(__builtin_fmaf(bf16_bits_to_f32(ov.y & 0xFFFFu), wo, wn * y2)) |
+               (f32_to_bf16_bits(__builtin_fmaf(bf16_bits_to_f32(ov.y >> 16), wo, wn * y3)) << 16);
+        *reinterpret_cast<uint2*>(op + b0) = nv;
+      }
   }
 }
 
