@@ -51,8 +51,11 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) { return static_cast<uint
 // holds one channel a of K over 8 rows; B = V: one channel b over the same
 // 8 rows).  sum k and sum v are the same products against a bf16 ones
 // operand.  Wave w takes the KV tiles w*TPW .. w*TPW+TPW-1 (32 x 32 each)
-// and SPW of the 2*D/32 sum blocks (k blocks first, then v blocks).
-template <int D>
+// and SPW of the 2*D/32 sum blocks (k blocks first, then v blocks).  LDS
+// holds exactly the block's SUB = Bk/64 sub-tiles of K and V (32 KB at
+// d = 128, Bk = 64, three workgroups per CU), and the d x d block leaves
+// through the same area.
+template <int D, int SUB>
 __global__ __launch_bounds__(kCompThreads) void kv_moments_kernel(const uint16_t* __restrict__ K,
                                                                   const uint16_t* __restrict__ V,
                                                                   int N, int Bk, int nk, int nkp,
@@ -64,8 +67,10 @@ __global__ __launch_bounds__(kCompThreads) void kv_moments_kernel(const uint16_t
   constexpr int TPW = DB * DB / 4, SPW = 2 * DB / 4;
   typedef short s4 __attribute__((ext_vector_type(4)));
   typedef short s8 __attribute__((ext_vector_type(8)));
-  __shared__ __attribute__((aligned(1024))) uint8_t kt[2][TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vt[2][TB];
+  // K sub-tiles u at u * TB, V sub-tiles at (SUB + u) * TB (SUB = Bk / 64)
+  __shared__ __attribute__((aligned(1024))) uint8_t kvs[2 * SUB * TB];
+  auto kt = [&](int u) { return kvs + u * TB; };
+  auto vt = [&](int u) { return kvs + (SUB + u) * TB; };
   const int g = blockIdx.x / nkp, j = blockIdx.x % nkp;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -82,13 +87,12 @@ __global__ __launch_bounds__(kCompThreads) void kv_moments_kernel(const uint16_t
   // load q of wave w fills rows RPI*(4q + w) + lane/CH; the swizzle does not depend on q
   const int rl = RPI * w + lane / CH;
   const uint32_t voff = static_cast<uint32_t>(rl * ROWB + (((lane % CH) ^ ((2 * rl) & (CH - 1))) << 4));
-  const int nsub = Bk / 64;
-  for (int u = 0; u < nsub; u++)
+  for (int u = 0; u < SUB; u++)
 #pragma unroll
     for (int q = 0; q < NI; q++) {
       const uint32_t so = static_cast<uint32_t>((r0 + 64 * u + 4 * RPI * q) * ROWB);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(&kt[u][(4 * q + w) * 1024]), 16, voff, so, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(&vt[u][(4 * q + w) * 1024]), 16, voff, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)(kt(u) + (4 * q + w) * 1024), 16, voff, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)(vt(u) + (4 * q + w) * 1024), 16, voff, so, 0, 0);
     }
   // transposed-read offsets (channel block x: xor x << 6)
   const int rsub = (lane & 15) >> 2;
@@ -109,27 +113,28 @@ __global__ __launch_bounds__(kCompThreads) void kv_moments_kernel(const uint16_t
   for (int y = 0; y < SPW; y++) sm[y] = f32x16{};
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int u = 0; u < nsub; u++)
+#pragma unroll
+  for (int u = 0; u < SUB; u++)
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
 #pragma unroll
       for (int x = 0; x < TPW; x++) {
         const int k = w * TPW + x, ab = k / DB, bb = k % DB;
-        kv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr(kt[u], ks, ab), tr(vt[u], ks, bb), kv[x], 0, 0, 0);
+        kv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr(kt(u), ks, ab), tr(vt(u), ks, bb), kv[x], 0, 0, 0);
       }
 #pragma unroll
       for (int y = 0; y < SPW; y++) {
         const int sb = w * SPW + y;
-        if (sb < DB) sm[y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr(kt[u], ks, sb), ones, sm[y], 0, 0, 0);
-        else sm[y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, tr(vt[u], ks, sb - DB), sm[y], 0, 0, 0);
+        if (sb < DB) sm[y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr(kt(u), ks, sb), ones, sm[y], 0, 0, 0);
+        else sm[y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, tr(vt(u), ks, sb - DB), sm[y], 0, 0, 0);
       }
     }
   // KV tile: lane holds channel b = 32bb + l32 of rows a = 32ab + 8(r/4) + 4h + r%4.
   // The tiles go through LDS (over the staged K, which every wave has
   // finished reading) so that the row is written with 16-byte stores.
-  static_assert(2 * TB >= D * D * 2, "the K staging area holds the d x d block");
+  static_assert(2 * SUB * TB >= D * D * 2, "the staging area holds the d x d block");
   __syncthreads();
-  uint16_t* ot = reinterpret_cast<uint16_t*>(&kt[0][0]);
+  uint16_t* ot = reinterpret_cast<uint16_t*>(kvs);
 #pragma unroll
   for (int x = 0; x < TPW; x++) {
     const int k = w * TPW + x, ab = k / DB, bb = k % DB;
@@ -497,8 +502,10 @@ hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint
   auto* Ct = reinterpret_cast<float*>(ws + L.ct);
   const float sm = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d));
   const uint32_t gm = static_cast<uint32_t>(G) * L.nkp;
-  if (d == 128) kv_moments_kernel<128><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
-  else kv_moments_kernel<64><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
+  if (d == 128 && Bk == 64) kv_moments_kernel<128, 1><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
+  else if (d == 128) kv_moments_kernel<128, 2><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
+  else if (Bk == 64) kv_moments_kernel<64, 1><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
+  else kv_moments_kernel<64, 2><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
   skip_mask_kernel<<<static_cast<uint32_t>(G) * L.nqp, kCompThreads, sizeof(uint16_t) * L.nkp, s>>>(
       row_ptr, col_idx, col_len, mask_G, L.nq, L.nk, L.nqp, L.nkp, S);
   const int ti = L.nqp / kTileI, tc = L.Lp / kTileC;
