@@ -22,7 +22,8 @@
 //   1. kv_moments_kernel: per kv-block j, X_j = [sum k v^T (d x d, row-major)
 //      | sum k | sum v | rows | 0...], bf16, one row of length Lp;
 //   2. skip_mask_kernel: S[i][j] = 1 for the kv-blocks row i skips, else 0
-//      (bf16; rows padded to a multiple of 128, columns to one of 64, with zeros);
+//      (bits, one 64-bit word per row and 64 kv-blocks; rows padded to a
+//      multiple of 128, columns to one of 64, with zeros);
 //   3. skip_gemm_kernel: C = S . X per head (bf16 MFMA, fp32 accumulation):
 //      row i of C holds the sums over U_i, so M_i = C_kv - kbar Vhat^T (the
 //      d x d block C_kv stored as bf16, the sums and the count as fp32);
@@ -165,15 +166,18 @@ __global__ __launch_bounds__(kCompThreads) void kv_moments_kernel(const uint16_t
     *reinterpret_cast<uint4*>(xr + 8 * c) = *reinterpret_cast<const uint4*>(ot + 8 * c);
 }
 
-// 2. S[g][i][j] = 1 for the kv-blocks q-block row i skips (padding: 0)
+// 2. the skip mask as bits: S[g][i][j] = 1 for the kv-blocks q-block row i
+// skips (padding: 0).  Word w of a row covers kv-blocks 64w .. 64w+63; its
+// byte 2ks + h holds in bits 0..3 the kv-blocks 16ks + 4h + 0..3 and in
+// bits 4..7 the kv-blocks 16ks + 8 + 4h + 0..3 of the word: the order in
+// which the GEMM's transposing reads of X hand lane half h its k values.
 __global__ __launch_bounds__(kCompThreads) void skip_mask_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
-    int mask_G, int nq, int nk, int nqp, int nkp, uint16_t* __restrict__ S) {
-  extern __shared__ uint16_t srow[];  // [nkp]
+    int mask_G, int nq, int nk, int nqp, int nkp, uint64_t* __restrict__ S) {
+  extern __shared__ uint8_t srow[];  // [nkp]
   const int g = blockIdx.x / nqp, i = blockIdx.x % nqp;
   const int t = threadIdx.x;
-  const uint16_t one = 0x3F80;
-  for (int j = t; j < nkp; j += kCompThreads) srow[j] = (i < nq && j < nk) ? one : 0;
+  for (int j = t; j < nkp; j += kCompThreads) srow[j] = (i < nq && j < nk) ? 1 : 0;
   __syncthreads();
   if (i < nq) {
     const int64_t r = static_cast<int64_t>(g % mask_G) * nq + i;
@@ -186,22 +190,34 @@ __global__ __launch_bounds__(kCompThreads) void skip_mask_kernel(
     }
   }
   __syncthreads();
-  uint16_t* out = S + (static_cast<int64_t>(g) * nqp + i) * nkp;
-  for (int j = t; j < nkp; j += kCompThreads) out[j] = srow[j];
+  const int nw = nkp / 64;
+  uint64_t* out = S + (static_cast<int64_t>(g) * nqp + i) * nw;
+  for (int wd = t; wd < nw; wd += kCompThreads) {
+    uint64_t v = 0;
+#pragma unroll
+    for (int by = 0; by < 8; by++) {
+      const int base = 64 * wd + 16 * (by >> 1) + 4 * (by & 1);
+#pragma unroll
+      for (int bt = 0; bt < 8; bt++)
+        v |= static_cast<uint64_t>(srow[base + (bt & 3) + 8 * (bt >> 2)]) << (8 * by + bt);
+    }
+    out[wd] = v;
+  }
 }
 
 // 3. C[g][i][c] = sum_j S[g][i][j] X[g][j][c].  Products C^T = X^T . S^T on
 // v_mfma_f32_32x32x16_bf16: A = X^T (32 columns x 16 kv-blocks), B = S^T
 // (16 kv-blocks x 32 rows).  A workgroup owns 128 rows i and 128 columns c;
-// each stage of 64 kv-blocks moves global -> LDS with 16-byte buffer loads
-// that write LDS directly (double-buffered, the next stage in flight under
-// the current one's products, one barrier per stage):
+// each stage of 64 kv-blocks of X moves global -> LDS with 16-byte buffer
+// loads that write LDS directly (double-buffered, the next stage in flight
+// under the current one's products, one barrier per stage):
 //   X stage: 64 x 128 (256-byte rows), chunk p of row r at
 //            p ^ (2r mod 16); A operands come out of ds_read_b64_tr_b16, two
 //            reads per operand, which give a lane half h the kv-blocks
 //            16ks + 4h + (0..3) and 16ks + 8 + 4h + (0..3) of k-step ks;
-//   S stage: 128 x 64 (128-byte rows), chunk p of row r at p ^ ((r/2) mod 8);
-//            B operands are two 8-byte reads in the same kv-block order.
+//   S:       each lane reads its row's 64-bit word of the stage straight from
+//            memory one stage ahead; the byte of its k-step and lane half
+//            indexes a 256-entry LDS table of the eight bf16 0/1 values.
 // Eight waves: wave w owns rows [32(w/2), +32) and columns [64(w%2), +64)
 // (channel blocks 2(w%2), 2(w%2)+1): two accumulators; lane l of an
 // accumulator holds row 32(w/2) + l%32 and columns cb + 8(r/4) + 4(l/32) + r%4.
@@ -209,16 +225,15 @@ __global__ __launch_bounds__(kCompThreads) void skip_mask_kernel(
 // tile), so the row tiles that share an X stage run together on one L2.
 constexpr int kGemmJ = 64;       // kv-blocks per stage
 constexpr int kXSub = 64 * 256;   // bytes of one X stage (64 rows x 128 columns)
-constexpr int kSTile = 128 * 128; // bytes of one S stage (128 rows x 64 kv-blocks)
 
-__global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __restrict__ S,
+__global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint64_t* __restrict__ S,
                                                                     const uint16_t* __restrict__ X,
                                                                     int G, int nqp, int nkp, int Lp,
                                                                     int dd, int tiles_i, int tiles_c,
                                                                     uint16_t* __restrict__ Ckv,
                                                                     float* __restrict__ Ct) {
   __shared__ __attribute__((aligned(1024))) uint8_t xs[2][kXSub];
-  __shared__ __attribute__((aligned(1024))) uint8_t ss[2][kSTile];
+  __shared__ __attribute__((aligned(16))) uint4 tbl[256];  // byte v -> eight bf16 (bit e ? 1 : 0)
   int g, item;
   if (!xcd_range_tile(blockIdx.x, tiles_i * tiles_c, G, g, item)) return;
   const int tc = item / tiles_i, ti = item % tiles_i;
@@ -226,18 +241,22 @@ __global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __res
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wr = w >> 1, wc = w & 1;  // 32-row quarter, 64-column half
   const int l32 = lane & 31, h = lane >> 5;
+  if (t < 256) {
+    uint32_t q[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+      q[e] = ((t >> (2 * e)) & 1 ? 0x3F80u : 0u) | ((t >> (2 * e + 1)) & 1 ? 0x3F800000u : 0u);
+    tbl[t] = make_uint4(q[0], q[1], q[2], q[3]);
+  }
   const uint16_t* Xg = X + static_cast<int64_t>(g) * nkp * Lp;
-  const uint16_t* Sg = S + static_cast<int64_t>(g) * nqp * nkp;
+  const int nw = nkp / kGemmJ;
+  const uint64_t* Srow = S + (static_cast<int64_t>(g) * nqp + i0 + 32 * wr + l32) * nw;
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Xg), 0, static_cast<int>(static_cast<int64_t>(nkp) * Lp * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Sg), 0, static_cast<int>(static_cast<int64_t>(nqp) * nkp * 2), 0x00020000);
-  // staging lane offsets: X load q of wave w fills rows 32q + 4w + lane/16,
-  // S load q rows 64q + 8w + lane/8 (the swizzles depend on lane and w only)
+  // staging lane offsets: X load q of wave w fills rows 32q + 4w + lane/16
+  // (the swizzle depends on lane and w only)
   const uint32_t vx_ld = static_cast<uint32_t>((4 * w + (lane >> 4)) * (Lp * 2) +
                                                (((lane & 15) ^ ((8 * w + 2 * (lane >> 4)) & 15)) << 4));
-  const uint32_t vs_ld = static_cast<uint32_t>((8 * w + (lane >> 3)) * (nkp * 2) +
-                                               (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4));
   const uint32_t wb = static_cast<uint32_t>(w) * 1024u;
   auto stage = [&](int j0, int buf) {
 #pragma unroll
@@ -245,11 +264,6 @@ __global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __res
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rx, (LDS_AS void*)(&xs[buf][q * 8192 + wb]), 16, vx_ld,
           static_cast<uint32_t>((j0 + 32 * q) * Lp * 2 + c0 * 2), 0, 0);
-#pragma unroll
-    for (int q = 0; q < 2; q++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (LDS_AS void*)(&ss[buf][q * 8192 + wb]), 16, vs_ld,
-          static_cast<uint32_t>((i0 + 64 * q) * nkp * 2 + j0 * 2), 0, 0);
   };
   // operand read offsets
   const int rsub = (lane & 15) >> 2;
@@ -259,23 +273,24 @@ __global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __res
   uint32_t ax[2];
 #pragma unroll
   for (int cbk = 0; cbk < 2; cbk++) ax[cbk] = vread ^ static_cast<uint32_t>((2 * wc + cbk) << 6);
-  uint32_t bx[1];
-  bx[0] = static_cast<uint32_t>((32 * wr + l32) * 128 + 8 * h);
-  const int bsw = (l32 >> 1) & 7;  // the same for every row block (64wr + 32ib + l32)
   f32x16 acc[2][1];
 #pragma unroll
   for (int a = 0; a < 2; a++) acc[a][0] = f32x16{};
   const int nst = nkp / kGemmJ;
   stage(0, 0);
+  uint64_t sw = Srow[0];
   for (int st = 0; st < nst; st++) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (st + 1 < nst) stage((st + 1) * kGemmJ, (st + 1) & 1);
+    const uint64_t cur = sw;
+    if (st + 1 < nst) {
+      stage((st + 1) * kGemmJ, (st + 1) & 1);
+      sw = Srow[st + 1];
+    }
     const uint8_t* xt = xs[st & 1];
-    const uint8_t* sl = ss[st & 1];
 #pragma unroll
     for (int ks = 0; ks < kGemmJ / 16; ks++) {
-      bf16x8 a[2], b[1];
+      bf16x8 a[2];
 #pragma unroll
       for (int cbk = 0; cbk < 2; cbk++) {
         typedef short s4 __attribute__((ext_vector_type(4)));
@@ -284,15 +299,12 @@ __global__ __launch_bounds__(512, 2) void skip_gemm_kernel(const uint16_t* __res
         a[cbk] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
                                                 lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
-#pragma unroll
-      for (int ib = 0; ib < 1; ib++) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(sl + bx[ib] + (((2 * ks) ^ bsw) << 4));
-        const uint2 hi = *reinterpret_cast<const uint2*>(sl + bx[ib] + (((2 * ks + 1) ^ bsw) << 4));
-        b[ib] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      }
+      const uint32_t half = ks < 2 ? static_cast<uint32_t>(cur) : static_cast<uint32_t>(cur >> 32);
+      const uint32_t idx = (half >> (8 * ((2 * ks + h) & 3))) & 0xFFu;
+      const bf16x8 b = __builtin_bit_cast(bf16x8, tbl[idx]);
 #pragma unroll
       for (int cbk = 0; cbk < 2; cbk++)
-        acc[cbk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cbk], b[0], acc[cbk][0], 0, 0, 0);
+        acc[cbk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cbk], b, acc[cbk][0], 0, 0, 0);
     }
   }
   // C's d x d block is stored as bf16 (it becomes the bf16 M^T operand of the
@@ -482,7 +494,7 @@ FoLayout fo_layout(int G, int N, int d, int Bq, int Bk) {
     return o;
   };
   L.x = take(sizeof(uint16_t) * static_cast<size_t>(G) * L.nkp * L.Lp);
-  L.s = take(sizeof(uint16_t) * static_cast<size_t>(G) * L.nqp * L.nkp);
+  L.s = take(static_cast<size_t>(G) * L.nqp * (L.nkp / 64) * sizeof(uint64_t));
   L.Lt = L.Lp - d * d;
   L.ckv = take(sizeof(uint16_t) * static_cast<size_t>(G) * L.nqp * d * d);
   L.ct = take(sizeof(float) * static_cast<size_t>(G) * L.nqp * L.Lt);
@@ -497,7 +509,7 @@ hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint
                                 hipStream_t s) {
   const FoLayout L = fo_layout(G, N, d, Bq, Bk);
   auto* X = reinterpret_cast<uint16_t*>(ws + L.x);
-  auto* S = reinterpret_cast<uint16_t*>(ws + L.s);
+  auto* S = reinterpret_cast<uint64_t*>(ws + L.s);
   auto* Ckv = reinterpret_cast<uint16_t*>(ws + L.ckv);
   auto* Ct = reinterpret_cast<float*>(ws + L.ct);
   const float sm = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf(static_cast<float>(d));
@@ -506,7 +518,7 @@ hipError_t launch_fo_compensate(const uint16_t* Q, const uint16_t* K, const uint
   else if (d == 128) kv_moments_kernel<128, 2><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
   else if (Bk == 64) kv_moments_kernel<64, 1><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
   else kv_moments_kernel<64, 2><<<gm, kCompThreads, 0, s>>>(K, V, N, Bk, L.nk, L.nkp, L.Lp, X);
-  skip_mask_kernel<<<static_cast<uint32_t>(G) * L.nqp, kCompThreads, sizeof(uint16_t) * L.nkp, s>>>(
+  skip_mask_kernel<<<static_cast<uint32_t>(G) * L.nqp, kCompThreads, L.nkp, s>>>(
       row_ptr, col_idx, col_len, mask_G, L.nq, L.nk, L.nqp, L.nkp, S);
   const int ti = L.nqp / kTileI, tc = L.Lp / kTileC;
   const uint32_t ng = kNumXcd * static_cast<uint32_t>((L.gemm_tiles + kNumXcd - 1) / kNumXcd);
