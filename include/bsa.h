@@ -311,7 +311,8 @@ int bsa_forward_int8_natural(const int8_t *Qq, const float *sQ, const int8_t *Kq
 
 /* bsa_fo_workspace — bytes of device workspace bsa_fo_compensate needs
  * (per-kv-block moments, the skip mask and the sums over each q-block
- * row's skipped set: about G*Nkv*d*d*2 + G*Nq*d*d*4 bytes), or a negative
+ * row's skipped set, the d x d parts in bf16: about 2*G*(Nkv + Nq)*d*d
+ * bytes, Nq and Nkv padded), or a negative
  * status (d not in {64, 128}, B not in {64, 128}, Nq or Nkv > 32768). */
 int64_t bsa_fo_workspace(int32_t G, int32_t N, int32_t d, int32_t Bq, int32_t Bk);
 
