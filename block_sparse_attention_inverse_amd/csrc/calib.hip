@@ -280,16 +280,19 @@ __global__ __launch_bounds__(kMetThreads) void paro_metric_kernel(
   const int64_t base = static_cast<int64_t>(g) * nblk;
   int nsp = 0;
   float isum = 0.0f;
-  for (int i = 0; i < nb; i++) {
-    const int li = min(B, N - i * B);
-    const int64_t rb = base + static_cast<int64_t>(i) * nb;
-    for (int j = t; j < nb; j += kMetThreads) {
-      const int lj = min(B, N - j * B);
-      const int64_t area = static_cast<int64_t>(li) * lj;
-      nsp += static_cast<int64_t>(cnt[rb + j]) * sigma_den >= static_cast<int64_t>(sigma_num) * area;
-      const float s = bsum[rb + j];
-      isum += s > 0.0f ? bmax[rb + j] * static_cast<float>(area) / s : 1.0f;
-    }
+  // every thread strides over the flattened nb x nb blocks (independent
+  // loads, all threads busy); (i, j) follow the flat index incrementally
+  const int di = kMetThreads / nb, dj = kMetThreads % nb;
+  int i = t / nb, j = t % nb;
+#pragma unroll 4
+  for (int64_t e = t; e < nblk; e += kMetThreads) {
+    const int64_t area = static_cast<int64_t>(min(B, N - i * B)) * min(B, N - j * B);
+    nsp += static_cast<int64_t>(cnt[base + e]) * sigma_den >= static_cast<int64_t>(sigma_num) * area;
+    const float s = bsum[base + e];
+    isum += s > 0.0f ? bmax[base + e] * static_cast<float>(area) / s : 1.0f;
+    i += di;
+    j += dj;
+    if (j >= nb) { j -= nb; i++; }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
