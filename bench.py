@@ -352,6 +352,25 @@ def event_ms(fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def graph_replay(step, eager_s, reps):
+    """The whole step captured once into a HIP graph (torch.cuda.graph on a
+    side stream after one eager pass there) and replayed back to back: time
+    per replay beside the eager step time."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    t = event_ms(g.replay, reps)
+    return {"replay_ms_per_step": t, "eager_ms_per_step": eager_s * 1e3}
+
+
 def reorder_bandwidth(plan, Q, od, F, H, W, reps):
     """The reorder judged by achieved GB/s: algorithmic bytes = read + write
     of one bf16 tensor (2*N*G*d*2; indices are computed, not read), against
@@ -819,6 +838,9 @@ def main():
         log("[bench] density sweep (30 % and 20 %)")
         result["density"] = density_sweep(plan, plan8, Q, K, V, od, F, H, W,
                                           reps=max(3, args.steps // 4))
+        log("[bench] the step captured into a HIP graph")
+        result["graph"] = graph_replay(step_bf16, wall, reps=max(5, args.steps // 2))
+        log(f"[bench] graph: {result['graph']}")
         log("[bench] first-order compensation")
         step_bf16()
         result["compensation"] = compensation(plan, od, F, H, W, reps=max(3, args.steps // 4),
